@@ -1,0 +1,159 @@
+"""fp64 CPU oracle of the tree-causal draft-head hot path.
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the CPU-baseline leg of
+the benchmark may use it; the product path (the HIP library and its binding)
+never imports it.  It shares no code with the HIP path.
+
+Thin ctypes wrappers over ``oracle.c`` (built with gcc into
+``oracle/liboracle.so``).  Inputs are numpy arrays already widened exactly to
+float64; see ``oracle.c`` for the definitions and the passages they follow.
+
+Parity status of each function (what pins it, see tests/test_oracle_*.py):
+  tree_mask  -- pinned: hand-derived golden fixture, chain/star closed forms,
+                set recursion, bad-tree cases.
+  tree_attn  -- pinned: chain == causal attention (library SDPA), star ==
+                prefix+self attention, path-by-path brute force, hand-computed
+                golden example, q=0 / lone-root closed forms, GQA head map via
+                library SDPA with grouped heads, perturbation invariance.
+  fuse_proj  -- pinned: numpy matmul of the concatenation, identity selector.
+  topk       -- pinned: numpy lexsort brute force, all-equal rows, signed
+                zeros, -inf, scipy logsumexp.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SO = os.path.join(_HERE, "liboracle.so")
+_SRC = os.path.join(_HERE, "oracle.c")
+_lib = None
+
+OK, INVALID, BAD_TREE, BAD_PAGE = 0, 1, 5, 6
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc (fp64, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_SO):
+        tmp = _SO + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+                               "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _SO)
+    return _SO
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(_SRC):
+        build(force=True)
+    lib = ctypes.CDLL(_SO)
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    lib.oracle_tree_mask.argtypes = [P, I64, I64, P, P, P]
+    lib.oracle_tree_mask.restype = ctypes.c_int
+    lib.oracle_fuse_proj.argtypes = [P, I64, I64, I64, P, I64, P]
+    lib.oracle_fuse_proj.restype = None
+    lib.oracle_fuse_proj_rows.argtypes = [P, I64, I64, I64, P, I64, P, I64, P]
+    lib.oracle_fuse_proj_rows.restype = None
+    lib.oracle_tree_attn.argtypes = [P, P, P, P, P, P, P, I64, P, I64, I64, I64, I64, I64,
+                                     I64, I64, ctypes.c_double, P, I64, P, P]
+    lib.oracle_tree_attn.restype = ctypes.c_int
+    lib.oracle_topk.argtypes = [P, I64, I64, I64, P, P, P]
+    lib.oracle_topk.restype = None
+    _lib = lib
+    return lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dt):
+    return np.ascontiguousarray(a, dtype=dt)
+
+
+def tree_mask(parent: np.ndarray):
+    """Ancestor bitmask [B, N, ceil(N/64)] uint64, depth [B, N], status, first bad row."""
+    parent = _c(parent, np.int32)
+    B, N = parent.shape
+    W = (N + 63) // 64
+    mask = np.zeros((B, N, W), dtype=np.uint64)
+    depth = np.zeros((B, N), dtype=np.int32)
+    bad = np.zeros(1, dtype=np.int64)
+    st = _load().oracle_tree_mask(_p(parent), B, N, _p(mask), _p(depth), _p(bad))
+    return mask, depth, int(st), int(bad[0])
+
+
+def fuse_proj(x: np.ndarray, w: np.ndarray, rows=None) -> np.ndarray:
+    """x [k, M, H_in] float64, w [H_out, k*H_in] float64 -> y [M or len(rows), H_out]."""
+    x = _c(x, np.float64)
+    w = _c(w, np.float64)
+    k, M, H_in = x.shape
+    H_out = w.shape[0]
+    assert w.shape == (H_out, k * H_in)
+    lib = _load()
+    if rows is None:
+        y = np.empty((M, H_out), dtype=np.float64)
+        lib.oracle_fuse_proj(_p(x), k, M, H_in, _p(w), H_out, _p(y))
+    else:
+        rows = _c(rows, np.int64)
+        y = np.empty((rows.shape[0], H_out), dtype=np.float64)
+        lib.oracle_fuse_proj_rows(_p(x), k, M, H_in, _p(w), H_out, _p(rows), rows.shape[0], _p(y))
+    return y
+
+
+def tree_attn(*, q, k_tree, v_tree, parent, k_cache, v_cache, block_table, prefix_len,
+              page_size, scale=None, rows=None):
+    """Tree attention in float64.
+
+    q [B,N,Hq,D], k_tree/v_tree [B,N,Hkv,D], k_cache/v_cache
+    [num_pages,page_size,Hkv,D] (all float64), parent [B,N] int32,
+    block_table [B,max_pages] int32, prefix_len [B] int32.
+    Returns (out, lse): [B,N,Hq,D] and [B,N,Hq], or [n_rows,D] and [n_rows]
+    for rows = flat ids (b*N+i)*Hq+h.
+    """
+    q = _c(q, np.float64)
+    k_tree = _c(k_tree, np.float64)
+    v_tree = _c(v_tree, np.float64)
+    k_cache = _c(k_cache, np.float64)
+    v_cache = _c(v_cache, np.float64)
+    parent = _c(parent, np.int32)
+    block_table = _c(block_table, np.int32)
+    prefix_len = _c(prefix_len, np.int32)
+    B, N, Hq, D = q.shape
+    Hkv = k_tree.shape[2]
+    num_pages = k_cache.shape[0]
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    if rows is None:
+        out = np.empty((B, N, Hq, D), dtype=np.float64)
+        lse = np.empty((B, N, Hq), dtype=np.float64)
+        rp, nr = None, 0
+    else:
+        rows = _c(rows, np.int64)
+        out = np.empty((rows.shape[0], D), dtype=np.float64)
+        lse = np.empty((rows.shape[0],), dtype=np.float64)
+        rp, nr = _p(rows), rows.shape[0]
+    st = _load().oracle_tree_attn(
+        _p(q), _p(k_tree), _p(v_tree), _p(parent), _p(k_cache), _p(v_cache),
+        _p(block_table), block_table.shape[1], _p(prefix_len), B, N, Hq, Hkv, D,
+        page_size, num_pages, float(scale), rp, nr, _p(out), _p(lse))
+    if st != OK:
+        raise ValueError(f"oracle_tree_attn status {st}")
+    return out, lse
+
+
+def topk(logits: np.ndarray, k: int, with_lse: bool = True):
+    """Top-k (value desc, index asc) of each row of float64 logits [R, V]."""
+    logits = _c(logits, np.float64)
+    R, V = logits.shape
+    idx = np.empty((R, k), dtype=np.int32)
+    val = np.empty((R, k), dtype=np.float64)
+    lse = np.empty((R,), dtype=np.float64) if with_lse else None
+    _load().oracle_topk(_p(logits), R, V, k, _p(idx), _p(val), _p(lse))
+    return idx, val, lse

@@ -1,0 +1,272 @@
+/*
+ * oracle.c -- plain fp64 CPU oracle of the tree-causal draft-head hot path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call, link or
+ * load this file or the library built from it; only the tests, the smoke
+ * check and the CPU-baseline leg of the benchmark do.  It shares no code,
+ * header, table or helper with the HIP kernels.
+ *
+ * Every function is the textbook definition written out in double precision
+ * over inputs that the caller has already widened exactly to double (bf16 and
+ * float32 values are exactly representable).  OpenMP only splits independent
+ * output rows across threads; no blocking, fusion or reordering of any sum.
+ *
+ * Sources (the JetFlow/JetSpec pages):
+ *   - tree-causal visibility: JetFlow blog page, "What JetFlow Does
+ *     Differently": a node sees the original prefix and its ancestors in the
+ *     tree, never its siblings or descendants.
+ *   - branch-wise factorisation (why per-node distributions are needed): same
+ *     section, the path probability as a product of conditionals along the
+ *     branch.
+ *   - hidden-state fusion from several frozen target layers: abstract (all
+ *     pages) and the same blog section; the pages do not give the fusion op.
+ *
+ * Readings where the pages are silent (listed with reasons in the design
+ * notes): a node is its own ancestor; parent -1 means "child of the prefix
+ * end"; softmax scale defaults to 1/sqrt(D); query head h reads KV head
+ * h / (Hq/Hkv); the fusion is concatenation followed by one bias-free linear
+ * map; top-k order is value descending then index ascending, -0 == +0.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OR_OK 0
+#define OR_INVALID 1
+#define OR_BAD_TREE 5
+#define OR_BAD_PAGE 6
+
+/* ---------------------------------------------------------------------------
+ * Ancestor sets.
+ *
+ * anc(i) = {i} u anc(parent(i)), with parent -1 ending the walk at the prefix.
+ * Row i of the mask holds bit j (word j/64, bit j%64) iff j is in anc(i);
+ * depth(i) = |anc(i)|.  A row is bad when its walk meets a parent outside
+ * [-1, N) or does not end within N steps (a cycle, including parent(i) == i).
+ * Returns OR_BAD_TREE and the smallest flat index b*N+i of a bad row, or OR_OK.
+ * ------------------------------------------------------------------------- */
+int oracle_tree_mask(const int32_t *parent, int64_t B, int64_t N,
+                     uint64_t *mask, int32_t *depth, int64_t *first_bad)
+{
+    int64_t W = (N + 63) / 64;
+    int64_t bad = -1;
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t i = 0; i < N; ++i) {
+            uint64_t *row = mask + (b * N + i) * W;
+            for (int64_t w = 0; w < W; ++w) row[w] = 0;
+            int64_t j = i, steps = 0;
+            int ok = 1;
+            while (j != -1) {
+                if (j < -1 || j >= N || steps >= N) { ok = 0; break; }
+                row[j / 64] |= (uint64_t)1 << (j % 64);
+                steps += 1;
+                j = parent[b * N + j];
+            }
+            if (depth) depth[b * N + i] = ok ? (int32_t)steps : 0;
+            if (!ok && bad < 0) bad = b * N + i;
+        }
+    }
+    if (first_bad) *first_bad = bad;
+    return bad < 0 ? OR_OK : OR_BAD_TREE;
+}
+
+/* Membership of j in anc(i), by walking the parent chain (no mask involved). */
+static int is_ancestor(const int32_t *par, int64_t N, int64_t i, int64_t j)
+{
+    int64_t k = i, steps = 0;
+    while (k != -1 && k >= 0 && k < N && steps <= N) {
+        if (k == j) return 1;
+        k = par[k];
+        steps += 1;
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Fused projection: y[m, o] = sum_l sum_c x_l[m, c] * w[o, l*H_in + c].
+ * x is [k, M, H_in] (the k fused layers stacked), w is [H_out, k*H_in]
+ * (row o holds the weights of output o, the torch Linear layout).
+ * ------------------------------------------------------------------------- */
+void oracle_fuse_proj(const double *x, int64_t k, int64_t M, int64_t H_in,
+                      const double *w, int64_t H_out, double *y)
+{
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t o = 0; o < H_out; ++o) {
+            double acc = 0.0;
+            for (int64_t l = 0; l < k; ++l) {
+                const double *xr = x + (l * M + m) * H_in;
+                const double *wr = w + o * (k * H_in) + l * H_in;
+                for (int64_t c = 0; c < H_in; ++c) acc += xr[c] * wr[c];
+            }
+            y[m * H_out + o] = acc;
+        }
+    }
+}
+
+/* Same, for a list of output rows only (rows[r] = m); y is [n_rows, H_out]. */
+void oracle_fuse_proj_rows(const double *x, int64_t k, int64_t M, int64_t H_in,
+                           const double *w, int64_t H_out, const int64_t *rows,
+                           int64_t n_rows, double *y)
+{
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t r = 0; r < n_rows; ++r) {
+        for (int64_t o = 0; o < H_out; ++o) {
+            int64_t m = rows[r];
+            double acc = 0.0;
+            for (int64_t l = 0; l < k; ++l) {
+                const double *xr = x + (l * M + m) * H_in;
+                const double *wr = w + o * (k * H_in) + l * H_in;
+                for (int64_t c = 0; c < H_in; ++c) acc += xr[c] * wr[c];
+            }
+            y[r * H_out + o] = acc;
+        }
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * Tree attention for one query row (b, i, h).
+ *
+ * Visible keys, in this order: prefix positions p = 0 .. P_b-1 of sequence b
+ * (page block_table[b][p / page_size], slot p % page_size), then every tree
+ * node j of sequence b with j in anc(i), in increasing j.
+ * s_t = scale * <q, k_t>;  M = max s_t;  w_t = exp(s_t - M);  Z = sum w_t;
+ * out = sum_t w_t v_t / Z;  lse = M + log Z.
+ * Returns OR_BAD_PAGE if a needed page id is outside [0, num_pages).
+ * ------------------------------------------------------------------------- */
+typedef struct {
+    const double *q, *k_tree, *v_tree, *k_cache, *v_cache;
+    const int32_t *parent, *block_table, *prefix_len;
+    int64_t max_pages, B, N, Hq, Hkv, D, page_size, num_pages;
+    double scale;
+} attn_args;
+
+static int attn_row(const attn_args *a, int64_t b, int64_t i, int64_t h,
+                    double *out, double *lse_out, double *s_buf,
+                    const double **v_buf)
+{
+    const int64_t D = a->D, Hkv = a->Hkv, G = a->Hq / a->Hkv;
+    const int64_t g = h / G;
+    const double *qv = a->q + ((b * a->N + i) * a->Hq + h) * D;
+    const int64_t P = a->prefix_len[b];
+    int64_t nk = 0;
+    for (int64_t p = 0; p < P; ++p) {
+        int64_t page = a->block_table[b * a->max_pages + p / a->page_size];
+        if (page < 0 || page >= a->num_pages) return OR_BAD_PAGE;
+        int64_t slot = p % a->page_size;
+        const double *kv = a->k_cache + ((page * a->page_size + slot) * Hkv + g) * D;
+        double dot = 0.0;
+        for (int64_t d = 0; d < D; ++d) dot += qv[d] * kv[d];
+        s_buf[nk] = a->scale * dot;
+        v_buf[nk] = a->v_cache + ((page * a->page_size + slot) * Hkv + g) * D;
+        nk += 1;
+    }
+    const int32_t *par = a->parent + b * a->N;
+    for (int64_t j = 0; j < a->N; ++j) {
+        if (!is_ancestor(par, a->N, i, j)) continue;
+        const double *kv = a->k_tree + ((b * a->N + j) * Hkv + g) * D;
+        double dot = 0.0;
+        for (int64_t d = 0; d < D; ++d) dot += qv[d] * kv[d];
+        s_buf[nk] = a->scale * dot;
+        v_buf[nk] = a->v_tree + ((b * a->N + j) * Hkv + g) * D;
+        nk += 1;
+    }
+    double M = -INFINITY;
+    for (int64_t t = 0; t < nk; ++t) if (s_buf[t] > M) M = s_buf[t];
+    double Z = 0.0;
+    for (int64_t t = 0; t < nk; ++t) { s_buf[t] = exp(s_buf[t] - M); Z += s_buf[t]; }
+    for (int64_t d = 0; d < D; ++d) {
+        double acc = 0.0;
+        for (int64_t t = 0; t < nk; ++t) acc += s_buf[t] * v_buf[t][d];
+        out[d] = acc / Z;
+    }
+    if (lse_out) *lse_out = M + log(Z);
+    return OR_OK;
+}
+
+/* All rows (rows == NULL: out is [B, N, Hq, D], lse [B, N, Hq]) or a list of
+ * flat row ids r = (b*N + i)*Hq + h (out is [n_rows, D], lse [n_rows]). */
+int oracle_tree_attn(const double *q, const double *k_tree, const double *v_tree,
+                     const int32_t *parent, const double *k_cache,
+                     const double *v_cache, const int32_t *block_table,
+                     int64_t max_pages, const int32_t *prefix_len, int64_t B,
+                     int64_t N, int64_t Hq, int64_t Hkv, int64_t D,
+                     int64_t page_size, int64_t num_pages, double scale,
+                     const int64_t *rows, int64_t n_rows, double *out,
+                     double *lse)
+{
+    if (B < 0 || N <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv != 0 ||
+        page_size <= 0)
+        return OR_INVALID;
+    attn_args a = {q, k_tree, v_tree, k_cache, v_cache, parent, block_table,
+                   prefix_len, max_pages, B, N, Hq, Hkv, D, page_size, num_pages,
+                   scale};
+    int64_t Pmax = 0;
+    for (int64_t b = 0; b < B; ++b) if (prefix_len[b] > Pmax) Pmax = prefix_len[b];
+    const int64_t total = rows ? n_rows : B * N * Hq;
+    int status = OR_OK;
+#pragma omp parallel
+    {
+        double *s_buf = (double *)malloc(sizeof(double) * (size_t)(Pmax + N + 1));
+        const double **v_buf = (const double **)malloc(sizeof(double *) * (size_t)(Pmax + N + 1));
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t r = 0; r < total; ++r) {
+            int64_t flat = rows ? rows[r] : r;
+            int64_t h = flat % Hq, bi = flat / Hq;
+            int64_t i = bi % N, b = bi / N;
+            int st = attn_row(&a, b, i, h, out + r * D, lse ? lse + r : NULL, s_buf, v_buf);
+            if (st != OR_OK) {
+#pragma omp atomic write
+                status = st;
+            }
+        }
+        free(s_buf);
+        free(v_buf);
+    }
+    return status;
+}
+
+/* ---------------------------------------------------------------------------
+ * Per-row top-k of the draft logits and the row log-sum-exp.
+ *
+ * Order: value descending, then index ascending (-0 == +0 as doubles compare;
+ * -inf is an ordinary value; NaN is not a supported input).  Pick t is the
+ * largest element that comes strictly after pick t-1 in that order.
+ * val is the picked value itself; lse = M + log sum exp(x - M), M = row max.
+ * ------------------------------------------------------------------------- */
+void oracle_topk(const double *logits, int64_t R, int64_t V, int64_t k,
+                 int32_t *idx, double *val, double *lse)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < R; ++r) {
+        const double *x = logits + r * V;
+        double prev_v = INFINITY;
+        int64_t prev_i = -1;
+        for (int64_t t = 0; t < k; ++t) {
+            int64_t best = -1;
+            double bv = 0.0;
+            for (int64_t v = 0; v < V; ++v) {
+                double xv = x[v];
+                int after_prev = (t == 0) || (xv < prev_v) || (xv == prev_v && v > prev_i);
+                if (!after_prev) continue;
+                if (best < 0 || xv > bv) { best = v; bv = xv; }
+            }
+            idx[r * k + t] = (int32_t)best;
+            val[r * k + t] = bv;
+            prev_v = bv;
+            prev_i = best;
+        }
+        if (lse) {
+            double M = -INFINITY;
+            for (int64_t v = 0; v < V; ++v) if (x[v] > M) M = x[v];
+            if (M == -INFINITY) {
+                lse[r] = -INFINITY;
+            } else {
+                double Z = 0.0;
+                for (int64_t v = 0; v < V; ++v) Z += exp(x[v] - M);
+                lse[r] = M + log(Z);
+            }
+        }
+    }
+}

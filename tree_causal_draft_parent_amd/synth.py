@@ -1,0 +1,287 @@
+"""Seeded synthetic inputs for the tree-causal draft-head hot path.
+
+This module only draws random numbers and lays them out; it holds none of the
+method's arithmetic (no masks, attention, projection or selection).  Both the
+HIP path and the fp64 oracle take their inputs from here.
+
+Workload shapes follow the draft budgets the pages discuss (16- and 256-token
+trees, "Empirical Results" on the JetFlow blog page; low/high budget in the
+arXiv page's section 1) and the Qwen3-8B / Qwen3-30B-A3B target shapes the
+pages evaluate on.  Value distributions: queries, keys and values ~ N(0, 1);
+projection weights ~ N(0, 0.02); fused hidden inputs ~ N(0, 1); draft logits
+~ N(0, 4), the second argument always being the standard deviation.
+
+bf16 tensors are produced by drawing float32 and rounding to nearest-even, and
+are returned as ``uint16`` bit patterns; ``bf16_bits_to_f32`` widens them
+exactly.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+# ----------------------------------------------------------------------------
+# workload table
+# ----------------------------------------------------------------------------
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    prefix: Sequence[int] | None  # fixed prefix length per sequence (None: ragged)
+    prefix_range: tuple | None    # (lo, hi) inclusive, for ragged prefixes
+    N: int
+    max_depth: int
+    branching: tuple              # (lo, hi) inclusive children per expansion
+    Hq: int
+    Hkv: int
+    D: int
+    dtype: str                    # "f32" or "bf16"
+    H: int                        # hidden size of the fused projection (3H -> H)
+    n_fused: int
+    V: int                        # vocab of the per-node draft logits
+    topk: int
+    page_size: int                # 0: one contiguous region per sequence
+    shuffled_pages: bool
+
+
+WORKLOADS: Dict[int, Workload] = {
+    # tiny fp32 tree, oracle-sized
+    0: Workload("tiny-fp32-p64-n16", 1, (64,), None, 16, 5, (1, 3), 4, 2, 64,
+                "f32", 256, 3, 1000, 4, 0, False),
+    # Qwen3-8B-shaped draft layer, low budget (16 nodes)
+    1: Workload("qwen3-8b-p1024-n16", 1, (1024,), None, 16, 8, (1, 4), 32, 8, 128,
+                "bf16", 4096, 3, 151936, 8, 0, False),
+    # Qwen3-8B-shaped draft layer, high budget (256 nodes)
+    2: Workload("qwen3-8b-p4096-n256", 1, (4096,), None, 256, 16, (1, 8), 32, 8, 128,
+                "bf16", 4096, 3, 151936, 8, 0, False),
+    # serving batch: 32 sequences, ragged prefixes, paged KV in shuffled pages
+    3: Workload("serving-b32-ragged-paged-n64", 32, None, (512, 8192), 64, 16, (1, 8),
+                32, 8, 128, "bf16", 4096, 3, 151936, 8, 16, True),
+    # Qwen3-30B-A3B-shaped draft layer, long prefix
+    4: Workload("qwen3-30b-a3b-b4-p32768-n256", 4, (32768,) * 4, None, 256, 16, (1, 8),
+                32, 4, 128, "bf16", 2048, 3, 151936, 8, 0, False),
+}
+
+
+def workload(i: int) -> Workload:
+    return WORKLOADS[i]
+
+
+# ----------------------------------------------------------------------------
+# bf16 bit handling (round to nearest even; the data never holds NaN)
+# ----------------------------------------------------------------------------
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (nearest, ties to even); return uint16 bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    r = (u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns to float32 exactly."""
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact float64 view of a stored tensor (bf16 bits or float32)."""
+    if dtype == "bf16":
+        return bf16_bits_to_f32(a).astype(np.float64)
+    return np.asarray(a, dtype=np.float32).astype(np.float64)
+
+
+def _draw(rng: np.random.Generator, shape, std: float, dtype: str) -> np.ndarray:
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        x *= np.float32(std)
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x)
+    return x
+
+
+# ----------------------------------------------------------------------------
+# trees
+# ----------------------------------------------------------------------------
+
+
+def best_first_tree(rng: np.random.Generator, N: int, max_depth: int,
+                    branching: tuple) -> np.ndarray:
+    """A parent array of N nodes grown best-first, as a drafter would grow it.
+
+    The prefix end is a virtual root (id -1, path log-probability 0, depth 0).
+    Repeatedly take the frontier entry with the highest path log-probability
+    (ties: lower id, the virtual root ranking lowest-id) and give it c children,
+    c uniform in ``branching``.  The children's conditional probabilities are a
+    seeded softmax sorted in descending order; a child's path log-probability is
+    its parent's plus the log of its own conditional.  Children shallower than
+    ``max_depth`` join the frontier.  If the frontier runs dry, the virtual root
+    is offered again (the result is then a forest of prefix children).  Node ids
+    are creation order, so every parent id is smaller than its child's.
+    """
+    parent = np.full(N, -1, dtype=np.int32)
+    depth = np.zeros(N, dtype=np.int32)
+    score = np.zeros(N, dtype=np.float64)
+    frontier: List[int] = [-1]  # node ids; -1 is the virtual root
+    count = 0
+    lo, hi = branching
+    while count < N:
+        if not frontier:
+            frontier.append(-1)
+
+        def key(nid: int):
+            s = 0.0 if nid < 0 else score[nid]
+            return (-s, nid)
+
+        frontier.sort(key=key)
+        p = frontier.pop(0)
+        c = int(rng.integers(lo, hi + 1))
+        c = min(c, N - count)
+        logits = rng.standard_normal(c) * 2.0
+        prob = np.exp(logits - logits.max())
+        prob = np.sort(prob / prob.sum())[::-1]
+        pd = 0 if p < 0 else depth[p]
+        ps = 0.0 if p < 0 else score[p]
+        for r in range(c):
+            nid = count
+            parent[nid] = p
+            depth[nid] = pd + 1
+            score[nid] = ps + float(np.log(prob[r]))
+            count += 1
+            if depth[nid] < max_depth:
+                frontier.append(nid)
+    return parent
+
+
+def chain_tree(N: int) -> np.ndarray:
+    p = np.arange(-1, N - 1, dtype=np.int32)
+    return p
+
+
+def star_tree(N: int) -> np.ndarray:
+    return np.full(N, -1, dtype=np.int32)
+
+
+# ----------------------------------------------------------------------------
+# full input sets
+# ----------------------------------------------------------------------------
+
+
+def _seeds(seed: int, names: Sequence[str]) -> Dict[str, np.random.Generator]:
+    ss = np.random.SeedSequence(seed)
+    children = ss.spawn(len(names))
+    return {n: np.random.Generator(np.random.PCG64(c)) for n, c in zip(names, children)}
+
+
+_STREAMS = ("tree", "prefix_len", "pages", "q", "k_tree", "v_tree", "k_cache",
+            "v_cache", "x", "w", "logits")
+
+
+def make_attn_inputs(*, B: int, N: int, Hq: int, Hkv: int, D: int, dtype: str,
+                     prefix_lens: Sequence[int], page_size: int = 0,
+                     shuffled_pages: bool = False, parents: Optional[np.ndarray] = None,
+                     max_depth: int = 16, branching: tuple = (1, 8),
+                     seed: int = 1234, extra_pages: int = 0) -> dict:
+    """Inputs of one tree-attention call.
+
+    Prefix K/V live in a page pool ``[num_pages, page_size, Hkv, D]`` addressed
+    through ``block_table[B, max_pages]`` (padding -1).  ``page_size == 0`` asks
+    for the contiguous form: one page per sequence, ``page_size = max(P)``, page
+    id = sequence id.
+    """
+    rng = _seeds(seed, _STREAMS)
+    prefix_lens = np.asarray(prefix_lens, dtype=np.int32)
+    assert prefix_lens.shape == (B,)
+    if parents is None:
+        parents = np.stack([best_first_tree(rng["tree"], N, max_depth, branching)
+                            for _ in range(B)]).astype(np.int32)
+    parents = np.asarray(parents, dtype=np.int32).reshape(B, N)
+    Pmax = int(prefix_lens.max()) if B > 0 else 0
+    if page_size == 0:
+        ps = max(Pmax, 1)
+        max_pages = 1
+        num_pages = B + extra_pages
+        block_table = np.arange(B, dtype=np.int32).reshape(B, 1)
+    else:
+        ps = page_size
+        npg = [(int(p) + ps - 1) // ps for p in prefix_lens]
+        max_pages = max(max(npg) if npg else 0, 1)
+        num_pages = int(sum(npg)) + extra_pages
+        ids = np.arange(num_pages, dtype=np.int32)
+        if shuffled_pages:
+            ids = rng["pages"].permutation(ids).astype(np.int32)
+        block_table = np.full((B, max_pages), -1, dtype=np.int32)
+        off = 0
+        for b in range(B):
+            block_table[b, :npg[b]] = ids[off:off + npg[b]]
+            off += npg[b]
+    q = _draw(rng["q"], (B, N, Hq, D), 1.0, dtype)
+    k_tree = _draw(rng["k_tree"], (B, N, Hkv, D), 1.0, dtype)
+    v_tree = _draw(rng["v_tree"], (B, N, Hkv, D), 1.0, dtype)
+    k_cache = _draw(rng["k_cache"], (num_pages, ps, Hkv, D), 1.0, dtype)
+    v_cache = _draw(rng["v_cache"], (num_pages, ps, Hkv, D), 1.0, dtype)
+    return dict(B=B, N=N, Hq=Hq, Hkv=Hkv, D=D, dtype=dtype, page_size=ps,
+                max_pages=max_pages, num_pages=num_pages, prefix_len=prefix_lens,
+                parent=parents, block_table=block_table, q=q, k_tree=k_tree,
+                v_tree=v_tree, k_cache=k_cache, v_cache=v_cache)
+
+
+def make_fuse_inputs(*, M: int, H_in: int, H_out: int, n_fused: int, dtype: str,
+                     seed: int = 1234, w_std: float = 0.02) -> dict:
+    rng = _seeds(seed, _STREAMS)
+    x = _draw(rng["x"], (n_fused, M, H_in), 1.0, dtype)
+    w = _draw(rng["w"], (H_out, n_fused * H_in), w_std, dtype)
+    return dict(M=M, H_in=H_in, H_out=H_out, n_fused=n_fused, dtype=dtype, x=x, w=w)
+
+
+def make_logits(*, R: int, V: int, dtype: str, seed: int = 1234, std: float = 4.0) -> np.ndarray:
+    rng = _seeds(seed, _STREAMS)
+    return _draw(rng["logits"], (R, V), std, dtype)
+
+
+def tie_forcing_logits(logits_bits: np.ndarray, dtype: str) -> np.ndarray:
+    """Round draft logits to integers so that many values repeat (tie stress)."""
+    x = bf16_bits_to_f32(logits_bits) if dtype == "bf16" else np.asarray(logits_bits, np.float32)
+    x = np.rint(x).astype(np.float32)
+    return f32_to_bf16_bits(x) if dtype == "bf16" else x
+
+
+def config_seed(i: int) -> int:
+    return 1000 + i
+
+
+def prefix_lengths(i: int, seed: Optional[int] = None) -> np.ndarray:
+    w = WORKLOADS[i]
+    if w.prefix is not None:
+        return np.asarray(w.prefix, dtype=np.int32)
+    rng = _seeds(config_seed(i) if seed is None else seed, _STREAMS)["prefix_len"]
+    lo, hi = w.prefix_range
+    return rng.integers(lo, hi + 1, size=w.B).astype(np.int32)
+
+
+def make_workload(i: int, parts=("attn", "fuse", "topk"), seed: Optional[int] = None) -> dict:
+    """All inputs of one draft step for workload ``i``.
+
+    The fused projection runs over one row per tree node (M = B*N); the logits
+    hold one row per tree node as well.
+    """
+    w = WORKLOADS[i]
+    s = config_seed(i) if seed is None else seed
+    out = {"workload": w, "seed": s}
+    if "attn" in parts:
+        out["attn"] = make_attn_inputs(
+            B=w.B, N=w.N, Hq=w.Hq, Hkv=w.Hkv, D=w.D, dtype=w.dtype,
+            prefix_lens=prefix_lengths(i, seed), page_size=w.page_size,
+            shuffled_pages=w.shuffled_pages, max_depth=w.max_depth,
+            branching=w.branching, seed=s)
+    if "fuse" in parts:
+        out["fuse"] = make_fuse_inputs(M=w.B * w.N, H_in=w.H, H_out=w.H,
+                                       n_fused=w.n_fused, dtype=w.dtype, seed=s + 7)
+    if "topk" in parts:
+        out["logits"] = make_logits(R=w.B * w.N, V=w.V, dtype=w.dtype, seed=s + 13)
+    return out
