@@ -1,0 +1,180 @@
+/*
+ * jf.h -- C ABI of the MI355X (gfx950) tree-causal draft-head hot path.
+ *
+ * One forward pass of a causal parallel draft head scores every node of a
+ * candidate token tree at once.  Each node attends to the shared prefix and to
+ * its own ancestors in the tree, never to siblings or descendants (JetFlow
+ * blog page, "What JetFlow Does Differently"), over hidden states fused from
+ * several frozen target-model layers (abstract, on every page).  The per-node
+ * draft distributions multiply along a branch into that branch's probability
+ * (same section), so every node needs its own top candidates and its
+ * normaliser.
+ *
+ * Conventions shared by every call
+ *   - Every tensor pointer is DEVICE memory owned by the caller, unless the
+ *     argument says "host".  The library never allocates, frees or
+ *     synchronises; all work is enqueued on `stream` (a hipStream_t; NULL is
+ *     the default stream) and is asynchronous.
+ *   - Tensors are dense row-major in the stated shape, 16-byte aligned.
+ *   - Argument errors are returned synchronously and launch nothing.  Data
+ *     errors that only the device can see (a parent array that is not a
+ *     forest, a page id out of range) are written to caller-provided device
+ *     words, described per call.
+ *   - Calls are re-entrant: there is no mutable global state beyond a cached
+ *     device-property query.  Concurrent calls need distinct workspaces.
+ *   - bf16 is IEEE binary32 truncated to its upper 16 bits (round to nearest
+ *     even on conversion); accumulation is always fp32.
+ */
+#ifndef JF_H
+#define JF_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    JF_OK = 0,
+    JF_ERR_INVALID_ARG = 1,  /* null pointer, non-positive size, inconsistent dims */
+    JF_ERR_UNSUPPORTED = 2,  /* valid but not implemented (head dim, dtype mix, k) */
+    JF_ERR_ALIGN = 3,        /* pointer or leading dimension not 16-byte aligned */
+    JF_ERR_WORKSPACE = 4,    /* workspace missing or smaller than the size query */
+    JF_ERR_BAD_TREE = 5,     /* device-side only: parent array is not a forest */
+    JF_ERR_BAD_PAGE = 6,     /* device-side only: block-table entry out of range */
+    JF_ERR_HIP = 7           /* the HIP runtime refused a launch */
+} jf_status;
+
+typedef enum { JF_F32 = 0, JF_BF16 = 1 } jf_dtype;
+
+/* Human-readable name of a status code (static storage). */
+const char *jf_status_string(int status);
+
+/* ABI version, bumped on any signature change. */
+int jf_abi_version(void);
+
+/* --------------------------------------------------------------------------
+ * jf_tree_mask_build -- ancestor bitmask of every tree node.
+ *
+ * Realises the visibility rule (a node sees the prefix and its ancestors;
+ * JetFlow blog page, "What JetFlow Does Differently") as data: node i's row
+ * has bit j set iff j is an ancestor of i, the node itself included.
+ * parent[b][i] is the index of node i's parent within sequence b, or -1 when
+ * node i hangs directly off the prefix end (several such roots are allowed).
+ * Node ids need not be in creation order.
+ *
+ *   parent     [B, N] int32.
+ *   mask       [B, N, W] uint64, W = ceil(N / 64): bit (j % 64) of word j / 64
+ *              of row (b, i) <=> j in anc(i).  Bits for j >= N are zero.
+ *   depth      [B, N] int32, |anc(i)| (1 for a prefix child), or NULL.
+ *   seq_status [B] int32 or NULL: -1 when sequence b is a forest, otherwise
+ *              the smallest node index i whose walk to the prefix meets a
+ *              parent outside [-1, N) or does not end within N steps (a
+ *              cycle).  Rows of such nodes are zero and their depth is 0.
+ *              Written on every call.
+ *   B >= 1, 1 <= N <= 4096.
+ * ------------------------------------------------------------------------ */
+jf_status jf_tree_mask_build(const int32_t *parent, int32_t B, int32_t N,
+                             uint64_t *mask, int32_t *depth,
+                             int32_t *seq_status, void *stream);
+
+/* --------------------------------------------------------------------------
+ * jf_fuse_proj -- projection of hidden states fused from several layers.
+ *
+ * The pages train the draft head "over fused hidden states" of the frozen
+ * target (abstract; JetFlow blog page, "What JetFlow Does Differently") but
+ * do not give the fusion operator.  Reading taken here: concatenate the k
+ * layers' states and apply one bias-free linear map,
+ *     y[m, o] = sum_l sum_c x_l[m, c] * w[o, l*H_in + c].
+ *
+ *   x        HOST array of k DEVICE pointers; x[l] is [M, H_in] with row
+ *            stride ldx elements (ldx >= H_in).
+ *   w        [H_out, k*H_in] (row o = weights of output o; torch Linear).
+ *   y        [M, H_out] of out_dtype.
+ *   in_dtype JF_BF16 (MFMA, fp32 accumulation) or JF_F32 (fp32 FMA).
+ *   out_dtype JF_F32 or JF_BF16 (bf16 inputs) / JF_F32 (fp32 inputs).
+ *   1 <= k <= 8; H_in % 64 == 0 for bf16; ldx % 8 == 0 for bf16.
+ *   Alignment: bf16 x and w 16 bytes, y 16 (fp32 out) or 8 (bf16 out);
+ *   fp32 inputs need only 4-byte alignment.
+ *   workspace: jf_fuse_proj_workspace_size() bytes (may be 0 -> NULL ok).
+ * ------------------------------------------------------------------------ */
+size_t jf_fuse_proj_workspace_size(int64_t M, int64_t H_in, int32_t k,
+                                   int64_t H_out, jf_dtype in_dtype);
+jf_status jf_fuse_proj(const void *const *x, int32_t k, int64_t M,
+                       int64_t H_in, int64_t ldx, const void *w, int64_t H_out,
+                       jf_dtype in_dtype, void *y, jf_dtype out_dtype,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/* --------------------------------------------------------------------------
+ * jf_tree_attn_fwd -- tree-causal attention of all draft nodes in one pass.
+ *
+ * For sequence b, tree node i and query head h (KV head g = h / (Hq/Hkv)):
+ * keys are the P_b prefix positions followed by the tree nodes j with
+ * j in anc(i) (JetFlow blog page, "What JetFlow Does Differently";
+ * "block-level causal attention", arxivlens methodology and the arXiv page's
+ * section 1).  s_t = scale * <q, k_t>,
+ *     out = sum_t softmax(s)_t v_t,   lse = log sum_t exp(s_t).
+ *
+ *   q           [B, N, Hq, D]       dtype
+ *   k_tree/v_tree [B, N, Hkv, D]    dtype (the tree nodes' own keys/values)
+ *   mask        [B, N, ceil(N/64)]  from jf_tree_mask_build
+ *   k_cache/v_cache [num_pages, page_size, Hkv, D] dtype: prefix pages.
+ *   block_table [B, max_pages] int32 (device): page of prefix position p of
+ *               sequence b is block_table[b][p / page_size], slot
+ *               p % page_size.  A contiguous prefix is one page per sequence
+ *               (page_size >= max P_b, block_table[b][0] = b).
+ *   prefix_len  HOST [B] int32, P_b >= 0 (0: the nodes see only their path).
+ *   scale       softmax scale; <= 0 selects 1/sqrt(D).
+ *   out         [B, N, Hq, D] dtype;  lse [B, N, Hq] fp32 or NULL.
+ *   page_status one device int32 or NULL: set to JF_ERR_BAD_PAGE when a
+ *               needed block-table entry is outside [0, num_pages) (that
+ *               prefix position then reads as zero keys with zero values);
+ *               never cleared by the library, so zero it once beforehand.
+ *   dtype       JF_BF16: D == 128, MFMA split-KV path;  JF_F32: D <= 128,
+ *               plain fp32 path (small problems).
+ *   Limits: 1 <= B <= 256, 1 <= N <= 1024, Hq % Hkv == 0.
+ *   workspace:  jf_tree_attn_workspace_size() bytes with the same arguments.
+ * ------------------------------------------------------------------------ */
+size_t jf_tree_attn_workspace_size(int32_t B, int32_t N, int32_t Hq,
+                                   int32_t Hkv, int32_t D,
+                                   const int32_t *prefix_len, jf_dtype dtype);
+jf_status jf_tree_attn_fwd(const void *q, const void *k_tree,
+                           const void *v_tree, const uint64_t *mask,
+                           const void *k_cache, const void *v_cache,
+                           int64_t num_pages, int32_t page_size,
+                           const int32_t *block_table, int32_t max_pages,
+                           const int32_t *prefix_len, int32_t B, int32_t N,
+                           int32_t Hq, int32_t Hkv, int32_t D, float scale,
+                           jf_dtype dtype, void *out, float *lse,
+                           void *workspace, size_t workspace_bytes,
+                           int32_t *page_status, void *stream);
+
+/* --------------------------------------------------------------------------
+ * jf_node_topk -- the k best candidates of every node's draft distribution.
+ *
+ * A tree grows by expanding nodes with their most likely next tokens, and a
+ * branch's probability is the product of its per-node conditionals (JetFlow
+ * blog page, "What JetFlow Does Differently"), so each row needs its top-k
+ * logits and its log-normaliser.
+ *
+ *   logits [R, V] dtype with row stride ld (elements; ld >= V, ld % 8 == 0
+ *          for bf16, % 4 == 0 for fp32).  NaN is not a supported value.
+ *   idx    [R, k] int32: indices ordered by value descending, ties by the
+ *          lower index; -0 and +0 are equal.
+ *   val    [R, k] fp32: the selected values.
+ *   lse    [R] fp32 or NULL: log sum_v exp(logits[r, v]).
+ *   1 <= k <= 64, k <= V.
+ *   workspace: jf_node_topk_workspace_size() bytes.
+ * ------------------------------------------------------------------------ */
+size_t jf_node_topk_workspace_size(int64_t R, int64_t V, int32_t k);
+jf_status jf_node_topk(const void *logits, int64_t R, int64_t V, int64_t ld,
+                       jf_dtype dtype, int32_t k, int32_t *idx, float *val,
+                       float *lse, void *workspace, size_t workspace_bytes,
+                       void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* JF_H */

@@ -1,0 +1,121 @@
+"""The C ABI on a machine without a GPU: the library loads, exports every
+function include/jf.h declares, and rejects bad arguments before any HIP call
+(no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from tree_causal_draft_parent_amd import jf
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "jf.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(jf_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert len(names) == 9
+    assert sorted(jf.EXPORTS) == names
+    L = jf.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings_and_version():
+    assert jf.status_string(0) == "JF_OK"
+    assert jf.status_string(5) == "JF_ERR_BAD_TREE"
+    assert jf.lib().jf_abi_version() == 1
+
+
+FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: every call below fails validation
+FAKE_ODD = ctypes.c_void_p(0x10001)
+
+
+def test_mask_argument_errors():
+    L = jf.lib()
+    assert L.jf_tree_mask_build(None, 1, 4, FAKE, None, None, None) == jf.JF_ERR_INVALID_ARG
+    assert L.jf_tree_mask_build(FAKE, 0, 4, FAKE, None, None, None) == jf.JF_ERR_INVALID_ARG
+    assert L.jf_tree_mask_build(FAKE, 1, 0, FAKE, None, None, None) == jf.JF_ERR_INVALID_ARG
+    assert L.jf_tree_mask_build(FAKE, 1, 5000, FAKE, None, None, None) == jf.JF_ERR_INVALID_ARG
+    assert L.jf_tree_mask_build(FAKE, 1, 4, FAKE_ODD, None, None, None) == jf.JF_ERR_ALIGN
+
+
+def _attn(L, **kw):
+    a = dict(q=FAKE, kt=FAKE, vt=FAKE, mask=FAKE, kc=FAKE, vc=FAKE, num_pages=4, page_size=16,
+             bt=FAKE, max_pages=4, pl=np.array([10, 20], np.int32), B=2, N=8, Hq=8, Hkv=2, D=128,
+             scale=0.0, dtype=jf.JF_BF16, out=FAKE, lse=None, ws=None, ws_bytes=0, ps=None)
+    a.update(kw)
+    pl = a["pl"]
+    plp = None if pl is None else pl.ctypes.data_as(ctypes.c_void_p)
+    return L.jf_tree_attn_fwd(a["q"], a["kt"], a["vt"], a["mask"], a["kc"], a["vc"], a["num_pages"],
+                              a["page_size"], a["bt"], a["max_pages"], plp, a["B"], a["N"], a["Hq"],
+                              a["Hkv"], a["D"], a["scale"], a["dtype"], a["out"], a["lse"], a["ws"],
+                              a["ws_bytes"], a["ps"], None)
+
+
+def test_attn_argument_errors():
+    L = jf.lib()
+    assert _attn(L, q=None) == jf.JF_ERR_INVALID_ARG
+    assert _attn(L, pl=None) == jf.JF_ERR_INVALID_ARG
+    assert _attn(L, Hq=6, Hkv=4) == jf.JF_ERR_INVALID_ARG
+    assert _attn(L, D=64) == jf.JF_ERR_UNSUPPORTED
+    assert _attn(L, D=256, dtype=jf.JF_F32) == jf.JF_ERR_UNSUPPORTED
+    assert _attn(L, N=2000) == jf.JF_ERR_UNSUPPORTED
+    assert _attn(L, B=300, pl=np.zeros(300, np.int32)) == jf.JF_ERR_UNSUPPORTED
+    assert _attn(L, pl=np.array([10, -1], np.int32)) == jf.JF_ERR_INVALID_ARG
+    assert _attn(L, pl=np.array([10, 65], np.int32)) == jf.JF_ERR_INVALID_ARG  # > 4 pages of 16
+    assert _attn(L, page_size=0) == jf.JF_ERR_INVALID_ARG
+    assert _attn(L, q=FAKE_ODD) == jf.JF_ERR_ALIGN
+    # this shape splits the keys, so a workspace is required
+    pl = np.array([4096, 4096], np.int32)
+    need = L.jf_tree_attn_workspace_size(2, 256, 32, 8, 128, pl.ctypes.data_as(ctypes.c_void_p), 1)
+    assert need > 0
+    assert _attn(L, pl=pl, N=256, Hq=32, Hkv=8, max_pages=1, page_size=4096,
+                 ws=FAKE, ws_bytes=need - 1) == jf.JF_ERR_WORKSPACE
+
+
+def test_workspace_sizes_are_host_side_and_consistent():
+    L = jf.lib()
+    pl = np.array([4096], np.int32).ctypes.data_as(ctypes.c_void_p)
+    a = L.jf_tree_attn_workspace_size(1, 256, 32, 8, 128, pl, 1)
+    assert a % 4 == 0
+    assert L.jf_tree_attn_workspace_size(1, 256, 32, 8, 128, pl, 0) == 0  # fp32 path: no splits
+    assert L.jf_tree_attn_workspace_size(1, 256, 32, 7, 128, pl, 1) == 0  # invalid -> 0
+    assert L.jf_node_topk_workspace_size(256, 151936, 8) > 0
+    assert L.jf_node_topk_workspace_size(4, 10, 65) == 0
+    assert L.jf_fuse_proj_workspace_size(256, 4096, 3, 4096, 1) >= 0
+    assert L.jf_fuse_proj_workspace_size(256, 100, 3, 4096, 1) == 0  # H_in % 64 != 0
+
+
+def test_fuse_and_topk_argument_errors():
+    L = jf.lib()
+    xs = (ctypes.c_void_p * 3)(0x10000, 0x20000, 0x30000)
+    assert L.jf_fuse_proj(None, 3, 16, 256, 256, FAKE, 256, 1, FAKE, 0, None, 0, None) == jf.JF_ERR_INVALID_ARG
+    assert L.jf_fuse_proj(xs, 0, 16, 256, 256, FAKE, 256, 1, FAKE, 0, None, 0, None) == jf.JF_ERR_INVALID_ARG
+    assert L.jf_fuse_proj(xs, 3, 16, 100, 128, FAKE, 256, 1, FAKE, 0, None, 0, None) == jf.JF_ERR_UNSUPPORTED
+    assert L.jf_fuse_proj(xs, 3, 16, 256, 200, FAKE, 256, 1, FAKE, 0, None, 0, None) == jf.JF_ERR_INVALID_ARG
+    assert L.jf_fuse_proj(xs, 3, 16, 256, 260, FAKE, 256, 1, FAKE, 0, None, 0, None) == jf.JF_ERR_ALIGN
+    assert L.jf_fuse_proj(xs, 3, 16, 256, 256, FAKE, 256, 0, FAKE, 1, None, 0, None) == jf.JF_ERR_UNSUPPORTED
+    assert L.jf_node_topk(None, 4, 100, 100, 1, 4, FAKE, FAKE, None, FAKE, 1 << 20, None) == jf.JF_ERR_INVALID_ARG
+    assert L.jf_node_topk(FAKE, 4, 100, 99, 1, 4, FAKE, FAKE, None, FAKE, 1 << 20, None) == jf.JF_ERR_INVALID_ARG
+    assert L.jf_node_topk(FAKE, 4, 100, 100, 1, 65, FAKE, FAKE, None, FAKE, 1 << 20, None) == jf.JF_ERR_UNSUPPORTED
+    assert L.jf_node_topk(FAKE, 4, 100, 100, 1, 101, FAKE, FAKE, None, FAKE, 1 << 20, None) == jf.JF_ERR_UNSUPPORTED
+    assert L.jf_node_topk(FAKE, 4, 100, 100, 1, 4, FAKE, FAKE, None, FAKE, 1 << 20, None) == jf.JF_ERR_ALIGN
+    assert L.jf_node_topk(FAKE, 4, 104, 104, 1, 4, FAKE, FAKE, None, None, 0, None) == jf.JF_ERR_WORKSPACE
+
+
+def test_product_path_does_not_import_the_oracle():
+    pkg = os.path.join(ROOT, "tree_causal_draft_parent_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in src and "from oracle" not in src, f
+                assert "liboracle" not in src, f

@@ -1,0 +1,76 @@
+"""jf_fuse_proj vs the oracle (fp32 inputs: max-abs <= 1e-5; bf16 inputs with
+fp32 accumulation: max-abs <= 2e-2 and rel-RMS <= 1e-2; bf16 outputs may also
+differ from the exact value by the output's own rounding, one bf16 ulp)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import dev_tensor, host_f64, say
+from helpers import rel_rms
+from tree_causal_draft_parent_amd import jf, synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(inp, out_dtype=torch.float32, ldx=None, rows=None):
+    dt = inp["dtype"]
+    k, M, H_in = inp["x"].shape
+    say(f"fuse: k={k} M={M} H_in={H_in} H_out={inp['w'].shape[0]} dtype={dt} out={out_dtype} ldx={ldx}")
+    if ldx is not None:
+        pad = np.zeros((k, M, ldx), dtype=inp["x"].dtype)
+        pad[:, :, :H_in] = inp["x"]
+        xt = dev_tensor(pad, dt)
+        xs = [xt[l, :, :H_in] for l in range(k)]
+    else:
+        xt = dev_tensor(inp["x"], dt)
+        xs = [xt[l] for l in range(k)]
+    y = jf.jf_fuse_proj(xs, dev_tensor(inp["w"], dt), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    got = host_f64(y)
+    ref = oracle.fuse_proj(synth.to_f64(inp["x"], dt), synth.to_f64(inp["w"], dt), rows=rows)
+    if rows is not None:
+        got = got[rows]
+    if dt == "f32":
+        assert np.max(np.abs(got - ref)) <= 1e-5
+    else:
+        err = np.abs(got - ref)
+        if out_dtype == torch.bfloat16:
+            ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 7)
+            assert np.all(err <= np.maximum(2e-2, ulp))
+        else:
+            assert err.max() <= 2e-2, err.max()
+        assert rel_rms(got, ref) <= 1e-2
+
+
+def test_tiny_fp32_workload():
+    _run(synth.make_workload(0, parts=("fuse",))["fuse"])
+
+
+@pytest.mark.parametrize("M,H_in,H_out", [(1, 64, 1), (200, 192, 130), (129, 128, 257)])
+def test_bf16_ragged_tiles(M, H_in, H_out):
+    _run(synth.make_fuse_inputs(M=M, H_in=H_in, H_out=H_out, n_fused=3, dtype="bf16", seed=M))
+
+
+def test_bf16_out_and_strided_rows():
+    inp = synth.make_fuse_inputs(M=70, H_in=256, H_out=300, n_fused=3, dtype="bf16", seed=2)
+    _run(inp, out_dtype=torch.bfloat16)
+    _run(inp, ldx=264)
+
+
+def test_fp32_ragged():
+    _run(synth.make_fuse_inputs(M=33, H_in=50, H_out=17, n_fused=2, dtype="f32", seed=4))
+
+
+def test_qwen3_8b_low_budget_full():
+    _run(synth.make_workload(1, parts=("fuse",))["fuse"])
+
+
+def test_qwen3_8b_high_budget_sampled_rows():
+    rows = np.sort(np.random.default_rng(2).choice(256, 32, replace=False))
+    _run(synth.make_workload(2, parts=("fuse",))["fuse"], rows=rows)
+
+
+def test_qwen3_30b_shape_sampled_rows():
+    rows = np.sort(np.random.default_rng(4).choice(1024, 32, replace=False))
+    _run(synth.make_workload(4, parts=("fuse",))["fuse"], rows=rows)

@@ -1,0 +1,82 @@
+"""jf_node_topk vs the oracle: bit-exact indices and values, lse within the
+fp32 / bf16 tolerances."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import dev_tensor, say
+from tree_causal_draft_parent_amd import jf, synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(bits, dtype, k, ld=None, rows=None):
+    R, V = bits.shape
+    x = synth.to_f64(bits, dtype)
+    say(f"topk: R={R} V={V} k={k} dtype={dtype} ld={ld}")
+    if ld is not None and ld != V:
+        pad = np.zeros((R, ld), dtype=bits.dtype)
+        pad[:, :V] = bits
+        t = dev_tensor(pad, dtype)[:, :V]
+    else:
+        t = dev_tensor(bits, dtype)
+    idx, val, lse = jf.jf_node_topk(t, k)
+    torch.cuda.synchronize()
+    idx, val, lse = idx.cpu().numpy(), val.cpu().numpy(), lse.cpu().numpy()
+    sel = np.arange(R) if rows is None else rows
+    oi, ov, ol = oracle.topk(x[sel], k)
+    assert np.array_equal(idx[sel], oi)
+    assert np.array_equal(val[sel].astype(np.float64), ov)
+    fin = np.isfinite(ol)
+    assert np.array_equal(np.isfinite(lse[sel]), fin)
+    # lse is fp32 arithmetic over exactly widened inputs for both dtypes; the
+    # stated bounds are 1e-5 (fp32 path) and 2e-2 (bf16 path) max-abs.
+    tol = 1e-5 if dtype == "f32" else 2e-2
+    assert np.max(np.abs(lse[sel][fin] - ol[fin]), initial=0.0) <= tol
+
+
+def test_tiny_fp32_workload():
+    w = synth.workload(0)
+    _check(synth.make_logits(R=w.B * w.N, V=w.V, dtype="f32", seed=1013), "f32", w.topk)
+
+
+@pytest.mark.parametrize("k", [1, 8, 64])
+def test_bf16_vocab_rows(k):
+    _check(synth.make_logits(R=16, V=151936, dtype="bf16", seed=k), "bf16", k)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_tie_forcing_rows(dtype):
+    bits = synth.tie_forcing_logits(synth.make_logits(R=8, V=20000, dtype=dtype, seed=5), dtype)
+    _check(bits, dtype, 8)
+    _check(bits, dtype, 64)
+
+
+@pytest.mark.parametrize("V,ld", [(1, 8), (7, 8), (1001, 1008), (4099, 4104), (513, 520)])
+def test_ragged_vocab_and_stride(V, ld):
+    bits = synth.make_logits(R=5, V=V, dtype="bf16", seed=V)
+    _check(bits, "bf16", min(8, V), ld=ld)
+
+
+def test_special_values():
+    x = np.full((4, 3000), -np.inf, dtype=np.float32)
+    x[1] = 2.5                             # all equal
+    x[2, ::7] = 0.0
+    x[2, 3::7] = -0.0                      # signed zeros, equal
+    x[3, 100] = 1.0                        # one finite value among -inf
+    _check(x, "f32", 8)
+    _check(synth.f32_to_bf16_bits(x), "bf16", 8)
+
+
+def test_qwen3_8b_high_budget_rows_full_size():
+    w = synth.workload(2)
+    bits = synth.make_logits(R=w.B * w.N, V=w.V, dtype="bf16", seed=1015)
+    _check(bits, "bf16", w.topk)
+
+
+def test_qwen3_30b_rows_full_size_sampled():
+    w = synth.workload(4)
+    bits = synth.make_logits(R=w.B * w.N, V=w.V, dtype="bf16", seed=1017)
+    rows = np.random.default_rng(0).choice(w.B * w.N, size=96, replace=False)
+    _check(bits, "bf16", w.topk, rows=np.sort(rows))

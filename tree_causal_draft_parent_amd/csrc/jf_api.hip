@@ -1,0 +1,195 @@
+// jf_api.hip -- the extern "C" entry points of libjf: argument validation,
+// planning and launches on the caller's stream.  Nothing here allocates or
+// synchronises.  Every argument error returns before any HIP call, so the
+// checks work on a machine without a GPU.
+#include <math.h>
+#include <string.h>
+
+#include "jf_internal.h"
+
+namespace jf {
+
+int num_cus() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+static inline bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+}  // namespace jf
+
+using namespace jf;
+
+extern "C" {
+
+const char *jf_status_string(int status) {
+    switch (status) {
+        case JF_OK: return "JF_OK";
+        case JF_ERR_INVALID_ARG: return "JF_ERR_INVALID_ARG";
+        case JF_ERR_UNSUPPORTED: return "JF_ERR_UNSUPPORTED";
+        case JF_ERR_ALIGN: return "JF_ERR_ALIGN";
+        case JF_ERR_WORKSPACE: return "JF_ERR_WORKSPACE";
+        case JF_ERR_BAD_TREE: return "JF_ERR_BAD_TREE";
+        case JF_ERR_BAD_PAGE: return "JF_ERR_BAD_PAGE";
+        case JF_ERR_HIP: return "JF_ERR_HIP";
+        default: return "JF_ERR_UNKNOWN";
+    }
+}
+
+int jf_abi_version(void) { return 1; }
+
+jf_status jf_tree_mask_build(const int32_t *parent, int32_t B, int32_t N, uint64_t *mask,
+                             int32_t *depth, int32_t *seq_status, void *stream) {
+    if (!parent || !mask) return JF_ERR_INVALID_ARG;
+    if (B < 1 || N < 1 || N > 4096) return JF_ERR_INVALID_ARG;
+    if (!aligned(parent, 4) || !aligned(mask, 8) || (depth && !aligned(depth, 4)) ||
+        (seq_status && !aligned(seq_status, 4)))
+        return JF_ERR_ALIGN;
+    hipError_t e = launch_tree_mask(parent, B, N, mask, depth, seq_status, (hipStream_t)stream);
+    return e == hipSuccess ? JF_OK : JF_ERR_HIP;
+}
+
+// ---------------------------------------------------------------------------
+static jf_status check_fuse(int32_t k, int64_t M, int64_t H_in, int64_t ldx, int64_t H_out,
+                            jf_dtype in_dtype) {
+    if (k < 1 || k > 8 || M < 1 || H_in < 1 || H_out < 1 || ldx < H_in) return JF_ERR_INVALID_ARG;
+    if (in_dtype != JF_BF16 && in_dtype != JF_F32) return JF_ERR_INVALID_ARG;
+    if (in_dtype == JF_BF16 && H_in % 64 != 0) return JF_ERR_UNSUPPORTED;
+    if (M > (int64_t)1 << 30 || H_out > (int64_t)1 << 30) return JF_ERR_UNSUPPORTED;
+    return JF_OK;
+}
+
+size_t jf_fuse_proj_workspace_size(int64_t M, int64_t H_in, int32_t k, int64_t H_out,
+                                   jf_dtype in_dtype) {
+    if (check_fuse(k, M, H_in, H_in, H_out, in_dtype) != JF_OK) return 0;
+    FusePlan p;
+    plan_fuse(p, M, H_in, k, H_out, in_dtype);
+    return fuse_workspace_bytes(p);
+}
+
+jf_status jf_fuse_proj(const void *const *x, int32_t k, int64_t M, int64_t H_in, int64_t ldx,
+                       const void *w, int64_t H_out, jf_dtype in_dtype, void *y,
+                       jf_dtype out_dtype, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!x || !w || !y) return JF_ERR_INVALID_ARG;
+    jf_status st = check_fuse(k, M, H_in, ldx, H_out, in_dtype);
+    if (st != JF_OK) return st;
+    for (int l = 0; l < k; ++l)
+        if (!x[l]) return JF_ERR_INVALID_ARG;
+    if (out_dtype != JF_F32 && out_dtype != JF_BF16) return JF_ERR_INVALID_ARG;
+    if (in_dtype == JF_F32 && out_dtype != JF_F32) return JF_ERR_UNSUPPORTED;
+    // bf16 operands are read as 16-byte vectors; the fp32 path reads scalars.
+    const size_t a = in_dtype == JF_BF16 ? 16 : 4;
+    for (int l = 0; l < k; ++l)
+        if (!aligned(x[l], a)) return JF_ERR_ALIGN;
+    if (!aligned(w, a) || !aligned(y, in_dtype == JF_BF16 ? (out_dtype == JF_BF16 ? 8 : 16) : 4))
+        return JF_ERR_ALIGN;
+    if (in_dtype == JF_BF16 && ldx % 8 != 0) return JF_ERR_ALIGN;
+    FusePlan p;
+    plan_fuse(p, M, H_in, k, H_out, in_dtype);
+    const size_t need = fuse_workspace_bytes(p);
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
+        return JF_ERR_WORKSPACE;
+    hipError_t e = in_dtype == JF_BF16
+                       ? launch_fuse_bf16(p, x, ldx, w, y, out_dtype, workspace, (hipStream_t)stream)
+                       : launch_fuse_f32(p, x, ldx, w, (float *)y, (hipStream_t)stream);
+    return e == hipSuccess ? JF_OK : JF_ERR_HIP;
+}
+
+// ---------------------------------------------------------------------------
+static jf_status check_attn_dims(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
+                                 const int32_t *prefix_len, jf_dtype dtype) {
+    if (!prefix_len) return JF_ERR_INVALID_ARG;
+    if (B < 1 || N < 1 || Hq < 1 || Hkv < 1 || D < 1) return JF_ERR_INVALID_ARG;
+    if (Hq % Hkv != 0) return JF_ERR_INVALID_ARG;
+    if (dtype != JF_BF16 && dtype != JF_F32) return JF_ERR_INVALID_ARG;
+    if (B > kMaxBatch || N > 1024) return JF_ERR_UNSUPPORTED;
+    if (dtype == JF_BF16 && D != 128) return JF_ERR_UNSUPPORTED;
+    if (dtype == JF_F32 && D > 128) return JF_ERR_UNSUPPORTED;
+    for (int b = 0; b < B; ++b)
+        if (prefix_len[b] < 0) return JF_ERR_INVALID_ARG;
+    return JF_OK;
+}
+
+size_t jf_tree_attn_workspace_size(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
+                                   const int32_t *prefix_len, jf_dtype dtype) {
+    if (check_attn_dims(B, N, Hq, Hkv, D, prefix_len, dtype) != JF_OK) return 0;
+    if (dtype == JF_F32) return 0;
+    AttnPlan p;
+    plan_tree_attn(p, B, N, Hq, Hkv, D, prefix_len, dtype);
+    return tree_attn_workspace_bytes(p);
+}
+
+jf_status jf_tree_attn_fwd(const void *q, const void *k_tree, const void *v_tree,
+                           const uint64_t *mask, const void *k_cache, const void *v_cache,
+                           int64_t num_pages, int32_t page_size, const int32_t *block_table,
+                           int32_t max_pages, const int32_t *prefix_len, int32_t B, int32_t N,
+                           int32_t Hq, int32_t Hkv, int32_t D, float scale, jf_dtype dtype,
+                           void *out, float *lse, void *workspace, size_t workspace_bytes,
+                           int32_t *page_status, void *stream) {
+    if (!q || !k_tree || !v_tree || !mask || !k_cache || !v_cache || !block_table || !out)
+        return JF_ERR_INVALID_ARG;
+    jf_status st = check_attn_dims(B, N, Hq, Hkv, D, prefix_len, dtype);
+    if (st != JF_OK) return st;
+    if (page_size < 1 || max_pages < 1 || num_pages < 0) return JF_ERR_INVALID_ARG;
+    for (int b = 0; b < B; ++b)
+        if ((int64_t)prefix_len[b] > (int64_t)max_pages * page_size) return JF_ERR_INVALID_ARG;
+    const size_t al = 16;
+    if (!aligned(q, al) || !aligned(k_tree, al) || !aligned(v_tree, al) || !aligned(k_cache, al) ||
+        !aligned(v_cache, al) || !aligned(out, al) || !aligned(mask, 8) || !aligned(block_table, 4) ||
+        (lse && !aligned(lse, 4)) || (page_status && !aligned(page_status, 4)))
+        return JF_ERR_ALIGN;
+    if (!(scale > 0.f)) scale = 1.f / sqrtf((float)D);
+    AttnPlan p;
+    plan_tree_attn(p, B, N, Hq, Hkv, D, prefix_len, dtype);
+    hipError_t e;
+    if (dtype == JF_BF16) {
+        const size_t need = tree_attn_workspace_bytes(p);
+        if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
+            return JF_ERR_WORKSPACE;
+        e = launch_tree_attn_bf16(p, q, k_tree, v_tree, mask, k_cache, v_cache, num_pages, page_size,
+                                  block_table, max_pages, scale, out, lse, workspace, page_status,
+                                  (hipStream_t)stream);
+    } else {
+        e = launch_tree_attn_f32(p, (const float *)q, (const float *)k_tree, (const float *)v_tree,
+                                 mask, (const float *)k_cache, (const float *)v_cache, num_pages,
+                                 page_size, block_table, max_pages, scale, (float *)out, lse,
+                                 page_status, (hipStream_t)stream);
+    }
+    return e == hipSuccess ? JF_OK : JF_ERR_HIP;
+}
+
+// ---------------------------------------------------------------------------
+size_t jf_node_topk_workspace_size(int64_t R, int64_t V, int32_t k) {
+    if (R < 1 || V < 1 || k < 1 || k > 64 || k > V || V > INT32_MAX) return 0;
+    TopkPlan p;
+    plan_topk(p, R, V, k);
+    return topk_workspace_bytes(p);
+}
+
+jf_status jf_node_topk(const void *logits, int64_t R, int64_t V, int64_t ld, jf_dtype dtype,
+                       int32_t k, int32_t *idx, float *val, float *lse, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+    if (!logits || !idx || !val) return JF_ERR_INVALID_ARG;
+    if (R < 1 || V < 1 || ld < V || k < 1) return JF_ERR_INVALID_ARG;
+    if (dtype != JF_BF16 && dtype != JF_F32) return JF_ERR_INVALID_ARG;
+    if (k > 64 || k > V || V > INT32_MAX) return JF_ERR_UNSUPPORTED;
+    if (R > (int64_t)1 << 30) return JF_ERR_UNSUPPORTED;
+    if (!aligned(logits, 16) || ld % (dtype == JF_BF16 ? 8 : 4) != 0) return JF_ERR_ALIGN;
+    if (!aligned(idx, 4) || !aligned(val, 4) || (lse && !aligned(lse, 4))) return JF_ERR_ALIGN;
+    TopkPlan p;
+    plan_topk(p, R, V, k);
+    const size_t need = topk_workspace_bytes(p);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return JF_ERR_WORKSPACE;
+    hipError_t e = launch_topk(p, logits, ld, dtype, idx, val, lse, workspace, (hipStream_t)stream);
+    return e == hipSuccess ? JF_OK : JF_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,110 @@
+// jf_internal.h -- shared device types and launcher declarations of libjf.
+// gfx950 only: wave64, MFMA bf16 32x32x16, 160 KiB LDS per CU, 8 XCDs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/jf.h"
+
+namespace jf {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kNumXcd = 8;
+
+// bf16 bits -> fp32 (exact)
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs)
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// Consecutive workgroup ids are spread round-robin over the XCDs.  Map the
+// hardware id so that the workgroups landing on one XCD get one contiguous
+// range of logical ids: neighbours in logical order then share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int bid, int n) {
+    int xcd = bid % kNumXcd, local = bid / kNumXcd;
+    int q = n / kNumXcd, rem = n % kNumXcd;
+    return xcd * q + (xcd < rem ? xcd : rem) + local;
+}
+
+// Device properties cached once per process and device.
+int num_cus();
+
+// ----- launchers (host) ------------------------------------------------------
+hipError_t launch_tree_mask(const int32_t *parent, int B, int N, uint64_t *mask,
+                            int32_t *depth, int32_t *seq_status, hipStream_t s);
+
+constexpr int kMaxBatch = 256;
+
+struct AttnPlan {
+    int B, N, Hq, Hkv, D, G, R, W;
+    int n_qt;            // query tiles per (sequence, kv head)
+    int tq;              // query rows per tile
+    int chunk_blocks;    // 64-key blocks per split
+    int n_tree_blocks;   // ceil(N / 64)
+    int total_chunks;    // sum over sequences of splits
+    int total_items;     // workgroups of the split kernel
+    bool any_split;      // some sequence has more than one split
+    int prefix_len[kMaxBatch];
+    int chunk_start[kMaxBatch + 1];
+};
+void plan_tree_attn(AttnPlan &p, int B, int N, int Hq, int Hkv, int D,
+                    const int32_t *prefix_len, jf_dtype dtype);
+size_t tree_attn_workspace_bytes(const AttnPlan &p);
+
+hipError_t launch_tree_attn_bf16(const AttnPlan &p, const void *q, const void *k_tree,
+                                 const void *v_tree, const uint64_t *mask,
+                                 const void *k_cache, const void *v_cache,
+                                 int64_t num_pages, int page_size,
+                                 const int32_t *block_table, int max_pages, float scale,
+                                 void *out, float *lse, void *workspace,
+                                 int32_t *page_status, hipStream_t s);
+hipError_t launch_tree_attn_f32(const AttnPlan &p, const float *q, const float *k_tree,
+                                const float *v_tree, const uint64_t *mask,
+                                const float *k_cache, const float *v_cache,
+                                int64_t num_pages, int page_size,
+                                const int32_t *block_table, int max_pages, float scale,
+                                float *out, float *lse, int32_t *page_status,
+                                hipStream_t s);
+
+struct TopkPlan {
+    int64_t R, V;
+    int k;
+    int chunks;        // splits of each row
+    int64_t chunk_len; // elements per split (multiple of 512)
+};
+void plan_topk(TopkPlan &p, int64_t R, int64_t V, int k);
+size_t topk_workspace_bytes(const TopkPlan &p);
+hipError_t launch_topk(const TopkPlan &p, const void *logits, int64_t ld, jf_dtype dtype,
+                       int32_t *idx, float *val, float *lse, void *workspace, hipStream_t s);
+
+struct FusePlan {
+    int64_t M, H_in, H_out;
+    int k;
+    int bm, bn;        // output tile
+    int split_k;       // K slices (>1 uses the fp32 partial workspace)
+    int64_t k_per_split;
+};
+void plan_fuse(FusePlan &p, int64_t M, int64_t H_in, int k, int64_t H_out, jf_dtype in_dtype);
+size_t fuse_workspace_bytes(const FusePlan &p);
+hipError_t launch_fuse_bf16(const FusePlan &p, const void *const *x, int64_t ldx,
+                            const void *w, void *y, jf_dtype out_dtype, void *workspace,
+                            hipStream_t s);
+hipError_t launch_fuse_f32(const FusePlan &p, const void *const *x, int64_t ldx,
+                           const void *w, float *y, hipStream_t s);
+
+}  // namespace jf

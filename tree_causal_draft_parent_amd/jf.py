@@ -1,0 +1,228 @@
+"""Python binding of libjf (include/jf.h): argument marshalling only.
+
+Each function has the C entry point's name, takes torch tensors that live on
+the GPU, passes their device pointers and sizes to the C ABI, and raises
+``JfError`` on a non-OK status.  Outputs and workspaces that the caller does
+not pass are allocated with torch (PyTorch is the memory and stream provider);
+every step of the computation runs in the HIP kernels of libjf.  There is no
+fallback: if libjf.so is missing, loading fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libjf.so")
+
+JF_OK, JF_ERR_INVALID_ARG, JF_ERR_UNSUPPORTED, JF_ERR_ALIGN = 0, 1, 2, 3
+JF_ERR_WORKSPACE, JF_ERR_BAD_TREE, JF_ERR_BAD_PAGE, JF_ERR_HIP = 4, 5, 6, 7
+JF_F32, JF_BF16 = 0, 1
+
+EXPORTS = ("jf_status_string", "jf_abi_version", "jf_tree_mask_build",
+           "jf_fuse_proj_workspace_size", "jf_fuse_proj", "jf_tree_attn_workspace_size",
+           "jf_tree_attn_fwd", "jf_node_topk_workspace_size", "jf_node_topk")
+
+_lib = None
+
+
+class JfError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {status_string(status)}")
+
+
+def lib():
+    """Load libjf.so (built by tree_causal_draft_parent_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m tree_causal_draft_parent_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    L.jf_status_string.argtypes = [ctypes.c_int]
+    L.jf_status_string.restype = ctypes.c_char_p
+    L.jf_abi_version.argtypes = []
+    L.jf_abi_version.restype = ctypes.c_int
+    L.jf_tree_mask_build.argtypes = [P, I32, I32, P, P, P, P]
+    L.jf_tree_mask_build.restype = ctypes.c_int
+    L.jf_fuse_proj_workspace_size.argtypes = [I64, I64, I32, I64, ctypes.c_int]
+    L.jf_fuse_proj_workspace_size.restype = SZ
+    L.jf_fuse_proj.argtypes = [P, I32, I64, I64, I64, P, I64, ctypes.c_int, P, ctypes.c_int,
+                               P, SZ, P]
+    L.jf_fuse_proj.restype = ctypes.c_int
+    L.jf_tree_attn_workspace_size.argtypes = [I32, I32, I32, I32, I32, P, ctypes.c_int]
+    L.jf_tree_attn_workspace_size.restype = SZ
+    L.jf_tree_attn_fwd.argtypes = [P, P, P, P, P, P, I64, I32, P, I32, P, I32, I32, I32, I32, I32,
+                                   ctypes.c_float, ctypes.c_int, P, P, P, SZ, P, P]
+    L.jf_tree_attn_fwd.restype = ctypes.c_int
+    L.jf_node_topk_workspace_size.argtypes = [I64, I64, I32]
+    L.jf_node_topk_workspace_size.restype = SZ
+    L.jf_node_topk.argtypes = [P, I64, I64, I64, ctypes.c_int, I32, P, P, P, P, SZ, P]
+    L.jf_node_topk.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().jf_status_string(int(status)).decode()
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return JF_BF16
+    if t.dtype == torch.float32:
+        return JF_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _check(fn: str, st: int):
+    if st != JF_OK:
+        raise JfError(fn, st)
+
+
+def _contig(name: str, t: torch.Tensor):
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# ---------------------------------------------------------------------------
+def jf_tree_mask_build(parent: torch.Tensor, mask: Optional[torch.Tensor] = None,
+                       depth: Optional[torch.Tensor] = None,
+                       seq_status: Optional[torch.Tensor] = None, stream=None):
+    """parent [B, N] int32 -> (mask [B, N, ceil(N/64)] uint64 (as int64), depth [B, N],
+    seq_status [B]) on the parent's device."""
+    _contig("parent", parent)
+    B, N = parent.shape
+    W = (N + 63) // 64
+    dev = parent.device
+    if mask is None:
+        mask = torch.empty((B, N, W), dtype=torch.int64, device=dev)
+    if depth is None:
+        depth = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if seq_status is None:
+        seq_status = torch.empty((B,), dtype=torch.int32, device=dev)
+    st = lib().jf_tree_mask_build(_p(parent), B, N, _p(mask), _p(depth), _p(seq_status),
+                                  _stream(stream))
+    _check("jf_tree_mask_build", st)
+    return mask, depth, seq_status
+
+
+def jf_fuse_proj_workspace_size(M: int, H_in: int, k: int, H_out: int, in_dtype: int) -> int:
+    return int(lib().jf_fuse_proj_workspace_size(M, H_in, k, H_out, in_dtype))
+
+
+def jf_fuse_proj(xs: Sequence[torch.Tensor], w: torch.Tensor, out_dtype=torch.float32,
+                 y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                 stream=None):
+    """y[m, o] = sum_l xs[l][m, :] . w[o, l*H_in:(l+1)*H_in]  (xs[l]: [M, H_in], rows may be
+    strided; w: [H_out, k*H_in])."""
+    k = len(xs)
+    M, H_in = xs[0].shape
+    ldx = xs[0].stride(0)
+    for x in xs:
+        if x.shape != (M, H_in) or x.stride(1) != 1 or x.stride(0) != ldx or x.dtype != xs[0].dtype:
+            raise ValueError("fused inputs must share shape, dtype and row stride")
+    _contig("w", w)
+    H_out = w.shape[0]
+    in_code = _dtype_code(xs[0])
+    if y is None:
+        y = torch.empty((M, H_out), dtype=out_dtype, device=w.device)
+    out_code = _dtype_code(y)
+    need = jf_fuse_proj_workspace_size(M, H_in, k, H_out, in_code)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=w.device)
+    arr = (ctypes.c_void_p * k)(*[x.data_ptr() for x in xs])
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().jf_fuse_proj(arr, k, M, H_in, ldx, _p(w), H_out, in_code, _p(y), out_code,
+                            _p(workspace), ws_bytes, _stream(stream))
+    _check("jf_fuse_proj", st)
+    return y
+
+
+def _host_i32(a) -> np.ndarray:
+    if isinstance(a, torch.Tensor):
+        a = a.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def jf_tree_attn_workspace_size(B: int, N: int, Hq: int, Hkv: int, D: int, prefix_len,
+                                dtype: int) -> int:
+    pl = _host_i32(prefix_len)
+    return int(lib().jf_tree_attn_workspace_size(B, N, Hq, Hkv, D,
+                                                 pl.ctypes.data_as(ctypes.c_void_p), dtype))
+
+
+def jf_tree_attn_fwd(q, k_tree, v_tree, mask, k_cache, v_cache, block_table, prefix_len,
+                     scale: float = 0.0, out=None, lse=None, with_lse: bool = True,
+                     workspace=None, page_status=None, stream=None):
+    """Tree attention.  q [B,N,Hq,D]; k_tree/v_tree [B,N,Hkv,D]; mask from
+    jf_tree_mask_build; k_cache/v_cache [num_pages, page_size, Hkv, D];
+    block_table [B, max_pages] int32 (device); prefix_len host ints [B]."""
+    for n, t in (("q", q), ("k_tree", k_tree), ("v_tree", v_tree), ("mask", mask),
+                 ("k_cache", k_cache), ("v_cache", v_cache), ("block_table", block_table)):
+        _contig(n, t)
+    B, N, Hq, D = q.shape
+    Hkv = k_tree.shape[2]
+    num_pages, page_size = k_cache.shape[0], k_cache.shape[1]
+    max_pages = block_table.shape[1]
+    dt = _dtype_code(q)
+    pl = _host_i32(prefix_len)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and with_lse:
+        lse = torch.empty((B, N, Hq), dtype=torch.float32, device=q.device)
+    need = jf_tree_attn_workspace_size(B, N, Hq, Hkv, D, pl, dt)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().jf_tree_attn_fwd(_p(q), _p(k_tree), _p(v_tree), _p(mask), _p(k_cache), _p(v_cache),
+                                num_pages, page_size, _p(block_table), max_pages,
+                                pl.ctypes.data_as(ctypes.c_void_p), B, N, Hq, Hkv, D,
+                                float(scale), dt, _p(out), _p(lse), _p(workspace), ws_bytes,
+                                _p(page_status), _stream(stream))
+    _check("jf_tree_attn_fwd", st)
+    return out, lse
+
+
+def jf_node_topk_workspace_size(R: int, V: int, k: int) -> int:
+    return int(lib().jf_node_topk_workspace_size(R, V, k))
+
+
+def jf_node_topk(logits: torch.Tensor, k: int, with_lse: bool = True, idx=None, val=None,
+                 lse=None, workspace=None, stream=None):
+    """logits [R, V] (row stride may exceed V) -> idx [R, k] int32, val [R, k] fp32, lse [R]."""
+    if logits.stride(1) != 1:
+        raise ValueError("logits rows must be contiguous")
+    R, V = logits.shape
+    ld = logits.stride(0)
+    dev = logits.device
+    if idx is None:
+        idx = torch.empty((R, k), dtype=torch.int32, device=dev)
+    if val is None:
+        val = torch.empty((R, k), dtype=torch.float32, device=dev)
+    if lse is None and with_lse:
+        lse = torch.empty((R,), dtype=torch.float32, device=dev)
+    need = jf_node_topk_workspace_size(R, V, k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib().jf_node_topk(_p(logits), R, V, ld, _dtype_code(logits), k, _p(idx), _p(val), _p(lse),
+                            _p(workspace), ws_bytes, _stream(stream))
+    _check("jf_node_topk", st)
+    return idx, val, lse
