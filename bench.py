@@ -1,0 +1,279 @@
+#!/usr/bin/env python3
+"""Throughput of one draft step of the tree-causal draft head on one MI355X.
+
+A step is the whole hot path over one batch of synthetic input:
+  1. jf_tree_mask_build  -- ancestor bitmask of the 256-node tree
+  2. jf_fuse_proj        -- fused projection of 3 target-layer hidden states
+                            (one row per tree node, 3*4096 -> 4096, bf16 MFMA)
+  3. jf_tree_attn_fwd    -- tree-causal attention over the 4096-token prefix
+  4. jf_node_topk        -- per-node top-8 over a 151936-token vocabulary + lse
+on the Qwen3-8B-shaped high-budget workload (1 sequence, 4096-token prefix,
+256-node tree, 32/8 heads, head dim 128, bf16).  Inputs are generated on the
+host, uploaded, and resident in HBM before the timed region.
+
+Prints one JSON line: value = tree nodes per second over K back-to-back steps
+(wall clock between device synchronisations), per-call HIP-event timings,
+the roofline of the dominant call and of the tree attention, a cold-cache
+variant (a 512 MiB write between steps evicts the 256 MiB last-level cache),
+and the fp64 oracle timed on this host's cores on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "draft-tree nodes/sec + tree-attn HBM GB/s (% of peak), 256-node tree @ 1 GPU"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=2, help="workload id (synth.WORKLOADS)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-steps", type=int, default=20)
+    ap.add_argument("--cpu-sample-nodes", type=int, default=256)
+    return ap.parse_args()
+
+
+def to_dev(a, dtype, torch):
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def algorithmic(wl, inp, fuse_out_bytes):
+    """Bytes and flops each call must move / do at minimum (no re-reads)."""
+    a = inp["attn"]
+    B, N, Hq, Hkv, D = wl.B, wl.N, wl.Hq, wl.Hkv, wl.D
+    e = 2 if wl.dtype == "bf16" else 4
+    W = (N + 63) // 64
+    sumP = int(np.sum(a["prefix_len"]))
+    depth_sum = 0
+    for b in range(B):
+        par = a["parent"][b]
+        d = np.zeros(N, np.int64)
+        for i in range(N):
+            d[i] = 1 if par[i] < 0 else d[par[i]] + 1
+        depth_sum += int(d.sum())
+    M, H, k = B * N, wl.H, wl.n_fused
+    out = {}
+    out["mask"] = dict(bytes=B * N * 4 + B * N * W * 8 + B * N * 4, flops=0)
+    out["fuse"] = dict(bytes=k * M * H * e + H * k * H * e + M * H * fuse_out_bytes,
+                       flops=2 * M * H * k * H)
+    out["attn"] = dict(bytes=B * N * Hq * D * e + 2 * B * N * Hkv * D * e + 2 * sumP * Hkv * D * e
+                       + B * N * W * 8 + B * N * Hq * D * e + B * N * Hq * 4,
+                       flops=4 * Hq * D * (N * sumP + depth_sum))
+    R = B * N
+    out["topk"] = dict(bytes=R * wl.V * e + R * wl.topk * 8 + R * 4, flops=0)
+    return out
+
+
+def cpu_baseline(wl, inp, n_nodes):
+    """The fp64 oracle (test infrastructure) on this host over a sample of the
+    step: the first n_nodes tree nodes of sequence 0 through all four parts."""
+    import oracle
+    from tree_causal_draft_parent_amd import synth
+    a = inp["attn"]
+    N, Hq = wl.N, wl.Hq
+    n = min(n_nodes, N)
+    rows_attn = np.arange(n * Hq, dtype=np.int64)           # sequence 0, nodes 0..n-1, all heads
+    rows_node = np.arange(n, dtype=np.int64)
+    x64 = synth.to_f64(inp["fuse"]["x"], wl.dtype)
+    w64 = synth.to_f64(inp["fuse"]["w"], wl.dtype)
+    lg64 = synth.to_f64(inp["logits"][:n], wl.dtype)
+    f = {key: synth.to_f64(a[key], wl.dtype) for key in ("q", "k_tree", "v_tree", "k_cache", "v_cache")}
+    t0 = time.perf_counter()
+    oracle.tree_mask(a["parent"])
+    oracle.fuse_proj(x64, w64, rows=rows_node)
+    oracle.tree_attn(q=f["q"], k_tree=f["k_tree"], v_tree=f["v_tree"], parent=a["parent"],
+                     k_cache=f["k_cache"], v_cache=f["v_cache"], block_table=a["block_table"],
+                     prefix_len=a["prefix_len"], page_size=a["page_size"], rows=rows_attn)
+    oracle.topk(lg64, wl.topk)
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "nodes/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{n} of {N} tree nodes of sequence 0 through mask, fused projection, "
+                      f"tree attention (all {Hq} heads) and top-{wl.topk}+lse; {dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from tree_causal_draft_parent_amd import jf, synth
+
+    wl = synth.workload(args.workload)
+    inp = synth.make_workload(args.workload)
+    dt = wl.dtype
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    a = inp["attn"]
+    dev = {k: to_dev(a[k], dt, torch) for k in ("q", "k_tree", "v_tree", "k_cache", "v_cache")}
+    parent = torch.from_numpy(a["parent"]).cuda()
+    block_table = torch.from_numpy(a["block_table"]).cuda()
+    prefix_len = a["prefix_len"]
+    xt = to_dev(inp["fuse"]["x"], dt, torch)
+    xs = [xt[l] for l in range(wl.n_fused)]
+    w = to_dev(inp["fuse"]["w"], dt, torch)
+    logits = to_dev(inp["logits"], dt, torch)
+
+    B, N = wl.B, wl.N
+    W = (N + 63) // 64
+    mask = torch.empty((B, N, W), dtype=torch.int64, device="cuda")
+    depth = torch.empty((B, N), dtype=torch.int32, device="cuda")
+    seq_status = torch.empty((B,), dtype=torch.int32, device="cuda")
+    fuse_out_dtype = tdt
+    y = torch.empty((B * N, wl.H), dtype=fuse_out_dtype, device="cuda")
+    fws = jf.jf_fuse_proj_workspace_size(B * N, wl.H, wl.n_fused, wl.H, jf.JF_BF16 if dt == "bf16" else jf.JF_F32)
+    fuse_ws = torch.empty(max(fws, 1), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(dev["q"])
+    lse = torch.empty((B, N, wl.Hq), dtype=torch.float32, device="cuda")
+    aws = jf.jf_tree_attn_workspace_size(B, N, wl.Hq, wl.Hkv, wl.D, a["page_size"], prefix_len,
+                                         jf.JF_BF16 if dt == "bf16" else jf.JF_F32)
+    attn_ws = torch.empty(max(aws, 1), dtype=torch.uint8, device="cuda")
+    R = B * N
+    idx = torch.empty((R, wl.topk), dtype=torch.int32, device="cuda")
+    val = torch.empty((R, wl.topk), dtype=torch.float32, device="cuda")
+    rlse = torch.empty((R,), dtype=torch.float32, device="cuda")
+    tws = jf.jf_node_topk_workspace_size(R, wl.V, wl.topk)
+    topk_ws = torch.empty(max(tws, 1), dtype=torch.uint8, device="cuda")
+    page_status = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    calls = ["mask", "fuse", "attn", "topk"]
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        jf.jf_tree_mask_build(parent, mask, depth, seq_status)
+        if ev is not None:
+            ev[1].record()
+        jf.jf_fuse_proj(xs, w, y=y, workspace=fuse_ws)
+        if ev is not None:
+            ev[2].record()
+        jf.jf_tree_attn_fwd(dev["q"], dev["k_tree"], dev["v_tree"], mask, dev["k_cache"],
+                            dev["v_cache"], block_table, prefix_len, out=out, lse=lse,
+                            workspace=attn_ws, page_status=page_status)
+        if ev is not None:
+            ev[3].record()
+        jf.jf_node_topk(logits, wl.topk, idx=idx, val=val, lse=rlse, workspace=topk_ws)
+        if ev is not None:
+            ev[4].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] workload {wl.name}: warmup done", file=sys.stderr, flush=True)
+
+    # ---- timed region: K back-to-back steps --------------------------------
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        step(evs[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+    per_call = {c: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(K)]))
+                for i, c in enumerate(calls)}
+    gpu_step_ms = float(np.mean([evs[k][0].elapsed_time(evs[k][4]) for k in range(K)]))
+    print(f"[bench] timed {K} steps: {ms_per_step:.4f} ms/step", file=sys.stderr, flush=True)
+
+    # ---- cold-cache steps: evict the last-level cache before each step -------
+    flush_buf = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+    cold = []
+    cold_call = {c: [] for c in calls}
+    for k in range(args.cold_steps):
+        flush_buf.fill_(float(k))
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        step(ev)
+        torch.cuda.synchronize()
+        cold.append(ev[0].elapsed_time(ev[4]))
+        for i, c in enumerate(calls):
+            cold_call[c].append(ev[i].elapsed_time(ev[i + 1]))
+    del flush_buf
+    assert int(page_status.item()) == 0 and bool((seq_status == -1).all())
+
+    def med(v):
+        return float(np.median(v)) if len(v) else float("nan")
+
+    alg = algorithmic(wl, inp, 2 if fuse_out_dtype == torch.bfloat16 else 4)
+    bound = {"mask": "latency", "fuse": "hbm", "attn": "mfma", "topk": "hbm"}
+    if wl.dtype == "f32":
+        bound.update(fuse="alu", attn="alu")
+
+    def roof(c, ms):
+        s = ms * 1e-3
+        gbs = alg[c]["bytes"] / s / 1e9
+        tfs = alg[c]["flops"] / s / 1e12
+        return gbs, tfs
+
+    dom = max(("fuse", "attn", "topk"), key=lambda c: per_call[c])
+    gbs, tfs = roof(dom, per_call[dom])
+    if bound[dom] == "mfma":
+        roofline = {"bound": "mfma", "achieved": round(tfs, 2), "peak": BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(tfs / BF16_PEAK_TFLOPS, 4), "traffic": None}
+    else:
+        roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}
+    roofline["kernel"] = {"fuse": "jf_fuse_proj (k_fuse_gemm_bf16 + k_fuse_reduce)",
+                          "attn": "jf_tree_attn_fwd (k_tree_attn_split + k_tree_attn_merge)",
+                          "topk": "jf_node_topk (k_topk_stage1 + k_topk_stage2)"}[dom]
+    roofline["algorithmic"] = {"bytes": alg[dom]["bytes"], "flops": alg[dom]["flops"]}
+
+    a_gbs, a_tfs = roof("attn", per_call["attn"])
+    ca_gbs, ca_tfs = roof("attn", med(cold_call["attn"]))
+    tree_attn = {
+        "ms": round(per_call["attn"], 5), "nodes_per_s": round(B * N / (per_call["attn"] * 1e-3), 1),
+        "hbm_GBps": round(a_gbs, 1), "hbm_frac": round(a_gbs / HBM_PEAK_GBS, 4),
+        "TFLOPs": round(a_tfs, 2), "mfma_frac": round(a_tfs / BF16_PEAK_TFLOPS, 4),
+        "cold_ms": round(med(cold_call["attn"]), 5),
+        "cold_hbm_GBps": round(ca_gbs, 1), "cold_hbm_frac": round(ca_gbs / HBM_PEAK_GBS, 4),
+        "algorithmic": alg["attn"],
+    }
+    calls_out = {}
+    for c in calls:
+        g_, t_ = roof(c, per_call[c])
+        calls_out[c] = {"ms": round(per_call[c], 5), "cold_ms": round(med(cold_call[c]), 5),
+                        "GBps": round(g_, 1), "TFLOPs": round(t_, 2), "bound": bound[c]}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on host cores", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wl, inp, args.cpu_sample_nodes)
+
+    value = B * N * K / (t1 - t0)
+    rec = {
+        "metric": METRIC, "value": round(value, 1), "unit": "nodes/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "prefix": int(np.max(prefix_len)), "tree_nodes": N,
+                   "q_heads": wl.Hq, "kv_heads": wl.Hkv, "head_dim": wl.D, "hidden": wl.H,
+                   "fused_layers": wl.n_fused, "vocab": wl.V, "topk": wl.topk,
+                   "step": "mask+fuse_proj+tree_attn+topk"},
+        "gpu_step_ms": round(gpu_step_ms, 5),
+        "cold_step_ms": round(med(cold), 5),
+        "cold_nodes_per_s": round(B * N / (med(cold) * 1e-3), 1),
+        "calls": calls_out,
+        "tree_attn": tree_attn,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -52,7 +52,7 @@ typedef enum { JF_F32 = 0, JF_BF16 = 1 } jf_dtype;
 const char *jf_status_string(int status);
 
 /* ABI version, bumped on any signature change. */
-int jf_abi_version(void);
+int jf_abi_version(void);  /* 2 */
 
 /* --------------------------------------------------------------------------
  * jf_tree_mask_build -- ancestor bitmask of every tree node.
@@ -133,11 +133,13 @@ jf_status jf_fuse_proj(const void *const *x, int32_t k, int64_t M,
  *               never cleared by the library, so zero it once beforehand.
  *   dtype       JF_BF16: D == 128, MFMA split-KV path;  JF_F32: D <= 128,
  *               plain fp32 path (small problems).
- *   Limits: 1 <= B <= 256, 1 <= N <= 1024, Hq % Hkv == 0.
+ *   Limits: 1 <= B <= 256, 1 <= N <= 1024, Hq % Hkv == 0; on the bf16
+ *   path each of q, k_tree, k_cache (and their value twins) must be smaller
+ *   than 4 GiB - 256 bytes (32-bit buffer offsets), else JF_ERR_UNSUPPORTED.
  *   workspace:  jf_tree_attn_workspace_size() bytes with the same arguments.
  * ------------------------------------------------------------------------ */
 size_t jf_tree_attn_workspace_size(int32_t B, int32_t N, int32_t Hq,
-                                   int32_t Hkv, int32_t D,
+                                   int32_t Hkv, int32_t D, int32_t page_size,
                                    const int32_t *prefix_len, jf_dtype dtype);
 jf_status jf_tree_attn_fwd(const void *q, const void *k_tree,
                            const void *v_tree, const uint64_t *mask,

@@ -65,6 +65,8 @@ def _load():
     lib.oracle_tree_attn.restype = ctypes.c_int
     lib.oracle_topk.argtypes = [P, I64, I64, I64, P, P, P]
     lib.oracle_topk.restype = None
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -157,3 +159,8 @@ def topk(logits: np.ndarray, k: int, with_lse: bool = True):
     lse = np.empty((R,), dtype=np.float64) if with_lse else None
     _load().oracle_topk(_p(logits), R, V, k, _p(idx), _p(val), _p(lse))
     return idx, val, lse
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(_load().oracle_num_threads())

@@ -28,6 +28,7 @@
  * map; top-k order is value descending then index ascending, -0 == +0.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -270,3 +271,6 @@ void oracle_topk(const double *logits, int64_t R, int64_t V, int64_t k,
         }
     }
 }
+
+/* Threads an OpenMP region of this library uses (for reporting). */
+int oracle_num_threads(void) { return omp_get_max_threads(); }

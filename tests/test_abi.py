@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
 def test_status_strings_and_version():
     assert jf.status_string(0) == "JF_OK"
     assert jf.status_string(5) == "JF_ERR_BAD_TREE"
-    assert jf.lib().jf_abi_version() == 1
+    assert jf.lib().jf_abi_version() == 2
 
 
 FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: every call below fails validation
@@ -75,7 +75,7 @@ def test_attn_argument_errors():
     assert _attn(L, q=FAKE_ODD) == jf.JF_ERR_ALIGN
     # this shape splits the keys, so a workspace is required
     pl = np.array([4096, 4096], np.int32)
-    need = L.jf_tree_attn_workspace_size(2, 256, 32, 8, 128, pl.ctypes.data_as(ctypes.c_void_p), 1)
+    need = L.jf_tree_attn_workspace_size(2, 256, 32, 8, 128, 4096, pl.ctypes.data_as(ctypes.c_void_p), 1)
     assert need > 0
     assert _attn(L, pl=pl, N=256, Hq=32, Hkv=8, max_pages=1, page_size=4096,
                  ws=FAKE, ws_bytes=need - 1) == jf.JF_ERR_WORKSPACE
@@ -84,10 +84,10 @@ def test_attn_argument_errors():
 def test_workspace_sizes_are_host_side_and_consistent():
     L = jf.lib()
     pl = np.array([4096], np.int32).ctypes.data_as(ctypes.c_void_p)
-    a = L.jf_tree_attn_workspace_size(1, 256, 32, 8, 128, pl, 1)
+    a = L.jf_tree_attn_workspace_size(1, 256, 32, 8, 128, 4096, pl, 1)
     assert a % 4 == 0
-    assert L.jf_tree_attn_workspace_size(1, 256, 32, 8, 128, pl, 0) == 0  # fp32 path: no splits
-    assert L.jf_tree_attn_workspace_size(1, 256, 32, 7, 128, pl, 1) == 0  # invalid -> 0
+    assert L.jf_tree_attn_workspace_size(1, 256, 32, 8, 128, 4096, pl, 0) == 0  # fp32 path: no splits
+    assert L.jf_tree_attn_workspace_size(1, 256, 32, 7, 128, 4096, pl, 1) == 0  # invalid -> 0
     assert L.jf_node_topk_workspace_size(256, 151936, 8) > 0
     assert L.jf_node_topk_workspace_size(4, 10, 65) == 0
     assert L.jf_fuse_proj_workspace_size(256, 4096, 3, 4096, 1) >= 0

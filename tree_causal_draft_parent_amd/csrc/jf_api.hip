@@ -44,7 +44,7 @@ const char *jf_status_string(int status) {
     }
 }
 
-int jf_abi_version(void) { return 1; }
+int jf_abi_version(void) { return 2; }
 
 jf_status jf_tree_mask_build(const int32_t *parent, int32_t B, int32_t N, uint64_t *mask,
                              int32_t *depth, int32_t *seq_status, void *stream) {
@@ -119,11 +119,11 @@ static jf_status check_attn_dims(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, 
 }
 
 size_t jf_tree_attn_workspace_size(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
-                                   const int32_t *prefix_len, jf_dtype dtype) {
-    if (check_attn_dims(B, N, Hq, Hkv, D, prefix_len, dtype) != JF_OK) return 0;
+                                   int32_t page_size, const int32_t *prefix_len, jf_dtype dtype) {
+    if (check_attn_dims(B, N, Hq, Hkv, D, prefix_len, dtype) != JF_OK || page_size < 1) return 0;
     if (dtype == JF_F32) return 0;
     AttnPlan p;
-    plan_tree_attn(p, B, N, Hq, Hkv, D, prefix_len, dtype);
+    plan_tree_attn(p, B, N, Hq, Hkv, D, page_size, prefix_len, dtype);
     return tree_attn_workspace_bytes(p);
 }
 
@@ -146,9 +146,16 @@ jf_status jf_tree_attn_fwd(const void *q, const void *k_tree, const void *v_tree
         !aligned(v_cache, al) || !aligned(out, al) || !aligned(mask, 8) || !aligned(block_table, 4) ||
         (lse && !aligned(lse, 4)) || (page_status && !aligned(page_status, 4)))
         return JF_ERR_ALIGN;
+    if (dtype == JF_BF16) {
+        // the bf16 kernel addresses each tensor with 32-bit buffer offsets
+        const int64_t lim = 0xffffff00LL;
+        if (num_pages * page_size * (int64_t)Hkv * D * 2 > lim ||
+            (int64_t)B * N * Hq * D * 2 > lim || (int64_t)B * N * Hkv * D * 2 > lim)
+            return JF_ERR_UNSUPPORTED;
+    }
     if (!(scale > 0.f)) scale = 1.f / sqrtf((float)D);
     AttnPlan p;
-    plan_tree_attn(p, B, N, Hq, Hkv, D, prefix_len, dtype);
+    plan_tree_attn(p, B, N, Hq, Hkv, D, page_size, prefix_len, dtype);
     hipError_t e;
     if (dtype == JF_BF16) {
         const size_t need = tree_attn_workspace_bytes(p);

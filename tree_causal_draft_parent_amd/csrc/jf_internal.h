@@ -22,15 +22,15 @@ constexpr int kNumXcd = 8;
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs)
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
-}
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+    f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) { return pack_bf16x2(f, 0.f) & 0xffffu; }
 
 // Consecutive workgroup ids are spread round-robin over the XCDs.  Map the
 // hardware id so that the workgroups landing on one XCD get one contiguous
@@ -56,13 +56,14 @@ struct AttnPlan {
     int tq;              // query rows per tile
     int chunk_blocks;    // 64-key blocks per split
     int n_tree_blocks;   // ceil(N / 64)
+    int page_size;
     int total_chunks;    // sum over sequences of splits
     int total_items;     // workgroups of the split kernel
     bool any_split;      // some sequence has more than one split
     int prefix_len[kMaxBatch];
     int chunk_start[kMaxBatch + 1];
 };
-void plan_tree_attn(AttnPlan &p, int B, int N, int Hq, int Hkv, int D,
+void plan_tree_attn(AttnPlan &p, int B, int N, int Hq, int Hkv, int D, int page_size,
                     const int32_t *prefix_len, jf_dtype dtype);
 size_t tree_attn_workspace_bytes(const AttnPlan &p);
 

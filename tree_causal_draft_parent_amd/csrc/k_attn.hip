@@ -25,9 +25,17 @@
 //   * Online softmax in base 2 with a lazy rescale: the running maximum is
 //     only moved when a block's maximum exceeds it by more than 2^8, which
 //     keeps every exponent bounded while leaving the arithmetic exact.
-//   * K/V tiles are prefetched into registers one block ahead and written to
-//     a double-buffered LDS stage (K row-major, V transposed in registers so
-//     that the PV operand reads are contiguous in keys); one barrier a block.
+//   * K and V tiles go straight from HBM into LDS (buffer_load ... lds, 16
+//     bytes a lane) one block ahead, into a double-buffered stage; no
+//     registers are spent on the prefetch.  One copy instruction fills 1 KiB
+//     of LDS; block n of a tile holds rows n, n+16, n+32, n+48, and the
+//     blocks are padded (16 bytes for K, 64 for V) so that both the K operand
+//     reads (ds_read_b128) and the V operand reads hit distinct banks, while
+//     every operand address is one base register plus an immediate.  V stays
+//     row-major:
+//     ds_read_b64_tr_b16 hands each lane four consecutive keys of one head-dim
+//     column, which is exactly the V^T operand layout.  One wait + barrier a
+//     block.
 //   * Each split writes (O / l, log-sum-exp) partials; a merge kernel combines
 //     the splits of a row with LSE weights.  A sequence with one split writes
 //     the final output directly.
@@ -40,29 +48,34 @@ constexpr int kKB = 64;                  // keys per block
 constexpr int kNW = 4;                   // waves per workgroup
 constexpr int kTQ = 32 * kNW;            // query rows per workgroup
 constexpr int kD = 128;                  // head dim of the bf16 path
-constexpr int kKRow = kD * 2 + 16;       // bytes per K row in LDS (padded)
-constexpr int kVRow = kKB * 2 + 8;       // bytes per V^T row in LDS (padded)
-constexpr int kKTile = kKB * kKRow;
-constexpr int kVTile = kD * kVRow;
-constexpr int kStage = kKTile + kVTile;
+constexpr int kRow = kD * 2;             // bytes per K or V row
+constexpr int kKBlk = 4 * kRow + 16;     // LDS block of 4 K rows (n, n+16, n+32, n+48)
+constexpr int kVBlk = 4 * kRow + 64;     // LDS block of 4 V rows
+constexpr int kKTile = 16 * kKBlk;
+constexpr int kVTile = 16 * kVBlk;
+constexpr int kStage = kKTile + kVTile;  // K tile then V tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazyLog2 = 8.f;
 
 struct AttnArgs {
-    const uint16_t *q, *k_tree, *v_tree;
+    const uint16_t *q, *k_tree, *v_tree, *k_cache, *v_cache;
     const uint64_t *mask;
-    const uint16_t *k_cache, *v_cache;
     const int32_t *block_table;
     void *out;
     float *lse, *part_o, *part_lse;
     int32_t *page_status;
+    uint32_t q_bytes, tree_bytes, cache_bytes, mask_bytes;
     int64_t num_pages;
-    int page_size, max_pages, B, N, Hq, Hkv, G, R, W, n_qt, chunk_blocks, n_tree_blocks,
-        total_items;
+    int page_mode;  // 1: one page per sequence; 2: power-of-two pages >= 16; 0: other
+    int page_size, page_shift, max_pages, B, N, Hq, Hkv, G, R, W, n_qt, chunk_blocks,
+        n_tree_blocks, total_items;
     float scale, c2, lazy_raw;
     int prefix_len[kMaxBatch];
     int chunk_start[kMaxBatch + 1];
 };
+
+constexpr int kPageLds = 1024;     // page ids of one split staged in LDS
+constexpr uint32_t kOob = 0xffffff00u;  // offset past every buffer: loads return zeros
 
 __device__ __forceinline__ int find_seq(const AttnArgs &a, int cg) {
     int lo = 0, hi = a.B - 1;
@@ -73,91 +86,45 @@ __device__ __forceinline__ int find_seq(const AttnArgs &a, int cg) {
     return lo;
 }
 
-struct TileRegs {
-    u32x4 k[4];
-    u32x4 v[4];
-};
-
-// Row offset (in elements) of prefix position pos of sequence b, KV head g, or
-// -1 when the page id is out of range.
-__device__ __forceinline__ int64_t prefix_row(const AttnArgs &a, int b, int g, int pos) {
-    int64_t page;
-    int slot;
-    if (a.max_pages == 1) {
-        page = a.block_table[b * a.max_pages];
-        slot = pos;
-    } else {
-        page = a.block_table[(int64_t)b * a.max_pages + pos / a.page_size];
-        slot = pos % a.page_size;
-    }
-    if (page < 0 || page >= a.num_pages) return -1;
-    return ((page * a.page_size + slot) * a.Hkv + g) * (int64_t)kD;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
 }
 
-__device__ __forceinline__ void load_tile(const AttnArgs &a, int b, int g, int P, int nPB, int kb,
-                                          int tid, TileRegs &t, bool &bad_page) {
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    const int kc = tid & 15;   // K: 16-byte chunk of a key row
-    const int kr = tid >> 4;   // K: key kr + 16 r
-    const int vq = tid & 15;   // V: key quad (keys 4 vq .. 4 vq + 3)
-    const int vd = tid >> 4;   // V: 8-wide d chunk
+typedef __attribute__((address_space(3))) char lds_t;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Byte offset of (key row, 16-byte chunk) of block kb in its buffer, or kOob.
+// Prefix rows go through the split's page ids in LDS; tree rows index the
+// nodes' own K/V.  An out-of-range page id reads as zeros and is flagged.
+__device__ __forceinline__ uint32_t row_offset(const AttnArgs &a, const int *pages, int page0, int b,
+                                               int g, int P, int nPB, int kb, int row, int chunk,
+                                               bool &bad) {
     if (kb < nPB) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int pos = kb * kKB + kr + 16 * r;
-            t.k[r] = zero;
-            if (pos < P) {
-                int64_t off = prefix_row(a, b, g, pos);
-                if (off >= 0) t.k[r] = *(const u32x4 *)(a.k_cache + off + kc * 8);
-                else bad_page = true;
-            }
+        const int pos = kb * kKB + row;
+        if (pos >= P) return kOob;
+        int pg, slot;
+        if (a.page_shift >= 0) {
+            pg = pos >> a.page_shift;
+            slot = pos & (a.page_size - 1);
+        } else {
+            pg = pos / a.page_size;
+            slot = pos - pg * a.page_size;
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int pos = kb * kKB + 4 * vq + r;
-            t.v[r] = zero;
-            if (pos < P) {
-                int64_t off = prefix_row(a, b, g, pos);
-                if (off >= 0) t.v[r] = *(const u32x4 *)(a.v_cache + off + vd * 8);
-                else bad_page = true;
-            }
+        const int page = pages[pg - page0];
+        if (page < 0 || page >= a.num_pages) {
+            bad = true;
+            return kOob;
         }
-    } else {
-        const int j0 = (kb - nPB) * kKB;
-        const int64_t base = ((int64_t)b * a.N) * a.Hkv + g;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int j = j0 + kr + 16 * r;
-            t.k[r] = j < a.N ? *(const u32x4 *)(a.k_tree + (base + (int64_t)j * a.Hkv) * kD + kc * 8) : zero;
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int j = j0 + 4 * vq + r;
-            t.v[r] = j < a.N ? *(const u32x4 *)(a.v_tree + (base + (int64_t)j * a.Hkv) * kD + vd * 8) : zero;
-        }
+        return ((((uint32_t)page * a.page_size + slot) * a.Hkv + g) * kD + chunk * 8) * 2u;
     }
+    const int j = (kb - nPB) * kKB + row;
+    if (j >= a.N) return kOob;
+    return ((((uint32_t)b * a.N + j) * a.Hkv + g) * kD + chunk * 8) * 2u;
 }
 
-__device__ __forceinline__ void store_tile(char *stage, int tid, const TileRegs &t) {
-    const int kc = tid & 15, kr = tid >> 4;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) *(u32x4 *)(stage + (kr + 16 * r) * kKRow + kc * 16) = t.k[r];
-    // V^T: this thread holds V[4vq + r][8vd .. 8vd + 7] for r = 0..3; word w of
-    // each row packs d = 8vd + 2w (low half) and 8vd + 2w + 1 (high half).
-    char *vt = stage + kKTile;
-    const int vq = tid & 15, vd = tid >> 4;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        const uint32_t a0 = t.v[0][w], a1 = t.v[1][w], a2 = t.v[2][w], a3 = t.v[3][w];
-        u32x2 lo, hi;
-        lo[0] = (a0 & 0xffffu) | (a1 << 16);
-        lo[1] = (a2 & 0xffffu) | (a3 << 16);
-        hi[0] = (a0 >> 16) | (a1 & 0xffff0000u);
-        hi[1] = (a2 >> 16) | (a3 & 0xffff0000u);
-        *(u32x2 *)(vt + (8 * vd + 2 * w) * kVRow + vq * 8) = lo;
-        *(u32x2 *)(vt + (8 * vd + 2 * w + 1) * kVRow + vq * 8) = hi;
-    }
-}
+// LDS byte offset of key row r of a tile: block r % 16, slot r / 16
+__device__ __forceinline__ int k_lds(int r) { return (r & 15) * kKBlk + (r >> 4) * kRow; }
+__device__ __forceinline__ int v_lds(int r) { return (r & 15) * kVBlk + (r >> 4) * kRow; }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -168,8 +135,235 @@ __device__ __forceinline__ bf16x8 cvt8(const f32x16 &s, int base) {
     return as_bf16x8(w);
 }
 
-__global__ __launch_bounds__(kNW * kWave) void k_tree_attn_split(AttnArgs a) {
-    __shared__ __attribute__((aligned(16))) char smem[2 * kStage];
+struct SplitCtx {
+    __amdgpu_buffer_rsrc_t r_kt, r_vt, r_kc, r_vc, r_m;
+    int b, g, P, nPB, kb1, page0, lane, wave;
+    uint32_t moff;
+};
+
+// One 16-byte-per-lane copy HBM -> LDS: lane L's 16 bytes land at lds + 16 L.
+// Issued as inline asm so that the compiler does not order later LDS reads of
+// the other stage behind it; completion is waited for explicitly (vmcnt) at
+// the next block's barrier.
+__device__ __forceinline__ void copy16(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(r) : "memory");
+}
+
+// Start the copy of block kb's K and V tiles into stage `dst` (asynchronous;
+// each wave fills 4 of the 16 LDS blocks of each tile, one copy each: LDS
+// block n holds rows n + 16*slot, lane L copying row n + 16*(L/16), 16-byte
+// chunk L%16).  K and V rows share their byte offsets.  Also loads this lane's
+// 64-bit mask word of the block (zero for prefix blocks).
+__device__ __forceinline__ uint64_t issue_block(const AttnArgs &a, const SplitCtx &c, const int *pages,
+                                                uint32_t dst, int kb, bool &bad) {
+    const bool tree = kb >= c.nPB;
+    const __amdgpu_buffer_rsrc_t rk = tree ? c.r_kt : c.r_kc;
+    const __amdgpu_buffer_rsrc_t rv = tree ? c.r_vt : c.r_vc;
+    const int sub = c.lane >> 4, ch = c.lane & 15;
+    const uint32_t rowb = (uint32_t)a.Hkv * kD * 2;       // bytes between consecutive keys
+    const uint32_t dstk = __builtin_amdgcn_readfirstlane(dst + 4 * c.wave * kKBlk);
+    const uint32_t dstv = __builtin_amdgcn_readfirstlane(dst + kKTile + 4 * c.wave * kVBlk);
+    uint32_t off[4];
+    if (tree || a.page_mode != 0) {
+        // rows 16*sub + n (n < 16) are contiguous keys of one page (or of the tree)
+        uint32_t vbase = kOob;
+        int lim;
+        if (tree) {
+            const int j0 = (kb - c.nPB) * kKB;
+            lim = a.N - j0;
+            vbase = ((((uint32_t)c.b * a.N + j0 + 16 * sub) * a.Hkv + c.g) * kD + ch * 8) * 2u;
+        } else {
+            const int pos = kb * kKB + 16 * sub;
+            lim = c.P - kb * kKB;
+            if (16 * sub < lim) {
+                int pg, slot;
+                if (a.page_mode == 1) {                    // one page per sequence
+                    pg = c.page0;
+                    slot = pos;
+                } else {                                   // power-of-two pages of >= 16
+                    pg = pos >> a.page_shift;
+                    slot = pos & (a.page_size - 1);
+                }
+                const int page = pages[pg - c.page0];
+                if (page >= 0 && page < a.num_pages)
+                    vbase = ((((uint32_t)page * a.page_size + slot) * a.Hkv + c.g) * kD + ch * 8) * 2u;
+                else
+                    bad = true;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int n = 4 * c.wave + i;
+            off[i] = (16 * sub + n < lim && vbase != kOob) ? vbase + n * rowb : kOob;
+        }
+    } else {
+        // small or irregular pages: look every row up
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            off[i] = row_offset(a, pages, c.page0, c.b, c.g, c.P, c.nPB, kb, 4 * c.wave + i + 16 * sub,
+                                ch, bad);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) copy16(rk, dstk + i * kKBlk, off[i]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) copy16(rv, dstv + i * kVBlk, off[i]);
+    const uint32_t moff = (tree && c.moff != kOob) ? c.moff + (kb - c.nPB) * 8 : kOob;
+    u32x2 mw = __builtin_amdgcn_raw_buffer_load_b64(c.r_m, moff, 0, 0);
+    return ((uint64_t)mw[1] << 32) | mw[0];
+}
+
+struct SoftmaxState {
+    f32x16 o[kD / 32];
+    float m, l;
+};
+
+// One 64-key block: S^T = K Q^T, masking, online softmax, O^T += V^T P^T.
+__device__ __forceinline__ void compute_block(const AttnArgs &a, const lds_t *__restrict__ st,
+                                              const bf16x8 *qf, int kb, int nPB, int P,
+                                              uint64_t word, int lane, SoftmaxState &S) {
+    const int half = lane >> 5, l32 = lane & 31;
+    f32x16 s0, s1;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { s0[i] = 0.f; s1[i] = 0.f; }
+    // K operand reads run one k-step ahead of the MFMAs; the scheduling
+    // fences keep the compiler from hoisting every read of the block (which
+    // would cost ~130 registers and halve occupancy).
+    const lds_t *kbase = st + k_lds(l32) + half * 16;   // row l32, chunk half; + 32 rows = 2 slots
+    auto kread = [&](int t, bf16x8 &k0, bf16x8 &k1) {
+        k0 = *(const __attribute__((address_space(3))) bf16x8 *)(kbase + t * 32);
+        k1 = *(const __attribute__((address_space(3))) bf16x8 *)(kbase + 2 * kRow + t * 32);
+    };
+    bf16x8 ka0, ka1, kb0v, kb1v;
+    kread(0, ka0, ka1);
+#pragma unroll
+    for (int t = 0; t < kD / 16; t += 2) {
+        kread(t + 1, kb0v, kb1v);
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka0, qf[t], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka1, qf[t], s1, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (t + 2 < kD / 16) kread(t + 2, ka0, ka1);
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb0v, qf[t + 1], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb1v, qf[t + 1], s1, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // Register i of a half-wave holds key 4*(2*(i/4) + half) + i%4 (+32 for
+    // s1): the half-wave's keys are the nibbles half, half+2, ... of the
+    // block's 64-bit visibility word.  Gather them into bits 0-15 (s0) and
+    // 16-31 (s1) of one 32-bit word and test bit i.
+    const bool is_tree = kb >= nPB;
+    const bool tail = !is_tree && (kb + 1) * kKB > P;
+    if (is_tree || tail) {
+        uint64_t vis;
+        if (is_tree) {
+            const int left = a.N - (kb - nPB) * kKB;     // tree keys that exist in this block
+            vis = word & (left >= 64 ? ~0ull : ((1ull << left) - 1ull));
+        } else {
+            const int left = P - kb * kKB;
+            vis = (1ull << left) - 1ull;                 // 0 < left < 64
+        }
+        uint64_t x = (vis >> (4 * half)) & 0x0F0F0F0F0F0F0F0Full;
+        x = (x | (x >> 4)) & 0x00FF00FF00FF00FFull;
+        x = (x | (x >> 8)) & 0x0000FFFF0000FFFFull;
+        const uint32_t m = (uint32_t)(x | (x >> 16));
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            s0[i] = ((m >> i) & 1u) ? s0[i] : -INFINITY;
+            s1[i] = ((m >> (16 + i)) & 1u) ? s1[i] : -INFINITY;
+        }
+    }
+    float mx = fmaxf(s0[0], s1[0]);
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(fmaxf(mx, s0[i]), s1[i]);   // v_max3_f32
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const bool need = mx > S.m + a.lazy_raw;
+    if (__ballot(need)) {
+        const float m_new = need ? mx : S.m;
+        const float alpha = need ? __builtin_amdgcn_exp2f((S.m - m_new) * a.c2) : 1.f;
+        S.l *= alpha;
+#pragma unroll
+        for (int d = 0; d < kD / 32; ++d)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) S.o[d][i] *= alpha;
+        S.m = m_new;
+    }
+    const float base = S.m == -INFINITY ? 0.f : S.m * a.c2;
+    float ls = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        s0[i] = __builtin_amdgcn_exp2f(fmaf(s0[i], a.c2, -base));
+        s1[i] = __builtin_amdgcn_exp2f(fmaf(s1[i], a.c2, -base));
+        ls += s0[i] + s1[i];
+    }
+    S.l += ls;
+    bf16x8 p[4];
+    p[0] = cvt8(s0, 0);
+    p[1] = cvt8(s0, 8);
+    p[2] = cvt8(s1, 0);
+    p[3] = cvt8(s1, 8);
+
+    // O^T (d x rows) += V^T P^T.  Within each 16-lane group, ds_read_b64_tr_b16
+    // gives lane i element (i%4) of the 8-byte rows supplied by lanes i/4 + 4e
+    // (e = 0..3): if lane q + 4e points at V[key0 + e][d0 + 4q], lane i receives
+    // V[key0 .. key0+3][d0 + i].  Two such reads (keys key0 and key0 + 8) form
+    // the operand slots 0-3 and 4-7 that match the score registers in p[].
+    const int grp = l32 >> 4, gi = lane & 15, q4 = gi & 3, e4 = gi >> 2;
+    // lane (group grp, q4, e4) points at row key0 + e4, columns grp*16 + 4*q4 ...;
+    // key0 = sb*32 + 16*t + 4*half (+8 for the second read): row % 16 =
+    // 4*half + e4 (+8), row / 16 = 2*sb + t.
+    const lds_t *vbase = st + kKTile + (4 * half + e4) * kVBlk + (grp * 16 + 4 * q4) * 2;
+    auto vread = [&](int idx) -> bf16x8 {
+        const int d = idx >> 2, stp = idx & 3;           // stp = 2*sb + t
+        const lds_t *pa = vbase + stp * kRow + d * 64;
+        s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)pa);
+        s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4 *)(pa + 8 * kVBlk));
+        u32x2 lw = __builtin_bit_cast(u32x2, lo), hw = __builtin_bit_cast(u32x2, hi);
+        u32x4 w = {lw[0], lw[1], hw[0], hw[1]};
+        return as_bf16x8(w);
+    };
+    bf16x8 va = vread(0), vb;
+#pragma unroll
+    for (int idx = 0; idx < (kD / 32) * 4; idx += 2) {
+        vb = vread(idx + 1);
+        S.o[idx >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p[idx & 3], S.o[idx >> 2], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (idx + 2 < (kD / 32) * 4) va = vread(idx + 2);
+        S.o[(idx + 1) >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb, p[(idx + 1) & 3], S.o[(idx + 1) >> 2], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// Wait for this wave's outstanding copies and LDS reads, then barrier: after
+// it, every wave's copies into the current stage have landed and no wave still
+// reads the other stage.  The wait is the s_waitcnt builtin (not asm) so that
+// the compiler knows every older load is complete and adds no waits of its
+// own inside the block; the empty asm is a compiler fence for memory.
+__device__ __forceinline__ void stage_barrier() {
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ void run_block(const AttnArgs &a, const SplitCtx &c, const int *pages,
+                                          const lds_t *cur, uint32_t nxt, const bf16x8 *qf,
+                                          uint32_t used, int &kb, uint64_t &word, SoftmaxState &S,
+                                          bool &bad) {
+    stage_barrier();
+    int kbn = kb + 1;
+    while (kbn < c.kb1 && kbn >= c.nPB && !((used >> (kbn - c.nPB)) & 1u)) ++kbn;
+    uint64_t word_n = 0ull;
+    if (kbn < c.kb1) word_n = issue_block(a, c, pages, nxt, kbn, bad);
+    compute_block(a, cur, qf, kb, c.nPB, c.P, word, c.lane, S);
+    kb = kbn;
+    word = word_n;
+}
+
+__global__ __launch_bounds__(kNW * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_tree_attn_split(AttnArgs a) {
+    __shared__ __attribute__((aligned(1024))) char stage0[kStage];
+    __shared__ __attribute__((aligned(1024))) char stage1[kStage];
+    __shared__ int s_pages[kPageLds];
     __shared__ uint32_t s_used;
     __shared__ int s_bad;
 
@@ -183,13 +377,40 @@ __global__ __launch_bounds__(kNW * kWave) void k_tree_attn_split(AttnArgs a) {
     const int g = tmp % a.Hkv;
     const int cg = tmp / a.Hkv;
     const int b = find_seq(a, cg);
-    const int c = cg - a.chunk_start[b];
+    const int cidx = cg - a.chunk_start[b];
     const int nchunks = a.chunk_start[b + 1] - a.chunk_start[b];
     const int P = a.prefix_len[b];
     const int nPB = (P + kKB - 1) / kKB;
     const int nB = nPB + a.n_tree_blocks;
-    const int kb0 = c * a.chunk_blocks;
+    const int kb0 = cidx * a.chunk_blocks;
     const int kb1 = min(kb0 + a.chunk_blocks, nB);
+
+    SplitCtx c;
+    c.r_kt = rsrc(a.k_tree, a.tree_bytes);
+    c.r_vt = rsrc(a.v_tree, a.tree_bytes);
+    c.r_kc = rsrc(a.k_cache, a.cache_bytes);
+    c.r_vc = rsrc(a.v_cache, a.cache_bytes);
+    c.r_m = rsrc(a.mask, a.mask_bytes);
+    c.b = b; c.g = g; c.P = P; c.nPB = nPB; c.kb1 = kb1; c.lane = lane; c.wave = wave;
+
+    // ---- page ids of this split's prefix range ----
+    c.page0 = 0;
+    {
+        const int pos0 = kb0 * kKB;
+        const int pos1 = min(kb1 * kKB, P);
+        if (pos1 > pos0) {
+            int pend;
+            if (a.page_shift >= 0) {
+                c.page0 = pos0 >> a.page_shift;
+                pend = ((pos1 - 1) >> a.page_shift) + 1;
+            } else {
+                c.page0 = pos0 / a.page_size;
+                pend = (pos1 - 1) / a.page_size + 1;
+            }
+            const int32_t *bt = a.block_table + (int64_t)b * a.max_pages;
+            for (int i = tid; i < pend - c.page0; i += kNW * kWave) s_pages[i] = bt[c.page0 + i];
+        }
+    }
 
     // ---- this lane's query row ----
     const int r = qt * kTQ + wave * 32 + l32;
@@ -198,17 +419,15 @@ __global__ __launch_bounds__(kNW * kWave) void k_tree_attn_split(AttnArgs a) {
     const int hq = g * a.G + (row_ok ? r % a.G : 0);
     bf16x8 qf[kD / 16];
     {
-        const uint16_t *qrow = a.q + (((int64_t)b * a.N + node) * a.Hq + hq) * kD + half * 8;
+        const __amdgpu_buffer_rsrc_t r_q = rsrc(a.q, a.q_bytes);
+        const uint32_t qoff = row_ok ? (uint32_t)(((((int64_t)b * a.N + node) * a.Hq + hq) * kD + half * 8) * 2) : kOob;
 #pragma unroll
-        for (int t = 0; t < kD / 16; ++t) {
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (row_ok) v = *(const u32x4 *)(qrow + t * 16);
-            qf[t] = as_bf16x8(v);
-        }
+        for (int t = 0; t < kD / 16; ++t)
+            qf[t] = as_bf16x8(__builtin_amdgcn_raw_buffer_load_b128(r_q, row_ok ? qoff + t * 32 : kOob, 0, 0));
     }
-    const uint64_t *mrow = a.mask + ((int64_t)b * a.N + node) * a.W;
+    c.moff = row_ok ? (uint32_t)(((int64_t)b * a.N + node) * a.W * 8) : kOob;
 
-    // ---- which tree blocks of this chunk does any row of the tile see? ----
+    // ---- which tree blocks of this split does any row of the tile see? ----
     if (tid == 0) { s_used = 0u; s_bad = 0; }
     __syncthreads();
     if (kb1 > nPB && tid < kTQ) {
@@ -223,134 +442,37 @@ __global__ __launch_bounds__(kNW * kWave) void k_tree_attn_split(AttnArgs a) {
     }
     __syncthreads();
     const uint32_t used = s_used;
-    auto usable = [&](int kb) { return kb < nPB || ((used >> (kb - nPB)) & 1u); };
-    auto next_block = [&](int kb) {
-        ++kb;
-        while (kb < kb1 && !usable(kb)) ++kb;
-        return kb;
-    };
 
-    f32x16 o[kD / 32];
+    SoftmaxState S;
 #pragma unroll
     for (int d = 0; d < kD / 32; ++d)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) o[d][i] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
-    bool bad_page = false;
+        for (int i = 0; i < 16; ++i) S.o[d][i] = 0.f;
+    S.m = -INFINITY;
+    S.l = 0.f;
+    bool bad = false;
 
+    lds_t *st0 = (lds_t *)stage0;
+    lds_t *st1 = (lds_t *)stage1;
+    uint32_t a0 = (uint32_t)(uintptr_t)st0, a1 = (uint32_t)(uintptr_t)st1;
     int kb = kb0;
-    while (kb < kb1 && !usable(kb)) ++kb;
-    TileRegs tr;
+    while (kb < kb1 && kb >= nPB && !((used >> (kb - nPB)) & 1u)) ++kb;
     uint64_t word = 0ull;
-    if (kb < kb1) {
-        load_tile(a, b, g, P, nPB, kb, tid, tr, bad_page);
-        store_tile(smem, tid, tr);
-        if (kb >= nPB && row_ok) word = mrow[kb - nPB];
-    }
-    __syncthreads();
-    int buf = 0;
+    if (kb < kb1) word = issue_block(a, c, s_pages, a0, kb, bad);
     while (kb < kb1) {
-        const int kbn = next_block(kb);
-        uint64_t word_n = 0ull;
-        if (kbn < kb1) {
-            load_tile(a, b, g, P, nPB, kbn, tid, tr, bad_page);
-            if (kbn >= nPB && row_ok) word_n = mrow[kbn - nPB];
-        }
-        const char *stage = smem + buf * kStage;
-
-        // S^T (keys x rows) for the two 32-key halves of the block
-        f32x16 s0, s1;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) { s0[i] = 0.f; s1[i] = 0.f; }
-        {
-            const char *k0p = stage + l32 * kKRow + half * 16;
-            const char *k1p = k0p + 32 * kKRow;
-#pragma unroll
-            for (int t = 0; t < kD / 16; ++t) {
-                bf16x8 ka = *(const bf16x8 *)(k0p + t * 32);
-                bf16x8 kbv = *(const bf16x8 *)(k1p + t * 32);
-                s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[t], s0, 0, 0, 0);
-                s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kbv, qf[t], s1, 0, 0, 0);
-            }
-        }
-        // register i of a half holds key (i/4)*8 + half*4 + i%4 (+32 for s1)
-        const bool is_tree = kb >= nPB;
-        const bool tail = !is_tree && (kb + 1) * kKB > P;
-        if (is_tree) {
-            const int jbase = (kb - nPB) * kKB;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int key = (i >> 2) * 8 + half * 4 + (i & 3);
-                const bool v0 = ((word >> key) & 1ull) && (jbase + key < a.N);
-                const bool v1 = ((word >> (key + 32)) & 1ull) && (jbase + key + 32 < a.N);
-                s0[i] = v0 ? s0[i] : -INFINITY;
-                s1[i] = v1 ? s1[i] : -INFINITY;
-            }
-        } else if (tail) {
-            const int lim = P - kb * kKB;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int key = (i >> 2) * 8 + half * 4 + (i & 3);
-                s0[i] = key < lim ? s0[i] : -INFINITY;
-                s1[i] = key + 32 < lim ? s1[i] : -INFINITY;
-            }
-        }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const bool need = mx > m_run + a.lazy_raw;
-        if (__ballot(need)) {
-            const float m_new = need ? mx : m_run;
-            const float alpha = need ? __builtin_amdgcn_exp2f((m_run - m_new) * a.c2) : 1.f;
-            l_run *= alpha;
-#pragma unroll
-            for (int d = 0; d < kD / 32; ++d)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) o[d][i] *= alpha;
-            m_run = m_new;
-        }
-        const float base = m_run == -INFINITY ? 0.f : m_run * a.c2;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            s0[i] = __builtin_amdgcn_exp2f(fmaf(s0[i], a.c2, -base));
-            s1[i] = __builtin_amdgcn_exp2f(fmaf(s1[i], a.c2, -base));
-            l_run += s0[i] + s1[i];
-        }
-        bf16x8 p[4];
-        p[0] = cvt8(s0, 0);
-        p[1] = cvt8(s0, 8);
-        p[2] = cvt8(s1, 0);
-        p[3] = cvt8(s1, 8);
-
-        // O^T (d x rows) += V^T P^T
-        {
-            const char *vt = stage + kKTile + l32 * kVRow + half * 8;
-#pragma unroll
-            for (int d = 0; d < kD / 32; ++d) {
-                const char *vrow = vt + d * 32 * kVRow;
-#pragma unroll
-                for (int st = 0; st < 4; ++st) {  // k-step: keys (st/2)*32 + (st%2)*16 ...
-                    const int key0 = (st >> 1) * 32 + (st & 1) * 16;
-                    u32x2 lo = *(const u32x2 *)(vrow + key0 * 2);
-                    u32x2 hi = *(const u32x2 *)(vrow + (key0 + 8) * 2);
-                    u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
-                    o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(w), p[st], o[d], 0, 0, 0);
-                }
-            }
-        }
-
-        if (kbn < kb1) store_tile(smem + (buf ^ 1) * kStage, tid, tr);
-        __syncthreads();
-        buf ^= 1;
-        kb = kbn;
-        word = word_n;
+        run_block(a, c, s_pages, st0, a1, qf, used, kb, word, S, bad);
+        lds_t *t = st0;
+        st0 = st1;
+        st1 = t;
+        const uint32_t ta = a0;
+        a0 = a1;
+        a1 = ta;
     }
 
-    if (bad_page) s_bad = 1;  // benign race: every writer stores 1
-    l_run += __shfl_xor(l_run, 32);
+    if (bad) s_bad = 1;  // benign race: every writer stores 1
+    float l_run = S.l + __shfl_xor(S.l, 32);
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    const float lse_v = l_run > 0.f ? m_run * a.scale + logf(l_run) : -INFINITY;
+    const float lse_v = l_run > 0.f ? S.m * a.scale + logf(l_run) : -INFINITY;
     if (row_ok) {
         if (nchunks == 1) {
             const int64_t orow = ((int64_t)b * a.N + node) * a.Hq + hq;
@@ -358,11 +480,11 @@ __global__ __launch_bounds__(kNW * kWave) void k_tree_attn_split(AttnArgs a) {
 #pragma unroll
             for (int d = 0; d < kD / 32; ++d)
 #pragma unroll
-                for (int gi = 0; gi < 4; ++gi) {
+                for (int gq = 0; gq < 4; ++gq) {
                     u32x2 w;
-                    w[0] = pack_bf16x2(o[d][gi * 4 + 0] * inv, o[d][gi * 4 + 1] * inv);
-                    w[1] = pack_bf16x2(o[d][gi * 4 + 2] * inv, o[d][gi * 4 + 3] * inv);
-                    *(u32x2 *)(op + d * 32 + gi * 8) = w;
+                    w[0] = pack_bf16x2(S.o[d][gq * 4 + 0] * inv, S.o[d][gq * 4 + 1] * inv);
+                    w[1] = pack_bf16x2(S.o[d][gq * 4 + 2] * inv, S.o[d][gq * 4 + 3] * inv);
+                    *(u32x2 *)(op + d * 32 + gq * 8) = w;
                 }
             if (a.lse && half == 0) a.lse[orow] = lse_v;
         } else {
@@ -371,10 +493,10 @@ __global__ __launch_bounds__(kNW * kWave) void k_tree_attn_split(AttnArgs a) {
 #pragma unroll
             for (int d = 0; d < kD / 32; ++d)
 #pragma unroll
-                for (int gi = 0; gi < 4; ++gi) {
-                    f32x4 w = {o[d][gi * 4 + 0] * inv, o[d][gi * 4 + 1] * inv,
-                               o[d][gi * 4 + 2] * inv, o[d][gi * 4 + 3] * inv};
-                    *(f32x4 *)(op + d * 32 + gi * 8) = w;
+                for (int gq = 0; gq < 4; ++gq) {
+                    f32x4 w = {S.o[d][gq * 4 + 0] * inv, S.o[d][gq * 4 + 1] * inv,
+                               S.o[d][gq * 4 + 2] * inv, S.o[d][gq * 4 + 3] * inv};
+                    *(f32x4 *)(op + d * 32 + gq * 8) = w;
                 }
             if (half == 0) a.part_lse[prow] = lse_v;
         }
@@ -517,9 +639,10 @@ __global__ __launch_bounds__(256) void k_tree_attn_f32(AttnArgsF32 a) {
 // Split planning.  Every (sequence, KV head, query tile) is a row of blocks;
 // cut all rows into splits of the same block count so that about two
 // workgroups per compute unit come out, never less than two blocks a split.
-void plan_tree_attn(AttnPlan &p, int B, int N, int Hq, int Hkv, int D,
+void plan_tree_attn(AttnPlan &p, int B, int N, int Hq, int Hkv, int D, int page_size,
                     const int32_t *prefix_len, jf_dtype dtype) {
     p.B = B; p.N = N; p.Hq = Hq; p.Hkv = Hkv; p.D = D;
+    p.page_size = page_size;
     p.G = Hq / Hkv;
     p.R = N * p.G;
     p.W = (N + 63) / 64;
@@ -538,6 +661,14 @@ void plan_tree_attn(AttnPlan &p, int B, int N, int Hq, int Hkv, int D,
     const int64_t target = 2 * (int64_t)num_cus();
     int64_t cb = (units + target - 1) / target;
     if (cb < 2) cb = 2;
+    // a split's page ids must fit the LDS staging array
+    int64_t Pmax = 0;
+    for (int b = 0; b < B; ++b) Pmax = prefix_len[b] > Pmax ? prefix_len[b] : Pmax;
+    if (page_size < Pmax) {
+        int64_t cap = ((int64_t)(kPageLds - 2) * page_size) / kKB;
+        if (cap < 1) cap = 1;
+        if (cb > cap) cb = cap;
+    }
     if (cb > max_blocks) cb = max_blocks;
     if (dtype == JF_F32) cb = max_blocks;  // the fp32 path does not split
     p.chunk_blocks = (int)cb;
@@ -583,9 +714,25 @@ hipError_t launch_tree_attn_bf16(const AttnPlan &p, const void *q, const void *k
     a.part_o = p.any_split ? (float *)workspace : nullptr;
     a.part_lse = p.any_split ? (float *)((char *)workspace + obytes) : nullptr;
     a.page_status = page_status;
+    a.q_bytes = (uint32_t)((int64_t)p.B * p.N * p.Hq * kD * 2);
+    a.tree_bytes = (uint32_t)((int64_t)p.B * p.N * p.Hkv * kD * 2);
+    a.cache_bytes = (uint32_t)(num_pages * page_size * (int64_t)p.Hkv * kD * 2);
+    a.mask_bytes = (uint32_t)((int64_t)p.B * p.N * p.W * 8);
     a.num_pages = num_pages;
     a.page_size = page_size;
+    a.page_shift = -1;
+    if ((page_size & (page_size - 1)) == 0) {
+        int sh = 0;
+        while ((1 << sh) < page_size) ++sh;
+        a.page_shift = sh;
+    }
     a.max_pages = max_pages;
+    {
+        int Pmax = 0;
+        for (int b = 0; b < p.B; ++b) Pmax = p.prefix_len[b] > Pmax ? p.prefix_len[b] : Pmax;
+        a.page_mode = (max_pages == 1 && page_size >= Pmax) ? 1
+                      : (a.page_shift >= 4 ? 2 : 0);
+    }
     a.B = p.B; a.N = p.N; a.Hq = p.Hq; a.Hkv = p.Hkv; a.G = p.G; a.R = p.R; a.W = p.W;
     a.n_qt = p.n_qt;
     a.chunk_blocks = p.chunk_blocks;

@@ -57,7 +57,7 @@ def lib():
     L.jf_fuse_proj.argtypes = [P, I32, I64, I64, I64, P, I64, ctypes.c_int, P, ctypes.c_int,
                                P, SZ, P]
     L.jf_fuse_proj.restype = ctypes.c_int
-    L.jf_tree_attn_workspace_size.argtypes = [I32, I32, I32, I32, I32, P, ctypes.c_int]
+    L.jf_tree_attn_workspace_size.argtypes = [I32, I32, I32, I32, I32, I32, P, ctypes.c_int]
     L.jf_tree_attn_workspace_size.restype = SZ
     L.jf_tree_attn_fwd.argtypes = [P, P, P, P, P, P, I64, I32, P, I32, P, I32, I32, I32, I32, I32,
                                    ctypes.c_float, ctypes.c_int, P, P, P, SZ, P, P]
@@ -161,10 +161,10 @@ def _host_i32(a) -> np.ndarray:
     return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
 
 
-def jf_tree_attn_workspace_size(B: int, N: int, Hq: int, Hkv: int, D: int, prefix_len,
-                                dtype: int) -> int:
+def jf_tree_attn_workspace_size(B: int, N: int, Hq: int, Hkv: int, D: int, page_size: int,
+                                prefix_len, dtype: int) -> int:
     pl = _host_i32(prefix_len)
-    return int(lib().jf_tree_attn_workspace_size(B, N, Hq, Hkv, D,
+    return int(lib().jf_tree_attn_workspace_size(B, N, Hq, Hkv, D, page_size,
                                                  pl.ctypes.data_as(ctypes.c_void_p), dtype))
 
 
@@ -187,7 +187,7 @@ def jf_tree_attn_fwd(q, k_tree, v_tree, mask, k_cache, v_cache, block_table, pre
         out = torch.empty_like(q)
     if lse is None and with_lse:
         lse = torch.empty((B, N, Hq), dtype=torch.float32, device=q.device)
-    need = jf_tree_attn_workspace_size(B, N, Hq, Hkv, D, pl, dt)
+    need = jf_tree_attn_workspace_size(B, N, Hq, Hkv, D, page_size, pl, dt)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
