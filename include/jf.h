@@ -166,7 +166,9 @@ jf_status jf_tree_attn_fwd(const void *q, const void *k_tree,
  *          lower index; -0 and +0 are equal.
  *   val    [R, k] fp32: the selected values.
  *   lse    [R] fp32 or NULL: log sum_v exp(logits[r, v]).
- *   1 <= k <= 64, k <= V.
+ *   1 <= k <= 64, k <= V, and ceil(V / S) * k <= 4096 with S = 9728 (bf16)
+ *   or 4864 (fp32): V up to 311296 at k = 64 for fp32, about 4.9 million at
+ *   k = 8 for bf16; else JF_ERR_UNSUPPORTED.
  *   workspace: jf_node_topk_workspace_size() bytes.
  * ------------------------------------------------------------------------ */
 size_t jf_node_topk_workspace_size(int64_t R, int64_t V, int32_t k);

@@ -176,9 +176,13 @@ jf_status jf_tree_attn_fwd(const void *q, const void *k_tree, const void *v_tree
 // ---------------------------------------------------------------------------
 size_t jf_node_topk_workspace_size(int64_t R, int64_t V, int32_t k) {
     if (R < 1 || V < 1 || k < 1 || k > 64 || k > V || V > INT32_MAX) return 0;
-    TopkPlan p;
-    plan_topk(p, R, V, k);
-    return topk_workspace_bytes(p);
+    // the fp32 plan has the most slices; its workspace also fits the bf16 plan
+    TopkPlan p, pb;
+    plan_topk(p, R, V, k, JF_F32);
+    plan_topk(pb, R, V, k, JF_BF16);
+    if (p.chunks == 0 && pb.chunks == 0) return 0;
+    size_t a = p.chunks > 0 ? topk_workspace_bytes(p) : 0, b = pb.chunks > 0 ? topk_workspace_bytes(pb) : 0;
+    return a > b ? a : b;
 }
 
 jf_status jf_node_topk(const void *logits, int64_t R, int64_t V, int64_t ld, jf_dtype dtype,
@@ -192,7 +196,8 @@ jf_status jf_node_topk(const void *logits, int64_t R, int64_t V, int64_t ld, jf_
     if (!aligned(logits, 16) || ld % (dtype == JF_BF16 ? 8 : 4) != 0) return JF_ERR_ALIGN;
     if (!aligned(idx, 4) || !aligned(val, 4) || (lse && !aligned(lse, 4))) return JF_ERR_ALIGN;
     TopkPlan p;
-    plan_topk(p, R, V, k);
+    plan_topk(p, R, V, k, dtype);
+    if (p.chunks == 0) return JF_ERR_UNSUPPORTED;   // V too large for k slices to merge
     const size_t need = topk_workspace_bytes(p);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return JF_ERR_WORKSPACE;
     hipError_t e = launch_topk(p, logits, ld, dtype, idx, val, lse, workspace, (hipStream_t)stream);

@@ -88,7 +88,7 @@ struct TopkPlan {
     int chunks;        // splits of each row
     int64_t chunk_len; // elements per split (multiple of 512)
 };
-void plan_topk(TopkPlan &p, int64_t R, int64_t V, int k);
+void plan_topk(TopkPlan &p, int64_t R, int64_t V, int k, jf_dtype dtype);
 size_t topk_workspace_bytes(const TopkPlan &p);
 hipError_t launch_topk(const TopkPlan &p, const void *logits, int64_t ld, jf_dtype dtype,
                        int32_t *idx, float *val, float *lse, void *workspace, hipStream_t s);

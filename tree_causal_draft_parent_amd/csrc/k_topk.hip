@@ -24,9 +24,10 @@ namespace jf {
 namespace {
 
 constexpr int kT1Waves = 4;
-constexpr int kCap = 512;     // candidate buffer entries per wave
-constexpr int kUnroll = 4;    // 16-byte vectors in flight per lane
+constexpr int kCap = 576;     // survivors a wave can buffer before the register fallback
+constexpr int kMaxVec = 19;   // 16-byte vectors per lane a wave holds in registers
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazy = 5.545177444479562f;   // 8 * ln 2: rescale the running sum past 2^8
 
 __device__ __forceinline__ uint32_t ordered_bits(float x) {
     uint32_t u = __float_as_uint(x);
@@ -41,33 +42,65 @@ __device__ __forceinline__ uint64_t make_key(float x, uint32_t idx) {
     return ((uint64_t)ordered_bits(x) << 32) | (uint64_t)(~idx);
 }
 
+// DPP lane moves within 16-lane rows (quad_perm [1,0,3,2], [2,3,0,1],
+// row_half_mirror, row_mirror): after the four steps every lane holds the
+// maximum of its row.
+template <int kCtrl>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+    const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)v, kCtrl, 0xf, 0xf, false);
+    const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(v >> 32), kCtrl, 0xf, 0xf, false);
+    return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// Maximum over the wavefront, returned to every lane (wave-uniform).
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+    v = umax64(v, dpp_u64<0xb1>(v));
+    v = umax64(v, dpp_u64<0x4e>(v));
+    v = umax64(v, dpp_u64<0x141>(v));
+    v = umax64(v, dpp_u64<0x140>(v));
+    uint64_t r = 0;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        uint32_t lo = __shfl_xor((uint32_t)v, off);
-        uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off);
-        uint64_t o = ((uint64_t)hi << 32) | lo;
-        v = o > v ? o : v;
+    for (int row = 0; row < 4; ++row) {
+        const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, row * 16);
+        const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), row * 16);
+        r = umax64(r, ((uint64_t)hi << 32) | lo);
     }
-    return v;
+    return r;
 }
 
-// Select the k best keys among buf[0..n); lanes 0..k-1 receive them in order.
-// Returns the key held by this lane (0 for lanes >= min(k, n)).
-__device__ uint64_t wave_select(const uint64_t *buf, int n, int k, int lane) {
-    uint64_t mine = 0, prev = ~0ull;
-    const int rounds = n < k ? n : k;
-    for (int t = 0; t < rounds; ++t) {
-        uint64_t best = 0;
-        for (int e = lane; e < n; e += kWave) {
-            uint64_t x = buf[e];
-            best = (x < prev && x > best) ? x : best;
-        }
-        best = wave_max_u64(best);
+// The k largest of the keys c[0..kPer) held by each lane (unique, nonzero keys;
+// 0 marks an empty slot): lanes 0..k-1 receive them in descending order.
+// Returns this lane's pick and, through kth, the k-th largest (0 if fewer).
+template <int kPer>
+__device__ uint64_t wave_select(const uint64_t *c, int k, int lane, uint64_t &kth) {
+    uint64_t mine = 0, prev = ~0ull, best = 0;
+    for (int t = 0; t < k; ++t) {
+        uint64_t m = 0;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) m = (c[j] < prev && c[j] > m) ? c[j] : m;
+        best = wave_max_u64(m);
         if (lane == t) mine = best;
         prev = best;
+        if (best == 0) break;
     }
+    kth = best;
     return mine;
+}
+
+// Rank of `key` among the n keys in LDS (the number of larger ones; keys are
+// unique).  Every lane reads the same entries, so each read is a broadcast.
+__device__ __forceinline__ int rank_in(const uint64_t *keys, int n, uint64_t key) {
+    int rank = 0;
+    int j = 0;
+#pragma unroll 4
+    for (; j + 2 <= n; j += 2) {
+        const u32x4 q = *(const u32x4 *)(keys + j);       // keys j, j+1 (16-byte aligned)
+        rank += (((uint64_t)q[1] << 32) | q[0]) > key;
+        rank += (((uint64_t)q[3] << 32) | q[2]) > key;
+    }
+    if (j < n) rank += keys[j] > key;
+    return rank;
 }
 
 template <typename T> struct Vec;
@@ -94,7 +127,7 @@ template <typename T, bool kLse>
 __global__ __launch_bounds__(kT1Waves * kWave) void k_topk_stage1(
     const T *__restrict__ logits, int64_t ld, int64_t V, int64_t chunk_len, int chunks, int64_t R,
     int k, uint64_t *__restrict__ cand, float2 *__restrict__ stats) {
-    __shared__ uint64_t sbuf[kT1Waves][kCap];
+    __shared__ __attribute__((aligned(16))) uint64_t sbuf[kT1Waves][kCap];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int64_t gw = (int64_t)blockIdx.x * kT1Waves + wv;
     if (gw >= R * chunks) return;  // whole wave leaves; no block barriers below
@@ -106,100 +139,190 @@ __global__ __launch_bounds__(kT1Waves * kWave) void k_topk_stage1(
     uint64_t *buf = sbuf[wv];
 
     constexpr int VEC = Vec<T>::n;
-    constexpr int PER_ITER = kWave * VEC * kUnroll;
-    float tv = -INFINITY;       // threshold value (k-th best so far)
-    uint32_t ti = 0xffffffffu;  // and its index
-    int n = 0;                  // buffered candidates
-    float m = -INFINITY, s = 0.f;
+    constexpr int STEP = kWave * VEC;          // elements per wave-wide vector
+    constexpr int MAXV = kMaxVec;              // vectors per lane held in registers
+    typedef typename Vec<T>::raw Raw;
+    const int nv = (int)((end - start) / STEP);   // whole vectors (<= MAXV by the plan)
+    const int64_t tail0 = start + (int64_t)nv * STEP;
 
-    auto flush = [&]() {
-        uint64_t mine = wave_select(buf, n, k, lane);
-        const int kept = n < k ? n : k;
-        if (lane < kept) buf[lane] = mine;
-        if (n >= k) {
-            uint64_t kth = __shfl(mine, k - 1);
-            tv = ordered_to_float((uint32_t)(kth >> 32));
-            ti = ~(uint32_t)kth;
-        }
-        n = kept;
-    };
-
-    auto consider = [&](float x, uint32_t idx, bool valid) {
-        bool pass = valid && ((x > tv) || (x == tv && idx < ti));
-        uint64_t bal = __ballot(pass);
-        if (bal) {
-            if (n + kWave > kCap) flush();
-            // re-test against a possibly raised threshold
-            pass = valid && ((x > tv) || (x == tv && idx < ti));
-            bal = __ballot(pass);
-            if (pass) {
-                int pos = n + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
-                                                        __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
-                buf[pos] = make_key(x, idx);
-            }
-            n += __popcll(bal);
-        }
-    };
-
-    auto lse_update = [&](const float *x, int cnt) {
-        float mx = m;
+    // ---- all loads in flight at once ----
+    Raw d[MAXV];
 #pragma unroll
-        for (int j = 0; j < VEC; ++j) if (j < cnt) mx = fmaxf(mx, x[j]);
-        const float base = mx == -INFINITY ? 0.f : mx * kLog2e;
-        float acc = s * __builtin_amdgcn_exp2f(m * kLog2e - base);
+    for (int v = 0; v < MAXV; ++v)
+        if (v < nv) d[v] = *(const Raw *)(row + start + (int64_t)v * STEP + (int64_t)lane * VEC);
+    float tx[VEC];                             // tail: element tail0 + lane + 64 t
+    int ntail = 0;
+#pragma unroll
+    for (int t = 0; t < VEC; ++t) {
+        const int64_t e = tail0 + lane + (int64_t)t * kWave;
+        tx[t] = e < end ? Vec<T>::scalar(row + e) : -INFINITY;
+    }
+    ntail = (int)(end - tail0);                // 0 .. STEP-1, wave-uniform
+
+    // ---- pass 1: lane maximum and the running log-sum-exp ----
+    float lmax = -INFINITY;
+    float m = -INFINITY, s = 0.f;
+    auto lse_add = [&](const float *x, float vmax, int cnt) {
+        if (vmax > m + kLazy) {
+            s *= __builtin_amdgcn_exp2f((m - vmax) * kLog2e);
+            m = vmax;
+        }
+        const float base = m == -INFINITY ? 0.f : m * kLog2e;
 #pragma unroll
         for (int j = 0; j < VEC; ++j)
-            if (j < cnt) acc += __builtin_amdgcn_exp2f(fmaf(x[j], kLog2e, -base));
-        s = acc;
-        m = mx;
+            if (j < cnt) s += __builtin_amdgcn_exp2f(fmaf(x[j], kLog2e, -base));
     };
-
-    int64_t base = start;
-    // full iterations: every lane has kUnroll whole vectors
-    for (; base + PER_ITER <= end; base += PER_ITER) {
-        typename Vec<T>::raw raw[kUnroll];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-            raw[u] = *(const typename Vec<T>::raw *)(row + base + (int64_t)(u * kWave + lane) * VEC);
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
+    for (int v = 0; v < MAXV; ++v) {
+        if (v < nv) {
             float x[VEC];
-            Vec<T>::unpack(raw[u], x);
-            const uint32_t i0 = (uint32_t)(base + (int64_t)(u * kWave + lane) * VEC);
-            if (kLse) lse_update(x, VEC);
-            // fast reject of the whole vector
+            Vec<T>::unpack(d[v], x);
             float vmax = x[0];
 #pragma unroll
             for (int j = 1; j < VEC; ++j) vmax = fmaxf(vmax, x[j]);
-            bool any = vmax > tv || vmax == tv;
-            if (__ballot(any)) {
+            lmax = fmaxf(lmax, vmax);
+            if (kLse) lse_add(x, vmax, VEC);
+        }
+    }
+    if (kLse && ntail > 0) {
 #pragma unroll
-                for (int j = 0; j < VEC; ++j) consider(x[j], i0 + j, true);
+        for (int t = 0; t < VEC; ++t) {
+            const bool ok = lane + t * kWave < ntail;
+            float x1 = ok ? tx[t] : -INFINITY;
+            if (ok) lse_add(&x1, x1, 1);
+        }
+    }
+
+    // Make the raw vectors look modified so that the compiler recomputes the
+    // unpacked values in pass 2 instead of keeping them all live from pass 1.
+    auto touch = [&]() {
+#pragma unroll
+        for (int v = 0; v < MAXV; ++v) asm volatile("" : "+v"(d[v]));
+    };
+    touch();
+
+    // ---- threshold: a lower bound on the slice's k-th largest element ----
+    // At least k elements are >= tv, so every element below it is out.
+    float tv = -INFINITY;
+    if (nv > 0) {
+        // the k-th largest lane maximum (ties ordered by lane): each lane
+        // counts the maxima above its own, reading four at a time
+        float *fb = (float *)buf;
+        fb[lane] = lmax;
+        int rk = 0;
+#pragma unroll 4
+        for (int j = 0; j < kWave; j += 4) {
+            const f32x4 q = *(const f32x4 *)(fb + j);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) rk += (q[u] > lmax) || (q[u] == lmax && j + u < lane);
+        }
+        const uint64_t hit = __ballot(rk == k - 1);
+        tv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lmax), __builtin_ctzll(hit)));
+    }
+
+    // ---- pass 2: mark survivors (x >= tv) and count them ----
+    uint32_t marks[(MAXV * VEC + 31) / 32];
+#pragma unroll
+    for (int w = 0; w < (MAXV * VEC + 31) / 32; ++w) marks[w] = 0u;
+    int cnt = 0;
+    if (VEC == 8 && tv > 0.f) {
+        // bf16 with a positive threshold: x >= tv exactly when x's bit pattern,
+        // read as a signed integer, is >= tv's (negative values and -0 read as
+        // negative integers), and tv's low 16 bits are zero, so each packed
+        // word is tested without unpacking.
+        const int32_t tb = __float_as_int(tv);
+#pragma unroll
+        for (int v = 0; v < MAXV; ++v) {
+            if (v < nv) {
+                uint32_t pm = 0;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const uint32_t word = (uint32_t)d[v][w];
+                    pm |= (uint32_t)((int32_t)(word << 16) >= tb) << (2 * w);
+                    pm |= (uint32_t)((int32_t)word >= tb) << (2 * w + 1);
+                }
+                marks[(v * VEC) / 32] |= pm << ((v * VEC) % 32);
+                cnt += __popc(pm);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int v = 0; v < MAXV; ++v) {
+            if (v < nv) {
+                float x[VEC];
+                Vec<T>::unpack(d[v], x);
+                uint32_t pm = 0;
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) pm |= (uint32_t)(x[j] >= tv) << j;
+                marks[(v * VEC) / 32] |= pm << ((v * VEC) % 32);
+                cnt += __popc(pm);
             }
         }
     }
-    // one whole vector per lane
-    for (; base + kWave * VEC <= end; base += kWave * VEC) {
-        typename Vec<T>::raw raw = *(const typename Vec<T>::raw *)(row + base + (int64_t)lane * VEC);
-        float x[VEC];
-        Vec<T>::unpack(raw, x);
-        const uint32_t i0 = (uint32_t)(base + (int64_t)lane * VEC);
-        if (kLse) lse_update(x, VEC);
+    uint32_t tmark = 0;
 #pragma unroll
-        for (int j = 0; j < VEC; ++j) consider(x[j], i0 + j, true);
+    for (int t = 0; t < VEC; ++t)
+        tmark |= (uint32_t)(lane + t * kWave < ntail && tx[t] >= tv) << t;
+    cnt += __popc(tmark);
+
+    // ---- compaction: one wave prefix sum places every survivor ----
+    int pre = 0, tot = 0;
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit) {        // cnt <= MAXV*VEC + VEC < 256
+        const uint64_t b = __ballot((cnt >> bit) & 1);
+        pre += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0)) << bit;
+        tot += __popcll(b) << bit;
     }
-    // tail: element-wise, bounds-checked
-    for (; base < end; base += kWave) {
-        const int64_t e = base + lane;
-        const bool valid = e < end;
-        float x = valid ? Vec<T>::scalar(row + e) : -INFINITY;
-        if (kLse && valid) lse_update(&x, 1);
-        consider(x, (uint32_t)e, valid);
-    }
-    flush();
-    // write this slice's k best (padding with key 0 when the slice is short)
     uint64_t *out = cand + ((int64_t)r * chunks + c) * k;
-    for (int t = lane; t < k; t += kWave) out[t] = t < n ? buf[t] : 0ull;
+    if (tot <= kCap) {
+        int pos = pre;
+#pragma unroll
+        for (int v = 0; v < MAXV; ++v) {
+            uint32_t pm = (marks[(v * VEC) / 32] >> ((v * VEC) % 32)) & ((1u << VEC) - 1u);
+            if (v < nv && __ballot(pm != 0)) {
+                const uint32_t i0 = (uint32_t)(start + (int64_t)v * STEP + (int64_t)lane * VEC);
+                while (pm) {                   // survivors are rare: visit set bits only
+                    const int j = __builtin_ctz(pm);
+                    pm &= pm - 1u;
+                    const u32x4 raw = __builtin_bit_cast(u32x4, d[v]);
+                    uint32_t bits;
+                    if (VEC == 8) {
+                        const uint32_t word = raw[j >> 1];
+                        bits = (j & 1) ? (word & 0xffff0000u) : (word << 16);
+                    } else {
+                        bits = raw[j & 3];
+                    }
+                    buf[pos++] = make_key(__uint_as_float(bits), i0 + j);
+                }
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < VEC; ++t)
+            if ((tmark >> t) & 1u) buf[pos++] = make_key(tx[t], (uint32_t)(tail0 + lane + t * kWave));
+        // every buffered survivor learns its rank; the k best write themselves
+        for (int e = lane; e < tot; e += kWave) {
+            const uint64_t key = buf[e];
+            const int rk = rank_in(buf, tot, key);
+            if (rk < k) out[rk] = key;
+        }
+        for (int e = tot + lane; e < k; e += kWave) out[e] = 0ull;   // short slice
+    } else {
+        // Too many ties at the threshold for the buffer (rare): select straight
+        // from memory, k rounds of "best key below the previous pick".  Kept
+        // out of registers on purpose so that it costs the common path nothing.
+        uint64_t prev = ~0ull, mine = 0;
+        for (int t = 0; t < k; ++t) {
+            uint64_t best = 0;
+            for (int64_t e = start + lane; e < end; e += kWave) {
+                const uint64_t kk = make_key(Vec<T>::scalar(row + e), (uint32_t)e);
+                best = (kk < prev && kk > best) ? kk : best;
+            }
+            best = wave_max_u64(best);
+            if (lane == t) mine = best;
+            prev = best;
+        }
+        if (lane < k) out[lane] = mine;
+    }
     if (kLse) {
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) {
@@ -213,29 +336,34 @@ __global__ __launch_bounds__(kT1Waves * kWave) void k_topk_stage1(
     }
 }
 
-constexpr int kMaxCand = 4096;
+constexpr int kMaxCand = 4096;   // chunks * k candidates merged per row
 
 template <bool kLse>
-__global__ __launch_bounds__(kWave) void k_topk_stage2(const uint64_t *__restrict__ cand,
-                                                      const float2 *__restrict__ stats, int chunks,
-                                                      int k, int32_t *__restrict__ idx,
-                                                      float *__restrict__ val,
-                                                      float *__restrict__ lse) {
-    __shared__ uint64_t buf[kMaxCand];
-    const int lane = threadIdx.x;
+__global__ __launch_bounds__(256) void k_topk_stage2(const uint64_t *__restrict__ cand,
+                                                    const float2 *__restrict__ stats, int chunks,
+                                                    int k, int32_t *__restrict__ idx,
+                                                    float *__restrict__ val,
+                                                    float *__restrict__ lse) {
+    __shared__ __attribute__((aligned(16))) uint64_t keys[kMaxCand];
+    __shared__ float2 part[4];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int64_t r = blockIdx.x;
-    const int n = chunks * k;
+    const int n = chunks * k;                    // <= kMaxCand
     const uint64_t *src = cand + r * (int64_t)n;
-    for (int e = lane; e < n; e += kWave) buf[e] = src[e];
+    for (int e = tid; e < n; e += 256) keys[e] = src[e];
     __syncthreads();
-    uint64_t mine = wave_select(buf, n, k, lane);
-    if (lane < k) {
-        idx[r * k + lane] = (int32_t)(~(uint32_t)mine);
-        val[r * k + lane] = ordered_to_float((uint32_t)(mine >> 32));
+    for (int e = tid; e < n; e += 256) {
+        const uint64_t key = keys[e];
+        if (key == 0ull) continue;               // padding of a short slice
+        const int rk = rank_in(keys, n, key);
+        if (rk < k) {
+            idx[r * k + rk] = (int32_t)(~(uint32_t)key);
+            val[r * k + rk] = ordered_to_float((uint32_t)(key >> 32));
+        }
     }
     if (kLse) {
         float m = -INFINITY, s = 0.f;
-        for (int c = lane; c < chunks; c += kWave) {
+        for (int c = tid; c < chunks; c += 256) {
             float2 st = stats[r * chunks + c];
             float mn = fmaxf(m, st.x);
             float bn = mn == -INFINITY ? 0.f : mn * kLog2e;
@@ -250,24 +378,45 @@ __global__ __launch_bounds__(kWave) void k_topk_stage2(const uint64_t *__restric
             s = s * __builtin_amdgcn_exp2f(m * kLog2e - bn) + so * __builtin_amdgcn_exp2f(mo * kLog2e - bn);
             m = mn;
         }
-        if (lane == 0) lse[r] = m == -INFINITY ? -INFINITY : m + logf(s);
+        if (lane == 0) part[wv] = make_float2(m, s);
+        __syncthreads();
+        if (tid == 0) {
+            m = -INFINITY;
+            s = 0.f;
+            for (int w = 0; w < 4; ++w) {
+                float mn = fmaxf(m, part[w].x);
+                float bn = mn == -INFINITY ? 0.f : mn * kLog2e;
+                s = s * __builtin_amdgcn_exp2f(m * kLog2e - bn) +
+                    part[w].y * __builtin_amdgcn_exp2f(part[w].x * kLog2e - bn);
+                m = mn;
+            }
+            lse[r] = m == -INFINITY ? -INFINITY : m + logf(s);
+        }
     }
 }
 
 }  // namespace
 
-void plan_topk(TopkPlan &p, int64_t R, int64_t V, int k) {
+void plan_topk(TopkPlan &p, int64_t R, int64_t V, int k, jf_dtype dtype) {
     p.R = R;
     p.V = V;
     p.k = k;
-    int64_t chunks = (4096 + R - 1) / R;  // aim for >= 4096 wavefronts
+    // a slice must fit one wave's registers: kMaxVec 16-byte vectors a lane
+    const int64_t max_len = (int64_t)kMaxVec * kWave * (dtype == JF_BF16 ? 8 : 4);
+    int64_t chunks = (2048 + R - 1) / R;  // aim for >= 2048 wavefronts
+    if (chunks > kMaxCand / k) chunks = kMaxCand / k;
     if (chunks < 1) chunks = 1;
-    if (chunks > 64) chunks = 64;
-    if (chunks * k > kMaxCand) chunks = kMaxCand / k;
     int64_t len = (V + chunks - 1) / chunks;
     len = (len + 511) / 512 * 512;
+    if (len > max_len) len = max_len;
+    chunks = (V + len - 1) / len;
+    if (chunks * k > kMaxCand) {          // too many slices to merge: the plan is refused
+        p.chunks = 0;
+        p.chunk_len = 0;
+        return;
+    }
     p.chunk_len = len;
-    p.chunks = (int)((V + len - 1) / len);
+    p.chunks = (int)chunks;
 }
 
 size_t topk_workspace_bytes(const TopkPlan &p) {
@@ -303,10 +452,10 @@ hipError_t launch_topk(const TopkPlan &p, const void *logits, int64_t ld, jf_dty
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (with_lse)
-        hipLaunchKernelGGL((k_topk_stage2<true>), dim3((unsigned)p.R), dim3(kWave), 0, s, cand, stats,
+        hipLaunchKernelGGL((k_topk_stage2<true>), dim3((unsigned)p.R), dim3(256), 0, s, cand, stats,
                            p.chunks, p.k, idx, val, lse);
     else
-        hipLaunchKernelGGL((k_topk_stage2<false>), dim3((unsigned)p.R), dim3(kWave), 0, s, cand, stats,
+        hipLaunchKernelGGL((k_topk_stage2<false>), dim3((unsigned)p.R), dim3(256), 0, s, cand, stats,
                            p.chunks, p.k, idx, val, lse);
     return hipGetLastError();
 }
