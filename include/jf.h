@@ -96,7 +96,8 @@ jf_status jf_tree_mask_build(const int32_t *parent, int32_t B, int32_t N,
  *   out_dtype JF_F32 or JF_BF16 (bf16 inputs) / JF_F32 (fp32 inputs).
  *   1 <= k <= 8; H_in % 64 == 0 for bf16; ldx % 8 == 0 for bf16.
  *   Alignment: bf16 x and w 16 bytes, y 16 (fp32 out) or 8 (bf16 out);
- *   fp32 inputs need only 4-byte alignment.
+ *   fp32 inputs need only 4-byte alignment.  bf16: each x[l] and w must
+ *   span less than 3.75 GiB (32-bit buffer offsets), else JF_ERR_UNSUPPORTED.
  *   workspace: jf_fuse_proj_workspace_size() bytes (may be 0 -> NULL ok).
  * ------------------------------------------------------------------------ */
 size_t jf_fuse_proj_workspace_size(int64_t M, int64_t H_in, int32_t k,

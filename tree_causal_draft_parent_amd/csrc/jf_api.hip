@@ -92,6 +92,12 @@ jf_status jf_fuse_proj(const void *const *x, int32_t k, int64_t M, int64_t H_in,
     if (!aligned(w, a) || !aligned(y, in_dtype == JF_BF16 ? (out_dtype == JF_BF16 ? 8 : 16) : 4))
         return JF_ERR_ALIGN;
     if (in_dtype == JF_BF16 && ldx % 8 != 0) return JF_ERR_ALIGN;
+    if (in_dtype == JF_BF16) {
+        // 32-bit buffer offsets with room for the K position: each operand < 3.75 GiB
+        const int64_t lim = 0xf0000000LL;
+        if (((M - 1) * ldx + H_in) * 2 > lim || H_out * (int64_t)k * H_in * 2 > lim)
+            return JF_ERR_UNSUPPORTED;
+    }
     FusePlan p;
     plan_fuse(p, M, H_in, k, H_out, in_dtype);
     const size_t need = fuse_workspace_bytes(p);

@@ -41,6 +41,49 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
     return xcd * q + (xcd < rem ? xcd : rem) + local;
 }
 
+typedef __attribute__((address_space(3))) char lds_t;
+
+// Buffer resource over [p, p + bytes): loads past the end return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
+}
+constexpr uint32_t kOob = 0xffffff00u;  // an offset past every buffer (reads as zeros)
+
+// One 16-byte-per-lane copy HBM -> LDS: lane L's 16 bytes land at lds + 16 L
+// (lds must be wave-uniform).  Issued as inline asm so that the compiler does
+// not order later LDS reads of another stage behind it; completion is waited
+// for explicitly with stage_barrier().
+__device__ __forceinline__ void copy16(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(r) : "memory");
+}
+
+// Wait for this wave's outstanding memory operations, then barrier: every
+// wave's copies into the current stage have landed and no wave still reads
+// the other stage.  The wait is the s_waitcnt builtin (not asm) so that the
+// compiler knows every older load is complete; the empty asm is a compiler
+// fence for memory.
+__device__ __forceinline__ void stage_barrier() {
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Wait until at most n vector-memory operations of this wave are outstanding
+// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt
+// left at their maxima), then barrier.  Used by multi-stage copy rings where
+// later stages' copies stay in flight.
+template <int kN>
+__device__ __forceinline__ void ring_barrier() {
+    static_assert(kN >= 0 && kN < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((kN & 0xf) | ((kN >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS reads are done
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
 // Device properties cached once per process and device.
 int num_cus();
 

@@ -75,7 +75,6 @@ struct AttnArgs {
 };
 
 constexpr int kPageLds = 1024;     // page ids of one split staged in LDS
-constexpr uint32_t kOob = 0xffffff00u;  // offset past every buffer: loads return zeros
 
 __device__ __forceinline__ int find_seq(const AttnArgs &a, int cg) {
     int lo = 0, hi = a.B - 1;
@@ -86,11 +85,8 @@ __device__ __forceinline__ int find_seq(const AttnArgs &a, int cg) {
     return lo;
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
-}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, uint32_t bytes) { return make_rsrc(p, bytes); }
 
-typedef __attribute__((address_space(3))) char lds_t;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // Byte offset of (key row, 16-byte chunk) of block kb in its buffer, or kOob.
@@ -126,8 +122,6 @@ __device__ __forceinline__ uint32_t row_offset(const AttnArgs &a, const int *pag
 __device__ __forceinline__ int k_lds(int r) { return (r & 15) * kKBlk + (r >> 4) * kRow; }
 __device__ __forceinline__ int v_lds(int r) { return (r & 15) * kVBlk + (r >> 4) * kRow; }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
-
 __device__ __forceinline__ bf16x8 cvt8(const f32x16 &s, int base) {
     u32x4 w;
 #pragma unroll
@@ -140,15 +134,6 @@ struct SplitCtx {
     int b, g, P, nPB, kb1, page0, lane, wave;
     uint32_t moff;
 };
-
-// One 16-byte-per-lane copy HBM -> LDS: lane L's 16 bytes land at lds + 16 L.
-// Issued as inline asm so that the compiler does not order later LDS reads of
-// the other stage behind it; completion is waited for explicitly (vmcnt) at
-// the next block's barrier.
-__device__ __forceinline__ void copy16(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff) {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :: "s"(lds), "v"(voff), "s"(r) : "memory");
-}
 
 // Start the copy of block kb's K and V tiles into stage `dst` (asynchronous;
 // each wave fills 4 of the 16 LDS blocks of each tile, one copy each: LDS
@@ -332,17 +317,6 @@ __device__ __forceinline__ void compute_block(const AttnArgs &a, const lds_t *__
         S.o[(idx + 1) >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb, p[(idx + 1) & 3], S.o[(idx + 1) >> 2], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
     }
-}
-
-// Wait for this wave's outstanding copies and LDS reads, then barrier: after
-// it, every wave's copies into the current stage have landed and no wave still
-// reads the other stage.  The wait is the s_waitcnt builtin (not asm) so that
-// the compiler knows every older load is complete and adds no waits of its
-// own inside the block; the empty asm is a compiler fence for memory.
-__device__ __forceinline__ void stage_barrier() {
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
 }
 
 __device__ __forceinline__ void run_block(const AttnArgs &a, const SplitCtx &c, const int *pages,

@@ -8,24 +8,27 @@
 // i.e. an NT GEMM with K = k*H_in in which the A operand's K axis hops from one
 // layer's tensor to the next every H_in columns (no concatenated copy).
 //
-// bf16 path: 128x128 output tiles, 64-deep K steps, four waves each owning a
-// 64x64 quarter as 2x2 blocks of v_mfma_f32_32x32x16_bf16.  Both operands are
-// K-contiguous in memory and in LDS (rows padded to avoid bank conflicts), so
-// the MFMA operands are plain 16-byte LDS reads.  Tiles are prefetched into
-// registers one K step ahead and double-buffered in LDS.  When the output has
-// too few tiles to fill the GPU, K is split and the slices' fp32 partials are
-// summed by a second kernel.
+// bf16 path: output tiles of 256x128 (M >= 192: every weight is read once;
+// eight waves, two per SIMD so that one covers the other's LDS and barrier
+// stalls) or 128x128 (four waves), 64-deep K steps, each wave owning 64x64 of
+// the tile as 32x32 blocks of v_mfma_f32_32x32x16_bf16.  A and B tiles go from
+// HBM straight into a double-buffered LDS stage with buffer_load ... lds (one
+// K step ahead, no registers); one copy fills 1 KiB = 8 K-contiguous rows
+// (rows n, n+T/8, ... of a T-row tile) and 16-byte block padding keeps the
+// 16-byte operand reads conflict-free.  Per-lane row offsets are computed once;
+// the K position rides in the scalar offset.  When the output has too few
+// tiles to fill the GPU, K is split and the slices' fp32 partials are summed
+// by a second kernel.
 #include "jf_internal.h"
 
 namespace jf {
 namespace {
 
-constexpr int kBM = 128, kBN = 128, kBK = 64;
-constexpr int kRowB = kBK * 2 + 16;      // bytes per LDS row (padded)
-constexpr int kTileA = kBM * kRowB;
-constexpr int kTileB = kBN * kRowB;
-constexpr int kStageB = kTileA + kTileB;
+constexpr int kBN = 128, kBK = 64;
+constexpr int kRowG = kBK * 2;           // bytes per tile row (64 bf16)
+constexpr int kBlkG = 8 * kRowG + 16;    // LDS block: 8 rows + pad
 constexpr int kMaxLayers = 8;
+constexpr uint32_t kOobRow = 0xf0000000u; // past every buffer even after adding the K offset
 
 struct FuseArgs {
     const uint16_t *x[kMaxLayers];
@@ -34,113 +37,157 @@ struct FuseArgs {
     float *part;
     int64_t M, N, H_in, ldx, K;
     int64_t k_per_split;
+    uint32_t x_bytes, w_bytes;
     int out_bf16;
     int split_k;
     int tiles_m, tiles_n;
 };
 
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ void copy16s(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff,
+                                        uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory");
+}
 
-struct GemmRegs {
-    u32x4 a[4];
-    u32x4 b[4];
+template <int BM>
+struct Cfg {
+    static constexpr int kStages = BM == 256 ? 3 : 4;   // copy ring depth (LDS <= 150 KiB)
+    static constexpr int kWaves = BM == 256 ? 8 : 4;    // 256-row tiles: two waves per SIMD
+    static constexpr int kANb = BM / 8;             // LDS blocks of the A tile
+    static constexpr int kBNb = kBN / 8;            // 16
+    static constexpr int kATile = kANb * kBlkG;
+    static constexpr int kBTile = kBNb * kBlkG;
+    static constexpr int kStage = kATile + kBTile;
+    static constexpr int WM = BM == 256 ? 4 : 2;    // waves along M
+    static constexpr int WN = kWaves / WM;          // waves along N
+    static constexpr int TM = BM / WM / 32;         // 32x32 blocks per wave along M
+    static constexpr int TN = kBN / WN / 32;        // ... along N
+    static constexpr int kACopies = kANb / kWaves;  // copies per wave per K step
+    static constexpr int kBCopies = kBNb / kWaves;
 };
 
-__device__ __forceinline__ void gemm_load(const FuseArgs &f, int64_t m0, int64_t n0, int64_t kk0,
-                                          int tid, GemmRegs &g) {
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    const int ch = tid & 7, rr = tid >> 3;
-    const int layer = (int)(kk0 / f.H_in);
-    const int64_t col = kk0 - (int64_t)layer * f.H_in + ch * 8;
-    const uint16_t *xa = f.x[layer];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int64_t m = m0 + rr + 32 * r;
-        g.a[r] = m < f.M ? *(const u32x4 *)(xa + m * f.ldx + col) : zero;
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int64_t n = n0 + rr + 32 * r;
-        g.b[r] = n < f.N ? *(const u32x4 *)(f.w + n * f.K + kk0 + ch * 8) : zero;
-    }
-}
+// LDS byte offset of row r of a tile with nb blocks
+__device__ __forceinline__ int g_lds(int r, int nb) { return (r % nb) * kBlkG + (r / nb) * kRowG; }
 
-__device__ __forceinline__ void gemm_store(char *stage, int tid, const GemmRegs &g) {
-    const int ch = tid & 7, rr = tid >> 3;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        *(u32x4 *)(stage + (rr + 32 * r) * kRowB + ch * 16) = g.a[r];
-        *(u32x4 *)(stage + kTileA + (rr + 32 * r) * kRowB + ch * 16) = g.b[r];
-    }
-}
-
-__global__ __launch_bounds__(256) void k_fuse_gemm_bf16(FuseArgs f) {
-    __shared__ __attribute__((aligned(16))) char smem[2 * kStageB];
+template <int BM>
+__global__ __launch_bounds__(Cfg<BM>::kWaves * kWave) void k_fuse_gemm_bf16(FuseArgs f) {
+    typedef Cfg<BM> C;
+    __shared__ __attribute__((aligned(1024))) char ring[C::kStages][C::kStage];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int half = lane >> 5, l32 = lane & 31;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / C::WN, wn = wave % C::WN;
 
     const int total = f.tiles_m * f.tiles_n * f.split_k;
     const int item = xcd_remap(blockIdx.x, total);
-    // tiles sharing a weight slab (same n tile) are adjacent
-    const int tm = item % f.tiles_m;
-    const int rest = item / f.tiles_m;
-    const int tn = rest % f.tiles_n;
-    const int sk = rest / f.tiles_n;
-    const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBN;
+    // the n tiles of one (m tile, K slice) are neighbours: they share A in L2
+    const int tn = item % f.tiles_n;
+    const int rest = item / f.tiles_n;
+    const int tm = rest % f.tiles_m;
+    const int sk = rest / f.tiles_m;
+    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * kBN;
     const int64_t kb = (int64_t)sk * f.k_per_split;
     const int64_t ke = min(f.K, kb + f.k_per_split);
+    const int nk = (int)((ke - kb) / kBK);
 
-    f32x16 acc[2][2];
+    // per-lane row offsets of this wave's copies (K-step independent)
+    const int sub = lane >> 3, ch = lane & 7;
+    uint32_t aoff[C::kACopies], boff[C::kBCopies];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < C::kACopies; ++i) {
+        const int n = wave * C::kACopies + i;          // block
+        const int64_t m = m0 + n + C::kANb * sub;       // row
+        aoff[i] = m < f.M ? (uint32_t)((m * f.ldx + ch * 8) * 2) : kOobRow;
+    }
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+    for (int i = 0; i < C::kBCopies; ++i) {
+        const int n = wave * C::kBCopies + i;
+        const int64_t nn = n0 + n + C::kBNb * sub;
+        boff[i] = nn < f.N ? (uint32_t)((nn * f.K + ch * 8) * 2) : kOobRow;
+    }
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(f.w, f.w_bytes);
+
+    auto issue = [&](uint32_t dst, int64_t kk) {
+        const int layer = (int)(kk / f.H_in);
+        const __amdgpu_buffer_rsrc_t rx = make_rsrc(f.x[layer], f.x_bytes);
+        const uint32_t sa = (uint32_t)((kk - (int64_t)layer * f.H_in) * 2);
+        const uint32_t sb = (uint32_t)(kk * 2);
+        const uint32_t da = __builtin_amdgcn_readfirstlane(dst + wave * C::kACopies * kBlkG);
+        const uint32_t db = __builtin_amdgcn_readfirstlane(dst + C::kATile + wave * C::kBCopies * kBlkG);
+#pragma unroll
+        for (int i = 0; i < C::kACopies; ++i) copy16s(rx, da + i * kBlkG, aoff[i], sa);
+#pragma unroll
+        for (int i = 0; i < C::kBCopies; ++i) copy16s(rw, db + i * kBlkG, boff[i], sb);
+    };
+
+    f32x16 acc[C::TM][C::TN];
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    GemmRegs g;
-    int buf = 0;
-    if (kb < ke) {
-        gemm_load(f, m0, n0, kb, tid, g);
-        gemm_store(smem, tid, g);
-    }
-    __syncthreads();
-    for (int64_t kk = kb; kk < ke; kk += kBK) {
-        const bool more = kk + kBK < ke;
-        if (more) gemm_load(f, m0, n0, kk + kBK, tid, g);
-        const char *sa = smem + buf * kStageB;
-        const char *sb = sa + kTileA;
+    // operand bases: A rows wm*(BM/WM) + i*32 + l32, B rows wn*(128/WN) + j*32 + l32
+    auto compute = [&](const lds_t *st) {
+        const lds_t *abase = st + g_lds(wm * (BM / C::WM) + l32, C::kANb) + half * 16;
+        const lds_t *bbase = st + C::kATile + g_lds(wn * (kBN / C::WN) + l32, C::kBNb) + half * 16;
+        auto rd = [&](int t, bf16x8 *av, bf16x8 *bv) {
 #pragma unroll
-        for (int t = 0; t < kBK / 16; ++t) {
-            bf16x8 av[2], bv[2];
+            for (int i = 0; i < C::TM; ++i)
+                av[i] = *(const __attribute__((address_space(3))) bf16x8 *)(abase + (i * 32 / C::kANb) * kRowG + t * 32);
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
-                av[i] = *(const bf16x8 *)(sa + (wm * 64 + i * 32 + l32) * kRowB + t * 32 + half * 16);
+            for (int j = 0; j < C::TN; ++j)
+                bv[j] = *(const __attribute__((address_space(3))) bf16x8 *)(bbase + (j * 32 / C::kBNb) * kRowG + t * 32);
+        };
+        bf16x8 a0[C::TM], b0[C::TN], a1[C::TM], b1[C::TN];
+        rd(0, a0, b0);
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-                bv[j] = *(const bf16x8 *)(sb + (wn * 64 + j * 32 + l32) * kRowB + t * 32 + half * 16);
+        for (int t = 0; t < kBK / 16; t += 2) {
+            rd(t + 1, a1, b1);
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+                for (int j = 0; j < C::TN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[i], b0[j], acc[i][j], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            if (t + 2 < kBK / 16) rd(t + 2, a0, b0);
+#pragma unroll
+            for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+                for (int j = 0; j < C::TN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[i], b1[j], acc[i][j], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        if (more) gemm_store(smem + (buf ^ 1) * kStageB, tid, g);
-        __syncthreads();
-        buf ^= 1;
+    };
+
+    // Copy ring: step i lives in stage i % NS; steps i+1 .. i+NS-1 are in
+    // flight while step i is multiplied.  Each wave issues kCopies copies a
+    // step, so "step i has landed" is "at most kCopies * (steps issued after
+    // i) copies outstanding".
+    constexpr int NS = C::kStages;
+    constexpr int kCopies = C::kACopies + C::kBCopies;
+    const uint32_t ring0 = (uint32_t)(uintptr_t)(lds_t *)&ring[0][0];
+    for (int i = 0; i < NS - 1 && i < nk; ++i) issue(ring0 + i * C::kStage, kb + (int64_t)i * kBK);
+    for (int i = 0; i < nk; ++i) {
+        const int ahead = min(NS - 2, nk - 1 - i);   // steps issued after i and still in flight
+        if (ahead >= 2) ring_barrier<2 * kCopies>();
+        else if (ahead == 1) ring_barrier<kCopies>();
+        else ring_barrier<0>();
+        if (i + NS - 1 < nk)
+            issue(ring0 + ((i + NS - 1) % NS) * C::kStage, kb + (int64_t)(i + NS - 1) * kBK);
+        compute((const lds_t *)&ring[i % NS][0]);
     }
 
     // lane holds rows (r/4)*8 + half*4 + r%4 of each 32x32 block, column l32
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int64_t n = n0 + wn * 64 + j * 32 + l32;
+        for (int j = 0; j < C::TN; ++j) {
+            const int64_t n = n0 + wn * (kBN / C::WN) + j * 32 + l32;
             if (n >= f.N) continue;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int64_t m = m0 + wm * 64 + i * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
+                const int64_t m = m0 + wm * (BM / C::WM) + i * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
                 if (m >= f.M) continue;
                 const float v = acc[i][j][r];
                 if (f.split_k > 1) {
@@ -224,7 +271,7 @@ void plan_fuse(FusePlan &p, int64_t M, int64_t H_in, int k, int64_t H_out, jf_dt
     p.H_in = H_in;
     p.H_out = H_out;
     p.k = k;
-    p.bm = kBM;
+    p.bm = M >= 192 ? 256 : 128;
     p.bn = kBN;
     const int64_t K = (int64_t)k * H_in;
     if (in_dtype != JF_BF16) {
@@ -232,8 +279,8 @@ void plan_fuse(FusePlan &p, int64_t M, int64_t H_in, int k, int64_t H_out, jf_dt
         p.k_per_split = K;
         return;
     }
-    const int64_t tiles = ((M + kBM - 1) / kBM) * ((H_out + kBN - 1) / kBN);
-    const int64_t target = 2 * (int64_t)num_cus();
+    const int64_t tiles = ((M + p.bm - 1) / p.bm) * ((H_out + kBN - 1) / kBN);
+    const int64_t target = (int64_t)num_cus();       // one 4-wave workgroup per CU
     int64_t s = (target + tiles - 1) / tiles;
     const int64_t ksteps = K / kBK;
     int64_t max_s = ksteps / 8;  // at least eight K steps per slice
@@ -263,12 +310,17 @@ hipError_t launch_fuse_bf16(const FusePlan &p, const void *const *x, int64_t ldx
     f.ldx = ldx;
     f.K = (int64_t)p.k * p.H_in;
     f.k_per_split = p.k_per_split;
+    f.x_bytes = (uint32_t)(((p.M - 1) * ldx + p.H_in) * 2);
+    f.w_bytes = (uint32_t)(p.H_out * f.K * 2);
     f.out_bf16 = out_dtype == JF_BF16;
     f.split_k = p.split_k;
-    f.tiles_m = (int)((p.M + kBM - 1) / kBM);
+    f.tiles_m = (int)((p.M + p.bm - 1) / p.bm);
     f.tiles_n = (int)((p.H_out + kBN - 1) / kBN);
     const unsigned grid = (unsigned)(f.tiles_m * f.tiles_n * f.split_k);
-    hipLaunchKernelGGL(k_fuse_gemm_bf16, dim3(grid), dim3(256), 0, s, f);
+    if (p.bm == 256)
+        hipLaunchKernelGGL(k_fuse_gemm_bf16<256>, dim3(grid), dim3(Cfg<256>::kWaves * kWave), 0, s, f);
+    else
+        hipLaunchKernelGGL(k_fuse_gemm_bf16<128>, dim3(grid), dim3(Cfg<128>::kWaves * kWave), 0, s, f);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.split_k <= 1) return e;
     const int64_t MN = p.M * p.H_out;
