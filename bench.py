@@ -44,7 +44,49 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-steps", type=int, default=20)
     ap.add_argument("--cpu-sample-nodes", type=int, default=256)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy 5 times (counter calibration)")
     return ap.parse_args()
+
+
+KERNELS = {"mask": ["k_tree_mask"],
+           "fuse": ["k_fuse_gemm_bf16", "k_fuse_reduce", "k_fuse_gemm_f32"],
+           "attn": ["k_tree_attn_split", "k_tree_attn_merge", "k_tree_attn_f32"],
+           "topk": ["k_topk_stage1", "k_topk_stage2"]}
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+COPY_BYTES = 256 * 1024 * 1024
+
+
+def copy_calibration():
+    """A plain device copy of known size, for scaling the fabric byte counters."""
+    import torch
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_each_way": COPY_BYTES, "launches": 5}), flush=True)
+
+
+def measured_traffic(call, workload):
+    """HBM-side bytes per launch of a call's kernels from the committed counter
+    record (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when there is
+    no record for this workload or the kernel sources changed since it was taken."""
+    from tree_causal_draft_parent_amd import profsum
+    try:
+        with open(TRAFFIC_JSON) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("workload") != workload or rec.get("sources_sha256") != profsum.sources_hash():
+        return None
+    total, found = 0, False
+    for k, v in rec.get("kernels", {}).items():
+        base = k.split("<")[0]
+        if base in KERNELS[call] and v.get("fetch_bytes") is not None and v.get("write_bytes") is not None:
+            total += v["fetch_bytes"] + v["write_bytes"]
+            found = True
+    return total if found else None
 
 
 def to_dev(a, dtype, torch):
@@ -80,9 +122,10 @@ def algorithmic(wl, inp, fuse_out_bytes):
     return out
 
 
-def cpu_baseline(wl, inp, n_nodes):
+def cpu_baseline(wl, inp, n_nodes, min_seconds=10.0):
     """The fp64 oracle (test infrastructure) on this host over a sample of the
-    step: the first n_nodes tree nodes of sequence 0 through all four parts."""
+    step: the first n_nodes tree nodes of sequence 0 through all four parts,
+    repeated until at least min_seconds of CPU work have been timed."""
     import oracle
     from tree_causal_draft_parent_amd import synth
     a = inp["attn"]
@@ -94,17 +137,22 @@ def cpu_baseline(wl, inp, n_nodes):
     w64 = synth.to_f64(inp["fuse"]["w"], wl.dtype)
     lg64 = synth.to_f64(inp["logits"][:n], wl.dtype)
     f = {key: synth.to_f64(a[key], wl.dtype) for key in ("q", "k_tree", "v_tree", "k_cache", "v_cache")}
+    reps = 0
     t0 = time.perf_counter()
-    oracle.tree_mask(a["parent"])
-    oracle.fuse_proj(x64, w64, rows=rows_node)
-    oracle.tree_attn(q=f["q"], k_tree=f["k_tree"], v_tree=f["v_tree"], parent=a["parent"],
-                     k_cache=f["k_cache"], v_cache=f["v_cache"], block_table=a["block_table"],
-                     prefix_len=a["prefix_len"], page_size=a["page_size"], rows=rows_attn)
-    oracle.topk(lg64, wl.topk)
-    dt = time.perf_counter() - t0
-    return {"value": n / dt, "unit": "nodes/s", "cores": oracle.num_threads(), "kind": "oracle",
+    while True:
+        oracle.tree_mask(a["parent"])
+        oracle.fuse_proj(x64, w64, rows=rows_node)
+        oracle.tree_attn(q=f["q"], k_tree=f["k_tree"], v_tree=f["v_tree"], parent=a["parent"],
+                         k_cache=f["k_cache"], v_cache=f["v_cache"], block_table=a["block_table"],
+                         prefix_len=a["prefix_len"], page_size=a["page_size"], rows=rows_attn)
+        oracle.topk(lg64, wl.topk)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    return {"value": n * reps / dt, "unit": "nodes/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"{n} of {N} tree nodes of sequence 0 through mask, fused projection, "
-                      f"tree attention (all {Hq} heads) and top-{wl.topk}+lse; {dt:.2f} s"}
+                      f"tree attention (all {Hq} heads) and top-{wl.topk}+lse, {reps} times; {dt:.2f} s"}
 
 
 def main():
@@ -113,6 +161,9 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(this build has no multi-GPU path).", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import torch
     from tree_causal_draft_parent_amd import jf, synth
 
@@ -223,12 +274,15 @@ def main():
 
     dom = max(("fuse", "attn", "topk"), key=lambda c: per_call[c])
     gbs, tfs = roof(dom, per_call[dom])
+    traffic = measured_traffic(dom, wl.name)
     if bound[dom] == "mfma":
         roofline = {"bound": "mfma", "achieved": round(tfs, 2), "peak": BF16_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(tfs / BF16_PEAK_TFLOPS, 4), "traffic": None}
+                    "unit": "TFLOP/s", "frac": round(tfs / BF16_PEAK_TFLOPS, 4), "traffic": traffic}
     else:
         roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}
+                    "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
+    roofline["kernels"] = [k for k in KERNELS[dom]]
+    roofline["avg_launch_us"] = round(per_call[dom] * 1e3, 2)
     roofline["kernel"] = {"fuse": "jf_fuse_proj (k_fuse_gemm_bf16 + k_fuse_reduce)",
                           "attn": "jf_tree_attn_fwd (k_tree_attn_split + k_tree_attn_merge)",
                           "topk": "jf_node_topk (k_topk_stage1 + k_topk_stage2)"}[dom]

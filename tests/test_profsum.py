@@ -1,0 +1,46 @@
+"""Host-side checks of the rocprofv3 summary helper (no GPU)."""
+import json
+import os
+
+from tree_causal_draft_parent_amd import profsum
+
+
+def test_short_name():
+    assert profsum.short_name("void jf::(anonymous namespace)::k_fuse_gemm_bf16<256>("
+                              "jf::(anonymous namespace)::FuseArgs)") == "k_fuse_gemm_bf16<256>"
+    assert profsum.short_name("jf::(anonymous namespace)::k_tree_attn_split("
+                              "jf::(anonymous namespace)::AttnArgs)") == "k_tree_attn_split"
+    assert profsum.short_name("void jf::(anonymous namespace)::k_topk_stage1<unsigned short, true>("
+                              "unsigned short const*, long)") == "k_topk_stage1<unsigned short, true>"
+
+
+def _counter_csv(path, rows):
+    cols = ["Correlation_Id", "Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    with open(path, "w") as f:
+        f.write(",".join(f'"{c}"' for c in cols) + "\n")
+        for i, (k, c, v) in enumerate(rows):
+            f.write(f'{i},{i},"{k}","{c}",{v}\n')
+
+
+def test_traffic_scaling(tmp_path):
+    d = {n: tmp_path / n for n in ("f", "w", "cf", "cw")}
+    for p in d.values():
+        p.mkdir()
+    g = "void jf::(anonymous namespace)::k_fuse_gemm_bf16<256>(jf::(anonymous namespace)::FuseArgs)"
+    _counter_csv(d["f"] / "r_counter_collection.csv", [(g, "FETCH_SIZE", 1000.0), (g, "FETCH_SIZE", 1200.0)])
+    _counter_csv(d["w"] / "r_counter_collection.csv", [(g, "WRITE_SIZE", 10.0)])
+    copy = "void at::native::copy_kernel(int)"
+    # the copy reads and writes 2048 KiB; the counters read 1024 / 4096 KiB
+    _counter_csv(d["cf"] / "r_counter_collection.csv", [(copy, "FETCH_SIZE", 1024.0)])
+    _counter_csv(d["cw"] / "r_counter_collection.csv", [(copy, "WRITE_SIZE", 4096.0)])
+    out = tmp_path / "t.json"
+    profsum.main(["traffic", "--fetch", str(d["f"]), "--write", str(d["w"]), "--copy-fetch", str(d["cf"]),
+                  "--copy-write", str(d["cw"]), "--copy-bytes", str(2048 * 1024), "--workload", "x",
+                  "--out", str(out)])
+    rec = json.loads(out.read_text())
+    k = rec["kernels"]["k_fuse_gemm_bf16<256>"]
+    assert k["launches"] == 2
+    assert k["fetch_bytes"] == round(1100.0 * 1024 * 2.0)
+    assert k["write_bytes"] == round(10.0 * 1024 * 0.5)
+    assert rec["sources_sha256"] == profsum.sources_hash()
+    assert os.path.exists(out)

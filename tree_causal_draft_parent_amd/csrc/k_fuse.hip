@@ -12,8 +12,8 @@
 // eight waves, two per SIMD so that one covers the other's LDS and barrier
 // stalls) or 128x128 (four waves), 64-deep K steps, each wave owning 64x64 of
 // the tile as 32x32 blocks of v_mfma_f32_32x32x16_bf16.  A and B tiles go from
-// HBM straight into a double-buffered LDS stage with buffer_load ... lds (one
-// K step ahead, no registers); one copy fills 1 KiB = 8 K-contiguous rows
+// HBM straight into a 3-stage (256-row tiles) or 4-stage LDS ring with
+// buffer_load ... lds (no registers); one copy fills 1 KiB = 8 K-contiguous rows
 // (rows n, n+T/8, ... of a T-row tile) and 16-byte block padding keeps the
 // 16-byte operand reads conflict-free.  Per-lane row offsets are computed once;
 // the K position rides in the scalar offset.  When the output has too few
@@ -201,14 +201,26 @@ __global__ __launch_bounds__(Cfg<BM>::kWaves * kWave) void k_fuse_gemm_bf16(Fuse
         }
 }
 
-// y = sum over K slices of the fp32 partials, converted to the output type.
+// y = sum over K slices of the fp32 partials (in slice order), converted to
+// the output type.  Four slices are loaded per round so that a thread's loads
+// overlap.
 __global__ __launch_bounds__(256) void k_fuse_reduce(const float *__restrict__ part, int split_k,
                                                      int64_t MN, void *y, int out_bf16) {
     const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
     if (i >= MN) return;
     if (i + 4 <= MN) {
         f32x4 s = *(const f32x4 *)(part + i);
-        for (int k = 1; k < split_k; ++k) {
+        int k = 1;
+        for (; k + 4 <= split_k; k += 4) {
+            f32x4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = *(const f32x4 *)(part + (int64_t)(k + u) * MN + i);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                s[0] += v[u][0]; s[1] += v[u][1]; s[2] += v[u][2]; s[3] += v[u][3];
+            }
+        }
+        for (; k < split_k; ++k) {
             f32x4 v = *(const f32x4 *)(part + (int64_t)k * MN + i);
             s[0] += v[0]; s[1] += v[1]; s[2] += v[2]; s[3] += v[3];
         }
