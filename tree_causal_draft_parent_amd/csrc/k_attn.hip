@@ -10,9 +10,10 @@
 // bf16 path (gfx950 MFMA), split over keys:
 //   * A sequence's keys are cut into 64-key blocks: ceil(P/64) prefix blocks
 //     (read through the page table), then ceil(N/64) tree blocks (the nodes'
-//     own K/V).  Consecutive blocks form a split ("chunk"); one workgroup
-//     handles one (chunk, KV head, tile of 128 query rows).  Query row
-//     r = node * G + (h % G), so the G heads of a node share a mask row.
+//     own K/V).  Consecutive blocks form a split ("chunk"); one workgroup of
+//     eight waves (two per SIMD) handles one (chunk, KV head, tile of 256
+//     query rows).  Query row r = node * G + (h % G), so the G heads of a node
+//     share a mask row.
 //   * Per block, each wave computes S^T = K Q^T for its 32 rows with
 //     v_mfma_f32_32x32x16_bf16 (K from LDS as the A operand, Q^T held in
 //     registers as B), so each lane ends up owning one query row's scores.
@@ -20,32 +21,39 @@
 //     partner lane+32), and O^T = V^T P^T (V^T from LDS as A, P^T straight
 //     from the score registers as B) leaves the output row in the same lane:
 //     no shuffles besides one max exchange between the two half-waves.
-//   * Tree blocks apply the ancestor bitmask: the lane's row reads one 64-bit
-//     word per block; a tree block no row of the workgroup can see is skipped.
+//   * Software pipeline inside each wave: the exponentials of block j are
+//     interleaved with the score MFMAs of block j+1, and the row maximum of
+//     block j+1 with the output MFMAs of block j, so the VALU and the MFMA
+//     pipes work at the same time.
+//   * Tree blocks apply the ancestor bitmask: each row's 64-bit word of the
+//     block travels with the block's K/V tiles; a tree block no row of the
+//     workgroup can see is skipped.
 //   * Online softmax in base 2 with a lazy rescale: the running maximum is
 //     only moved when a block's maximum exceeds it by more than 2^8, which
-//     keeps every exponent bounded while leaving the arithmetic exact.
+//     keeps every exponent bounded while leaving the arithmetic exact.  Row
+//     sums use v_dot2 on the same bf16 probabilities the MFMA consumes.
 //   * K and V tiles go straight from HBM into LDS (buffer_load ... lds, 16
-//     bytes a lane) one block ahead, into a double-buffered stage; no
-//     registers are spent on the prefetch.  One copy instruction fills 1 KiB
-//     of LDS; block n of a tile holds rows n, n+16, n+32, n+48, and the
-//     blocks are padded (16 bytes for K, 64 for V) so that both the K operand
-//     reads (ds_read_b128) and the V operand reads hit distinct banks, while
-//     every operand address is one base register plus an immediate.  V stays
-//     row-major:
-//     ds_read_b64_tr_b16 hands each lane four consecutive keys of one head-dim
-//     column, which is exactly the V^T operand layout.  One wait + barrier a
-//     block.
-//   * Each split writes (O / l, log-sum-exp) partials; a merge kernel combines
-//     the splits of a row with LSE weights.  A sequence with one split writes
-//     the final output directly.
+//     bytes a lane) through a 4-stage ring, three blocks ahead; no registers
+//     are spent on the prefetch.  For contiguous prefixes and tree blocks the
+//     block position lives in the buffer descriptor (scalar work only), whose
+//     record count also zero-fills rows past the end.  One copy instruction
+//     fills 1 KiB of LDS; block n of a tile holds rows n, n+16, n+32, n+48,
+//     and the blocks are padded (16 bytes for K, 64 for V) so that both the K
+//     operand reads (ds_read_b128) and the V operand reads hit distinct
+//     banks, while every operand address is one base register plus an
+//     immediate.  V stays row-major: ds_read_b64_tr_b16 hands each lane four
+//     consecutive keys of one head-dim column, which is exactly the V^T
+//     operand layout.
+//   * Each split writes (O / l in bf16, log-sum-exp in fp32) partials; a merge
+//     kernel combines the splits of a row with LSE weights.  A sequence with
+//     one split writes the final output directly.
 #include "jf_internal.h"
 
 namespace jf {
 namespace {
 
 constexpr int kKB = 64;                  // keys per block
-constexpr int kNW = 4;                   // waves per workgroup
+constexpr int kNW = 8;                   // waves per workgroup (two per SIMD)
 constexpr int kTQ = 32 * kNW;            // query rows per workgroup
 constexpr int kD = 128;                  // head dim of the bf16 path
 constexpr int kRow = kD * 2;             // bytes per K or V row
@@ -53,7 +61,11 @@ constexpr int kKBlk = 4 * kRow + 16;     // LDS block of 4 K rows (n, n+16, n+32
 constexpr int kVBlk = 4 * kRow + 64;     // LDS block of 4 V rows
 constexpr int kKTile = 16 * kKBlk;
 constexpr int kVTile = 16 * kVBlk;
-constexpr int kStage = kKTile + kVTile;  // K tile then V tile
+constexpr int kMTile = kTQ * 8;          // one 64-bit visibility word per query row
+constexpr int kStage = kKTile + kVTile + kMTile;
+constexpr int kNS = 4;                   // stages of the copy ring (three blocks in flight)
+constexpr int kCpw = 16 / kNW;           // K (and V) LDS blocks each wave fills per key block
+constexpr int kOps = 2 * kCpw + 1;       // memory operations per wave per key block
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazyLog2 = 8.f;
 
@@ -62,7 +74,9 @@ struct AttnArgs {
     const uint64_t *mask;
     const int32_t *block_table;
     void *out;
-    float *lse, *part_o, *part_lse;
+    float *lse;
+    uint16_t *part_o;      // split partials O / l, bf16 (the output itself is bf16)
+    float *part_lse;
     int32_t *page_status;
     uint32_t q_bytes, tree_bytes, cache_bytes, mask_bytes;
     int64_t num_pages;
@@ -130,242 +144,188 @@ __device__ __forceinline__ bf16x8 cvt8(const f32x16 &s, int base) {
 }
 
 struct SplitCtx {
-    __amdgpu_buffer_rsrc_t r_kt, r_vt, r_kc, r_vc, r_m;
-    int b, g, P, nPB, kb1, page0, lane, wave;
-    uint32_t moff;
+    __amdgpu_buffer_rsrc_t r_kc, r_vc, r_m;  // whole prefix cache (paged layouts), mask buffer
+    const uint16_t *kc0, *vc0;               // one-page layout: KV head g of prefix row 0
+    const uint16_t *kt0, *vt0;               // KV head g of tree row 0 of the sequence
+    int b, g, P, nPB, page0, lane, wave;
+    bool pzero;                              // one-page layout with a bad page id: zeros
+    uint32_t rowb;                           // bytes between consecutive keys
+    uint32_t vrow;                           // lane's offset of its first copy in a block
+    uint32_t mrow;                           // lane's mask dword offset (kOob: none)
 };
 
-// Start the copy of block kb's K and V tiles into stage `dst` (asynchronous;
-// each wave fills 4 of the 16 LDS blocks of each tile, one copy each: LDS
-// block n holds rows n + 16*slot, lane L copying row n + 16*(L/16), 16-byte
-// chunk L%16).  K and V rows share their byte offsets.  Also loads this lane's
-// 64-bit mask word of the block (zero for prefix blocks).
-__device__ __forceinline__ uint64_t issue_block(const AttnArgs &a, const SplitCtx &c, const int *pages,
-                                                uint32_t dst, int kb, bool &bad) {
+// A pointer known to be the same in every lane, moved to scalar registers.
+__device__ __forceinline__ const uint16_t *uniform_ptr(const uint16_t *p) {
+    const uint64_t v = (uint64_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const uint16_t *)(((uint64_t)hi << 32) | lo);
+}
+
+// This lane's eight 16-byte query fragments (k-steps t = 0..7 at +32 t bytes).
+// Issued as inline asm so that they are counted with the copies by the
+// explicit waits; the registers are read only after such a wait (and passed
+// through an empty asm statement there).
+__device__ __forceinline__ void load_q(u32x4 (&d)[kD / 16], __amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    asm volatile("buffer_load_dwordx4 %0, %8, %9, 0 offen\n\t"
+                 "buffer_load_dwordx4 %1, %8, %9, 0 offen offset:32\n\t"
+                 "buffer_load_dwordx4 %2, %8, %9, 0 offen offset:64\n\t"
+                 "buffer_load_dwordx4 %3, %8, %9, 0 offen offset:96\n\t"
+                 "buffer_load_dwordx4 %4, %8, %9, 0 offen offset:128\n\t"
+                 "buffer_load_dwordx4 %5, %8, %9, 0 offen offset:160\n\t"
+                 "buffer_load_dwordx4 %6, %8, %9, 0 offen offset:192\n\t"
+                 "buffer_load_dwordx4 %7, %8, %9, 0 offen offset:224"
+                 : "=&v"(d[0]), "=&v"(d[1]), "=&v"(d[2]), "=&v"(d[3]), "=&v"(d[4]), "=&v"(d[5]),
+                   "=&v"(d[6]), "=&v"(d[7])
+                 : "v"(voff), "s"(r) : "memory");
+}
+
+// 4 bytes per lane HBM -> LDS: lane L's dword lands at lds + 4 L.
+__device__ __forceinline__ void copy4s(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff,
+                                       uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory");
+}
+
+// Start the copy of block kb into stage `dst` (asynchronous, kOps memory
+// operations per wave): K and V tiles -- wave w fills LDS blocks 2w and 2w+1
+// of each, lane L copying row n + 16*(L/16), 16-byte chunk L%16 -- and the
+// visibility words of the workgroup's 256 query rows (zeros for prefix
+// blocks), thread t copying dword t%2 of row t/2.
+template <bool kPaged>
+__device__ __forceinline__ void issue_block(const AttnArgs &a, const SplitCtx &c, const int *pages,
+                                            uint32_t dst, int kb, bool &bad) {
     const bool tree = kb >= c.nPB;
-    const __amdgpu_buffer_rsrc_t rk = tree ? c.r_kt : c.r_kc;
-    const __amdgpu_buffer_rsrc_t rv = tree ? c.r_vt : c.r_vc;
-    const int sub = c.lane >> 4, ch = c.lane & 15;
-    const uint32_t rowb = (uint32_t)a.Hkv * kD * 2;       // bytes between consecutive keys
-    const uint32_t dstk = __builtin_amdgcn_readfirstlane(dst + 4 * c.wave * kKBlk);
-    const uint32_t dstv = __builtin_amdgcn_readfirstlane(dst + kKTile + 4 * c.wave * kVBlk);
-    uint32_t off[4];
-    if (tree || a.page_mode != 0) {
-        // rows 16*sub + n (n < 16) are contiguous keys of one page (or of the tree)
-        uint32_t vbase = kOob;
-        int lim;
+    const uint32_t dk = __builtin_amdgcn_readfirstlane(dst + kCpw * c.wave * kKBlk);
+    const uint32_t dv = __builtin_amdgcn_readfirstlane(dst + kKTile + kCpw * c.wave * kVBlk);
+    const uint32_t dm = __builtin_amdgcn_readfirstlane(dst + kKTile + kVTile + c.wave * 256);
+    if (!kPaged || tree) {
+        // the block's rows are contiguous keys: position in the descriptor,
+        // rows past the end of the prefix (or tree) read as zeros
+        const uint16_t *kp, *vp;
+        int rows;
         if (tree) {
             const int j0 = (kb - c.nPB) * kKB;
-            lim = a.N - j0;
-            vbase = ((((uint32_t)c.b * a.N + j0 + 16 * sub) * a.Hkv + c.g) * kD + ch * 8) * 2u;
+            kp = c.kt0 + (int64_t)j0 * a.Hkv * kD;
+            vp = c.vt0 + (int64_t)j0 * a.Hkv * kD;
+            rows = min(kKB, a.N - j0);
         } else {
+            const int p0 = kb * kKB;
+            kp = c.kc0 + (int64_t)p0 * a.Hkv * kD;
+            vp = c.vc0 + (int64_t)p0 * a.Hkv * kD;
+            rows = c.pzero ? 0 : min(kKB, c.P - p0);
+        }
+        // every value here is wave-uniform; say so, so that the descriptors live in SGPRs
+        const uint32_t nbytes = __builtin_amdgcn_readfirstlane((uint32_t)rows * c.rowb);
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(uniform_ptr(kp), nbytes);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(uniform_ptr(vp), nbytes);
+#pragma unroll
+        for (int i = 0; i < kCpw; ++i) copy16(rk, dk + i * kKBlk, c.vrow + i * c.rowb);
+#pragma unroll
+        for (int i = 0; i < kCpw; ++i) copy16(rv, dv + i * kVBlk, c.vrow + i * c.rowb);
+    } else {
+        // paged layouts: every group of 16 rows sits in one page (page_mode 2)
+        // or every row is looked up (page_mode 0)
+        const int sub = c.lane >> 4, ch = c.lane & 15;
+        uint32_t off[kCpw];
+        if (a.page_mode == 2) {
             const int pos = kb * kKB + 16 * sub;
-            lim = c.P - kb * kKB;
+            const int lim = c.P - kb * kKB;
+            uint32_t vbase = kOob;
             if (16 * sub < lim) {
-                int pg, slot;
-                if (a.page_mode == 1) {                    // one page per sequence
-                    pg = c.page0;
-                    slot = pos;
-                } else {                                   // power-of-two pages of >= 16
-                    pg = pos >> a.page_shift;
-                    slot = pos & (a.page_size - 1);
-                }
-                const int page = pages[pg - c.page0];
+                const int page = pages[(pos >> a.page_shift) - c.page0];
                 if (page >= 0 && page < a.num_pages)
-                    vbase = ((((uint32_t)page * a.page_size + slot) * a.Hkv + c.g) * kD + ch * 8) * 2u;
+                    vbase = ((((uint32_t)page * a.page_size + (pos & (a.page_size - 1))) * a.Hkv + c.g) * kD +
+                             ch * 8) * 2u;
                 else
                     bad = true;
             }
+#pragma unroll
+            for (int i = 0; i < kCpw; ++i) {
+                const int n = kCpw * c.wave + i;
+                off[i] = (16 * sub + n < lim && vbase != kOob) ? vbase + n * c.rowb : kOob;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < kCpw; ++i)
+                off[i] = row_offset(a, pages, c.page0, c.b, c.g, c.P, c.nPB, kb, kCpw * c.wave + i + 16 * sub,
+                                    ch, bad);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int n = 4 * c.wave + i;
-            off[i] = (16 * sub + n < lim && vbase != kOob) ? vbase + n * rowb : kOob;
-        }
-    } else {
-        // small or irregular pages: look every row up
+        for (int i = 0; i < kCpw; ++i) copy16(c.r_kc, dk + i * kKBlk, off[i]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            off[i] = row_offset(a, pages, c.page0, c.b, c.g, c.P, c.nPB, kb, 4 * c.wave + i + 16 * sub,
-                                ch, bad);
+        for (int i = 0; i < kCpw; ++i) copy16(c.r_vc, dv + i * kVBlk, off[i]);
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) copy16(rk, dstk + i * kKBlk, off[i]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) copy16(rv, dstv + i * kVBlk, off[i]);
-    const uint32_t moff = (tree && c.moff != kOob) ? c.moff + (kb - c.nPB) * 8 : kOob;
-    u32x2 mw = __builtin_amdgcn_raw_buffer_load_b64(c.r_m, moff, 0, 0);
-    return ((uint64_t)mw[1] << 32) | mw[0];
+    copy4s(c.r_m, dm, tree ? c.mrow : kOob, tree ? (uint32_t)(kb - c.nPB) * 8u : 0u);
 }
+
+template <bool B>
+struct Flag { static constexpr bool value = B; };
 
 struct SoftmaxState {
     f32x16 o[kD / 32];
     float m, l;
 };
 
-// One 64-key block: S^T = K Q^T, masking, online softmax, O^T += V^T P^T.
-__device__ __forceinline__ void compute_block(const AttnArgs &a, const lds_t *__restrict__ st,
-                                              const bf16x8 *qf, int kb, int nPB, int P,
-                                              uint64_t word, int lane, SoftmaxState &S) {
-    const int half = lane >> 5, l32 = lane & 31;
-    f32x16 s0, s1;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) { s0[i] = 0.f; s1[i] = 0.f; }
-    // K operand reads run one k-step ahead of the MFMAs; the scheduling
-    // fences keep the compiler from hoisting every read of the block (which
-    // would cost ~130 registers and halve occupancy).
-    const lds_t *kbase = st + k_lds(l32) + half * 16;   // row l32, chunk half; + 32 rows = 2 slots
-    auto kread = [&](int t, bf16x8 &k0, bf16x8 &k1) {
-        k0 = *(const __attribute__((address_space(3))) bf16x8 *)(kbase + t * 32);
-        k1 = *(const __attribute__((address_space(3))) bf16x8 *)(kbase + 2 * kRow + t * 32);
-    };
-    bf16x8 ka0, ka1, kb0v, kb1v;
-    kread(0, ka0, ka1);
-#pragma unroll
-    for (int t = 0; t < kD / 16; t += 2) {
-        kread(t + 1, kb0v, kb1v);
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka0, qf[t], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka1, qf[t], s1, 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        if (t + 2 < kD / 16) kread(t + 2, ka0, ka1);
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb0v, qf[t + 1], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb1v, qf[t + 1], s1, 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    // Register i of a half-wave holds key 4*(2*(i/4) + half) + i%4 (+32 for
-    // s1): the half-wave's keys are the nibbles half, half+2, ... of the
-    // block's 64-bit visibility word.  Gather them into bits 0-15 (s0) and
-    // 16-31 (s1) of one 32-bit word and test bit i.
-    const bool is_tree = kb >= nPB;
-    const bool tail = !is_tree && (kb + 1) * kKB > P;
-    if (is_tree || tail) {
-        uint64_t vis;
-        if (is_tree) {
-            const int left = a.N - (kb - nPB) * kKB;     // tree keys that exist in this block
-            vis = word & (left >= 64 ? ~0ull : ((1ull << left) - 1ull));
-        } else {
-            const int left = P - kb * kKB;
-            vis = (1ull << left) - 1ull;                 // 0 < left < 64
-        }
-        uint64_t x = (vis >> (4 * half)) & 0x0F0F0F0F0F0F0F0Full;
-        x = (x | (x >> 4)) & 0x00FF00FF00FF00FFull;
-        x = (x | (x >> 8)) & 0x0000FFFF0000FFFFull;
-        const uint32_t m = (uint32_t)(x | (x >> 16));
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            s0[i] = ((m >> i) & 1u) ? s0[i] : -INFINITY;
-            s1[i] = ((m >> (16 + i)) & 1u) ? s1[i] : -INFINITY;
-        }
-    }
-    float mx = fmaxf(s0[0], s1[0]);
-#pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(fmaxf(mx, s0[i]), s1[i]);   // v_max3_f32
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const bool need = mx > S.m + a.lazy_raw;
-    if (__ballot(need)) {
-        const float m_new = need ? mx : S.m;
-        const float alpha = need ? __builtin_amdgcn_exp2f((S.m - m_new) * a.c2) : 1.f;
-        S.l *= alpha;
-#pragma unroll
-        for (int d = 0; d < kD / 32; ++d)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) S.o[d][i] *= alpha;
-        S.m = m_new;
-    }
-    const float base = S.m == -INFINITY ? 0.f : S.m * a.c2;
-    float ls = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        s0[i] = __builtin_amdgcn_exp2f(fmaf(s0[i], a.c2, -base));
-        s1[i] = __builtin_amdgcn_exp2f(fmaf(s1[i], a.c2, -base));
-        ls += s0[i] + s1[i];
-    }
-    S.l += ls;
-    bf16x8 p[4];
-    p[0] = cvt8(s0, 0);
-    p[1] = cvt8(s0, 8);
-    p[2] = cvt8(s1, 0);
-    p[3] = cvt8(s1, 8);
-
-    // O^T (d x rows) += V^T P^T.  Within each 16-lane group, ds_read_b64_tr_b16
-    // gives lane i element (i%4) of the 8-byte rows supplied by lanes i/4 + 4e
-    // (e = 0..3): if lane q + 4e points at V[key0 + e][d0 + 4q], lane i receives
-    // V[key0 .. key0+3][d0 + i].  Two such reads (keys key0 and key0 + 8) form
-    // the operand slots 0-3 and 4-7 that match the score registers in p[].
-    const int grp = l32 >> 4, gi = lane & 15, q4 = gi & 3, e4 = gi >> 2;
-    // lane (group grp, q4, e4) points at row key0 + e4, columns grp*16 + 4*q4 ...;
-    // key0 = sb*32 + 16*t + 4*half (+8 for the second read): row % 16 =
-    // 4*half + e4 (+8), row / 16 = 2*sb + t.
-    const lds_t *vbase = st + kKTile + (4 * half + e4) * kVBlk + (grp * 16 + 4 * q4) * 2;
-    auto vread = [&](int idx) -> bf16x8 {
-        const int d = idx >> 2, stp = idx & 3;           // stp = 2*sb + t
-        const lds_t *pa = vbase + stp * kRow + d * 64;
-        s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)pa);
-        s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4 *)(pa + 8 * kVBlk));
-        u32x2 lw = __builtin_bit_cast(u32x2, lo), hw = __builtin_bit_cast(u32x2, hi);
-        u32x4 w = {lw[0], lw[1], hw[0], hw[1]};
-        return as_bf16x8(w);
-    };
-    bf16x8 va = vread(0), vb;
-#pragma unroll
-    for (int idx = 0; idx < (kD / 32) * 4; idx += 2) {
-        vb = vread(idx + 1);
-        S.o[idx >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p[idx & 3], S.o[idx >> 2], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        if (idx + 2 < (kD / 32) * 4) va = vread(idx + 2);
-        S.o[(idx + 1) >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb, p[(idx + 1) & 3], S.o[(idx + 1) >> 2], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-    }
+// Wait until at most n memory operations of this wave are outstanding, then
+// barrier (n is a multiple of kOps up to (kNS - 2) * kOps).
+__device__ __forceinline__ void ring_wait(int n) {
+    if (n >= 2 * kOps) ring_barrier<2 * kOps>();
+    else if (n >= kOps) ring_barrier<kOps>();
+    else ring_barrier<0>();
 }
 
-__device__ __forceinline__ void run_block(const AttnArgs &a, const SplitCtx &c, const int *pages,
-                                          const lds_t *cur, uint32_t nxt, const bf16x8 *qf,
-                                          uint32_t used, int &kb, uint64_t &word, SoftmaxState &S,
-                                          bool &bad) {
-    stage_barrier();
-    int kbn = kb + 1;
-    while (kbn < c.kb1 && kbn >= c.nPB && !((used >> (kbn - c.nPB)) & 1u)) ++kbn;
-    uint64_t word_n = 0ull;
-    if (kbn < c.kb1) word_n = issue_block(a, c, pages, nxt, kbn, bad);
-    compute_block(a, cur, qf, kb, c.nPB, c.P, word, c.lane, S);
-    kb = kbn;
-    word = word_n;
+// Register i of a half-wave's score tile holds key 4*(2*(i/4) + half) + i%4
+// (+32 for the second tile).
+__device__ __forceinline__ uint32_t half_bits(uint64_t vis, int half) {
+    uint64_t x = (vis >> (4 * half)) & 0x0F0F0F0F0F0F0F0Full;
+    x = (x | (x >> 4)) & 0x00FF00FF00FF00FFull;
+    x = (x | (x >> 8)) & 0x0000FFFF0000FFFFull;
+    return (uint32_t)(x | (x >> 16));
 }
 
+// kPaged = false: every prefix is one page (page_mode 1); true: page_mode 0 or 2.
+template <bool kPaged>
 __global__ __launch_bounds__(kNW * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_tree_attn_split(AttnArgs a) {
-    __shared__ __attribute__((aligned(1024))) char stage0[kStage];
-    __shared__ __attribute__((aligned(1024))) char stage1[kStage];
+    __shared__ __attribute__((aligned(1024))) char ring[kNS][kStage];
     __shared__ int s_pages[kPageLds];
     __shared__ uint32_t s_used;
     __shared__ int s_bad;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: lets wave math stay scalar
     const int half = lane >> 5, l32 = lane & 31;
 
     // ---- work item ----
     const int item = xcd_remap(blockIdx.x, a.total_items);
-    const int qt = item % a.n_qt;
+    const int qt = __builtin_amdgcn_readfirstlane(item % a.n_qt);
     const int tmp = item / a.n_qt;
-    const int g = tmp % a.Hkv;
-    const int cg = tmp / a.Hkv;
-    const int b = find_seq(a, cg);
+    const int g = __builtin_amdgcn_readfirstlane(tmp % a.Hkv);
+    const int cg = __builtin_amdgcn_readfirstlane(tmp / a.Hkv);
+    const int b = __builtin_amdgcn_readfirstlane(find_seq(a, cg));
     const int cidx = cg - a.chunk_start[b];
     const int nchunks = a.chunk_start[b + 1] - a.chunk_start[b];
-    const int P = a.prefix_len[b];
+    int P = __builtin_amdgcn_readfirstlane(a.prefix_len[b]);
     const int nPB = (P + kKB - 1) / kKB;
     const int nB = nPB + a.n_tree_blocks;
     const int kb0 = cidx * a.chunk_blocks;
     const int kb1 = min(kb0 + a.chunk_blocks, nB);
 
     SplitCtx c;
-    c.r_kt = rsrc(a.k_tree, a.tree_bytes);
-    c.r_vt = rsrc(a.v_tree, a.tree_bytes);
-    c.r_kc = rsrc(a.k_cache, a.cache_bytes);
-    c.r_vc = rsrc(a.v_cache, a.cache_bytes);
-    c.r_m = rsrc(a.mask, a.mask_bytes);
-    c.b = b; c.g = g; c.P = P; c.nPB = nPB; c.kb1 = kb1; c.lane = lane; c.wave = wave;
+    c.r_kc = make_rsrc(a.k_cache, a.cache_bytes);
+    c.r_vc = make_rsrc(a.v_cache, a.cache_bytes);
+    c.r_m = make_rsrc(a.mask, a.mask_bytes);
+    c.b = b; c.g = g; c.P = P; c.nPB = nPB; c.lane = lane; c.wave = wave;
+    c.rowb = (uint32_t)a.Hkv * kRow;
+    c.vrow = (uint32_t)(kCpw * wave + 16 * (lane >> 4)) * c.rowb + (uint32_t)(lane & 15) * 16u;
+    c.kt0 = uniform_ptr(a.k_tree + ((int64_t)b * a.N * a.Hkv + g) * kD);
+    c.vt0 = uniform_ptr(a.v_tree + ((int64_t)b * a.N * a.Hkv + g) * kD);
+    c.kc0 = a.k_cache;
+    c.vc0 = a.v_cache;
+    c.pzero = false;
+    if (tid == 0) { s_used = 0u; s_bad = 0; }
+    __syncthreads();
 
     // ---- page ids of this split's prefix range ----
     c.page0 = 0;
@@ -373,37 +333,44 @@ void k_tree_attn_split(AttnArgs a) {
         const int pos0 = kb0 * kKB;
         const int pos1 = min(kb1 * kKB, P);
         if (pos1 > pos0) {
-            int pend;
-            if (a.page_shift >= 0) {
-                c.page0 = pos0 >> a.page_shift;
-                pend = ((pos1 - 1) >> a.page_shift) + 1;
-            } else {
-                c.page0 = pos0 / a.page_size;
-                pend = (pos1 - 1) / a.page_size + 1;
-            }
             const int32_t *bt = a.block_table + (int64_t)b * a.max_pages;
-            for (int i = tid; i < pend - c.page0; i += kNW * kWave) s_pages[i] = bt[c.page0 + i];
+            if (!kPaged) {
+                // one page per sequence: a bad id reads as zeros and is flagged
+                const int page = __builtin_amdgcn_readfirstlane(bt[0]);
+                if (page >= 0 && page < a.num_pages) {
+                    const int64_t e0 = ((int64_t)page * a.page_size * a.Hkv + g) * kD;
+                    c.kc0 = uniform_ptr(a.k_cache + e0);
+                    c.vc0 = uniform_ptr(a.v_cache + e0);
+                } else {
+                    c.pzero = true;     // the prefix reads as zero keys and values
+                    if (tid == 0) s_bad = 1;
+                }
+            } else {
+                int pend;
+                if (a.page_shift >= 0) {
+                    c.page0 = pos0 >> a.page_shift;
+                    pend = ((pos1 - 1) >> a.page_shift) + 1;
+                } else {
+                    c.page0 = pos0 / a.page_size;
+                    pend = (pos1 - 1) / a.page_size + 1;
+                }
+                for (int i = tid; i < pend - c.page0; i += kNW * kWave) s_pages[i] = bt[c.page0 + i];
+            }
         }
     }
 
-    // ---- this lane's query row ----
+    // ---- this lane's query row and mask dword ----
     const int r = qt * kTQ + wave * 32 + l32;
     const bool row_ok = r < a.R;
     const int node = row_ok ? r / a.G : 0;
     const int hq = g * a.G + (row_ok ? r % a.G : 0);
-    bf16x8 qf[kD / 16];
     {
-        const __amdgpu_buffer_rsrc_t r_q = rsrc(a.q, a.q_bytes);
-        const uint32_t qoff = row_ok ? (uint32_t)(((((int64_t)b * a.N + node) * a.Hq + hq) * kD + half * 8) * 2) : kOob;
-#pragma unroll
-        for (int t = 0; t < kD / 16; ++t)
-            qf[t] = as_bf16x8(__builtin_amdgcn_raw_buffer_load_b128(r_q, row_ok ? qoff + t * 32 : kOob, 0, 0));
+        const int rm = qt * kTQ + (tid >> 1);
+        c.mrow = rm < a.R ? (uint32_t)((((int64_t)b * a.N + rm / a.G) * a.W) * 8 + (tid & 1) * 4) : kOob;
     }
-    c.moff = row_ok ? (uint32_t)(((int64_t)b * a.N + node) * a.W * 8) : kOob;
 
     // ---- which tree blocks of this split does any row of the tile see? ----
-    if (tid == 0) { s_used = 0u; s_bad = 0; }
-    __syncthreads();
+    __syncthreads();   // s_pages / s_bad written above
     if (kb1 > nPB && tid < kTQ) {
         const int rr = qt * kTQ + tid;
         if (rr < a.R) {
@@ -416,6 +383,10 @@ void k_tree_attn_split(AttnArgs a) {
     }
     __syncthreads();
     const uint32_t used = s_used;
+    auto next_vis = [&](int kb) {        // first visible block >= kb (kb1 if none)
+        while (kb < kb1 && kb >= nPB && !((used >> (kb - nPB)) & 1u)) ++kb;
+        return kb;
+    };
 
     SoftmaxState S;
 #pragma unroll
@@ -426,21 +397,257 @@ void k_tree_attn_split(AttnArgs a) {
     S.l = 0.f;
     bool bad = false;
 
-    lds_t *st0 = (lds_t *)stage0;
-    lds_t *st1 = (lds_t *)stage1;
-    uint32_t a0 = (uint32_t)(uintptr_t)st0, a1 = (uint32_t)(uintptr_t)st1;
-    int kb = kb0;
-    while (kb < kb1 && kb >= nPB && !((used >> (kb - nPB)) & 1u)) ++kb;
-    uint64_t word = 0ull;
-    if (kb < kb1) word = issue_block(a, c, s_pages, a0, kb, bad);
-    while (kb < kb1) {
-        run_block(a, c, s_pages, st0, a1, qf, used, kb, word, S, bad);
-        lds_t *t = st0;
-        st0 = st1;
-        st1 = t;
-        const uint32_t ta = a0;
-        a0 = a1;
-        a1 = ta;
+    const uint32_t ring0 = (uint32_t)(uintptr_t)(lds_t *)&ring[0][0];
+    auto stage_of = [&](int j) { return (const lds_t *)&ring[j % kNS][0]; };
+
+    // visible blocks in order: v(0), v(1), ... ; block v(j) goes to stage j % kNS.
+    // Issue order: block 0, this lane's query fragments, blocks 1 .. kNS-2, so
+    // that waiting for block 0 and the queries leaves the later blocks in
+    // flight (loads complete in issue order).
+    int kb_iss = next_vis(kb0);         // next block to issue
+    int n_iss = 0;                      // blocks issued so far
+    if (kb_iss < kb1) {
+        issue_block<kPaged>(a, c, s_pages, ring0, kb_iss, bad);
+        kb_iss = next_vis(kb_iss + 1);
+        n_iss = 1;
+    }
+    // ---- queries (Q^T fragments in registers) ----
+    u32x4 qraw[kD / 16];
+    {
+        const __amdgpu_buffer_rsrc_t r_q = make_rsrc(a.q, a.q_bytes);
+        const uint32_t qoff = row_ok ? (uint32_t)(((((int64_t)b * a.N + node) * a.Hq + hq) * kD + half * 8) * 2) : kOob;
+        load_q(qraw, r_q, qoff);
+    }
+    bf16x8 qf[kD / 16];                 // set from qraw after the first wait
+    for (; n_iss < kNS - 1 && kb_iss < kb1; ++n_iss) {
+        issue_block<kPaged>(a, c, s_pages, ring0 + (n_iss % kNS) * kStage, kb_iss, bad);
+        kb_iss = next_vis(kb_iss + 1);
+    }
+
+    // ---- per-block pieces ----
+    const int koff = k_lds(l32) + half * 16;                             // row l32, chunk half
+    auto qk = [&](const lds_t *st, f32x16 &s0, f32x16 &s1) {            // S^T = K Q^T, with no other work
+#pragma unroll
+        for (int i = 0; i < 16; ++i) { s0[i] = 0.f; s1[i] = 0.f; }
+        const lds_t *kb_ = st + koff;
+#pragma unroll
+        for (int t = 0; t < kD / 16; ++t) {
+            const bf16x8 k0 = *(const __attribute__((address_space(3))) bf16x8 *)(kb_ + t * 32);
+            const bf16x8 k1 = *(const __attribute__((address_space(3))) bf16x8 *)(kb_ + 2 * kRow + t * 32);
+            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[t], s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[t], s1, 0, 0, 0);
+        }
+    };
+    // visibility of a block's scores: tree blocks (ancestor words) and the prefix tail
+    auto apply_mask = [&](const lds_t *st, int kb, f32x16 &s0, f32x16 &s1) {
+        const bool is_tree = kb >= nPB;
+        const bool tail = !is_tree && (kb + 1) * kKB > P;
+        if (is_tree || tail) {
+            uint64_t vis;
+            if (is_tree) {
+                const int left = a.N - (kb - nPB) * kKB;
+                const uint64_t word = *(const __attribute__((address_space(3))) uint64_t *)(
+                    st + kKTile + kVTile + (wave * 32 + l32) * 8);
+                vis = word & (left >= 64 ? ~0ull : ((1ull << left) - 1ull));
+            } else {
+                vis = (1ull << (P - kb * kKB)) - 1ull;           // 0 < P - kb*64 < 64
+            }
+            const uint32_t m = half_bits(vis, half);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                s0[i] = ((m >> i) & 1u) ? s0[i] : -INFINITY;
+                s1[i] = ((m >> (16 + i)) & 1u) ? s1[i] : -INFINITY;
+            }
+        }
+    };
+    auto row_max = [&](const f32x16 &s0, const f32x16 &s1) -> float {
+        float mx = fmaxf(s0[0], s1[0]);
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mx = fmaxf(fmaxf(mx, s0[i]), s1[i]);
+        return fmaxf(mx, __shfl_xor(mx, 32));
+    };
+    // move the running maximum when the block's maximum exceeds it by > 2^8
+    auto rescale = [&](float mx) {
+        const bool need = mx > S.m + a.lazy_raw;
+        if (__ballot(need)) {
+            const float m_new = need ? mx : S.m;
+            const float alpha = need ? __builtin_amdgcn_exp2f((S.m - m_new) * a.c2) : 1.f;
+            S.l *= alpha;
+#pragma unroll
+            for (int d = 0; d < kD / 32; ++d)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) S.o[d][i] *= alpha;
+            S.m = m_new;
+        }
+    };
+
+    // V^T operand reads (see the layout note at the top of the file)
+    const int grp = l32 >> 4, gi = lane & 15, q4 = gi & 3, e4 = gi >> 2;
+    const int vlane = kKTile + (4 * half + e4) * kVBlk + (grp * 16 + 4 * q4) * 2;
+    auto vread = [&](const lds_t *st, int idx) -> bf16x8 {
+        const int d = idx >> 2, stp = idx & 3;
+        const lds_t *pa = st + vlane + stp * kRow + d * 64;
+        s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)pa);
+        s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4 *)(pa + 8 * kVBlk));
+        u32x2 lw = __builtin_bit_cast(u32x2, lo), hw = __builtin_bit_cast(u32x2, hi);
+        u32x4 w = {lw[0], lw[1], hw[0], hw[1]};
+        return as_bf16x8(w);
+    };
+
+    // One pipelined step: finish block j (scores sc, maximum already folded
+    // into S.m) while computing the scores sn of block j+1 (if has_next).
+    //   region A: the 16 score MFMAs of block j+1 | exps of keys 0-31 of block j
+    //   region B: O += V^T P^T for keys 0-31      | exps of keys 32-63
+    //             O += V^T P^T for keys 32-63     | row maximum of block j+1
+    // Each slot pairs MFMAs with a matching amount of VALU work (an exp runs
+    // at a quarter of the VALU rate).  Empty asm statements at every slot
+    // boundary pass the slot's MFMA results and VALU results through, and the
+    // scores later slots read, so no optimisation can move work between
+    // slots.
+    auto step = [&](auto next_tag, const lds_t *stj, const lds_t *stn, int kbn,
+                    f32x16 &sc0, f32x16 &sc1, f32x16 &sn0, f32x16 &sn1) -> float {
+        constexpr bool has_next = decltype(next_tag)::value;
+        const float nb = S.m == -INFINITY ? 0.f : -S.m * a.c2;
+        float ls = 0.f;
+        u32x4 pw[4];
+        // exps of registers i, i+1 of tile sx as one bf16 pair; the row sum
+        // uses the same bf16 probabilities as the MFMA
+        auto exp_pair = [&](const f32x16 &sx, int i) -> uint32_t {
+            const float e0 = __builtin_amdgcn_exp2f(fmaf(sx[i], a.c2, nb));
+            const float e1 = __builtin_amdgcn_exp2f(fmaf(sx[i + 1], a.c2, nb));
+            const uint32_t w = pack_bf16x2(e0, e1);
+            ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w),
+                                                 __builtin_bit_cast(bf16x2_t, 0x3f803f80u), ls, false);
+            return w;
+        };
+        const lds_t *kb_ = stn + koff;
+        // K operand of k-step t for key rows 0-31 (h = 0) or 32-63 (h = 1)
+        auto kread = [&](int h, int t) {
+            return *(const __attribute__((address_space(3))) bf16x8 *)(kb_ + h * 2 * kRow + t * 32);
+        };
+        bf16x8 kc0, kc1, kn0, kn1;
+        if constexpr (has_next) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sn0[i] = 0.f;
+            kc0 = kread(0, 0);
+            kc1 = kread(0, 1);
+        }
+        // ---- region A: slot t = two score MFMAs of block j+1 + two exps of sc0 ----
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            if constexpr (has_next) {
+                const int h = t >> 2, u = (t & 3) * 2;       // k-steps u, u+1 of half h
+                if (t + 1 < 8) {
+                    const int h1 = (t + 1) >> 2, u1 = ((t + 1) & 3) * 2;
+                    kn0 = kread(h1, u1);
+                    kn1 = kread(h1, u1 + 1);
+                }
+                if (t == 4) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) sn1[i] = 0.f;
+                }
+                f32x16 &acc = h == 0 ? sn0 : sn1;
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc0, qf[u], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc1, qf[u + 1], acc, 0, 0, 0);
+            }
+            uint32_t w = exp_pair(sc0, 2 * t);               // registers 2t, 2t+1 of sc0
+            if constexpr (has_next) {
+                if (t < 4) asm volatile("" : "+v"(sn0), "+v"(w));
+                else asm volatile("" : "+v"(sn1), "+v"(w));
+            } else {
+                asm volatile("" : "+v"(w));
+            }
+            if (t < 7) asm volatile("" : "+v"(sc0));
+            pw[t >> 2][t & 3] = w;                            // P^T operand q holds registers 8q .. 8q+7
+            kc0 = kn0;
+            kc1 = kn1;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (has_next) apply_mask(stn, kbn, sn0, sn1);
+        bf16x8 p[4];
+        p[0] = as_bf16x8(pw[0]);
+        p[1] = as_bf16x8(pw[1]);
+        // ---- region B: slot m = one output MFMA + (two exps of sc1 | row max) ----
+        float mxn = -INFINITY;
+        bf16x8 va = vread(stj, 0), vb;                       // V^T operand of (d, k-substep kk): idx 4d + kk
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+            const int kk = m >> 2, d = m & 3;
+            if (m + 1 < 16) vb = vread(stj, 4 * ((m + 1) & 3) + ((m + 1) >> 2));
+            if (m == 8) {
+                p[2] = as_bf16x8(pw[2]);
+                p[3] = as_bf16x8(pw[3]);
+            }
+            S.o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p[kk], S.o[d], 0, 0, 0);
+            if (m < 8) {
+                uint32_t w = exp_pair(sc1, 2 * m);           // registers 2m, 2m+1 of sc1
+                asm volatile("" : "+v"(S.o[d]), "+v"(w));
+                if (m < 7) asm volatile("" : "+v"(sc1));
+                pw[2 + (m >> 2)][m & 3] = w;
+            } else if constexpr (has_next) {
+                const int i = 2 * (m - 8);                   // registers i, i+1 of both tiles
+                mxn = fmaxf(fmaxf(mxn, sn0[i]), sn0[i + 1]);
+                mxn = fmaxf(fmaxf(mxn, sn1[i]), sn1[i + 1]);
+                asm volatile("" : "+v"(S.o[d]), "+v"(mxn));
+            } else {
+                asm volatile("" : "+v"(S.o[d]));
+            }
+            va = vb;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        S.l += ls;
+        return has_next ? fmaxf(mxn, __shfl_xor(mxn, 32)) : -INFINITY;
+    };
+
+    // ---- main loop over the visible blocks ----
+    int kb_cur = next_vis(kb0);
+    const int n_vis_first = n_iss;      // blocks in flight before the first wait
+    f32x16 sa0, sa1, sb0, sb1;
+    float mx_cur = -INFINITY;
+    if (kb_cur < kb1) {
+        ring_wait((n_vis_first - 1) * kOps);          // block 0 and the queries have landed
+        asm volatile("" : "+v"(qraw[0]), "+v"(qraw[1]), "+v"(qraw[2]), "+v"(qraw[3]),
+                          "+v"(qraw[4]), "+v"(qraw[5]), "+v"(qraw[6]), "+v"(qraw[7]));
+#pragma unroll
+        for (int t = 0; t < kD / 16; ++t) qf[t] = as_bf16x8(qraw[t]);
+        qk(stage_of(0), sa0, sa1);
+        apply_mask(stage_of(0), kb_cur, sa0, sa1);
+        mx_cur = row_max(sa0, sa1);
+    }
+    int j = 0;
+    // block j with a visible successor kb_nxt (which has landed after the wait)
+    auto iter_next = [&](f32x16 &sc0, f32x16 &sc1, f32x16 &sn0, f32x16 &sn1, int kb_nxt) {
+        ring_wait((n_iss - (j + 2)) * kOps);            // blocks issued after j+1 stay in flight
+        if (kb_iss < kb1) {                             // the stage of block j-1 is free
+            issue_block<kPaged>(a, c, s_pages, ring0 + (n_iss % kNS) * kStage, kb_iss, bad);
+            kb_iss = next_vis(kb_iss + 1);
+            ++n_iss;
+        }
+        rescale(mx_cur);
+        mx_cur = step(Flag<true>{}, stage_of(j), stage_of(j + 1), kb_nxt, sc0, sc1, sn0, sn1);
+        kb_cur = kb_nxt;
+        ++j;
+    };
+    // the last visible block (it landed before the previous step)
+    auto iter_last = [&](f32x16 &sc0, f32x16 &sc1) {
+        rescale(mx_cur);
+        step(Flag<false>{}, stage_of(j), stage_of(j), kb_cur, sc0, sc1, sc0, sc1);
+    };
+    if (kb_cur < kb1) {
+        // the loop only runs blocks with a successor (the last block's step is
+        // outside it, which keeps the loop's register pressure down)
+        bool in_b = false;                              // the last block's scores sit in sb
+        for (;;) {
+            int kn = next_vis(kb_cur + 1);
+            if (kn >= kb1) break;
+            iter_next(sa0, sa1, sb0, sb1, kn);
+            kn = next_vis(kb_cur + 1);
+            if (kn >= kb1) { in_b = true; break; }
+            iter_next(sb0, sb1, sa0, sa1, kn);
+        }
+        if (in_b) iter_last(sb0, sb1);
+        else iter_last(sa0, sa1);
     }
 
     if (bad) s_bad = 1;  // benign race: every writer stores 1
@@ -463,24 +670,26 @@ void k_tree_attn_split(AttnArgs a) {
             if (a.lse && half == 0) a.lse[orow] = lse_v;
         } else {
             const int64_t prow = ((int64_t)cg * a.Hkv + g) * a.R + r;
-            float *op = a.part_o + prow * kD + half * 4;
+            uint16_t *op = a.part_o + prow * kD + half * 4;
 #pragma unroll
             for (int d = 0; d < kD / 32; ++d)
 #pragma unroll
                 for (int gq = 0; gq < 4; ++gq) {
-                    f32x4 w = {S.o[d][gq * 4 + 0] * inv, S.o[d][gq * 4 + 1] * inv,
-                               S.o[d][gq * 4 + 2] * inv, S.o[d][gq * 4 + 3] * inv};
-                    *(f32x4 *)(op + d * 32 + gq * 8) = w;
+                    u32x2 w;
+                    w[0] = pack_bf16x2(S.o[d][gq * 4 + 0] * inv, S.o[d][gq * 4 + 1] * inv);
+                    w[1] = pack_bf16x2(S.o[d][gq * 4 + 2] * inv, S.o[d][gq * 4 + 3] * inv);
+                    *(u32x2 *)(op + d * 32 + gq * 8) = w;
                 }
             if (half == 0) a.part_lse[prow] = lse_v;
         }
     }
-    __syncthreads();
+    ring_barrier<0>();   // no copy is left in flight when the workgroup ends
     if (tid == 0 && s_bad && a.page_status) *a.page_status = JF_ERR_BAD_PAGE;
 }
 
 // Combine the splits of one row: O = sum_s w_s O_s / sum_s w_s with
-// w_s = exp(lse_s - max lse); lse = max + log sum w_s.  One wave per row.
+// w_s = exp(lse_s - max lse); lse = max + log sum w_s.  One wave per row, each
+// lane two output columns; the splits' loads are issued four at a time.
 __global__ __launch_bounds__(256) void k_tree_attn_merge(AttnArgs a) {
     const int lane = threadIdx.x & 63;
     const int64_t flat = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -494,16 +703,34 @@ __global__ __launch_bounds__(256) void k_tree_attn_merge(AttnArgs a) {
     if (nc == 1) return;
     const int g = hq / a.G;
     const int r = node * a.G + hq % a.G;
+    const int64_t stride = (int64_t)a.Hkv * a.R;             // rows between consecutive splits
+    const int64_t row0 = ((int64_t)c0 * a.Hkv + g) * a.R + r;
     float M = -INFINITY;
-    for (int c = 0; c < nc; ++c) M = fmaxf(M, a.part_lse[((int64_t)(c0 + c) * a.Hkv + g) * a.R + r]);
+    for (int c = 0; c < nc; ++c) M = fmaxf(M, a.part_lse[row0 + c * stride]);
     float acc0 = 0.f, acc1 = 0.f, wsum = 0.f;
-    for (int c = 0; c < nc; ++c) {
-        const int64_t prow = ((int64_t)(c0 + c) * a.Hkv + g) * a.R + r;
-        const float l = a.part_lse[prow];
-        const float w = l == -INFINITY ? 0.f : expf(l - M);
-        const float2 v = *(const float2 *)(a.part_o + prow * kD + 2 * lane);
-        acc0 += w * v.x;
-        acc1 += w * v.y;
+    int c = 0;
+    for (; c + 4 <= nc; c += 4) {
+        float l[4];
+        uint32_t v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            l[u] = a.part_lse[row0 + (c + u) * stride];
+            v[u] = *(const uint32_t *)(a.part_o + (row0 + (c + u) * stride) * kD + 2 * lane);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float w = l[u] == -INFINITY ? 0.f : __expf(l[u] - M);
+            acc0 += w * bf16_lo(v[u]);
+            acc1 += w * bf16_hi(v[u]);
+            wsum += w;
+        }
+    }
+    for (; c < nc; ++c) {
+        const float l = a.part_lse[row0 + c * stride];
+        const uint32_t v = *(const uint32_t *)(a.part_o + (row0 + c * stride) * kD + 2 * lane);
+        const float w = l == -INFINITY ? 0.f : __expf(l - M);
+        acc0 += w * bf16_lo(v);
+        acc1 += w * bf16_hi(v);
         wsum += w;
     }
     const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
@@ -611,8 +838,9 @@ __global__ __launch_bounds__(256) void k_tree_attn_f32(AttnArgsF32 a) {
 
 // ---------------------------------------------------------------------------
 // Split planning.  Every (sequence, KV head, query tile) is a row of blocks;
-// cut all rows into splits of the same block count so that about two
-// workgroups per compute unit come out, never less than two blocks a split.
+// cut all rows into splits of the same block count so that about one
+// workgroup per compute unit comes out (a workgroup fills a compute unit's
+// LDS), never less than two blocks a split.
 void plan_tree_attn(AttnPlan &p, int B, int N, int Hq, int Hkv, int D, int page_size,
                     const int32_t *prefix_len, jf_dtype dtype) {
     p.B = B; p.N = N; p.Hq = Hq; p.Hkv = Hkv; p.D = D;
@@ -632,7 +860,7 @@ void plan_tree_attn(AttnPlan &p, int B, int N, int Hq, int Hkv, int D, int page_
         if (nb > max_blocks) max_blocks = nb;
     }
     units *= (int64_t)Hkv * p.n_qt;
-    const int64_t target = 2 * (int64_t)num_cus();
+    const int64_t target = (int64_t)num_cus();
     int64_t cb = (units + target - 1) / target;
     if (cb < 2) cb = 2;
     // a split's page ids must fit the LDS staging array
@@ -663,7 +891,7 @@ void plan_tree_attn(AttnPlan &p, int B, int N, int Hq, int Hkv, int D, int page_
 size_t tree_attn_workspace_bytes(const AttnPlan &p) {
     if (!p.any_split) return 0;
     const size_t rows = (size_t)p.total_chunks * p.Hkv * p.R;
-    size_t o = rows * kD * sizeof(float);
+    size_t o = rows * kD * sizeof(uint16_t);
     o = (o + 255) / 256 * 256;
     return o + rows * sizeof(float);
 }
@@ -684,8 +912,8 @@ hipError_t launch_tree_attn_bf16(const AttnPlan &p, const void *q, const void *k
     a.out = out;
     a.lse = lse;
     const size_t rows = (size_t)p.total_chunks * p.Hkv * p.R;
-    size_t obytes = (rows * kD * sizeof(float) + 255) / 256 * 256;
-    a.part_o = p.any_split ? (float *)workspace : nullptr;
+    size_t obytes = (rows * kD * sizeof(uint16_t) + 255) / 256 * 256;
+    a.part_o = p.any_split ? (uint16_t *)workspace : nullptr;
     a.part_lse = p.any_split ? (float *)((char *)workspace + obytes) : nullptr;
     a.page_status = page_status;
     a.q_bytes = (uint32_t)((int64_t)p.B * p.N * p.Hq * kD * 2);
@@ -717,7 +945,10 @@ hipError_t launch_tree_attn_bf16(const AttnPlan &p, const void *q, const void *k
     a.lazy_raw = kLazyLog2 / a.c2;
     for (int b = 0; b < p.B; ++b) a.prefix_len[b] = p.prefix_len[b];
     for (int b = 0; b <= p.B; ++b) a.chunk_start[b] = p.chunk_start[b];
-    hipLaunchKernelGGL(k_tree_attn_split, dim3(p.total_items), dim3(kNW * kWave), 0, s, a);
+    if (a.page_mode == 1)
+        hipLaunchKernelGGL(k_tree_attn_split<false>, dim3(p.total_items), dim3(kNW * kWave), 0, s, a);
+    else
+        hipLaunchKernelGGL(k_tree_attn_split<true>, dim3(p.total_items), dim3(kNW * kWave), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !p.any_split) return e;
     const int64_t total = (int64_t)p.B * p.N * p.Hq;
