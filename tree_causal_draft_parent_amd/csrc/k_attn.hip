@@ -526,30 +526,32 @@ void k_tree_attn_split(AttnArgs a) {
         auto kread = [&](int h, int t) {
             return *(const __attribute__((address_space(3))) bf16x8 *)(kb_ + h * 2 * kRow + t * 32);
         };
-        bf16x8 kc0, kc1, kn0, kn1;
+        // K operands of slot t: k-steps u, u+1 of half h (t = 4h + u/2); read two slots ahead
+        bf16x8 kr[3][2];
+        auto kload = [&](int t, bf16x8 (&dst)[2]) {
+            const int h = t >> 2, u = (t & 3) * 2;
+            dst[0] = kread(h, u);
+            dst[1] = kread(h, u + 1);
+        };
         if constexpr (has_next) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) sn0[i] = 0.f;
-            kc0 = kread(0, 0);
-            kc1 = kread(0, 1);
+            kload(0, kr[0]);
+            kload(1, kr[1]);
         }
         // ---- region A: slot t = two score MFMAs of block j+1 + two exps of sc0 ----
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
             if constexpr (has_next) {
                 const int h = t >> 2, u = (t & 3) * 2;       // k-steps u, u+1 of half h
-                if (t + 1 < 8) {
-                    const int h1 = (t + 1) >> 2, u1 = ((t + 1) & 3) * 2;
-                    kn0 = kread(h1, u1);
-                    kn1 = kread(h1, u1 + 1);
-                }
+                if (t + 2 < 8) kload(t + 2, kr[(t + 2) % 3]);
                 if (t == 4) {
 #pragma unroll
                     for (int i = 0; i < 16; ++i) sn1[i] = 0.f;
                 }
                 f32x16 &acc = h == 0 ? sn0 : sn1;
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc0, qf[u], acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc1, qf[u + 1], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[t % 3][0], qf[u], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[t % 3][1], qf[u + 1], acc, 0, 0, 0);
             }
             uint32_t w = exp_pair(sc0, 2 * t);               // registers 2t, 2t+1 of sc0
             if constexpr (has_next) {
@@ -560,8 +562,6 @@ void k_tree_attn_split(AttnArgs a) {
             }
             if (t < 7) asm volatile("" : "+v"(sc0));
             pw[t >> 2][t & 3] = w;                            // P^T operand q holds registers 8q .. 8q+7
-            kc0 = kn0;
-            kc1 = kn1;
             __builtin_amdgcn_sched_barrier(0);
         }
         if constexpr (has_next) apply_mask(stn, kbn, sn0, sn1);
@@ -570,16 +570,19 @@ void k_tree_attn_split(AttnArgs a) {
         p[1] = as_bf16x8(pw[1]);
         // ---- region B: slot m = one output MFMA + (two exps of sc1 | row max) ----
         float mxn = -INFINITY;
-        bf16x8 va = vread(stj, 0), vb;                       // V^T operand of (d, k-substep kk): idx 4d + kk
+        // V^T operand of slot m (d = m%4, k-substep kk = m/4) is idx 4d + kk; read two slots ahead
+        bf16x8 vr[3];
+        vr[0] = vread(stj, 0);
+        vr[1] = vread(stj, 4);
 #pragma unroll
         for (int m = 0; m < 16; ++m) {
             const int kk = m >> 2, d = m & 3;
-            if (m + 1 < 16) vb = vread(stj, 4 * ((m + 1) & 3) + ((m + 1) >> 2));
+            if (m + 2 < 16) vr[(m + 2) % 3] = vread(stj, 4 * ((m + 2) & 3) + ((m + 2) >> 2));
             if (m == 8) {
                 p[2] = as_bf16x8(pw[2]);
                 p[3] = as_bf16x8(pw[3]);
             }
-            S.o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p[kk], S.o[d], 0, 0, 0);
+            S.o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[m % 3], p[kk], S.o[d], 0, 0, 0);
             if (m < 8) {
                 uint32_t w = exp_pair(sc1, 2 * m);           // registers 2m, 2m+1 of sc1
                 asm volatile("" : "+v"(S.o[d]), "+v"(w));
@@ -593,7 +596,6 @@ void k_tree_attn_split(AttnArgs a) {
             } else {
                 asm volatile("" : "+v"(S.o[d]));
             }
-            va = vb;
             __builtin_amdgcn_sched_barrier(0);
         }
         S.l += ls;
@@ -688,11 +690,13 @@ void k_tree_attn_split(AttnArgs a) {
 }
 
 // Combine the splits of one row: O = sum_s w_s O_s / sum_s w_s with
-// w_s = exp(lse_s - max lse); lse = max + log sum w_s.  One wave per row, each
-// lane two output columns; the splits' loads are issued four at a time.
+// w_s = exp(lse_s - max lse); lse = max + log sum w_s.  Sixteen threads per
+// row, eight output columns (one 16-byte load per split) each; one pass over
+// the splits, eight at a time, rescaling when the running maximum moves.
+constexpr int kMergeTPR = kD / 8;        // threads per row
 __global__ __launch_bounds__(256) void k_tree_attn_merge(AttnArgs a) {
-    const int lane = threadIdx.x & 63;
-    const int64_t flat = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int sub = threadIdx.x % kMergeTPR;
+    const int64_t flat = (int64_t)blockIdx.x * (256 / kMergeTPR) + threadIdx.x / kMergeTPR;
     const int64_t total = (int64_t)a.B * a.N * a.Hq;
     if (flat >= total) return;
     const int hq = (int)(flat % a.Hq);
@@ -705,38 +709,47 @@ __global__ __launch_bounds__(256) void k_tree_attn_merge(AttnArgs a) {
     const int r = node * a.G + hq % a.G;
     const int64_t stride = (int64_t)a.Hkv * a.R;             // rows between consecutive splits
     const int64_t row0 = ((int64_t)c0 * a.Hkv + g) * a.R + r;
+    const uint16_t *po = a.part_o + row0 * kD + sub * 8;
+    // one pass, eight splits' loads in flight at a time, online rescaling
     float M = -INFINITY;
-    for (int c = 0; c < nc; ++c) M = fmaxf(M, a.part_lse[row0 + c * stride]);
-    float acc0 = 0.f, acc1 = 0.f, wsum = 0.f;
-    int c = 0;
-    for (; c + 4 <= nc; c += 4) {
-        float l[4];
-        uint32_t v[4];
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float wsum = 0.f;
+    constexpr int kGroup = 8;
+    for (int c = 0; c < nc; c += kGroup) {
+        float l[kGroup];
+        u32x4 v[kGroup];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            l[u] = a.part_lse[row0 + (c + u) * stride];
-            v[u] = *(const uint32_t *)(a.part_o + (row0 + (c + u) * stride) * kD + 2 * lane);
+        for (int u = 0; u < kGroup; ++u) {
+            const bool ok = c + u < nc;
+            l[u] = ok ? a.part_lse[row0 + (c + u) * stride] : -INFINITY;
+            v[u] = ok ? *(const u32x4 *)(po + (c + u) * stride * kD) : u32x4{0u, 0u, 0u, 0u};
         }
+        float mg = M;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < kGroup; ++u) mg = fmaxf(mg, l[u]);
+        if (mg == -INFINITY) continue;                       // nothing visible yet
+        const float alpha = M == -INFINITY ? 0.f : __expf(M - mg);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] *= alpha;
+        wsum *= alpha;
+        M = mg;
+#pragma unroll
+        for (int u = 0; u < kGroup; ++u) {
             const float w = l[u] == -INFINITY ? 0.f : __expf(l[u] - M);
-            acc0 += w * bf16_lo(v[u]);
-            acc1 += w * bf16_hi(v[u]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[2 * e] += w * bf16_lo(v[u][e]);
+                acc[2 * e + 1] += w * bf16_hi(v[u][e]);
+            }
             wsum += w;
         }
     }
-    for (; c < nc; ++c) {
-        const float l = a.part_lse[row0 + c * stride];
-        const uint32_t v = *(const uint32_t *)(a.part_o + (row0 + c * stride) * kD + 2 * lane);
-        const float w = l == -INFINITY ? 0.f : __expf(l - M);
-        acc0 += w * bf16_lo(v);
-        acc1 += w * bf16_hi(v);
-        wsum += w;
-    }
     const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-    uint16_t *op = (uint16_t *)a.out + flat * kD + 2 * lane;
-    *(uint32_t *)op = pack_bf16x2(acc0 * inv, acc1 * inv);
-    if (a.lse && lane == 0) a.lse[flat] = wsum > 0.f ? M + logf(wsum) : -INFINITY;
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
+    *(u32x4 *)((uint16_t *)a.out + flat * kD + sub * 8) = o;
+    if (a.lse && sub == 0) a.lse[flat] = wsum > 0.f ? M + logf(wsum) : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -952,7 +965,9 @@ hipError_t launch_tree_attn_bf16(const AttnPlan &p, const void *q, const void *k
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !p.any_split) return e;
     const int64_t total = (int64_t)p.B * p.N * p.Hq;
-    hipLaunchKernelGGL(k_tree_attn_merge, dim3((unsigned)((total + 3) / 4)), dim3(256), 0, s, a);
+    const int64_t rows_per_wg = 256 / kMergeTPR;
+    hipLaunchKernelGGL(k_tree_attn_merge, dim3((unsigned)((total + rows_per_wg - 1) / rows_per_wg)), dim3(256), 0,
+                       s, a);
     return hipGetLastError();
 }
 
