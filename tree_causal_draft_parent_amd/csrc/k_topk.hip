@@ -6,14 +6,15 @@
 // logits (value descending, ties by lower index) and its normaliser.
 //
 // The scan is HBM-bound (one pass over R x V logits).  Stage 1: one wavefront
-// per (row, slice of the vocabulary).  Each lane streams 16-byte vectors; an
-// element can only enter the top-k if it beats the wave's current k-th best
-// (value, index) pair, so almost every element costs one compare.  Passing
-// elements are compacted into a per-wave LDS buffer with ballot + mbcnt; when
-// the buffer fills, the wave selects its k best keys (k rounds of a wave-wide
-// max), raising the threshold.  The online (max, sum-exp) of the slice rides
-// along.  Stage 2: one wavefront per row merges the slices' k-best lists and
-// (max, sum-exp) pairs.
+// per (row, slice of the vocabulary).  Every lane issues all of its 16-byte
+// loads at once and keeps the slice in registers.  Pass 1 folds each vector
+// into the lane maximum and the running (max, sum-exp) as it arrives.  The
+// k-th largest of the 64 lane maxima bounds the slice's k-th best from below,
+// so only elements at or above it can survive, and they sit in the few lanes
+// whose maximum reaches it: those lanes copy their vectors to LDS, the whole
+// wave scans them, and the survivors are compacted (ballot prefix sums) and
+// ranked against each other.  Stage 2: one block per row merges the slices'
+// k-best lists and (max, sum-exp) pairs.
 //
 // Candidates are 64-bit keys: high word = order-preserving image of the fp32
 // value (-0 folded onto +0), low word = ~index, so that a larger key is a
@@ -24,8 +25,10 @@ namespace jf {
 namespace {
 
 constexpr int kT1Waves = 4;
-constexpr int kCap = 576;     // survivors a wave can buffer before the register fallback
+constexpr int kCap = 512;     // survivors a wave can buffer before the selection from memory
 constexpr int kMaxVec = 19;   // 16-byte vectors per lane a wave holds in registers
+constexpr int kHot = 16;      // hot lanes whose vectors go through LDS
+constexpr int kScan = (kHot * kMaxVec + 63) / 64;   // scan rounds over the hot vectors
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazy = 5.545177444479562f;   // 8 * ln 2: rescale the running sum past 2^8
 
@@ -69,25 +72,6 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
     return r;
 }
 
-// The k largest of the keys c[0..kPer) held by each lane (unique, nonzero keys;
-// 0 marks an empty slot): lanes 0..k-1 receive them in descending order.
-// Returns this lane's pick and, through kth, the k-th largest (0 if fewer).
-template <int kPer>
-__device__ uint64_t wave_select(const uint64_t *c, int k, int lane, uint64_t &kth) {
-    uint64_t mine = 0, prev = ~0ull, best = 0;
-    for (int t = 0; t < k; ++t) {
-        uint64_t m = 0;
-#pragma unroll
-        for (int j = 0; j < kPer; ++j) m = (c[j] < prev && c[j] > m) ? c[j] : m;
-        best = wave_max_u64(m);
-        if (lane == t) mine = best;
-        prev = best;
-        if (best == 0) break;
-    }
-    kth = best;
-    return mine;
-}
-
 // Rank of `key` among the n keys in LDS (the number of larger ones; keys are
 // unique).  Every lane reads the same entries, so each read is a broadcast.
 __device__ __forceinline__ int rank_in(const uint64_t *keys, int n, uint64_t key) {
@@ -112,6 +96,10 @@ template <> struct Vec<uint16_t> {  // bf16 bits
         for (int j = 0; j < 4; ++j) { x[2 * j] = bf16_lo(r[j]); x[2 * j + 1] = bf16_hi(r[j]); }
     }
     __device__ static float scalar(const uint16_t *p) { return __uint_as_float((uint32_t)(*p) << 16); }
+    __device__ static uint32_t load1(__amdgpu_buffer_rsrc_t r, int off) {
+        return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+    }
+    __device__ static float widen(uint32_t b) { return __uint_as_float(b << 16); }
 };
 template <> struct Vec<float> {
     static constexpr int n = 4;
@@ -121,6 +109,10 @@ template <> struct Vec<float> {
         for (int j = 0; j < 4; ++j) x[j] = r[j];
     }
     __device__ static float scalar(const float *p) { return *p; }
+    __device__ static uint32_t load1(__amdgpu_buffer_rsrc_t r, int off) {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    }
+    __device__ static float widen(uint32_t b) { return __uint_as_float(b); }
 };
 
 template <typename T, bool kLse>
@@ -128,7 +120,10 @@ __global__ __launch_bounds__(kT1Waves * kWave) void k_topk_stage1(
     const T *__restrict__ logits, int64_t ld, int64_t V, int64_t chunk_len, int chunks, int64_t R,
     int k, uint64_t *__restrict__ cand, float2 *__restrict__ stats) {
     __shared__ __attribute__((aligned(16))) uint64_t sbuf[kT1Waves][kCap];
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    __shared__ __attribute__((aligned(16))) u32x4 hbuf[kT1Waves][kHot * kMaxVec];
+    __shared__ int hlane[kT1Waves][kHot];
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));   // wave-uniform
     const int64_t gw = (int64_t)blockIdx.x * kT1Waves + wv;
     if (gw >= R * chunks) return;  // whole wave leaves; no block barriers below
     const int64_t r = gw / chunks;
@@ -146,18 +141,26 @@ __global__ __launch_bounds__(kT1Waves * kWave) void k_topk_stage1(
     const int64_t tail0 = start + (int64_t)nv * STEP;
 
     // ---- all loads in flight at once ----
+    // Range-checked buffer loads: a read past the slice returns zeros instead
+    // of faulting, so every load is issued unconditionally and the compiler
+    // can wait for each vector on its own (vmcnt counts) as pass 1 reaches it.
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(row + start, (uint32_t)((end - start) * (int64_t)sizeof(T)));
     Raw d[MAXV];
 #pragma unroll
     for (int v = 0; v < MAXV; ++v)
-        if (v < nv) d[v] = *(const Raw *)(row + start + (int64_t)v * STEP + (int64_t)lane * VEC);
-    float tx[VEC];                             // tail: element tail0 + lane + 64 t
-    int ntail = 0;
+        d[v] = __builtin_bit_cast(Raw, __builtin_amdgcn_raw_buffer_load_b128(
+                   rs, (v * STEP + lane * VEC) * (int)sizeof(T), 0, 0));
+    uint32_t traw[VEC];                        // tail: element tail0 + lane + 64 t (raw bits)
 #pragma unroll
-    for (int t = 0; t < VEC; ++t) {
-        const int64_t e = tail0 + lane + (int64_t)t * kWave;
-        tx[t] = e < end ? Vec<T>::scalar(row + e) : -INFINITY;
-    }
-    ntail = (int)(end - tail0);                // 0 .. STEP-1, wave-uniform
+    for (int t = 0; t < VEC; ++t)
+        traw[t] = Vec<T>::load1(rs, (nv * STEP + lane + t * kWave) * (int)sizeof(T));
+    const int ntail = (int)(end - tail0);      // 0 .. STEP-1, wave-uniform
+    float tx[VEC];
+    auto tail_values = [&]() {
+#pragma unroll
+        for (int t = 0; t < VEC; ++t)
+            tx[t] = lane + t * kWave < ntail ? Vec<T>::widen(traw[t]) : -INFINITY;
+    };
 
     // ---- pass 1: lane maximum and the running log-sum-exp ----
     float lmax = -INFINITY;
@@ -184,6 +187,7 @@ __global__ __launch_bounds__(kT1Waves * kWave) void k_topk_stage1(
             if (kLse) lse_add(x, vmax, VEC);
         }
     }
+    tail_values();
     if (kLse && ntail > 0) {
 #pragma unroll
         for (int t = 0; t < VEC; ++t) {
@@ -201,104 +205,166 @@ __global__ __launch_bounds__(kT1Waves * kWave) void k_topk_stage1(
     };
     touch();
 
-    // ---- threshold: a lower bound on the slice's k-th largest element ----
-    // At least k elements are >= tv, so every element below it is out.
+    // ---- threshold ----
+    // tv = the k-th largest lane maximum.  k lanes hold an element >= tv, so
+    // the slice's k-th largest element is >= tv and everything below tv is
+    // out: survivors sit only in the "hot" lanes (lane maximum >= tv) and in
+    // the tail.  tv is found by bisection on the order-preserving bits: the
+    // largest key that at least k lane maxima reach (k <= 64).
     float tv = -INFINITY;
+    uint64_t hot = 0;
     if (nv > 0) {
-        // the k-th largest lane maximum (ties ordered by lane): each lane
-        // counts the maxima above its own, reading four at a time
-        float *fb = (float *)buf;
-        fb[lane] = lmax;
-        int rk = 0;
-#pragma unroll 4
-        for (int j = 0; j < kWave; j += 4) {
-            const f32x4 q = *(const f32x4 *)(fb + j);
+        const uint32_t key = ordered_bits(lmax);
+        constexpr int kLow = VEC == 8 ? 16 : 0;   // widened bf16: the low half follows the sign
+        uint32_t p = 0;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) rk += (q[u] > lmax) || (q[u] == lmax && j + u < lane);
+        for (int b = 31; b >= kLow; --b) {
+            const uint32_t cb = p | (1u << b);
+            p = __popcll(__ballot(key >= cb)) >= (uint32_t)k ? cb : p;
         }
-        const uint64_t hit = __ballot(rk == k - 1);
-        tv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lmax), __builtin_ctzll(hit)));
+        if (kLow) p |= (p & 0x80000000u) ? 0u : 0xffffu;
+        tv = ordered_to_float(p);
+        hot = __ballot(lmax >= tv);
     }
+    const int nhot = __popcll(hot);
 
-    // ---- pass 2: mark survivors (x >= tv) and count them ----
-    uint32_t marks[(MAXV * VEC + 31) / 32];
+    // survivor bits (x >= tv) of one 16-byte vector
+    auto survivors = [&](const Raw &rv) -> uint32_t {
+        uint32_t pm = 0;
+        if (VEC == 8 && tv > 0.f) {
+            // bf16 with a positive threshold: x >= tv exactly when x's bit
+            // pattern, read as a signed integer, is >= tv's (negative values
+            // and -0 read as negative integers), and tv's low 16 bits are
+            // zero, so each packed word is tested without unpacking.
+            const int32_t tb = __float_as_int(tv);
+            const u32x4 raw = __builtin_bit_cast(u32x4, rv);
 #pragma unroll
-    for (int w = 0; w < (MAXV * VEC + 31) / 32; ++w) marks[w] = 0u;
-    int cnt = 0;
-    if (VEC == 8 && tv > 0.f) {
-        // bf16 with a positive threshold: x >= tv exactly when x's bit pattern,
-        // read as a signed integer, is >= tv's (negative values and -0 read as
-        // negative integers), and tv's low 16 bits are zero, so each packed
-        // word is tested without unpacking.
-        const int32_t tb = __float_as_int(tv);
-#pragma unroll
-        for (int v = 0; v < MAXV; ++v) {
-            if (v < nv) {
-                uint32_t pm = 0;
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const uint32_t word = (uint32_t)d[v][w];
-                    pm |= (uint32_t)((int32_t)(word << 16) >= tb) << (2 * w);
-                    pm |= (uint32_t)((int32_t)word >= tb) << (2 * w + 1);
-                }
-                marks[(v * VEC) / 32] |= pm << ((v * VEC) % 32);
-                cnt += __popc(pm);
+            for (int w = 0; w < 4; ++w) {
+                pm |= (uint32_t)((int32_t)(raw[w] << 16) >= tb) << (2 * w);
+                pm |= (uint32_t)((int32_t)raw[w] >= tb) << (2 * w + 1);
             }
-        }
-    } else {
+        } else {
+            float x[VEC];
+            Vec<T>::unpack(rv, x);
 #pragma unroll
-        for (int v = 0; v < MAXV; ++v) {
-            if (v < nv) {
-                float x[VEC];
-                Vec<T>::unpack(d[v], x);
-                uint32_t pm = 0;
-#pragma unroll
-                for (int j = 0; j < VEC; ++j) pm |= (uint32_t)(x[j] >= tv) << j;
-                marks[(v * VEC) / 32] |= pm << ((v * VEC) % 32);
-                cnt += __popc(pm);
-            }
+            for (int j = 0; j < VEC; ++j) pm |= (uint32_t)(x[j] >= tv) << j;
         }
-    }
+        return pm;
+    };
+    // element j of a raw vector as fp32
+    auto element = [&](const Raw &rv, int j) -> float {
+        const u32x4 raw = __builtin_bit_cast(u32x4, rv);
+        if (VEC == 8) {
+            const uint32_t word = raw[j >> 1];
+            return __uint_as_float((j & 1) ? (word & 0xffff0000u) : (word << 16));
+        }
+        return __uint_as_float(raw[j & 3]);
+    };
     uint32_t tmark = 0;
 #pragma unroll
     for (int t = 0; t < VEC; ++t)
         tmark |= (uint32_t)(lane + t * kWave < ntail && tx[t] >= tv) << t;
-    cnt += __popc(tmark);
 
-    // ---- compaction: one wave prefix sum places every survivor ----
+    // one wave prefix sum over the per-lane survivor counts (each < 256)
     int pre = 0, tot = 0;
+    auto place = [&](int cnt) {
 #pragma unroll
-    for (int bit = 0; bit < 8; ++bit) {        // cnt <= MAXV*VEC + VEC < 256
-        const uint64_t b = __ballot((cnt >> bit) & 1);
-        pre += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0)) << bit;
-        tot += __popcll(b) << bit;
-    }
-    uint64_t *out = cand + ((int64_t)r * chunks + c) * k;
-    if (tot <= kCap) {
-        int pos = pre;
-#pragma unroll
-        for (int v = 0; v < MAXV; ++v) {
-            uint32_t pm = (marks[(v * VEC) / 32] >> ((v * VEC) % 32)) & ((1u << VEC) - 1u);
-            if (v < nv && __ballot(pm != 0)) {
-                const uint32_t i0 = (uint32_t)(start + (int64_t)v * STEP + (int64_t)lane * VEC);
-                while (pm) {                   // survivors are rare: visit set bits only
-                    const int j = __builtin_ctz(pm);
-                    pm &= pm - 1u;
-                    const u32x4 raw = __builtin_bit_cast(u32x4, d[v]);
-                    uint32_t bits;
-                    if (VEC == 8) {
-                        const uint32_t word = raw[j >> 1];
-                        bits = (j & 1) ? (word & 0xffff0000u) : (word << 16);
-                    } else {
-                        bits = raw[j & 3];
-                    }
-                    buf[pos++] = make_key(__uint_as_float(bits), i0 + j);
-                }
-            }
+        for (int bit = 0; bit < 8; ++bit) {
+            const uint64_t b = __ballot((cnt >> bit) & 1);
+            pre += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0)) << bit;
+            tot += __popcll(b) << bit;
         }
+    };
+    auto put_tail = [&](int &pos) {
 #pragma unroll
         for (int t = 0; t < VEC; ++t)
             if ((tmark >> t) & 1u) buf[pos++] = make_key(tx[t], (uint32_t)(tail0 + lane + t * kWave));
+    };
+
+    if (nhot <= kHot) {
+        // ---- few hot lanes: they copy their vectors to LDS and the whole
+        // wave scans them, one vector a lane per round ----
+        u32x4 *hv = hbuf[wv];                    // [nhot][nv] vectors, slot-major
+        int *hl = hlane[wv];                     // slot -> lane
+        if ((hot >> lane) & 1ull) {
+            const int slot = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(hot >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)hot, 0));
+            hl[slot] = lane;
+#pragma unroll
+            for (int v = 0; v < MAXV; ++v)
+                if (v < nv) hv[slot * nv + v] = __builtin_bit_cast(u32x4, d[v]);
+        }
+        __builtin_amdgcn_wave_barrier();
+        const int nvec = nhot * nv;
+        Raw sv[kScan];
+        uint32_t spm[kScan];
+        int cnt = __popc(tmark);
+#pragma unroll
+        for (int i = 0; i < kScan; ++i) {
+            const int q = lane + i * kWave;
+            spm[i] = 0;
+            if (q < nvec) {
+                sv[i] = __builtin_bit_cast(Raw, hv[q]);
+                spm[i] = survivors(sv[i]);
+                cnt += __popc(spm[i]);
+            }
+        }
+        place(cnt);
+        if (tot <= kCap) {
+            int pos = pre;
+#pragma unroll
+            for (int i = 0; i < kScan; ++i) {
+                uint32_t pm = spm[i];
+                if (pm) {
+                    const int q = lane + i * kWave;
+                    const int sl = q / nv, v = q - sl * nv;
+                    const uint32_t i0 = (uint32_t)(start + (int64_t)v * STEP + (int64_t)hl[sl] * VEC);
+                    while (pm) {
+                        const int j = __builtin_ctz(pm);
+                        pm &= pm - 1u;
+                        buf[pos++] = make_key(element(sv[i], j), i0 + j);
+                    }
+                }
+            }
+            put_tail(pos);
+        }
+    } else {
+        // ---- many lanes tie at the threshold: every lane marks its own
+        // vectors, then writes its survivors ----
+        uint32_t marks[(MAXV * VEC + 31) / 32];
+#pragma unroll
+        for (int w = 0; w < (MAXV * VEC + 31) / 32; ++w) marks[w] = 0u;
+        int cnt = __popc(tmark);
+#pragma unroll
+        for (int v = 0; v < MAXV; ++v) {
+            if (v < nv) {
+                const uint32_t pm = survivors(d[v]);
+                marks[(v * VEC) / 32] |= pm << ((v * VEC) % 32);
+                cnt += __popc(pm);
+            }
+        }
+        place(cnt);
+        if (tot <= kCap) {
+            int pos = pre;
+#pragma unroll
+            for (int v = 0; v < MAXV; ++v) {
+                uint32_t pm = (marks[(v * VEC) / 32] >> ((v * VEC) % 32)) & ((1u << VEC) - 1u);
+                if (v < nv && __ballot(pm != 0)) {
+                    const uint32_t i0 = (uint32_t)(start + (int64_t)v * STEP + (int64_t)lane * VEC);
+                    while (pm) {
+                        const int j = __builtin_ctz(pm);
+                        pm &= pm - 1u;
+                        buf[pos++] = make_key(element(d[v], j), i0 + j);
+                    }
+                }
+            }
+            put_tail(pos);
+        }
+    }
+
+    uint64_t *out = cand + ((int64_t)r * chunks + c) * k;
+    if (tot <= kCap) {
+        __builtin_amdgcn_wave_barrier();
         // every buffered survivor learns its rank; the k best write themselves
         for (int e = lane; e < tot; e += kWave) {
             const uint64_t key = buf[e];
