@@ -19,6 +19,8 @@
 // Candidates are 64-bit keys: high word = order-preserving image of the fp32
 // value (-0 folded onto +0), low word = ~index, so that a larger key is a
 // better candidate and keys are unique within a row.
+#include <type_traits>
+
 #include "jf_internal.h"
 
 namespace jf {
@@ -137,269 +139,276 @@ __global__ __launch_bounds__(kT1Waves * kWave) void k_topk_stage1(
     constexpr int STEP = kWave * VEC;          // elements per wave-wide vector
     constexpr int MAXV = kMaxVec;              // vectors per lane held in registers
     typedef typename Vec<T>::raw Raw;
-    const int nv = (int)((end - start) / STEP);   // whole vectors (<= MAXV by the plan)
-    const int64_t tail0 = start + (int64_t)nv * STEP;
+    // whole vectors of the slice (<= MAXV by the plan); every slice but a
+    // row's last is full, and a full slice runs with nv a compile-time constant
+    const int nv_rt = (int)((end - start) / STEP);
+    auto slice = [&](auto NV) {
+        const int nv = NV;
+        const int64_t tail0 = start + (int64_t)nv * STEP;
 
-    // ---- all loads in flight at once ----
-    // Range-checked buffer loads: a read past the slice returns zeros instead
-    // of faulting, so every load is issued unconditionally and the compiler
-    // can wait for each vector on its own (vmcnt counts) as pass 1 reaches it.
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(row + start, (uint32_t)((end - start) * (int64_t)sizeof(T)));
-    Raw d[MAXV];
+        // ---- all loads in flight at once ----
+        // Range-checked buffer loads: a read past the slice returns zeros instead
+        // of faulting, so every load is issued unconditionally and the compiler
+        // can wait for each vector on its own (vmcnt counts) as pass 1 reaches it.
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(row + start, (uint32_t)((end - start) * (int64_t)sizeof(T)));
+        Raw d[MAXV];
 #pragma unroll
-    for (int v = 0; v < MAXV; ++v)
-        d[v] = __builtin_bit_cast(Raw, __builtin_amdgcn_raw_buffer_load_b128(
-                   rs, (v * STEP + lane * VEC) * (int)sizeof(T), 0, 0));
-    uint32_t traw[VEC];                        // tail: element tail0 + lane + 64 t (raw bits)
-#pragma unroll
-    for (int t = 0; t < VEC; ++t)
-        traw[t] = Vec<T>::load1(rs, (nv * STEP + lane + t * kWave) * (int)sizeof(T));
-    const int ntail = (int)(end - tail0);      // 0 .. STEP-1, wave-uniform
-    float tx[VEC];
-    auto tail_values = [&]() {
+        for (int v = 0; v < MAXV; ++v)
+            d[v] = __builtin_bit_cast(Raw, __builtin_amdgcn_raw_buffer_load_b128(
+                       rs, (v * STEP + lane * VEC) * (int)sizeof(T), 0, 0));
+        uint32_t traw[VEC];                        // tail: element tail0 + lane + 64 t (raw bits)
 #pragma unroll
         for (int t = 0; t < VEC; ++t)
-            tx[t] = lane + t * kWave < ntail ? Vec<T>::widen(traw[t]) : -INFINITY;
-    };
+            traw[t] = Vec<T>::load1(rs, (nv * STEP + lane + t * kWave) * (int)sizeof(T));
+        const int ntail = (int)(end - tail0);      // 0 .. STEP-1, wave-uniform
+        float tx[VEC];
+        auto tail_values = [&]() {
+#pragma unroll
+            for (int t = 0; t < VEC; ++t)
+                tx[t] = lane + t * kWave < ntail ? Vec<T>::widen(traw[t]) : -INFINITY;
+        };
 
-    // ---- pass 1: lane maximum and the running log-sum-exp ----
-    float lmax = -INFINITY;
-    float m = -INFINITY, s = 0.f;
-    auto lse_add = [&](const float *x, float vmax, int cnt) {
-        if (vmax > m + kLazy) {
-            s *= __builtin_amdgcn_exp2f((m - vmax) * kLog2e);
-            m = vmax;
-        }
-        const float base = m == -INFINITY ? 0.f : m * kLog2e;
-#pragma unroll
-        for (int j = 0; j < VEC; ++j)
-            if (j < cnt) s += __builtin_amdgcn_exp2f(fmaf(x[j], kLog2e, -base));
-    };
-#pragma unroll
-    for (int v = 0; v < MAXV; ++v) {
-        if (v < nv) {
-            float x[VEC];
-            Vec<T>::unpack(d[v], x);
-            float vmax = x[0];
-#pragma unroll
-            for (int j = 1; j < VEC; ++j) vmax = fmaxf(vmax, x[j]);
-            lmax = fmaxf(lmax, vmax);
-            if (kLse) lse_add(x, vmax, VEC);
-        }
-    }
-    tail_values();
-    if (kLse && ntail > 0) {
-#pragma unroll
-        for (int t = 0; t < VEC; ++t) {
-            const bool ok = lane + t * kWave < ntail;
-            float x1 = ok ? tx[t] : -INFINITY;
-            if (ok) lse_add(&x1, x1, 1);
-        }
-    }
-
-    // Make the raw vectors look modified so that the compiler recomputes the
-    // unpacked values in pass 2 instead of keeping them all live from pass 1.
-    auto touch = [&]() {
-#pragma unroll
-        for (int v = 0; v < MAXV; ++v) asm volatile("" : "+v"(d[v]));
-    };
-    touch();
-
-    // ---- threshold ----
-    // tv = the k-th largest lane maximum.  k lanes hold an element >= tv, so
-    // the slice's k-th largest element is >= tv and everything below tv is
-    // out: survivors sit only in the "hot" lanes (lane maximum >= tv) and in
-    // the tail.  tv is found by bisection on the order-preserving bits: the
-    // largest key that at least k lane maxima reach (k <= 64).
-    float tv = -INFINITY;
-    uint64_t hot = 0;
-    if (nv > 0) {
-        const uint32_t key = ordered_bits(lmax);
-        constexpr int kLow = VEC == 8 ? 16 : 0;   // widened bf16: the low half follows the sign
-        uint32_t p = 0;
-#pragma unroll
-        for (int b = 31; b >= kLow; --b) {
-            const uint32_t cb = p | (1u << b);
-            p = __popcll(__ballot(key >= cb)) >= (uint32_t)k ? cb : p;
-        }
-        if (kLow) p |= (p & 0x80000000u) ? 0u : 0xffffu;
-        tv = ordered_to_float(p);
-        hot = __ballot(lmax >= tv);
-    }
-    const int nhot = __popcll(hot);
-
-    // survivor bits (x >= tv) of one 16-byte vector
-    auto survivors = [&](const Raw &rv) -> uint32_t {
-        uint32_t pm = 0;
-        if (VEC == 8 && tv > 0.f) {
-            // bf16 with a positive threshold: x >= tv exactly when x's bit
-            // pattern, read as a signed integer, is >= tv's (negative values
-            // and -0 read as negative integers), and tv's low 16 bits are
-            // zero, so each packed word is tested without unpacking.
-            const int32_t tb = __float_as_int(tv);
-            const u32x4 raw = __builtin_bit_cast(u32x4, rv);
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                pm |= (uint32_t)((int32_t)(raw[w] << 16) >= tb) << (2 * w);
-                pm |= (uint32_t)((int32_t)raw[w] >= tb) << (2 * w + 1);
+        // ---- pass 1: lane maximum and the running log-sum-exp ----
+        float lmax = -INFINITY;
+        float m = -INFINITY, s = 0.f;
+        auto lse_add = [&](const float *x, float vmax, int cnt) {
+            if (vmax > m + kLazy) {
+                s *= __builtin_amdgcn_exp2f((m - vmax) * kLog2e);
+                m = vmax;
             }
-        } else {
-            float x[VEC];
-            Vec<T>::unpack(rv, x);
+            const float base = m == -INFINITY ? 0.f : m * kLog2e;
 #pragma unroll
-            for (int j = 0; j < VEC; ++j) pm |= (uint32_t)(x[j] >= tv) << j;
-        }
-        return pm;
-    };
-    // element j of a raw vector as fp32
-    auto element = [&](const Raw &rv, int j) -> float {
-        const u32x4 raw = __builtin_bit_cast(u32x4, rv);
-        if (VEC == 8) {
-            const uint32_t word = raw[j >> 1];
-            return __uint_as_float((j & 1) ? (word & 0xffff0000u) : (word << 16));
-        }
-        return __uint_as_float(raw[j & 3]);
-    };
-    uint32_t tmark = 0;
-#pragma unroll
-    for (int t = 0; t < VEC; ++t)
-        tmark |= (uint32_t)(lane + t * kWave < ntail && tx[t] >= tv) << t;
-
-    // one wave prefix sum over the per-lane survivor counts (each < 256)
-    int pre = 0, tot = 0;
-    auto place = [&](int cnt) {
-#pragma unroll
-        for (int bit = 0; bit < 8; ++bit) {
-            const uint64_t b = __ballot((cnt >> bit) & 1);
-            pre += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0)) << bit;
-            tot += __popcll(b) << bit;
-        }
-    };
-    auto put_tail = [&](int &pos) {
-#pragma unroll
-        for (int t = 0; t < VEC; ++t)
-            if ((tmark >> t) & 1u) buf[pos++] = make_key(tx[t], (uint32_t)(tail0 + lane + t * kWave));
-    };
-
-    if (nhot <= kHot) {
-        // ---- few hot lanes: they copy their vectors to LDS and the whole
-        // wave scans them, one vector a lane per round ----
-        u32x4 *hv = hbuf[wv];                    // [nhot][nv] vectors, slot-major
-        int *hl = hlane[wv];                     // slot -> lane
-        if ((hot >> lane) & 1ull) {
-            const int slot = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(hot >> 32),
-                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)hot, 0));
-            hl[slot] = lane;
-#pragma unroll
-            for (int v = 0; v < MAXV; ++v)
-                if (v < nv) hv[slot * nv + v] = __builtin_bit_cast(u32x4, d[v]);
-        }
-        __builtin_amdgcn_wave_barrier();
-        const int nvec = nhot * nv;
-        Raw sv[kScan];
-        uint32_t spm[kScan];
-        int cnt = __popc(tmark);
-#pragma unroll
-        for (int i = 0; i < kScan; ++i) {
-            const int q = lane + i * kWave;
-            spm[i] = 0;
-            if (q < nvec) {
-                sv[i] = __builtin_bit_cast(Raw, hv[q]);
-                spm[i] = survivors(sv[i]);
-                cnt += __popc(spm[i]);
-            }
-        }
-        place(cnt);
-        if (tot <= kCap) {
-            int pos = pre;
-#pragma unroll
-            for (int i = 0; i < kScan; ++i) {
-                uint32_t pm = spm[i];
-                if (pm) {
-                    const int q = lane + i * kWave;
-                    const int sl = q / nv, v = q - sl * nv;
-                    const uint32_t i0 = (uint32_t)(start + (int64_t)v * STEP + (int64_t)hl[sl] * VEC);
-                    while (pm) {
-                        const int j = __builtin_ctz(pm);
-                        pm &= pm - 1u;
-                        buf[pos++] = make_key(element(sv[i], j), i0 + j);
-                    }
-                }
-            }
-            put_tail(pos);
-        }
-    } else {
-        // ---- many lanes tie at the threshold: every lane marks its own
-        // vectors, then writes its survivors ----
-        uint32_t marks[(MAXV * VEC + 31) / 32];
-#pragma unroll
-        for (int w = 0; w < (MAXV * VEC + 31) / 32; ++w) marks[w] = 0u;
-        int cnt = __popc(tmark);
+            for (int j = 0; j < VEC; ++j)
+                if (j < cnt) s += __builtin_amdgcn_exp2f(fmaf(x[j], kLog2e, -base));
+        };
 #pragma unroll
         for (int v = 0; v < MAXV; ++v) {
             if (v < nv) {
-                const uint32_t pm = survivors(d[v]);
-                marks[(v * VEC) / 32] |= pm << ((v * VEC) % 32);
-                cnt += __popc(pm);
+                float x[VEC];
+                Vec<T>::unpack(d[v], x);
+                float vmax = x[0];
+#pragma unroll
+                for (int j = 1; j < VEC; ++j) vmax = fmaxf(vmax, x[j]);
+                lmax = fmaxf(lmax, vmax);
+                if (kLse) lse_add(x, vmax, VEC);
             }
         }
-        place(cnt);
-        if (tot <= kCap) {
-            int pos = pre;
+        tail_values();
+        if (kLse && ntail > 0) {
 #pragma unroll
-            for (int v = 0; v < MAXV; ++v) {
-                uint32_t pm = (marks[(v * VEC) / 32] >> ((v * VEC) % 32)) & ((1u << VEC) - 1u);
-                if (v < nv && __ballot(pm != 0)) {
-                    const uint32_t i0 = (uint32_t)(start + (int64_t)v * STEP + (int64_t)lane * VEC);
-                    while (pm) {
-                        const int j = __builtin_ctz(pm);
-                        pm &= pm - 1u;
-                        buf[pos++] = make_key(element(d[v], j), i0 + j);
-                    }
+            for (int t = 0; t < VEC; ++t) {
+                const bool ok = lane + t * kWave < ntail;
+                float x1 = ok ? tx[t] : -INFINITY;
+                if (ok) lse_add(&x1, x1, 1);
+            }
+        }
+
+        // Make the raw vectors look modified so that the compiler recomputes the
+        // unpacked values in pass 2 instead of keeping them all live from pass 1.
+        auto touch = [&]() {
+#pragma unroll
+            for (int v = 0; v < MAXV; ++v) asm volatile("" : "+v"(d[v]));
+        };
+        touch();
+
+        // ---- threshold ----
+        // tv = the k-th largest lane maximum.  k lanes hold an element >= tv, so
+        // the slice's k-th largest element is >= tv and everything below tv is
+        // out: survivors sit only in the "hot" lanes (lane maximum >= tv) and in
+        // the tail.  tv is found by bisection on the order-preserving bits: the
+        // largest key that at least k lane maxima reach (k <= 64).
+        float tv = -INFINITY;
+        uint64_t hot = 0;
+        if (nv > 0) {
+            const uint32_t key = ordered_bits(lmax);
+            constexpr int kLow = VEC == 8 ? 16 : 0;   // widened bf16: the low half follows the sign
+            uint32_t p = 0;
+#pragma unroll
+            for (int b = 31; b >= kLow; --b) {
+                const uint32_t cb = p | (1u << b);
+                p = __popcll(__ballot(key >= cb)) >= (uint32_t)k ? cb : p;
+            }
+            if (kLow) p |= (p & 0x80000000u) ? 0u : 0xffffu;
+            tv = ordered_to_float(p);
+            hot = __ballot(lmax >= tv);
+        }
+        const int nhot = __popcll(hot);
+
+        // survivor bits (x >= tv) of one 16-byte vector
+        auto survivors = [&](const Raw &rv) -> uint32_t {
+            uint32_t pm = 0;
+            if (VEC == 8 && tv > 0.f) {
+                // bf16 with a positive threshold: x >= tv exactly when x's bit
+                // pattern, read as a signed integer, is >= tv's (negative values
+                // and -0 read as negative integers), and tv's low 16 bits are
+                // zero, so each packed word is tested without unpacking.
+                const int32_t tb = __float_as_int(tv);
+                const u32x4 raw = __builtin_bit_cast(u32x4, rv);
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    pm |= (uint32_t)((int32_t)(raw[w] << 16) >= tb) << (2 * w);
+                    pm |= (uint32_t)((int32_t)raw[w] >= tb) << (2 * w + 1);
+                }
+            } else {
+                float x[VEC];
+                Vec<T>::unpack(rv, x);
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) pm |= (uint32_t)(x[j] >= tv) << j;
+            }
+            return pm;
+        };
+        // element j of a raw vector as fp32
+        auto element = [&](const Raw &rv, int j) -> float {
+            const u32x4 raw = __builtin_bit_cast(u32x4, rv);
+            if (VEC == 8) {
+                const uint32_t word = raw[j >> 1];
+                return __uint_as_float((j & 1) ? (word & 0xffff0000u) : (word << 16));
+            }
+            return __uint_as_float(raw[j & 3]);
+        };
+        uint32_t tmark = 0;
+#pragma unroll
+        for (int t = 0; t < VEC; ++t)
+            tmark |= (uint32_t)(lane + t * kWave < ntail && tx[t] >= tv) << t;
+
+        // one wave prefix sum over the per-lane survivor counts (each < 256)
+        int pre = 0, tot = 0;
+        auto place = [&](int cnt) {
+#pragma unroll
+            for (int bit = 0; bit < 8; ++bit) {
+                const uint64_t b = __ballot((cnt >> bit) & 1);
+                pre += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0)) << bit;
+                tot += __popcll(b) << bit;
+            }
+        };
+        auto put_tail = [&](int &pos) {
+#pragma unroll
+            for (int t = 0; t < VEC; ++t)
+                if ((tmark >> t) & 1u) buf[pos++] = make_key(tx[t], (uint32_t)(tail0 + lane + t * kWave));
+        };
+
+        if (nhot <= kHot) {
+            // ---- few hot lanes: they copy their vectors to LDS and the whole
+            // wave scans them, one vector a lane per round ----
+            u32x4 *hv = hbuf[wv];                    // [nhot][nv] vectors, slot-major
+            int *hl = hlane[wv];                     // slot -> lane
+            if ((hot >> lane) & 1ull) {
+                const int slot = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(hot >> 32),
+                                                                __builtin_amdgcn_mbcnt_lo((uint32_t)hot, 0));
+                hl[slot] = lane;
+#pragma unroll
+                for (int v = 0; v < MAXV; ++v)
+                    if (v < nv) hv[slot * nv + v] = __builtin_bit_cast(u32x4, d[v]);
+            }
+            __builtin_amdgcn_wave_barrier();
+            const int nvec = nhot * nv;
+            Raw sv[kScan];
+            uint32_t spm[kScan];
+            int cnt = __popc(tmark);
+#pragma unroll
+            for (int i = 0; i < kScan; ++i) {
+                const int q = lane + i * kWave;
+                spm[i] = 0;
+                if (q < nvec) {
+                    sv[i] = __builtin_bit_cast(Raw, hv[q]);
+                    spm[i] = survivors(sv[i]);
+                    cnt += __popc(spm[i]);
                 }
             }
-            put_tail(pos);
-        }
-    }
-
-    uint64_t *out = cand + ((int64_t)r * chunks + c) * k;
-    if (tot <= kCap) {
-        __builtin_amdgcn_wave_barrier();
-        // every buffered survivor learns its rank; the k best write themselves
-        for (int e = lane; e < tot; e += kWave) {
-            const uint64_t key = buf[e];
-            const int rk = rank_in(buf, tot, key);
-            if (rk < k) out[rk] = key;
-        }
-        for (int e = tot + lane; e < k; e += kWave) out[e] = 0ull;   // short slice
-    } else {
-        // Too many ties at the threshold for the buffer (rare): select straight
-        // from memory, k rounds of "best key below the previous pick".  Kept
-        // out of registers on purpose so that it costs the common path nothing.
-        uint64_t prev = ~0ull, mine = 0;
-        for (int t = 0; t < k; ++t) {
-            uint64_t best = 0;
-            for (int64_t e = start + lane; e < end; e += kWave) {
-                const uint64_t kk = make_key(Vec<T>::scalar(row + e), (uint32_t)e);
-                best = (kk < prev && kk > best) ? kk : best;
-            }
-            best = wave_max_u64(best);
-            if (lane == t) mine = best;
-            prev = best;
-        }
-        if (lane < k) out[lane] = mine;
-    }
-    if (kLse) {
+            place(cnt);
+            if (tot <= kCap) {
+                int pos = pre;
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            float mo = __shfl_xor(m, off), so = __shfl_xor(s, off);
-            float mn = fmaxf(m, mo);
-            float bn = mn == -INFINITY ? 0.f : mn * kLog2e;
-            s = s * __builtin_amdgcn_exp2f(m * kLog2e - bn) + so * __builtin_amdgcn_exp2f(mo * kLog2e - bn);
-            m = mn;
+                for (int i = 0; i < kScan; ++i) {
+                    uint32_t pm = spm[i];
+                    if (pm) {
+                        const int q = lane + i * kWave;
+                        const int sl = q / nv, v = q - sl * nv;
+                        const uint32_t i0 = (uint32_t)(start + (int64_t)v * STEP + (int64_t)hl[sl] * VEC);
+                        while (pm) {
+                            const int j = __builtin_ctz(pm);
+                            pm &= pm - 1u;
+                            buf[pos++] = make_key(element(sv[i], j), i0 + j);
+                        }
+                    }
+                }
+                put_tail(pos);
+            }
+        } else {
+            // ---- many lanes tie at the threshold: every lane marks its own
+            // vectors, then writes its survivors ----
+            uint32_t marks[(MAXV * VEC + 31) / 32];
+#pragma unroll
+            for (int w = 0; w < (MAXV * VEC + 31) / 32; ++w) marks[w] = 0u;
+            int cnt = __popc(tmark);
+#pragma unroll
+            for (int v = 0; v < MAXV; ++v) {
+                if (v < nv) {
+                    const uint32_t pm = survivors(d[v]);
+                    marks[(v * VEC) / 32] |= pm << ((v * VEC) % 32);
+                    cnt += __popc(pm);
+                }
+            }
+            place(cnt);
+            if (tot <= kCap) {
+                int pos = pre;
+#pragma unroll
+                for (int v = 0; v < MAXV; ++v) {
+                    uint32_t pm = (marks[(v * VEC) / 32] >> ((v * VEC) % 32)) & ((1u << VEC) - 1u);
+                    if (v < nv && __ballot(pm != 0)) {
+                        const uint32_t i0 = (uint32_t)(start + (int64_t)v * STEP + (int64_t)lane * VEC);
+                        while (pm) {
+                            const int j = __builtin_ctz(pm);
+                            pm &= pm - 1u;
+                            buf[pos++] = make_key(element(d[v], j), i0 + j);
+                        }
+                    }
+                }
+                put_tail(pos);
+            }
         }
-        if (lane == 0) stats[(int64_t)r * chunks + c] = make_float2(m, s);
-    }
+
+        uint64_t *out = cand + ((int64_t)r * chunks + c) * k;
+        if (tot <= kCap) {
+            __builtin_amdgcn_wave_barrier();
+            // every buffered survivor learns its rank; the k best write themselves
+            for (int e = lane; e < tot; e += kWave) {
+                const uint64_t key = buf[e];
+                const int rk = rank_in(buf, tot, key);
+                if (rk < k) out[rk] = key;
+            }
+            for (int e = tot + lane; e < k; e += kWave) out[e] = 0ull;   // short slice
+        } else {
+            // Too many ties at the threshold for the buffer (rare): select straight
+            // from memory, k rounds of "best key below the previous pick".  Kept
+            // out of registers on purpose so that it costs the common path nothing.
+            uint64_t prev = ~0ull, mine = 0;
+            for (int t = 0; t < k; ++t) {
+                uint64_t best = 0;
+                for (int64_t e = start + lane; e < end; e += kWave) {
+                    const uint64_t kk = make_key(Vec<T>::scalar(row + e), (uint32_t)e);
+                    best = (kk < prev && kk > best) ? kk : best;
+                }
+                best = wave_max_u64(best);
+                if (lane == t) mine = best;
+                prev = best;
+            }
+            if (lane < k) out[lane] = mine;
+        }
+        if (kLse) {
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) {
+                float mo = __shfl_xor(m, off), so = __shfl_xor(s, off);
+                float mn = fmaxf(m, mo);
+                float bn = mn == -INFINITY ? 0.f : mn * kLog2e;
+                s = s * __builtin_amdgcn_exp2f(m * kLog2e - bn) + so * __builtin_amdgcn_exp2f(mo * kLog2e - bn);
+                m = mn;
+            }
+            if (lane == 0) stats[(int64_t)r * chunks + c] = make_float2(m, s);
+        }
+    };
+    if (nv_rt == MAXV) slice(std::integral_constant<int, MAXV>());
+    else slice(nv_rt);
 }
 
 constexpr int kMaxCand = 4096;   // chunks * k candidates merged per row
