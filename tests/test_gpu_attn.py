@@ -128,3 +128,23 @@ def test_serving_batch_full_size_sampled():
 def test_qwen3_30b_shape_full_size_sampled():
     inp = synth.make_workload(4, parts=("attn",))["attn"]
     compare(inp, rows=_sample_rows(inp, 256, 4), label="qwen3-30b")
+
+
+def test_score_jump_past_reference_maximum():
+    # Keys after the first 64-key block are made to score far above it (a key
+    # equal to 4 q gives a raw score of about 4 |q|^2 = 512 with D = 128, over
+    # 2^32 in exp2 units above the first block's maximum of about 40), which
+    # sends the first split of each (KV head, query tile) through its second
+    # pass with the true maxima.  The oracle's softmax is exact, so the
+    # output must still match it.
+    inp = synth.make_attn_inputs(B=1, N=24, Hq=8, Hkv=2, D=128, dtype="bf16", prefix_lens=[640],
+                                 seed=11)
+    q = synth.bf16_bits_to_f32(inp["q"])              # [B, N, Hq, D]
+    kc = synth.bf16_bits_to_f32(inp["k_cache"])       # [pages, page_size, Hkv, D]
+    G = 8 // 2
+    for p in range(64 + 5, 640, 64):                  # one key per block, never in block 0
+        node = (p // 64) % 24
+        for g in range(2):
+            kc[0, p, g] = 4.0 * q[0, node, g * G]
+    inp["k_cache"] = synth.f32_to_bf16_bits(kc)
+    compare(inp, label="score jump")

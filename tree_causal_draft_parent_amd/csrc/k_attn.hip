@@ -382,11 +382,33 @@ void k_tree_attn_split(AttnArgs a) {
         }
     }
     __syncthreads();
-    const uint32_t used = s_used;
+    const uint32_t used = __builtin_amdgcn_readfirstlane(s_used);   // uniform: block choice stays scalar
     auto next_vis = [&](int kb) {        // first visible block >= kb (kb1 if none)
         while (kb < kb1 && kb >= nPB && !((used >> (kb - nPB)) & 1u)) ++kb;
         return kb;
     };
+    if (next_vis(kb0) >= kb1) {
+        // no row of the tile sees a key of this split: zero rows, lse = -inf;
+        // the whole workgroup leaves here with nothing in flight
+        if (row_ok) {
+            uint16_t *op;
+            if (nchunks == 1) {
+                const int64_t orow = ((int64_t)b * a.N + node) * a.Hq + hq;
+                op = (uint16_t *)a.out + orow * kD + half * 4;
+                if (a.lse && half == 0) a.lse[orow] = -INFINITY;
+            } else {
+                const int64_t prow = ((int64_t)cg * a.Hkv + g) * a.R + r;
+                op = a.part_o + prow * kD + half * 4;
+                if (half == 0) a.part_lse[prow] = -INFINITY;
+            }
+#pragma unroll
+            for (int d = 0; d < kD / 32; ++d)
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) *(u32x2 *)(op + d * 32 + gq * 8) = u32x2{0u, 0u};
+        }
+        if (tid == 0 && s_bad && a.page_status) *a.page_status = JF_ERR_BAD_PAGE;
+        return;
+    }
 
     SoftmaxState S;
 #pragma unroll
