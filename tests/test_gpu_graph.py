@@ -1,0 +1,97 @@
+"""The whole draft step (mask, fused projection, tree attention, top-k)
+captured once in a HIP graph and replayed: every replay must reproduce the
+eager step bit for bit.  Between replays the outputs are overwritten and
+unrelated eager work runs, so a replay that skipped or reused work shows.
+The entry points take every buffer from the caller and issue no memset or
+allocation, which is what makes them capturable."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import dev_tensor, say
+from tree_causal_draft_parent_amd import jf, synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _setup(i):
+    wl = synth.workload(i)
+    inp = synth.make_workload(i)
+    dt = wl.dtype
+    a = inp["attn"]
+    d = {k: dev_tensor(a[k], dt) for k in ("q", "k_tree", "v_tree", "k_cache", "v_cache")}
+    d["parent"] = dev_tensor(a["parent"])
+    d["block_table"] = dev_tensor(a["block_table"])
+    xt = dev_tensor(inp["fuse"]["x"], dt)
+    d["xs"] = [xt[l] for l in range(wl.n_fused)]
+    d["w"] = dev_tensor(inp["fuse"]["w"], dt)
+    d["logits"] = dev_tensor(inp["logits"], dt)
+    B, N, R = wl.B, wl.N, wl.B * wl.N
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    code = jf.JF_BF16 if dt == "bf16" else jf.JF_F32
+    o = dict(
+        mask=torch.empty((B, N, (N + 63) // 64), dtype=torch.int64, device="cuda"),
+        depth=torch.empty((B, N), dtype=torch.int32, device="cuda"),
+        seq_status=torch.empty((B,), dtype=torch.int32, device="cuda"),
+        y=torch.empty((R, wl.H), dtype=tdt, device="cuda"),
+        out=torch.empty_like(d["q"]),
+        lse=torch.empty((B, N, wl.Hq), dtype=torch.float32, device="cuda"),
+        idx=torch.empty((R, wl.topk), dtype=torch.int32, device="cuda"),
+        val=torch.empty((R, wl.topk), dtype=torch.float32, device="cuda"),
+        rlse=torch.empty((R,), dtype=torch.float32, device="cuda"),
+    )
+    ws = dict(
+        fuse=torch.empty(max(jf.jf_fuse_proj_workspace_size(R, wl.H, wl.n_fused, wl.H, code), 1),
+                         dtype=torch.uint8, device="cuda"),
+        attn=torch.empty(max(jf.jf_tree_attn_workspace_size(B, N, wl.Hq, wl.Hkv, wl.D, a["page_size"],
+                                                            a["prefix_len"], code), 1),
+                         dtype=torch.uint8, device="cuda"),
+        topk=torch.empty(max(jf.jf_node_topk_workspace_size(R, wl.V, wl.topk), 1),
+                         dtype=torch.uint8, device="cuda"),
+    )
+    page_status = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def step():
+        jf.jf_tree_mask_build(d["parent"], o["mask"], o["depth"], o["seq_status"])
+        jf.jf_fuse_proj(d["xs"], d["w"], y=o["y"], workspace=ws["fuse"])
+        jf.jf_tree_attn_fwd(d["q"], d["k_tree"], d["v_tree"], o["mask"], d["k_cache"], d["v_cache"],
+                            d["block_table"], a["prefix_len"], out=o["out"], lse=o["lse"],
+                            workspace=ws["attn"], page_status=page_status)
+        jf.jf_node_topk(d["logits"], wl.topk, idx=o["idx"], val=o["val"], lse=o["rlse"],
+                        workspace=ws["topk"])
+
+    return wl, d, o, step
+
+
+@pytest.mark.parametrize("i", [2, 3])
+def test_step_graph_replays_match_eager(i):
+    wl, d, o, step = _setup(i)
+    say(f"graph replay: workload {wl.name}")
+    step()
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in o.items()}
+    # a few eager steps on a side stream before capture, as capture requires
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(2):
+            step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    other = torch.randn(64, 4096, device="cuda").to(torch.bfloat16)
+    for rep in range(4):
+        for v in o.values():                         # stale results must not survive
+            if v.dtype.is_floating_point:
+                v.fill_(float("nan"))
+            else:
+                v.fill_(-7)
+        jf.jf_node_topk(other, 8)                    # unrelated eager work in between
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in o:
+            assert torch.equal(o[k], ref[k]), (rep, k)
