@@ -284,6 +284,15 @@ __device__ __forceinline__ uint32_t half_bits(uint64_t vis, int half) {
     return (uint32_t)(x | (x >> 16));
 }
 
+// Barrier that publishes LDS writes only: unlike __syncthreads it does not
+// wait for outstanding global loads (the query fragments are in flight while
+// the set-up runs).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // kPaged = false: every prefix is one page (page_mode 1); true: page_mode 0 or 2.
 template <bool kPaged>
 __global__ __launch_bounds__(kNW * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -324,8 +333,18 @@ void k_tree_attn_split(AttnArgs a) {
     c.kc0 = a.k_cache;
     c.vc0 = a.v_cache;
     c.pzero = false;
+    // ---- this lane's query row and mask dword ----
+    const int r = qt * kTQ + wave * 32 + l32;
+    const bool row_ok = r < a.R;
+    const int node = row_ok ? r / a.G : 0;
+    const int hq = g * a.G + (row_ok ? r % a.G : 0);
+    {
+        const int rm = qt * kTQ + (tid >> 1);
+        c.mrow = rm < a.R ? (uint32_t)((((int64_t)b * a.N + rm / a.G) * a.W) * 8 + (tid & 1) * 4) : kOob;
+    }
+
     if (tid == 0) { s_used = 0u; s_bad = 0; }
-    __syncthreads();
+    lds_barrier();
 
     // ---- page ids of this split's prefix range ----
     c.page0 = 0;
@@ -359,18 +378,19 @@ void k_tree_attn_split(AttnArgs a) {
         }
     }
 
-    // ---- this lane's query row and mask dword ----
-    const int r = qt * kTQ + wave * 32 + l32;
-    const bool row_ok = r < a.R;
-    const int node = row_ok ? r / a.G : 0;
-    const int hq = g * a.G + (row_ok ? r % a.G : 0);
+    // ---- queries (Q^T fragments in registers), issued before the mask scan
+    // and the first copies so that their latency overlaps that work; the
+    // first ring wait covers them (loads complete in issue order).  They come
+    // after the page-table reads above, whose own waits would otherwise also
+    // wait for them.
+    u32x4 qraw[kD / 16];
     {
-        const int rm = qt * kTQ + (tid >> 1);
-        c.mrow = rm < a.R ? (uint32_t)((((int64_t)b * a.N + rm / a.G) * a.W) * 8 + (tid & 1) * 4) : kOob;
+        const __amdgpu_buffer_rsrc_t r_q = make_rsrc(a.q, a.q_bytes);
+        const uint32_t qoff = row_ok ? (uint32_t)(((((int64_t)b * a.N + node) * a.Hq + hq) * kD + half * 8) * 2) : kOob;
+        load_q(qraw, r_q, qoff);
     }
-
     // ---- which tree blocks of this split does any row of the tile see? ----
-    __syncthreads();   // s_pages / s_bad written above
+    lds_barrier();   // s_pages / s_bad written above
     if (kb1 > nPB && tid < kTQ) {
         const int rr = qt * kTQ + tid;
         if (rr < a.R) {
@@ -381,7 +401,7 @@ void k_tree_attn_split(AttnArgs a) {
             if (bits) atomicOr(&s_used, bits);
         }
     }
-    __syncthreads();
+    lds_barrier();
     const uint32_t used = __builtin_amdgcn_readfirstlane(s_used);   // uniform: block choice stays scalar
     auto next_vis = [&](int kb) {        // first visible block >= kb (kb1 if none)
         while (kb < kb1 && kb >= nPB && !((used >> (kb - nPB)) & 1u)) ++kb;
@@ -407,6 +427,7 @@ void k_tree_attn_split(AttnArgs a) {
                 for (int gq = 0; gq < 4; ++gq) *(u32x2 *)(op + d * 32 + gq * 8) = u32x2{0u, 0u};
         }
         if (tid == 0 && s_bad && a.page_status) *a.page_status = JF_ERR_BAD_PAGE;
+        __builtin_amdgcn_s_waitcnt(0);   // the query loads have returned
         return;
     }
 
@@ -423,22 +444,14 @@ void k_tree_attn_split(AttnArgs a) {
     auto stage_of = [&](int j) { return (const lds_t *)&ring[j % kNS][0]; };
 
     // visible blocks in order: v(0), v(1), ... ; block v(j) goes to stage j % kNS.
-    // Issue order: block 0, this lane's query fragments, blocks 1 .. kNS-2, so
-    // that waiting for block 0 and the queries leaves the later blocks in
-    // flight (loads complete in issue order).
+    // Issue order: the query fragments (above), blocks 0 .. kNS-2, so that
+    // waiting for block 0 leaves the later blocks in flight.
     int kb_iss = next_vis(kb0);         // next block to issue
     int n_iss = 0;                      // blocks issued so far
     if (kb_iss < kb1) {
         issue_block<kPaged>(a, c, s_pages, ring0, kb_iss, bad);
         kb_iss = next_vis(kb_iss + 1);
         n_iss = 1;
-    }
-    // ---- queries (Q^T fragments in registers) ----
-    u32x4 qraw[kD / 16];
-    {
-        const __amdgpu_buffer_rsrc_t r_q = make_rsrc(a.q, a.q_bytes);
-        const uint32_t qoff = row_ok ? (uint32_t)(((((int64_t)b * a.N + node) * a.Hq + hq) * kD + half * 8) * 2) : kOob;
-        load_q(qraw, r_q, qoff);
     }
     bf16x8 qf[kD / 16];                 // set from qraw after the first wait
     for (; n_iss < kNS - 1 && kb_iss < kb1; ++n_iss) {
@@ -678,36 +691,49 @@ void k_tree_attn_split(AttnArgs a) {
     float l_run = S.l + __shfl_xor(S.l, 32);
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
     const float lse_v = l_run > 0.f ? S.m * a.scale + logf(l_run) : -INFINITY;
-    if (row_ok) {
-        if (nchunks == 1) {
-            const int64_t orow = ((int64_t)b * a.N + node) * a.Hq + hq;
-            uint16_t *op = (uint16_t *)a.out + orow * kD + half * 4;
+    // The wave's 32 output rows are stored row-contiguous: each lane leaves
+    // its 4-column pieces in LDS (the ring is idle once every copy has landed
+    // and every wave is past its last step), then the wave writes 16-byte
+    // chunks, 1 KiB per store instruction.  (A lane's own pieces would
+    // scatter 8 bytes over 64 rows per store instruction.)
+    ring_barrier<0>();
+    constexpr int kOutRow = kRow + 16;                  // padded row: rows fall on shifted banks
+    lds_t *ob = (lds_t *)&ring[0][0] + wave * 32 * kOutRow;
 #pragma unroll
-            for (int d = 0; d < kD / 32; ++d)
+    for (int d = 0; d < kD / 32; ++d)
 #pragma unroll
-                for (int gq = 0; gq < 4; ++gq) {
-                    u32x2 w;
-                    w[0] = pack_bf16x2(S.o[d][gq * 4 + 0] * inv, S.o[d][gq * 4 + 1] * inv);
-                    w[1] = pack_bf16x2(S.o[d][gq * 4 + 2] * inv, S.o[d][gq * 4 + 3] * inv);
-                    *(u32x2 *)(op + d * 32 + gq * 8) = w;
-                }
-            if (a.lse && half == 0) a.lse[orow] = lse_v;
-        } else {
-            const int64_t prow = ((int64_t)cg * a.Hkv + g) * a.R + r;
-            uint16_t *op = a.part_o + prow * kD + half * 4;
+        for (int gq = 0; gq < 4; ++gq) {
+            u32x2 w;
+            w[0] = pack_bf16x2(S.o[d][gq * 4 + 0] * inv, S.o[d][gq * 4 + 1] * inv);
+            w[1] = pack_bf16x2(S.o[d][gq * 4 + 2] * inv, S.o[d][gq * 4 + 3] * inv);
+            *(__attribute__((address_space(3))) u32x2 *)(ob + l32 * kOutRow + (d * 32 + gq * 8 + half * 4) * 2) = w;
+        }
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
-            for (int d = 0; d < kD / 32; ++d)
-#pragma unroll
-                for (int gq = 0; gq < 4; ++gq) {
-                    u32x2 w;
-                    w[0] = pack_bf16x2(S.o[d][gq * 4 + 0] * inv, S.o[d][gq * 4 + 1] * inv);
-                    w[1] = pack_bf16x2(S.o[d][gq * 4 + 2] * inv, S.o[d][gq * 4 + 3] * inv);
-                    *(u32x2 *)(op + d * 32 + gq * 8) = w;
-                }
-            if (half == 0) a.part_lse[prow] = lse_v;
+    for (int c = 0; c < 32 * (kRow / 16) / kWave; ++c) {
+        const int idx = c * kWave + lane, row = idx >> 4, ch = idx & 15;
+        const int rr = qt * kTQ + wave * 32 + row;
+        const u32x4 v = *(const __attribute__((address_space(3))) u32x4 *)(ob + row * kOutRow + ch * 16);
+        if (rr < a.R) {
+            int64_t orow;
+            uint16_t *base;
+            if (nchunks == 1) {
+                orow = ((int64_t)b * a.N + rr / a.G) * a.Hq + g * a.G + rr % a.G;
+                base = (uint16_t *)a.out;
+            } else {
+                orow = ((int64_t)cg * a.Hkv + g) * a.R + rr;
+                base = a.part_o;
+            }
+            *(u32x4 *)(base + orow * kD + ch * 8) = v;
         }
     }
-    ring_barrier<0>();   // no copy is left in flight when the workgroup ends
+    if (row_ok && half == 0) {
+        if (nchunks == 1) {
+            if (a.lse) a.lse[((int64_t)b * a.N + node) * a.Hq + hq] = lse_v;
+        } else {
+            a.part_lse[((int64_t)cg * a.Hkv + g) * a.R + r] = lse_v;
+        }
+    }
     if (tid == 0 && s_bad && a.page_status) *a.page_status = JF_ERR_BAD_PAGE;
 }
 
