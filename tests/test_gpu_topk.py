@@ -80,3 +80,20 @@ def test_qwen3_30b_rows_full_size_sampled():
     bits = synth.make_logits(R=w.B * w.N, V=w.V, dtype="bf16", seed=1017)
     rows = np.random.default_rng(0).choice(w.B * w.N, size=96, replace=False)
     _check(bits, "bf16", w.topk, rows=np.sort(rows))
+
+
+# 128 rows or more with at most 16 slices a row take the one-block-a-row path
+# (slices merged in LDS); these cases cover it for both dtypes, k = 1 and 64,
+# forced ties and a ragged vocabulary with a padded row stride.
+@pytest.mark.parametrize("dtype,R,V,k", [("bf16", 128, 151936, 1), ("bf16", 128, 151936, 64),
+                                         ("f32", 128, 50000, 8), ("bf16", 130, 4099, 8)])
+def test_one_block_per_row_path(dtype, R, V, k):
+    ld = V if V % 8 == 0 else (V + 7) // 8 * 8 + 8       # padded row stride for the ragged case
+    bits = synth.make_logits(R=R, V=V, dtype=dtype, seed=R + V + k)
+    _check(bits, dtype, k, ld=ld)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_one_block_per_row_ties(dtype):
+    bits = synth.tie_forcing_logits(synth.make_logits(R=128, V=20000, dtype=dtype, seed=9), dtype)
+    _check(bits, dtype, 8)

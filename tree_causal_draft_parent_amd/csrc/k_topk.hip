@@ -27,6 +27,8 @@ namespace jf {
 namespace {
 
 constexpr int kT1Waves = 4;
+constexpr int kFuseWaves = 16;    // one block a row: up to 16 slices
+constexpr int kFuseMinRows = 128; // rows that fill the chip with one block a row
 constexpr int kCap = 512;     // survivors a wave can buffer before the selection from memory
 constexpr int kMaxVec = 19;   // 16-byte vectors per lane a wave holds in registers
 constexpr int kHot = 16;      // hot lanes whose vectors go through LDS
@@ -117,17 +119,24 @@ template <> struct Vec<float> {
     __device__ static float widen(uint32_t b) { return __uint_as_float(b); }
 };
 
-template <typename T, bool kLse>
-__global__ __launch_bounds__(kT1Waves * kWave) void k_topk_stage1(
+// kFused = false: kWB waves a block, one (row, slice) a wave; the k best keys
+// and (max, sum-exp) of every slice go to the workspace for the merge kernel.
+// kFused = true: one block a row, wave c taking slice c (chunks <= kWB); the
+// slices' results stay in LDS and wave 0 merges them.
+template <typename T, bool kLse, int kWB, bool kFused>
+__global__ __launch_bounds__(kWB * kWave) void k_topk_stage1(
     const T *__restrict__ logits, int64_t ld, int64_t V, int64_t chunk_len, int chunks, int64_t R,
-    int k, uint64_t *__restrict__ cand, float2 *__restrict__ stats) {
-    __shared__ __attribute__((aligned(16))) uint64_t sbuf[kT1Waves][kCap];
-    __shared__ __attribute__((aligned(16))) u32x4 hbuf[kT1Waves][kHot * kMaxVec];
-    __shared__ int hlane[kT1Waves][kHot];
+    int k, uint64_t *__restrict__ cand, float2 *__restrict__ stats, int32_t *__restrict__ idx,
+    float *__restrict__ val, float *__restrict__ lse) {
+    __shared__ __attribute__((aligned(16))) uint64_t sbuf[kWB][kCap];
+    __shared__ __attribute__((aligned(16))) u32x4 hbuf[kWB][kHot * kMaxVec];
+    __shared__ int hlane[kWB][kHot];
+    __shared__ __attribute__((aligned(16))) uint64_t mkeys[kFused ? kWB * 64 : 2];   // slices' k best
+    __shared__ float2 mstats[kFused ? kWB : 1];
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));   // wave-uniform
-    const int64_t gw = (int64_t)blockIdx.x * kT1Waves + wv;
-    if (gw >= R * chunks) return;  // whole wave leaves; no block barriers below
+    const int64_t gw = kFused ? (int64_t)blockIdx.x * chunks + wv : (int64_t)blockIdx.x * kWB + wv;
+    if (!kFused && gw >= R * chunks) return;  // whole wave leaves; no block barriers below
     const int64_t r = gw / chunks;
     const int c = (int)(gw % chunks);
     const int64_t start = (int64_t)c * chunk_len;
@@ -368,7 +377,7 @@ __global__ __launch_bounds__(kT1Waves * kWave) void k_topk_stage1(
             }
         }
 
-        uint64_t *out = cand + ((int64_t)r * chunks + c) * k;
+        uint64_t *out = kFused ? mkeys + c * k : cand + ((int64_t)r * chunks + c) * k;
         if (tot <= kCap) {
             __builtin_amdgcn_wave_barrier();
             // every buffered survivor learns its rank; the k best write themselves
@@ -404,11 +413,44 @@ __global__ __launch_bounds__(kT1Waves * kWave) void k_topk_stage1(
                 s = s * __builtin_amdgcn_exp2f(m * kLog2e - bn) + so * __builtin_amdgcn_exp2f(mo * kLog2e - bn);
                 m = mn;
             }
-            if (lane == 0) stats[(int64_t)r * chunks + c] = make_float2(m, s);
+            if (lane == 0) {
+                if (kFused) mstats[c] = make_float2(m, s);
+                else stats[(int64_t)r * chunks + c] = make_float2(m, s);
+            }
         }
     };
     if (nv_rt == MAXV) slice(std::integral_constant<int, MAXV>());
     else slice(nv_rt);
+
+    if constexpr (kFused) {
+        // ---- merge the row's slices (wave 0): rank every candidate among the
+        // chunks * k keys; combine the (max, sum-exp) pairs ----
+        __syncthreads();
+        if (wv != 0) return;
+        const int n = chunks * k;
+        for (int e = lane; e < n; e += kWave) {
+            const uint64_t key = mkeys[e];
+            if (key == 0ull) continue;               // padding of a short slice
+            const int rk = rank_in(mkeys, n, key);
+            if (rk < k) {
+                idx[r * k + rk] = (int32_t)(~(uint32_t)key);
+                val[r * k + rk] = ordered_to_float((uint32_t)(key >> 32));
+            }
+        }
+        if (kLse) {
+            float m = lane < chunks ? mstats[lane].x : -INFINITY;
+            float s = lane < chunks ? mstats[lane].y : 0.f;
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) {
+                float mo = __shfl_xor(m, off), so = __shfl_xor(s, off);
+                float mn = fmaxf(m, mo);
+                float bn = mn == -INFINITY ? 0.f : mn * kLog2e;
+                s = s * __builtin_amdgcn_exp2f(m * kLog2e - bn) + so * __builtin_amdgcn_exp2f(mo * kLog2e - bn);
+                m = mn;
+            }
+            if (lane == 0) lse[r] = m == -INFINITY ? -INFINITY : m + logf(s);
+        }
+    }
 }
 
 constexpr int kMaxCand = 4096;   // chunks * k candidates merged per row
@@ -509,21 +551,31 @@ hipError_t launch_topk(const TopkPlan &p, const void *logits, int64_t ld, jf_dty
     float2 *stats = (float2 *)((char *)workspace + cand_bytes);
     const unsigned g1 = (unsigned)((rows + kT1Waves - 1) / kT1Waves);
     const bool with_lse = lse != nullptr;
-    if (dtype == JF_BF16) {
-        if (with_lse)
-            hipLaunchKernelGGL((k_topk_stage1<uint16_t, true>), dim3(g1), dim3(kT1Waves * kWave), 0, s,
-                               (const uint16_t *)logits, ld, p.V, p.chunk_len, p.chunks, p.R, p.k, cand, stats);
-        else
-            hipLaunchKernelGGL((k_topk_stage1<uint16_t, false>), dim3(g1), dim3(kT1Waves * kWave), 0, s,
-                               (const uint16_t *)logits, ld, p.V, p.chunk_len, p.chunks, p.R, p.k, cand, stats);
-    } else {
-        if (with_lse)
-            hipLaunchKernelGGL((k_topk_stage1<float, true>), dim3(g1), dim3(kT1Waves * kWave), 0, s,
-                               (const float *)logits, ld, p.V, p.chunk_len, p.chunks, p.R, p.k, cand, stats);
-        else
-            hipLaunchKernelGGL((k_topk_stage1<float, false>), dim3(g1), dim3(kT1Waves * kWave), 0, s,
-                               (const float *)logits, ld, p.V, p.chunk_len, p.chunks, p.R, p.k, cand, stats);
+    // One block a row when the row's slices fit one block and the rows alone
+    // fill the chip; else slices as independent waves and a merge kernel.
+    const bool fused = p.chunks <= kFuseWaves && p.R >= kFuseMinRows;
+#define JF_TOPK1(T, L, WB, F, grid, block)                                                           \
+    hipLaunchKernelGGL((k_topk_stage1<T, L, WB, F>), dim3(grid), dim3(block), 0, s, (const T *)logits, \
+                       ld, p.V, p.chunk_len, p.chunks, p.R, p.k, cand, stats, idx, val, lse)
+    if (fused) {
+        const unsigned gr = (unsigned)p.R, bl = (unsigned)(p.chunks * kWave);
+        if (dtype == JF_BF16) {
+            if (with_lse) JF_TOPK1(uint16_t, true, kFuseWaves, true, gr, bl);
+            else JF_TOPK1(uint16_t, false, kFuseWaves, true, gr, bl);
+        } else {
+            if (with_lse) JF_TOPK1(float, true, kFuseWaves, true, gr, bl);
+            else JF_TOPK1(float, false, kFuseWaves, true, gr, bl);
+        }
+        return hipGetLastError();
     }
+    if (dtype == JF_BF16) {
+        if (with_lse) JF_TOPK1(uint16_t, true, kT1Waves, false, g1, kT1Waves * kWave);
+        else JF_TOPK1(uint16_t, false, kT1Waves, false, g1, kT1Waves * kWave);
+    } else {
+        if (with_lse) JF_TOPK1(float, true, kT1Waves, false, g1, kT1Waves * kWave);
+        else JF_TOPK1(float, false, kT1Waves, false, g1, kT1Waves * kWave);
+    }
+#undef JF_TOPK1
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (with_lse)
