@@ -533,6 +533,8 @@ void k_tree_attn_split(AttnArgs a) {
     // One pipelined step: finish block j (scores sc, maximum already folded
     // into S.m) while computing the scores sn of block j+1 (if has_next).
     //   region A: the 16 score MFMAs of block j+1 | exps of keys 0-31 of block j
+    //             (slot t: k-step t of both key halves, so that the two
+    //             accumulation chains of a wave interleave)
     //   region B: O += V^T P^T for keys 0-31      | exps of keys 32-63
     //             O += V^T P^T for keys 32-63     | row maximum of block j+1
     // Each slot pairs MFMAs with a matching amount of VALU work (an exp runs
@@ -544,7 +546,7 @@ void k_tree_attn_split(AttnArgs a) {
                     f32x16 &sc0, f32x16 &sc1, f32x16 &sn0, f32x16 &sn1) -> float {
         constexpr bool has_next = decltype(next_tag)::value;
         const float nb = S.m == -INFINITY ? 0.f : -S.m * a.c2;
-        float ls = 0.f;
+        float ls[2] = {0.f, 0.f};                  // two partial row sums: shorter dependency chains
         u32x4 pw[4];
         // exps of registers i, i+1 of tile sx as one bf16 pair; the row sum
         // uses the same bf16 probabilities as the MFMA
@@ -552,8 +554,9 @@ void k_tree_attn_split(AttnArgs a) {
             const float e0 = __builtin_amdgcn_exp2f(fmaf(sx[i], a.c2, nb));
             const float e1 = __builtin_amdgcn_exp2f(fmaf(sx[i + 1], a.c2, nb));
             const uint32_t w = pack_bf16x2(e0, e1);
-            ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w),
-                                                 __builtin_bit_cast(bf16x2_t, 0x3f803f80u), ls, false);
+            float &acc = ls[(i >> 1) & 1];
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w),
+                                                  __builtin_bit_cast(bf16x2_t, 0x3f803f80u), acc, false);
             return w;
         };
         const lds_t *kb_ = stn + koff;
@@ -561,37 +564,30 @@ void k_tree_attn_split(AttnArgs a) {
         auto kread = [&](int h, int t) {
             return *(const __attribute__((address_space(3))) bf16x8 *)(kb_ + h * 2 * kRow + t * 32);
         };
-        // K operands of slot t: k-steps u, u+1 of half h (t = 4h + u/2); read two slots ahead
+        // K operands of slot t: k-step t of both key halves (two independent
+        // accumulation chains per slot); read two slots ahead
         bf16x8 kr[3][2];
         auto kload = [&](int t, bf16x8 (&dst)[2]) {
-            const int h = t >> 2, u = (t & 3) * 2;
-            dst[0] = kread(h, u);
-            dst[1] = kread(h, u + 1);
+            dst[0] = kread(0, t);
+            dst[1] = kread(1, t);
         };
         if constexpr (has_next) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) sn0[i] = 0.f;
+            for (int i = 0; i < 16; ++i) { sn0[i] = 0.f; sn1[i] = 0.f; }
             kload(0, kr[0]);
             kload(1, kr[1]);
         }
-        // ---- region A: slot t = two score MFMAs of block j+1 + two exps of sc0 ----
+        // ---- region A: slot t = k-step t of both key halves of block j+1 + two exps of sc0 ----
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
             if constexpr (has_next) {
-                const int h = t >> 2, u = (t & 3) * 2;       // k-steps u, u+1 of half h
                 if (t + 2 < 8) kload(t + 2, kr[(t + 2) % 3]);
-                if (t == 4) {
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) sn1[i] = 0.f;
-                }
-                f32x16 &acc = h == 0 ? sn0 : sn1;
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[t % 3][0], qf[u], acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[t % 3][1], qf[u + 1], acc, 0, 0, 0);
+                sn0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[t % 3][0], qf[t], sn0, 0, 0, 0);
+                sn1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[t % 3][1], qf[t], sn1, 0, 0, 0);
             }
             uint32_t w = exp_pair(sc0, 2 * t);               // registers 2t, 2t+1 of sc0
             if constexpr (has_next) {
-                if (t < 4) asm volatile("" : "+v"(sn0), "+v"(w));
-                else asm volatile("" : "+v"(sn1), "+v"(w));
+                asm volatile("" : "+v"(sn0), "+v"(sn1), "+v"(w));
             } else {
                 asm volatile("" : "+v"(w));
             }
@@ -604,7 +600,7 @@ void k_tree_attn_split(AttnArgs a) {
         p[0] = as_bf16x8(pw[0]);
         p[1] = as_bf16x8(pw[1]);
         // ---- region B: slot m = one output MFMA + (two exps of sc1 | row max) ----
-        float mxn = -INFINITY;
+        float mxn = -INFINITY, mxn1 = -INFINITY;   // row maximum of block j+1, one chain per key half
         // V^T operand of slot m (d = m%4, k-substep kk = m/4) is idx 4d + kk; read two slots ahead
         bf16x8 vr[3];
         vr[0] = vread(stj, 0);
@@ -626,14 +622,15 @@ void k_tree_attn_split(AttnArgs a) {
             } else if constexpr (has_next) {
                 const int i = 2 * (m - 8);                   // registers i, i+1 of both tiles
                 mxn = fmaxf(fmaxf(mxn, sn0[i]), sn0[i + 1]);
-                mxn = fmaxf(fmaxf(mxn, sn1[i]), sn1[i + 1]);
-                asm volatile("" : "+v"(S.o[d]), "+v"(mxn));
+                mxn1 = fmaxf(fmaxf(mxn1, sn1[i]), sn1[i + 1]);
+                asm volatile("" : "+v"(S.o[d]), "+v"(mxn), "+v"(mxn1));
             } else {
                 asm volatile("" : "+v"(S.o[d]));
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        S.l += ls;
+        S.l += ls[0] + ls[1];
+        mxn = fmaxf(mxn, mxn1);
         return has_next ? fmaxf(mxn, __shfl_xor(mxn, 32)) : -INFINITY;
     };
 
