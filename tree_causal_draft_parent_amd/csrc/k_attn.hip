@@ -275,6 +275,17 @@ __device__ __forceinline__ void ring_wait(int n) {
     else ring_barrier<0>();
 }
 
+// A row's statistics live in lanes l and l + 32: combine them with one
+// v_permlane32_swap (lanes l and l ^ 32 exchange in registers; no LDS trip).
+__device__ __forceinline__ float max_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Register i of a half-wave's score tile holds key 4*(2*(i/4) + half) + i%4
 // (+32 for the second tile).
 __device__ __forceinline__ uint32_t half_bits(uint64_t vis, int half) {
@@ -499,7 +510,7 @@ void k_tree_attn_split(AttnArgs a) {
         float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
         for (int i = 1; i < 16; ++i) mx = fmaxf(fmaxf(mx, s0[i]), s1[i]);
-        return fmaxf(mx, __shfl_xor(mx, 32));
+        return max_halves(mx);
     };
     // move the running maximum when the block's maximum exceeds it by > 2^8
     auto rescale = [&](float mx) {
@@ -631,7 +642,7 @@ void k_tree_attn_split(AttnArgs a) {
         }
         S.l += ls[0] + ls[1];
         mxn = fmaxf(mxn, mxn1);
-        return has_next ? fmaxf(mxn, __shfl_xor(mxn, 32)) : -INFINITY;
+        return has_next ? max_halves(mxn) : -INFINITY;
     };
 
     // ---- main loop over the visible blocks ----
@@ -685,7 +696,7 @@ void k_tree_attn_split(AttnArgs a) {
     }
 
     if (bad) s_bad = 1;  // benign race: every writer stores 1
-    float l_run = S.l + __shfl_xor(S.l, 32);
+    float l_run = sum_halves(S.l);
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
     const float lse_v = l_run > 0.f ? S.m * a.scale + logf(l_run) : -INFINITY;
     // The wave's 32 output rows are stored row-contiguous: each lane leaves
@@ -738,18 +749,20 @@ void k_tree_attn_split(AttnArgs a) {
 // w_s = exp(lse_s - max lse); lse = max + log sum w_s.  Sixteen threads per
 // row, eight output columns (one 16-byte load per split) each; one pass over
 // the splits, eight at a time, rescaling when the running maximum moves.
+// The grid's y index is the sequence, so that the split range of a block is
+// uniform (scalar kernel-argument reads, no dependent vector load).
 constexpr int kMergeTPR = kD / 8;        // threads per row
 __global__ __launch_bounds__(256) void k_tree_attn_merge(AttnArgs a) {
     const int sub = threadIdx.x % kMergeTPR;
-    const int64_t flat = (int64_t)blockIdx.x * (256 / kMergeTPR) + threadIdx.x / kMergeTPR;
-    const int64_t total = (int64_t)a.B * a.N * a.Hq;
-    if (flat >= total) return;
-    const int hq = (int)(flat % a.Hq);
-    const int node = (int)((flat / a.Hq) % a.N);
-    const int b = (int)(flat / ((int64_t)a.Hq * a.N));
+    const int b = blockIdx.y;
     const int c0 = a.chunk_start[b];
     const int nc = a.chunk_start[b + 1] - c0;
-    if (nc == 1) return;
+    if (nc == 1) return;                                     // written by the split kernel
+    const int in_seq = blockIdx.x * (256 / kMergeTPR) + threadIdx.x / kMergeTPR;
+    if (in_seq >= a.N * a.Hq) return;
+    const int64_t flat = (int64_t)b * a.N * a.Hq + in_seq;
+    const int hq = in_seq % a.Hq;
+    const int node = in_seq / a.Hq;
     const int g = hq / a.G;
     const int r = node * a.G + hq % a.G;
     const int64_t stride = (int64_t)a.Hkv * a.R;             // rows between consecutive splits
@@ -1009,10 +1022,10 @@ hipError_t launch_tree_attn_bf16(const AttnPlan &p, const void *q, const void *k
         hipLaunchKernelGGL(k_tree_attn_split<true>, dim3(p.total_items), dim3(kNW * kWave), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !p.any_split) return e;
-    const int64_t total = (int64_t)p.B * p.N * p.Hq;
+    const int64_t per_seq = (int64_t)p.N * p.Hq;
     const int64_t rows_per_wg = 256 / kMergeTPR;
-    hipLaunchKernelGGL(k_tree_attn_merge, dim3((unsigned)((total + rows_per_wg - 1) / rows_per_wg)), dim3(256), 0,
-                       s, a);
+    hipLaunchKernelGGL(k_tree_attn_merge, dim3((unsigned)((per_seq + rows_per_wg - 1) / rows_per_wg), (unsigned)p.B),
+                       dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
