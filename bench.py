@@ -121,6 +121,7 @@ def algorithmic(wl, inp, fuse_out_bytes):
     out["attn"] = dict(bytes=B * N * Hq * D * e + 2 * B * N * Hkv * D * e + 2 * sumP * Hkv * D * e
                        + B * N * W * 8 + B * N * Hq * D * e + B * N * Hq * 4,
                        flops=4 * Hq * D * (N * sumP + depth_sum))
+    out["attn_prefix_kv_bytes"] = 2 * sumP * Hkv * D * e
     R = B * N
     out["topk"] = dict(bytes=R * wl.V * e + R * wl.topk * 8 + R * 4, flops=0)
     return out
@@ -326,6 +327,18 @@ def main():
         "cold_ms": round(med(cold_call["attn"]), 5),
         "cold_hbm_GBps": round(ca_gbs, 1), "cold_hbm_frac": round(ca_gbs / HBM_PEAK_GBS, 4),
         "algorithmic": alg["attn"],
+        # the prefix K/V stream alone (2 * sum(P) * Hkv * D elements), the part
+        # the attention must bring from HBM
+        "prefix_kv_bytes": alg["attn_prefix_kv_bytes"],
+        "prefix_kv_GBps": round(alg["attn_prefix_kv_bytes"] / (per_call["attn"] * 1e-3) / 1e9, 1),
+        "prefix_kv_frac": round(alg["attn_prefix_kv_bytes"] / (per_call["attn"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+    }
+    f_gbs, f_tfs = roof("fuse", per_call["fuse"])
+    projection = {
+        "ms": round(per_call["fuse"], 5),
+        "TFLOPs": round(f_tfs, 2), "mfma_frac": round(f_tfs / BF16_PEAK_TFLOPS, 4),
+        "hbm_GBps": round(f_gbs, 1), "hbm_frac": round(f_gbs / HBM_PEAK_GBS, 4),
+        "algorithmic": alg["fuse"],
     }
     calls_out = {}
     for c in calls:
@@ -354,6 +367,7 @@ def main():
         "cold_nodes_per_s": round(B * N / (med(cold) * 1e-3), 1),
         "calls": calls_out,
         "tree_attn": tree_attn,
+        "projection": projection,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -454,6 +454,7 @@ __global__ __launch_bounds__(kWB * kWave) void k_topk_stage1(
 }
 
 constexpr int kMaxCand = 4096;   // chunks * k candidates merged per row
+constexpr int kMergeTarget = 256;  // preferred bound on chunks * k
 
 template <bool kLse>
 __global__ __launch_bounds__(256) void k_topk_stage2(const uint64_t *__restrict__ cand,
@@ -521,6 +522,12 @@ void plan_topk(TopkPlan &p, int64_t R, int64_t V, int k, jf_dtype dtype) {
     // a slice must fit one wave's registers: kMaxVec 16-byte vectors a lane
     const int64_t max_len = (int64_t)kMaxVec * kWave * (dtype == JF_BF16 ? 8 : 4);
     int64_t chunks = (2048 + R - 1) / R;  // aim for >= 2048 wavefronts
+    // ... but the merge ranks every candidate against all chunks * k of them,
+    // so keep that list short (256) unless the slice size forces more slices
+    int64_t cap = kMergeTarget / k;
+    const int64_t min_chunks = (V + max_len - 1) / max_len;
+    if (cap < min_chunks) cap = min_chunks;
+    if (chunks > cap) chunks = cap;
     if (chunks > kMaxCand / k) chunks = kMaxCand / k;
     if (chunks < 1) chunks = 1;
     int64_t len = (V + chunks - 1) / chunks;
