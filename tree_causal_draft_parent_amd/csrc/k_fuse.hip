@@ -10,8 +10,10 @@
 //
 // bf16 path: output tiles of 256x128 (M >= 192: every weight is read once;
 // eight waves, two per SIMD so that one covers the other's LDS and barrier
-// stalls) or 128x128 (four waves), 64-deep K steps, each wave owning 64x64 of
-// the tile as 32x32 blocks of v_mfma_f32_32x32x16_bf16.  A and B tiles go from
+// stalls), 128x128 (four waves) or, for at most 32 rows, 32x128 (four waves
+// side by side along N, a weight stream with a 6-deep ring), 64-deep K steps,
+// each wave owning 64x64 (32x32 for 32-row tiles) of the tile as 32x32
+// blocks of v_mfma_f32_32x32x16_bf16.  A and B tiles go from
 // HBM straight into a 3-stage (256-row tiles) or 4-stage LDS ring with
 // buffer_load ... lds (no registers); one copy fills 1 KiB = 8 K-contiguous rows
 // (rows n, n+T/8, ... of a T-row tile) and 16-byte block padding keeps the
@@ -51,14 +53,14 @@ __device__ __forceinline__ void copy16s(__amdgpu_buffer_rsrc_t r, uint32_t lds, 
 
 template <int BM>
 struct Cfg {
-    static constexpr int kStages = BM == 256 ? 3 : 4;   // copy ring depth (LDS <= 150 KiB)
+    static constexpr int kStages = BM == 256 ? 3 : (BM == 128 ? 4 : 6);   // copy ring depth (LDS <= 150 KiB)
     static constexpr int kWaves = BM == 256 ? 8 : 4;    // 256-row tiles: two waves per SIMD
     static constexpr int kANb = BM / 8;             // LDS blocks of the A tile
     static constexpr int kBNb = kBN / 8;            // 16
     static constexpr int kATile = kANb * kBlkG;
     static constexpr int kBTile = kBNb * kBlkG;
     static constexpr int kStage = kATile + kBTile;
-    static constexpr int WM = BM == 256 ? 4 : 2;    // waves along M
+    static constexpr int WM = BM == 256 ? 4 : (BM == 128 ? 2 : 1);   // waves along M
     static constexpr int WN = kWaves / WM;          // waves along N
     static constexpr int TM = BM / WM / 32;         // 32x32 blocks per wave along M
     static constexpr int TN = kBN / WN / 32;        // ... along N
@@ -170,7 +172,9 @@ __global__ __launch_bounds__(Cfg<BM>::kWaves * kWave) void k_fuse_gemm_bf16(Fuse
     for (int i = 0; i < NS - 1 && i < nk; ++i) issue(ring0 + i * C::kStage, kb + (int64_t)i * kBK);
     for (int i = 0; i < nk; ++i) {
         const int ahead = min(NS - 2, nk - 1 - i);   // steps issued after i and still in flight
-        if (ahead >= 2) ring_barrier<2 * kCopies>();
+        if (ahead >= 4) ring_barrier<(NS >= 6 ? 4 : 0) * kCopies>();
+        else if (ahead == 3) ring_barrier<(NS >= 5 ? 3 : 0) * kCopies>();
+        else if (ahead == 2) ring_barrier<2 * kCopies>();
         else if (ahead == 1) ring_barrier<kCopies>();
         else ring_barrier<0>();
         if (i + NS - 1 < nk)
@@ -283,7 +287,7 @@ void plan_fuse(FusePlan &p, int64_t M, int64_t H_in, int k, int64_t H_out, jf_dt
     p.H_in = H_in;
     p.H_out = H_out;
     p.k = k;
-    p.bm = M >= 192 ? 256 : 128;
+    p.bm = M >= 192 ? 256 : (M > 32 ? 128 : 32);      // 32-row tiles: a weight stream for few rows
     p.bn = kBN;
     const int64_t K = (int64_t)k * H_in;
     if (in_dtype != JF_BF16) {
@@ -331,8 +335,10 @@ hipError_t launch_fuse_bf16(const FusePlan &p, const void *const *x, int64_t ldx
     const unsigned grid = (unsigned)(f.tiles_m * f.tiles_n * f.split_k);
     if (p.bm == 256)
         hipLaunchKernelGGL(k_fuse_gemm_bf16<256>, dim3(grid), dim3(Cfg<256>::kWaves * kWave), 0, s, f);
-    else
+    else if (p.bm == 128)
         hipLaunchKernelGGL(k_fuse_gemm_bf16<128>, dim3(grid), dim3(Cfg<128>::kWaves * kWave), 0, s, f);
+    else
+        hipLaunchKernelGGL(k_fuse_gemm_bf16<32>, dim3(grid), dim3(Cfg<32>::kWaves * kWave), 0, s, f);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.split_k <= 1) return e;
     const int64_t MN = p.M * p.H_out;
