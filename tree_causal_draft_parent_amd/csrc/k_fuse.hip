@@ -108,17 +108,28 @@ __global__ __launch_bounds__(Cfg<BM>::kWaves * kWave) void k_fuse_gemm_bf16(Fuse
     }
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(f.w, f.w_bytes);
 
-    auto issue = [&](uint32_t dst, int64_t kk) {
-        const int layer = (int)(kk / f.H_in);
-        const __amdgpu_buffer_rsrc_t rx = make_rsrc(f.x[layer], f.x_bytes);
-        const uint32_t sa = (uint32_t)((kk - (int64_t)layer * f.H_in) * 2);
-        const uint32_t sb = (uint32_t)(kk * 2);
+    // Copies are issued in K order, so the layer of the next step and the
+    // offset inside it advance by one K step at a time (H_in is a multiple
+    // of the K step); no division per step.
+    int ilayer = (int)(kb / f.H_in);
+    uint32_t ioff = (uint32_t)((kb - (int64_t)ilayer * f.H_in) * 2);   // bytes into the layer's rows
+    uint32_t ikk = (uint32_t)(kb * 2);                                  // bytes into the weight rows
+    const uint32_t layer_bytes = (uint32_t)(f.H_in * 2);
+    __amdgpu_buffer_rsrc_t rx = make_rsrc(f.x[ilayer], f.x_bytes);
+    auto issue = [&](uint32_t dst) {
         const uint32_t da = __builtin_amdgcn_readfirstlane(dst + wave * C::kACopies * kBlkG);
         const uint32_t db = __builtin_amdgcn_readfirstlane(dst + C::kATile + wave * C::kBCopies * kBlkG);
 #pragma unroll
-        for (int i = 0; i < C::kACopies; ++i) copy16s(rx, da + i * kBlkG, aoff[i], sa);
+        for (int i = 0; i < C::kACopies; ++i) copy16s(rx, da + i * kBlkG, aoff[i], ioff);
 #pragma unroll
-        for (int i = 0; i < C::kBCopies; ++i) copy16s(rw, db + i * kBlkG, boff[i], sb);
+        for (int i = 0; i < C::kBCopies; ++i) copy16s(rw, db + i * kBlkG, boff[i], ikk);
+        ikk += kBK * 2;
+        ioff += kBK * 2;
+        if (ioff == layer_bytes && ilayer + 1 < kMaxLayers) {
+            ioff = 0;
+            ++ilayer;
+            rx = make_rsrc(f.x[ilayer], f.x_bytes);
+        }
     };
 
     f32x16 acc[C::TM][C::TN];
@@ -130,56 +141,67 @@ __global__ __launch_bounds__(Cfg<BM>::kWaves * kWave) void k_fuse_gemm_bf16(Fuse
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     // operand bases: A rows wm*(BM/WM) + i*32 + l32, B rows wn*(128/WN) + j*32 + l32
-    auto compute = [&](const lds_t *st) {
-        const lds_t *abase = st + g_lds(wm * (BM / C::WM) + l32, C::kANb) + half * 16;
-        const lds_t *bbase = st + C::kATile + g_lds(wn * (kBN / C::WN) + l32, C::kBNb) + half * 16;
-        auto rd = [&](int t, bf16x8 *av, bf16x8 *bv) {
+    const int a_lane = g_lds(wm * (BM / C::WM) + l32, C::kANb) + half * 16;
+    const int b_lane = C::kATile + g_lds(wn * (kBN / C::WN) + l32, C::kBNb) + half * 16;
+    auto rd = [&](const lds_t *st, int t, bf16x8 *av, bf16x8 *bv) {
 #pragma unroll
-            for (int i = 0; i < C::TM; ++i)
-                av[i] = *(const __attribute__((address_space(3))) bf16x8 *)(abase + (i * 32 / C::kANb) * kRowG + t * 32);
+        for (int i = 0; i < C::TM; ++i)
+            av[i] = *(const __attribute__((address_space(3))) bf16x8 *)(st + a_lane + (i * 32 / C::kANb) * kRowG + t * 32);
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j)
+            bv[j] = *(const __attribute__((address_space(3))) bf16x8 *)(st + b_lane + (j * 32 / C::kBNb) * kRowG + t * 32);
+    };
+    auto mma = [&](const bf16x8 *av, const bf16x8 *bv) {
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i)
 #pragma unroll
             for (int j = 0; j < C::TN; ++j)
-                bv[j] = *(const __attribute__((address_space(3))) bf16x8 *)(bbase + (j * 32 / C::kBNb) * kRowG + t * 32);
-        };
-        bf16x8 a0[C::TM], b0[C::TN], a1[C::TM], b1[C::TN];
-        rd(0, a0, b0);
-#pragma unroll
-        for (int t = 0; t < kBK / 16; t += 2) {
-            rd(t + 1, a1, b1);
-#pragma unroll
-            for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-                for (int j = 0; j < C::TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[i], b0[j], acc[i][j], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-            if (t + 2 < kBK / 16) rd(t + 2, a0, b0);
-#pragma unroll
-            for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-                for (int j = 0; j < C::TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[i], b1[j], acc[i][j], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-        }
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
     };
 
     // Copy ring: step i lives in stage i % NS; steps i+1 .. i+NS-1 are in
     // flight while step i is multiplied.  Each wave issues kCopies copies a
     // step, so "step i has landed" is "at most kCopies * (steps issued after
-    // i) copies outstanding".
+    // i) copies outstanding".  The wait and barrier for step i+1 sit before
+    // the last MFMA group of step i, and the first operands of step i+1 are
+    // read while that group runs; a wave issues the copies of step i+NS-1
+    // (into the stage of step i-1, which every wave finished reading before
+    // that barrier) after the first MFMA group of step i.
     constexpr int NS = C::kStages;
+    static_assert(NS >= 3, "the ring needs three stages or more");
+    static_assert(kBK / 16 == 4, "four 16-deep MFMA groups per K step");
     constexpr int kCopies = C::kACopies + C::kBCopies;
     const uint32_t ring0 = (uint32_t)(uintptr_t)(lds_t *)&ring[0][0];
-    for (int i = 0; i < NS - 1 && i < nk; ++i) issue(ring0 + i * C::kStage, kb + (int64_t)i * kBK);
-    for (int i = 0; i < nk; ++i) {
+    auto wait_step = [&](int i) {
         const int ahead = min(NS - 2, nk - 1 - i);   // steps issued after i and still in flight
         if (ahead >= 4) ring_barrier<(NS >= 6 ? 4 : 0) * kCopies>();
         else if (ahead == 3) ring_barrier<(NS >= 5 ? 3 : 0) * kCopies>();
         else if (ahead == 2) ring_barrier<2 * kCopies>();
         else if (ahead == 1) ring_barrier<kCopies>();
         else ring_barrier<0>();
-        if (i + NS - 1 < nk)
-            issue(ring0 + ((i + NS - 1) % NS) * C::kStage, kb + (int64_t)(i + NS - 1) * kBK);
-        compute((const lds_t *)&ring[i % NS][0]);
+    };
+    auto stage = [&](int i) { return (const lds_t *)&ring[i % NS][0]; };
+    bf16x8 a0[C::TM], b0[C::TN], a1[C::TM], b1[C::TN];
+    for (int i = 0; i < NS - 1 && i < nk; ++i) issue(ring0 + i * C::kStage);
+    if (nk > 0) {
+        wait_step(0);
+        rd(stage(0), 0, a0, b0);
+    }
+    for (int i = 0; i < nk; ++i) {
+        const lds_t *st = stage(i);
+        rd(st, 1, a1, b1);
+        mma(a0, b0);
+        if (i + NS - 1 < nk) issue(ring0 + ((i + NS - 1) % NS) * C::kStage);
+        rd(st, 2, a0, b0);
+        mma(a1, b1);
+        rd(st, 3, a1, b1);
+        mma(a0, b0);
+        if (i + 1 < nk) {
+            wait_step(i + 1);
+            rd(stage(i + 1), 0, a0, b0);
+        }
+        mma(a1, b1);
     }
 
     // lane holds rows (r/4)*8 + half*4 + r%4 of each 32x32 block, column l32
