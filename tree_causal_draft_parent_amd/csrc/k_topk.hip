@@ -180,12 +180,18 @@ __global__ __launch_bounds__(kWB * kWave) void k_topk_stage1(
         // ---- pass 1: lane maximum and the running log-sum-exp ----
         float lmax = -INFINITY;
         float m = -INFINITY, s = 0.f;
+        float base = 0.f;                          // m * log2(e), 0 while m = -inf
         auto lse_add = [&](const float *x, float vmax, int cnt) {
-            if (vmax > m + kLazy) {
-                s *= __builtin_amdgcn_exp2f((m - vmax) * kLog2e);
-                m = vmax;
+            // the running maximum moves rarely once the first vectors are in,
+            // so the rescale sits behind a wave-uniform branch
+            if (__ballot(vmax > m + kLazy)) {
+                asm volatile("");                  // a real branch: not computed speculatively
+                if (vmax > m + kLazy) {
+                    s *= __builtin_amdgcn_exp2f((m - vmax) * kLog2e);
+                    m = vmax;
+                    base = m * kLog2e;
+                }
             }
-            const float base = m == -INFINITY ? 0.f : m * kLog2e;
 #pragma unroll
             for (int j = 0; j < VEC; ++j)
                 if (j < cnt) s += __builtin_amdgcn_exp2f(fmaf(x[j], kLog2e, -base));
