@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--eager", action="store_true",
                     help="time the eager launches (no graph) for the headline value")
     ap.add_argument("--cpu-sample-nodes", type=int, default=256)
+    ap.add_argument("--no-context-projection", action="store_true",
+                    help="skip timing the projection at one row per prefix token")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy 5 times (counter calibration)")
     return ap.parse_args()
@@ -160,6 +162,63 @@ def cpu_baseline(wl, inp, n_nodes, min_seconds=10.0):
                       f"tree attention (all {Hq} heads) and top-{wl.topk}+lse, {reps} times; {dt:.2f} s"}
 
 
+def cpu_baseline_one_thread(wl, inp, n_nodes, min_seconds=5.0):
+    """The same oracle sample on one host thread (a smaller node sample)."""
+    import oracle
+    all_threads = oracle.num_threads()
+    oracle.set_num_threads(1)
+    try:
+        r = cpu_baseline(wl, inp, n_nodes, min_seconds)
+    finally:
+        oracle.set_num_threads(all_threads)
+    return {"value": r["value"], "unit": "nodes/s", "cores": 1, "sample": r["sample"]}
+
+
+def copy_bandwidth(torch, reps=10):
+    """Achievable device-copy rate (bytes read + written per second) of a plain
+    256 MiB torch copy, timed with events on the current stream."""
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    return 2 * COPY_BYTES * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+
+def projection_context(wl, M, steps, torch, jf):
+    """The fused projection over one row per prefix token (M = sum of prefix
+    lengths): the MFMA-bound use of the same call. Inputs are seeded device
+    normals; only the time is used."""
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1000 + M)
+    xs = [(torch.randn((M, wl.H), generator=g, device="cuda")).to(tdt) for _ in range(wl.n_fused)]
+    w = (0.02 * torch.randn((wl.H, wl.n_fused * wl.H), generator=g, device="cuda")).to(tdt)
+    y = torch.empty((M, wl.H), dtype=tdt, device="cuda")
+    ws = torch.empty(max(jf.jf_fuse_proj_workspace_size(M, wl.H, wl.n_fused, wl.H,
+                                                        jf.JF_BF16 if wl.dtype == "bf16" else jf.JF_F32), 1),
+                     dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        jf.jf_fuse_proj(xs, w, y=y, workspace=ws)
+    n = max(1, min(steps, 20))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        jf.jf_fuse_proj(xs, w, y=y, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    flops = 2 * M * wl.H * wl.n_fused * wl.H
+    tfs = flops / (ms * 1e-3) / 1e12
+    return {"M": M, "ms": round(ms, 5), "TFLOPs": round(tfs, 2), "mfma_frac": round(tfs / BF16_PEAK_TFLOPS, 4),
+            "flops": flops, "launches": n}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -243,8 +302,8 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     eager_ms_per_step = (t1 - t0) * 1e3 / K
-    per_call = {c: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(K)]))
-                for i, c in enumerate(calls)}
+    call_ms = {c: [evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(K)] for i, c in enumerate(calls)}
+    per_call = {c: float(np.mean(v)) for c, v in call_ms.items()}
     gpu_step_ms = float(np.mean([evs[k][0].elapsed_time(evs[k][4]) for k in range(K)]))
     print(f"[bench] eager: {K} steps, {eager_ms_per_step:.4f} ms/step", file=sys.stderr, flush=True)
 
@@ -287,6 +346,12 @@ def main():
             cold_call[c].append(ev[i].elapsed_time(ev[i + 1]))
     del flush_buf
     assert int(page_status.item()) == 0 and bool((seq_status == -1).all())
+    copy_gbs = copy_bandwidth(torch)
+    print(f"[bench] device copy: {copy_gbs:.1f} GB/s", file=sys.stderr, flush=True)
+    proj_ctx = None
+    if not args.no_context_projection:
+        proj_ctx = projection_context(wl, int(np.sum(prefix_len)), K, torch, jf)
+        print(f"[bench] context projection: M={proj_ctx['M']} {proj_ctx['ms']:.4f} ms", file=sys.stderr, flush=True)
 
     def med(v):
         return float(np.median(v)) if len(v) else float("nan")
@@ -343,13 +408,19 @@ def main():
     calls_out = {}
     for c in calls:
         g_, t_ = roof(c, per_call[c])
-        calls_out[c] = {"ms": round(per_call[c], 5), "cold_ms": round(med(cold_call[c]), 5),
+        p10, p50, p90 = np.percentile(call_ms[c], [10, 50, 90])
+        calls_out[c] = {"ms": round(per_call[c], 5), "p10_ms": round(float(p10), 5),
+                        "p50_ms": round(float(p50), 5), "p90_ms": round(float(p90), 5),
+                        "cold_ms": round(med(cold_call[c]), 5),
                         "GBps": round(g_, 1), "TFLOPs": round(t_, 2), "bound": bound[c]}
+        if bound[c] == "hbm":
+            calls_out[c]["frac_of_copy"] = round(g_ / copy_gbs, 4)
 
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on host cores", file=sys.stderr, flush=True)
         cpu = cpu_baseline(wl, inp, args.cpu_sample_nodes)
+        cpu["one_thread"] = cpu_baseline_one_thread(wl, inp, max(1, args.cpu_sample_nodes // 16))
 
     value = B * N * K / (t1 - t0)
     rec = {
@@ -368,6 +439,8 @@ def main():
         "calls": calls_out,
         "tree_attn": tree_attn,
         "projection": projection,
+        "projection_context": proj_ctx,
+        "copy_GBps": round(copy_gbs, 1),
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -67,6 +67,8 @@ def _load():
     lib.oracle_topk.restype = None
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+    lib.oracle_set_num_threads.restype = None
     _lib = lib
     return lib
 
@@ -164,3 +166,8 @@ def topk(logits: np.ndarray, k: int, with_lse: bool = True):
 def num_threads() -> int:
     """OpenMP threads the oracle's parallel loops use."""
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Thread count for the oracle's later parallel loops (at least 1)."""
+    _load().oracle_set_num_threads(int(n))

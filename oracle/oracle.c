@@ -274,3 +274,7 @@ void oracle_topk(const double *logits, int64_t R, int64_t V, int64_t k,
 
 /* Threads an OpenMP region of this library uses (for reporting). */
 int oracle_num_threads(void) { return omp_get_max_threads(); }
+
+/* Sets the thread count of later OpenMP regions (n >= 1); used to time the
+   oracle on one core beside the all-core figure. */
+void oracle_set_num_threads(int n) { omp_set_num_threads(n < 1 ? 1 : n); }

@@ -74,3 +74,13 @@ def test_qwen3_8b_high_budget_sampled_rows():
 def test_qwen3_30b_shape_sampled_rows():
     rows = np.sort(np.random.default_rng(4).choice(1024, 32, replace=False))
     _run(synth.make_workload(4, parts=("fuse",))["fuse"], rows=rows)
+
+
+def test_context_rows_sampled():
+    # one row per prefix token of a 4096-token prefix (plus a ragged 4-row tail):
+    # the MFMA-bound shape, 17 x 32 tiles of 256 x 128 with no K split
+    M = 4100
+    rows = np.concatenate([np.sort(np.random.default_rng(6).choice(4096, 28, replace=False)),
+                           np.arange(4096, 4100)])
+    _run(synth.make_fuse_inputs(M=M, H_in=4096, H_out=4096, n_fused=3, dtype="bf16", seed=1019),
+         rows=rows)
