@@ -30,6 +30,7 @@ constexpr int kBN = 128, kBK = 64;
 constexpr int kRowG = kBK * 2;           // bytes per tile row (64 bf16)
 constexpr int kBlkG = 8 * kRowG + 16;    // LDS block: 8 rows + pad
 constexpr int kMaxLayers = 8;
+constexpr int kGroupM = 4;              // m tiles per group of the item order
 constexpr uint32_t kOobRow = 0xf0000000u; // past every buffer even after adding the K offset
 
 struct FuseArgs {
@@ -81,11 +82,19 @@ __global__ __launch_bounds__(Cfg<BM>::kWaves * kWave) void k_fuse_gemm_bf16(Fuse
 
     const int total = f.tiles_m * f.tiles_n * f.split_k;
     const int item = xcd_remap(blockIdx.x, total);
-    // the n tiles of one (m tile, K slice) are neighbours: they share A in L2
-    const int tn = item % f.tiles_n;
-    const int rest = item / f.tiles_n;
-    const int tm = rest % f.tiles_m;
-    const int sk = rest / f.tiles_m;
+    // Grouped order inside a K slice: groups of up to four m tiles, the n tiles
+    // of a group in turn, the m tiles of a group fastest.  An XCD's contiguous
+    // range of items is then a block of m x n tiles that share A rows and
+    // weight rows in its L2 (with one m tile this is plain n-tile order).
+    const int per_slice = f.tiles_m * f.tiles_n;
+    const int sk = item / per_slice;
+    const int t = item % per_slice;
+    const int group = t / (kGroupM * f.tiles_n);
+    const int first_m = group * kGroupM;
+    const int gm = min(f.tiles_m - first_m, kGroupM);
+    const int tin = t % (kGroupM * f.tiles_n);
+    const int tm = first_m + tin % gm;
+    const int tn = tin / gm;
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * kBN;
     const int64_t kb = (int64_t)sk * f.k_per_split;
     const int64_t ke = min(f.K, kb + f.k_per_split);
