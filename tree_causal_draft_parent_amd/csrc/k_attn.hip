@@ -49,6 +49,8 @@
 //     one split writes the final output directly.
 #include "jf_internal.h"
 
+#include <vector>
+
 namespace jf {
 namespace {
 
@@ -908,6 +910,43 @@ __global__ __launch_bounds__(256) void k_tree_attn_f32(AttnArgsF32 a) {
 }  // namespace
 
 // ---------------------------------------------------------------------------
+// Predicted span (in quarter blocks) of the split kernel's workgroups for
+// splits of c blocks: each split gives `per_chunk` workgroups, launched in
+// the kernel's item order, each costing a fixed overhead plus its blocks on
+// the compute unit that frees first.
+static int64_t plan_span(int B, const int32_t *prefix_len, int n_tree_blocks, int c, int per_chunk,
+                         int cus) {
+    constexpr int64_t kOverhead = 16;    // quarter blocks: prologue, partial write and its merge
+    std::vector<int64_t> heap((size_t)cus, 0);   // min-heap of compute-unit free times
+    auto push_pop = [&](int64_t cost) {
+        // replace the minimum (heap[0]) by heap[0] + cost and restore the heap
+        int64_t v = heap[0] + cost;
+        size_t i = 0;
+        const size_t n = heap.size();
+        for (;;) {
+            size_t l = 2 * i + 1, r = l + 1, m = i;
+            int64_t mv = v;
+            if (l < n && heap[l] < mv) { m = l; mv = heap[l]; }
+            if (r < n && heap[r] < mv) { m = r; mv = heap[r]; }
+            if (m == i) break;
+            heap[i] = heap[m];
+            i = m;
+        }
+        heap[i] = v;
+    };
+    for (int b = 0; b < B; ++b) {
+        const int64_t nb = (prefix_len[b] + kKB - 1) / kKB + n_tree_blocks;
+        for (int64_t k0 = 0; k0 < nb; k0 += c) {
+            const int64_t size = (k0 + c < nb ? c : nb - k0) * 4 + kOverhead;
+            for (int w = 0; w < per_chunk; ++w) push_pop(size);
+        }
+    }
+    int64_t span = 0;
+    for (int64_t v : heap) span = v > span ? v : span;
+    return span;
+}
+
+// ---------------------------------------------------------------------------
 // Split planning.  Every (sequence, KV head, query tile) is a row of blocks;
 // cut all rows into splits of the same block count so that about one
 // workgroup per compute unit comes out (a workgroup fills a compute unit's
@@ -943,6 +982,35 @@ void plan_tree_attn(AttnPlan &p, int B, int N, int Hq, int Hkv, int D, int page_
         if (cb > cap) cb = cap;
     }
     if (cb > max_blocks) cb = max_blocks;
+    // Ragged prefixes leave partial splits, and the workgroups can then spill
+    // over one wave of the chip.  Splits of the base size are then compared
+    // with smaller ones by a model of the dispatch (workgroups in launch order,
+    // each to the compute unit that frees first; cost = a fixed per-workgroup
+    // overhead + its block count), and the shortest predicted span is kept.
+    if (dtype != JF_F32) {
+        auto n_items = [&](int64_t c) {
+            int64_t n = 0;
+            for (int b = 0; b < B; ++b) {
+                const int64_t nb = (prefix_len[b] + kKB - 1) / kKB + p.n_tree_blocks;
+                n += (nb + c - 1) / c;
+            }
+            return n * Hkv * p.n_qt;
+        };
+        if (n_items(cb) > target) {
+            const int64_t base = cb;
+            int64_t best = -1;
+            int64_t best_cb = cb;
+            for (int d = 4; d <= 12; ++d) {        // base * 4/d: 1, 0.8, ..., 1/3 of the base size
+                int64_t c = (base * 4 + d - 1) / d;
+                if (c < 2) c = 2;
+                if (d > 4 && c == best_cb) continue;
+                const int64_t span = plan_span(B, prefix_len, p.n_tree_blocks, (int)c, Hkv * p.n_qt,
+                                               (int)target);
+                if (best < 0 || span < best) { best = span; best_cb = c; }
+            }
+            cb = best_cb;
+        }
+    }
     if (dtype == JF_F32) cb = max_blocks;  // the fp32 path does not split
     p.chunk_blocks = (int)cb;
     int cs = 0;
