@@ -60,14 +60,32 @@ def _setup(i):
         jf.jf_node_topk(d["logits"], wl.topk, idx=o["idx"], val=o["val"], lse=o["rlse"],
                         workspace=ws["topk"])
 
-    return wl, d, o, step
+    # the same step on two streams: projection then top-k beside mask then
+    # attention (the projection and the top-k depend on neither)
+    s_side = torch.cuda.Stream()
+
+    def step_streams():
+        main = torch.cuda.current_stream()
+        s_side.wait_stream(main)
+        with torch.cuda.stream(s_side):
+            jf.jf_fuse_proj(d["xs"], d["w"], y=o["y"], workspace=ws["fuse"])
+            jf.jf_node_topk(d["logits"], wl.topk, idx=o["idx"], val=o["val"], lse=o["rlse"],
+                            workspace=ws["topk"])
+        jf.jf_tree_mask_build(d["parent"], o["mask"], o["depth"], o["seq_status"])
+        jf.jf_tree_attn_fwd(d["q"], d["k_tree"], d["v_tree"], o["mask"], d["k_cache"], d["v_cache"],
+                            d["block_table"], a["prefix_len"], out=o["out"], lse=o["lse"],
+                            workspace=ws["attn"], page_status=page_status)
+        main.wait_stream(s_side)
+
+    return wl, d, o, step, step_streams
 
 
-@pytest.mark.parametrize("i", [2, 3])
-def test_step_graph_replays_match_eager(i):
-    wl, d, o, step = _setup(i)
-    say(f"graph replay: workload {wl.name}")
-    step()
+@pytest.mark.parametrize("i,streams", [(2, False), (3, False), (2, True), (3, True)])
+def test_step_graph_replays_match_eager(i, streams):
+    wl, d, o, step_serial, step_streams = _setup(i)
+    step = step_streams if streams else step_serial
+    say(f"graph replay: workload {wl.name}, {'two streams' if streams else 'one stream'}")
+    step_serial()
     torch.cuda.synchronize()
     ref = {k: v.clone() for k, v in o.items()}
     # a few eager steps on a side stream before capture, as capture requires
