@@ -47,6 +47,10 @@ def parse():
     ap.add_argument("--cold-steps", type=int, default=20)
     ap.add_argument("--eager", action="store_true",
                     help="time the eager launches (no graph) for the headline value")
+    ap.add_argument("--attn-cus", type=int, default=-1,
+                    help="compute units the attention's key splits are planned for in the two-stream "
+                         "step (-1: three quarters of the device's when mask + attention is the "
+                         "shorter stream by the eager per-call times, else all; 0: all)")
     ap.add_argument("--one-stream", action="store_true",
                     help="headline from the graph of the step on one stream (default: two streams)")
     ap.add_argument("--cpu-sample-nodes", type=int, default=256)
@@ -318,6 +322,19 @@ def main():
     # tails, and the small kernels (split-K reduce, split merge) overlap the
     # other stream's work.  Same kernels, same arguments.
     s_side = torch.cuda.Stream()
+    # When mask + attention is the shorter of the two streams, the attention
+    # is planned for three quarters of the compute units (fewer, longer key
+    # splits): the units it leaves go to the projection and the top-k, and it
+    # writes fewer partial results.  When it is the longer one it keeps them all.
+    n_cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if args.attn_cus >= 0:
+        attn_cus = args.attn_cus
+    else:
+        shorter = per_call["mask"] + per_call["attn"] < per_call["fuse"] + per_call["topk"]
+        attn_cus = (3 * n_cus) // 4 if shorter else 0
+    aws_side = jf.jf_tree_attn_workspace_size(B, N, wl.Hq, wl.Hkv, wl.D, a["page_size"], prefix_len,
+                                              jf.JF_BF16 if dt == "bf16" else jf.JF_F32, attn_cus)
+    attn_ws_side = torch.empty(max(aws_side, 1), dtype=torch.uint8, device="cuda")
 
     def step_streams():
         main = torch.cuda.current_stream()
@@ -328,7 +345,7 @@ def main():
         jf.jf_tree_mask_build(parent, mask, depth, seq_status)
         jf.jf_tree_attn_fwd(dev["q"], dev["k_tree"], dev["v_tree"], mask, dev["k_cache"],
                             dev["v_cache"], block_table, prefix_len, out=out, lse=lse,
-                            workspace=attn_ws, page_status=page_status)
+                            workspace=attn_ws_side, page_status=page_status, cus=attn_cus)
         main.wait_stream(s_side)
 
     def time_graph(fn):
@@ -465,6 +482,7 @@ def main():
                    "step": "mask+fuse_proj+tree_attn+topk"},
         "launch": "eager" if args.eager else ("hip_graph" if args.one_stream else "hip_graph_2_streams"),
         "graph_one_stream_ms_per_step": None if serial_graph_ms is None else round(serial_graph_ms, 5),
+        "attn_cus_two_streams": attn_cus,
         "eager_ms_per_step": round(eager_ms_per_step, 5),
         "gpu_step_ms": round(gpu_step_ms, 5),
         "cold_step_ms": round(med(cold), 5),

@@ -52,7 +52,7 @@ typedef enum { JF_F32 = 0, JF_BF16 = 1 } jf_dtype;
 const char *jf_status_string(int status);
 
 /* ABI version, bumped on any signature change. */
-int jf_abi_version(void);  /* 2 */
+int jf_abi_version(void);  /* 3 */
 
 /* --------------------------------------------------------------------------
  * jf_tree_mask_build -- ancestor bitmask of every tree node.
@@ -152,6 +152,31 @@ jf_status jf_tree_attn_fwd(const void *q, const void *k_tree,
                            jf_dtype dtype, void *out, float *lse,
                            void *workspace, size_t workspace_bytes,
                            int32_t *page_status, void *stream);
+
+/* --------------------------------------------------------------------------
+ * jf_tree_attn_fwd_cus / jf_tree_attn_workspace_size_cus -- the same
+ * computation (same citation and arguments as above), with the key splits
+ * planned for `cus` compute units instead of all of the device's (cus <= 0
+ * or above the device's count: all).  For a caller that runs other work
+ * beside the attention on another stream: fewer, longer splits leave compute
+ * units to that work and write fewer partial results.  The workspace size
+ * must come from jf_tree_attn_workspace_size_cus with the same cus.  Results
+ * agree with jf_tree_attn_fwd to the rounding of the split combination.
+ * ------------------------------------------------------------------------ */
+size_t jf_tree_attn_workspace_size_cus(int32_t B, int32_t N, int32_t Hq,
+                                       int32_t Hkv, int32_t D, int32_t page_size,
+                                       const int32_t *prefix_len, jf_dtype dtype,
+                                       int32_t cus);
+jf_status jf_tree_attn_fwd_cus(const void *q, const void *k_tree,
+                               const void *v_tree, const uint64_t *mask,
+                               const void *k_cache, const void *v_cache,
+                               int64_t num_pages, int32_t page_size,
+                               const int32_t *block_table, int32_t max_pages,
+                               const int32_t *prefix_len, int32_t B, int32_t N,
+                               int32_t Hq, int32_t Hkv, int32_t D, float scale,
+                               jf_dtype dtype, void *out, float *lse,
+                               void *workspace, size_t workspace_bytes,
+                               int32_t *page_status, int32_t cus, void *stream);
 
 /* --------------------------------------------------------------------------
  * jf_node_topk -- the k best candidates of every node's draft distribution.

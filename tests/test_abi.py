@@ -21,7 +21,7 @@ def _declared():
 
 def test_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 9
+    assert len(names) == 11
     assert sorted(jf.EXPORTS) == names
     L = jf.lib()
     for n in names:
@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
 def test_status_strings_and_version():
     assert jf.status_string(0) == "JF_OK"
     assert jf.status_string(5) == "JF_ERR_BAD_TREE"
-    assert jf.lib().jf_abi_version() == 2
+    assert jf.lib().jf_abi_version() == 3
 
 
 FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: every call below fails validation
@@ -92,6 +92,23 @@ def test_workspace_sizes_are_host_side_and_consistent():
     assert L.jf_node_topk_workspace_size(4, 10, 65) == 0
     assert L.jf_fuse_proj_workspace_size(256, 4096, 3, 4096, 1) >= 0
     assert L.jf_fuse_proj_workspace_size(256, 100, 3, 4096, 1) == 0  # H_in % 64 != 0
+
+
+def test_attn_plan_for_fewer_compute_units():
+    # the _cus entry points plan the key splits for fewer compute units: at
+    # 4096 prefix tokens and 256 nodes (68 key blocks, 8 KV heads, 4 query
+    # tiles) 192 units give splits of 12 blocks (6 a sequence) instead of 9
+    # (8 a sequence), so the partials take 6/8 of the bytes
+    L = jf.lib()
+    pl = np.array([4096], np.int32).ctypes.data_as(ctypes.c_void_p)
+    full = L.jf_tree_attn_workspace_size(1, 256, 32, 8, 128, 4096, pl, 1)
+    assert L.jf_tree_attn_workspace_size_cus(1, 256, 32, 8, 128, 4096, pl, 1, 0) == full
+    assert L.jf_tree_attn_workspace_size_cus(1, 256, 32, 8, 128, 4096, pl, 1, 100000) == full
+    rows8, rows6 = 8 * 8 * 1024, 6 * 8 * 1024
+    assert full == (rows8 * 128 * 2 + 255) // 256 * 256 + rows8 * 4
+    part = L.jf_tree_attn_workspace_size_cus(1, 256, 32, 8, 128, 4096, pl, 1, 192)
+    assert part == (rows6 * 128 * 2 + 255) // 256 * 256 + rows6 * 4
+    assert L.jf_tree_attn_workspace_size_cus(1, 256, 32, 7, 128, 4096, pl, 1, 192) == 0  # invalid -> 0
 
 
 def test_fuse_and_topk_argument_errors():

@@ -16,23 +16,23 @@ from tree_causal_draft_parent_amd import jf, synth
 pytestmark = pytest.mark.gpu
 
 
-def run_gpu(inp, page_status=None):
+def run_gpu(inp, page_status=None, cus=0):
     d = upload_attn(inp)
     mask, _, st = jf.jf_tree_mask_build(d["parent"])
     out, lse = jf.jf_tree_attn_fwd(d["q"], d["k_tree"], d["v_tree"], mask, d["k_cache"],
                                    d["v_cache"], d["block_table"], inp["prefix_len"],
-                                   page_status=page_status)
+                                   page_status=page_status, cus=cus)
     torch.cuda.synchronize()
     assert np.all(st.cpu().numpy() == -1)
     return host_f64(out), host_f64(lse)
 
 
-def compare(inp, rows=None, label=""):
+def compare(inp, rows=None, label="", cus=0):
     B, N, Hq, D = inp["q"].shape
     say(f"attn {label}: B={B} N={N} Hq={Hq} Hkv={inp['k_tree'].shape[2]} D={D} "
         f"P={list(inp['prefix_len'][:4])} page={inp['page_size']} dtype={inp['dtype']} "
-        f"rows={'all' if rows is None else len(rows)}")
-    out, lse = run_gpu(inp)
+        f"rows={'all' if rows is None else len(rows)} cus={cus}")
+    out, lse = run_gpu(inp, cus=cus)
     ro, rl = oracle_attn(inp, rows=rows)
     go = out.reshape(-1, D) if rows is None else out.reshape(-1, D)[rows]
     gl = lse.reshape(-1) if rows is None else lse.reshape(-1)[rows]
@@ -113,6 +113,18 @@ def test_qwen3_8b_low_budget_full():
 
 def test_qwen3_8b_high_budget_full():
     compare(synth.make_workload(2, parts=("attn",))["attn"], label="qwen3-8b n256")
+
+
+@pytest.mark.parametrize("cus", [192, 64, 7])
+def test_splits_planned_for_fewer_compute_units(cus):
+    # jf_tree_attn_fwd_cus: fewer, longer key splits; same results to the
+    # parity bar (all rows at 4096 prefix tokens and 256 nodes)
+    compare(synth.make_workload(2, parts=("attn",))["attn"], label="qwen3-8b n256", cus=cus)
+
+
+def test_serving_batch_fewer_compute_units_sampled():
+    inp = synth.make_workload(3, parts=("attn",))["attn"]
+    compare(inp, rows=_sample_rows(inp, 256, 5), label="serving b32", cus=192)
 
 
 def _sample_rows(inp, n, seed):

@@ -44,7 +44,7 @@ const char *jf_status_string(int status) {
     }
 }
 
-int jf_abi_version(void) { return 2; }
+int jf_abi_version(void) { return 3; }
 
 jf_status jf_tree_mask_build(const int32_t *parent, int32_t B, int32_t N, uint64_t *mask,
                              int32_t *depth, int32_t *seq_status, void *stream) {
@@ -124,13 +124,19 @@ static jf_status check_attn_dims(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, 
     return JF_OK;
 }
 
-size_t jf_tree_attn_workspace_size(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
-                                   int32_t page_size, const int32_t *prefix_len, jf_dtype dtype) {
+size_t jf_tree_attn_workspace_size_cus(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
+                                       int32_t page_size, const int32_t *prefix_len,
+                                       jf_dtype dtype, int32_t cus) {
     if (check_attn_dims(B, N, Hq, Hkv, D, prefix_len, dtype) != JF_OK || page_size < 1) return 0;
     if (dtype == JF_F32) return 0;
     AttnPlan p;
-    plan_tree_attn(p, B, N, Hq, Hkv, D, page_size, prefix_len, dtype);
+    plan_tree_attn(p, B, N, Hq, Hkv, D, page_size, prefix_len, dtype, cus);
     return tree_attn_workspace_bytes(p);
+}
+
+size_t jf_tree_attn_workspace_size(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
+                                   int32_t page_size, const int32_t *prefix_len, jf_dtype dtype) {
+    return jf_tree_attn_workspace_size_cus(B, N, Hq, Hkv, D, page_size, prefix_len, dtype, 0);
 }
 
 jf_status jf_tree_attn_fwd(const void *q, const void *k_tree, const void *v_tree,
@@ -140,6 +146,18 @@ jf_status jf_tree_attn_fwd(const void *q, const void *k_tree, const void *v_tree
                            int32_t Hq, int32_t Hkv, int32_t D, float scale, jf_dtype dtype,
                            void *out, float *lse, void *workspace, size_t workspace_bytes,
                            int32_t *page_status, void *stream) {
+    return jf_tree_attn_fwd_cus(q, k_tree, v_tree, mask, k_cache, v_cache, num_pages, page_size,
+                                block_table, max_pages, prefix_len, B, N, Hq, Hkv, D, scale, dtype,
+                                out, lse, workspace, workspace_bytes, page_status, 0, stream);
+}
+
+jf_status jf_tree_attn_fwd_cus(const void *q, const void *k_tree, const void *v_tree,
+                               const uint64_t *mask, const void *k_cache, const void *v_cache,
+                               int64_t num_pages, int32_t page_size, const int32_t *block_table,
+                               int32_t max_pages, const int32_t *prefix_len, int32_t B, int32_t N,
+                               int32_t Hq, int32_t Hkv, int32_t D, float scale, jf_dtype dtype,
+                               void *out, float *lse, void *workspace, size_t workspace_bytes,
+                               int32_t *page_status, int32_t cus, void *stream) {
     if (!q || !k_tree || !v_tree || !mask || !k_cache || !v_cache || !block_table || !out)
         return JF_ERR_INVALID_ARG;
     jf_status st = check_attn_dims(B, N, Hq, Hkv, D, prefix_len, dtype);
@@ -161,7 +179,7 @@ jf_status jf_tree_attn_fwd(const void *q, const void *k_tree, const void *v_tree
     }
     if (!(scale > 0.f)) scale = 1.f / sqrtf((float)D);
     AttnPlan p;
-    plan_tree_attn(p, B, N, Hq, Hkv, D, page_size, prefix_len, dtype);
+    plan_tree_attn(p, B, N, Hq, Hkv, D, page_size, prefix_len, dtype, cus);
     hipError_t e;
     if (dtype == JF_BF16) {
         const size_t need = tree_attn_workspace_bytes(p);

@@ -106,8 +106,9 @@ struct AttnPlan {
     int prefix_len[kMaxBatch];
     int chunk_start[kMaxBatch + 1];
 };
+// cus: compute units the split plan fills (<= 0: all of the device's)
 void plan_tree_attn(AttnPlan &p, int B, int N, int Hq, int Hkv, int D, int page_size,
-                    const int32_t *prefix_len, jf_dtype dtype);
+                    const int32_t *prefix_len, jf_dtype dtype, int cus = 0);
 size_t tree_attn_workspace_bytes(const AttnPlan &p);
 
 hipError_t launch_tree_attn_bf16(const AttnPlan &p, const void *q, const void *k_tree,

@@ -950,9 +950,10 @@ static int64_t plan_span(int B, const int32_t *prefix_len, int n_tree_blocks, in
 // Split planning.  Every (sequence, KV head, query tile) is a row of blocks;
 // cut all rows into splits of the same block count so that about one
 // workgroup per compute unit comes out (a workgroup fills a compute unit's
-// LDS), never less than two blocks a split.
+// LDS), never less than two blocks a split.  A caller that runs other work
+// beside the attention can plan it for fewer compute units.
 void plan_tree_attn(AttnPlan &p, int B, int N, int Hq, int Hkv, int D, int page_size,
-                    const int32_t *prefix_len, jf_dtype dtype) {
+                    const int32_t *prefix_len, jf_dtype dtype, int cus) {
     p.B = B; p.N = N; p.Hq = Hq; p.Hkv = Hkv; p.D = D;
     p.page_size = page_size;
     p.G = Hq / Hkv;
@@ -970,7 +971,7 @@ void plan_tree_attn(AttnPlan &p, int B, int N, int Hq, int Hkv, int D, int page_
         if (nb > max_blocks) max_blocks = nb;
     }
     units *= (int64_t)Hkv * p.n_qt;
-    const int64_t target = (int64_t)num_cus();
+    const int64_t target = cus > 0 && cus < num_cus() ? (int64_t)cus : (int64_t)num_cus();
     int64_t cb = (units + target - 1) / target;
     if (cb < 2) cb = 2;
     // a split's page ids must fit the LDS staging array

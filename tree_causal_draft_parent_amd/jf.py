@@ -25,7 +25,8 @@ JF_F32, JF_BF16 = 0, 1
 
 EXPORTS = ("jf_status_string", "jf_abi_version", "jf_tree_mask_build",
            "jf_fuse_proj_workspace_size", "jf_fuse_proj", "jf_tree_attn_workspace_size",
-           "jf_tree_attn_fwd", "jf_node_topk_workspace_size", "jf_node_topk")
+           "jf_tree_attn_fwd", "jf_tree_attn_workspace_size_cus", "jf_tree_attn_fwd_cus",
+           "jf_node_topk_workspace_size", "jf_node_topk")
 
 _lib = None
 
@@ -62,6 +63,11 @@ def lib():
     L.jf_tree_attn_fwd.argtypes = [P, P, P, P, P, P, I64, I32, P, I32, P, I32, I32, I32, I32, I32,
                                    ctypes.c_float, ctypes.c_int, P, P, P, SZ, P, P]
     L.jf_tree_attn_fwd.restype = ctypes.c_int
+    L.jf_tree_attn_workspace_size_cus.argtypes = [I32, I32, I32, I32, I32, I32, P, ctypes.c_int, I32]
+    L.jf_tree_attn_workspace_size_cus.restype = SZ
+    L.jf_tree_attn_fwd_cus.argtypes = [P, P, P, P, P, P, I64, I32, P, I32, P, I32, I32, I32, I32, I32,
+                                       ctypes.c_float, ctypes.c_int, P, P, P, SZ, P, I32, P]
+    L.jf_tree_attn_fwd_cus.restype = ctypes.c_int
     L.jf_node_topk_workspace_size.argtypes = [I64, I64, I32]
     L.jf_node_topk_workspace_size.restype = SZ
     L.jf_node_topk.argtypes = [P, I64, I64, I64, ctypes.c_int, I32, P, P, P, P, SZ, P]
@@ -162,18 +168,24 @@ def _host_i32(a) -> np.ndarray:
 
 
 def jf_tree_attn_workspace_size(B: int, N: int, Hq: int, Hkv: int, D: int, page_size: int,
-                                prefix_len, dtype: int) -> int:
+                                prefix_len, dtype: int, cus: int = 0) -> int:
+    """cus > 0: the plan of jf_tree_attn_fwd(..., cus=cus) (see jf_tree_attn_fwd_cus)."""
     pl = _host_i32(prefix_len)
+    if cus > 0:
+        return int(lib().jf_tree_attn_workspace_size_cus(B, N, Hq, Hkv, D, page_size,
+                                                         pl.ctypes.data_as(ctypes.c_void_p), dtype, cus))
     return int(lib().jf_tree_attn_workspace_size(B, N, Hq, Hkv, D, page_size,
                                                  pl.ctypes.data_as(ctypes.c_void_p), dtype))
 
 
 def jf_tree_attn_fwd(q, k_tree, v_tree, mask, k_cache, v_cache, block_table, prefix_len,
                      scale: float = 0.0, out=None, lse=None, with_lse: bool = True,
-                     workspace=None, page_status=None, stream=None):
+                     workspace=None, page_status=None, stream=None, cus: int = 0):
     """Tree attention.  q [B,N,Hq,D]; k_tree/v_tree [B,N,Hkv,D]; mask from
     jf_tree_mask_build; k_cache/v_cache [num_pages, page_size, Hkv, D];
-    block_table [B, max_pages] int32 (device); prefix_len host ints [B]."""
+    block_table [B, max_pages] int32 (device); prefix_len host ints [B].
+    cus > 0 plans the key splits for that many compute units
+    (jf_tree_attn_fwd_cus); the workspace must then be sized with the same cus."""
     for n, t in (("q", q), ("k_tree", k_tree), ("v_tree", v_tree), ("mask", mask),
                  ("k_cache", k_cache), ("v_cache", v_cache), ("block_table", block_table)):
         _contig(n, t)
@@ -187,15 +199,22 @@ def jf_tree_attn_fwd(q, k_tree, v_tree, mask, k_cache, v_cache, block_table, pre
         out = torch.empty_like(q)
     if lse is None and with_lse:
         lse = torch.empty((B, N, Hq), dtype=torch.float32, device=q.device)
-    need = jf_tree_attn_workspace_size(B, N, Hq, Hkv, D, page_size, pl, dt)
+    need = jf_tree_attn_workspace_size(B, N, Hq, Hkv, D, page_size, pl, dt, cus)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().jf_tree_attn_fwd(_p(q), _p(k_tree), _p(v_tree), _p(mask), _p(k_cache), _p(v_cache),
-                                num_pages, page_size, _p(block_table), max_pages,
-                                pl.ctypes.data_as(ctypes.c_void_p), B, N, Hq, Hkv, D,
-                                float(scale), dt, _p(out), _p(lse), _p(workspace), ws_bytes,
-                                _p(page_status), _stream(stream))
+    if cus > 0:
+        st = lib().jf_tree_attn_fwd_cus(_p(q), _p(k_tree), _p(v_tree), _p(mask), _p(k_cache),
+                                        _p(v_cache), num_pages, page_size, _p(block_table), max_pages,
+                                        pl.ctypes.data_as(ctypes.c_void_p), B, N, Hq, Hkv, D,
+                                        float(scale), dt, _p(out), _p(lse), _p(workspace), ws_bytes,
+                                        _p(page_status), int(cus), _stream(stream))
+    else:
+        st = lib().jf_tree_attn_fwd(_p(q), _p(k_tree), _p(v_tree), _p(mask), _p(k_cache), _p(v_cache),
+                                    num_pages, page_size, _p(block_table), max_pages,
+                                    pl.ctypes.data_as(ctypes.c_void_p), B, N, Hq, Hkv, D,
+                                    float(scale), dt, _p(out), _p(lse), _p(workspace), ws_bytes,
+                                    _p(page_status), _stream(stream))
     _check("jf_tree_attn_fwd", st)
     return out, lse
 
