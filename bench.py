@@ -51,6 +51,9 @@ def parse():
                     help="compute units the attention's key splits are planned for in the two-stream "
                          "step (-1: three quarters of the device's when mask + attention is the "
                          "shorter stream by the eager per-call times, else all; 0: all)")
+    ap.add_argument("--fuse-cus", type=int, default=-1,
+                    help="compute units the projection's K split is planned for in the two-stream "
+                         "step (-1: three quarters of the device's; 0: all)")
     ap.add_argument("--one-stream", action="store_true",
                     help="headline from the graph of the step on one stream (default: two streams)")
     ap.add_argument("--cpu-sample-nodes", type=int, default=256)
@@ -335,12 +338,18 @@ def main():
     aws_side = jf.jf_tree_attn_workspace_size(B, N, wl.Hq, wl.Hkv, wl.D, a["page_size"], prefix_len,
                                               jf.JF_BF16 if dt == "bf16" else jf.JF_F32, attn_cus)
     attn_ws_side = torch.empty(max(aws_side, 1), dtype=torch.uint8, device="cuda")
+    # the projection's K split likewise leaves a quarter of the units to the
+    # other stream (fewer slices of fp32 partials)
+    fuse_cus = (3 * n_cus) // 4 if args.fuse_cus < 0 else args.fuse_cus
+    fws_side = jf.jf_fuse_proj_workspace_size(B * N, wl.H, wl.n_fused, wl.H,
+                                              jf.JF_BF16 if dt == "bf16" else jf.JF_F32, fuse_cus)
+    fuse_ws_side = torch.empty(max(fws_side, 1), dtype=torch.uint8, device="cuda")
 
     def step_streams():
         main = torch.cuda.current_stream()
         s_side.wait_stream(main)
         with torch.cuda.stream(s_side):
-            jf.jf_fuse_proj(xs, w, y=y, workspace=fuse_ws)
+            jf.jf_fuse_proj(xs, w, y=y, workspace=fuse_ws_side, cus=fuse_cus)
             jf.jf_node_topk(logits, wl.topk, idx=idx, val=val, lse=rlse, workspace=topk_ws)
         jf.jf_tree_mask_build(parent, mask, depth, seq_status)
         jf.jf_tree_attn_fwd(dev["q"], dev["k_tree"], dev["v_tree"], mask, dev["k_cache"],
@@ -483,6 +492,7 @@ def main():
         "launch": "eager" if args.eager else ("hip_graph" if args.one_stream else "hip_graph_2_streams"),
         "graph_one_stream_ms_per_step": None if serial_graph_ms is None else round(serial_graph_ms, 5),
         "attn_cus_two_streams": attn_cus,
+        "fuse_cus_two_streams": fuse_cus,
         "eager_ms_per_step": round(eager_ms_per_step, 5),
         "gpu_step_ms": round(gpu_step_ms, 5),
         "cold_step_ms": round(med(cold), 5),

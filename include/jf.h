@@ -108,6 +108,25 @@ jf_status jf_fuse_proj(const void *const *x, int32_t k, int64_t M,
                        void *workspace, size_t workspace_bytes, void *stream);
 
 /* --------------------------------------------------------------------------
+ * jf_fuse_proj_cus / jf_fuse_proj_workspace_size_cus -- the same projection
+ * (same citation and arguments as above), with the K split planned for `cus`
+ * compute units instead of all of the device's (cus <= 0 or above the
+ * device's count: all).  For a caller that runs other work beside the
+ * projection on another stream: fewer K slices leave compute units to that
+ * work and write fewer fp32 partials.  The workspace size must come from
+ * jf_fuse_proj_workspace_size_cus with the same cus.  Results agree with
+ * jf_fuse_proj to the rounding of the fp32 slice sums.
+ * ------------------------------------------------------------------------ */
+size_t jf_fuse_proj_workspace_size_cus(int64_t M, int64_t H_in, int32_t k,
+                                       int64_t H_out, jf_dtype in_dtype,
+                                       int32_t cus);
+jf_status jf_fuse_proj_cus(const void *const *x, int32_t k, int64_t M,
+                           int64_t H_in, int64_t ldx, const void *w,
+                           int64_t H_out, jf_dtype in_dtype, void *y,
+                           jf_dtype out_dtype, void *workspace,
+                           size_t workspace_bytes, int32_t cus, void *stream);
+
+/* --------------------------------------------------------------------------
  * jf_tree_attn_fwd -- tree-causal attention of all draft nodes in one pass.
  *
  * For sequence b, tree node i and query head h (KV head g = h / (Hq/Hkv)):

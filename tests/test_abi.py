@@ -21,7 +21,7 @@ def _declared():
 
 def test_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 11
+    assert len(names) == 13
     assert sorted(jf.EXPORTS) == names
     L = jf.lib()
     for n in names:
@@ -109,6 +109,18 @@ def test_attn_plan_for_fewer_compute_units():
     part = L.jf_tree_attn_workspace_size_cus(1, 256, 32, 8, 128, 4096, pl, 1, 192)
     assert part == (rows6 * 128 * 2 + 255) // 256 * 256 + rows6 * 4
     assert L.jf_tree_attn_workspace_size_cus(1, 256, 32, 7, 128, 4096, pl, 1, 192) == 0  # invalid -> 0
+
+
+def test_fuse_plan_for_fewer_compute_units():
+    # 256 rows x 4096 outputs from 3 x 4096 inputs: 32 output tiles; 256 units
+    # take 8 K slices of fp32 partials, 192 units 6
+    L = jf.lib()
+    full = L.jf_fuse_proj_workspace_size(256, 4096, 3, 4096, 1)
+    assert full == 8 * 256 * 4096 * 4
+    assert L.jf_fuse_proj_workspace_size_cus(256, 4096, 3, 4096, 1, 0) == full
+    assert L.jf_fuse_proj_workspace_size_cus(256, 4096, 3, 4096, 1, 192) == 6 * 256 * 4096 * 4
+    assert L.jf_fuse_proj_workspace_size_cus(256, 4096, 3, 4096, 1, 32) == 0      # one slice: no partials
+    assert L.jf_fuse_proj_workspace_size_cus(256, 100, 3, 4096, 1, 192) == 0      # invalid -> 0
 
 
 def test_fuse_and_topk_argument_errors():

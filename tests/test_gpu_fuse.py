@@ -13,10 +13,10 @@ from tree_causal_draft_parent_amd import jf, synth
 pytestmark = pytest.mark.gpu
 
 
-def _run(inp, out_dtype=torch.float32, ldx=None, rows=None):
+def _run(inp, out_dtype=torch.float32, ldx=None, rows=None, cus=0):
     dt = inp["dtype"]
     k, M, H_in = inp["x"].shape
-    say(f"fuse: k={k} M={M} H_in={H_in} H_out={inp['w'].shape[0]} dtype={dt} out={out_dtype} ldx={ldx}")
+    say(f"fuse: k={k} M={M} H_in={H_in} H_out={inp['w'].shape[0]} dtype={dt} out={out_dtype} ldx={ldx} cus={cus}")
     if ldx is not None:
         pad = np.zeros((k, M, ldx), dtype=inp["x"].dtype)
         pad[:, :, :H_in] = inp["x"]
@@ -25,7 +25,7 @@ def _run(inp, out_dtype=torch.float32, ldx=None, rows=None):
     else:
         xt = dev_tensor(inp["x"], dt)
         xs = [xt[l] for l in range(k)]
-    y = jf.jf_fuse_proj(xs, dev_tensor(inp["w"], dt), out_dtype=out_dtype)
+    y = jf.jf_fuse_proj(xs, dev_tensor(inp["w"], dt), out_dtype=out_dtype, cus=cus)
     torch.cuda.synchronize()
     got = host_f64(y)
     ref = oracle.fuse_proj(synth.to_f64(inp["x"], dt), synth.to_f64(inp["w"], dt), rows=rows)
@@ -69,6 +69,14 @@ def test_qwen3_8b_low_budget_full():
 def test_qwen3_8b_high_budget_sampled_rows():
     rows = np.sort(np.random.default_rng(2).choice(256, 32, replace=False))
     _run(synth.make_workload(2, parts=("fuse",))["fuse"], rows=rows)
+
+
+@pytest.mark.parametrize("cus", [192, 32, 5])
+def test_split_planned_for_fewer_compute_units(cus):
+    # jf_fuse_proj_cus: fewer K slices (192 units: 6, 32: 1, 5: 1), same
+    # results to the parity bar
+    rows = np.sort(np.random.default_rng(3).choice(256, 48, replace=False))
+    _run(synth.make_workload(2, parts=("fuse",))["fuse"], rows=rows, cus=cus)
 
 
 def test_qwen3_30b_shape_sampled_rows():

@@ -67,17 +67,30 @@ static jf_status check_fuse(int32_t k, int64_t M, int64_t H_in, int64_t ldx, int
     return JF_OK;
 }
 
-size_t jf_fuse_proj_workspace_size(int64_t M, int64_t H_in, int32_t k, int64_t H_out,
-                                   jf_dtype in_dtype) {
+size_t jf_fuse_proj_workspace_size_cus(int64_t M, int64_t H_in, int32_t k, int64_t H_out,
+                                       jf_dtype in_dtype, int32_t cus) {
     if (check_fuse(k, M, H_in, H_in, H_out, in_dtype) != JF_OK) return 0;
     FusePlan p;
-    plan_fuse(p, M, H_in, k, H_out, in_dtype);
+    plan_fuse(p, M, H_in, k, H_out, in_dtype, cus);
     return fuse_workspace_bytes(p);
+}
+
+size_t jf_fuse_proj_workspace_size(int64_t M, int64_t H_in, int32_t k, int64_t H_out,
+                                   jf_dtype in_dtype) {
+    return jf_fuse_proj_workspace_size_cus(M, H_in, k, H_out, in_dtype, 0);
 }
 
 jf_status jf_fuse_proj(const void *const *x, int32_t k, int64_t M, int64_t H_in, int64_t ldx,
                        const void *w, int64_t H_out, jf_dtype in_dtype, void *y,
                        jf_dtype out_dtype, void *workspace, size_t workspace_bytes, void *stream) {
+    return jf_fuse_proj_cus(x, k, M, H_in, ldx, w, H_out, in_dtype, y, out_dtype, workspace,
+                            workspace_bytes, 0, stream);
+}
+
+jf_status jf_fuse_proj_cus(const void *const *x, int32_t k, int64_t M, int64_t H_in, int64_t ldx,
+                           const void *w, int64_t H_out, jf_dtype in_dtype, void *y,
+                           jf_dtype out_dtype, void *workspace, size_t workspace_bytes, int32_t cus,
+                           void *stream) {
     if (!x || !w || !y) return JF_ERR_INVALID_ARG;
     jf_status st = check_fuse(k, M, H_in, ldx, H_out, in_dtype);
     if (st != JF_OK) return st;
@@ -99,7 +112,7 @@ jf_status jf_fuse_proj(const void *const *x, int32_t k, int64_t M, int64_t H_in,
             return JF_ERR_UNSUPPORTED;
     }
     FusePlan p;
-    plan_fuse(p, M, H_in, k, H_out, in_dtype);
+    plan_fuse(p, M, H_in, k, H_out, in_dtype, cus);
     const size_t need = fuse_workspace_bytes(p);
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
         return JF_ERR_WORKSPACE;

@@ -144,7 +144,9 @@ struct FusePlan {
     int split_k;       // K slices (>1 uses the fp32 partial workspace)
     int64_t k_per_split;
 };
-void plan_fuse(FusePlan &p, int64_t M, int64_t H_in, int k, int64_t H_out, jf_dtype in_dtype);
+// cus: compute units the split-K plan fills (<= 0: all of the device's)
+void plan_fuse(FusePlan &p, int64_t M, int64_t H_in, int k, int64_t H_out, jf_dtype in_dtype,
+               int cus = 0);
 size_t fuse_workspace_bytes(const FusePlan &p);
 hipError_t launch_fuse_bf16(const FusePlan &p, const void *const *x, int64_t ldx,
                             const void *w, void *y, jf_dtype out_dtype, void *workspace,

@@ -313,7 +313,8 @@ __global__ __launch_bounds__(256) void k_fuse_gemm_f32(FuseArgsF32 f) {
 
 }  // namespace
 
-void plan_fuse(FusePlan &p, int64_t M, int64_t H_in, int k, int64_t H_out, jf_dtype in_dtype) {
+void plan_fuse(FusePlan &p, int64_t M, int64_t H_in, int k, int64_t H_out, jf_dtype in_dtype,
+               int cus) {
     p.M = M;
     p.H_in = H_in;
     p.H_out = H_out;
@@ -327,7 +328,9 @@ void plan_fuse(FusePlan &p, int64_t M, int64_t H_in, int k, int64_t H_out, jf_dt
         return;
     }
     const int64_t tiles = ((M + p.bm - 1) / p.bm) * ((H_out + kBN - 1) / kBN);
-    const int64_t target = (int64_t)num_cus();       // one 4-wave workgroup per CU
+    // one workgroup per compute unit of the budget (all units unless a caller
+    // leaves some to work on another stream)
+    const int64_t target = cus > 0 && cus < num_cus() ? (int64_t)cus : (int64_t)num_cus();
     int64_t s = (target + tiles - 1) / tiles;
     const int64_t ksteps = K / kBK;
     int64_t max_s = ksteps / 8;  // at least eight K steps per slice

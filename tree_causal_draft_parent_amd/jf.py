@@ -24,7 +24,8 @@ JF_ERR_WORKSPACE, JF_ERR_BAD_TREE, JF_ERR_BAD_PAGE, JF_ERR_HIP = 4, 5, 6, 7
 JF_F32, JF_BF16 = 0, 1
 
 EXPORTS = ("jf_status_string", "jf_abi_version", "jf_tree_mask_build",
-           "jf_fuse_proj_workspace_size", "jf_fuse_proj", "jf_tree_attn_workspace_size",
+           "jf_fuse_proj_workspace_size", "jf_fuse_proj", "jf_fuse_proj_workspace_size_cus",
+           "jf_fuse_proj_cus", "jf_tree_attn_workspace_size",
            "jf_tree_attn_fwd", "jf_tree_attn_workspace_size_cus", "jf_tree_attn_fwd_cus",
            "jf_node_topk_workspace_size", "jf_node_topk")
 
@@ -58,6 +59,11 @@ def lib():
     L.jf_fuse_proj.argtypes = [P, I32, I64, I64, I64, P, I64, ctypes.c_int, P, ctypes.c_int,
                                P, SZ, P]
     L.jf_fuse_proj.restype = ctypes.c_int
+    L.jf_fuse_proj_workspace_size_cus.argtypes = [I64, I64, I32, I64, ctypes.c_int, I32]
+    L.jf_fuse_proj_workspace_size_cus.restype = SZ
+    L.jf_fuse_proj_cus.argtypes = [P, I32, I64, I64, I64, P, I64, ctypes.c_int, P, ctypes.c_int,
+                                   P, SZ, I32, P]
+    L.jf_fuse_proj_cus.restype = ctypes.c_int
     L.jf_tree_attn_workspace_size.argtypes = [I32, I32, I32, I32, I32, I32, P, ctypes.c_int]
     L.jf_tree_attn_workspace_size.restype = SZ
     L.jf_tree_attn_fwd.argtypes = [P, P, P, P, P, P, I64, I32, P, I32, P, I32, I32, I32, I32, I32,
@@ -129,15 +135,21 @@ def jf_tree_mask_build(parent: torch.Tensor, mask: Optional[torch.Tensor] = None
     return mask, depth, seq_status
 
 
-def jf_fuse_proj_workspace_size(M: int, H_in: int, k: int, H_out: int, in_dtype: int) -> int:
+def jf_fuse_proj_workspace_size(M: int, H_in: int, k: int, H_out: int, in_dtype: int,
+                                cus: int = 0) -> int:
+    """cus > 0: the plan of jf_fuse_proj(..., cus=cus) (see jf_fuse_proj_cus)."""
+    if cus > 0:
+        return int(lib().jf_fuse_proj_workspace_size_cus(M, H_in, k, H_out, in_dtype, cus))
     return int(lib().jf_fuse_proj_workspace_size(M, H_in, k, H_out, in_dtype))
 
 
 def jf_fuse_proj(xs: Sequence[torch.Tensor], w: torch.Tensor, out_dtype=torch.float32,
                  y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                 stream=None):
+                 stream=None, cus: int = 0):
     """y[m, o] = sum_l xs[l][m, :] . w[o, l*H_in:(l+1)*H_in]  (xs[l]: [M, H_in], rows may be
-    strided; w: [H_out, k*H_in])."""
+    strided; w: [H_out, k*H_in]).  cus > 0 plans the K split for that many
+    compute units (jf_fuse_proj_cus); the workspace must then be sized with
+    the same cus."""
     k = len(xs)
     M, H_in = xs[0].shape
     ldx = xs[0].stride(0)
@@ -150,13 +162,17 @@ def jf_fuse_proj(xs: Sequence[torch.Tensor], w: torch.Tensor, out_dtype=torch.fl
     if y is None:
         y = torch.empty((M, H_out), dtype=out_dtype, device=w.device)
     out_code = _dtype_code(y)
-    need = jf_fuse_proj_workspace_size(M, H_in, k, H_out, in_code)
+    need = jf_fuse_proj_workspace_size(M, H_in, k, H_out, in_code, cus)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=w.device)
     arr = (ctypes.c_void_p * k)(*[x.data_ptr() for x in xs])
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().jf_fuse_proj(arr, k, M, H_in, ldx, _p(w), H_out, in_code, _p(y), out_code,
-                            _p(workspace), ws_bytes, _stream(stream))
+    if cus > 0:
+        st = lib().jf_fuse_proj_cus(arr, k, M, H_in, ldx, _p(w), H_out, in_code, _p(y), out_code,
+                                    _p(workspace), ws_bytes, int(cus), _stream(stream))
+    else:
+        st = lib().jf_fuse_proj(arr, k, M, H_in, ldx, _p(w), H_out, in_code, _p(y), out_code,
+                                _p(workspace), ws_bytes, _stream(stream))
     _check("jf_fuse_proj", st)
     return y
 
