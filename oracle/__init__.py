@@ -65,6 +65,10 @@ def _load():
     lib.oracle_tree_attn.restype = ctypes.c_int
     lib.oracle_topk.argtypes = [P, I64, I64, I64, P, P, P]
     lib.oracle_topk.restype = None
+    lib.oracle_path_scores.argtypes = [P, P, I64, I64, P, P]
+    lib.oracle_path_scores.restype = ctypes.c_int
+    lib.oracle_tree_expand.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, P, P, P, P]
+    lib.oracle_tree_expand.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
@@ -161,6 +165,40 @@ def topk(logits: np.ndarray, k: int, with_lse: bool = True):
     lse = np.empty((R,), dtype=np.float64) if with_lse else None
     _load().oracle_topk(_p(logits), R, V, k, _p(idx), _p(val), _p(lse))
     return idx, val, lse
+
+
+def path_scores(parent: np.ndarray, logp: np.ndarray):
+    """Path log-probability [B, N] float64 (sum of logp over anc(i)), status, first bad row."""
+    parent = _c(parent, np.int32)
+    logp = _c(logp, np.float64)
+    B, N = parent.shape
+    score = np.zeros((B, N), dtype=np.float64)
+    bad = np.zeros(1, dtype=np.int64)
+    st = _load().oracle_path_scores(_p(parent), _p(logp), B, N, _p(score), _p(bad))
+    return score, int(st), int(bad[0])
+
+
+def tree_expand(score: np.ndarray, depth: np.ndarray, idx: np.ndarray, val: np.ndarray,
+                lse: np.ndarray, M: int, max_depth: int):
+    """One best-first expansion step: the M best (parent, rank) candidates of each
+    sequence -> new parent, token, score (float32), depth, each [B, M]."""
+    score = _c(score, np.float32)
+    depth = _c(depth, np.int32)
+    idx = _c(idx, np.int32)
+    val = _c(val, np.float32)
+    lse = _c(lse, np.float32)
+    B, N = score.shape
+    k = idx.shape[-1]
+    assert idx.shape == (B, N, k) and val.shape == (B, N, k) and lse.shape == (B, N)
+    outp = np.zeros((B, M), dtype=np.int32)
+    outt = np.zeros((B, M), dtype=np.int32)
+    outs = np.zeros((B, M), dtype=np.float32)
+    outd = np.zeros((B, M), dtype=np.int32)
+    st = _load().oracle_tree_expand(_p(score), _p(depth), _p(idx), _p(val), _p(lse), B, N, k, M,
+                                    max_depth, _p(outp), _p(outt), _p(outs), _p(outd))
+    if st != 0:
+        raise ValueError(f"oracle_tree_expand: status {st}")
+    return outp, outt, outs, outd
 
 
 def num_threads() -> int:

@@ -25,7 +25,9 @@
  * notes): a node is its own ancestor; parent -1 means "child of the prefix
  * end"; softmax scale defaults to 1/sqrt(D); query head h reads KV head
  * h / (Hq/Hkv); the fusion is concatenation followed by one bias-free linear
- * map; top-k order is value descending then index ascending, -0 == +0.
+ * map; top-k order is value descending then index ascending, -0 == +0; a path
+ * score is the sum of the conditional log-probabilities along the branch, and
+ * one expansion step keeps the M best one-token extensions of the tree.
  */
 #include <math.h>
 #include <omp.h>
@@ -270,6 +272,111 @@ void oracle_topk(const double *logits, int64_t R, int64_t V, int64_t k,
             }
         }
     }
+}
+
+/* ---------------------------------------------------------------------------
+ * Path scores.
+ *
+ * A branch's draft probability is the product of the conditionals along it
+ * (JetFlow blog page, "What JetFlow Does Differently").  With logp(a) the
+ * conditional log-probability of node a's own token given its ancestors, the
+ * log-probability of the path from the prefix to node i is
+ *     score(i) = sum of logp(a) over a in anc(i).
+ * Bad rows (as in oracle_tree_mask) get score 0.  Returns OR_BAD_TREE and the
+ * smallest flat index of a bad row, or OR_OK.
+ * ------------------------------------------------------------------------- */
+int oracle_path_scores(const int32_t *parent, const double *logp, int64_t B, int64_t N,
+                       double *score, int64_t *first_bad)
+{
+    int64_t bad = -1;
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t i = 0; i < N; ++i) {
+            double sum = 0.0;
+            int64_t j = i, steps = 0;
+            int ok = 1;
+            while (j != -1) {
+                if (j < -1 || j >= N || steps >= N) { ok = 0; break; }
+                sum += logp[b * N + j];
+                j = parent[b * N + j];
+                ++steps;
+            }
+            score[b * N + i] = ok ? sum : 0.0;
+            if (!ok && bad < 0) bad = b * N + i;
+        }
+    }
+    if (first_bad) *first_bad = bad;
+    return bad >= 0 ? OR_BAD_TREE : OR_OK;
+}
+
+/* ---------------------------------------------------------------------------
+ * Budgeted best-first expansion by one level.
+ *
+ * The candidates of sequence b are the pairs (p, r): node p's r-th best next
+ * token idx[p][r] (from the per-node top-k), whose path score is the parent's
+ * path score plus the child's conditional log-probability, the log-softmax
+ * of p's row at that token:
+ *     s(p, r) = score[p] + (val[p][r] - lse[p]).
+ * A candidate is eligible when 1 <= depth[p] and depth[p] + 1 <= max_depth.
+ * With a budget of M new nodes, best-first expansion takes the M best
+ * eligible candidates in the order (s descending, p ascending, r ascending),
+ * written in that order: new parent p, token, s, depth depth[p] + 1.  Slots
+ * left over (fewer eligible candidates than M) read parent -2, token -1,
+ * score -inf, depth 0.  The scores decide which candidates survive, so they
+ * are computed in float32 with the two roundings in the order written (the
+ * precision the selection is made in); inputs are float32.
+ * ------------------------------------------------------------------------- */
+typedef struct { float s; int32_t p, r; } cand_t;
+
+static int cand_cmp(const void *x, const void *y)
+{
+    const cand_t *a = (const cand_t *)x, *b = (const cand_t *)y;
+    if (a->s != b->s) return a->s > b->s ? -1 : 1;
+    if (a->p != b->p) return a->p < b->p ? -1 : 1;
+    return a->r < b->r ? -1 : (a->r > b->r);
+}
+
+int oracle_tree_expand(const float *score, const int32_t *depth, const int32_t *idx,
+                       const float *val, const float *lse, int64_t B, int64_t N, int64_t k,
+                       int64_t M, int64_t max_depth, int32_t *new_parent, int32_t *new_token,
+                       float *new_score, int32_t *new_depth)
+{
+    if (B < 1 || N < 1 || k < 1 || M < 1) return OR_INVALID;
+    cand_t *c = (cand_t *)malloc((size_t)(N * k) * sizeof(cand_t));
+    if (!c) return OR_INVALID;
+    for (int64_t b = 0; b < B; ++b) {
+        int64_t n = 0;
+        for (int64_t p = 0; p < N; ++p) {
+            const int32_t d = depth[b * N + p];
+            if (d < 1 || (int64_t)d + 1 > max_depth) continue;
+            for (int64_t r = 0; r < k; ++r) {
+                const int64_t e = (b * N + p) * k + r;
+                volatile float t = val[e] - lse[b * N + p];     /* rounded to float */
+                volatile float sc = score[b * N + p] + t;        /* rounded to float */
+                c[n].s = sc;
+                c[n].p = (int32_t)p;
+                c[n].r = (int32_t)r;
+                ++n;
+            }
+        }
+        qsort(c, (size_t)n, sizeof(cand_t), cand_cmp);
+        for (int64_t m = 0; m < M; ++m) {
+            const int64_t o = b * M + m;
+            if (m < n) {
+                const int64_t e = (b * N + c[m].p) * k + c[m].r;
+                new_parent[o] = c[m].p;
+                new_token[o] = idx[e];
+                new_score[o] = c[m].s;
+                new_depth[o] = depth[b * N + c[m].p] + 1;
+            } else {
+                new_parent[o] = -2;
+                new_token[o] = -1;
+                new_score[o] = -INFINITY;
+                new_depth[o] = 0;
+            }
+        }
+    }
+    free(c);
+    return OR_OK;
 }
 
 /* Threads an OpenMP region of this library uses (for reporting). */

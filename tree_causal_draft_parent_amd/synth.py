@@ -251,6 +251,36 @@ def tie_forcing_logits(logits_bits: np.ndarray, dtype: str) -> np.ndarray:
     return f32_to_bf16_bits(x) if dtype == "bf16" else x
 
 
+def make_path_inputs(*, B: int, N: int, max_depth: int = 16, branching=(1, 8),
+                     seed: int = 1234) -> dict:
+    """Best-first parent arrays and each node's conditional log-probability of
+    its own token (float32, -|N(0, 2)|)."""
+    rng = _seeds(seed, ("tree", "logp"))
+    parents = np.stack([best_first_tree(rng["tree"], N, max_depth, branching) for _ in range(B)])
+    logp = (-np.abs(rng["logp"].standard_normal((B, N)) * 2.0)).astype(np.float32)
+    return dict(parent=parents.astype(np.int32), logp=logp)
+
+
+def make_expand_inputs(*, B: int, N: int, k: int, V: int = 151936, max_depth: int = 16,
+                       seed: int = 1234, ties: bool = False) -> dict:
+    """Inputs of one expansion step: the current nodes' path scores (float32,
+    N(-5, 3)), depths U{1..max_depth}, and per-node top-k lists as the top-k
+    call returns them (token ids U[0, V), values N(8, 3) in descending order)
+    with a row log-normaliser above the row's largest value.  ties=True rounds
+    scores, values and normalisers to integers so that many candidates tie."""
+    rng = _seeds(seed, ("score", "depth", "idx", "val", "lse"))
+    score = rng["score"].standard_normal((B, N)) * 3.0 - 5.0
+    depth = rng["depth"].integers(1, max_depth + 1, size=(B, N)).astype(np.int32)
+    idx = rng["idx"].integers(0, V, size=(B, N, k)).astype(np.int32)
+    val = np.sort(rng["val"].standard_normal((B, N, k)) * 3.0 + 8.0, axis=-1)[..., ::-1]
+    lse = val[..., 0] + rng["lse"].uniform(0.0, 3.0, size=(B, N))
+    if ties:
+        score, val, lse = np.round(score), np.round(val), np.ceil(lse)
+    return dict(score=score.astype(np.float32), depth=depth, idx=idx,
+                val=np.ascontiguousarray(val, dtype=np.float32), lse=lse.astype(np.float32),
+                max_depth=max_depth)
+
+
 def config_seed(i: int) -> int:
     return 1000 + i
 
