@@ -323,7 +323,8 @@ int oracle_path_scores(const int32_t *parent, const double *logp, int64_t B, int
  * left over (fewer eligible candidates than M) read parent -2, token -1,
  * score -inf, depth 0.  The scores decide which candidates survive, so they
  * are computed in float32 with the two roundings in the order written (the
- * precision the selection is made in); inputs are float32.
+ * precision the selection is made in); inputs are float32.  -0 and +0 are the
+ * same score (ties go by p, r) and a zero score is written as +0.
  * ------------------------------------------------------------------------- */
 typedef struct { float s; int32_t p, r; } cand_t;
 
@@ -365,7 +366,7 @@ int oracle_tree_expand(const float *score, const int32_t *depth, const int32_t *
                 const int64_t e = (b * N + c[m].p) * k + c[m].r;
                 new_parent[o] = c[m].p;
                 new_token[o] = idx[e];
-                new_score[o] = c[m].s;
+                new_score[o] = c[m].s == 0.0f ? 0.0f : c[m].s;   /* -0 written as +0 */
                 new_depth[o] = depth[b * N + c[m].p] + 1;
             } else {
                 new_parent[o] = -2;

@@ -143,3 +143,15 @@ def test_expand_takes_all_when_budget_allows():
     assert sorted(zip(p[0, :20], t[0, :20])) == sorted(
         (i, inp["idx"][0, i, r]) for i in range(10) for r in range(2))
     assert np.all(p[0, 20:] == -2)
+
+
+def test_expand_signed_zero_is_plus_zero():
+    # -0 ties +0 (candidate order decides) and is written as +0
+    inp = synth.make_expand_inputs(B=1, N=2, k=1, seed=14, max_depth=100)
+    inp["score"][:] = np.array([-0.0, 0.0], np.float32)
+    inp["val"][:] = np.array([[[-0.0], [0.0]]], np.float32)
+    inp["lse"][:] = 0.0
+    p, t, s, d = oracle.tree_expand(inp["score"], inp["depth"], inp["idx"], inp["val"], inp["lse"],
+                                    2, 100)
+    assert list(p[0]) == [0, 1]
+    assert list(s[0].view(np.uint32)) == [0, 0]
