@@ -199,6 +199,65 @@ def copy_bandwidth(torch, reps=10):
     return 2 * COPY_BYTES * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
 
+def tree_growth(wl, parent, depth, idx, val, rlse, steps, torch, jf):
+    """The calls that grow the tree after a step (outside the timed step):
+    jf_path_scores over the step's tree (per-node conditional log-probabilities
+    drawn from a seeded generator) and one jf_tree_expand of that tree by N new
+    nodes from the step's top-k lists.  Both are latency-bound (a few KiB per
+    sequence)."""
+    from tree_causal_draft_parent_amd import synth
+    B, N, k = wl.B, wl.N, wl.topk
+    lp = synth.make_path_inputs(B=B, N=N, seed=synth.config_seed(wl_id(wl)) + 17)["logp"]
+    logp = torch.from_numpy(lp).cuda()
+    score = torch.empty((B, N), dtype=torch.float32, device="cuda")
+    st = torch.empty((B,), dtype=torch.int32, device="cuda")
+    M = N
+    outs = tuple(torch.empty((B, M), dtype=t, device="cuda")
+                 for t in (torch.int32, torch.int32, torch.float32, torch.int32))
+    idx3, val3, lse2 = idx.view(B, N, k), val.view(B, N, k), rlse.view(B, N)
+
+    def path():
+        jf.jf_path_scores(parent, logp, score=score, seq_status=st)
+
+    def expand():
+        jf.jf_tree_expand(score, depth, idx3, val3, lse2, M, wl.max_depth, out=outs)
+
+    # An isolated call would leave the GPU waiting for the host's launch, so
+    # each call is captured REP times into a HIP graph and the replays are timed.
+    REP = 20
+    res = {}
+    for name, fn in (("path_scores", path), ("tree_expand", expand)):
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(REP):
+                fn()
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(max(5, steps // REP)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1) / REP)
+        res[name] = {"ms": round(float(np.mean(ms)), 5), "p50_ms": round(float(np.median(ms)), 5),
+                     "bound": "latency", "timing": f"graph of {REP} back-to-back calls"}
+        del g
+    assert bool((st == -1).all())
+    res["tree_expand"].update(candidates=B * N * k, budget=M)
+    res["new_nodes_per_s"] = round(B * M / (res["tree_expand"]["ms"] * 1e-3), 1)
+    return res
+
+
+def wl_id(wl):
+    from tree_causal_draft_parent_amd import synth
+    return next(i for i, w in synth.WORKLOADS.items() if w.name == wl.name)
+
+
 def projection_context(wl, M, steps, torch, jf):
     """The fused projection over one row per prefix token (M = sum of prefix
     lengths): the MFMA-bound use of the same call. Inputs are seeded device
@@ -411,6 +470,10 @@ def main():
         proj_ctx = projection_context(wl, int(np.sum(prefix_len)), K, torch, jf)
         print(f"[bench] context projection: M={proj_ctx['M']} {proj_ctx['ms']:.4f} ms", file=sys.stderr, flush=True)
 
+    growth = tree_growth(wl, parent, depth, idx, val, rlse, K, torch, jf)
+    print(f"[bench] tree growth: path scores {growth['path_scores']['ms']:.4f} ms, "
+          f"expansion {growth['tree_expand']['ms']:.4f} ms", file=sys.stderr, flush=True)
+
     def med(v):
         return float(np.median(v)) if len(v) else float("nan")
 
@@ -501,6 +564,7 @@ def main():
         "tree_attn": tree_attn,
         "projection": projection,
         "projection_context": proj_ctx,
+        "tree_growth": growth,
         "copy_GBps": round(copy_gbs, 1),
         "roofline": roofline,
         "cpu_baseline": cpu,

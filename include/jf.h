@@ -52,7 +52,7 @@ typedef enum { JF_F32 = 0, JF_BF16 = 1 } jf_dtype;
 const char *jf_status_string(int status);
 
 /* ABI version, bumped on any signature change. */
-int jf_abi_version(void);  /* 3 */
+int jf_abi_version(void);  /* 4 */
 
 /* --------------------------------------------------------------------------
  * jf_tree_mask_build -- ancestor bitmask of every tree node.
@@ -221,6 +221,59 @@ jf_status jf_node_topk(const void *logits, int64_t R, int64_t V, int64_t ld,
                        jf_dtype dtype, int32_t k, int32_t *idx, float *val,
                        float *lse, void *workspace, size_t workspace_bytes,
                        void *stream);
+
+/* --------------------------------------------------------------------------
+ * jf_path_scores -- path log-probability of every draft-tree node.
+ *
+ * A branch's draft probability is the product of the conditionals of the
+ * nodes along it (JetFlow blog page, "What JetFlow Does Differently"), so
+ * with logp[i] the conditional log-probability of node i's own token given
+ * its ancestors,
+ *     score[i] = sum of logp[a] over a in anc(i)   (i itself included).
+ * The sum runs from the node up to the prefix in fp64 and is rounded once to
+ * fp32, so the result does not depend on the launch shape.
+ *
+ *   parent     [B, N] int32, as for jf_tree_mask_build.
+ *   logp       [B, N] fp32.
+ *   score      [B, N] fp32 out; 0 for nodes of a bad walk.
+ *   seq_status [B] int32 or NULL: as for jf_tree_mask_build.
+ *   B >= 1, 1 <= N <= 4096.
+ * ------------------------------------------------------------------------ */
+jf_status jf_path_scores(const int32_t *parent, const float *logp, int32_t B,
+                         int32_t N, float *score, int32_t *seq_status,
+                         void *stream);
+
+/* --------------------------------------------------------------------------
+ * jf_tree_expand -- one budgeted best-first expansion step of the tree.
+ *
+ * The tree grows with each node's most likely next tokens, ranked by the
+ * product of conditionals along the branch (JetFlow blog page, "What JetFlow
+ * Does Differently"), under a node budget (the 16- and 256-token draft
+ * budgets of the "Empirical Results" section).  The pages do not print the
+ * expansion rule (their Algorithm 1 is absent); reading taken: per sequence
+ * the candidates are the pairs (p, r), node p's r-th top token, with score
+ *     s(p, r) = score[p] + (val[p][r] - lse[p])
+ * (two fp32 roundings, in that order), eligible when
+ * 1 <= depth[p] < max_depth.  The M best eligible candidates in the order
+ * (s descending, p ascending, r ascending) become the new nodes, written in
+ * that order: new_parent = p, new_token = idx[p][r], new_score = s (a zero
+ * written as +0; -0 and +0 tie), new_depth = depth[p] + 1.  Slots beyond
+ * the eligible count read parent -2, token -1, score -inf, depth 0.
+ *
+ *   score  [B, N] fp32 path scores of the current nodes (jf_path_scores).
+ *   depth  [B, N] int32 (jf_tree_mask_build).
+ *   idx    [B, N, k] int32, val [B, N, k] fp32, lse [B, N] fp32: the
+ *          per-node top-k lists and log-normalisers (jf_node_topk).
+ *   new_parent, new_token, new_depth [B, M] int32; new_score [B, M] fp32.
+ *   B >= 1, N >= 1, 1 <= k, N * k <= 16384, M >= 1; NaN scores, values or
+ *   normalisers are not supported.
+ * ------------------------------------------------------------------------ */
+jf_status jf_tree_expand(const float *score, const int32_t *depth,
+                         const int32_t *idx, const float *val, const float *lse,
+                         int32_t B, int32_t N, int32_t k, int32_t M,
+                         int32_t max_depth, int32_t *new_parent,
+                         int32_t *new_token, float *new_score,
+                         int32_t *new_depth, void *stream);
 
 #ifdef __cplusplus
 }

@@ -21,7 +21,7 @@ def _declared():
 
 def test_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 13
+    assert len(names) == 15
     assert sorted(jf.EXPORTS) == names
     L = jf.lib()
     for n in names:
@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
 def test_status_strings_and_version():
     assert jf.status_string(0) == "JF_OK"
     assert jf.status_string(5) == "JF_ERR_BAD_TREE"
-    assert jf.lib().jf_abi_version() == 3
+    assert jf.lib().jf_abi_version() == 4
 
 
 FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: every call below fails validation
@@ -138,6 +138,31 @@ def test_fuse_and_topk_argument_errors():
     assert L.jf_node_topk(FAKE, 4, 100, 100, 1, 101, FAKE, FAKE, None, FAKE, 1 << 20, None) == jf.JF_ERR_UNSUPPORTED
     assert L.jf_node_topk(FAKE, 4, 100, 100, 1, 4, FAKE, FAKE, None, FAKE, 1 << 20, None) == jf.JF_ERR_ALIGN
     assert L.jf_node_topk(FAKE, 4, 104, 104, 1, 4, FAKE, FAKE, None, None, 0, None) == jf.JF_ERR_WORKSPACE
+
+
+def test_path_and_expand_argument_errors():
+    L = jf.lib()
+    assert L.jf_path_scores(None, FAKE, 1, 4, FAKE, None, None) == jf.JF_ERR_INVALID_ARG
+    assert L.jf_path_scores(FAKE, FAKE, 0, 4, FAKE, None, None) == jf.JF_ERR_INVALID_ARG
+    assert L.jf_path_scores(FAKE, FAKE, 1, 4097, FAKE, None, None) == jf.JF_ERR_INVALID_ARG
+    assert L.jf_path_scores(FAKE, FAKE_ODD, 1, 4, FAKE, None, None) == jf.JF_ERR_ALIGN
+
+    def exp(**kw):
+        a = dict(score=FAKE, depth=FAKE, idx=FAKE, val=FAKE, lse=FAKE, B=1, N=256, k=8, M=256,
+                 max_depth=16, np_=FAKE, nt=FAKE, ns=FAKE, nd=FAKE)
+        a.update(kw)
+        return L.jf_tree_expand(a["score"], a["depth"], a["idx"], a["val"], a["lse"], a["B"],
+                                a["N"], a["k"], a["M"], a["max_depth"], a["np_"], a["nt"],
+                                a["ns"], a["nd"], None)
+
+    assert exp(lse=None) == jf.JF_ERR_INVALID_ARG
+    assert exp(nd=None) == jf.JF_ERR_INVALID_ARG
+    assert exp(B=0) == jf.JF_ERR_INVALID_ARG
+    assert exp(k=0) == jf.JF_ERR_INVALID_ARG
+    assert exp(M=0) == jf.JF_ERR_INVALID_ARG
+    assert exp(N=2049) == jf.JF_ERR_UNSUPPORTED          # 2049 * 8 candidates > 16384
+    assert exp(N=16384, k=2) == jf.JF_ERR_UNSUPPORTED
+    assert exp(val=FAKE_ODD) == jf.JF_ERR_ALIGN
 
 
 def test_product_path_does_not_import_the_oracle():

@@ -1,0 +1,139 @@
+"""jf_path_scores and jf_tree_expand vs the oracle, bit for bit.
+
+Path scores: the kernel sums in fp64 in the oracle's order (node, then each
+parent up to the prefix) and rounds once, so it must equal the oracle's fp64
+score rounded to fp32 exactly.  Expansion: the candidate scores are the same
+two fp32 roundings on both sides and the selection is a total order, so the
+new parents, tokens, scores (as bit patterns) and depths must all be equal.
+Inputs come from the seeded generators only; none from the GPU path."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import dev_tensor, say
+from tree_causal_draft_parent_amd import jf, synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _path(parent: np.ndarray, logp: np.ndarray):
+    say(f"path_scores: B={parent.shape[0]} N={parent.shape[1]}")
+    s, st = jf.jf_path_scores(dev_tensor(parent.astype(np.int32)), dev_tensor(logp.astype(np.float32)))
+    torch.cuda.synchronize()
+    return s.cpu().numpy(), st.cpu().numpy()
+
+
+def _expect_path(parent, logp):
+    score, st, bad = oracle.path_scores(parent, logp.astype(np.float32).astype(np.float64))
+    return score.astype(np.float32), st, bad
+
+
+@pytest.mark.parametrize("N", [1, 16, 64, 65, 256, 1000, 4096])
+def test_path_random_forests(N):
+    inp = synth.make_path_inputs(B=3, N=N, seed=N)
+    got, st = _path(inp["parent"], inp["logp"])
+    want, ost, _ = _expect_path(inp["parent"], inp["logp"])
+    assert ost == oracle.OK and np.all(st == -1)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+@pytest.mark.parametrize("kind", ["chain", "star", "unordered"])
+def test_path_shapes(kind):
+    N = 300
+    rng = np.random.default_rng(11)
+    if kind == "chain":
+        par = synth.chain_tree(N)
+    elif kind == "star":
+        par = synth.star_tree(N)
+    else:
+        base = synth.best_first_tree(rng, N, 16, (1, 8))
+        perm = rng.permutation(N)
+        inv = np.argsort(perm)
+        par = np.array([perm[base[inv[n]]] if base[inv[n]] >= 0 else -1 for n in range(N)])
+    par = par.astype(np.int32)[None]
+    lp = (-np.abs(rng.standard_normal((1, N)) * 2.0)).astype(np.float32)
+    lp[0, ::7] = -0.0                       # signed zeros sum like the oracle's
+    got, st = _path(par, lp)
+    want, _, _ = _expect_path(par, lp)
+    assert st[0] == -1
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_path_bad_trees_are_reported_per_sequence():
+    par = np.array([[-1, 0, 1, 2],
+                    [-1, 2, 1, 0],      # 1 <-> 2 cycle
+                    [-1, 0, 9, 1],      # out of range at node 2
+                    [3, -1, 1, 3]],     # self-parent at node 3
+                   np.int32)
+    lp = -np.arange(1, 17, dtype=np.float32).reshape(4, 4) / 8
+    got, st = _path(par, lp)
+    assert list(st) == [-1, 1, 2, 0]
+    for b in range(4):
+        want, ost, bad = _expect_path(par[b:b + 1], lp[b:b + 1])
+        assert np.array_equal(got[b:b + 1].view(np.uint32), want.view(np.uint32))
+        assert (ost == oracle.OK) == (st[b] == -1)
+        if st[b] >= 0:
+            assert bad == st[b]
+
+
+# ---------------------------------------------------------------------------
+def _expand(inp, M):
+    B, N, k = inp["idx"].shape
+    say(f"tree_expand: B={B} N={N} k={k} M={M} max_depth={inp['max_depth']}")
+    outs = jf.jf_tree_expand(dev_tensor(inp["score"]), dev_tensor(inp["depth"]),
+                             dev_tensor(inp["idx"]), dev_tensor(inp["val"]), dev_tensor(inp["lse"]),
+                             M, inp["max_depth"])
+    torch.cuda.synchronize()
+    return [o.cpu().numpy() for o in outs]
+
+
+def _check_expand(inp, M):
+    gp, gt, gs, gd = _expand(inp, M)
+    op, ot, os_, od = oracle.tree_expand(inp["score"], inp["depth"], inp["idx"], inp["val"],
+                                         inp["lse"], M, inp["max_depth"])
+    assert np.array_equal(gp, op)
+    assert np.array_equal(gt, ot)
+    assert np.array_equal(gs.view(np.uint32), os_.view(np.uint32))
+    assert np.array_equal(gd, od)
+    return gp
+
+
+@pytest.mark.parametrize("B,N,k,M,max_depth", [
+    (1, 16, 4, 16, 5),            # tiny workload shape
+    (1, 16, 8, 16, 8),            # 16-node budget, top-8
+    (1, 256, 8, 256, 16),         # 256-node budget, one sequence
+    (32, 64, 8, 64, 16),          # serving batch, 64 nodes each
+    (4, 256, 8, 256, 16),         # four sequences of 256 nodes
+    (1, 100, 7, 37, 16),          # ragged candidate count
+    (3, 2048, 8, 300, 16),        # 16384 candidates: the largest sort
+    (1, 256, 64, 16384, 16),      # k = 64, every candidate kept
+    (2, 50, 3, 1, 16),            # budget of one
+])
+@pytest.mark.parametrize("ties", [False, True])
+def test_expand_matches_oracle(B, N, k, M, max_depth, ties):
+    inp = synth.make_expand_inputs(B=B, N=N, k=k, max_depth=max_depth, seed=B * 1000 + N + k,
+                                   ties=ties)
+    _check_expand(inp, M)
+
+
+def test_expand_budget_above_eligible_and_depth_cap():
+    inp = synth.make_expand_inputs(B=2, N=10, k=3, max_depth=16, seed=5)
+    inp["max_depth"] = 4                      # most nodes are at the cap
+    gp = _check_expand(inp, 50)
+    assert (gp == -2).any()
+
+
+def test_expand_nothing_eligible():
+    inp = synth.make_expand_inputs(B=2, N=40, k=4, max_depth=16, seed=6)
+    inp["max_depth"] = 1
+    gp = _check_expand(inp, 8)
+    assert np.all(gp == -2)
+
+
+def test_expand_signed_zero_and_infinite_scores():
+    inp = synth.make_expand_inputs(B=1, N=64, k=4, max_depth=16, seed=7, ties=True)
+    inp["score"][0, ::3] = -0.0
+    inp["val"][0, ::5, :] = inp["lse"][0, ::5, None]          # t = +0
+    inp["score"][0, 1::9] = -np.inf
+    _check_expand(inp, 200)

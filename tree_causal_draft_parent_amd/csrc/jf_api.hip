@@ -44,7 +44,7 @@ const char *jf_status_string(int status) {
     }
 }
 
-int jf_abi_version(void) { return 3; }
+int jf_abi_version(void) { return 4; }
 
 jf_status jf_tree_mask_build(const int32_t *parent, int32_t B, int32_t N, uint64_t *mask,
                              int32_t *depth, int32_t *seq_status, void *stream) {
@@ -238,6 +238,35 @@ jf_status jf_node_topk(const void *logits, int64_t R, int64_t V, int64_t ld, jf_
     const size_t need = topk_workspace_bytes(p);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return JF_ERR_WORKSPACE;
     hipError_t e = launch_topk(p, logits, ld, dtype, idx, val, lse, workspace, (hipStream_t)stream);
+    return e == hipSuccess ? JF_OK : JF_ERR_HIP;
+}
+
+// ---------------------------------------------------------------------------
+jf_status jf_path_scores(const int32_t *parent, const float *logp, int32_t B, int32_t N,
+                         float *score, int32_t *seq_status, void *stream) {
+    if (!parent || !logp || !score) return JF_ERR_INVALID_ARG;
+    if (B < 1 || N < 1 || N > 4096) return JF_ERR_INVALID_ARG;
+    if (!aligned(parent, 4) || !aligned(logp, 4) || !aligned(score, 4) ||
+        (seq_status && !aligned(seq_status, 4)))
+        return JF_ERR_ALIGN;
+    hipError_t e = launch_path_scores(parent, logp, B, N, score, seq_status, (hipStream_t)stream);
+    return e == hipSuccess ? JF_OK : JF_ERR_HIP;
+}
+
+jf_status jf_tree_expand(const float *score, const int32_t *depth, const int32_t *idx,
+                         const float *val, const float *lse, int32_t B, int32_t N, int32_t k,
+                         int32_t M, int32_t max_depth, int32_t *new_parent, int32_t *new_token,
+                         float *new_score, int32_t *new_depth, void *stream) {
+    if (!score || !depth || !idx || !val || !lse || !new_parent || !new_token || !new_score ||
+        !new_depth)
+        return JF_ERR_INVALID_ARG;
+    if (B < 1 || N < 1 || k < 1 || M < 1) return JF_ERR_INVALID_ARG;
+    if ((int64_t)N * k > kExpandMaxCands) return JF_ERR_UNSUPPORTED;
+    const void *ptrs[] = {score, depth, idx, val, lse, new_parent, new_token, new_score, new_depth};
+    for (const void *q : ptrs)
+        if (!aligned(q, 4)) return JF_ERR_ALIGN;
+    hipError_t e = launch_tree_expand(score, depth, idx, val, lse, B, N, k, M, max_depth, new_parent,
+                                      new_token, new_score, new_depth, (hipStream_t)stream);
     return e == hipSuccess ? JF_OK : JF_ERR_HIP;
 }
 

@@ -93,6 +93,16 @@ hipError_t launch_tree_mask(const int32_t *parent, int B, int N, uint64_t *mask,
 
 constexpr int kMaxBatch = 256;
 
+hipError_t launch_path_scores(const int32_t *parent, const float *logp, int B, int N, float *score,
+                              int32_t *seq_status, hipStream_t s);
+
+// One expansion step sorts every (node, rank) candidate of a sequence in LDS.
+constexpr int kExpandMaxCands = 16384;
+hipError_t launch_tree_expand(const float *score, const int32_t *depth, const int32_t *idx,
+                              const float *val, const float *lse, int B, int N, int k, int M,
+                              int max_depth, int32_t *new_parent, int32_t *new_token,
+                              float *new_score, int32_t *new_depth, hipStream_t s);
+
 struct AttnPlan {
     int B, N, Hq, Hkv, D, G, R, W;
     int n_qt;            // query tiles per (sequence, kv head)

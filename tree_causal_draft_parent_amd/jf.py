@@ -27,7 +27,7 @@ EXPORTS = ("jf_status_string", "jf_abi_version", "jf_tree_mask_build",
            "jf_fuse_proj_workspace_size", "jf_fuse_proj", "jf_fuse_proj_workspace_size_cus",
            "jf_fuse_proj_cus", "jf_tree_attn_workspace_size",
            "jf_tree_attn_fwd", "jf_tree_attn_workspace_size_cus", "jf_tree_attn_fwd_cus",
-           "jf_node_topk_workspace_size", "jf_node_topk")
+           "jf_node_topk_workspace_size", "jf_node_topk", "jf_path_scores", "jf_tree_expand")
 
 _lib = None
 
@@ -78,6 +78,10 @@ def lib():
     L.jf_node_topk_workspace_size.restype = SZ
     L.jf_node_topk.argtypes = [P, I64, I64, I64, ctypes.c_int, I32, P, P, P, P, SZ, P]
     L.jf_node_topk.restype = ctypes.c_int
+    L.jf_path_scores.argtypes = [P, P, I32, I32, P, P, P]
+    L.jf_path_scores.restype = ctypes.c_int
+    L.jf_tree_expand.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, P, P, P, P, P]
+    L.jf_tree_expand.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -261,3 +265,53 @@ def jf_node_topk(logits: torch.Tensor, k: int, with_lse: bool = True, idx=None, 
                             _p(workspace), ws_bytes, _stream(stream))
     _check("jf_node_topk", st)
     return idx, val, lse
+
+
+def jf_path_scores(parent: torch.Tensor, logp: torch.Tensor, score=None, seq_status=None,
+                   stream=None):
+    """parent [B, N] int32, logp [B, N] fp32 -> (score [B, N] fp32, seq_status [B] int32):
+    the sum of logp over each node's ancestors, itself included."""
+    _contig("parent", parent)
+    _contig("logp", logp)
+    B, N = parent.shape
+    if logp.shape != (B, N) or logp.dtype != torch.float32 or parent.dtype != torch.int32:
+        raise ValueError("parent [B, N] int32 and logp [B, N] float32 expected")
+    dev = parent.device
+    if score is None:
+        score = torch.empty((B, N), dtype=torch.float32, device=dev)
+    if seq_status is None:
+        seq_status = torch.empty((B,), dtype=torch.int32, device=dev)
+    st = lib().jf_path_scores(_p(parent), _p(logp), B, N, _p(score), _p(seq_status),
+                              _stream(stream))
+    _check("jf_path_scores", st)
+    return score, seq_status
+
+
+def jf_tree_expand(score: torch.Tensor, depth: torch.Tensor, idx: torch.Tensor,
+                   val: torch.Tensor, lse: torch.Tensor, M: int, max_depth: int, out=None,
+                   stream=None):
+    """One best-first expansion step: score [B, N] fp32, depth [B, N] int32,
+    idx [B, N, k] int32, val [B, N, k] fp32, lse [B, N] fp32 -> the M best
+    one-token extensions of each sequence's tree as (new_parent, new_token,
+    new_score, new_depth), each [B, M]."""
+    for n, t in (("score", score), ("depth", depth), ("idx", idx), ("val", val), ("lse", lse)):
+        _contig(n, t)
+    B, N = score.shape
+    k = idx.shape[-1]
+    if (depth.shape != (B, N) or idx.shape != (B, N, k) or val.shape != (B, N, k)
+            or lse.shape != (B, N)):
+        raise ValueError("inconsistent shapes")
+    if (score.dtype != torch.float32 or val.dtype != torch.float32 or lse.dtype != torch.float32
+            or depth.dtype != torch.int32 or idx.dtype != torch.int32):
+        raise ValueError("score/val/lse float32 and depth/idx int32 expected")
+    dev = score.device
+    if out is None:
+        out = (torch.empty((B, M), dtype=torch.int32, device=dev),
+               torch.empty((B, M), dtype=torch.int32, device=dev),
+               torch.empty((B, M), dtype=torch.float32, device=dev),
+               torch.empty((B, M), dtype=torch.int32, device=dev))
+    np_, nt, ns, nd = out
+    st = lib().jf_tree_expand(_p(score), _p(depth), _p(idx), _p(val), _p(lse), B, N, k, int(M),
+                              int(max_depth), _p(np_), _p(nt), _p(ns), _p(nd), _stream(stream))
+    _check("jf_tree_expand", st)
+    return np_, nt, ns, nd
