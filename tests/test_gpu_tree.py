@@ -137,3 +137,22 @@ def test_expand_signed_zero_and_infinite_scores():
     inp["val"][0, ::5, :] = inp["lse"][0, ::5, None]          # t = +0
     inp["score"][0, 1::9] = -np.inf
     _check_expand(inp, 200)
+
+
+@pytest.mark.parametrize("N,k", [(10, 8), (256, 8)])
+def test_expand_all_scores_equal(N, k):
+    # one selection bin holds every candidate: up to 96 of them are ranked
+    # inside the bin, more take the full sort
+    inp = synth.make_expand_inputs(B=2, N=N, k=k, max_depth=16, seed=8)
+    inp["score"][:] = 0.0
+    inp["val"][:] = inp["lse"][..., None]
+    _check_expand(inp, min(N * k, 300))
+
+
+def test_expand_crowded_bin_near_the_cut():
+    # a wide score range with a dense cluster at the budget boundary
+    inp = synth.make_expand_inputs(B=1, N=512, k=8, max_depth=16, seed=9)
+    inp["score"][0, 100:300] = 1.0
+    inp["val"][0, 100:300, :] = inp["lse"][0, 100:300, None]
+    inp["score"][0, :5] = 50.0
+    _check_expand(inp, 256)

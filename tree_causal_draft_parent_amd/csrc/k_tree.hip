@@ -60,7 +60,7 @@ __global__ __launch_bounds__(kPathThreads) void k_path_scores(const int32_t *__r
 }
 
 // ---------------------------------------------------------------------------
-constexpr int kExpThreads = 1024;
+constexpr int kExpThreads = 256;           // four wavefronts
 constexpr uint64_t kNoCand = ~0ull;
 
 // Order-preserving image of a float: a < b  <=>  ord(a) < ord(b) (NaN aside);
@@ -75,98 +75,311 @@ __device__ __forceinline__ float unord_f32(uint32_t o) {
     return __uint_as_float(u);
 }
 
-// Compare-exchange of a lane's key with the key of lane (lane ^ j), j < 64,
-// toward ascending order inside runs of length kk (descending in odd runs).
-__device__ __forceinline__ uint64_t xchg_lanes(uint64_t key, int e, int j, int kk) {
-    const int lane = threadIdx.x & 63;
-    const uint32_t lo = (uint32_t)key, hi = (uint32_t)(key >> 32);
-    const int src = (lane ^ j) << 2;
-    const uint32_t olo = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)lo);
-    const uint32_t ohi = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)hi);
-    const uint64_t other = ((uint64_t)ohi << 32) | olo;
-    const bool up = (e & kk) == 0;          // this run sorts ascending
-    const bool lower = (e & j) == 0;        // this lane holds the lower slot of the pair
-    const bool take_min = up == lower;
-    const uint64_t mn = key < other ? key : other;
-    const uint64_t mx = key < other ? other : key;
-    return take_min ? mn : mx;
+__device__ __forceinline__ uint64_t lane_xor(uint64_t v, int m) {
+    const int src = (((int)threadIdx.x & 63) ^ m) << 2;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
 }
 
-template <int LMAX>
+// Compare-exchange of the slot pairs (r, r ^ J) inside one lane's registers,
+// toward ascending order in runs of length kk (descending in odd runs).
+template <int R, int J>
+__device__ __forceinline__ void local_step(uint64_t (&key)[R], int e0, int kk) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        if (r & J) continue;
+        const bool up = ((e0 + r) & kk) == 0;
+        const uint64_t a = key[r], c = key[r | J];
+        const bool swap = (a > c) == up;
+        key[r] = swap ? c : a;
+        key[r | J] = swap ? a : c;
+    }
+}
+
+template <int R>
+__device__ __forceinline__ void local_steps(uint64_t (&key)[R], int e0, int kk, int j) {
+    // strides below R, largest first
+    if constexpr (R > 32) if (j >= 32) local_step<R, 32>(key, e0, kk);
+    if constexpr (R > 16) if (j >= 16) local_step<R, 16>(key, e0, kk);
+    if constexpr (R > 8) if (j >= 8) local_step<R, 8>(key, e0, kk);
+    if constexpr (R > 4) if (j >= 4) local_step<R, 4>(key, e0, kk);
+    if constexpr (R > 2) if (j >= 2) local_step<R, 2>(key, e0, kk);
+    if constexpr (R > 1) local_step<R, 1>(key, e0, kk);
+}
+
+// Bitonic sort of the L = 256*R keys held R per lane (slot e = thread*R + r),
+// ascending.  Strides j < R stay in a lane's registers, R <= j < 64R pair
+// lanes of one wavefront (cross-lane moves), j >= 64R pair wavefronts through
+// LDS.  Used when a selection bin near the top is crowded (mass ties).
+template <int R>
+__device__ __forceinline__ void bitonic_sort(uint64_t (&key)[R], uint64_t *lds, int e0) {
+    constexpr int L = kExpThreads * R;
+    const int lane = threadIdx.x & 63;
+    for (int kk = 2; kk <= L; kk <<= 1) {
+        int j = kk >> 1;
+        for (; j >= 64 * R; j >>= 1) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) lds[e0 + r] = key[r];
+            __syncthreads();
+            const bool lower = (e0 & j) == 0, up = (e0 & kk) == 0;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const uint64_t o = lds[(e0 + r) ^ j];
+                const uint64_t mn = key[r] < o ? key[r] : o, mx = key[r] < o ? o : key[r];
+                key[r] = (up == lower) ? mn : mx;
+            }
+            __syncthreads();
+        }
+        for (; j >= R; j >>= 1) {
+            const int m = j / R;
+            const bool lower = (lane & m) == 0, up = (e0 & kk) == 0;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const uint64_t o = lane_xor(key[r], m);
+                const uint64_t mn = key[r] < o ? key[r] : o, mx = key[r] < o ? o : key[r];
+                key[r] = (up == lower) ? mn : mx;
+            }
+        }
+        if (j >= 1) local_steps<R>(key, e0, kk, j);
+    }
+}
+
+constexpr int kSelBins = 1024;          // selection histogram bins
+constexpr int kSelMaxBin = 96;          // larger bin at or above the cut: sort instead
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1)
+        v = fmaxf(v, __int_as_float(__builtin_amdgcn_ds_bpermute(((threadIdx.x & 63) ^ m) << 2,
+                                                                  __float_as_int(v))));
+    return v;
+}
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1)
+        v = fminf(v, __int_as_float(__builtin_amdgcn_ds_bpermute(((threadIdx.x & 63) ^ m) << 2,
+                                                                  __float_as_int(v))));
+    return v;
+}
+
+// Inclusive prefix sum across a wavefront: shifts of 1, 2, 4 and 8 lanes
+// inside each row of 16 (DPP row_shr, zero from outside the row), then the
+// last lane of row 0 into rows 1 and 3 and of row 1 into rows 2 and 3
+// (row_bcast:15 / row_bcast:31).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+    int x = (int)v;
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31
+    return (uint32_t)x;
+}
+
+// One workgroup per sequence, R candidate slots per lane (slot e =
+// thread*R + r).  Selection of the M best keys:
+//   1. bins: bin(s) = floor((s_max - s) * kSelBins / (s_max - s_min)), clamped
+//      to [0, kSelBins); non-increasing in s, so a lower bin holds only
+//      strictly better scores and equal scores share a bin;
+//   2. an LDS histogram whose atomic return value is each key's place in its
+//      bin; one scan gives each bin's offset and the cut bin c, the first bin
+//      whose inclusive count reaches M;
+//   3. the keys of bins <= c go to their bin's segment of an LDS array, and
+//      each one's rank is its bin offset plus the number of smaller keys in
+//      its segment; ranks below M are output slots.
+// A bin of more than kSelMaxBin keys at or below the cut (mass ties) switches
+// the workgroup to the full bitonic sort.
+template <int R>
 __global__ __launch_bounds__(kExpThreads) void k_tree_expand(
     const float *__restrict__ score, const int32_t *__restrict__ depth,
     const int32_t *__restrict__ idx, const float *__restrict__ val, const float *__restrict__ lse,
-    int N, int k, int M, int max_depth, int L, int32_t *__restrict__ new_parent,
+    int N, int k, int M, int max_depth, int32_t *__restrict__ new_parent,
     int32_t *__restrict__ new_token, float *__restrict__ new_score,
     int32_t *__restrict__ new_depth) {
-    __shared__ uint64_t keys[LMAX];           // L = 2^n, 64 <= L <= LMAX, L >= N*k
+    constexpr int L = kExpThreads * R;
+    __shared__ uint64_t lds[L];
+    __shared__ uint32_t hist[kSelBins];
+    __shared__ uint32_t boff[kSelBins];
+    __shared__ float red[2][kExpThreads / 64];
+    __shared__ int sel[3];                  // cut bin, eligible count, use the sort
     const int b = blockIdx.x;
     const int nc = N * k;
     const int64_t nbase = (int64_t)b * N;
     const int64_t cbase = nbase * k;
+    const int e0 = threadIdx.x * R;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+
+    for (int i = threadIdx.x; i < kSelBins; i += kExpThreads) hist[i] = 0;
 
     // Keys: high word ~ord(score) (descending score first), low word the flat
-    // candidate index p*k + r (node ascending, then rank ascending).
-    for (int e = threadIdx.x; e < L; e += kExpThreads) {
-        uint64_t key = kNoCand;
-        if (e < nc) {
-            const int p = e / k;
-            const int d = depth[nbase + p];
-            if (d >= 1 && d < max_depth) {            // child depth d + 1 <= max_depth
-                const float t = val[cbase + e] - lse[nbase + p];   // rounded to fp32
-                const float s = score[nbase + p] + t;              // rounded to fp32
-                key = ((uint64_t)(~ord_f32(s)) << 32) | (uint32_t)e;
-            }
+    // candidate index p*k + r (node ascending, then rank ascending).  Every
+    // slot issues its loads unconditionally (indices clamped into range), so a
+    // lane's loads are in flight together instead of one slot after another.
+    int pr[R];
+    int32_t dr[R], tk[R];
+    float vr[R], lr[R], sr[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int e = min(e0 + r, nc - 1);
+        pr[r] = e / k;
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int e = min(e0 + r, nc - 1);
+        dr[r] = depth[nbase + pr[r]];
+        vr[r] = val[cbase + e];
+        lr[r] = lse[nbase + pr[r]];
+        sr[r] = score[nbase + pr[r]];
+        tk[r] = idx[cbase + e];
+    }
+    // Pin the loaded values here so no pass sinks a load back into the
+    // eligibility branch below (that would serialise the round trips again).
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        asm volatile("" : "+v"(dr[r]), "+v"(vr[r]), "+v"(lr[r]), "+v"(sr[r]), "+v"(tk[r]));
+    uint64_t key[R];
+    float sc[R];
+    float smax = -__builtin_inff(), smin = __builtin_inff();
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int e = e0 + r;
+        const float t = vr[r] - lr[r];            // rounded to fp32
+        sc[r] = sr[r] + t;                        // rounded to fp32
+        // eligible: child depth d + 1 <= max_depth
+        const bool ok = e < nc && dr[r] >= 1 && dr[r] < max_depth;
+        key[r] = ok ? (((uint64_t)(~ord_f32(sc[r])) << 32) | (uint32_t)e) : kNoCand;
+        if (ok && __builtin_isfinite(sc[r])) {
+            smax = fmaxf(smax, sc[r]);
+            smin = fminf(smin, sc[r]);
         }
-        keys[e] = key;
+    }
+    smax = wave_max(smax);
+    smin = wave_min(smin);
+    if (lane == 0) {
+        red[0][wave] = smax;
+        red[1][wave] = smin;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kExpThreads / 64; ++w) {
+        smax = fmaxf(smax, red[0][w]);
+        smin = fminf(smin, red[1][w]);
+    }
+    // Bin width from the finite range (0 when there is no range: one bin).
+    const float inv_w = smax > smin ? (float)kSelBins / (smax - smin) : 0.f;
+
+    int bin[R];
+    uint32_t pos[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        float x = (smax - sc[r]) * inv_w;         // NaN only for s = +inf with no range
+        x = x >= 0.f ? x : 0.f;                   // s above the finite maximum (+inf)
+        bin[r] = (int)fminf(x, (float)(kSelBins - 1));
+        pos[r] = key[r] != kNoCand ? atomicAdd(&hist[bin[r]], 1u) : 0u;
     }
     __syncthreads();
 
-    // Bitonic sort, ascending.  Runs of length kk are merged with strides
-    // j = kk/2 .. 1.  Strides >= 64 pair slots in different wavefronts and go
-    // through LDS; the strides below 64 of one run are done in registers
-    // between a load and a store of the lane's slots.
-    for (int kk = 2; kk <= L; kk <<= 1) {
-        int j = kk >> 1;
-        for (; j >= 64; j >>= 1) {
-            for (int t = threadIdx.x; t < (L >> 1); t += kExpThreads) {
-                const int lo = ((t & ~(j - 1)) << 1) | (t & (j - 1));
-                const int hi = lo | j;
-                const uint64_t a = keys[lo], c = keys[hi];
-                const bool up = (lo & kk) == 0;
-                if ((a > c) == up) {
-                    keys[lo] = c;
-                    keys[hi] = a;
-                }
-            }
-            __syncthreads();
+    // Wave 0: exclusive bin offsets, the cut bin and the crowding test.
+    if (wave == 0) {
+        constexpr int PER = kSelBins / 64;
+        uint32_t c[PER];
+        uint32_t sum = 0;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            c[i] = hist[lane * PER + i];
+            sum += c[i];
         }
-        // j < 64: each lane owns slot e; pairs (e, e ^ j) sit in one wavefront.
-        for (int e = threadIdx.x; e < L; e += kExpThreads) {
-            uint64_t key = keys[e];
-            for (int jj = j; jj >= 1; jj >>= 1) key = xchg_lanes(key, e, jj, kk);
-            keys[e] = key;
+        const uint32_t incl = wave_incl_scan(sum);   // inclusive scan of lane sums
+        const uint32_t total = (uint32_t)__builtin_amdgcn_ds_bpermute(63 << 2, (int)incl);
+        const uint32_t need = min((uint32_t)M, total);
+        uint32_t run = incl - sum;
+        int cut = kSelBins;                       // first bin whose inclusive count reaches need
+        uint32_t crowd = 0;                       // largest bin at or below the cut
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            boff[lane * PER + i] = run;
+            const uint32_t before = run;
+            run += c[i];
+            if (before < need) crowd = max(crowd, c[i]);
+            if (cut == kSelBins && run >= need && need > 0) cut = lane * PER + i;
         }
+        // smallest cut over lanes, largest crowding over lanes
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) {
+            cut = min(cut, __builtin_amdgcn_ds_bpermute((lane ^ m) << 2, cut));
+            crowd = max(crowd, (uint32_t)__builtin_amdgcn_ds_bpermute((lane ^ m) << 2, (int)crowd));
+        }
+        if (lane == 0) {
+            sel[0] = cut;
+            sel[1] = (int)total;
+            sel[2] = crowd > (uint32_t)kSelMaxBin;
+        }
+    }
+    __syncthreads();
+    const int cut = sel[0], n_elig = sel[1];
+
+    int rank[R];
+    if (!sel[2]) {
+        // scatter the keys at or below the cut into their bins' segments
+        // (indices are in range by construction; the clamps keep every LDS
+        // access inside the array whatever the offsets hold)
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            if (key[r] != kNoCand && bin[r] <= cut) lds[min((int)(boff[bin[r]] + pos[r]), L - 1)] = key[r];
         __syncthreads();
+        // rank = bin offset + smaller keys in the bin; the R keys' segment
+        // scans run side by side (a key outside the cut scans nothing)
+        int o[R], n[R], less[R];
+        int nmax = 0;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const bool in = key[r] != kNoCand && bin[r] <= cut;
+            o[r] = in ? (int)boff[bin[r]] : 0;
+            n[r] = in ? (int)hist[bin[r]] : 0;
+            less[r] = 0;
+            nmax = max(nmax, n[r]);
+        }
+        for (int i = 0; i < nmax; ++i) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const uint64_t v = lds[min(o[r] + min(i, max(n[r] - 1, 0)), L - 1)];
+                less[r] += (i < n[r]) & (v < key[r]);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) rank[r] = n[r] > 0 ? o[r] + less[r] : -1;
+    } else {
+        bitonic_sort<R>(key, lds, e0);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            rank[r] = key[r] != kNoCand ? e0 + r : -1;
+            // the sort moved the keys: gather their tokens and depths
+            const int e = rank[r] >= 0 ? (int)(uint32_t)key[r] : 0;
+            tk[r] = idx[cbase + e];
+            dr[r] = depth[nbase + e / k];
+        }
     }
 
-    // The first M keys, in order, are the new nodes.
+    // Keys with rank < M are the new nodes.
     const int64_t obase = (int64_t)b * M;
-    for (int m = threadIdx.x; m < M; m += kExpThreads) {
-        const uint64_t key = m < L ? keys[m] : kNoCand;
-        if (key != kNoCand) {
-            const int e = (int)(uint32_t)key;
-            const int p = e / k;
-            new_parent[obase + m] = p;
-            new_token[obase + m] = idx[cbase + e];
-            new_score[obase + m] = unord_f32(~(uint32_t)(key >> 32));
-            new_depth[obase + m] = depth[nbase + p] + 1;
-        } else {
-            new_parent[obase + m] = -2;
-            new_token[obase + m] = -1;
-            new_score[obase + m] = -__builtin_inff();
-            new_depth[obase + m] = 0;
-        }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int m = rank[r];
+        if (m < 0 || m >= M) continue;
+        const int e = (int)(uint32_t)key[r];
+        new_parent[obase + m] = e / k;
+        new_token[obase + m] = tk[r];
+        new_score[obase + m] = unord_f32(~(uint32_t)(key[r] >> 32));
+        new_depth[obase + m] = dr[r] + 1;
+    }
+    // Budget slots beyond the eligible candidates are empty.
+    for (int m = n_elig + threadIdx.x; m < M; m += kExpThreads) {
+        new_parent[obase + m] = -2;
+        new_token[obase + m] = -1;
+        new_score[obase + m] = -__builtin_inff();
+        new_depth[obase + m] = 0;
     }
 }
 
@@ -179,25 +392,26 @@ hipError_t launch_path_scores(const int32_t *parent, const float *logp, int B, i
     return hipGetLastError();
 }
 
-int tree_expand_slots(int N, int k) {
-    int L = 64;
-    while (L < N * k) L <<= 1;
-    return L;
-}
-
 hipError_t launch_tree_expand(const float *score, const int32_t *depth, const int32_t *idx,
                               const float *val, const float *lse, int B, int N, int k, int M,
                               int max_depth, int32_t *new_parent, int32_t *new_token,
                               float *new_score, int32_t *new_depth, hipStream_t s) {
-    const int L = tree_expand_slots(N, k);
-    if (L <= 2048)
-        hipLaunchKernelGGL(k_tree_expand<2048>, dim3(B), dim3(kExpThreads), 0, s, score, depth, idx,
-                           val, lse, N, k, M, max_depth, L, new_parent, new_token, new_score,
-                           new_depth);
-    else
-        hipLaunchKernelGGL(k_tree_expand<kExpandMaxCands>, dim3(B), dim3(kExpThreads), 0, s, score,
-                           depth, idx, val, lse, N, k, M, max_depth, L, new_parent, new_token,
-                           new_score, new_depth);
+    int R = 1;                                    // slots per lane: 256*R >= N*k
+    while (kExpThreads * R < N * k) R <<= 1;
+#define JF_EXPAND(RR)                                                                            \
+    hipLaunchKernelGGL(k_tree_expand<RR>, dim3(B), dim3(kExpThreads), 0, s, score, depth, idx,   \
+                       val, lse, N, k, M, max_depth, new_parent, new_token, new_score, new_depth)
+    switch (R) {
+        case 1: JF_EXPAND(1); break;
+        case 2: JF_EXPAND(2); break;
+        case 4: JF_EXPAND(4); break;
+        case 8: JF_EXPAND(8); break;
+        case 16: JF_EXPAND(16); break;
+        case 32: JF_EXPAND(32); break;
+        case 64: JF_EXPAND(64); break;
+        default: return hipErrorInvalidValue;
+    }
+#undef JF_EXPAND
     return hipGetLastError();
 }
 
