@@ -59,6 +59,8 @@ def parse():
     ap.add_argument("--cpu-sample-nodes", type=int, default=256)
     ap.add_argument("--no-context-projection", action="store_true",
                     help="skip timing the projection at one row per prefix token")
+    ap.add_argument("--no-tree-growth", action="store_true",
+                    help="skip timing the path-score and expansion calls after the step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy 5 times (counter calibration)")
     return ap.parse_args()
@@ -470,9 +472,11 @@ def main():
         proj_ctx = projection_context(wl, int(np.sum(prefix_len)), K, torch, jf)
         print(f"[bench] context projection: M={proj_ctx['M']} {proj_ctx['ms']:.4f} ms", file=sys.stderr, flush=True)
 
-    growth = tree_growth(wl, parent, depth, idx, val, rlse, K, torch, jf)
-    print(f"[bench] tree growth: path scores {growth['path_scores']['ms']:.4f} ms, "
-          f"expansion {growth['tree_expand']['ms']:.4f} ms", file=sys.stderr, flush=True)
+    growth = None
+    if not args.no_tree_growth:
+        growth = tree_growth(wl, parent, depth, idx, val, rlse, K, torch, jf)
+        print(f"[bench] tree growth: path scores {growth['path_scores']['ms']:.4f} ms, "
+              f"expansion {growth['tree_expand']['ms']:.4f} ms", file=sys.stderr, flush=True)
 
     def med(v):
         return float(np.median(v)) if len(v) else float("nan")
