@@ -18,6 +18,13 @@ Parity status of each function (what pins it, see tests/test_oracle_*.py):
   fuse_proj  -- pinned: numpy matmul of the concatenation, identity selector.
   topk       -- pinned: numpy lexsort brute force, all-equal rows, signed
                 zeros, -inf, scipy logsumexp.
+  path_scores -- pinned: hand-derived golden forest, chain == numpy cumsum,
+                star == inputs, recursion on random forests, relabelling.
+  tree_expand -- pinned: hand-derived golden step, numpy lexsort brute force
+                over float32 scores, depth cap, budget, ties, signed zeros.
+  tree_accept -- pinned: hand-derived golden tree, top-down greedy-decoding
+                simulation on trees with distinct sibling tokens, chain / star
+                / nothing-accepted closed cases, duplicate siblings, bad trees.
 """
 from __future__ import annotations
 
@@ -69,6 +76,8 @@ def _load():
     lib.oracle_path_scores.restype = ctypes.c_int
     lib.oracle_tree_expand.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, P, P, P, P]
     lib.oracle_tree_expand.restype = ctypes.c_int
+    lib.oracle_tree_accept.argtypes = [P, P, P, P, I64, I64, P, P, P, P, P]
+    lib.oracle_tree_accept.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
@@ -199,6 +208,28 @@ def tree_expand(score: np.ndarray, depth: np.ndarray, idx: np.ndarray, val: np.n
     if st != 0:
         raise ValueError(f"oracle_tree_expand: status {st}")
     return outp, outt, outs, outd
+
+
+def tree_accept(parent: np.ndarray, token: np.ndarray, target_next: np.ndarray,
+                root_next: np.ndarray):
+    """Greedy verification of a drafted tree: (accept_len [B], accept_node [B],
+    next_token [B], path [B, N], bad_node [B])."""
+    parent = _c(parent, np.int32)
+    token = _c(token, np.int32)
+    target_next = _c(target_next, np.int32)
+    root_next = _c(root_next, np.int32)
+    B, N = parent.shape
+    assert token.shape == (B, N) and target_next.shape == (B, N) and root_next.shape == (B,)
+    alen = np.zeros(B, np.int32)
+    anode = np.zeros(B, np.int32)
+    ntok = np.zeros(B, np.int32)
+    path = np.zeros((B, N), np.int32)
+    bad = np.zeros(B, np.int32)
+    st = _load().oracle_tree_accept(_p(parent), _p(token), _p(target_next), _p(root_next), B, N,
+                                    _p(alen), _p(anode), _p(ntok), _p(path), _p(bad))
+    if st != 0:
+        raise ValueError(f"oracle_tree_accept: status {st}")
+    return alen, anode, ntok, path, bad
 
 
 def num_threads() -> int:

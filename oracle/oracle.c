@@ -27,7 +27,9 @@
  * h / (Hq/Hkv); the fusion is concatenation followed by one bias-free linear
  * map; top-k order is value descending then index ascending, -0 == +0; a path
  * score is the sum of the conditional log-probabilities along the branch, and
- * one expansion step keeps the M best one-token extensions of the tree.
+ * one expansion step keeps the M best one-token extensions of the tree;
+ * verification is greedy (a node is accepted when its token is the target's
+ * next token after its parent) and keeps the deepest fully accepted node.
  */
 #include <math.h>
 #include <omp.h>
@@ -377,6 +379,66 @@ int oracle_tree_expand(const float *score, const int32_t *depth, const int32_t *
         }
     }
     free(c);
+    return OR_OK;
+}
+
+/* ---------------------------------------------------------------------------
+ * Greedy verification of a drafted tree: the longest accepted path.
+ *
+ * The target checks the whole tree in one parallel pass and accepts a prefix
+ * of the proposal, so a larger budget pays off only through a longer
+ * accepted prefix (JetFlow blog page, "The Causality-Efficiency Dilemma" and
+ * its introduction).  Reading taken (greedy verification; the pages do not
+ * spell out the rule): with pred(-1) = root_next[b], the target's next token
+ * after the prefix, and pred(j) = target_next[b][j], its next token after
+ * node j, node i is accepted when token[i] == pred(parent(i)) and every
+ * ancestor of i is accepted.  The answer is the deepest accepted node (depth
+ * = |anc(i)|; ties to the lower index), its depth as the accepted length, the
+ * nodes of its path from the prefix down to it, and the target's token after
+ * it (after the prefix when nothing is accepted).  A sequence whose parent
+ * array is not a forest (as in oracle_tree_mask) reports its smallest bad
+ * node and accepts nothing.
+ *
+ *   accept_len [B], accept_node [B] (-1: none), next_token [B],
+ *   path [B, N] (the first accept_len entries, the rest -1),
+ *   bad_node [B] (-1 for a forest).
+ * ------------------------------------------------------------------------- */
+int oracle_tree_accept(const int32_t *parent, const int32_t *token, const int32_t *target_next,
+                       const int32_t *root_next, int64_t B, int64_t N, int32_t *accept_len,
+                       int32_t *accept_node, int32_t *next_token, int32_t *path,
+                       int32_t *bad_node)
+{
+    if (B < 1 || N < 1) return OR_INVALID;
+    for (int64_t b = 0; b < B; ++b) {
+        const int32_t *par = parent + b * N;
+        const int32_t *tok = token + b * N;
+        const int32_t *nxt = target_next + b * N;
+        int64_t bad = -1, best = -1, best_depth = 0;
+        for (int64_t i = 0; i < N && bad < 0; ++i) {
+            /* walk i -> prefix: every node on the way must be accepted */
+            int64_t j = i, steps = 0;
+            int ok = 1;
+            while (j != -1) {
+                if (j < -1 || j >= N || steps >= N) { bad = i; break; }
+                const int64_t pj = par[j];
+                const int32_t pred = pj == -1 ? root_next[b]
+                                   : (pj >= 0 && pj < N ? nxt[pj] : -1);
+                if (tok[j] != pred) ok = 0;
+                j = pj;
+                ++steps;
+            }
+            if (bad >= 0) break;
+            if (ok && steps > best_depth) { best = i; best_depth = steps; }
+        }
+        for (int64_t i = 0; i < N; ++i) path[b * N + i] = -1;
+        bad_node[b] = (int32_t)bad;
+        if (bad >= 0) { best = -1; best_depth = 0; }
+        accept_node[b] = (int32_t)best;
+        accept_len[b] = (int32_t)best_depth;
+        next_token[b] = best >= 0 ? nxt[best] : root_next[b];
+        for (int64_t j = best, d = best_depth - 1; j != -1 && d >= 0; j = par[j], --d)
+            path[b * N + d] = (int32_t)j;
+    }
     return OR_OK;
 }
 

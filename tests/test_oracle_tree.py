@@ -155,3 +155,107 @@ def test_expand_signed_zero_is_plus_zero():
                                     2, 100)
     assert list(p[0]) == [0, 1]
     assert list(s[0].view(np.uint32)) == [0, 0]
+
+
+# ---------------------------------------------------------------------------
+# Greedy verification (longest accepted path)
+
+def test_accept_golden():
+    g = _read("accept_tree7.txt")
+    arr = {k: np.array([[int(t) for t in g[k]]], np.int32)
+           for k in ("parent", "token", "target_next")}
+    root = np.array([int(g["root_next"][0])], np.int32)
+    alen, anode, ntok, path, bad = oracle.tree_accept(arr["parent"], arr["token"],
+                                                      arr["target_next"], root)
+    assert alen[0] == int(g["accept_len"][0]) and anode[0] == int(g["accept_node"][0])
+    assert ntok[0] == int(g["next_token"][0]) and bad[0] == -1
+    assert list(path[0]) == [int(t) for t in g["path"]]
+
+
+def _greedy_decode(par, tok, nxt, root):
+    """Top-down: from the prefix, repeatedly step to the child whose token is
+    the target's next token (trees with distinct sibling tokens have at most
+    one), as greedy decoding of the target would."""
+    node, path = -1, []
+    while True:
+        want = root if node == -1 else nxt[node]
+        kids = [c for c in range(len(par)) if par[c] == node and tok[c] == want]
+        assert len(kids) <= 1
+        if not kids:
+            return len(path), node, want, path
+        node = kids[0]
+        path.append(node)
+
+
+def _verify_inputs(rng, N, q):
+    """A best-first tree with distinct sibling tokens; the target's next token
+    after a node is one of its children's tokens with probability q."""
+    par = synth.best_first_tree(rng, N, 16, (1, 8)).astype(np.int32)
+    tok = np.zeros(N, np.int32)
+    for p in range(-1, N):
+        kids = np.flatnonzero(par == p)
+        tok[kids] = rng.choice(1000, size=len(kids), replace=False)
+    nxt = rng.integers(1000, 2000, size=N).astype(np.int32)      # never a draft token
+    for j in range(N):
+        kids = np.flatnonzero(par == j)
+        if len(kids) and rng.random() < q:
+            nxt[j] = tok[rng.choice(kids)]
+    roots = np.flatnonzero(par == -1)
+    root = tok[rng.choice(roots)] if rng.random() < 0.9 else 5000
+    return par, tok, nxt, np.int32(root)
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("N,q", [(16, 0.8), (64, 0.9), (256, 0.95)])
+def test_accept_equals_greedy_decoding(seed, N, q):
+    rng = np.random.default_rng(seed * 100 + N)
+    B = 3
+    ins = [_verify_inputs(rng, N, q) for _ in range(B)]
+    par = np.stack([i[0] for i in ins])
+    tok = np.stack([i[1] for i in ins])
+    nxt = np.stack([i[2] for i in ins])
+    root = np.array([i[3] for i in ins], np.int32)
+    alen, anode, ntok, path, bad = oracle.tree_accept(par, tok, nxt, root)
+    for b in range(B):
+        L, node, want, p = _greedy_decode(par[b], tok[b], nxt[b], root[b])
+        assert (alen[b], anode[b], ntok[b]) == (L, node, want)
+        assert list(path[b, :L]) == p and np.all(path[b, L:] == -1) and bad[b] == -1
+
+
+def test_accept_closed_cases():
+    N = 12
+    chain = synth.chain_tree(N)[None].astype(np.int32)
+    tok = np.arange(100, 100 + N, dtype=np.int32)[None]
+    nxt = np.arange(101, 101 + N, dtype=np.int32)[None]       # each node predicts the next
+    alen, anode, ntok, path, _ = oracle.tree_accept(chain, tok, nxt, np.array([100], np.int32))
+    assert alen[0] == N and anode[0] == N - 1 and ntok[0] == 100 + N
+    assert list(path[0]) == list(range(N))
+    # nothing accepted: the next token is the target's token after the prefix
+    alen, anode, ntok, path, _ = oracle.tree_accept(chain, tok, nxt, np.array([7], np.int32))
+    assert (alen[0], anode[0], ntok[0]) == (0, -1, 7) and np.all(path == -1)
+    # star: several accepted roots of depth 1 -> the lowest index
+    star = synth.star_tree(N)[None].astype(np.int32)
+    tok = np.array([[5, 9, 9, 5, 9, 3, 9, 9, 9, 9, 9, 9]], np.int32)
+    alen, anode, ntok, path, _ = oracle.tree_accept(star, tok, nxt, np.array([9], np.int32))
+    assert (alen[0], anode[0], ntok[0]) == (1, 1, nxt[0, 1]) and path[0, 0] == 1
+
+
+def test_accept_duplicate_siblings_take_the_deeper_branch():
+    # nodes 0 and 1 both carry the target's first token; only node 1's branch
+    # continues, so the deepest accepted node is under node 1
+    par = np.array([[-1, -1, 1, 2, 0]], np.int32)
+    tok = np.array([[4, 4, 6, 8, 9]], np.int32)
+    nxt = np.array([[1, 6, 8, 2, 3]], np.int32)
+    alen, anode, ntok, path, _ = oracle.tree_accept(par, tok, nxt, np.array([4], np.int32))
+    assert (alen[0], anode[0], ntok[0]) == (3, 3, 2) and list(path[0, :3]) == [1, 2, 3]
+
+
+def test_accept_bad_trees_accept_nothing():
+    par = np.array([[-1, 0, 1, 2], [-1, 2, 1, 0], [-1, 0, 9, 1]], np.int32)
+    tok = np.zeros((3, 4), np.int32)
+    nxt = np.zeros((3, 4), np.int32)
+    alen, anode, ntok, path, bad = oracle.tree_accept(par, tok, nxt, np.zeros(3, np.int32))
+    assert list(bad) == [-1, 1, 2]
+    assert alen[0] == 4 and list(alen[1:]) == [0, 0] and list(anode[1:]) == [-1, -1]
+    _, _, mst, mbad = oracle.tree_mask(par[1:2])
+    assert mst == oracle.BAD_TREE and mbad == 1
