@@ -201,7 +201,7 @@ def copy_bandwidth(torch, reps=10):
     return 2 * COPY_BYTES * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
 
-def tree_growth(wl, parent, depth, idx, val, rlse, steps, torch, jf):
+def tree_growth(wl, parent, depth, idx, val, rlse, steps, torch, jf, parent_np=None, logits=None):
     """The calls that grow the tree after a step (outside the timed step):
     jf_path_scores over the step's tree (per-node conditional log-probabilities
     drawn from a seeded generator) and one jf_tree_expand of that tree by N new
@@ -224,11 +224,36 @@ def tree_growth(wl, parent, depth, idx, val, rlse, steps, torch, jf):
     def expand():
         jf.jf_tree_expand(score, depth, idx3, val3, lse2, M, wl.max_depth, out=outs)
 
+    # greedy verification of the same tree: the target's next tokens as the
+    # top-1 of logits of the verification pass's shape (the step's logits
+    # stand in for the target's), then the longest accepted path
+    v = synth.make_verify_inputs(parent_np, q=0.9, seed=synth.config_seed(wl_id(wl)) + 19)
+    vtok = torch.from_numpy(v["token"]).cuda()
+    vnxt = torch.from_numpy(v["target_next"]).cuda()
+    vroot = torch.from_numpy(v["root_next"]).cuda()
+    aouts = (torch.empty((B,), dtype=torch.int32, device="cuda"),
+             torch.empty((B,), dtype=torch.int32, device="cuda"),
+             torch.empty((B,), dtype=torch.int32, device="cuda"),
+             torch.empty((B, N), dtype=torch.int32, device="cuda"),
+             torch.empty((B,), dtype=torch.int32, device="cuda"))
+    R = logits.shape[0]
+    t1 = (torch.empty((R, 1), dtype=torch.int32, device="cuda"),
+          torch.empty((R, 1), dtype=torch.float32, device="cuda"))
+    t1_ws = torch.empty(max(jf.jf_node_topk_workspace_size(R, logits.shape[1], 1), 1),
+                        dtype=torch.uint8, device="cuda")
+
+    def accept():
+        jf.jf_tree_accept(parent, vtok, vnxt, vroot, out=aouts)
+
+    def argmax():
+        jf.jf_node_topk(logits, 1, with_lse=False, idx=t1[0], val=t1[1], workspace=t1_ws)
+
     # An isolated call would leave the GPU waiting for the host's launch, so
     # each call is captured REP times into a HIP graph and the replays are timed.
     REP = 20
     res = {}
-    for name, fn in (("path_scores", path), ("tree_expand", expand)):
+    for name, fn in (("path_scores", path), ("tree_expand", expand), ("tree_accept", accept),
+                     ("target_argmax", argmax)):
         fn()
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
@@ -249,8 +274,12 @@ def tree_growth(wl, parent, depth, idx, val, rlse, steps, torch, jf):
         res[name] = {"ms": round(float(np.mean(ms)), 5), "p50_ms": round(float(np.median(ms)), 5),
                      "bound": "latency", "timing": f"graph of {REP} back-to-back calls"}
         del g
-    assert bool((st == -1).all())
+    assert bool((st == -1).all()) and bool((aouts[4] == -1).all())
     res["tree_expand"].update(candidates=B * N * k, budget=M)
+    res["tree_accept"]["accepted_len"] = [int(x) for x in aouts[0].cpu()]
+    res["target_argmax"].update(rows=R, vocab=int(logits.shape[1]),
+                                GBps=round(logits.numel() * logits.element_size()
+                                           / (res["target_argmax"]["ms"] * 1e-3) / 1e9, 1))
     res["new_nodes_per_s"] = round(B * M / (res["tree_expand"]["ms"] * 1e-3), 1)
     return res
 
@@ -474,9 +503,12 @@ def main():
 
     growth = None
     if not args.no_tree_growth:
-        growth = tree_growth(wl, parent, depth, idx, val, rlse, K, torch, jf)
+        growth = tree_growth(wl, parent, depth, idx, val, rlse, K, torch, jf,
+                             parent_np=a["parent"], logits=logits)
         print(f"[bench] tree growth: path scores {growth['path_scores']['ms']:.4f} ms, "
-              f"expansion {growth['tree_expand']['ms']:.4f} ms", file=sys.stderr, flush=True)
+              f"expansion {growth['tree_expand']['ms']:.4f} ms, acceptance "
+              f"{growth['tree_accept']['ms']:.4f} ms, target top-1 {growth['target_argmax']['ms']:.4f} ms",
+              file=sys.stderr, flush=True)
 
     def med(v):
         return float(np.median(v)) if len(v) else float("nan")

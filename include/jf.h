@@ -275,6 +275,39 @@ jf_status jf_tree_expand(const float *score, const int32_t *depth,
                          int32_t *new_token, float *new_score,
                          int32_t *new_depth, void *stream);
 
+/* --------------------------------------------------------------------------
+ * jf_tree_accept -- greedy verification: the longest accepted path.
+ *
+ * The target model checks the whole drafted tree in one parallel pass and
+ * accepts a prefix of the proposal; a larger budget pays off only through a
+ * longer accepted prefix (JetFlow blog page, introduction and "The
+ * Causality-Efficiency Dilemma").  The pages do not spell out the rule;
+ * reading taken (greedy verification): node i is accepted when
+ * token[i] == target_next[parent(i)] (root_next for parent -1) and all its
+ * ancestors are accepted.  The deepest accepted node wins (ties to the
+ * lower index).  The target's next tokens come from its logits, e.g. from
+ * jf_node_topk with k = 1 over the verification pass's rows.
+ *
+ *   parent      [B, N] int32, as for jf_tree_mask_build.
+ *   token       [B, N] int32: each node's drafted token.
+ *   target_next [B, N] int32: the target's next token after each node.
+ *   root_next   [B] int32: the target's next token after the prefix.
+ *   accept_len  [B] int32: depth of the deepest accepted node (0: none).
+ *   accept_node [B] int32: that node, or -1.
+ *   next_token  [B] int32: target_next[accept_node], or root_next[b] when
+ *               nothing is accepted.
+ *   path        [B, N] int32 or NULL: the accepted nodes from the prefix
+ *               down (the first accept_len entries), then -1.
+ *   seq_status  [B] int32 or NULL: as for jf_tree_mask_build; a sequence
+ *               that is not a forest accepts nothing.
+ *   B >= 1, 1 <= N <= 4096.
+ * ------------------------------------------------------------------------ */
+jf_status jf_tree_accept(const int32_t *parent, const int32_t *token,
+                         const int32_t *target_next, const int32_t *root_next,
+                         int32_t B, int32_t N, int32_t *accept_len,
+                         int32_t *accept_node, int32_t *next_token,
+                         int32_t *path, int32_t *seq_status, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,7 +21,7 @@ def _declared():
 
 def test_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 15
+    assert len(names) == 16
     assert sorted(jf.EXPORTS) == names
     L = jf.lib()
     for n in names:
@@ -163,6 +163,20 @@ def test_path_and_expand_argument_errors():
     assert exp(N=2049) == jf.JF_ERR_UNSUPPORTED          # 2049 * 8 candidates > 16384
     assert exp(N=16384, k=2) == jf.JF_ERR_UNSUPPORTED
     assert exp(val=FAKE_ODD) == jf.JF_ERR_ALIGN
+
+
+def test_accept_argument_errors():
+    L = jf.lib()
+    ok = [FAKE, FAKE, FAKE, FAKE, 2, 64, FAKE, FAKE, FAKE, None, None, None]
+    assert L.jf_tree_accept(*ok[:0], None, *ok[1:]) == jf.JF_ERR_INVALID_ARG
+    bad = list(ok); bad[3] = None
+    assert L.jf_tree_accept(*bad) == jf.JF_ERR_INVALID_ARG
+    bad = list(ok); bad[4] = 0
+    assert L.jf_tree_accept(*bad) == jf.JF_ERR_INVALID_ARG
+    bad = list(ok); bad[5] = 4097
+    assert L.jf_tree_accept(*bad) == jf.JF_ERR_INVALID_ARG
+    bad = list(ok); bad[9] = FAKE_ODD                      # path misaligned
+    assert L.jf_tree_accept(*bad) == jf.JF_ERR_ALIGN
 
 
 def test_product_path_does_not_import_the_oracle():

@@ -156,3 +156,76 @@ def test_expand_crowded_bin_near_the_cut():
     inp["val"][0, 100:300, :] = inp["lse"][0, 100:300, None]
     inp["score"][0, :5] = 50.0
     _check_expand(inp, 256)
+
+
+# ---------------------------------------------------------------------------
+def _accept(par, v, with_path=True):
+    B, N = par.shape
+    say(f"tree_accept: B={B} N={N} path={with_path}")
+    outs = jf.jf_tree_accept(dev_tensor(par.astype(np.int32)), dev_tensor(v["token"]),
+                             dev_tensor(v["target_next"]), dev_tensor(v["root_next"]),
+                             with_path=with_path)
+    torch.cuda.synchronize()
+    return [None if o is None else o.cpu().numpy() for o in outs]
+
+
+def _check_accept(par, v):
+    alen, anode, ntok, path, st = _accept(par, v)
+    olen, onode, otok, opath, obad = oracle.tree_accept(par, v["token"], v["target_next"],
+                                                        v["root_next"])
+    assert np.array_equal(alen, olen) and np.array_equal(anode, onode)
+    assert np.array_equal(ntok, otok) and np.array_equal(path, opath)
+    assert np.array_equal(st, obad)
+    return alen
+
+
+@pytest.mark.parametrize("N,q", [(1, 0.9), (16, 0.8), (64, 0.9), (256, 0.95), (1000, 0.97),
+                                 (4096, 0.99)])
+def test_accept_random_trees(N, q):
+    rng = np.random.default_rng(N + 5)
+    par = np.stack([synth.best_first_tree(rng, N, 16, (1, 8)) for _ in range(4)]).astype(np.int32)
+    v = synth.make_verify_inputs(par, q=q, seed=N)
+    _check_accept(par, v)
+
+
+def test_accept_serving_batch():
+    rng = np.random.default_rng(32)
+    par = np.stack([synth.best_first_tree(rng, 64, 16, (1, 8)) for _ in range(32)]).astype(np.int32)
+    v = synth.make_verify_inputs(par, q=0.9, seed=32)
+    alen = _check_accept(par, v)
+    assert alen.max() > 1
+
+
+def test_accept_long_chain_and_none():
+    N = 4096
+    par = synth.chain_tree(N)[None].astype(np.int32)
+    v = dict(token=np.arange(N, dtype=np.int32)[None], target_next=np.arange(1, N + 1, dtype=np.int32)[None],
+             root_next=np.array([0], np.int32))
+    assert _check_accept(par, v)[0] == N
+    v["root_next"][:] = 77777
+    assert _check_accept(par, v)[0] == 0
+
+
+def test_accept_duplicates_star_and_bad_trees():
+    par = np.array([[-1, -1, 1, 2, 0]], np.int32)
+    v = dict(token=np.array([[4, 4, 6, 8, 9]], np.int32),
+             target_next=np.array([[1, 6, 8, 2, 3]], np.int32), root_next=np.array([4], np.int32))
+    _check_accept(par, v)
+    star = synth.star_tree(12)[None].astype(np.int32)
+    v = dict(token=np.array([[5, 9, 9, 5, 9, 3, 9, 9, 9, 9, 9, 9]], np.int32),
+             target_next=np.arange(12, dtype=np.int32)[None], root_next=np.array([9], np.int32))
+    _check_accept(star, v)
+    par = np.array([[-1, 0, 1, 2], [-1, 2, 1, 0], [-1, 0, 9, 1], [3, -1, 1, 3]], np.int32)
+    v = dict(token=np.zeros((4, 4), np.int32), target_next=np.zeros((4, 4), np.int32),
+             root_next=np.zeros(4, np.int32))
+    _check_accept(par, v)
+
+
+def test_accept_without_path():
+    rng = np.random.default_rng(3)
+    par = np.stack([synth.best_first_tree(rng, 256, 16, (1, 8)) for _ in range(2)]).astype(np.int32)
+    v = synth.make_verify_inputs(par, q=0.95, seed=3)
+    alen, anode, ntok, path, st = _accept(par, v, with_path=False)
+    olen, onode, otok, _, _ = oracle.tree_accept(par, v["token"], v["target_next"], v["root_next"])
+    assert path is None
+    assert np.array_equal(alen, olen) and np.array_equal(anode, onode) and np.array_equal(ntok, otok)

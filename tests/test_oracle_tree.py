@@ -205,6 +205,20 @@ def _verify_inputs(rng, N, q):
     return par, tok, nxt, np.int32(root)
 
 
+@pytest.mark.parametrize("N,q", [(16, 0.8), (64, 0.9), (256, 0.95)])
+def test_accept_equals_greedy_decoding_synth(N, q):
+    # the shared input generator's trees and tokens, checked the same way
+    rng = np.random.default_rng(N)
+    par = np.stack([synth.best_first_tree(rng, N, 16, (1, 8)) for _ in range(4)]).astype(np.int32)
+    v = synth.make_verify_inputs(par, q=q, seed=N)
+    alen, anode, ntok, path, bad = oracle.tree_accept(par, v["token"], v["target_next"],
+                                                      v["root_next"])
+    for b in range(4):
+        L, node, want, p = _greedy_decode(par[b], v["token"][b], v["target_next"][b],
+                                          v["root_next"][b])
+        assert (alen[b], anode[b], ntok[b]) == (L, node, want) and list(path[b, :L]) == p
+
+
 @pytest.mark.parametrize("seed", range(6))
 @pytest.mark.parametrize("N,q", [(16, 0.8), (64, 0.9), (256, 0.95)])
 def test_accept_equals_greedy_decoding(seed, N, q):

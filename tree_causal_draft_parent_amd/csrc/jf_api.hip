@@ -253,6 +253,24 @@ jf_status jf_path_scores(const int32_t *parent, const float *logp, int32_t B, in
     return e == hipSuccess ? JF_OK : JF_ERR_HIP;
 }
 
+jf_status jf_tree_accept(const int32_t *parent, const int32_t *token, const int32_t *target_next,
+                         const int32_t *root_next, int32_t B, int32_t N, int32_t *accept_len,
+                         int32_t *accept_node, int32_t *next_token, int32_t *path,
+                         int32_t *seq_status, void *stream) {
+    if (!parent || !token || !target_next || !root_next || !accept_len || !accept_node ||
+        !next_token)
+        return JF_ERR_INVALID_ARG;
+    if (B < 1 || N < 1 || N > 4096) return JF_ERR_INVALID_ARG;
+    const void *ptrs[] = {parent, token, target_next, root_next, accept_len, accept_node,
+                          next_token, path, seq_status};
+    for (const void *q : ptrs)
+        if (q && !aligned(q, 4)) return JF_ERR_ALIGN;
+    hipError_t e = launch_tree_accept(parent, token, target_next, root_next, B, N, accept_len,
+                                      accept_node, next_token, path, seq_status,
+                                      (hipStream_t)stream);
+    return e == hipSuccess ? JF_OK : JF_ERR_HIP;
+}
+
 jf_status jf_tree_expand(const float *score, const int32_t *depth, const int32_t *idx,
                          const float *val, const float *lse, int32_t B, int32_t N, int32_t k,
                          int32_t M, int32_t max_depth, int32_t *new_parent, int32_t *new_token,

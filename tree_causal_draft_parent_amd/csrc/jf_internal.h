@@ -96,6 +96,11 @@ constexpr int kMaxBatch = 256;
 hipError_t launch_path_scores(const int32_t *parent, const float *logp, int B, int N, float *score,
                               int32_t *seq_status, hipStream_t s);
 
+hipError_t launch_tree_accept(const int32_t *parent, const int32_t *token,
+                              const int32_t *target_next, const int32_t *root_next, int B, int N,
+                              int32_t *accept_len, int32_t *accept_node, int32_t *next_token,
+                              int32_t *path, int32_t *seq_status, hipStream_t s);
+
 // One expansion step sorts every (node, rank) candidate of a sequence in LDS.
 constexpr int kExpandMaxCands = 16384;
 hipError_t launch_tree_expand(const float *score, const int32_t *depth, const int32_t *idx,

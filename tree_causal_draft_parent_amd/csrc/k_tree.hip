@@ -383,12 +383,89 @@ __global__ __launch_bounds__(kExpThreads) void k_tree_expand(
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Greedy verification: node i is accepted when its token is the target's next
+// token after its parent (after the prefix for a root) and every ancestor is
+// accepted; the deepest accepted node wins, ties to the lower index.  One
+// workgroup per sequence with parents, tokens and the target's tokens in LDS.
+constexpr int kAccThreads = 256;
+
+__global__ __launch_bounds__(kAccThreads) void k_tree_accept(
+    const int32_t *__restrict__ parent, const int32_t *__restrict__ token,
+    const int32_t *__restrict__ target_next, const int32_t *__restrict__ root_next, int N,
+    int32_t *__restrict__ accept_len, int32_t *__restrict__ accept_node,
+    int32_t *__restrict__ next_token, int32_t *__restrict__ path,
+    int32_t *__restrict__ seq_status) {
+    __shared__ int32_t par[kPathMaxN];
+    __shared__ int32_t tok[kPathMaxN];
+    __shared__ int32_t nxt[kPathMaxN];
+    __shared__ int32_t first_bad;
+    __shared__ int32_t best;                  // depth * 8192 + (8191 - node), 0: none
+    const int b = blockIdx.x;
+    const int64_t base = (int64_t)b * N;
+    for (int i = threadIdx.x; i < N; i += kAccThreads) {
+        par[i] = parent[base + i];
+        tok[i] = token[base + i];
+        nxt[i] = target_next[base + i];
+    }
+    if (threadIdx.x == 0) {
+        first_bad = INT32_MAX;
+        best = 0;
+    }
+    const int32_t root = root_next[b];
+    __syncthreads();
+
+    for (int i = threadIdx.x; i < N; i += kAccThreads) {
+        int j = i, steps = 0;
+        bool ok = true, acc = true;
+        while (j != -1) {
+            if (j < -1 || j >= N || steps >= N) { ok = false; break; }
+            const int pj = par[j];
+            const int32_t pred = pj == -1 ? root : (pj >= 0 && pj < N ? nxt[pj] : -1);
+            acc = acc && tok[j] == pred;
+            j = pj;
+            ++steps;
+        }
+        if (!ok) atomicMin(&first_bad, i);
+        else if (acc) atomicMax(&best, steps * 8192 + (8191 - i));
+    }
+    __syncthreads();
+
+    const bool bad = first_bad != INT32_MAX;
+    const int key = bad ? 0 : best;
+    const int len = key >> 13;
+    const int node = key ? 8191 - (key & 8191) : -1;
+    // Path slot d holds the ancestor of `node` at depth d + 1: lane 0 walks
+    // up once and writes slots len-1 .. 0; the other slots read -1.
+    if (path) {
+        for (int d = len + threadIdx.x; d < N; d += kAccThreads) path[base + d] = -1;
+        if (threadIdx.x == 0)
+            for (int a = node, d = len - 1; d >= 0; a = par[a], --d) path[base + d] = a;
+    }
+    if (threadIdx.x == 0) {
+        accept_len[b] = len;
+        accept_node[b] = node;
+        next_token[b] = node >= 0 ? nxt[node] : root;
+        if (seq_status) seq_status[b] = bad ? first_bad : -1;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_path_scores(const int32_t *parent, const float *logp, int B, int N, float *score,
                               int32_t *seq_status, hipStream_t s) {
     hipLaunchKernelGGL(k_path_scores, dim3(B), dim3(kPathThreads), 0, s, parent, logp, N, score,
                        seq_status);
+    return hipGetLastError();
+}
+
+hipError_t launch_tree_accept(const int32_t *parent, const int32_t *token,
+                              const int32_t *target_next, const int32_t *root_next, int B, int N,
+                              int32_t *accept_len, int32_t *accept_node, int32_t *next_token,
+                              int32_t *path, int32_t *seq_status, hipStream_t s) {
+    hipLaunchKernelGGL(k_tree_accept, dim3(B), dim3(kAccThreads), 0, s, parent, token, target_next,
+                       root_next, N, accept_len, accept_node, next_token, path, seq_status);
     return hipGetLastError();
 }
 

@@ -27,7 +27,8 @@ EXPORTS = ("jf_status_string", "jf_abi_version", "jf_tree_mask_build",
            "jf_fuse_proj_workspace_size", "jf_fuse_proj", "jf_fuse_proj_workspace_size_cus",
            "jf_fuse_proj_cus", "jf_tree_attn_workspace_size",
            "jf_tree_attn_fwd", "jf_tree_attn_workspace_size_cus", "jf_tree_attn_fwd_cus",
-           "jf_node_topk_workspace_size", "jf_node_topk", "jf_path_scores", "jf_tree_expand")
+           "jf_node_topk_workspace_size", "jf_node_topk", "jf_path_scores", "jf_tree_expand",
+           "jf_tree_accept")
 
 _lib = None
 
@@ -82,6 +83,8 @@ def lib():
     L.jf_path_scores.restype = ctypes.c_int
     L.jf_tree_expand.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, P, P, P, P, P]
     L.jf_tree_expand.restype = ctypes.c_int
+    L.jf_tree_accept.argtypes = [P, P, P, P, I32, I32, P, P, P, P, P, P]
+    L.jf_tree_accept.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -315,3 +318,30 @@ def jf_tree_expand(score: torch.Tensor, depth: torch.Tensor, idx: torch.Tensor,
                               int(max_depth), _p(np_), _p(nt), _p(ns), _p(nd), _stream(stream))
     _check("jf_tree_expand", st)
     return np_, nt, ns, nd
+
+
+def jf_tree_accept(parent: torch.Tensor, token: torch.Tensor, target_next: torch.Tensor,
+                   root_next: torch.Tensor, out=None, with_path: bool = True, stream=None):
+    """Greedy verification: parent, token, target_next [B, N] int32 and
+    root_next [B] int32 -> (accept_len [B], accept_node [B], next_token [B],
+    path [B, N] or None, seq_status [B])."""
+    for n, t in (("parent", parent), ("token", token), ("target_next", target_next),
+                 ("root_next", root_next)):
+        _contig(n, t)
+        if t.dtype != torch.int32:
+            raise ValueError(f"{n} must be int32")
+    B, N = parent.shape
+    if token.shape != (B, N) or target_next.shape != (B, N) or root_next.shape != (B,):
+        raise ValueError("inconsistent shapes")
+    dev = parent.device
+    if out is None:
+        out = (torch.empty((B,), dtype=torch.int32, device=dev),
+               torch.empty((B,), dtype=torch.int32, device=dev),
+               torch.empty((B,), dtype=torch.int32, device=dev),
+               torch.empty((B, N), dtype=torch.int32, device=dev) if with_path else None,
+               torch.empty((B,), dtype=torch.int32, device=dev))
+    alen, anode, ntok, path, st = out
+    s = lib().jf_tree_accept(_p(parent), _p(token), _p(target_next), _p(root_next), B, N,
+                             _p(alen), _p(anode), _p(ntok), _p(path), _p(st), _stream(stream))
+    _check("jf_tree_accept", s)
+    return alen, anode, ntok, path, st

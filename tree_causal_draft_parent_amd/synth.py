@@ -281,6 +281,33 @@ def make_expand_inputs(*, B: int, N: int, k: int, V: int = 151936, max_depth: in
                 max_depth=max_depth)
 
 
+def make_verify_inputs(parent: np.ndarray, *, q: float = 0.9, seed: int = 1234) -> dict:
+    """Draft tokens and target tokens for greedy verification of the trees
+    `parent` [B, N]: sibling tokens are distinct draws from [0, 1000); the
+    target's next token after a node is one of its children's tokens with
+    probability q, else a token in [1000, 2000) that no node carries; after
+    the prefix it is one root's token with probability 0.9, else 5000."""
+    rng = _seeds(seed, ("tok", "nxt", "root"))
+    B, N = parent.shape
+    tok = np.zeros((B, N), np.int32)
+    nxt = rng["nxt"].integers(1000, 2000, size=(B, N)).astype(np.int32)
+    root = np.full(B, 5000, np.int32)
+    for b in range(B):
+        kids_of = {}
+        for i, p in enumerate(parent[b]):
+            kids_of.setdefault(int(p), []).append(i)
+        for p, kids in kids_of.items():
+            tok[b, kids] = rng["tok"].choice(1000, size=len(kids), replace=False)
+        for j in range(N):
+            kids = kids_of.get(j)
+            if kids and rng["nxt"].random() < q:
+                nxt[b, j] = tok[b, kids[rng["nxt"].integers(len(kids))]]
+        roots = kids_of.get(-1, [])
+        if roots and rng["root"].random() < 0.9:
+            root[b] = tok[b, roots[rng["root"].integers(len(roots))]]
+    return dict(token=tok, target_next=nxt, root_next=root)
+
+
 def config_seed(i: int) -> int:
     return 1000 + i
 
