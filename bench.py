@@ -61,6 +61,8 @@ def parse():
                     help="skip timing the projection at one row per prefix token")
     ap.add_argument("--no-tree-growth", action="store_true",
                     help="skip timing the path-score and expansion calls after the step")
+    ap.add_argument("--no-lm-head", action="store_true",
+                    help="skip timing the LM-head contraction (one-layer jf_fuse_proj to the vocabulary)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy 5 times (counter calibration)")
     return ap.parse_args()
@@ -281,6 +283,42 @@ def tree_growth(wl, parent, depth, idx, val, rlse, steps, torch, jf, parent_np=N
                                 GBps=round(logits.numel() * logits.element_size()
                                            / (res["target_argmax"]["ms"] * 1e-3) / 1e9, 1))
     res["new_nodes_per_s"] = round(B * M / (res["tree_expand"]["ms"] * 1e-3), 1)
+    return res
+
+
+def lm_head(wl, steps, torch, jf):
+    """The draft layer's LM head as jf_fuse_proj with one layer: B*N tree-node
+    rows x H hidden -> V vocabulary logits in bf16 (the top-k's input shape).
+    The weights are random bf16 drawn on the device (timing only; parity is
+    tested on the seeded generator's weights).  HBM-bound: the V x H weight
+    stream dominates."""
+    if wl.dtype != "bf16":
+        return None
+    M, H, V = wl.B * wl.N, wl.H, wl.V
+    g = torch.Generator(device="cuda").manual_seed(31)
+    w = (torch.randn((V, H), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    x = torch.randn((M, H), generator=g, device="cuda").to(torch.bfloat16)
+    y = torch.empty((M, V), dtype=torch.bfloat16, device="cuda")
+    need = jf.jf_fuse_proj_workspace_size(M, H, 1, V, jf.JF_BF16)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        jf.jf_fuse_proj([x], w, y=y, workspace=ws)
+    torch.cuda.synchronize()
+    n = max(5, steps // 5)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        jf.jf_fuse_proj([x], w, y=y, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    nbytes = V * H * 2 + M * H * 2 + M * V * 2
+    flops = 2 * M * H * V
+    res = {"M": M, "K": H, "N": V, "ms": round(ms, 5), "bytes": nbytes,
+           "hbm_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+           "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2), "launches": n}
+    del w, x, y, ws
     return res
 
 
@@ -510,6 +548,13 @@ def main():
               f"{growth['tree_accept']['ms']:.4f} ms, target top-1 {growth['target_argmax']['ms']:.4f} ms",
               file=sys.stderr, flush=True)
 
+    head = None
+    if not args.no_lm_head:
+        head = lm_head(wl, K, torch, jf)
+        if head is not None:
+            print(f"[bench] LM head {head['M']}x{head['K']}->{head['N']}: {head['ms']:.4f} ms, "
+                  f"{head['hbm_GBps']:.0f} GB/s", file=sys.stderr, flush=True)
+
     def med(v):
         return float(np.median(v)) if len(v) else float("nan")
 
@@ -601,6 +646,7 @@ def main():
         "projection": projection,
         "projection_context": proj_ctx,
         "tree_growth": growth,
+        "lm_head": head,
         "copy_GBps": round(copy_gbs, 1),
         "roofline": roofline,
         "cpu_baseline": cpu,

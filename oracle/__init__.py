@@ -22,6 +22,10 @@ Parity status of each function (what pins it, see tests/test_oracle_*.py):
                 star == inputs, recursion on random forests, relabelling.
   tree_expand -- pinned: hand-derived golden step, numpy lexsort brute force
                 over float32 scores, depth cap, budget, ties, signed zeros.
+  tree_rope  -- pinned: hand-derived golden rotation (D = 4), position 0 is
+                the identity, pair norms kept, rotations compose by adding
+                positions, scores depend only on the position difference,
+                a chain's positions are P, P+1, ...
   tree_accept -- pinned: hand-derived golden tree, top-down greedy-decoding
                 simulation on trees with distinct sibling tokens, chain / star
                 / nothing-accepted closed cases, duplicate siblings, bad trees.
@@ -78,6 +82,8 @@ def _load():
     lib.oracle_tree_expand.restype = ctypes.c_int
     lib.oracle_tree_accept.argtypes = [P, P, P, P, I64, I64, P, P, P, P, P]
     lib.oracle_tree_accept.restype = ctypes.c_int
+    lib.oracle_tree_rope.argtypes = [P, P, P, I64, I64, I64, I64, ctypes.c_double]
+    lib.oracle_tree_rope.restype = None
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
@@ -230,6 +236,18 @@ def tree_accept(parent: np.ndarray, token: np.ndarray, target_next: np.ndarray,
     if st != 0:
         raise ValueError(f"oracle_tree_accept: status {st}")
     return alen, anode, ntok, path, bad
+
+
+def tree_rope(x: np.ndarray, depth: np.ndarray, prefix_len, theta: float = 1e6) -> np.ndarray:
+    """Rotary embedding of x [B, N, H, D] (float64 copy returned) at positions
+    prefix_len[b] + depth[b, i] - 1; depth < 1 leaves a node unchanged."""
+    x = np.array(x, dtype=np.float64, copy=True, order="C")
+    depth = _c(depth, np.int32)
+    pl = _c(np.asarray(prefix_len), np.int32)
+    B, N, H, D = x.shape
+    assert D % 2 == 0 and depth.shape == (B, N) and pl.shape == (B,)
+    _load().oracle_tree_rope(_p(x), _p(depth), _p(pl), B, N, H, D, float(theta))
+    return x
 
 
 def num_threads() -> int:

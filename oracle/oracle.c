@@ -383,6 +383,43 @@ int oracle_tree_expand(const float *score, const int32_t *depth, const int32_t *
 }
 
 /* ---------------------------------------------------------------------------
+ * Rotary position embedding of the tree nodes' queries and keys.
+ *
+ * The pages draft with Qwen3 target models (abstract), which rotate queries
+ * and keys by their positions (rotary embedding, RoFormer).  A tree node's
+ * position is the prefix length plus its depth minus one: a node hanging off
+ * the prefix end sits right after the last prefix token, and every node of
+ * a branch sits one step after its parent, as in ordinary decoding of that
+ * branch.  Pairing as in the Qwen3 models (component d with d + D/2):
+ *     a = pos * theta^(-2j/D),  j < D/2
+ *     out[j]       = x[j] cos a - x[j + D/2] sin a
+ *     out[j + D/2] = x[j + D/2] cos a + x[j] sin a
+ * Nodes of depth < 1 (bad rows of the mask builder) are left unchanged.
+ * x [B, N, H, D] in place; depth [B, N]; prefix_len [B].
+ * ------------------------------------------------------------------------- */
+void oracle_tree_rope(double *x, const int32_t *depth, const int32_t *prefix_len, int64_t B,
+                      int64_t N, int64_t H, int64_t D, double theta)
+{
+    const int64_t half = D / 2;
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t i = 0; i < N; ++i) {
+            const int32_t d = depth[b * N + i];
+            if (d < 1) continue;
+            const double pos = (double)prefix_len[b] + (double)d - 1.0;
+            for (int64_t h = 0; h < H; ++h) {
+                double *row = x + ((b * N + i) * H + h) * D;
+                for (int64_t j = 0; j < half; ++j) {
+                    const double a = pos * pow(theta, -2.0 * (double)j / (double)D);
+                    const double c = cos(a), sn = sin(a);
+                    const double x0 = row[j], x1 = row[j + half];
+                    row[j] = x0 * c - x1 * sn;
+                    row[j + half] = x1 * c + x0 * sn;
+                }
+            }
+        }
+}
+
+/* ---------------------------------------------------------------------------
  * Greedy verification of a drafted tree: the longest accepted path.
  *
  * The target checks the whole tree in one parallel pass and accepts a prefix

@@ -92,3 +92,24 @@ def test_context_rows_sampled():
                            np.arange(4096, 4100)])
     _run(synth.make_fuse_inputs(M=M, H_in=4096, H_out=4096, n_fused=3, dtype="bf16", seed=1019),
          rows=rows)
+
+
+def test_lm_head_shape_sampled():
+    # the draft layer's LM head as the same call with one layer: 256 tree-node
+    # rows x 4096 hidden -> 151936 vocabulary logits (1187 output tiles, no K
+    # split); checked on sampled rows and vocabulary columns (the oracle is
+    # the definition restricted to them)
+    inp = synth.make_fuse_inputs(M=256, H_in=4096, H_out=151936, n_fused=1, dtype="bf16", seed=2027)
+    say("fuse: LM head 256 x 4096 -> 151936")
+    xt = dev_tensor(inp["x"], "bf16")
+    y = jf.jf_fuse_proj([xt[0]], dev_tensor(inp["w"], "bf16"), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    rows = np.sort(rng.choice(256, 8, replace=False))
+    cols = np.concatenate([np.sort(rng.choice(151936, 2000, replace=False)), np.arange(151808, 151936)])
+    got = host_f64(y)[rows][:, cols]
+    ref = oracle.fuse_proj(synth.to_f64(inp["x"], "bf16"), synth.to_f64(inp["w"][cols], "bf16"),
+                           rows=rows)
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 7)
+    assert np.all(np.abs(got - ref) <= np.maximum(2e-2, ulp))
+    assert rel_rms(got, ref) <= 1e-2
