@@ -322,6 +322,35 @@ def lm_head(wl, steps, torch, jf):
     return res
 
 
+def rope_timing(wl, q, k_tree, depth, prefix_len, steps, torch, jf):
+    """jf_tree_rope over the step's queries and tree keys (copies), at the
+    tree positions; latency-bound, timed as a HIP graph of 20 calls."""
+    qc, kc = q.clone(), k_tree.clone()
+    pl = torch.from_numpy(np.asarray(prefix_len, np.int32)).cuda()
+    REP = 20
+    jf.jf_tree_rope(qc, kc, depth, pl)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(REP):
+            jf.jf_tree_rope(qc, kc, depth, pl)
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(max(5, steps // REP)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1) / REP)
+    nbytes = 2 * (qc.numel() + kc.numel()) * qc.element_size()
+    t = float(np.mean(ms))
+    return {"ms": round(t, 5), "bytes": nbytes, "GBps": round(nbytes / (t * 1e-3) / 1e9, 1),
+            "bound": "latency", "timing": f"graph of {REP} back-to-back calls"}
+
+
 def wl_id(wl):
     from tree_causal_draft_parent_amd import synth
     return next(i for i, w in synth.WORKLOADS.items() if w.name == wl.name)
@@ -550,7 +579,10 @@ def main():
 
     head = None
     if not args.no_lm_head:
+        rope = rope_timing(wl, dev["q"], dev["k_tree"], depth, prefix_len, K, torch, jf)
         head = lm_head(wl, K, torch, jf)
+        if head is not None:
+            head["rope"] = rope
         if head is not None:
             print(f"[bench] LM head {head['M']}x{head['K']}->{head['N']}: {head['ms']:.4f} ms, "
                   f"{head['hbm_GBps']:.0f} GB/s", file=sys.stderr, flush=True)
@@ -646,7 +678,7 @@ def main():
         "projection": projection,
         "projection_context": proj_ctx,
         "tree_growth": growth,
-        "lm_head": head,
+        "draft_layer": head,
         "copy_GBps": round(copy_gbs, 1),
         "roofline": roofline,
         "cpu_baseline": cpu,

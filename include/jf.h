@@ -276,6 +276,31 @@ jf_status jf_tree_expand(const float *score, const int32_t *depth,
                          int32_t *new_depth, void *stream);
 
 /* --------------------------------------------------------------------------
+ * jf_tree_rope -- rotary position embedding of the tree nodes, in place.
+ *
+ * The pages draft for Qwen3 target models (abstract), which rotate queries
+ * and keys by position (rotary embedding, RoFormer).  A node's position is
+ * prefix_len[b] + depth[b][i] - 1, the position of ordinary decoding along
+ * its branch (a prefix child sits right after the last prefix token).
+ * Pairs (j, j + D/2) as in the Qwen3 models:
+ *     a = pos * theta^(-2j/D),  x[j] <- x[j] cos a - x[j+D/2] sin a,
+ *                               x[j+D/2] <- x[j+D/2] cos a + x[j] sin a.
+ * Angles are formed in fp64, the rotation in fp32 (bf16 storage rounds to
+ * nearest even).  Nodes of depth < 1 are left unchanged.
+ *
+ *   q          [B, N, Hq, D] dtype, rotated in place.
+ *   k          [B, N, Hkv, D] dtype or NULL, rotated in place.
+ *   depth      [B, N] int32 (jf_tree_mask_build).
+ *   prefix_len [B] int32, DEVICE memory.
+ *   theta      rotary base; <= 0 selects 1e6 (the Qwen3 models' base).
+ *   D even, 2 <= D <= 256.
+ * ------------------------------------------------------------------------ */
+jf_status jf_tree_rope(void *q, void *k, const int32_t *depth,
+                       const int32_t *prefix_len, int32_t B, int32_t N,
+                       int32_t Hq, int32_t Hkv, int32_t D, double theta,
+                       jf_dtype dtype, void *stream);
+
+/* --------------------------------------------------------------------------
  * jf_tree_accept -- greedy verification: the longest accepted path.
  *
  * The target model checks the whole drafted tree in one parallel pass and

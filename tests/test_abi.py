@@ -21,7 +21,7 @@ def _declared():
 
 def test_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 16
+    assert len(names) == 17
     assert sorted(jf.EXPORTS) == names
     L = jf.lib()
     for n in names:
@@ -177,6 +177,26 @@ def test_accept_argument_errors():
     assert L.jf_tree_accept(*bad) == jf.JF_ERR_INVALID_ARG
     bad = list(ok); bad[9] = FAKE_ODD                      # path misaligned
     assert L.jf_tree_accept(*bad) == jf.JF_ERR_ALIGN
+
+
+def test_rope_argument_errors():
+    L = jf.lib()
+
+    def rope(**kw):
+        a = dict(q=FAKE, k=FAKE, depth=FAKE, pl=FAKE, B=1, N=16, Hq=32, Hkv=8, D=128, theta=0.0,
+                 dtype=jf.JF_BF16)
+        a.update(kw)
+        return L.jf_tree_rope(a["q"], a["k"], a["depth"], a["pl"], a["B"], a["N"], a["Hq"],
+                              a["Hkv"], a["D"], a["theta"], a["dtype"], None)
+
+    assert rope(q=None) == jf.JF_ERR_INVALID_ARG
+    assert rope(pl=None) == jf.JF_ERR_INVALID_ARG
+    assert rope(D=127) == jf.JF_ERR_INVALID_ARG
+    assert rope(D=0) == jf.JF_ERR_INVALID_ARG
+    assert rope(Hkv=0) == jf.JF_ERR_INVALID_ARG
+    assert rope(D=512) == jf.JF_ERR_UNSUPPORTED
+    assert rope(dtype=5) == jf.JF_ERR_INVALID_ARG
+    assert rope(q=FAKE_ODD) == jf.JF_ERR_ALIGN
 
 
 def test_product_path_does_not_import_the_oracle():

@@ -253,6 +253,23 @@ jf_status jf_path_scores(const int32_t *parent, const float *logp, int32_t B, in
     return e == hipSuccess ? JF_OK : JF_ERR_HIP;
 }
 
+jf_status jf_tree_rope(void *q, void *k, const int32_t *depth, const int32_t *prefix_len,
+                       int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D, double theta,
+                       jf_dtype dtype, void *stream) {
+    if (!q || !depth || !prefix_len) return JF_ERR_INVALID_ARG;
+    if (B < 1 || N < 1 || Hq < 1 || (k && Hkv < 1) || D < 2 || D % 2 != 0) return JF_ERR_INVALID_ARG;
+    if (dtype != JF_BF16 && dtype != JF_F32) return JF_ERR_INVALID_ARG;
+    if (D > 256) return JF_ERR_UNSUPPORTED;
+    if ((int64_t)B * N > INT32_MAX) return JF_ERR_UNSUPPORTED;
+    const size_t e = dtype == JF_BF16 ? 2 : 4;
+    if (!aligned(q, e) || (k && !aligned(k, e)) || !aligned(depth, 4) || !aligned(prefix_len, 4))
+        return JF_ERR_ALIGN;
+    if (!(theta > 0.0)) theta = 1e6;
+    hipError_t err = launch_tree_rope(q, k, depth, prefix_len, B, N, Hq, Hkv, D, theta, dtype,
+                                      (hipStream_t)stream);
+    return err == hipSuccess ? JF_OK : JF_ERR_HIP;
+}
+
 jf_status jf_tree_accept(const int32_t *parent, const int32_t *token, const int32_t *target_next,
                          const int32_t *root_next, int32_t B, int32_t N, int32_t *accept_len,
                          int32_t *accept_node, int32_t *next_token, int32_t *path,

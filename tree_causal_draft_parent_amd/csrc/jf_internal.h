@@ -101,6 +101,10 @@ hipError_t launch_tree_accept(const int32_t *parent, const int32_t *token,
                               int32_t *accept_len, int32_t *accept_node, int32_t *next_token,
                               int32_t *path, int32_t *seq_status, hipStream_t s);
 
+hipError_t launch_tree_rope(void *q, void *k, const int32_t *depth, const int32_t *prefix_len,
+                            int B, int N, int Hq, int Hkv, int D, double theta, jf_dtype dtype,
+                            hipStream_t s);
+
 // One expansion step sorts every (node, rank) candidate of a sequence in LDS.
 constexpr int kExpandMaxCands = 16384;
 hipError_t launch_tree_expand(const float *score, const int32_t *depth, const int32_t *idx,

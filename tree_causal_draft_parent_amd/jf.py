@@ -28,7 +28,7 @@ EXPORTS = ("jf_status_string", "jf_abi_version", "jf_tree_mask_build",
            "jf_fuse_proj_cus", "jf_tree_attn_workspace_size",
            "jf_tree_attn_fwd", "jf_tree_attn_workspace_size_cus", "jf_tree_attn_fwd_cus",
            "jf_node_topk_workspace_size", "jf_node_topk", "jf_path_scores", "jf_tree_expand",
-           "jf_tree_accept")
+           "jf_tree_accept", "jf_tree_rope")
 
 _lib = None
 
@@ -85,6 +85,8 @@ def lib():
     L.jf_tree_expand.restype = ctypes.c_int
     L.jf_tree_accept.argtypes = [P, P, P, P, I32, I32, P, P, P, P, P, P]
     L.jf_tree_accept.restype = ctypes.c_int
+    L.jf_tree_rope.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, ctypes.c_double, ctypes.c_int, P]
+    L.jf_tree_rope.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -345,3 +347,25 @@ def jf_tree_accept(parent: torch.Tensor, token: torch.Tensor, target_next: torch
                              _p(alen), _p(anode), _p(ntok), _p(path), _p(st), _stream(stream))
     _check("jf_tree_accept", s)
     return alen, anode, ntok, path, st
+
+
+def jf_tree_rope(q: torch.Tensor, k: Optional[torch.Tensor], depth: torch.Tensor,
+                 prefix_len: torch.Tensor, theta: float = 0.0, stream=None):
+    """Rotate q [B, N, Hq, D] (and k [B, N, Hkv, D]) in place at positions
+    prefix_len[b] + depth[b, i] - 1 (prefix_len: device int32 [B])."""
+    _contig("q", q)
+    if k is not None:
+        _contig("k", k)
+        if k.dtype != q.dtype or k.shape[:2] != q.shape[:2] or k.shape[3] != q.shape[3]:
+            raise ValueError("k must match q in dtype, B, N and D")
+    _contig("depth", depth)
+    _contig("prefix_len", prefix_len)
+    B, N, Hq, D = q.shape
+    Hkv = 0 if k is None else k.shape[2]
+    if depth.shape != (B, N) or depth.dtype != torch.int32 or prefix_len.shape != (B,) \
+            or prefix_len.dtype != torch.int32:
+        raise ValueError("depth [B, N] and prefix_len [B] int32 expected")
+    st = lib().jf_tree_rope(_p(q), _p(k), _p(depth), _p(prefix_len), B, N, Hq, Hkv, D,
+                            float(theta), _dtype_code(q), _stream(stream))
+    _check("jf_tree_rope", st)
+    return q, k
