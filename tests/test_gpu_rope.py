@@ -80,3 +80,20 @@ def test_head_dim_edges_and_theta(D):
 def test_bad_rows_are_unchanged():
     par = np.array([[-1, 2, 1, 0]], np.int32)          # nodes 1 and 2 form a cycle
     _run(par, [10], 2, 1, 64, "f32", 7)
+
+
+def test_unaligned_rows_take_the_scalar_path():
+    # q starting 4 bytes into an allocation: the 16-byte path is not taken
+    B, N, Hq, D = 1, 24, 3, 64
+    par = _trees(B, N, 16, (1, 8), 8)
+    q = _draw((B, N, Hq, D), "f32", 8)
+    buf = torch.zeros(B * N * Hq * D + 1, dtype=torch.float32, device="cuda")
+    qd = buf[1:].view(B, N, Hq, D)
+    qd.copy_(torch.from_numpy(q).cuda())
+    _, dg, _ = jf.jf_tree_mask_build(dev_tensor(par.astype(np.int32)))
+    say("rope: unaligned q")
+    jf.jf_tree_rope(qd, None, dg, dev_tensor(np.array([300], np.int32)))
+    torch.cuda.synchronize()
+    _, depth, _, _ = oracle.tree_mask(par)
+    ref = oracle.tree_rope(q.astype(np.float64), depth, [300])
+    assert np.max(np.abs(host_f64(qd) - ref)) <= 1e-5

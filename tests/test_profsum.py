@@ -44,3 +44,19 @@ def test_traffic_scaling(tmp_path):
     assert k["write_bytes"] == round(10.0 * 1024 * 0.5)
     assert rec["sources_sha256"] == profsum.sources_hash()
     assert os.path.exists(out)
+
+
+def test_trace_split_by_grid(tmp_path, capsys):
+    d = tmp_path / "trace"
+    d.mkdir()
+    hdr = '"Kind","Kernel_Name","Start_Timestamp","End_Timestamp","Grid_Size_X"\n'
+    rows = ['"KERNEL_DISPATCH","void jf::(anonymous namespace)::k_fuse_gemm_bf16<256>(jf::FuseArgs)",100,2100,131072\n',
+            '"KERNEL_DISPATCH","void jf::(anonymous namespace)::k_fuse_gemm_bf16<256>(jf::FuseArgs)",5000,9000,131072\n',
+            '"KERNEL_DISPATCH","void jf::(anonymous namespace)::k_fuse_gemm_bf16<256>(jf::FuseArgs)",10000,410000,607744\n']
+    (d / "run_kernel_trace.csv").write_text(hdr + "".join(rows))
+    per = profsum.read_trace_by_grid(str(d))
+    assert per[("k_fuse_gemm_bf16<256>", 131072)] == [2.0, 4.0]
+    assert per[("k_fuse_gemm_bf16<256>", 607744)] == [400.0]
+    profsum.main(["stats", str(d), "--by-grid"])
+    out = capsys.readouterr().out
+    assert "607744" in out and "131072" in out

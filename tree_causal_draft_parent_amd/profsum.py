@@ -1,7 +1,8 @@
 """Summaries of rocprofv3 CSV output for the draft-step kernels (host only).
 
-    python -m tree_causal_draft_parent_amd.profsum stats DIR
+    python -m tree_causal_draft_parent_amd.profsum stats DIR [--by-grid]
         per-kernel calls / average / total duration from *_kernel_stats.csv
+        (--by-grid: per kernel and grid size, from *_kernel_trace.csv)
     python -m tree_causal_draft_parent_amd.profsum traffic --fetch DIR --write DIR \
             --copy-fetch DIR --copy-write DIR --copy-bytes N --out JSON
         per-launch FETCH_SIZE / WRITE_SIZE of every libjf kernel, scaled by the
@@ -91,7 +92,24 @@ def read_counter(dirname: str, counter: str):
     return {k: list(v.values()) for k, v in per.items()}
 
 
+def read_trace_by_grid(dirname: str):
+    """(kernel short name, grid size) -> per-dispatch durations in us, from
+    *_kernel_trace.csv: one kernel launched at two shapes shows as two rows."""
+    per = defaultdict(list)
+    with open(_one(dirname, "_kernel_trace.csv")) as f:
+        for r in csv.DictReader(f):
+            key = (short_name(r["Kernel_Name"]), int(r["Grid_Size_X"]))
+            per[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    return per
+
+
 def cmd_stats(a):
+    if a.by_grid:
+        per = read_trace_by_grid(a.dir)
+        print(f"{'kernel':44s} {'grid':>8s} {'calls':>6s} {'avg us':>9s} {'min us':>9s} {'max us':>9s}")
+        for (name, grid), v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+            print(f"{name[:44]:44s} {grid:8d} {len(v):6d} {_mean(v):9.2f} {min(v):9.2f} {max(v):9.2f}")
+        return
     rows = read_stats(a.dir)
     print(f"{'kernel':44s} {'calls':>6s} {'avg us':>9s} {'min us':>9s} {'max us':>9s} {'total %':>8s}")
     for r in rows:
@@ -140,6 +158,8 @@ def main(argv=None):
     sub = ap.add_subparsers(dest="cmd", required=True)
     s = sub.add_parser("stats")
     s.add_argument("dir")
+    s.add_argument("--by-grid", action="store_true",
+                   help="per (kernel, grid size) from the kernel trace instead of the stats file")
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
