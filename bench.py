@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--fuse-cus", type=int, default=-1,
                     help="compute units the projection's K split is planned for in the two-stream "
                          "step (-1: three quarters of the device's; 0: all)")
+    ap.add_argument("--topk-split", type=float, default=0.0,
+                    help="fraction of the top-k rows run on the attention's stream in the two-stream "
+                         "step (after the attention; the rest follow the projection on the other)")
     ap.add_argument("--one-stream", action="store_true",
                     help="headline from the graph of the step on one stream (default: two streams)")
     ap.add_argument("--cpu-sample-nodes", type=int, default=256)
@@ -487,10 +490,14 @@ def main():
     # splits): the units it leaves go to the projection and the top-k, and it
     # writes fewer partial results.  When it is the longer one it keeps them all.
     n_cus = torch.cuda.get_device_properties(0).multi_processor_count
+    # top-k rows [0, r_split) follow the projection, [r_split, R) the attention
+    r_split = R - int(round(R * min(max(args.topk_split, 0.0), 1.0)))
     if args.attn_cus >= 0:
         attn_cus = args.attn_cus
     else:
-        shorter = per_call["mask"] + per_call["attn"] < per_call["fuse"] + per_call["topk"]
+        f_b = (R - r_split) / R
+        shorter = (per_call["mask"] + per_call["attn"] + f_b * per_call["topk"]
+                   < per_call["fuse"] + (1 - f_b) * per_call["topk"])
         attn_cus = (3 * n_cus) // 4 if shorter else 0
     aws_side = jf.jf_tree_attn_workspace_size(B, N, wl.Hq, wl.Hkv, wl.D, a["page_size"], prefix_len,
                                               jf.JF_BF16 if dt == "bf16" else jf.JF_F32, attn_cus)
@@ -502,16 +509,24 @@ def main():
                                               jf.JF_BF16 if dt == "bf16" else jf.JF_F32, fuse_cus)
     fuse_ws_side = torch.empty(max(fws_side, 1), dtype=torch.uint8, device="cuda")
 
+    topk_ws_b = torch.empty(max(jf.jf_node_topk_workspace_size(max(R - r_split, 1), wl.V, wl.topk), 1),
+                            dtype=torch.uint8, device="cuda")
+
     def step_streams():
         main = torch.cuda.current_stream()
         s_side.wait_stream(main)
         with torch.cuda.stream(s_side):
             jf.jf_fuse_proj(xs, w, y=y, workspace=fuse_ws_side, cus=fuse_cus)
-            jf.jf_node_topk(logits, wl.topk, idx=idx, val=val, lse=rlse, workspace=topk_ws)
+            if r_split > 0:
+                jf.jf_node_topk(logits[:r_split], wl.topk, idx=idx[:r_split], val=val[:r_split],
+                                lse=rlse[:r_split], workspace=topk_ws)
         jf.jf_tree_mask_build(parent, mask, depth, seq_status)
         jf.jf_tree_attn_fwd(dev["q"], dev["k_tree"], dev["v_tree"], mask, dev["k_cache"],
                             dev["v_cache"], block_table, prefix_len, out=out, lse=lse,
                             workspace=attn_ws_side, page_status=page_status, cus=attn_cus)
+        if r_split < R:
+            jf.jf_node_topk(logits[r_split:], wl.topk, idx=idx[r_split:], val=val[r_split:],
+                            lse=rlse[r_split:], workspace=topk_ws_b)
         main.wait_stream(s_side)
 
     def time_graph(fn):
@@ -669,6 +684,7 @@ def main():
         "graph_one_stream_ms_per_step": None if serial_graph_ms is None else round(serial_graph_ms, 5),
         "attn_cus_two_streams": attn_cus,
         "fuse_cus_two_streams": fuse_cus,
+        "topk_rows_on_attention_stream": R - r_split,
         "eager_ms_per_step": round(eager_ms_per_step, 5),
         "gpu_step_ms": round(gpu_step_ms, 5),
         "cold_step_ms": round(med(cold), 5),
