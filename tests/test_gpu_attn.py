@@ -160,3 +160,20 @@ def test_score_jump_past_reference_maximum():
             kc[0, p, g] = 4.0 * q[0, node, g * G]
     inp["k_cache"] = synth.f32_to_bf16_bits(kc)
     compare(inp, label="score jump")
+
+
+def test_maximum_tree_size():
+    # N = 1024 nodes, the call's limit: 16 tree blocks, 1024 * 4 query rows
+    inp = synth.make_attn_inputs(B=1, N=1024, Hq=8, Hkv=2, D=128, dtype="bf16", prefix_lens=[512],
+                                 seed=1024)
+    rows = np.sort(np.random.default_rng(5).choice(1024 * 8, 1024, replace=False))
+    compare(inp, rows=rows, label="N=1024")
+
+
+def test_maximum_batch():
+    # B = 256 sequences, the call's limit, ragged prefixes including empty ones
+    pl = list(np.random.default_rng(256).integers(0, 200, size=256))
+    pl[0] = 0
+    inp = synth.make_attn_inputs(B=256, N=8, Hq=4, Hkv=1, D=128, dtype="bf16", prefix_lens=pl,
+                                 page_size=16, shuffled_pages=True, seed=256)
+    compare(inp, label="B=256")

@@ -97,3 +97,18 @@ def test_one_block_per_row_path(dtype, R, V, k):
 def test_one_block_per_row_ties(dtype):
     bits = synth.tie_forcing_logits(synth.make_logits(R=128, V=20000, dtype=dtype, seed=9), dtype)
     _check(bits, dtype, 8)
+
+
+@pytest.mark.parametrize("dtype,V", [("bf16", 64 * 9728), ("f32", 64 * 4864)])
+def test_largest_vocabulary_at_k64(dtype, V):
+    # the call's limit ceil(V / S) * k <= 4096 with S = 9728 (bf16) / 4864
+    # (fp32), reached exactly at k = 64; both merge paths (3 rows: per-slice
+    # waves and a second pass)
+    bits = synth.make_logits(R=3, V=V, dtype=dtype, seed=V)
+    _check(bits, dtype, 64)
+
+
+def test_beyond_largest_vocabulary_is_refused():
+    t = torch.zeros((1, 64 * 9728 + 1), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(jf.JfError):
+        jf.jf_node_topk(t, 64)
