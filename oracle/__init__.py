@@ -22,6 +22,9 @@ Parity status of each function (what pins it, see tests/test_oracle_*.py):
                 star == inputs, recursion on random forests, relabelling.
   tree_expand -- pinned: hand-derived golden step, numpy lexsort brute force
                 over float32 scores, depth cap, budget, ties, signed zeros.
+  rmsnorm    -- pinned: hand-derived golden rows, constant rows, unit RMS of
+                the output at eps = 0, scale invariance, the weight as a
+                per-column factor.
   tree_rope  -- pinned: hand-derived golden rotation (D = 4), position 0 is
                 the identity, pair norms kept, rotations compose by adding
                 positions, scores depend only on the position difference,
@@ -84,6 +87,8 @@ def _load():
     lib.oracle_tree_accept.restype = ctypes.c_int
     lib.oracle_tree_rope.argtypes = [P, P, P, I64, I64, I64, I64, ctypes.c_double]
     lib.oracle_tree_rope.restype = None
+    lib.oracle_rmsnorm.argtypes = [P, I64, I64, I64, P, ctypes.c_double, P]
+    lib.oracle_rmsnorm.restype = None
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
@@ -236,6 +241,17 @@ def tree_accept(parent: np.ndarray, token: np.ndarray, target_next: np.ndarray,
     if st != 0:
         raise ValueError(f"oracle_tree_accept: status {st}")
     return alen, anode, ntok, path, bad
+
+
+def rmsnorm(x: np.ndarray, w=None, eps: float = 1e-6) -> np.ndarray:
+    """Rows of x [rows, H] (float64) divided by their root mean square
+    (+ eps inside the root), times w [H] when given."""
+    x = _c(x, np.float64)
+    rows, H = x.shape
+    wv = None if w is None else _c(w, np.float64)
+    y = np.empty((rows, H), dtype=np.float64)
+    _load().oracle_rmsnorm(_p(x), rows, H, H, _p(wv), float(eps), _p(y))
+    return y
 
 
 def tree_rope(x: np.ndarray, depth: np.ndarray, prefix_len, theta: float = 1e6) -> np.ndarray:

@@ -383,6 +383,27 @@ int oracle_tree_expand(const float *score, const int32_t *depth, const int32_t *
 }
 
 /* ---------------------------------------------------------------------------
+ * Root-mean-square normalisation of rows.
+ *
+ * The Qwen3 models the pages draft for (abstract) normalise hidden states,
+ * and per head their queries and keys, by the root mean square:
+ *     y[r][c] = x[r][c] / sqrt(mean_c(x[r][c]^2) + eps) * w[c]
+ * (w = 1 when absent).  x and y [rows, H] (x rows ld apart).
+ * ------------------------------------------------------------------------- */
+void oracle_rmsnorm(const double *x, int64_t rows, int64_t H, int64_t ld, const double *w,
+                    double eps, double *y)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        const double *xr = x + r * ld;
+        double ss = 0.0;
+        for (int64_t c = 0; c < H; ++c) ss += xr[c] * xr[c];
+        const double inv = 1.0 / sqrt(ss / (double)H + eps);
+        for (int64_t c = 0; c < H; ++c) y[r * H + c] = xr[c] * inv * (w ? w[c] : 1.0);
+    }
+}
+
+/* ---------------------------------------------------------------------------
  * Rotary position embedding of the tree nodes' queries and keys.
  *
  * The pages draft with Qwen3 target models (abstract), which rotate queries
