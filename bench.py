@@ -325,6 +325,55 @@ def lm_head(wl, steps, torch, jf):
     return res
 
 
+def graph_time(fn, steps, torch, rep=20):
+    """Mean time of fn over replays of a HIP graph of `rep` back-to-back calls."""
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(rep):
+            fn()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(max(5, steps // rep)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1) / rep)
+    return float(np.mean(ms))
+
+
+def norm_timing(wl, q, k_tree, steps, torch, jf):
+    """jf_rmsnorm over the layer input (B*N rows x H) and per head over the
+    step's queries and tree keys (copies), each timed as a graph of 20 calls."""
+    B, N = wl.B, wl.N
+    g = torch.Generator(device="cuda").manual_seed(41)
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    hid = torch.randn((B * N, wl.H), generator=g, device="cuda").to(tdt)
+    wh = torch.randn((wl.H,), generator=g, device="cuda").to(tdt)
+    hy = torch.empty_like(hid)
+    qc, kc = q.clone().view(-1, wl.D), k_tree.clone().view(-1, wl.D)
+    wd = torch.randn((wl.D,), generator=g, device="cuda").to(tdt)
+    t_h = graph_time(lambda: jf.jf_rmsnorm(hid, wh, y=hy), steps, torch)
+
+    def heads():
+        jf.jf_rmsnorm(qc, wd, y=qc)
+        jf.jf_rmsnorm(kc, wd, y=kc)
+
+    t_q = graph_time(heads, steps, torch)
+    e = hid.element_size()
+    return {"hidden": {"rows": B * N, "H": wl.H, "ms": round(t_h, 5),
+                       "GBps": round(2 * hid.numel() * e / (t_h * 1e-3) / 1e9, 1)},
+            "qk_heads": {"rows": qc.shape[0] + kc.shape[0], "H": wl.D, "ms": round(t_q, 5),
+                         "GBps": round(2 * (qc.numel() + kc.numel()) * e / (t_q * 1e-3) / 1e9, 1),
+                         "launches": 2},
+            "bound": "latency", "timing": "graph of 20 back-to-back calls"}
+
+
 def rope_timing(wl, q, k_tree, depth, prefix_len, steps, torch, jf):
     """jf_tree_rope over the step's queries and tree keys (copies), at the
     tree positions; latency-bound, timed as a HIP graph of 20 calls."""
@@ -598,6 +647,7 @@ def main():
         head = lm_head(wl, K, torch, jf)
         if head is not None:
             head["rope"] = rope
+            head["rmsnorm"] = norm_timing(wl, dev["q"], dev["k_tree"], K, torch, jf)
         if head is not None:
             print(f"[bench] LM head {head['M']}x{head['K']}->{head['N']}: {head['ms']:.4f} ms, "
                   f"{head['hbm_GBps']:.0f} GB/s", file=sys.stderr, flush=True)

@@ -276,6 +276,25 @@ jf_status jf_tree_expand(const float *score, const int32_t *depth,
                          int32_t *new_depth, void *stream);
 
 /* --------------------------------------------------------------------------
+ * jf_rmsnorm -- root-mean-square normalisation of rows.
+ *
+ * The Qwen3 models the pages draft for (abstract) normalise a layer's hidden
+ * state, and per head its queries and keys, by the root mean square:
+ *     y[r][c] = x[r][c] / sqrt(mean_c(x[r][c]^2) + eps) * w[c].
+ * The sum of squares is accumulated in fp64, the inverse root rounded once
+ * to fp32, the products formed in fp32 (bf16 storage rounds to nearest even).
+ *
+ *   x    [rows, H] dtype, row stride ldx elements (ldx >= H).
+ *   w    [H] dtype or NULL (no weight).
+ *   eps  >= 0, added to the mean square inside the root.
+ *   y    [rows, H] dtype, dense; may be x itself when ldx == H (in place).
+ *   Per-head normalisation of q [B, N, Hq, D] is rows = B*N*Hq, H = D.
+ * ------------------------------------------------------------------------ */
+jf_status jf_rmsnorm(const void *x, int64_t rows, int64_t H, int64_t ldx,
+                     const void *w, float eps, jf_dtype dtype, void *y,
+                     void *stream);
+
+/* --------------------------------------------------------------------------
  * jf_tree_rope -- rotary position embedding of the tree nodes, in place.
  *
  * The pages draft for Qwen3 target models (abstract), which rotate queries

@@ -21,7 +21,7 @@ def _declared():
 
 def test_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 17
+    assert len(names) == 18
     assert sorted(jf.EXPORTS) == names
     L = jf.lib()
     for n in names:
@@ -197,6 +197,17 @@ def test_rope_argument_errors():
     assert rope(D=512) == jf.JF_ERR_UNSUPPORTED
     assert rope(dtype=5) == jf.JF_ERR_INVALID_ARG
     assert rope(q=FAKE_ODD) == jf.JF_ERR_ALIGN
+
+
+def test_rmsnorm_argument_errors():
+    L = jf.lib()
+    assert L.jf_rmsnorm(None, 4, 64, 64, None, 1e-6, 1, FAKE, None) == jf.JF_ERR_INVALID_ARG
+    assert L.jf_rmsnorm(FAKE, 0, 64, 64, None, 1e-6, 1, FAKE, None) == jf.JF_ERR_INVALID_ARG
+    assert L.jf_rmsnorm(FAKE, 4, 64, 63, None, 1e-6, 1, FAKE, None) == jf.JF_ERR_INVALID_ARG
+    assert L.jf_rmsnorm(FAKE, 4, 64, 64, None, -1.0, 1, FAKE, None) == jf.JF_ERR_INVALID_ARG
+    assert L.jf_rmsnorm(FAKE, 4, 64, 80, None, 1e-6, 1, FAKE, None) == jf.JF_ERR_INVALID_ARG  # in place, strided
+    assert L.jf_rmsnorm(FAKE_ODD, 4, 64, 64, None, 1e-6, 1, FAKE, None) == jf.JF_ERR_ALIGN
+    assert L.jf_rmsnorm(FAKE, 4, 64, 64, None, 1e-6, 9, FAKE, None) == jf.JF_ERR_INVALID_ARG
 
 
 def test_product_path_does_not_import_the_oracle():

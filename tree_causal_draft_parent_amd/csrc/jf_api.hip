@@ -253,6 +253,19 @@ jf_status jf_path_scores(const int32_t *parent, const float *logp, int32_t B, in
     return e == hipSuccess ? JF_OK : JF_ERR_HIP;
 }
 
+jf_status jf_rmsnorm(const void *x, int64_t rows, int64_t H, int64_t ldx, const void *w, float eps,
+                     jf_dtype dtype, void *y, void *stream) {
+    if (!x || !y) return JF_ERR_INVALID_ARG;
+    if (rows < 1 || H < 1 || ldx < H || !(eps >= 0.f)) return JF_ERR_INVALID_ARG;
+    if (dtype != JF_BF16 && dtype != JF_F32) return JF_ERR_INVALID_ARG;
+    if (H > INT32_MAX || rows > ((int64_t)INT32_MAX) * 4) return JF_ERR_UNSUPPORTED;
+    if (x == y && ldx != H) return JF_ERR_INVALID_ARG;     // in place needs dense rows
+    const size_t e = dtype == JF_BF16 ? 2 : 4;
+    if (!aligned(x, e) || !aligned(y, e) || (w && !aligned(w, e))) return JF_ERR_ALIGN;
+    hipError_t err = launch_rmsnorm(x, rows, (int)H, ldx, w, eps, dtype, y, (hipStream_t)stream);
+    return err == hipSuccess ? JF_OK : JF_ERR_HIP;
+}
+
 jf_status jf_tree_rope(void *q, void *k, const int32_t *depth, const int32_t *prefix_len,
                        int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D, double theta,
                        jf_dtype dtype, void *stream) {

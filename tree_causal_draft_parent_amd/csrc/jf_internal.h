@@ -105,6 +105,9 @@ hipError_t launch_tree_rope(void *q, void *k, const int32_t *depth, const int32_
                             int B, int N, int Hq, int Hkv, int D, double theta, jf_dtype dtype,
                             hipStream_t s);
 
+hipError_t launch_rmsnorm(const void *x, int64_t rows, int H, int64_t ldx, const void *w, float eps,
+                          jf_dtype dtype, void *y, hipStream_t s);
+
 // One expansion step sorts every (node, rank) candidate of a sequence in LDS.
 constexpr int kExpandMaxCands = 16384;
 hipError_t launch_tree_expand(const float *score, const int32_t *depth, const int32_t *idx,

@@ -28,7 +28,7 @@ EXPORTS = ("jf_status_string", "jf_abi_version", "jf_tree_mask_build",
            "jf_fuse_proj_cus", "jf_tree_attn_workspace_size",
            "jf_tree_attn_fwd", "jf_tree_attn_workspace_size_cus", "jf_tree_attn_fwd_cus",
            "jf_node_topk_workspace_size", "jf_node_topk", "jf_path_scores", "jf_tree_expand",
-           "jf_tree_accept", "jf_tree_rope")
+           "jf_tree_accept", "jf_tree_rope", "jf_rmsnorm")
 
 _lib = None
 
@@ -87,6 +87,8 @@ def lib():
     L.jf_tree_accept.restype = ctypes.c_int
     L.jf_tree_rope.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, ctypes.c_double, ctypes.c_int, P]
     L.jf_tree_rope.restype = ctypes.c_int
+    L.jf_rmsnorm.argtypes = [P, I64, I64, I64, P, ctypes.c_float, ctypes.c_int, P, P]
+    L.jf_rmsnorm.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -369,3 +371,24 @@ def jf_tree_rope(q: torch.Tensor, k: Optional[torch.Tensor], depth: torch.Tensor
                             float(theta), _dtype_code(q), _stream(stream))
     _check("jf_tree_rope", st)
     return q, k
+
+
+def jf_rmsnorm(x: torch.Tensor, w: Optional[torch.Tensor] = None, eps: float = 1e-6,
+               y: Optional[torch.Tensor] = None, stream=None):
+    """Rows of x (2-D, unit column stride; any leading row stride) divided by
+    their root mean square, times w [H] when given -> y [rows, H] (y may be x
+    when x is dense: in place)."""
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with contiguous rows")
+    rows, H = x.shape
+    if w is not None:
+        _contig("w", w)
+        if w.shape != (H,) or w.dtype != x.dtype:
+            raise ValueError("w must be [H] of x's dtype")
+    if y is None:
+        y = torch.empty((rows, H), dtype=x.dtype, device=x.device)
+    _contig("y", y)
+    st = lib().jf_rmsnorm(_p(x), rows, H, x.stride(0), _p(w), float(eps), _dtype_code(x), _p(y),
+                          _stream(stream))
+    _check("jf_rmsnorm", st)
+    return y
