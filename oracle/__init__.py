@@ -22,6 +22,9 @@ Parity status of each function (what pins it, see tests/test_oracle_*.py):
                 star == inputs, recursion on random forests, relabelling.
   tree_expand -- pinned: hand-derived golden step, numpy lexsort brute force
                 over float32 scores, depth cap, budget, ties, signed zeros.
+  swiglu     -- pinned: hand-derived golden values, silu(0) = 0, the odd
+                part silu(g) - silu(-g) = g, the large-|g| limits, the
+                logistic curve written as a tanh.
   rmsnorm    -- pinned: hand-derived golden rows, constant rows, unit RMS of
                 the output at eps = 0, scale invariance, the weight as a
                 per-column factor.
@@ -89,6 +92,8 @@ def _load():
     lib.oracle_tree_rope.restype = None
     lib.oracle_rmsnorm.argtypes = [P, I64, I64, I64, P, ctypes.c_double, P]
     lib.oracle_rmsnorm.restype = None
+    lib.oracle_swiglu.argtypes = [P, I64, I64, P]
+    lib.oracle_swiglu.restype = None
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
@@ -241,6 +246,16 @@ def tree_accept(parent: np.ndarray, token: np.ndarray, target_next: np.ndarray,
     if st != 0:
         raise ValueError(f"oracle_tree_accept: status {st}")
     return alen, anode, ntok, path, bad
+
+
+def swiglu(gu: np.ndarray) -> np.ndarray:
+    """silu(gate) * up from gu [M, 2I] (gate columns first) -> [M, I] float64."""
+    gu = _c(gu, np.float64)
+    M, I2 = gu.shape
+    assert I2 % 2 == 0
+    y = np.empty((M, I2 // 2), dtype=np.float64)
+    _load().oracle_swiglu(_p(gu), M, I2 // 2, _p(y))
+    return y
 
 
 def rmsnorm(x: np.ndarray, w=None, eps: float = 1e-6) -> np.ndarray:

@@ -383,6 +383,24 @@ int oracle_tree_expand(const float *score, const int32_t *depth, const int32_t *
 }
 
 /* ---------------------------------------------------------------------------
+ * Gated MLP activation.
+ *
+ * The Qwen3 models the pages draft for (abstract) gate their MLP with SiLU:
+ *     y[m][c] = silu(gu[m][c]) * gu[m][I + c],  silu(g) = g / (1 + exp(-g)),
+ * where gu [M, 2I] holds the gate projection in its first I columns and the
+ * up projection in its last I (one projection with the two weights stacked).
+ * ------------------------------------------------------------------------- */
+void oracle_swiglu(const double *gu, int64_t M, int64_t I, double *y)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t c = 0; c < I; ++c) {
+            const double g = gu[m * 2 * I + c], u = gu[m * 2 * I + I + c];
+            y[m * I + c] = g / (1.0 + exp(-g)) * u;
+        }
+}
+
+/* ---------------------------------------------------------------------------
  * Root-mean-square normalisation of rows.
  *
  * The Qwen3 models the pages draft for (abstract) normalise hidden states,

@@ -45,3 +45,31 @@ def test_rmsnorm_weight_scales_columns():
     x = np.random.default_rng(2).standard_normal((5, 64))
     w = np.random.default_rng(3).standard_normal(64)
     assert np.max(np.abs(oracle.rmsnorm(x, w=w) - oracle.rmsnorm(x) * w)) < 1e-14
+
+
+# ---------------------------------------------------------------------------
+# Gated MLP activation
+
+def test_swiglu_golden():
+    g = _read("swiglu_small.txt")
+    y = oracle.swiglu(np.array([g["gu"]]))
+    assert np.max(np.abs(y[0] - np.array(g["y"]))) < 1e-11
+
+
+def test_swiglu_odd_part_and_limits():
+    rng = np.random.default_rng(4)
+    g = rng.standard_normal((6, 50)) * 3
+    ones = np.ones_like(g)
+    sp = oracle.swiglu(np.concatenate([g, ones], axis=1))
+    sm = oracle.swiglu(np.concatenate([-g, ones], axis=1))
+    assert np.max(np.abs(sp - sm - g)) < 1e-13                # silu(g) - silu(-g) = g
+    big = oracle.swiglu(np.array([[40.0, -40.0, 0.0, 3.0, 5.0, 9.0]]))
+    assert abs(big[0, 0] - 120.0) < 1e-12 and abs(big[0, 1]) < 1e-14 and big[0, 2] == 0.0
+
+
+def test_swiglu_matches_tanh_form():
+    # logistic(g) = (1 + tanh(g / 2)) / 2, an independent formulation
+    rng = np.random.default_rng(5)
+    g, u = rng.standard_normal((4, 30)) * 4, rng.standard_normal((4, 30))
+    ref = g * (1.0 + np.tanh(g / 2.0)) / 2.0 * u
+    assert np.max(np.abs(oracle.swiglu(np.concatenate([g, u], axis=1)) - ref)) < 1e-13
