@@ -374,6 +374,37 @@ def norm_timing(wl, q, k_tree, steps, torch, jf):
             "bound": "latency", "timing": "graph of 20 back-to-back calls"}
 
 
+def mlp_timing(wl, steps, torch, jf, inter=12288):
+    """The draft layer's gated MLP over B*N rows: one projection to the gate
+    and up columns (weights stacked, [2I, H]), jf_swiglu, and the down
+    projection ([H, I]); device-drawn random bf16 weights (timing only)."""
+    if wl.dtype != "bf16":
+        return None
+    M, H = wl.B * wl.N, wl.H
+    g = torch.Generator(device="cuda").manual_seed(43)
+    x = torch.randn((M, H), generator=g, device="cuda").to(torch.bfloat16)
+    w_gu = (torch.randn((2 * inter, H), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    w_dn = (torch.randn((H, inter), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    gu = torch.empty((M, 2 * inter), dtype=torch.bfloat16, device="cuda")
+    act = torch.empty((M, inter), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+    ws1 = torch.empty(max(jf.jf_fuse_proj_workspace_size(M, H, 1, 2 * inter, jf.JF_BF16), 1),
+                      dtype=torch.uint8, device="cuda")
+    ws2 = torch.empty(max(jf.jf_fuse_proj_workspace_size(M, inter, 1, H, jf.JF_BF16), 1),
+                      dtype=torch.uint8, device="cuda")
+    t_gu = graph_time(lambda: jf.jf_fuse_proj([x], w_gu, y=gu, workspace=ws1), steps, torch, rep=5)
+    t_act = graph_time(lambda: jf.jf_swiglu(gu, y=act), steps, torch)
+    t_dn = graph_time(lambda: jf.jf_fuse_proj([act], w_dn, y=out, workspace=ws2), steps, torch, rep=5)
+    wbytes = (w_gu.numel() + w_dn.numel()) * 2
+    total = t_gu + t_act + t_dn
+    res = {"rows": M, "hidden": H, "intermediate": inter, "gate_up_ms": round(t_gu, 5),
+           "swiglu_ms": round(t_act, 5), "down_ms": round(t_dn, 5), "ms": round(total, 5),
+           "weight_bytes": wbytes, "weight_GBps": round(wbytes / (total * 1e-3) / 1e9, 1),
+           "swiglu_GBps": round(3 * M * inter * 2 / (t_act * 1e-3) / 1e9, 1)}
+    del w_gu, w_dn, gu, act
+    return res
+
+
 def rope_timing(wl, q, k_tree, depth, prefix_len, steps, torch, jf):
     """jf_tree_rope over the step's queries and tree keys (copies), at the
     tree positions; latency-bound, timed as a HIP graph of 20 calls."""
@@ -648,6 +679,7 @@ def main():
         if head is not None:
             head["rope"] = rope
             head["rmsnorm"] = norm_timing(wl, dev["q"], dev["k_tree"], K, torch, jf)
+            head["mlp"] = mlp_timing(wl, K, torch, jf)
         if head is not None:
             print(f"[bench] LM head {head['M']}x{head['K']}->{head['N']}: {head['ms']:.4f} ms, "
                   f"{head['hbm_GBps']:.0f} GB/s", file=sys.stderr, flush=True)

@@ -276,6 +276,21 @@ jf_status jf_tree_expand(const float *score, const int32_t *depth,
                          int32_t *new_depth, void *stream);
 
 /* --------------------------------------------------------------------------
+ * jf_swiglu -- gated MLP activation.
+ *
+ * The Qwen3 models the pages draft for (abstract) gate their MLP with SiLU:
+ *     y[m][c] = silu(gu[m][c]) * gu[m][I + c],  silu(g) = g / (1 + exp(-g)),
+ * the gate projection in the first I columns of gu, the up projection in
+ * the last I (e.g. one jf_fuse_proj call with the two weights stacked).
+ * fp32 arithmetic; bf16 storage rounds to nearest even.
+ *
+ *   gu  [M, 2I] dtype with row stride ld elements (ld >= 2I).
+ *   y   [M, I] dtype, dense; must not overlap gu.
+ * ------------------------------------------------------------------------ */
+jf_status jf_swiglu(const void *gu, int64_t M, int64_t I, int64_t ld,
+                    jf_dtype dtype, void *y, void *stream);
+
+/* --------------------------------------------------------------------------
  * jf_rmsnorm -- root-mean-square normalisation of rows.
  *
  * The Qwen3 models the pages draft for (abstract) normalise a layer's hidden

@@ -21,7 +21,7 @@ def _declared():
 
 def test_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 18
+    assert len(names) == 19
     assert sorted(jf.EXPORTS) == names
     L = jf.lib()
     for n in names:
@@ -208,6 +208,15 @@ def test_rmsnorm_argument_errors():
     assert L.jf_rmsnorm(FAKE, 4, 64, 80, None, 1e-6, 1, FAKE, None) == jf.JF_ERR_INVALID_ARG  # in place, strided
     assert L.jf_rmsnorm(FAKE_ODD, 4, 64, 64, None, 1e-6, 1, FAKE, None) == jf.JF_ERR_ALIGN
     assert L.jf_rmsnorm(FAKE, 4, 64, 64, None, 1e-6, 9, FAKE, None) == jf.JF_ERR_INVALID_ARG
+
+
+def test_swiglu_argument_errors():
+    L = jf.lib()
+    assert L.jf_swiglu(None, 4, 64, 128, 1, FAKE, None) == jf.JF_ERR_INVALID_ARG
+    assert L.jf_swiglu(FAKE, 0, 64, 128, 1, FAKE, None) == jf.JF_ERR_INVALID_ARG
+    assert L.jf_swiglu(FAKE, 4, 64, 127, 1, FAKE, None) == jf.JF_ERR_INVALID_ARG
+    assert L.jf_swiglu(FAKE, 4, 64, 128, 7, FAKE, None) == jf.JF_ERR_INVALID_ARG
+    assert L.jf_swiglu(FAKE_ODD, 4, 64, 128, 1, FAKE, None) == jf.JF_ERR_ALIGN
 
 
 def test_product_path_does_not_import_the_oracle():

@@ -59,3 +59,35 @@ def test_zero_rows_with_eps():
     y = jf.jf_rmsnorm(dev_tensor(x, "f32"), eps=1e-6)
     torch.cuda.synchronize()
     assert np.array_equal(y.cpu().numpy(), x)
+
+
+# ---------------------------------------------------------------------------
+# Gated MLP activation
+
+@pytest.mark.parametrize("dtype,M,I,ld", [("f32", 33, 100, None), ("f32", 5, 37, None),
+                                          ("bf16", 256, 12288, None), ("bf16", 9, 64, 136),
+                                          ("bf16", 3, 30, None)])
+def test_swiglu(dtype, M, I, ld):
+    say(f"swiglu: M={M} I={I} ld={ld} {dtype}")
+    gu = _draw((M, 2 * I), dtype, M * I, std=3.0)
+    if ld is not None:
+        pad = np.zeros((M, ld), dtype=gu.dtype)
+        pad[:, :2 * I] = gu
+        t = dev_tensor(pad, dtype)[:, :2 * I]
+    else:
+        t = dev_tensor(gu, dtype)
+    y = jf.jf_swiglu(t)
+    torch.cuda.synchronize()
+    _check(host_f64(y), oracle.swiglu(synth.to_f64(gu, dtype)), dtype)
+
+
+def test_swiglu_extremes():
+    g = np.array([[100.0, -100.0, 0.0, -0.0, 1e-30, 88.0, -88.0, 20.0]], np.float32)
+    u = np.array([[1.0, 1.0, 5.0, 5.0, 1.0, 0.5, 2.0, -1.0]], np.float32)
+    gu = np.concatenate([g, u], axis=1)
+    y = jf.jf_swiglu(dev_tensor(gu, "f32"))
+    torch.cuda.synchronize()
+    got = y.cpu().numpy().astype(np.float64)
+    ref = oracle.swiglu(gu.astype(np.float64))
+    assert np.all(np.isfinite(got))
+    assert np.max(np.abs(got - ref)) <= 1e-5

@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libjf.so")
-SOURCES = ["jf_api.hip", "k_mask.hip", "k_topk.hip", "k_attn.hip", "k_fuse.hip", "k_tree.hip", "k_rope.hip", "k_norm.hip"]
+SOURCES = ["jf_api.hip", "k_mask.hip", "k_topk.hip", "k_attn.hip", "k_fuse.hip", "k_tree.hip", "k_rope.hip", "k_norm.hip", "k_mlp.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

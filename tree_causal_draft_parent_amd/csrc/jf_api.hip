@@ -253,6 +253,17 @@ jf_status jf_path_scores(const int32_t *parent, const float *logp, int32_t B, in
     return e == hipSuccess ? JF_OK : JF_ERR_HIP;
 }
 
+jf_status jf_swiglu(const void *gu, int64_t M, int64_t I, int64_t ld, jf_dtype dtype, void *y,
+                    void *stream) {
+    if (!gu || !y) return JF_ERR_INVALID_ARG;
+    if (M < 1 || I < 1 || ld < 2 * I) return JF_ERR_INVALID_ARG;
+    if (dtype != JF_BF16 && dtype != JF_F32) return JF_ERR_INVALID_ARG;
+    const size_t e = dtype == JF_BF16 ? 2 : 4;
+    if (!aligned(gu, e) || !aligned(y, e)) return JF_ERR_ALIGN;
+    hipError_t err = launch_swiglu(gu, M, I, ld, dtype, y, (hipStream_t)stream);
+    return err == hipSuccess ? JF_OK : JF_ERR_HIP;
+}
+
 jf_status jf_rmsnorm(const void *x, int64_t rows, int64_t H, int64_t ldx, const void *w, float eps,
                      jf_dtype dtype, void *y, void *stream) {
     if (!x || !y) return JF_ERR_INVALID_ARG;

@@ -108,6 +108,9 @@ hipError_t launch_tree_rope(void *q, void *k, const int32_t *depth, const int32_
 hipError_t launch_rmsnorm(const void *x, int64_t rows, int H, int64_t ldx, const void *w, float eps,
                           jf_dtype dtype, void *y, hipStream_t s);
 
+hipError_t launch_swiglu(const void *gu, int64_t M, int64_t I, int64_t ld, jf_dtype dtype, void *y,
+                         hipStream_t s);
+
 // One expansion step sorts every (node, rank) candidate of a sequence in LDS.
 constexpr int kExpandMaxCands = 16384;
 hipError_t launch_tree_expand(const float *score, const int32_t *depth, const int32_t *idx,

@@ -28,7 +28,7 @@ EXPORTS = ("jf_status_string", "jf_abi_version", "jf_tree_mask_build",
            "jf_fuse_proj_cus", "jf_tree_attn_workspace_size",
            "jf_tree_attn_fwd", "jf_tree_attn_workspace_size_cus", "jf_tree_attn_fwd_cus",
            "jf_node_topk_workspace_size", "jf_node_topk", "jf_path_scores", "jf_tree_expand",
-           "jf_tree_accept", "jf_tree_rope", "jf_rmsnorm")
+           "jf_tree_accept", "jf_tree_rope", "jf_rmsnorm", "jf_swiglu")
 
 _lib = None
 
@@ -89,6 +89,8 @@ def lib():
     L.jf_tree_rope.restype = ctypes.c_int
     L.jf_rmsnorm.argtypes = [P, I64, I64, I64, P, ctypes.c_float, ctypes.c_int, P, P]
     L.jf_rmsnorm.restype = ctypes.c_int
+    L.jf_swiglu.argtypes = [P, I64, I64, I64, ctypes.c_int, P, P]
+    L.jf_swiglu.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -391,4 +393,18 @@ def jf_rmsnorm(x: torch.Tensor, w: Optional[torch.Tensor] = None, eps: float = 1
     st = lib().jf_rmsnorm(_p(x), rows, H, x.stride(0), _p(w), float(eps), _dtype_code(x), _p(y),
                           _stream(stream))
     _check("jf_rmsnorm", st)
+    return y
+
+
+def jf_swiglu(gu: torch.Tensor, y: Optional[torch.Tensor] = None, stream=None):
+    """silu(gate) * up from gu [M, 2I] (gate columns first; rows may be
+    strided) -> y [M, I]."""
+    if gu.dim() != 2 or gu.stride(1) != 1 or gu.shape[1] % 2:
+        raise ValueError("gu must be [M, 2I] with contiguous rows")
+    M, I = gu.shape[0], gu.shape[1] // 2
+    if y is None:
+        y = torch.empty((M, I), dtype=gu.dtype, device=gu.device)
+    _contig("y", y)
+    st = lib().jf_swiglu(_p(gu), M, I, gu.stride(0), _dtype_code(gu), _p(y), _stream(stream))
+    _check("jf_swiglu", st)
     return y
