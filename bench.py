@@ -565,51 +565,68 @@ def main():
     # tails, and the small kernels (split-K reduce, split merge) overlap the
     # other stream's work.  Same kernels, same arguments.
     s_side = torch.cuda.Stream()
-    # When mask + attention is the shorter of the two streams, the attention
-    # is planned for three quarters of the compute units (fewer, longer key
-    # splits): the units it leaves go to the projection and the top-k, and it
-    # writes fewer partial results.  When it is the longer one it keeps them all.
+    # The projection's K split and the attention's key splits can be planned
+    # for fewer compute units than the chip has (fewer, longer splits): the
+    # units they leave go to the other stream, and they write fewer partial
+    # results.  The plans tried are listed below.
     n_cus = torch.cuda.get_device_properties(0).multi_processor_count
     # top-k rows [0, r_split) follow the projection, [r_split, R) the attention
     r_split = R - int(round(R * min(max(args.topk_split, 0.0), 1.0)))
-    if args.attn_cus >= 0:
-        attn_cus = args.attn_cus
-    else:
-        f_b = (R - r_split) / R
-        shorter = (per_call["mask"] + per_call["attn"] + f_b * per_call["topk"]
-                   < per_call["fuse"] + (1 - f_b) * per_call["topk"])
-        attn_cus = (3 * n_cus) // 4 if shorter else 0
-    aws_side = jf.jf_tree_attn_workspace_size(B, N, wl.Hq, wl.Hkv, wl.D, a["page_size"], prefix_len,
-                                              jf.JF_BF16 if dt == "bf16" else jf.JF_F32, attn_cus)
-    attn_ws_side = torch.empty(max(aws_side, 1), dtype=torch.uint8, device="cuda")
-    # the projection's K split likewise leaves a quarter of the units to the
-    # other stream (fewer slices of fp32 partials)
-    fuse_cus = (3 * n_cus) // 4 if args.fuse_cus < 0 else args.fuse_cus
-    fws_side = jf.jf_fuse_proj_workspace_size(B * N, wl.H, wl.n_fused, wl.H,
-                                              jf.JF_BF16 if dt == "bf16" else jf.JF_F32, fuse_cus)
-    fuse_ws_side = torch.empty(max(fws_side, 1), dtype=torch.uint8, device="cuda")
-
+    f_b = (R - r_split) / R
+    shorter = (per_call["mask"] + per_call["attn"] + f_b * per_call["topk"]
+               < per_call["fuse"] + (1 - f_b) * per_call["topk"])
+    code = jf.JF_BF16 if dt == "bf16" else jf.JF_F32
     topk_ws_b = torch.empty(max(jf.jf_node_topk_workspace_size(max(R - r_split, 1), wl.V, wl.topk), 1),
                             dtype=torch.uint8, device="cuda")
 
-    def step_streams():
-        main = torch.cuda.current_stream()
-        s_side.wait_stream(main)
-        with torch.cuda.stream(s_side):
-            jf.jf_fuse_proj(xs, w, y=y, workspace=fuse_ws_side, cus=fuse_cus)
-            if r_split > 0:
-                jf.jf_node_topk(logits[:r_split], wl.topk, idx=idx[:r_split], val=val[:r_split],
-                                lse=rlse[:r_split], workspace=topk_ws)
-        jf.jf_tree_mask_build(parent, mask, depth, seq_status)
-        jf.jf_tree_attn_fwd(dev["q"], dev["k_tree"], dev["v_tree"], mask, dev["k_cache"],
-                            dev["v_cache"], block_table, prefix_len, out=out, lse=lse,
-                            workspace=attn_ws_side, page_status=page_status, cus=attn_cus)
-        if r_split < R:
-            jf.jf_node_topk(logits[r_split:], wl.topk, idx=idx[r_split:], val=val[r_split:],
-                            lse=rlse[r_split:], workspace=topk_ws_b)
-        main.wait_stream(s_side)
+    def make_step_streams(fuse_cus, attn_cus):
+        """The two-stream step with the projection's K split planned for
+        fuse_cus compute units and the attention's key splits for attn_cus
+        (0: all), each with its own workspace."""
+        aws = jf.jf_tree_attn_workspace_size(B, N, wl.Hq, wl.Hkv, wl.D, a["page_size"], prefix_len,
+                                             code, attn_cus)
+        attn_ws_s = torch.empty(max(aws, 1), dtype=torch.uint8, device="cuda")
+        fws = jf.jf_fuse_proj_workspace_size(B * N, wl.H, wl.n_fused, wl.H, code, fuse_cus)
+        fuse_ws_s = torch.empty(max(fws, 1), dtype=torch.uint8, device="cuda")
 
-    def time_graph(fn):
+        def step_streams():
+            main = torch.cuda.current_stream()
+            s_side.wait_stream(main)
+            with torch.cuda.stream(s_side):
+                jf.jf_fuse_proj(xs, w, y=y, workspace=fuse_ws_s, cus=fuse_cus)
+                if r_split > 0:
+                    jf.jf_node_topk(logits[:r_split], wl.topk, idx=idx[:r_split], val=val[:r_split],
+                                    lse=rlse[:r_split], workspace=topk_ws)
+            jf.jf_tree_mask_build(parent, mask, depth, seq_status)
+            jf.jf_tree_attn_fwd(dev["q"], dev["k_tree"], dev["v_tree"], mask, dev["k_cache"],
+                                dev["v_cache"], block_table, prefix_len, out=out, lse=lse,
+                                workspace=attn_ws_s, page_status=page_status, cus=attn_cus)
+            if r_split < R:
+                jf.jf_node_topk(logits[r_split:], wl.topk, idx=idx[r_split:], val=val[r_split:],
+                                lse=rlse[r_split:], workspace=topk_ws_b)
+            main.wait_stream(s_side)
+
+        return step_streams
+
+    # Compute-unit budgets of the two streams.  Given on the command line they
+    # are used as they are; otherwise a few plans are timed briefly as graphs
+    # and the fastest is kept:
+    #   "three_quarters": the projection's K split for 3/4 of the units, the
+    #       attention for 3/4 when mask + attention is the shorter stream;
+    #   "fit_together": 1/2 and 3/8, so both streams' workgroups fit on the
+    #       chip at once (the attention's fewer, longer splits leave units to
+    #       the projection and the top-k);
+    #   "fuse_half": 1/2 for the projection, all units for the attention.
+    if args.attn_cus >= 0 or args.fuse_cus >= 0:
+        plans = {"given": ((3 * n_cus) // 4 if args.fuse_cus < 0 else args.fuse_cus,
+                           (((3 * n_cus) // 4 if shorter else 0) if args.attn_cus < 0 else args.attn_cus))}
+    else:
+        plans = {"three_quarters": ((3 * n_cus) // 4, (3 * n_cus) // 4 if shorter else 0),
+                 "fit_together": (n_cus // 2, (3 * n_cus) // 8),
+                 "fuse_half": (n_cus // 2, 0)}
+
+    def time_graph(fn, reps=None):
+        reps = K if reps is None else reps
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
@@ -623,7 +640,7 @@ def main():
             graph.replay()
         torch.cuda.synchronize()
         a0 = time.perf_counter()
-        for k in range(K):
+        for k in range(reps):
             graph.replay()
         torch.cuda.synchronize()
         a1 = time.perf_counter()
@@ -631,6 +648,9 @@ def main():
 
     ms_per_step = eager_ms_per_step
     serial_graph_ms = None
+    plan_ms = {}
+    plan = next(iter(plans))
+    fuse_cus, attn_cus = plans[plan]
     if not args.eager:
         g0, g1 = time_graph(step)
         serial_graph_ms = (g1 - g0) * 1e3 / K
@@ -638,7 +658,15 @@ def main():
         if args.one_stream:
             t0, t1 = g0, g1
         else:
-            t0, t1 = time_graph(step_streams)
+            if len(plans) > 1:
+                for name, (fc, ac) in plans.items():
+                    p0, p1 = time_graph(make_step_streams(fc, ac), reps=max(20, K // 5))
+                    plan_ms[name] = round((p1 - p0) * 1e3 / max(20, K // 5), 5)
+                plan = min(plan_ms, key=plan_ms.get)
+                fuse_cus, attn_cus = plans[plan]
+                print(f"[bench] two-stream plans (ms/step): {plan_ms}; using {plan}", file=sys.stderr,
+                      flush=True)
+            t0, t1 = time_graph(make_step_streams(fuse_cus, attn_cus))
         ms_per_step = (t1 - t0) * 1e3 / K
         print(f"[bench] graph: {K} replays, {ms_per_step:.4f} ms/step", file=sys.stderr, flush=True)
 
@@ -765,6 +793,8 @@ def main():
         "launch": "eager" if args.eager else ("hip_graph" if args.one_stream else "hip_graph_2_streams"),
         "graph_one_stream_ms_per_step": None if serial_graph_ms is None else round(serial_graph_ms, 5),
         "attn_cus_two_streams": attn_cus,
+        "two_stream_plan": plan,
+        "two_stream_plans_ms": plan_ms or None,
         "fuse_cus_two_streams": fuse_cus,
         "topk_rows_on_attention_stream": R - r_split,
         "eager_ms_per_step": round(eager_ms_per_step, 5),
