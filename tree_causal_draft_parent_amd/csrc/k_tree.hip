@@ -1,5 +1,5 @@
-// k_tree.hip -- path scores of draft-tree nodes and one budgeted best-first
-// expansion of the tree.
+// k_tree.hip -- path scores of draft-tree nodes, one budgeted best-first
+// expansion of the tree, and greedy verification of a drafted tree.
 //
 // A branch's draft probability is the product of the per-node conditionals
 // along it (JetFlow blog page, "What JetFlow Does Differently"), so a node's
@@ -13,9 +13,13 @@
 //                   in fp64 from the node up to the prefix, then rounds once.
 //   k_tree_expand : one workgroup per sequence; every (node, rank) candidate
 //                   becomes one 64-bit key that orders (score desc, node asc,
-//                   rank asc); a bitonic sort of the keys in LDS (stages of
-//                   stride < 64 in registers with cross-lane moves), and the
-//                   first M keys decode into the new nodes.
+//                   rank asc); the M smallest keys are found with a score-bin
+//                   histogram and ranks counted inside a bin (a full bitonic
+//                   sort when a bin near the cut is crowded), and decode into
+//                   the new nodes.
+//   k_tree_accept : one workgroup per sequence; each lane walks its nodes'
+//                   chains checking the target's tokens; the deepest fully
+//                   accepted node and its path are written.
 #include "jf_internal.h"
 
 namespace jf {
