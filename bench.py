@@ -90,18 +90,32 @@ def copy_calibration():
     print(json.dumps({"calibration": "copy", "bytes_each_way": COPY_BYTES, "launches": 5}), flush=True)
 
 
+KERNEL_FILES = {"mask": ["k_mask.hip"], "fuse": ["k_fuse.hip"], "attn": ["k_attn.hip"],
+                "topk": ["k_topk.hip"]}
+
+
 def measured_traffic(call, workload):
     """HBM-side bytes per launch of a call's kernels from the committed counter
     record (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when there is
-    no record for this workload or the kernel sources changed since it was taken."""
+    no record for this workload or the call's kernel source (or the shared
+    internal header) changed since it was taken."""
     from tree_causal_draft_parent_amd import profsum
     try:
         with open(TRAFFIC_JSON) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("workload") != workload or rec.get("sources_sha256") != profsum.sources_hash():
+    if rec.get("workload") != workload:
         return None
+    measured = rec.get("file_sha256")
+    if measured is None:
+        if rec.get("sources_sha256") != profsum.sources_hash():
+            return None
+    else:
+        cur = profsum.file_hashes()
+        for fn in KERNEL_FILES[call] + ["jf_internal.h"]:
+            if measured.get(fn) is None or measured.get(fn) != cur.get(fn):
+                return None
     total, found = 0, False
     for k, v in rec.get("kernels", {}).items():
         base = k.split("<")[0]

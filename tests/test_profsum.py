@@ -43,7 +43,28 @@ def test_traffic_scaling(tmp_path):
     assert k["fetch_bytes"] == round(1100.0 * 1024 * 2.0)
     assert k["write_bytes"] == round(10.0 * 1024 * 0.5)
     assert rec["sources_sha256"] == profsum.sources_hash()
+    assert rec["file_sha256"] == profsum.file_hashes()
+    assert "k_fuse.hip" in rec["file_sha256"] and "jf_internal.h" in rec["file_sha256"]
     assert os.path.exists(out)
+
+
+def test_traffic_freshness_follows_the_calls_kernel_file(tmp_path, monkeypatch):
+    # a changed unrelated source leaves a call's counters valid; a changed
+    # kernel file of that call makes them stale
+    import bench
+    cur = profsum.file_hashes()
+    rec = {"workload": "w", "sources_sha256": "x", "file_sha256": dict(cur),
+           "kernels": {"k_fuse_gemm_bf16<256>": {"fetch_bytes": 10, "write_bytes": 5},
+                       "k_fuse_reduce": {"fetch_bytes": 3, "write_bytes": 1}}}
+    rec["file_sha256"]["k_tree.hip"] = "changed"
+    path = tmp_path / "traffic.json"
+    path.write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "TRAFFIC_JSON", str(path))
+    assert bench.measured_traffic("fuse", "w") == 19
+    assert bench.measured_traffic("fuse", "other") is None
+    rec["file_sha256"]["k_fuse.hip"] = "changed"
+    path.write_text(json.dumps(rec))
+    assert bench.measured_traffic("fuse", "w") is None
 
 
 def test_trace_split_by_grid(tmp_path, capsys):

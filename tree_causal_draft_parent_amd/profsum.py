@@ -8,8 +8,8 @@
         per-launch FETCH_SIZE / WRITE_SIZE of every libjf kernel, scaled by the
         factor that makes the same counters read N bytes for a plain copy
         kernel of N bytes read and N bytes written; written as JSON together
-        with a hash of the kernel sources (a reader treats the figures as stale
-        once the sources change).
+        with hashes of the kernel sources, whole and per file (a reader treats
+        a call's figures as stale once its kernel's source file changes).
 
 FETCH_SIZE and WRITE_SIZE are rocprofv3 derived counters in KiB per dispatch
 (bytes the L2 requested from / wrote to the memory fabric; on MI355X the
@@ -49,6 +49,15 @@ def short_name(name: str) -> str:
     n = n[:cut]
     n = n.replace("jf::(anonymous namespace)::", "").replace("(anonymous namespace)::", "")
     return n
+
+
+def file_hashes() -> dict:
+    """sha256 of each kernel source file (basename -> hex digest)."""
+    out = {}
+    for p in sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.h"))):
+        with open(p, "rb") as f:
+            out[os.path.basename(p)] = hashlib.sha256(f.read()).hexdigest()
+    return out
 
 
 def sources_hash() -> str:
@@ -141,6 +150,7 @@ def cmd_traffic(a):
                       "fetch_bytes": round(fk * 1024.0 * factor_f) if factor_f else None,
                       "write_bytes": round(wk * 1024.0 * factor_w) if factor_w else None}
     out = {"sources_sha256": sources_hash(),
+           "file_sha256": file_hashes(),
            "workload": a.workload,
            "copy_calibration": {"kernel": ck, "bytes_each_way": a.copy_bytes,
                                 "fetch_kib_raw": round(f_kib, 1), "write_kib_raw": round(w_kib, 1),
