@@ -593,10 +593,13 @@ def main():
     topk_ws_b = torch.empty(max(jf.jf_node_topk_workspace_size(max(R - r_split, 1), wl.V, wl.topk), 1),
                             dtype=torch.uint8, device="cuda")
 
-    def make_step_streams(fuse_cus, attn_cus):
-        """The two-stream step with the projection's K split planned for
+    s_third = torch.cuda.Stream()
+
+    def make_step_streams(fuse_cus, attn_cus, topk_apart=False):
+        """The multi-stream step with the projection's K split planned for
         fuse_cus compute units and the attention's key splits for attn_cus
-        (0: all), each with its own workspace."""
+        (0: all), each with its own workspace.  topk_apart: the top-k on a
+        third stream of its own instead of after the projection."""
         aws = jf.jf_tree_attn_workspace_size(B, N, wl.Hq, wl.Hkv, wl.D, a["page_size"], prefix_len,
                                              code, attn_cus)
         attn_ws_s = torch.empty(max(aws, 1), dtype=torch.uint8, device="cuda")
@@ -606,8 +609,11 @@ def main():
         def step_streams():
             main = torch.cuda.current_stream()
             s_side.wait_stream(main)
+            if topk_apart:
+                s_third.wait_stream(main)
             with torch.cuda.stream(s_side):
                 jf.jf_fuse_proj(xs, w, y=y, workspace=fuse_ws_s, cus=fuse_cus)
+            with torch.cuda.stream(s_third if topk_apart else s_side):
                 if r_split > 0:
                     jf.jf_node_topk(logits[:r_split], wl.topk, idx=idx[:r_split], val=val[:r_split],
                                     lse=rlse[:r_split], workspace=topk_ws)
@@ -619,6 +625,8 @@ def main():
                 jf.jf_node_topk(logits[r_split:], wl.topk, idx=idx[r_split:], val=val[r_split:],
                                 lse=rlse[r_split:], workspace=topk_ws_b)
             main.wait_stream(s_side)
+            if topk_apart:
+                main.wait_stream(s_third)
 
         return step_streams
 
@@ -630,14 +638,19 @@ def main():
     #   "fit_together": 1/2 and 3/8, so both streams' workgroups fit on the
     #       chip at once (the attention's fewer, longer splits leave units to
     #       the projection and the top-k);
-    #   "fuse_half": 1/2 for the projection, all units for the attention.
+    #   "fuse_half": 1/2 for the projection, all units for the attention;
+    #   "fit_five_eighths": 5/8 and 3/8;
+    #   "topk_apart": as fuse_half, the top-k on a third stream of its own.
     if args.attn_cus >= 0 or args.fuse_cus >= 0:
         plans = {"given": ((3 * n_cus) // 4 if args.fuse_cus < 0 else args.fuse_cus,
-                           (((3 * n_cus) // 4 if shorter else 0) if args.attn_cus < 0 else args.attn_cus))}
+                           (((3 * n_cus) // 4 if shorter else 0) if args.attn_cus < 0 else args.attn_cus),
+                           False)}
     else:
-        plans = {"three_quarters": ((3 * n_cus) // 4, (3 * n_cus) // 4 if shorter else 0),
-                 "fit_together": (n_cus // 2, (3 * n_cus) // 8),
-                 "fuse_half": (n_cus // 2, 0)}
+        plans = {"three_quarters": ((3 * n_cus) // 4, (3 * n_cus) // 4 if shorter else 0, False),
+                 "fit_together": (n_cus // 2, (3 * n_cus) // 8, False),
+                 "fuse_half": (n_cus // 2, 0, False),
+                 "fit_five_eighths": ((5 * n_cus) // 8, (3 * n_cus) // 8, False),
+                 "topk_apart": (n_cus // 2, 0, True)}
 
     def time_graph(fn, reps=None):
         reps = K if reps is None else reps
@@ -664,7 +677,7 @@ def main():
     serial_graph_ms = None
     plan_ms = {}
     plan = next(iter(plans))
-    fuse_cus, attn_cus = plans[plan]
+    fuse_cus, attn_cus, topk_apart = plans[plan]
     if not args.eager:
         g0, g1 = time_graph(step)
         serial_graph_ms = (g1 - g0) * 1e3 / K
@@ -673,14 +686,14 @@ def main():
             t0, t1 = g0, g1
         else:
             if len(plans) > 1:
-                for name, (fc, ac) in plans.items():
-                    p0, p1 = time_graph(make_step_streams(fc, ac), reps=max(20, K // 5))
+                for name, (fc, ac, ta) in plans.items():
+                    p0, p1 = time_graph(make_step_streams(fc, ac, ta), reps=max(20, K // 5))
                     plan_ms[name] = round((p1 - p0) * 1e3 / max(20, K // 5), 5)
                 plan = min(plan_ms, key=plan_ms.get)
-                fuse_cus, attn_cus = plans[plan]
+                fuse_cus, attn_cus, topk_apart = plans[plan]
                 print(f"[bench] two-stream plans (ms/step): {plan_ms}; using {plan}", file=sys.stderr,
                       flush=True)
-            t0, t1 = time_graph(make_step_streams(fuse_cus, attn_cus))
+            t0, t1 = time_graph(make_step_streams(fuse_cus, attn_cus, topk_apart))
         ms_per_step = (t1 - t0) * 1e3 / K
         print(f"[bench] graph: {K} replays, {ms_per_step:.4f} ms/step", file=sys.stderr, flush=True)
 
@@ -808,6 +821,7 @@ def main():
         "graph_one_stream_ms_per_step": None if serial_graph_ms is None else round(serial_graph_ms, 5),
         "attn_cus_two_streams": attn_cus,
         "two_stream_plan": plan,
+        "topk_own_stream": topk_apart,
         "two_stream_plans_ms": plan_ms or None,
         "fuse_cus_two_streams": fuse_cus,
         "topk_rows_on_attention_stream": R - r_split,
