@@ -60,32 +60,55 @@ def _setup(i):
         jf.jf_node_topk(d["logits"], wl.topk, idx=o["idx"], val=o["val"], lse=o["rlse"],
                         workspace=ws["topk"])
 
-    # the same step on two streams: projection then top-k beside mask then
-    # attention (the projection and the top-k depend on neither)
-    s_side = torch.cuda.Stream()
+    # the same step on two or three streams: projection (then top-k) beside
+    # mask then attention (the projection and the top-k depend on neither),
+    # with the projection's and the attention's splits planned for fuse_cus /
+    # attn_cus compute units (0: all), each plan with its own workspaces
+    s_side, s_third = torch.cuda.Stream(), torch.cuda.Stream()
 
-    def step_streams():
-        main = torch.cuda.current_stream()
-        s_side.wait_stream(main)
-        with torch.cuda.stream(s_side):
-            jf.jf_fuse_proj(d["xs"], d["w"], y=o["y"], workspace=ws["fuse"])
-            jf.jf_node_topk(d["logits"], wl.topk, idx=o["idx"], val=o["val"], lse=o["rlse"],
-                            workspace=ws["topk"])
-        jf.jf_tree_mask_build(d["parent"], o["mask"], o["depth"], o["seq_status"])
-        jf.jf_tree_attn_fwd(d["q"], d["k_tree"], d["v_tree"], o["mask"], d["k_cache"], d["v_cache"],
-                            d["block_table"], a["prefix_len"], out=o["out"], lse=o["lse"],
-                            workspace=ws["attn"], page_status=page_status)
-        main.wait_stream(s_side)
+    def make_streams(fuse_cus=0, attn_cus=0, topk_apart=False):
+        fws = torch.empty(max(jf.jf_fuse_proj_workspace_size(R, wl.H, wl.n_fused, wl.H, code, fuse_cus), 1),
+                          dtype=torch.uint8, device="cuda")
+        aws = torch.empty(max(jf.jf_tree_attn_workspace_size(B, N, wl.Hq, wl.Hkv, wl.D, a["page_size"],
+                                                             a["prefix_len"], code, attn_cus), 1),
+                          dtype=torch.uint8, device="cuda")
 
-    return wl, d, o, step, step_streams
+        def step_streams():
+            main = torch.cuda.current_stream()
+            s_side.wait_stream(main)
+            if topk_apart:
+                s_third.wait_stream(main)
+            with torch.cuda.stream(s_side):
+                jf.jf_fuse_proj(d["xs"], d["w"], y=o["y"], workspace=fws, cus=fuse_cus)
+            with torch.cuda.stream(s_third if topk_apart else s_side):
+                jf.jf_node_topk(d["logits"], wl.topk, idx=o["idx"], val=o["val"], lse=o["rlse"],
+                                workspace=ws["topk"])
+            jf.jf_tree_mask_build(d["parent"], o["mask"], o["depth"], o["seq_status"])
+            jf.jf_tree_attn_fwd(d["q"], d["k_tree"], d["v_tree"], o["mask"], d["k_cache"], d["v_cache"],
+                                d["block_table"], a["prefix_len"], out=o["out"], lse=o["lse"],
+                                workspace=aws, page_status=page_status, cus=attn_cus)
+            main.wait_stream(s_side)
+            if topk_apart:
+                main.wait_stream(s_third)
+
+        return step_streams
+
+    return wl, d, o, step, make_streams
 
 
-@pytest.mark.parametrize("i,streams", [(2, False), (3, False), (2, True), (3, True)])
-def test_step_graph_replays_match_eager(i, streams):
-    wl, d, o, step_serial, step_streams = _setup(i)
-    step = step_streams if streams else step_serial
-    say(f"graph replay: workload {wl.name}, {'two streams' if streams else 'one stream'}")
-    step_serial()
+@pytest.mark.parametrize("i", [2, 3])
+@pytest.mark.parametrize("plan", ["serial", "streams", "fit_five_eighths", "topk_apart"])
+def test_step_graph_replays_match_eager(i, plan):
+    # the schedules the benchmark times: one stream, two streams with all
+    # units, 5/8 + 3/8 of the units, and the top-k on a third stream; each
+    # replay must equal an eager run of the same schedule bit for bit
+    wl, d, o, step_serial, make_streams = _setup(i)
+    n_cus = torch.cuda.get_device_properties(0).multi_processor_count
+    step = {"serial": step_serial, "streams": make_streams(),
+            "fit_five_eighths": make_streams((5 * n_cus) // 8, (3 * n_cus) // 8),
+            "topk_apart": make_streams(n_cus // 2, 0, True)}[plan]
+    say(f"graph replay: workload {wl.name}, plan {plan}")
+    step()
     torch.cuda.synchronize()
     ref = {k: v.clone() for k, v in o.items()}
     # a few eager steps on a side stream before capture, as capture requires
