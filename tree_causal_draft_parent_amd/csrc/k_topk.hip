@@ -429,20 +429,28 @@ __global__ __launch_bounds__(kWB * kWave) void k_topk_stage1(
     else slice(nv_rt);
 
     if constexpr (kFused) {
-        // ---- merge the row's slices (wave 0): rank every candidate among the
-        // chunks * k keys; combine the (max, sum-exp) pairs ----
+        // ---- merge the row's slices: rank every candidate among the
+        // chunks * k keys with all of the block's waves (a group of G lanes a
+        // candidate, G the largest power of two with G * k <= 64, each lane
+        // counting the larger keys in its 1/G share); then wave 0 combines
+        // the (max, sum-exp) pairs ----
         __syncthreads();
-        if (wv != 0) return;
         const int n = chunks * k;
-        for (int e = lane; e < n; e += kWave) {
-            const uint64_t key = mkeys[e];
-            if (key == 0ull) continue;               // padding of a short slice
-            const int rk = rank_in(mkeys, n, key);
-            if (rk < k) {
-                idx[r * k + rk] = (int32_t)(~(uint32_t)key);
-                val[r * k + rk] = ordered_to_float((uint32_t)(key >> 32));
-            }
+        int lg = 0;
+        while (lg < 6 && (2 << lg) * k <= kWave) ++lg;
+        const int G = 1 << lg;
+        const int e = (int)threadIdx.x >> lg;           // candidate; < chunks * 64 / G, >= n only as spare
+        const int part = (int)threadIdx.x & (G - 1);
+        const uint64_t key = e < n ? mkeys[e] : 0ull;
+        int cnt = 0;
+        for (int j = part; j < n; j += G) cnt += mkeys[j] > key;
+        for (int m = G >> 1; m >= 1; m >>= 1) cnt += __shfl_xor(cnt, m);
+        // key 0: padding of a short slice, or a spare lane
+        if (part == 0 && key != 0ull && cnt < k) {
+            idx[r * k + cnt] = (int32_t)(~(uint32_t)key);
+            val[r * k + cnt] = ordered_to_float((uint32_t)(key >> 32));
         }
+        if (wv != 0) return;
         if (kLse) {
             float m = lane < chunks ? mstats[lane].x : -INFINITY;
             float s = lane < chunks ? mstats[lane].y : 0.f;
