@@ -689,11 +689,18 @@ def main():
                 for name, (fc, ac, ta) in plans.items():
                     p0, p1 = time_graph(make_step_streams(fc, ac, ta), reps=max(20, K // 5))
                     plan_ms[name] = round((p1 - p0) * 1e3 / max(20, K // 5), 5)
+                # the one-stream graph (already timed over K replays) competes too:
+                # for a small step the cross-stream waits cost more than they overlap
+                plan_ms["one_stream"] = round(serial_graph_ms, 5)
                 plan = min(plan_ms, key=plan_ms.get)
-                fuse_cus, attn_cus, topk_apart = plans[plan]
-                print(f"[bench] two-stream plans (ms/step): {plan_ms}; using {plan}", file=sys.stderr,
+                print(f"[bench] step plans (ms/step): {plan_ms}; using {plan}", file=sys.stderr,
                       flush=True)
-            t0, t1 = time_graph(make_step_streams(fuse_cus, attn_cus, topk_apart))
+            if plan == "one_stream":
+                t0, t1 = g0, g1
+                fuse_cus, attn_cus, topk_apart = 0, 0, False
+            else:
+                fuse_cus, attn_cus, topk_apart = plans[plan]
+                t0, t1 = time_graph(make_step_streams(fuse_cus, attn_cus, topk_apart))
         ms_per_step = (t1 - t0) * 1e3 / K
         print(f"[bench] graph: {K} replays, {ms_per_step:.4f} ms/step", file=sys.stderr, flush=True)
 
@@ -817,7 +824,9 @@ def main():
                    "q_heads": wl.Hq, "kv_heads": wl.Hkv, "head_dim": wl.D, "hidden": wl.H,
                    "fused_layers": wl.n_fused, "vocab": wl.V, "topk": wl.topk,
                    "step": "mask+fuse_proj+tree_attn+topk"},
-        "launch": "eager" if args.eager else ("hip_graph" if args.one_stream else "hip_graph_2_streams"),
+        "launch": ("eager" if args.eager else
+                   "hip_graph" if args.one_stream or plan == "one_stream" else
+                   "hip_graph_3_streams" if topk_apart else "hip_graph_2_streams"),
         "graph_one_stream_ms_per_step": None if serial_graph_ms is None else round(serial_graph_ms, 5),
         "attn_cus_two_streams": attn_cus,
         "two_stream_plan": plan,
