@@ -829,9 +829,9 @@ def main():
                    "hip_graph_3_streams" if topk_apart else "hip_graph_2_streams"),
         "graph_one_stream_ms_per_step": None if serial_graph_ms is None else round(serial_graph_ms, 5),
         "attn_cus_two_streams": attn_cus,
-        "two_stream_plan": plan,
+        "step_plan": plan,
         "topk_own_stream": topk_apart,
-        "two_stream_plans_ms": plan_ms or None,
+        "step_plans_ms": plan_ms or None,
         "fuse_cus_two_streams": fuse_cus,
         "topk_rows_on_attention_stream": R - r_split,
         "eager_ms_per_step": round(eager_ms_per_step, 5),
