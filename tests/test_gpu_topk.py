@@ -112,3 +112,34 @@ def test_beyond_largest_vocabulary_is_refused():
     t = torch.zeros((1, 64 * 9728 + 1), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(jf.JfError):
         jf.jf_node_topk(t, 64)
+
+
+# k above 16: every lane is "hot", the k-th largest lane maximum leaves
+# hundreds of survivors a slice, and the kernel raises the threshold from a
+# histogram of the survivors' keys (bins 2^sh keys wide) before ranking them.
+# These cases reach that step with one-key bins (bf16, normal logits), wider
+# bins (fp32 keys; bf16 logits spread over several binades, values up to a
+# few hundred), and k between the powers of two; the next test covers a row
+# where no bin helps (all equal: the selection reads the slice again).
+@pytest.mark.parametrize("dtype,R,k,wide", [("bf16", 128, 17, False), ("bf16", 128, 33, False),
+                                            ("f32", 128, 64, False), ("bf16", 128, 64, True),
+                                            ("bf16", 16, 40, True), ("f32", 16, 64, False)])
+def test_large_k_threshold_refinement(dtype, R, k, wide):
+    V = 151936 if dtype == "bf16" else 50000
+    bits = synth.make_logits(R=R, V=V, dtype=dtype, seed=R * 100 + k)
+    if wide:
+        x = synth.bf16_bits_to_f32(bits)
+        x = (np.sign(x) * np.exp2(np.abs(x) / 2)).astype(np.float32)
+        bits = synth.f32_to_bf16_bits(x)
+    _check(bits, dtype, k)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_large_k_all_equal_and_ties(dtype):
+    x = np.random.default_rng(4).standard_normal((128, 30000)).astype(np.float32)
+    x[0] = 1.5                                  # one value everywhere
+    x[1, :] = -np.inf
+    x[1, ::50] = 2.0                            # 600 equal finite values among -inf
+    x[2] = np.rint(x[2] * 2)                    # a handful of distinct values
+    bits = synth.f32_to_bf16_bits(x) if dtype == "bf16" else x
+    _check(bits, dtype, 64)

@@ -91,6 +91,37 @@ __device__ __forceinline__ int rank_in(const uint64_t *keys, int n, uint64_t key
     return rank;
 }
 
+// Rank of a key among `runs` runs of k keys, each in decreasing order (a
+// slice's candidates in rank order, zero padded): the keys above it, counted
+// in each run by a binary search (k <= 64).
+// Four runs are searched side by side so that their LDS reads overlap.
+__device__ __forceinline__ int rank_in_runs(const uint64_t *keys, int runs, int k, uint64_t key) {
+    int rank = 0;
+    int c = 0;
+    for (; c + 4 <= runs; c += 4) {
+        const uint64_t *run = keys + c * k;
+        int p0 = 0, p1 = 0, p2 = 0, p3 = 0;          // keys of each run above `key`
+#pragma unroll
+        for (int step = 64; step >= 1; step >>= 1) {
+            const bool in = (step <= k);              // p + step <= k needs step <= k
+            if (in && p0 + step <= k && run[p0 + step - 1] > key) p0 += step;
+            if (in && p1 + step <= k && run[k + p1 + step - 1] > key) p1 += step;
+            if (in && p2 + step <= k && run[2 * k + p2 + step - 1] > key) p2 += step;
+            if (in && p3 + step <= k && run[3 * k + p3 + step - 1] > key) p3 += step;
+        }
+        rank += p0 + p1 + p2 + p3;
+    }
+    for (; c < runs; ++c) {
+        const uint64_t *run = keys + c * k;
+        int pos = 0;
+#pragma unroll
+        for (int step = 64; step >= 1; step >>= 1)
+            if (pos + step <= k && run[pos + step - 1] > key) pos += step;
+        rank += pos;
+    }
+    return rank;
+}
+
 template <typename T> struct Vec;
 template <> struct Vec<uint16_t> {  // bf16 bits
     static constexpr int n = 8;
@@ -350,8 +381,8 @@ __global__ __launch_bounds__(kWB * kWave) void k_topk_stage1(
                 put_tail(pos);
             }
         } else {
-            // ---- many lanes tie at the threshold: every lane marks its own
-            // vectors, then writes its survivors ----
+            // ---- many hot lanes (k above kHot, or ties at the threshold):
+            // every lane marks its own vectors, then writes its survivors ----
             uint32_t marks[(MAXV * VEC + 31) / 32];
 #pragma unroll
             for (int w = 0; w < (MAXV * VEC + 31) / 32; ++w) marks[w] = 0u;
@@ -365,6 +396,82 @@ __global__ __launch_bounds__(kWB * kWave) void k_topk_stage1(
                 }
             }
             place(cnt);
+            if (tot > 2 * k) {
+                // With k above kHot the k-th largest lane maximum leaves several
+                // survivors a lane (hundreds a wave, at times more than the
+                // buffer).  Any threshold that keeps at least k elements keeps
+                // the k best, so raise it: a 256-bin histogram of the
+                // survivors' order-preserving keys above tv's (the top 16 bits
+                // for bf16, so every bin edge is a bf16 value; bins 2^sh keys
+                // wide, sh the least that spans the wave's largest key), then
+                // the highest bin edge that still keeps k.  The histogram sits
+                // in this wave's hot-vector area, unused on this path.
+                constexpr int kLow = VEC == 8 ? 16 : 0;
+                float wmax = lmax;
+#pragma unroll
+                for (int q = 0; q < VEC; ++q) wmax = fmaxf(wmax, tx[q]);   // -inf past the tail
+#pragma unroll
+                for (int off = 32; off >= 1; off >>= 1) wmax = fmaxf(wmax, __shfl_xor(wmax, off));
+                const uint32_t base = ordered_bits(tv) >> kLow;
+                const uint32_t span = (ordered_bits(wmax) >> kLow) - base;   // wmax >= tv
+                const int sh = span < 256u ? 0 : 24 - __builtin_clz(span);  // span >> sh < 256
+                uint32_t *hist = (uint32_t *)hbuf[wv];
+                hbuf[wv][lane] = u32x4{0u, 0u, 0u, 0u};
+                __builtin_amdgcn_wave_barrier();
+                auto bin_of = [&](float x) -> uint32_t {
+                    return ((ordered_bits(x) >> kLow) - base) >> sh;
+                };
+#pragma unroll
+                for (int v = 0; v < MAXV; ++v) {
+                    uint32_t pm = (marks[(v * VEC) / 32] >> ((v * VEC) % 32)) & ((1u << VEC) - 1u);
+                    if (v < nv && __ballot(pm != 0)) {
+                        while (pm) {
+                            const int j = __builtin_ctz(pm);
+                            pm &= pm - 1u;
+                            atomicAdd(&hist[bin_of(element(d[v], j))], 1u);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int q = 0; q < VEC; ++q)
+                    if ((tmark >> q) & 1u) atomicAdd(&hist[bin_of(tx[q])], 1u);
+                __builtin_amdgcn_wave_barrier();
+                const u32x4 h = hbuf[wv][lane];              // bins 4 lane .. 4 lane + 3
+                int above = (int)(h[0] + h[1] + h[2] + h[3]);  // then: bins >= 4 lane
+#pragma unroll
+                for (int off = 1; off < kWave; off <<= 1) {
+                    const int o = __shfl_down(above, off);
+                    above += lane + off < kWave ? o : 0;
+                }
+                const int s3 = above - (int)(h[0] + h[1] + h[2]);   // bins >= 4 lane + 3
+                const int s2 = s3 + (int)h[2], s1 = s2 + (int)h[1];
+                const int j = s3 >= k ? 3 : s2 >= k ? 2 : s1 >= k ? 1 : 0;
+                const uint64_t ok = __ballot(above >= k);     // lane 0 always: all survivors
+                const int L = 63 - __builtin_clzll(ok);
+                const int b = 4 * L + __shfl(j, L);
+                const uint32_t key = base + ((uint32_t)b << sh);
+                uint32_t pk = key << kLow;
+                if (kLow) pk |= (pk & 0x80000000u) ? 0u : 0xffffu;
+                tv = ordered_to_float(pk);
+                tmark = 0;
+#pragma unroll
+                for (int q = 0; q < VEC; ++q)
+                    tmark |= (uint32_t)(lane + q * kWave < ntail && tx[q] >= tv) << q;
+#pragma unroll
+                for (int w = 0; w < (MAXV * VEC + 31) / 32; ++w) marks[w] = 0u;
+                cnt = __popc(tmark);
+#pragma unroll
+                for (int v = 0; v < MAXV; ++v) {
+                    if (v < nv) {
+                        const uint32_t pm = survivors(d[v]);
+                        marks[(v * VEC) / 32] |= pm << ((v * VEC) % 32);
+                        cnt += __popc(pm);
+                    }
+                }
+                pre = 0;
+                tot = 0;
+                place(cnt);
+            }
             if (tot <= kCap) {
                 int pos = pre;
 #pragma unroll
@@ -436,19 +543,33 @@ __global__ __launch_bounds__(kWB * kWave) void k_topk_stage1(
         // the (max, sum-exp) pairs ----
         __syncthreads();
         const int n = chunks * k;
-        int lg = 0;
-        while (lg < 6 && (2 << lg) * k <= kWave) ++lg;
-        const int G = 1 << lg;
-        const int e = (int)threadIdx.x >> lg;           // candidate; < chunks * 64 / G, >= n only as spare
-        const int part = (int)threadIdx.x & (G - 1);
-        const uint64_t key = e < n ? mkeys[e] : 0ull;
-        int cnt = 0;
-        for (int j = part; j < n; j += G) cnt += mkeys[j] > key;
-        for (int m = G >> 1; m >= 1; m >>= 1) cnt += __shfl_xor(cnt, m);
-        // key 0: padding of a short slice, or a spare lane
-        if (part == 0 && key != 0ull && cnt < k) {
-            idx[r * k + cnt] = (int32_t)(~(uint32_t)key);
-            val[r * k + cnt] = ordered_to_float((uint32_t)(key >> 32));
+        if (k > kHot) {
+            // large k: a thread a candidate (n <= chunks * 64 threads), ranked
+            // by binary searches in the slices' sorted runs
+            const int e = (int)threadIdx.x;
+            const uint64_t key = e < n ? mkeys[e] : 0ull;
+            if (key != 0ull) {
+                const int cnt = rank_in_runs(mkeys, chunks, k, key);
+                if (cnt < k) {
+                    idx[r * k + cnt] = (int32_t)(~(uint32_t)key);
+                    val[r * k + cnt] = ordered_to_float((uint32_t)(key >> 32));
+                }
+            }
+        } else {
+            int lg = 0;
+            while (lg < 6 && (2 << lg) * k <= kWave) ++lg;
+            const int G = 1 << lg;
+            const int e = (int)threadIdx.x >> lg;           // candidate; < chunks * 64 / G, >= n only as spare
+            const int part = (int)threadIdx.x & (G - 1);
+            const uint64_t key = e < n ? mkeys[e] : 0ull;
+            int cnt = 0;
+            for (int j = part; j < n; j += G) cnt += mkeys[j] > key;
+            for (int m = G >> 1; m >= 1; m >>= 1) cnt += __shfl_xor(cnt, m);
+            // key 0: padding of a short slice, or a spare lane
+            if (part == 0 && key != 0ull && cnt < k) {
+                idx[r * k + cnt] = (int32_t)(~(uint32_t)key);
+                val[r * k + cnt] = ordered_to_float((uint32_t)(key >> 32));
+            }
         }
         if (wv != 0) return;
         if (kLse) {
@@ -470,8 +591,8 @@ __global__ __launch_bounds__(kWB * kWave) void k_topk_stage1(
 constexpr int kMaxCand = 4096;   // chunks * k candidates merged per row
 constexpr int kMergeTarget = 256;  // preferred bound on chunks * k
 
-template <bool kLse>
-__global__ __launch_bounds__(256) void k_topk_stage2(const uint64_t *__restrict__ cand,
+template <bool kLse, int kThreads>
+__global__ __launch_bounds__(kThreads) void k_topk_stage2(const uint64_t *__restrict__ cand,
                                                     const float2 *__restrict__ stats, int chunks,
                                                     int k, int32_t *__restrict__ idx,
                                                     float *__restrict__ val,
@@ -482,12 +603,12 @@ __global__ __launch_bounds__(256) void k_topk_stage2(const uint64_t *__restrict_
     const int64_t r = blockIdx.x;
     const int n = chunks * k;                    // <= kMaxCand
     const uint64_t *src = cand + r * (int64_t)n;
-    for (int e = tid; e < n; e += 256) keys[e] = src[e];
+    for (int e = tid; e < n; e += kThreads) keys[e] = src[e];
     __syncthreads();
-    for (int e = tid; e < n; e += 256) {
+    for (int e = tid; e < n; e += kThreads) {
         const uint64_t key = keys[e];
         if (key == 0ull) continue;               // padding of a short slice
-        const int rk = rank_in(keys, n, key);
+        const int rk = k > kHot ? rank_in_runs(keys, chunks, k, key) : rank_in(keys, n, key);
         if (rk < k) {
             idx[r * k + rk] = (int32_t)(~(uint32_t)key);
             val[r * k + rk] = ordered_to_float((uint32_t)(key >> 32));
@@ -495,7 +616,10 @@ __global__ __launch_bounds__(256) void k_topk_stage2(const uint64_t *__restrict_
     }
     if (kLse) {
         float m = -INFINITY, s = 0.f;
-        for (int c = tid; c < chunks; c += 256) {
+        // the slices' (max, sum-exp) pairs are combined by the first 256
+        // threads in the same order at every block size
+        constexpr int kLseThreads = 256;
+        for (int c = tid; tid < kLseThreads && c < chunks; c += kLseThreads) {
             float2 st = stats[r * chunks + c];
             float mn = fmaxf(m, st.x);
             float bn = mn == -INFINITY ? 0.f : mn * kLog2e;
@@ -510,12 +634,12 @@ __global__ __launch_bounds__(256) void k_topk_stage2(const uint64_t *__restrict_
             s = s * __builtin_amdgcn_exp2f(m * kLog2e - bn) + so * __builtin_amdgcn_exp2f(mo * kLog2e - bn);
             m = mn;
         }
-        if (lane == 0) part[wv] = make_float2(m, s);
+        if (lane == 0 && wv < kLseThreads / kWave) part[wv] = make_float2(m, s);
         __syncthreads();
         if (tid == 0) {
             m = -INFINITY;
             s = 0.f;
-            for (int w = 0; w < 4; ++w) {
+            for (int w = 0; w < kLseThreads / kWave; ++w) {
                 float mn = fmaxf(m, part[w].x);
                 float bn = mn == -INFINITY ? 0.f : mn * kLog2e;
                 s = s * __builtin_amdgcn_exp2f(m * kLog2e - bn) +
@@ -599,12 +723,19 @@ hipError_t launch_topk(const TopkPlan &p, const void *logits, int64_t ld, jf_dty
 #undef JF_TOPK1
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (with_lse)
-        hipLaunchKernelGGL((k_topk_stage2<true>), dim3((unsigned)p.R), dim3(256), 0, s, cand, stats,
-                           p.chunks, p.k, idx, val, lse);
-    else
-        hipLaunchKernelGGL((k_topk_stage2<false>), dim3((unsigned)p.R), dim3(256), 0, s, cand, stats,
-                           p.chunks, p.k, idx, val, lse);
+    // k above kHot: ranks by binary searches, latency-bound chains, so four
+    // times the threads a row
+#define JF_TOPK2(L, TH)                                                                             \
+    hipLaunchKernelGGL((k_topk_stage2<L, TH>), dim3((unsigned)p.R), dim3(TH), 0, s, cand, stats,     \
+                       p.chunks, p.k, idx, val, lse)
+    if (p.k > kHot) {
+        if (with_lse) JF_TOPK2(true, 1024);
+        else JF_TOPK2(false, 1024);
+    } else {
+        if (with_lse) JF_TOPK2(true, 256);
+        else JF_TOPK2(false, 256);
+    }
+#undef JF_TOPK2
     return hipGetLastError();
 }
 
