@@ -66,6 +66,8 @@ def parse():
                     help="skip timing the path-score and expansion calls after the step")
     ap.add_argument("--no-lm-head", action="store_true",
                     help="skip timing the LM-head contraction (one-layer jf_fuse_proj to the vocabulary)")
+    ap.add_argument("--topk-sweep", action="store_true",
+                    help="also time jf_node_topk over the step's logits at k = 1, 8, 16, 32, 64")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy 5 times (counter calibration)")
     return ap.parse_args()
@@ -218,6 +220,25 @@ def copy_bandwidth(torch, reps=10):
     e1.record()
     torch.cuda.synchronize()
     return 2 * COPY_BYTES * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+
+def topk_sweep(logits, steps, torch, jf):
+    """jf_node_topk over the step's logits (with the row log-sum-exp) at several
+    k, each timed as a graph of 20 back-to-back calls."""
+    R, V = logits.shape
+    out = {}
+    for k in (1, 8, 16, 32, 64):
+        idx = torch.empty((R, k), dtype=torch.int32, device="cuda")
+        val = torch.empty((R, k), dtype=torch.float32, device="cuda")
+        lse = torch.empty((R,), dtype=torch.float32, device="cuda")
+        ws = torch.empty(max(jf.jf_node_topk_workspace_size(R, V, k), 1), dtype=torch.uint8,
+                         device="cuda")
+        ms = graph_time(lambda: jf.jf_node_topk(logits, k, idx=idx, val=val, lse=lse, workspace=ws),
+                        steps, torch)
+        out[f"k{k}"] = {"ms": round(ms, 5),
+                        "GBps": round(logits.numel() * logits.element_size() / (ms * 1e-3) / 1e9, 1)}
+    out.update(rows=R, vocab=V, timing="graph of 20 back-to-back calls")
+    return out
 
 
 def tree_growth(wl, parent, depth, idx, val, rlse, steps, torch, jf, parent_np=None, logits=None):
@@ -746,6 +767,13 @@ def main():
             print(f"[bench] LM head {head['M']}x{head['K']}->{head['N']}: {head['ms']:.4f} ms, "
                   f"{head['hbm_GBps']:.0f} GB/s", file=sys.stderr, flush=True)
 
+    sweep = None
+    if args.topk_sweep:
+        sweep = topk_sweep(logits, K, torch, jf)
+        print(f"[bench] top-k sweep (ms): " + ", ".join(f"{c} {v['ms']:.4f}" for c, v in sweep.items()
+                                                        if isinstance(v, dict)),
+              file=sys.stderr, flush=True)
+
     def med(v):
         return float(np.median(v)) if len(v) else float("nan")
 
@@ -844,6 +872,7 @@ def main():
         "projection_context": proj_ctx,
         "tree_growth": growth,
         "draft_layer": head,
+        "topk_sweep": sweep,
         "copy_GBps": round(copy_gbs, 1),
         "roofline": roofline,
         "cpu_baseline": cpu,
