@@ -84,7 +84,7 @@ def _load():
     lib.oracle_topk.restype = None
     lib.oracle_path_scores.argtypes = [P, P, I64, I64, P, P]
     lib.oracle_path_scores.restype = ctypes.c_int
-    lib.oracle_tree_expand.argtypes = [P, P, P, P, P, I64, I64, I64, I64, I64, P, P, P, P]
+    lib.oracle_tree_expand.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, I64, P, P, P, P]
     lib.oracle_tree_expand.restype = ctypes.c_int
     lib.oracle_tree_accept.argtypes = [P, P, P, P, I64, I64, P, P, P, P, P]
     lib.oracle_tree_accept.restype = ctypes.c_int
@@ -204,23 +204,28 @@ def path_scores(parent: np.ndarray, logp: np.ndarray):
 
 
 def tree_expand(score: np.ndarray, depth: np.ndarray, idx: np.ndarray, val: np.ndarray,
-                lse: np.ndarray, M: int, max_depth: int):
-    """One best-first expansion step: the M best (parent, rank) candidates of each
-    sequence -> new parent, token, score (float32), depth, each [B, M]."""
+                lse: np.ndarray, M: int, max_depth: int, parent: np.ndarray, token: np.ndarray):
+    """One best-first expansion step of the trees (parent, token) [B, N]: the M
+    best (node, rank) candidates of each sequence that are not already a child
+    of their node -> new parent, token, score (float32), depth, each [B, M]."""
     score = _c(score, np.float32)
     depth = _c(depth, np.int32)
     idx = _c(idx, np.int32)
     val = _c(val, np.float32)
     lse = _c(lse, np.float32)
+    parent = _c(parent, np.int32)
+    token = _c(token, np.int32)
     B, N = score.shape
     k = idx.shape[-1]
     assert idx.shape == (B, N, k) and val.shape == (B, N, k) and lse.shape == (B, N)
+    assert parent.shape == (B, N) and token.shape == (B, N)
     outp = np.zeros((B, M), dtype=np.int32)
     outt = np.zeros((B, M), dtype=np.int32)
     outs = np.zeros((B, M), dtype=np.float32)
     outd = np.zeros((B, M), dtype=np.int32)
-    st = _load().oracle_tree_expand(_p(score), _p(depth), _p(idx), _p(val), _p(lse), B, N, k, M,
-                                    max_depth, _p(outp), _p(outt), _p(outs), _p(outd))
+    st = _load().oracle_tree_expand(_p(score), _p(depth), _p(idx), _p(val), _p(lse), _p(parent),
+                                    _p(token), B, N, k, M, max_depth, _p(outp), _p(outt), _p(outs),
+                                    _p(outd))
     if st != 0:
         raise ValueError(f"oracle_tree_expand: status {st}")
     return outp, outt, outs, outd

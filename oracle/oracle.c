@@ -27,7 +27,8 @@
  * h / (Hq/Hkv); the fusion is concatenation followed by one bias-free linear
  * map; top-k order is value descending then index ascending, -0 == +0; a path
  * score is the sum of the conditional log-probabilities along the branch, and
- * one expansion step keeps the M best one-token extensions of the tree;
+ * one expansion step keeps the M best one-token extensions of the tree that
+ * are not already in it;
  * verification is greedy (a node is accepted when its token is the target's
  * next token after its parent) and keeps the deepest fully accepted node.
  */
@@ -318,7 +319,12 @@ int oracle_path_scores(const int32_t *parent, const double *logp, int64_t B, int
  * path score plus the child's conditional log-probability, the log-softmax
  * of p's row at that token:
  *     s(p, r) = score[p] + (val[p][r] - lse[p]).
- * A candidate is eligible when 1 <= depth[p] and depth[p] + 1 <= max_depth.
+ * A candidate is eligible when 1 <= depth[p], depth[p] + 1 <= max_depth, and
+ * node p does not already have a child carrying token idx[p][r]: the step
+ * grows the tree as it stands, and a second child with the same token would
+ * be the same branch twice.  The tree's children are read from parent[] and
+ * token[] (node j is a child of parent[j] carrying token[j]; parents outside
+ * [0, N) name no node and exclude nothing).
  * With a budget of M new nodes, best-first expansion takes the M best
  * eligible candidates in the order (s descending, p ascending, r ascending),
  * written in that order: new parent p, token, s, depth depth[p] + 1.  Slots
@@ -338,8 +344,18 @@ static int cand_cmp(const void *x, const void *y)
     return a->r < b->r ? -1 : (a->r > b->r);
 }
 
+/* Does node p of sequence b already have a child carrying token t? */
+static int has_child_with_token(const int32_t *parent, const int32_t *token, int64_t b,
+                                int64_t N, int64_t p, int32_t t)
+{
+    for (int64_t j = 0; j < N; ++j)
+        if (parent[b * N + j] == p && token[b * N + j] == t) return 1;
+    return 0;
+}
+
 int oracle_tree_expand(const float *score, const int32_t *depth, const int32_t *idx,
-                       const float *val, const float *lse, int64_t B, int64_t N, int64_t k,
+                       const float *val, const float *lse, const int32_t *parent,
+                       const int32_t *token, int64_t B, int64_t N, int64_t k,
                        int64_t M, int64_t max_depth, int32_t *new_parent, int32_t *new_token,
                        float *new_score, int32_t *new_depth)
 {
@@ -353,6 +369,7 @@ int oracle_tree_expand(const float *score, const int32_t *depth, const int32_t *
             if (d < 1 || (int64_t)d + 1 > max_depth) continue;
             for (int64_t r = 0; r < k; ++r) {
                 const int64_t e = (b * N + p) * k + r;
+                if (has_child_with_token(parent, token, b, N, p, idx[e])) continue;
                 volatile float t = val[e] - lse[b * N + p];     /* rounded to float */
                 volatile float sc = score[b * N + p] + t;        /* rounded to float */
                 c[n].s = sc;

@@ -4,9 +4,12 @@ Path scores: a hand-derived golden forest (tests/golden/path_tree7.txt); a
 chain equals numpy's cumulative sum; a star equals the inputs; the recursion
 score(i) = score(parent(i)) + logp(i) on random forests; relabelling the nodes
 permutes the scores; bad trees are reported like the mask's.
-Expansion: a hand-derived golden step (tests/golden/expand_small.txt); a brute
-force with numpy's lexsort over float32 scores; the output order, the depth cap,
-the budget and ties on integer-valued inputs."""
+Expansion: hand-derived golden steps (tests/golden/expand_small.txt, and
+expand_grown.txt where two candidates are already children); a brute force
+with numpy's lexsort over float32 scores that drops the (parent, token) pairs
+already in the tree; two successive steps never give a node two children with
+the same token; the output order, the depth cap, the budget and ties on
+integer-valued inputs."""
 import os
 
 import numpy as np
@@ -82,20 +85,27 @@ def test_path_bad_trees_match_the_mask():
     assert score[0, 2] == 0.0 and score[0, 3] == 0.0 and score[1, 3] == 0.0 and score[1, 0] == -1.0
 
 
-def _golden_expand():
-    g = _read("expand_small.txt")
+def _golden_expand(name="expand_small.txt"):
+    g = _read(name)
     f = lambda k: np.array([float(t) for t in g[k]], np.float32)
     i = lambda k: np.array([int(t) for t in g[k]], np.int32)
     return dict(score=f("score")[None], depth=i("depth")[None], lse=f("lse")[None],
                 val=f("val").reshape(1, 4, 2), idx=i("idx").reshape(1, 4, 2),
-                max_depth=int(g["max_depth"][0])), g
+                max_depth=int(g["max_depth"][0]), parent=i("parent")[None],
+                token=i("token")[None]), g
 
 
-@pytest.mark.parametrize("M", [5, 8])
-def test_expand_golden(M):
-    inp, g = _golden_expand()
-    p, t, s, d = oracle.tree_expand(inp["score"], inp["depth"], inp["idx"], inp["val"], inp["lse"],
-                                    M, inp["max_depth"])
+def _expand(inp, M, **kw):
+    a = {**inp, **kw}
+    return oracle.tree_expand(a["score"], a["depth"], a["idx"], a["val"], a["lse"], M,
+                              a["max_depth"], a["parent"], a["token"])
+
+
+@pytest.mark.parametrize("name,M", [("expand_small.txt", 5), ("expand_small.txt", 8),
+                                    ("expand_grown.txt", 3), ("expand_grown.txt", 5)])
+def test_expand_golden(name, M):
+    inp, g = _golden_expand(name)
+    p, t, s, d = _expand(inp, M)
     assert list(p[0]) == [int(x) for x in g[f"m{M}_parent"]]
     assert list(t[0]) == [int(x) for x in g[f"m{M}_token"]]
     assert list(d[0]) == [int(x) for x in g[f"m{M}_depth"]]
@@ -103,7 +113,9 @@ def test_expand_golden(M):
 
 
 def _brute(inp, M):
-    """Brute force: every eligible candidate's float32 score, ordered with lexsort."""
+    """Brute force: every eligible candidate's float32 score, ordered with
+    lexsort; a candidate whose (parent, token) pair is already a child in the
+    tree is dropped (a set of the tree's pairs)."""
     B, N, k = inp["idx"].shape
     out = []
     for b in range(B):
@@ -111,7 +123,10 @@ def _brute(inp, M):
         s = (inp["score"][b][:, None] + t).astype(np.float32)
         p = np.repeat(np.arange(N), k).reshape(N, k)
         r = np.tile(np.arange(k), (N, 1))
-        ok = (inp["depth"][b] >= 1) & (inp["depth"][b] + 1 <= inp["max_depth"])
+        kids = set(zip(inp["parent"][b].tolist(), inp["token"][b].tolist()))
+        new = np.array([[(i, int(inp["idx"][b, i, j])) not in kids for j in range(k)]
+                        for i in range(N)])
+        ok = ((inp["depth"][b] >= 1) & (inp["depth"][b] + 1 <= inp["max_depth"]))[:, None] & new
         s, p, r = s[ok].ravel(), p[ok].ravel(), r[ok].ravel()
         order = np.lexsort((r, p, -s.astype(np.float64)))[:M]
         out.append((p[order], r[order], s[order]))
@@ -122,8 +137,7 @@ def _brute(inp, M):
 @pytest.mark.parametrize("N,k,M", [(16, 4, 10), (64, 8, 64), (256, 8, 256), (40, 3, 200)])
 def test_expand_matches_lexsort(ties, N, k, M):
     inp = synth.make_expand_inputs(B=2, N=N, k=k, seed=N + k + M, ties=ties, max_depth=12)
-    p, t, s, d = oracle.tree_expand(inp["score"], inp["depth"], inp["idx"], inp["val"], inp["lse"],
-                                    M, inp["max_depth"])
+    p, t, s, d = _expand(inp, M)
     for b, (bp, br, bs) in enumerate(_brute(inp, M)):
         n = len(bp)
         assert np.array_equal(p[b, :n], bp)
@@ -137,22 +151,64 @@ def test_expand_matches_lexsort(ties, N, k, M):
 
 
 def test_expand_takes_all_when_budget_allows():
-    inp = synth.make_expand_inputs(B=1, N=10, k=2, seed=9, max_depth=100)
-    p, t, s, d = oracle.tree_expand(inp["score"], inp["depth"], inp["idx"], inp["val"], inp["lse"],
-                                    25, inp["max_depth"])
+    # no child carries a listed token: every candidate is new
+    inp = synth.make_expand_inputs(B=1, N=10, k=2, seed=9, max_depth=100, child_frac=0.0)
+    p, t, s, d = _expand(inp, 25)
     assert sorted(zip(p[0, :20], t[0, :20])) == sorted(
         (i, inp["idx"][0, i, r]) for i in range(10) for r in range(2))
     assert np.all(p[0, 20:] == -2)
 
 
+def test_expand_skips_existing_children():
+    # every listed token of every node is already a child: nothing is new
+    inp = synth.make_expand_inputs(B=1, N=6, k=2, seed=10, max_depth=100, child_frac=0.0)
+    kids_p, kids_t = [-1] * 6, list(range(1000, 1006))
+    for i in range(6):
+        kids_p += [i, i]
+        kids_t += [int(inp["idx"][0, i, 0]), int(inp["idx"][0, i, 1])]
+    n = len(kids_p)
+    pad = lambda a, fill: np.concatenate([a, np.full((1, n - 6) + a.shape[2:], fill, a.dtype)], axis=1)
+    grown = dict(score=pad(inp["score"], -1.0), depth=pad(inp["depth"], 100), idx=pad(inp["idx"], 7),
+                 val=pad(inp["val"], 0.0), lse=pad(inp["lse"], 1.0), max_depth=100,
+                 parent=np.array([kids_p], np.int32), token=np.array([kids_t], np.int32))
+    # the padded nodes (depth 100 = max_depth) have no eligible children
+    p, t, s, d = _expand(grown, 8)
+    assert np.all(p == -2) and np.all(t == -1) and np.all(np.isneginf(s))
+
+
+@pytest.mark.parametrize("N,k,M", [(16, 4, 16), (64, 8, 64)])
+def test_two_growth_steps_never_duplicate_siblings(N, k, M):
+    # grow the tree twice: the second step sees the first step's children and
+    # proposes none of them again, so no node ends with two children carrying
+    # the same token (the first step's lists are unchanged: a node's
+    # conditional distribution does not depend on its children)
+    inp = synth.make_expand_inputs(B=2, N=N, k=k, seed=N + k, max_depth=64)
+    p1, t1, s1, d1 = _expand(inp, M)
+    extra = synth.make_expand_inputs(B=2, N=M, k=k, seed=N + k + 1, max_depth=64)
+    grown = {}
+    for key in ("idx", "val", "lse"):
+        grown[key] = np.concatenate([inp[key], extra[key]], axis=1)
+    grown["score"] = np.concatenate([inp["score"], s1], axis=1)
+    grown["depth"] = np.concatenate([inp["depth"], d1], axis=1)
+    grown["parent"] = np.concatenate([inp["parent"], p1], axis=1)
+    grown["token"] = np.concatenate([inp["token"], t1], axis=1)
+    grown["max_depth"] = inp["max_depth"]
+    assert np.all(p1 >= 0)                     # the budget was filled both times
+    p2, t2, s2, d2 = _expand(grown, M)
+    assert np.all(p2 >= 0)
+    for b in range(2):
+        pairs = list(zip(grown["parent"][b].tolist(), grown["token"][b].tolist())) + \
+            list(zip(p2[b].tolist(), t2[b].tolist()))
+        assert len(pairs) == len(set(pairs)), "a node got two children with the same token"
+
+
 def test_expand_signed_zero_is_plus_zero():
     # -0 ties +0 (candidate order decides) and is written as +0
-    inp = synth.make_expand_inputs(B=1, N=2, k=1, seed=14, max_depth=100)
+    inp = synth.make_expand_inputs(B=1, N=2, k=1, seed=14, max_depth=100, child_frac=0.0)
     inp["score"][:] = np.array([-0.0, 0.0], np.float32)
     inp["val"][:] = np.array([[[-0.0], [0.0]]], np.float32)
     inp["lse"][:] = 0.0
-    p, t, s, d = oracle.tree_expand(inp["score"], inp["depth"], inp["idx"], inp["val"], inp["lse"],
-                                    2, 100)
+    p, t, s, d = _expand(inp, 2, max_depth=100)
     assert list(p[0]) == [0, 1]
     assert list(s[0].view(np.uint32)) == [0, 0]
 

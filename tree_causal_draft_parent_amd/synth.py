@@ -262,23 +262,50 @@ def make_path_inputs(*, B: int, N: int, max_depth: int = 16, branching=(1, 8),
 
 
 def make_expand_inputs(*, B: int, N: int, k: int, V: int = 151936, max_depth: int = 16,
-                       seed: int = 1234, ties: bool = False) -> dict:
+                       seed: int = 1234, ties: bool = False, child_frac: float = 0.5) -> dict:
     """Inputs of one expansion step: the current nodes' path scores (float32,
     N(-5, 3)), depths U{1..max_depth}, and per-node top-k lists as the top-k
-    call returns them (token ids U[0, V), values N(8, 3) in descending order)
-    with a row log-normaliser above the row's largest value.  ties=True rounds
-    scores, values and normalisers to integers so that many candidates tie."""
-    rng = _seeds(seed, ("score", "depth", "idx", "val", "lse"))
+    call returns them (distinct token ids U[0, V), values N(8, 3) in
+    descending order) with a row log-normaliser above the row's largest value.
+    ties=True rounds scores, values and normalisers to integers so that many
+    candidates tie.  The tree the step grows: a forest in creation order
+    (parent -1 with probability 1/4, else a uniform earlier node); a child
+    carries one of its parent's listed tokens not taken by a sibling with
+    probability child_frac, else a token its parent does not list; siblings'
+    tokens are distinct."""
+    rng = _seeds(seed, ("score", "depth", "idx", "val", "lse", "parent", "token"))
     score = rng["score"].standard_normal((B, N)) * 3.0 - 5.0
     depth = rng["depth"].integers(1, max_depth + 1, size=(B, N)).astype(np.int32)
-    idx = rng["idx"].integers(0, V, size=(B, N, k)).astype(np.int32)
+    idx = np.empty((B, N, k), np.int32)
+    for b in range(B):
+        for i in range(N):
+            idx[b, i] = rng["idx"].choice(V, size=k, replace=False)
     val = np.sort(rng["val"].standard_normal((B, N, k)) * 3.0 + 8.0, axis=-1)[..., ::-1]
     lse = val[..., 0] + rng["lse"].uniform(0.0, 3.0, size=(B, N))
     if ties:
         score, val, lse = np.round(score), np.round(val), np.ceil(lse)
+    parent = np.full((B, N), -1, np.int32)
+    token = np.empty((B, N), np.int32)
+    rp, rt = rng["parent"], rng["token"]
+    for b in range(B):
+        used = {}                                   # parent -> tokens its children carry
+        for i in range(N):
+            p = -1 if i == 0 or rp.random() < 0.25 else int(rp.integers(0, i))
+            parent[b, i] = p
+            taken = used.setdefault(p, set())
+            listed = set(int(t) for t in idx[b, p]) if p >= 0 else set()
+            free = [t for t in idx[b, p] if int(t) not in taken] if p >= 0 else []
+            if free and rt.random() < child_frac:
+                t = int(free[int(rt.integers(len(free)))])
+            else:
+                t = int(rt.integers(0, V))
+                while t in listed or t in taken:
+                    t = int(rt.integers(0, V))
+            token[b, i] = t
+            taken.add(t)
     return dict(score=score.astype(np.float32), depth=depth, idx=idx,
                 val=np.ascontiguousarray(val, dtype=np.float32), lse=lse.astype(np.float32),
-                max_depth=max_depth)
+                max_depth=max_depth, parent=parent, token=token)
 
 
 def make_verify_inputs(parent: np.ndarray, *, q: float = 0.9, seed: int = 1234) -> dict:
