@@ -254,22 +254,29 @@ jf_status jf_path_scores(const int32_t *parent, const float *logp, int32_t B,
  * the candidates are the pairs (p, r), node p's r-th top token, with score
  *     s(p, r) = score[p] + (val[p][r] - lse[p])
  * (two fp32 roundings, in that order), eligible when
- * 1 <= depth[p] < max_depth.  The M best eligible candidates in the order
- * (s descending, p ascending, r ascending) become the new nodes, written in
- * that order: new_parent = p, new_token = idx[p][r], new_score = s (a zero
- * written as +0; -0 and +0 tie), new_depth = depth[p] + 1.  Slots beyond
- * the eligible count read parent -2, token -1, score -inf, depth 0.
+ * 1 <= depth[p] < max_depth and node p has no child carrying idx[p][r] yet
+ * (the step grows the tree as it stands; a second child with the same token
+ * would be the same branch twice).  The M best eligible candidates in the
+ * order (s descending, p ascending, r ascending) become the new nodes,
+ * written in that order: new_parent = p, new_token = idx[p][r], new_score = s
+ * (a zero written as +0; -0 and +0 tie), new_depth = depth[p] + 1.  Slots
+ * beyond the eligible count read parent -2, token -1, score -inf, depth 0.
  *
  *   score  [B, N] fp32 path scores of the current nodes (jf_path_scores).
  *   depth  [B, N] int32 (jf_tree_mask_build).
  *   idx    [B, N, k] int32, val [B, N, k] fp32, lse [B, N] fp32: the
- *          per-node top-k lists and log-normalisers (jf_node_topk).
+ *          per-node top-k lists and log-normalisers (jf_node_topk); a
+ *          node's listed tokens are distinct (as jf_node_topk returns them).
+ *   parent [B, N] int32, token [B, N] int32: the tree being grown; node j
+ *          is a child of parent[j] (-1: of the prefix) carrying token[j].
+ *          A parent outside [0, N) excludes nothing.
  *   new_parent, new_token, new_depth [B, M] int32; new_score [B, M] fp32.
  *   B >= 1, N >= 1, 1 <= k, N * k <= 16384, M >= 1; NaN scores, values or
  *   normalisers are not supported.
  * ------------------------------------------------------------------------ */
 jf_status jf_tree_expand(const float *score, const int32_t *depth,
                          const int32_t *idx, const float *val, const float *lse,
+                         const int32_t *parent, const int32_t *token,
                          int32_t B, int32_t N, int32_t k, int32_t M,
                          int32_t max_depth, int32_t *new_parent,
                          int32_t *new_token, float *new_score,

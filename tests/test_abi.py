@@ -148,14 +148,17 @@ def test_path_and_expand_argument_errors():
     assert L.jf_path_scores(FAKE, FAKE_ODD, 1, 4, FAKE, None, None) == jf.JF_ERR_ALIGN
 
     def exp(**kw):
-        a = dict(score=FAKE, depth=FAKE, idx=FAKE, val=FAKE, lse=FAKE, B=1, N=256, k=8, M=256,
-                 max_depth=16, np_=FAKE, nt=FAKE, ns=FAKE, nd=FAKE)
+        a = dict(score=FAKE, depth=FAKE, idx=FAKE, val=FAKE, lse=FAKE, parent=FAKE, token=FAKE,
+                 B=1, N=256, k=8, M=256, max_depth=16, np_=FAKE, nt=FAKE, ns=FAKE, nd=FAKE)
         a.update(kw)
-        return L.jf_tree_expand(a["score"], a["depth"], a["idx"], a["val"], a["lse"], a["B"],
-                                a["N"], a["k"], a["M"], a["max_depth"], a["np_"], a["nt"],
-                                a["ns"], a["nd"], None)
+        return L.jf_tree_expand(a["score"], a["depth"], a["idx"], a["val"], a["lse"], a["parent"],
+                                a["token"], a["B"], a["N"], a["k"], a["M"], a["max_depth"],
+                                a["np_"], a["nt"], a["ns"], a["nd"], None)
 
     assert exp(lse=None) == jf.JF_ERR_INVALID_ARG
+    assert exp(parent=None) == jf.JF_ERR_INVALID_ARG
+    assert exp(token=None) == jf.JF_ERR_INVALID_ARG
+    assert exp(token=FAKE_ODD) == jf.JF_ERR_ALIGN
     assert exp(nd=None) == jf.JF_ERR_INVALID_ARG
     assert exp(B=0) == jf.JF_ERR_INVALID_ARG
     assert exp(k=0) == jf.JF_ERR_INVALID_ARG

@@ -96,8 +96,11 @@ def _setup(i):
     return wl, d, o, step, make_streams
 
 
-@pytest.mark.parametrize("i", [2, 3])
-@pytest.mark.parametrize("plan", ["serial", "streams", "fit_five_eighths", "topk_apart"])
+# The 16-node workload (1) is replayed on one stream only: the benchmark
+# times only that schedule for it (its multi-stream plan loop once ended in a
+# host fault of unknown cause and is not run).
+@pytest.mark.parametrize("i,plan", [(1, "serial")] + [
+    (i, plan) for i in (2, 3, 4) for plan in ("serial", "streams", "fit_five_eighths", "topk_apart")])
 def test_step_graph_replays_match_eager(i, plan):
     # the schedules the benchmark times: one stream, two streams with all
     # units, 5/8 + 3/8 of the units, and the top-k on a third stream; each

@@ -83,20 +83,22 @@ def _expand(inp, M):
     say(f"tree_expand: B={B} N={N} k={k} M={M} max_depth={inp['max_depth']}")
     outs = jf.jf_tree_expand(dev_tensor(inp["score"]), dev_tensor(inp["depth"]),
                              dev_tensor(inp["idx"]), dev_tensor(inp["val"]), dev_tensor(inp["lse"]),
-                             M, inp["max_depth"])
+                             dev_tensor(inp["parent"]), dev_tensor(inp["token"]), M,
+                             inp["max_depth"])
     torch.cuda.synchronize()
     return [o.cpu().numpy() for o in outs]
 
 
-def _check_expand(inp, M):
+def _check_expand(inp, M, full=False):
     gp, gt, gs, gd = _expand(inp, M)
     op, ot, os_, od = oracle.tree_expand(inp["score"], inp["depth"], inp["idx"], inp["val"],
-                                         inp["lse"], M, inp["max_depth"])
+                                         inp["lse"], M, inp["max_depth"], inp["parent"],
+                                         inp["token"])
     assert np.array_equal(gp, op)
     assert np.array_equal(gt, ot)
     assert np.array_equal(gs.view(np.uint32), os_.view(np.uint32))
     assert np.array_equal(gd, od)
-    return gp
+    return (gp, gt, gs, gd) if full else gp
 
 
 @pytest.mark.parametrize("B,N,k,M,max_depth", [
@@ -147,6 +149,30 @@ def test_expand_all_scores_equal(N, k):
     inp["score"][:] = 0.0
     inp["val"][:] = inp["lse"][..., None]
     _check_expand(inp, min(N * k, 300))
+
+
+@pytest.mark.parametrize("child_frac", [0.0, 1.0])
+def test_expand_existing_children(child_frac):
+    # no listed token taken / as many taken as the lists allow
+    inp = synth.make_expand_inputs(B=4, N=256, k=8, max_depth=16, seed=11, child_frac=child_frac)
+    _check_expand(inp, 256)
+
+
+def test_expand_two_growth_steps():
+    # the second step sees the first step's children and proposes none again
+    inp = synth.make_expand_inputs(B=2, N=64, k=8, max_depth=64, seed=12)
+    p1, t1, s1, d1 = _check_expand(inp, 64, full=True)
+    extra = synth.make_expand_inputs(B=2, N=64, k=8, max_depth=64, seed=13)
+    grown = {key: np.concatenate([inp[key], extra[key]], axis=1) for key in ("idx", "val", "lse")}
+    grown.update(score=np.concatenate([inp["score"], s1], axis=1),
+                 depth=np.concatenate([inp["depth"], d1], axis=1),
+                 parent=np.concatenate([inp["parent"], p1], axis=1),
+                 token=np.concatenate([inp["token"], t1], axis=1), max_depth=64)
+    p2, t2, _, _ = _check_expand(grown, 64, full=True)
+    for b in range(2):
+        pairs = list(zip(grown["parent"][b].tolist(), grown["token"][b].tolist())) + \
+            list(zip(p2[b].tolist(), t2[b].tolist()))
+        assert len(pairs) == len(set(pairs))
 
 
 def test_expand_crowded_bin_near_the_cut():

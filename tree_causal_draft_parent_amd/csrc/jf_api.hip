@@ -313,19 +313,22 @@ jf_status jf_tree_accept(const int32_t *parent, const int32_t *token, const int3
 }
 
 jf_status jf_tree_expand(const float *score, const int32_t *depth, const int32_t *idx,
-                         const float *val, const float *lse, int32_t B, int32_t N, int32_t k,
+                         const float *val, const float *lse, const int32_t *parent,
+                         const int32_t *token, int32_t B, int32_t N, int32_t k,
                          int32_t M, int32_t max_depth, int32_t *new_parent, int32_t *new_token,
                          float *new_score, int32_t *new_depth, void *stream) {
-    if (!score || !depth || !idx || !val || !lse || !new_parent || !new_token || !new_score ||
-        !new_depth)
+    if (!score || !depth || !idx || !val || !lse || !parent || !token || !new_parent ||
+        !new_token || !new_score || !new_depth)
         return JF_ERR_INVALID_ARG;
     if (B < 1 || N < 1 || k < 1 || M < 1) return JF_ERR_INVALID_ARG;
     if ((int64_t)N * k > kExpandMaxCands) return JF_ERR_UNSUPPORTED;
-    const void *ptrs[] = {score, depth, idx, val, lse, new_parent, new_token, new_score, new_depth};
+    const void *ptrs[] = {score, depth, idx, val, lse, parent, token, new_parent, new_token,
+                          new_score, new_depth};
     for (const void *q : ptrs)
         if (!aligned(q, 4)) return JF_ERR_ALIGN;
-    hipError_t e = launch_tree_expand(score, depth, idx, val, lse, B, N, k, M, max_depth, new_parent,
-                                      new_token, new_score, new_depth, (hipStream_t)stream);
+    hipError_t e = launch_tree_expand(score, depth, idx, val, lse, parent, token, B, N, k, M,
+                                      max_depth, new_parent, new_token, new_score, new_depth,
+                                      (hipStream_t)stream);
     return e == hipSuccess ? JF_OK : JF_ERR_HIP;
 }
 

@@ -114,7 +114,8 @@ hipError_t launch_swiglu(const void *gu, int64_t M, int64_t I, int64_t ld, jf_dt
 // One expansion step sorts every (node, rank) candidate of a sequence in LDS.
 constexpr int kExpandMaxCands = 16384;
 hipError_t launch_tree_expand(const float *score, const int32_t *depth, const int32_t *idx,
-                              const float *val, const float *lse, int B, int N, int k, int M,
+                              const float *val, const float *lse, const int32_t *parent,
+                              const int32_t *token, int B, int N, int k, int M,
                               int max_depth, int32_t *new_parent, int32_t *new_token,
                               float *new_score, int32_t *new_depth, hipStream_t s);
 

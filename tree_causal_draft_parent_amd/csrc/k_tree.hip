@@ -11,7 +11,9 @@
 //   k_path_scores : one workgroup per sequence; parents and log-probabilities
 //                   staged in LDS; each lane walks its nodes' chains and sums
 //                   in fp64 from the node up to the prefix, then rounds once.
-//   k_tree_expand : one workgroup per sequence; every (node, rank) candidate
+//   k_tree_expand : one workgroup per sequence; the candidates that are
+//                   already children in the tree are marked in an LDS bitmap;
+//                   every other (node, rank) candidate
 //                   becomes one 64-bit key that orders (score desc, node asc,
 //                   rank asc); the M smallest keys are found with a score-bin
 //                   histogram and ranks counted inside a bin (a full bitonic
@@ -195,10 +197,15 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
 //      its segment; ranks below M are output slots.
 // A bin of more than kSelMaxBin keys at or below the cut (mass ties) switches
 // the workgroup to the full bitonic sort.
+// A candidate (p, r) whose token idx[p][r] some node j of the tree already
+// carries as a child of p (parent[j] == p, token[j] == idx[p][r]) is not
+// eligible: the step grows the tree as it stands, and a second child with
+// the same token would be the same branch twice.
 template <int R>
 __global__ __launch_bounds__(kExpThreads) void k_tree_expand(
     const float *__restrict__ score, const int32_t *__restrict__ depth,
     const int32_t *__restrict__ idx, const float *__restrict__ val, const float *__restrict__ lse,
+    const int32_t *__restrict__ parent, const int32_t *__restrict__ token,
     int N, int k, int M, int max_depth, int32_t *__restrict__ new_parent,
     int32_t *__restrict__ new_token, float *__restrict__ new_score,
     int32_t *__restrict__ new_depth) {
@@ -208,6 +215,7 @@ __global__ __launch_bounds__(kExpThreads) void k_tree_expand(
     __shared__ uint32_t boff[kSelBins];
     __shared__ float red[2][kExpThreads / 64];
     __shared__ int sel[3];                  // cut bin, eligible count, use the sort
+    __shared__ uint32_t taken[kExpandMaxCands / 32];   // bit p*k + r: already a child
     const int b = blockIdx.x;
     const int nc = N * k;
     const int64_t nbase = (int64_t)b * N;
@@ -216,6 +224,7 @@ __global__ __launch_bounds__(kExpThreads) void k_tree_expand(
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
     for (int i = threadIdx.x; i < kSelBins; i += kExpThreads) hist[i] = 0;
+    for (int i = threadIdx.x; i < (nc + 31) / 32; i += kExpThreads) taken[i] = 0u;
 
     // Keys: high word ~ord(score) (descending score first), low word the flat
     // candidate index p*k + r (node ascending, then rank ascending).  Every
@@ -243,6 +252,20 @@ __global__ __launch_bounds__(kExpThreads) void k_tree_expand(
 #pragma unroll
     for (int r = 0; r < R; ++r)
         asm volatile("" : "+v"(dr[r]), "+v"(vr[r]), "+v"(lr[r]), "+v"(sr[r]), "+v"(tk[r]));
+    __syncthreads();                          // taken[] cleared
+    // Mark the candidates that are already children: node j is the child of
+    // parent[j] carrying token[j], so the rank of that token in the parent's
+    // list (if it is listed) is taken.
+#pragma unroll 4
+    for (int j = threadIdx.x; j < N; j += kExpThreads) {
+        const int p = parent[nbase + j];
+        const int32_t t = token[nbase + j];
+        if (p < 0 || p >= N) continue;        // a root, or a parent that names no node
+        const int32_t *row = idx + cbase + (int64_t)p * k;
+        for (int r = 0; r < k; ++r)
+            if (row[r] == t) atomicOr(&taken[(p * k + r) >> 5], 1u << ((p * k + r) & 31));
+    }
+    __syncthreads();
     uint64_t key[R];
     float sc[R];
     float smax = -__builtin_inff(), smin = __builtin_inff();
@@ -251,8 +274,9 @@ __global__ __launch_bounds__(kExpThreads) void k_tree_expand(
         const int e = e0 + r;
         const float t = vr[r] - lr[r];            // rounded to fp32
         sc[r] = sr[r] + t;                        // rounded to fp32
-        // eligible: child depth d + 1 <= max_depth
-        const bool ok = e < nc && dr[r] >= 1 && dr[r] < max_depth;
+        // eligible: child depth d + 1 <= max_depth, not already a child
+        const bool ok = e < nc && dr[r] >= 1 && dr[r] < max_depth &&
+                        !((taken[min(e, nc - 1) >> 5] >> (e & 31)) & 1u);
         key[r] = ok ? (((uint64_t)(~ord_f32(sc[r])) << 32) | (uint32_t)e) : kNoCand;
         if (ok && __builtin_isfinite(sc[r])) {
             smax = fmaxf(smax, sc[r]);
@@ -474,14 +498,16 @@ hipError_t launch_tree_accept(const int32_t *parent, const int32_t *token,
 }
 
 hipError_t launch_tree_expand(const float *score, const int32_t *depth, const int32_t *idx,
-                              const float *val, const float *lse, int B, int N, int k, int M,
+                              const float *val, const float *lse, const int32_t *parent,
+                              const int32_t *token, int B, int N, int k, int M,
                               int max_depth, int32_t *new_parent, int32_t *new_token,
                               float *new_score, int32_t *new_depth, hipStream_t s) {
     int R = 1;                                    // slots per lane: 256*R >= N*k
     while (kExpThreads * R < N * k) R <<= 1;
 #define JF_EXPAND(RR)                                                                            \
     hipLaunchKernelGGL(k_tree_expand<RR>, dim3(B), dim3(kExpThreads), 0, s, score, depth, idx,   \
-                       val, lse, N, k, M, max_depth, new_parent, new_token, new_score, new_depth)
+                       val, lse, parent, token, N, k, M, max_depth, new_parent, new_token,         \
+                       new_score, new_depth)
     switch (R) {
         case 1: JF_EXPAND(1); break;
         case 2: JF_EXPAND(2); break;

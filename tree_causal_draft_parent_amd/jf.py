@@ -81,7 +81,7 @@ def lib():
     L.jf_node_topk.restype = ctypes.c_int
     L.jf_path_scores.argtypes = [P, P, I32, I32, P, P, P]
     L.jf_path_scores.restype = ctypes.c_int
-    L.jf_tree_expand.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, P, P, P, P, P]
+    L.jf_tree_expand.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, P, P, P, P, P]
     L.jf_tree_expand.restype = ctypes.c_int
     L.jf_tree_accept.argtypes = [P, P, P, P, I32, I32, P, P, P, P, P, P]
     L.jf_tree_accept.restype = ctypes.c_int
@@ -297,22 +297,25 @@ def jf_path_scores(parent: torch.Tensor, logp: torch.Tensor, score=None, seq_sta
 
 
 def jf_tree_expand(score: torch.Tensor, depth: torch.Tensor, idx: torch.Tensor,
-                   val: torch.Tensor, lse: torch.Tensor, M: int, max_depth: int, out=None,
-                   stream=None):
-    """One best-first expansion step: score [B, N] fp32, depth [B, N] int32,
-    idx [B, N, k] int32, val [B, N, k] fp32, lse [B, N] fp32 -> the M best
-    one-token extensions of each sequence's tree as (new_parent, new_token,
+                   val: torch.Tensor, lse: torch.Tensor, parent: torch.Tensor,
+                   token: torch.Tensor, M: int, max_depth: int, out=None, stream=None):
+    """One best-first expansion step of the trees (parent, token) [B, N] int32:
+    score [B, N] fp32, depth [B, N] int32, idx [B, N, k] int32, val [B, N, k]
+    fp32, lse [B, N] fp32 -> the M best one-token extensions of each
+    sequence's tree that are not already children, as (new_parent, new_token,
     new_score, new_depth), each [B, M]."""
-    for n, t in (("score", score), ("depth", depth), ("idx", idx), ("val", val), ("lse", lse)):
+    for n, t in (("score", score), ("depth", depth), ("idx", idx), ("val", val), ("lse", lse),
+                 ("parent", parent), ("token", token)):
         _contig(n, t)
     B, N = score.shape
     k = idx.shape[-1]
     if (depth.shape != (B, N) or idx.shape != (B, N, k) or val.shape != (B, N, k)
-            or lse.shape != (B, N)):
+            or lse.shape != (B, N) or parent.shape != (B, N) or token.shape != (B, N)):
         raise ValueError("inconsistent shapes")
     if (score.dtype != torch.float32 or val.dtype != torch.float32 or lse.dtype != torch.float32
-            or depth.dtype != torch.int32 or idx.dtype != torch.int32):
-        raise ValueError("score/val/lse float32 and depth/idx int32 expected")
+            or depth.dtype != torch.int32 or idx.dtype != torch.int32
+            or parent.dtype != torch.int32 or token.dtype != torch.int32):
+        raise ValueError("score/val/lse float32 and depth/idx/parent/token int32 expected")
     dev = score.device
     if out is None:
         out = (torch.empty((B, M), dtype=torch.int32, device=dev),
@@ -320,8 +323,9 @@ def jf_tree_expand(score: torch.Tensor, depth: torch.Tensor, idx: torch.Tensor,
                torch.empty((B, M), dtype=torch.float32, device=dev),
                torch.empty((B, M), dtype=torch.int32, device=dev))
     np_, nt, ns, nd = out
-    st = lib().jf_tree_expand(_p(score), _p(depth), _p(idx), _p(val), _p(lse), B, N, k, int(M),
-                              int(max_depth), _p(np_), _p(nt), _p(ns), _p(nd), _stream(stream))
+    st = lib().jf_tree_expand(_p(score), _p(depth), _p(idx), _p(val), _p(lse), _p(parent),
+                              _p(token), B, N, k, int(M), int(max_depth), _p(np_), _p(nt), _p(ns),
+                              _p(nd), _stream(stream))
     _check("jf_tree_expand", st)
     return np_, nt, ns, nd
 
