@@ -52,7 +52,7 @@ typedef enum { JF_F32 = 0, JF_BF16 = 1 } jf_dtype;
 const char *jf_status_string(int status);
 
 /* ABI version, bumped on any signature change. */
-int jf_abi_version(void);  /* 4 */
+int jf_abi_version(void);  /* 5 */
 
 /* --------------------------------------------------------------------------
  * jf_tree_mask_build -- ancestor bitmask of every tree node.
@@ -221,6 +221,26 @@ jf_status jf_node_topk(const void *logits, int64_t R, int64_t V, int64_t ld,
                        jf_dtype dtype, int32_t k, int32_t *idx, float *val,
                        float *lse, void *workspace, size_t workspace_bytes,
                        void *stream);
+
+/* --------------------------------------------------------------------------
+ * jf_node_topk_noalloc -- jf_node_topk (same arguments and results) for
+ * callers that cannot allocate: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  It takes no workspace and
+ * allocates nothing: its scratch is a static device array of
+ * JF_NODE_TOPK_SCRATCH_BYTES per GPU, held by each GPU the library runs on
+ * until the process ends (its address is looked up once per device, on the
+ * first call there).  A size whose jf_node_topk_workspace_size(R, V, k)
+ * exceeds that limit returns JF_ERR_WORKSPACE and launches nothing.  All
+ * calls on one GPU share the array: calls that overlap in time on one GPU
+ * (different streams, or one stream of another process sharing the library
+ * instance) race and must not be issued.  The array keeps the last call's
+ * contents; no part of it has to start at zero.
+ * ------------------------------------------------------------------------ */
+#define JF_NODE_TOPK_SCRATCH_BYTES ((size_t)4 << 20)
+jf_status jf_node_topk_noalloc(const void *logits, int64_t R, int64_t V,
+                               int64_t ld, jf_dtype dtype, int32_t k,
+                               int32_t *idx, float *val, float *lse,
+                               void *stream);
 
 /* --------------------------------------------------------------------------
  * jf_path_scores -- path log-probability of every draft-tree node.

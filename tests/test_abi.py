@@ -21,7 +21,7 @@ def _declared():
 
 def test_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 19
+    assert len(names) == 20
     assert sorted(jf.EXPORTS) == names
     L = jf.lib()
     for n in names:
@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
 def test_status_strings_and_version():
     assert jf.status_string(0) == "JF_OK"
     assert jf.status_string(5) == "JF_ERR_BAD_TREE"
-    assert jf.lib().jf_abi_version() == 4
+    assert jf.lib().jf_abi_version() == 5
 
 
 FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: every call below fails validation
@@ -138,6 +138,28 @@ def test_fuse_and_topk_argument_errors():
     assert L.jf_node_topk(FAKE, 4, 100, 100, 1, 101, FAKE, FAKE, None, FAKE, 1 << 20, None) == jf.JF_ERR_UNSUPPORTED
     assert L.jf_node_topk(FAKE, 4, 100, 100, 1, 4, FAKE, FAKE, None, FAKE, 1 << 20, None) == jf.JF_ERR_ALIGN
     assert L.jf_node_topk(FAKE, 4, 104, 104, 1, 4, FAKE, FAKE, None, None, 0, None) == jf.JF_ERR_WORKSPACE
+
+
+def test_noalloc_topk_argument_errors():
+    L = jf.lib()
+    ok = [FAKE, 4, 104, 104, 1, 4, FAKE, FAKE, None, None]
+    assert L.jf_node_topk_noalloc(*ok[:0], None, *ok[1:]) == jf.JF_ERR_INVALID_ARG
+    bad = list(ok); bad[1] = 0
+    assert L.jf_node_topk_noalloc(*bad) == jf.JF_ERR_INVALID_ARG
+    bad = list(ok); bad[5] = 65
+    assert L.jf_node_topk_noalloc(*bad) == jf.JF_ERR_UNSUPPORTED
+    bad = list(ok); bad[0] = FAKE_ODD
+    assert L.jf_node_topk_noalloc(*bad) == jf.JF_ERR_ALIGN
+    # a size whose workspace exceeds the static scratch is refused before any HIP call
+    big = [FAKE, 1024, 622592, 622592, 1, 64, FAKE, FAKE, None, None]
+    assert jf.jf_node_topk_workspace_size(1024, 622592, 64) > jf.NODE_TOPK_SCRATCH_BYTES
+    assert L.jf_node_topk_noalloc(*big) == jf.JF_ERR_WORKSPACE
+
+
+def test_noalloc_scratch_limit_matches_the_header():
+    src = open(os.path.join(ROOT, "include", "jf.h")).read()
+    m = re.search(r"#define JF_NODE_TOPK_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == jf.NODE_TOPK_SCRATCH_BYTES
 
 
 def test_path_and_expand_argument_errors():

@@ -44,7 +44,7 @@ const char *jf_status_string(int status) {
     }
 }
 
-int jf_abi_version(void) { return 4; }
+int jf_abi_version(void) { return 5; }
 
 jf_status jf_tree_mask_build(const int32_t *parent, int32_t B, int32_t N, uint64_t *mask,
                              int32_t *depth, int32_t *seq_status, void *stream) {
@@ -238,6 +238,26 @@ jf_status jf_node_topk(const void *logits, int64_t R, int64_t V, int64_t ld, jf_
     const size_t need = topk_workspace_bytes(p);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return JF_ERR_WORKSPACE;
     hipError_t e = launch_topk(p, logits, ld, dtype, idx, val, lse, workspace, (hipStream_t)stream);
+    return e == hipSuccess ? JF_OK : JF_ERR_HIP;
+}
+
+jf_status jf_node_topk_noalloc(const void *logits, int64_t R, int64_t V, int64_t ld,
+                               jf_dtype dtype, int32_t k, int32_t *idx, float *val, float *lse,
+                               void *stream) {
+    if (!logits || !idx || !val) return JF_ERR_INVALID_ARG;
+    if (R < 1 || V < 1 || ld < V || k < 1) return JF_ERR_INVALID_ARG;
+    if (dtype != JF_BF16 && dtype != JF_F32) return JF_ERR_INVALID_ARG;
+    if (k > 64 || k > V || V > INT32_MAX) return JF_ERR_UNSUPPORTED;
+    if (R > (int64_t)1 << 30) return JF_ERR_UNSUPPORTED;
+    if (!aligned(logits, 16) || ld % (dtype == JF_BF16 ? 8 : 4) != 0) return JF_ERR_ALIGN;
+    if (!aligned(idx, 4) || !aligned(val, 4) || (lse && !aligned(lse, 4))) return JF_ERR_ALIGN;
+    TopkPlan p;
+    plan_topk(p, R, V, k, dtype);
+    if (p.chunks == 0) return JF_ERR_UNSUPPORTED;
+    if (topk_workspace_bytes(p) > kTopkScratchBytes) return JF_ERR_WORKSPACE;
+    void *scratch_ptr = nullptr;
+    if (topk_scratch(&scratch_ptr) != hipSuccess) return JF_ERR_HIP;
+    hipError_t e = launch_topk(p, logits, ld, dtype, idx, val, lse, scratch_ptr, (hipStream_t)stream);
     return e == hipSuccess ? JF_OK : JF_ERR_HIP;
 }
 

@@ -162,6 +162,11 @@ void plan_topk(TopkPlan &p, int64_t R, int64_t V, int k, jf_dtype dtype);
 size_t topk_workspace_bytes(const TopkPlan &p);
 hipError_t launch_topk(const TopkPlan &p, const void *logits, int64_t ld, jf_dtype dtype,
                        int32_t *idx, float *val, float *lse, void *workspace, hipStream_t s);
+// The allocation-free top-k's static device scratch: its size, and its
+// address on the current device (taken once per device).
+constexpr size_t kTopkScratchBytes = JF_NODE_TOPK_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+hipError_t topk_scratch(void **ptr);
 
 struct FusePlan {
     int64_t M, H_in, H_out;

@@ -19,6 +19,7 @@
 // Candidates are 64-bit keys: high word = order-preserving image of the fp32
 // value (-0 folded onto +0), low word = ~index, so that a larger key is a
 // better candidate and keys are unique within a row.
+#include <mutex>
 #include <type_traits>
 
 #include "jf_internal.h"
@@ -737,6 +738,34 @@ hipError_t launch_topk(const TopkPlan &p, const void *logits, int64_t ld, jf_dty
     }
 #undef JF_TOPK2
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free entry point (jf_node_topk_noalloc): the
+// stage-1 candidates and (max, sum-exp) pairs live in this file-scope device
+// array instead of a caller's workspace.  Each device holds its own copy for
+// the life of the process.  Its address is taken once per device with
+// hipGetSymbolAddress, with that device current; host code passes only that
+// address to kernels (the array's name is a host-side stand-in).  Nothing in
+// it needs to start at zero: stage 1 writes every slot that stage 2 reads.
+static __device__ __align__(256) unsigned char scratch[kTopkScratchBytes];
+
+hipError_t topk_scratch(void **ptr) {
+    static std::mutex mu;
+    static void *per_device[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!per_device[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        per_device[dev] = p;
+    }
+    *ptr = per_device[dev];
+    return hipSuccess;
 }
 
 }  // namespace jf

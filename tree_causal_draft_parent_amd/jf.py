@@ -27,8 +27,8 @@ EXPORTS = ("jf_status_string", "jf_abi_version", "jf_tree_mask_build",
            "jf_fuse_proj_workspace_size", "jf_fuse_proj", "jf_fuse_proj_workspace_size_cus",
            "jf_fuse_proj_cus", "jf_tree_attn_workspace_size",
            "jf_tree_attn_fwd", "jf_tree_attn_workspace_size_cus", "jf_tree_attn_fwd_cus",
-           "jf_node_topk_workspace_size", "jf_node_topk", "jf_path_scores", "jf_tree_expand",
-           "jf_tree_accept", "jf_tree_rope", "jf_rmsnorm", "jf_swiglu")
+           "jf_node_topk_workspace_size", "jf_node_topk", "jf_node_topk_noalloc", "jf_path_scores",
+           "jf_tree_expand", "jf_tree_accept", "jf_tree_rope", "jf_rmsnorm", "jf_swiglu")
 
 _lib = None
 
@@ -79,6 +79,8 @@ def lib():
     L.jf_node_topk_workspace_size.restype = SZ
     L.jf_node_topk.argtypes = [P, I64, I64, I64, ctypes.c_int, I32, P, P, P, P, SZ, P]
     L.jf_node_topk.restype = ctypes.c_int
+    L.jf_node_topk_noalloc.argtypes = [P, I64, I64, I64, ctypes.c_int, I32, P, P, P, P]
+    L.jf_node_topk_noalloc.restype = ctypes.c_int
     L.jf_path_scores.argtypes = [P, P, I32, I32, P, P, P]
     L.jf_path_scores.restype = ctypes.c_int
     L.jf_tree_expand.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, P, P, P, P, P]
@@ -273,6 +275,30 @@ def jf_node_topk(logits: torch.Tensor, k: int, with_lse: bool = True, idx=None, 
     st = lib().jf_node_topk(_p(logits), R, V, ld, _dtype_code(logits), k, _p(idx), _p(val), _p(lse),
                             _p(workspace), ws_bytes, _stream(stream))
     _check("jf_node_topk", st)
+    return idx, val, lse
+
+
+# JF_NODE_TOPK_SCRATCH_BYTES of include/jf.h
+NODE_TOPK_SCRATCH_BYTES = 4 << 20
+
+
+def jf_node_topk_noalloc(logits: torch.Tensor, k: int, idx: torch.Tensor, val: torch.Tensor,
+                         lse: Optional[torch.Tensor] = None, stream=None):
+    """jf_node_topk without a workspace: the library's static per-GPU scratch
+    (calls that overlap on one GPU race).  The outputs are the caller's:
+    idx [R, k] int32, val [R, k] fp32, lse [R] fp32 or None."""
+    if logits.stride(1) != 1:
+        raise ValueError("logits rows must be contiguous")
+    R, V = logits.shape
+    for n, t, dt in (("idx", idx, torch.int32), ("val", val, torch.float32)):
+        _contig(n, t)
+        if t.shape != (R, k) or t.dtype != dt:
+            raise ValueError(f"{n} must be [R, k] {dt}")
+    if lse is not None and (lse.shape != (R,) or lse.dtype != torch.float32):
+        raise ValueError("lse must be [R] float32")
+    st = lib().jf_node_topk_noalloc(_p(logits), R, V, logits.stride(0), _dtype_code(logits), k,
+                                    _p(idx), _p(val), _p(lse), _stream(stream))
+    _check("jf_node_topk_noalloc", st)
     return idx, val, lse
 
 
