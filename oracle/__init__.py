@@ -71,13 +71,13 @@ def _load():
     lib = ctypes.CDLL(_SO)
     P = ctypes.c_void_p
     I64 = ctypes.c_int64
-    lib.oracle_tree_mask.argtypes = [P, I64, I64, P, P, P]
+    lib.oracle_tree_mask.argtypes = [P, P, I64, I64, P, P, P]
     lib.oracle_tree_mask.restype = ctypes.c_int
     lib.oracle_fuse_proj.argtypes = [P, I64, I64, I64, P, I64, P]
     lib.oracle_fuse_proj.restype = None
     lib.oracle_fuse_proj_rows.argtypes = [P, I64, I64, I64, P, I64, P, I64, P]
     lib.oracle_fuse_proj_rows.restype = None
-    lib.oracle_tree_attn.argtypes = [P, P, P, P, P, P, P, I64, P, I64, I64, I64, I64, I64,
+    lib.oracle_tree_attn.argtypes = [P, P, P, P, P, P, P, I64, P, P, I64, I64, I64, I64, I64,
                                      I64, I64, ctypes.c_double, P, I64, P, P]
     lib.oracle_tree_attn.restype = ctypes.c_int
     lib.oracle_topk.argtypes = [P, I64, I64, I64, P, P, P]
@@ -110,15 +110,30 @@ def _c(a, dt):
     return np.ascontiguousarray(a, dtype=dt)
 
 
-def tree_mask(parent: np.ndarray):
-    """Ancestor bitmask [B, N, ceil(N/64)] uint64, depth [B, N], status, first bad row."""
+def tree_mask(parent: np.ndarray, node_off=None):
+    """Ancestor bitmask, depth, status, first bad row.
+
+    Uniform trees: parent [B, N] -> mask [B, N, ceil(N/64)] uint64, depth [B, N].
+    Packed trees: parent [T] with node_off [B+1] (sequence b owns rows
+    node_off[b] .. node_off[b+1]-1, parents local to it) -> mask [T, W] with
+    W = ceil(max count / 64), depth [T]."""
     parent = _c(parent, np.int32)
-    B, N = parent.shape
+    if node_off is None:
+        B, N = parent.shape
+        no, T = None, B * N
+    else:
+        no = _c(node_off, np.int64)
+        B, T = no.shape[0] - 1, parent.shape[0]
+        assert no[0] == 0 and no[-1] == T and np.all(np.diff(no) >= 1)
+        N = int(np.max(np.diff(no)))
     W = (N + 63) // 64
-    mask = np.zeros((B, N, W), dtype=np.uint64)
-    depth = np.zeros((B, N), dtype=np.int32)
+    mask = np.zeros((T, W), dtype=np.uint64)
+    depth = np.zeros((T,), dtype=np.int32)
     bad = np.zeros(1, dtype=np.int64)
-    st = _load().oracle_tree_mask(_p(parent), B, N, _p(mask), _p(depth), _p(bad))
+    st = _load().oracle_tree_mask(_p(parent), _p(no) if no is not None else None, B, N, _p(mask),
+                                  _p(depth), _p(bad))
+    if no is None:
+        mask, depth = mask.reshape(B, N, W), depth.reshape(B, N)
     return mask, depth, int(st), int(bad[0])
 
 
@@ -140,15 +155,33 @@ def fuse_proj(x: np.ndarray, w: np.ndarray, rows=None) -> np.ndarray:
     return y
 
 
+def fp8_e4m3_to_f64(codes: np.ndarray, scale: float = 1.0) -> np.ndarray:
+    """Values of OCP FP8 E4M3 codes (the "fn" variant: no infinities), times a
+    per-tensor scale, in float64.  Sign bit 7; exponent bits 6..3 with bias 7;
+    mantissa bits 2..0.  Exponent 0: subnormal m/8 * 2^-6; exponent 15 with
+    mantissa 7: NaN; otherwise (1 + m/8) * 2^(e - 7)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sgn = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2((e - 7).astype(np.float64)))
+    mag = np.where((e == 15) & (c & 0x7 == 7), np.nan, mag)
+    return sgn * mag * float(scale)
+
+
 def tree_attn(*, q, k_tree, v_tree, parent, k_cache, v_cache, block_table, prefix_len,
-              page_size, scale=None, rows=None):
+              page_size, scale=None, rows=None, node_off=None, bad_page_ok=False):
     """Tree attention in float64.
 
-    q [B,N,Hq,D], k_tree/v_tree [B,N,Hkv,D], k_cache/v_cache
-    [num_pages,page_size,Hkv,D] (all float64), parent [B,N] int32,
-    block_table [B,max_pages] int32, prefix_len [B] int32.
-    Returns (out, lse): [B,N,Hq,D] and [B,N,Hq], or [n_rows,D] and [n_rows]
-    for rows = flat ids (b*N+i)*Hq+h.
+    Uniform trees: q [B,N,Hq,D], k_tree/v_tree [B,N,Hkv,D], parent [B,N].
+    Packed trees (node_off [B+1] given): q [T,Hq,D], k_tree/v_tree [T,Hkv,D],
+    parent [T] with parents local to each sequence.
+    k_cache/v_cache [num_pages,page_size,Hkv,D] (all float64), block_table
+    [B,max_pages] int32, prefix_len [B] int32.
+    Returns (out, lse): shaped like q and q without D, or [n_rows,D] and
+    [n_rows] for rows = flat ids t*Hq+h over the tree rows t.  A bad page id
+    raises unless bad_page_ok, which returns (out, lse, bad) with that
+    position read as a zero key and a zero value.
     """
     q = _c(q, np.float64)
     k_tree = _c(k_tree, np.float64)
@@ -158,14 +191,22 @@ def tree_attn(*, q, k_tree, v_tree, parent, k_cache, v_cache, block_table, prefi
     parent = _c(parent, np.int32)
     block_table = _c(block_table, np.int32)
     prefix_len = _c(prefix_len, np.int32)
-    B, N, Hq, D = q.shape
-    Hkv = k_tree.shape[2]
+    if node_off is None:
+        B, N, Hq, D = q.shape
+        Hkv = k_tree.shape[2]
+        no, T = None, B * N
+    else:
+        no = _c(node_off, np.int64)
+        B, (T, Hq, D) = no.shape[0] - 1, q.shape
+        Hkv = k_tree.shape[1]
+        assert no[0] == 0 and no[-1] == T and np.all(np.diff(no) >= 1) and parent.shape == (T,)
+        N = int(np.max(np.diff(no)))
     num_pages = k_cache.shape[0]
     if scale is None:
         scale = 1.0 / np.sqrt(D)
     if rows is None:
-        out = np.empty((B, N, Hq, D), dtype=np.float64)
-        lse = np.empty((B, N, Hq), dtype=np.float64)
+        out = np.empty(q.shape, dtype=np.float64)
+        lse = np.empty(q.shape[:-1], dtype=np.float64)
         rp, nr = None, 0
     else:
         rows = _c(rows, np.int64)
@@ -174,8 +215,10 @@ def tree_attn(*, q, k_tree, v_tree, parent, k_cache, v_cache, block_table, prefi
         rp, nr = _p(rows), rows.shape[0]
     st = _load().oracle_tree_attn(
         _p(q), _p(k_tree), _p(v_tree), _p(parent), _p(k_cache), _p(v_cache),
-        _p(block_table), block_table.shape[1], _p(prefix_len), B, N, Hq, Hkv, D,
-        page_size, num_pages, float(scale), rp, nr, _p(out), _p(lse))
+        _p(block_table), block_table.shape[1], _p(prefix_len), _p(no) if no is not None else None,
+        B, N, Hq, Hkv, D, page_size, num_pages, float(scale), rp, nr, _p(out), _p(lse))
+    if bad_page_ok and st in (OK, BAD_PAGE):
+        return out, lse, st == BAD_PAGE
     if st != OK:
         raise ValueError(f"oracle_tree_attn status {st}")
     return out, lse

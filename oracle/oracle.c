@@ -49,28 +49,35 @@
  * anc(i) = {i} u anc(parent(i)), with parent -1 ending the walk at the prefix.
  * Row i of the mask holds bit j (word j/64, bit j%64) iff j is in anc(i);
  * depth(i) = |anc(i)|.  A row is bad when its walk meets a parent outside
- * [-1, N) or does not end within N steps (a cycle, including parent(i) == i).
- * Returns OR_BAD_TREE and the smallest flat index b*N+i of a bad row, or OR_OK.
+ * [-1, n_b) or does not end within n_b steps (a cycle, including
+ * parent(i) == i).
+ * Layout: sequence b owns rows node_off[b] .. node_off[b+1]-1 of parent [T],
+ * mask [T, W] and depth [T], with n_b = node_off[b+1] - node_off[b] nodes and
+ * parents given as indices local to the sequence; W = ceil(N / 64) for the
+ * largest count N.  node_off == NULL means n_b = N for every b (rows b*N+i).
+ * Returns OR_BAD_TREE and the smallest row of a bad node, or OR_OK.
  * ------------------------------------------------------------------------- */
-int oracle_tree_mask(const int32_t *parent, int64_t B, int64_t N,
+int oracle_tree_mask(const int32_t *parent, const int64_t *node_off, int64_t B, int64_t N,
                      uint64_t *mask, int32_t *depth, int64_t *first_bad)
 {
     int64_t W = (N + 63) / 64;
     int64_t bad = -1;
     for (int64_t b = 0; b < B; ++b) {
-        for (int64_t i = 0; i < N; ++i) {
-            uint64_t *row = mask + (b * N + i) * W;
+        const int64_t off = node_off ? node_off[b] : b * N;
+        const int64_t n = node_off ? node_off[b + 1] - node_off[b] : N;
+        for (int64_t i = 0; i < n; ++i) {
+            uint64_t *row = mask + (off + i) * W;
             for (int64_t w = 0; w < W; ++w) row[w] = 0;
             int64_t j = i, steps = 0;
             int ok = 1;
             while (j != -1) {
-                if (j < -1 || j >= N || steps >= N) { ok = 0; break; }
+                if (j < -1 || j >= n || steps >= n) { ok = 0; break; }
                 row[j / 64] |= (uint64_t)1 << (j % 64);
                 steps += 1;
-                j = parent[b * N + j];
+                j = parent[off + j];
             }
-            if (depth) depth[b * N + i] = ok ? (int32_t)steps : 0;
-            if (!ok && bad < 0) bad = b * N + i;
+            if (depth) depth[off + i] = ok ? (int32_t)steps : 0;
+            if (!ok && bad < 0) bad = off + i;
         }
     }
     if (first_bad) *first_bad = bad;
@@ -139,14 +146,22 @@ void oracle_fuse_proj_rows(const double *x, int64_t k, int64_t M, int64_t H_in,
  * node j of sequence b with j in anc(i), in increasing j.
  * s_t = scale * <q, k_t>;  M = max s_t;  w_t = exp(s_t - M);  Z = sum w_t;
  * out = sum_t w_t v_t / Z;  lse = M + log Z.
- * Returns OR_BAD_PAGE if a needed page id is outside [0, num_pages).
+ * A prefix position whose page id is outside [0, num_pages) reads as a zero
+ * key with a zero value (score 0, still counted in Z: the library's contract
+ * for a bad block-table entry) and the row reports OR_BAD_PAGE.
+ * Tree rows: sequence b owns rows node_off[b] .. node_off[b+1]-1 of q
+ * [T, Hq, D], k_tree / v_tree [T, Hkv, D] and parent [T] (parents local to
+ * the sequence); node_off == NULL means N rows per sequence (b*N + i).
  * ------------------------------------------------------------------------- */
 typedef struct {
     const double *q, *k_tree, *v_tree, *k_cache, *v_cache;
     const int32_t *parent, *block_table, *prefix_len;
+    const int64_t *node_off;
     int64_t max_pages, B, N, Hq, Hkv, D, page_size, num_pages;
     double scale;
 } attn_args;
+
+static const double kZeroRow[1024];
 
 static int attn_row(const attn_args *a, int64_t b, int64_t i, int64_t h,
                     double *out, double *lse_out, double *s_buf,
@@ -154,12 +169,21 @@ static int attn_row(const attn_args *a, int64_t b, int64_t i, int64_t h,
 {
     const int64_t D = a->D, Hkv = a->Hkv, G = a->Hq / a->Hkv;
     const int64_t g = h / G;
-    const double *qv = a->q + ((b * a->N + i) * a->Hq + h) * D;
+    const int64_t off = a->node_off ? a->node_off[b] : b * a->N;
+    const int64_t n = a->node_off ? a->node_off[b + 1] - a->node_off[b] : a->N;
+    const double *qv = a->q + ((off + i) * a->Hq + h) * D;
     const int64_t P = a->prefix_len[b];
+    int status = OR_OK;
     int64_t nk = 0;
     for (int64_t p = 0; p < P; ++p) {
         int64_t page = a->block_table[b * a->max_pages + p / a->page_size];
-        if (page < 0 || page >= a->num_pages) return OR_BAD_PAGE;
+        if (page < 0 || page >= a->num_pages) {
+            status = OR_BAD_PAGE;             /* zero key, zero value */
+            s_buf[nk] = 0.0;
+            v_buf[nk] = kZeroRow;
+            nk += 1;
+            continue;
+        }
         int64_t slot = p % a->page_size;
         const double *kv = a->k_cache + ((page * a->page_size + slot) * Hkv + g) * D;
         double dot = 0.0;
@@ -168,14 +192,14 @@ static int attn_row(const attn_args *a, int64_t b, int64_t i, int64_t h,
         v_buf[nk] = a->v_cache + ((page * a->page_size + slot) * Hkv + g) * D;
         nk += 1;
     }
-    const int32_t *par = a->parent + b * a->N;
-    for (int64_t j = 0; j < a->N; ++j) {
-        if (!is_ancestor(par, a->N, i, j)) continue;
-        const double *kv = a->k_tree + ((b * a->N + j) * Hkv + g) * D;
+    const int32_t *par = a->parent + off;
+    for (int64_t j = 0; j < n; ++j) {
+        if (!is_ancestor(par, n, i, j)) continue;
+        const double *kv = a->k_tree + ((off + j) * Hkv + g) * D;
         double dot = 0.0;
         for (int64_t d = 0; d < D; ++d) dot += qv[d] * kv[d];
         s_buf[nk] = a->scale * dot;
-        v_buf[nk] = a->v_tree + ((b * a->N + j) * Hkv + g) * D;
+        v_buf[nk] = a->v_tree + ((off + j) * Hkv + g) * D;
         nk += 1;
     }
     double M = -INFINITY;
@@ -188,39 +212,50 @@ static int attn_row(const attn_args *a, int64_t b, int64_t i, int64_t h,
         out[d] = acc / Z;
     }
     if (lse_out) *lse_out = M + log(Z);
-    return OR_OK;
+    return status;
 }
 
-/* All rows (rows == NULL: out is [B, N, Hq, D], lse [B, N, Hq]) or a list of
- * flat row ids r = (b*N + i)*Hq + h (out is [n_rows, D], lse [n_rows]). */
+/* All rows (rows == NULL: out is [T, Hq, D], lse [T, Hq]) or a list of flat
+ * row ids r = t*Hq + h over the tree rows t (out is [n_rows, D], lse
+ * [n_rows]).  Every row is computed; the status is OR_BAD_PAGE when some row
+ * met a bad page id. */
 int oracle_tree_attn(const double *q, const double *k_tree, const double *v_tree,
                      const int32_t *parent, const double *k_cache,
                      const double *v_cache, const int32_t *block_table,
-                     int64_t max_pages, const int32_t *prefix_len, int64_t B,
+                     int64_t max_pages, const int32_t *prefix_len,
+                     const int64_t *node_off, int64_t B,
                      int64_t N, int64_t Hq, int64_t Hkv, int64_t D,
                      int64_t page_size, int64_t num_pages, double scale,
                      const int64_t *rows, int64_t n_rows, double *out,
                      double *lse)
 {
-    if (B < 0 || N <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv != 0 ||
+    if (B < 0 || N <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || D > 1024 || Hq % Hkv != 0 ||
         page_size <= 0)
         return OR_INVALID;
     attn_args a = {q, k_tree, v_tree, k_cache, v_cache, parent, block_table,
-                   prefix_len, max_pages, B, N, Hq, Hkv, D, page_size, num_pages,
+                   prefix_len, node_off, max_pages, B, N, Hq, Hkv, D, page_size, num_pages,
                    scale};
-    int64_t Pmax = 0;
-    for (int64_t b = 0; b < B; ++b) if (prefix_len[b] > Pmax) Pmax = prefix_len[b];
-    const int64_t total = rows ? n_rows : B * N * Hq;
+    int64_t Pmax = 0, nmax = 0;
+    for (int64_t b = 0; b < B; ++b) {
+        if (prefix_len[b] > Pmax) Pmax = prefix_len[b];
+        const int64_t n = node_off ? node_off[b + 1] - node_off[b] : N;
+        if (n > nmax) nmax = n;
+    }
+    const int64_t T = node_off ? node_off[B] : B * N;
+    const int64_t total = rows ? n_rows : T * Hq;
     int status = OR_OK;
 #pragma omp parallel
     {
-        double *s_buf = (double *)malloc(sizeof(double) * (size_t)(Pmax + N + 1));
-        const double **v_buf = (const double **)malloc(sizeof(double *) * (size_t)(Pmax + N + 1));
+        double *s_buf = (double *)malloc(sizeof(double) * (size_t)(Pmax + nmax + 1));
+        const double **v_buf = (const double **)malloc(sizeof(double *) * (size_t)(Pmax + nmax + 1));
 #pragma omp for schedule(dynamic, 4)
         for (int64_t r = 0; r < total; ++r) {
-            int64_t flat = rows ? rows[r] : r;
-            int64_t h = flat % Hq, bi = flat / Hq;
-            int64_t i = bi % N, b = bi / N;
+            const int64_t flat = rows ? rows[r] : r;
+            const int64_t h = flat % Hq, t = flat / Hq;
+            /* the sequence owning tree row t */
+            int64_t b = node_off ? 0 : t / N;
+            if (node_off) while (b + 1 < B && node_off[b + 1] <= t) ++b;
+            const int64_t i = t - (node_off ? node_off[b] : b * N);
             int st = attn_row(&a, b, i, h, out + r * D, lse ? lse + r : NULL, s_buf, v_buf);
             if (st != OR_OK) {
 #pragma omp atomic write

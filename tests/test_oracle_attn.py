@@ -214,3 +214,109 @@ def test_rows_subset_matches_full():
     o2, l2 = oracle_attn(inp, rows=rows)
     assert np.array_equal(o2, out.reshape(-1, 16)[rows])
     assert np.array_equal(l2, lse.reshape(-1)[rows])
+
+
+# ---------------------------------------------------------------------------
+# Packed trees of different sizes, bad page ids, FP8 prefix caches
+
+def _packed_inputs(seed, counts, P, paged=True, kv_dtype=None, D=8, G=2, Hkv=2):
+    return synth.make_attn_inputs(B=len(counts), N=0, Hq=Hkv * G, Hkv=Hkv, D=D, dtype="bf16",
+                                  prefix_lens=P, page_size=4 if paged else 0,
+                                  shuffled_pages=paged, max_depth=5, branching=(1, 3),
+                                  seed=seed, node_counts=counts, kv_dtype=kv_dtype)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_packed_trees_match_path_brute_force(seed):
+    # each sequence of a ragged packed batch, through the brute force of its own
+    # root-to-node paths (the brute force knows nothing of the packing)
+    counts = [3, 11, 1, 7][: 2 + seed]
+    P = np.array([5, 0, 9, 13][: len(counts)], np.int32)
+    inp = _packed_inputs(200 + seed, counts, P)
+    f = attn_f64(inp)
+    out, lse = oracle.tree_attn(q=f["q"], k_tree=f["k_tree"], v_tree=f["v_tree"],
+                                parent=inp["parent"], k_cache=f["k_cache"], v_cache=f["v_cache"],
+                                block_table=inp["block_table"], prefix_len=P,
+                                page_size=inp["page_size"], node_off=inp["node_off"])
+    off = inp["node_off"]
+    for b, n in enumerate(counts):
+        sl = slice(off[b], off[b + 1])
+        bo, bl = path_attention(q=f["q"][None, sl], k_tree=f["k_tree"][None, sl],
+                                v_tree=f["v_tree"][None, sl], parent=inp["parent"][None, sl],
+                                k_cache=f["k_cache"], v_cache=f["v_cache"],
+                                block_table=inp["block_table"][b:b + 1], prefix_len=P[b:b + 1],
+                                page_size=inp["page_size"])
+        assert np.max(np.abs(out[sl] - bo[0])) < 1e-12
+        assert np.max(np.abs(lse[sl] - bl[0])) < 1e-12
+
+
+def test_packed_mask_rows_match_each_tree_alone():
+    counts = [5, 70, 1, 64]
+    inp = _packed_inputs(210, counts, np.array([1, 2, 3, 4], np.int32))
+    mask, depth, st, bad = oracle.tree_mask(inp["parent"], node_off=inp["node_off"])
+    assert st == oracle.OK and mask.shape == (sum(counts), 2)
+    off = inp["node_off"]
+    for b, n in enumerate(counts):
+        m1, d1, _, _ = oracle.tree_mask(inp["parent"][None, off[b]:off[b + 1]])
+        assert np.array_equal(mask[off[b]:off[b + 1], :m1.shape[2]], m1[0])
+        assert np.all(mask[off[b]:off[b + 1], m1.shape[2]:] == 0)
+        assert np.array_equal(depth[off[b]:off[b + 1]], d1[0])
+
+
+def test_packed_bad_tree_reports_its_row():
+    par = np.array([-1, 0, -1, 5, 0], np.int32)        # sequence 1 = rows 2..4; row 3's parent 5 >= 3
+    _, _, st, bad = oracle.tree_mask(par, node_off=np.array([0, 2, 5]))
+    assert st == oracle.BAD_TREE and bad == 3
+
+
+def test_bad_page_reads_as_zero_key_and_zero_value():
+    # a block-table entry out of range equals a valid page holding zeros there
+    inp = synth.make_attn_inputs(B=2, N=6, Hq=4, Hkv=2, D=8, dtype="bf16",
+                                 prefix_lens=np.array([10, 7], np.int32), page_size=4,
+                                 shuffled_pages=True, max_depth=4, branching=(1, 2), seed=220,
+                                 extra_pages=1)
+    f = attn_f64(inp)
+    zero_page = inp["num_pages"] - 1                  # the spare page, never in the table
+    f["k_cache"][zero_page] = 0.0
+    f["v_cache"][zero_page] = 0.0
+    bt_bad, bt_zero = inp["block_table"].copy(), inp["block_table"].copy()
+    bt_bad[0, 1] = 999
+    bt_zero[0, 1] = zero_page
+    kw = dict(q=f["q"], k_tree=f["k_tree"], v_tree=f["v_tree"], parent=inp["parent"],
+              k_cache=f["k_cache"], v_cache=f["v_cache"], prefix_len=inp["prefix_len"],
+              page_size=4)
+    o1, l1, flag = oracle.tree_attn(block_table=bt_bad, bad_page_ok=True, **kw)
+    o2, l2 = oracle.tree_attn(block_table=bt_zero, **kw)
+    assert flag
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    with pytest.raises(ValueError):
+        oracle.tree_attn(block_table=bt_bad, **kw)
+
+
+def test_fp8_decode_matches_the_library_and_known_values():
+    codes = np.arange(256, dtype=np.uint8)
+    got = oracle.fp8_e4m3_to_f64(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = (codes & 0x7F) == 0x7F
+    assert np.all(np.isnan(got[nan])) and np.all(np.isnan(ref[nan]))
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert got[0x38] == 1.0 and got[0x7E] == 448.0 and got[0x08] == 2.0 ** -6
+    assert got[0x01] == 2.0 ** -9 and got[0xB8] == -1.0 and got[0x3C] == 1.5
+    assert np.signbit(got[0x80]) and got[0x80] == 0.0
+    assert np.array_equal(oracle.fp8_e4m3_to_f64(codes[:0x7F], 0.25), got[:0x7F] * 0.25)
+
+
+def test_fp8_cache_attention_equals_decoded_values():
+    # the generator's codes decode within half an E4M3 step of the drawn values,
+    # and attention over an FP8 cache is attention over its decoded values
+    inp = _packed_inputs(230, [6, 9], np.array([12, 5], np.int32), kv_dtype="fp8")
+    assert inp["k_cache"].dtype == np.uint8 and inp["k_scale"] > 0
+    f = attn_f64(inp)
+    v = f["k_cache"] / inp["k_scale"]
+    assert np.max(np.abs(v)) <= 448.0
+    out, lse = oracle_attn(inp)
+    o2, l2 = oracle.tree_attn(q=f["q"], k_tree=f["k_tree"], v_tree=f["v_tree"],
+                              parent=inp["parent"], k_cache=f["k_cache"], v_cache=f["v_cache"],
+                              block_table=inp["block_table"], prefix_len=inp["prefix_len"],
+                              page_size=inp["page_size"], node_off=inp["node_off"])
+    assert np.array_equal(out, o2) and np.array_equal(lse, l2)

@@ -182,25 +182,76 @@ _STREAMS = ("tree", "prefix_len", "pages", "q", "k_tree", "v_tree", "k_cache",
             "v_cache", "x", "w", "logits")
 
 
+def f32_to_fp8_e4m3_codes(x: np.ndarray) -> np.ndarray:
+    """OCP FP8 E4M3 ("fn": no infinities, max 448) codes of float32 values,
+    rounded to nearest even and clamped to +-448; the data never holds NaN.
+    Code layout: sign bit 7, exponent bits 6..3 (bias 7), mantissa bits 2..0;
+    exponent 0 holds the subnormals m * 2^-9."""
+    x = np.asarray(x, dtype=np.float64)
+    sign = (np.signbit(x)).astype(np.uint8) << 7
+    a = np.minimum(np.abs(x), 448.0)
+    code = np.zeros(a.shape, dtype=np.int64)
+    sub = a < 2.0 ** -6
+    code[sub] = np.rint(a[sub] / 2.0 ** -9).astype(np.int64)         # 0..8 (8: the least normal)
+    f, E = np.frexp(a[~sub])                                           # a = f * 2^E, f in [0.5, 1)
+    e = E - 1                                                          # a in [2^e, 2^(e+1))
+    m = np.rint(a[~sub] / np.ldexp(1.0, e - 3)).astype(np.int64)       # 8..16, ties to even
+    up = m == 16
+    e, m = np.where(up, e + 1, e), np.where(up, 8, m)
+    code[~sub] = ((e + 7) << 3) | (m - 8)
+    return (code.astype(np.uint8) | sign).astype(np.uint8)
+
+
+def _draw_fp8(rng: np.random.Generator, shape) -> tuple:
+    """N(0, 1) values as E4M3 codes with one per-tensor scale (max |x| / 448):
+    value = decoded code * scale."""
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    scale = float(np.float32(max(float(np.max(np.abs(x))), 1e-30) / 448.0))
+    return f32_to_fp8_e4m3_codes(x.astype(np.float64) / scale), scale
+
+
 def make_attn_inputs(*, B: int, N: int, Hq: int, Hkv: int, D: int, dtype: str,
                      prefix_lens: Sequence[int], page_size: int = 0,
                      shuffled_pages: bool = False, parents: Optional[np.ndarray] = None,
                      max_depth: int = 16, branching: tuple = (1, 8),
-                     seed: int = 1234, extra_pages: int = 0) -> dict:
+                     seed: int = 1234, extra_pages: int = 0,
+                     node_counts: Optional[Sequence[int]] = None,
+                     kv_dtype: Optional[str] = None) -> dict:
     """Inputs of one tree-attention call.
 
     Prefix K/V live in a page pool ``[num_pages, page_size, Hkv, D]`` addressed
     through ``block_table[B, max_pages]`` (padding -1).  ``page_size == 0`` asks
     for the contiguous form: one page per sequence, ``page_size = max(P)``, page
     id = sequence id.
+
+    ``node_counts`` (one tree size per sequence) asks for packed trees:
+    sequence b owns rows ``node_off[b] .. node_off[b+1]-1`` of q ``[T, Hq, D]``,
+    k_tree / v_tree ``[T, Hkv, D]`` and parent ``[T]`` (parents local to the
+    sequence), and ``N`` becomes the largest count.  ``kv_dtype="fp8"`` draws
+    the prefix cache as E4M3 codes (uint8) with per-tensor scales ``k_scale``
+    and ``v_scale`` (value = decoded code * scale).
     """
     rng = _seeds(seed, _STREAMS)
     prefix_lens = np.asarray(prefix_lens, dtype=np.int32)
     assert prefix_lens.shape == (B,)
-    if parents is None:
-        parents = np.stack([best_first_tree(rng["tree"], N, max_depth, branching)
-                            for _ in range(B)]).astype(np.int32)
-    parents = np.asarray(parents, dtype=np.int32).reshape(B, N)
+    packed = node_counts is not None
+    if packed:
+        counts = np.asarray(node_counts, dtype=np.int64)
+        assert counts.shape == (B,) and np.all(counts >= 1)
+        node_off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+        N = int(counts.max())
+        if parents is None:
+            parents = np.concatenate([best_first_tree(rng["tree"], int(n), max_depth, branching)
+                                      for n in counts]).astype(np.int32)
+        parents = np.asarray(parents, dtype=np.int32).reshape(int(node_off[-1]))
+        rows = (int(node_off[-1]),)
+    else:
+        node_off = None
+        if parents is None:
+            parents = np.stack([best_first_tree(rng["tree"], N, max_depth, branching)
+                                for _ in range(B)]).astype(np.int32)
+        parents = np.asarray(parents, dtype=np.int32).reshape(B, N)
+        rows = (B, N)
     Pmax = int(prefix_lens.max()) if B > 0 else 0
     if page_size == 0:
         ps = max(Pmax, 1)
@@ -220,15 +271,21 @@ def make_attn_inputs(*, B: int, N: int, Hq: int, Hkv: int, D: int, dtype: str,
         for b in range(B):
             block_table[b, :npg[b]] = ids[off:off + npg[b]]
             off += npg[b]
-    q = _draw(rng["q"], (B, N, Hq, D), 1.0, dtype)
-    k_tree = _draw(rng["k_tree"], (B, N, Hkv, D), 1.0, dtype)
-    v_tree = _draw(rng["v_tree"], (B, N, Hkv, D), 1.0, dtype)
-    k_cache = _draw(rng["k_cache"], (num_pages, ps, Hkv, D), 1.0, dtype)
-    v_cache = _draw(rng["v_cache"], (num_pages, ps, Hkv, D), 1.0, dtype)
-    return dict(B=B, N=N, Hq=Hq, Hkv=Hkv, D=D, dtype=dtype, page_size=ps,
-                max_pages=max_pages, num_pages=num_pages, prefix_len=prefix_lens,
-                parent=parents, block_table=block_table, q=q, k_tree=k_tree,
-                v_tree=v_tree, k_cache=k_cache, v_cache=v_cache)
+    q = _draw(rng["q"], rows + (Hq, D), 1.0, dtype)
+    k_tree = _draw(rng["k_tree"], rows + (Hkv, D), 1.0, dtype)
+    v_tree = _draw(rng["v_tree"], rows + (Hkv, D), 1.0, dtype)
+    out = dict(B=B, N=N, Hq=Hq, Hkv=Hkv, D=D, dtype=dtype, page_size=ps,
+               max_pages=max_pages, num_pages=num_pages, prefix_len=prefix_lens,
+               parent=parents, block_table=block_table, q=q, k_tree=k_tree,
+               v_tree=v_tree, node_off=node_off, kv_dtype=kv_dtype or dtype)
+    if kv_dtype == "fp8":
+        out["k_cache"], out["k_scale"] = _draw_fp8(rng["k_cache"], (num_pages, ps, Hkv, D))
+        out["v_cache"], out["v_scale"] = _draw_fp8(rng["v_cache"], (num_pages, ps, Hkv, D))
+    else:
+        assert kv_dtype in (None, dtype)
+        out["k_cache"] = _draw(rng["k_cache"], (num_pages, ps, Hkv, D), 1.0, dtype)
+        out["v_cache"] = _draw(rng["v_cache"], (num_pages, ps, Hkv, D), 1.0, dtype)
+    return out
 
 
 def make_fuse_inputs(*, M: int, H_in: int, H_out: int, n_fused: int, dtype: str,
