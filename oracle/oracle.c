@@ -206,11 +206,15 @@ static int attn_row(const attn_args *a, int64_t b, int64_t i, int64_t h,
     for (int64_t t = 0; t < nk; ++t) if (s_buf[t] > M) M = s_buf[t];
     double Z = 0.0;
     for (int64_t t = 0; t < nk; ++t) { s_buf[t] = exp(s_buf[t] - M); Z += s_buf[t]; }
-    for (int64_t d = 0; d < D; ++d) {
-        double acc = 0.0;
-        for (int64_t t = 0; t < nk; ++t) acc += s_buf[t] * v_buf[t][d];
-        out[d] = acc / Z;
+    /* out[d] = (sum over t, in increasing t, of w_t v_t[d]) / Z; the value
+     * rows are walked one at a time (each out[d] still sums in t order) */
+    for (int64_t d = 0; d < D; ++d) out[d] = 0.0;
+    for (int64_t t = 0; t < nk; ++t) {
+        const double w = s_buf[t];
+        const double *vt = v_buf[t];
+        for (int64_t d = 0; d < D; ++d) out[d] += w * vt[d];
     }
+    for (int64_t d = 0; d < D; ++d) out[d] = out[d] / Z;
     if (lse_out) *lse_out = M + log(Z);
     return status;
 }
