@@ -43,16 +43,19 @@ typedef enum {
     JF_ERR_WORKSPACE = 4,    /* workspace missing or smaller than the size query */
     JF_ERR_BAD_TREE = 5,     /* device-side only: parent array is not a forest */
     JF_ERR_BAD_PAGE = 6,     /* device-side only: block-table entry out of range */
-    JF_ERR_HIP = 7           /* the HIP runtime refused a launch */
+    JF_ERR_HIP = 7,          /* the HIP runtime refused a launch */
+    JF_ERR_BAD_PREFIX = 8    /* device-side only: a device prefix length outside [0, bound] */
 } jf_status;
 
-typedef enum { JF_F32 = 0, JF_BF16 = 1 } jf_dtype;
+/* JF_FP8_E4M3: OCP FP8 E4M3 ("fn": no infinities, max 448), one byte per
+ * element, for prefix K/V caches only (with a per-tensor scale). */
+typedef enum { JF_F32 = 0, JF_BF16 = 1, JF_FP8_E4M3 = 2 } jf_dtype;
 
 /* Human-readable name of a status code (static storage). */
 const char *jf_status_string(int status);
 
 /* ABI version, bumped on any signature change. */
-int jf_abi_version(void);  /* 5 */
+int jf_abi_version(void);  /* 6 */
 
 /* --------------------------------------------------------------------------
  * jf_tree_mask_build -- ancestor bitmask of every tree node.
@@ -60,24 +63,33 @@ int jf_abi_version(void);  /* 5 */
  * Realises the visibility rule (a node sees the prefix and its ancestors;
  * JetFlow blog page, "What JetFlow Does Differently") as data: node i's row
  * has bit j set iff j is an ancestor of i, the node itself included.
- * parent[b][i] is the index of node i's parent within sequence b, or -1 when
+ * parent[i] is the index of node i's parent within its sequence, or -1 when
  * node i hangs directly off the prefix end (several such roots are allowed).
  * Node ids need not be in creation order.
  *
- *   parent     [B, N] int32.
- *   mask       [B, N, W] uint64, W = ceil(N / 64): bit (j % 64) of word j / 64
- *              of row (b, i) <=> j in anc(i).  Bits for j >= N are zero.
- *   depth      [B, N] int32, |anc(i)| (1 for a prefix child), or NULL.
+ * Tree layout (shared with jf_tree_attn_fwd):
+ *   node_off == NULL: every sequence has N nodes; sequence b owns rows
+ *              b*N .. b*N+N-1 of parent, mask and depth.
+ *   node_off   HOST [B+1] int32 (packed trees of different sizes, as a
+ *              serving batch carries): sequence b owns rows node_off[b] ..
+ *              node_off[b+1]-1, with n_b = node_off[b+1] - node_off[b] >= 1
+ *              nodes and parents local to the sequence; node_off[0] = 0,
+ *              N = the largest n_b, B <= 256.
+ *
+ *   parent     [T] int32, T = B*N or node_off[B].
+ *   mask       [T, W] uint64, W = ceil(N / 64): bit (j % 64) of word j / 64
+ *              of a node's row <=> j in anc(node).  Bits for j >= n_b are zero.
+ *   depth      [T] int32, |anc(i)| (1 for a prefix child), or NULL.
  *   seq_status [B] int32 or NULL: -1 when sequence b is a forest, otherwise
- *              the smallest node index i whose walk to the prefix meets a
- *              parent outside [-1, N) or does not end within N steps (a
+ *              the smallest local index i whose walk to the prefix meets a
+ *              parent outside [-1, n_b) or does not end within n_b steps (a
  *              cycle).  Rows of such nodes are zero and their depth is 0.
  *              Written on every call.
  *   B >= 1, 1 <= N <= 4096.
  * ------------------------------------------------------------------------ */
-jf_status jf_tree_mask_build(const int32_t *parent, int32_t B, int32_t N,
-                             uint64_t *mask, int32_t *depth,
-                             int32_t *seq_status, void *stream);
+jf_status jf_tree_mask_build(const int32_t *parent, const int32_t *node_off,
+                             int32_t B, int32_t N, uint64_t *mask,
+                             int32_t *depth, int32_t *seq_status, void *stream);
 
 /* --------------------------------------------------------------------------
  * jf_fuse_proj -- projection of hidden states fused from several layers.
@@ -135,24 +147,38 @@ jf_status jf_fuse_proj_cus(const void *const *x, int32_t k, int64_t M,
  * "block-level causal attention", arxivlens methodology and the arXiv page's
  * section 1).  s_t = scale * <q, k_t>,
  *     out = sum_t softmax(s)_t v_t,   lse = log sum_t exp(s_t).
+ * Trees are laid out as for jf_tree_mask_build (N nodes a sequence, or
+ * packed with node_off); T = B*N or node_off[B] tree rows.
  *
- *   q           [B, N, Hq, D]       dtype
- *   k_tree/v_tree [B, N, Hkv, D]    dtype (the tree nodes' own keys/values)
- *   mask        [B, N, ceil(N/64)]  from jf_tree_mask_build
- *   k_cache/v_cache [num_pages, page_size, Hkv, D] dtype: prefix pages.
+ *   q           [T, Hq, D]          dtype
+ *   k_tree/v_tree [T, Hkv, D]       dtype (the tree nodes' own keys/values)
+ *   mask        [T, ceil(N/64)]     from jf_tree_mask_build
+ *   k_cache/v_cache [num_pages, page_size, Hkv, D] kv_dtype: prefix pages.
+ *   kv_dtype    dtype, or JF_FP8_E4M3 with dtype JF_BF16: the cache holds
+ *               E4M3 codes and a key's (value's) element is its decoded code
+ *               times k_scale (v_scale); the scales are ignored otherwise.
  *   block_table [B, max_pages] int32 (device): page of prefix position p of
  *               sequence b is block_table[b][p / page_size], slot
  *               p % page_size.  A contiguous prefix is one page per sequence
  *               (page_size >= max P_b, block_table[b][0] = b).
- *   prefix_len  HOST [B] int32, P_b >= 0 (0: the nodes see only their path).
+ *   prefix_len  HOST [B] int32 >= 0: the prefix lengths, or, when
+ *               prefix_len_dev is given, their upper bounds.  The key splits
+ *               and the launch are planned from these host values.
+ *   prefix_len_dev DEVICE [B] int32 or NULL: the prefix lengths, read by the
+ *               kernels; each must lie in [0, prefix_len[b]] (one captured
+ *               launch then serves any lengths up to the bounds).  A value
+ *               outside is clamped into the range and status is set.
+ *   node_off    HOST [B+1] int32 or NULL: packed trees (jf_tree_mask_build).
  *   scale       softmax scale; <= 0 selects 1/sqrt(D).
- *   out         [B, N, Hq, D] dtype;  lse [B, N, Hq] fp32 or NULL.
- *   page_status one device int32 or NULL: set to JF_ERR_BAD_PAGE when a
- *               needed block-table entry is outside [0, num_pages) (that
- *               prefix position then reads as zero keys with zero values);
- *               never cleared by the library, so zero it once beforehand.
- *   dtype       JF_BF16: D == 128, MFMA split-KV path;  JF_F32: D <= 128,
- *               plain fp32 path (small problems).
+ *   out         [T, Hq, D] dtype;  lse [T, Hq] fp32 or NULL.
+ *   status      one device int32 or NULL, never cleared by the library (zero
+ *               it once beforehand): set to JF_ERR_BAD_PAGE when a needed
+ *               block-table entry is outside [0, num_pages) (that prefix
+ *               position then reads as a zero key with a zero value: score 0,
+ *               counted in the normaliser), or to JF_ERR_BAD_PREFIX for a
+ *               device prefix length outside its bound.
+ *   dtype       JF_BF16: D == 128, MFMA split-KV path with fp32 split
+ *               partials;  JF_F32: D <= 128, plain fp32 path (small problems).
  *   Limits: 1 <= B <= 256, 1 <= N <= 1024, Hq % Hkv == 0; on the bf16
  *   path each of q, k_tree, k_cache (and their value twins) must be smaller
  *   than 4 GiB - 256 bytes (32-bit buffer offsets), else JF_ERR_UNSUPPORTED.
@@ -160,17 +186,21 @@ jf_status jf_fuse_proj_cus(const void *const *x, int32_t k, int64_t M,
  * ------------------------------------------------------------------------ */
 size_t jf_tree_attn_workspace_size(int32_t B, int32_t N, int32_t Hq,
                                    int32_t Hkv, int32_t D, int32_t page_size,
-                                   const int32_t *prefix_len, jf_dtype dtype);
+                                   const int32_t *prefix_len,
+                                   const int32_t *node_off, jf_dtype dtype);
 jf_status jf_tree_attn_fwd(const void *q, const void *k_tree,
                            const void *v_tree, const uint64_t *mask,
                            const void *k_cache, const void *v_cache,
+                           jf_dtype kv_dtype, float k_scale, float v_scale,
                            int64_t num_pages, int32_t page_size,
                            const int32_t *block_table, int32_t max_pages,
-                           const int32_t *prefix_len, int32_t B, int32_t N,
+                           const int32_t *prefix_len,
+                           const int32_t *prefix_len_dev,
+                           const int32_t *node_off, int32_t B, int32_t N,
                            int32_t Hq, int32_t Hkv, int32_t D, float scale,
                            jf_dtype dtype, void *out, float *lse,
                            void *workspace, size_t workspace_bytes,
-                           int32_t *page_status, void *stream);
+                           int32_t *status, void *stream);
 
 /* --------------------------------------------------------------------------
  * jf_tree_attn_fwd_cus / jf_tree_attn_workspace_size_cus -- the same
@@ -184,18 +214,22 @@ jf_status jf_tree_attn_fwd(const void *q, const void *k_tree,
  * ------------------------------------------------------------------------ */
 size_t jf_tree_attn_workspace_size_cus(int32_t B, int32_t N, int32_t Hq,
                                        int32_t Hkv, int32_t D, int32_t page_size,
-                                       const int32_t *prefix_len, jf_dtype dtype,
+                                       const int32_t *prefix_len,
+                                       const int32_t *node_off, jf_dtype dtype,
                                        int32_t cus);
 jf_status jf_tree_attn_fwd_cus(const void *q, const void *k_tree,
                                const void *v_tree, const uint64_t *mask,
                                const void *k_cache, const void *v_cache,
+                               jf_dtype kv_dtype, float k_scale, float v_scale,
                                int64_t num_pages, int32_t page_size,
                                const int32_t *block_table, int32_t max_pages,
-                               const int32_t *prefix_len, int32_t B, int32_t N,
+                               const int32_t *prefix_len,
+                               const int32_t *prefix_len_dev,
+                               const int32_t *node_off, int32_t B, int32_t N,
                                int32_t Hq, int32_t Hkv, int32_t D, float scale,
                                jf_dtype dtype, void *out, float *lse,
                                void *workspace, size_t workspace_bytes,
-                               int32_t *page_status, int32_t cus, void *stream);
+                               int32_t *status, int32_t cus, void *stream);
 
 /* --------------------------------------------------------------------------
  * jf_node_topk -- the k best candidates of every node's draft distribution.

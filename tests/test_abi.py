@@ -31,7 +31,8 @@ def test_exports_every_declared_symbol():
 def test_status_strings_and_version():
     assert jf.status_string(0) == "JF_OK"
     assert jf.status_string(5) == "JF_ERR_BAD_TREE"
-    assert jf.lib().jf_abi_version() == 5
+    assert jf.lib().jf_abi_version() == 6
+    assert jf.status_string(8) == "JF_ERR_BAD_PREFIX"
 
 
 FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: every call below fails validation
@@ -40,24 +41,44 @@ FAKE_ODD = ctypes.c_void_p(0x10001)
 
 def test_mask_argument_errors():
     L = jf.lib()
-    assert L.jf_tree_mask_build(None, 1, 4, FAKE, None, None, None) == jf.JF_ERR_INVALID_ARG
-    assert L.jf_tree_mask_build(FAKE, 0, 4, FAKE, None, None, None) == jf.JF_ERR_INVALID_ARG
-    assert L.jf_tree_mask_build(FAKE, 1, 0, FAKE, None, None, None) == jf.JF_ERR_INVALID_ARG
-    assert L.jf_tree_mask_build(FAKE, 1, 5000, FAKE, None, None, None) == jf.JF_ERR_INVALID_ARG
-    assert L.jf_tree_mask_build(FAKE, 1, 4, FAKE_ODD, None, None, None) == jf.JF_ERR_ALIGN
+    assert L.jf_tree_mask_build(None, None, 1, 4, FAKE, None, None, None) == jf.JF_ERR_INVALID_ARG
+    assert L.jf_tree_mask_build(FAKE, None, 0, 4, FAKE, None, None, None) == jf.JF_ERR_INVALID_ARG
+    assert L.jf_tree_mask_build(FAKE, None, 1, 0, FAKE, None, None, None) == jf.JF_ERR_INVALID_ARG
+    assert L.jf_tree_mask_build(FAKE, None, 1, 5000, FAKE, None, None, None) == jf.JF_ERR_INVALID_ARG
+    assert L.jf_tree_mask_build(FAKE, None, 1, 4, FAKE_ODD, None, None, None) == jf.JF_ERR_ALIGN
+    # packed node offsets: start at 0, at least one node a sequence, N = the largest count
+    off = lambda *v: np.array(v, np.int32).ctypes.data_as(ctypes.c_void_p)
+    assert L.jf_tree_mask_build(FAKE, off(1, 3, 7), 2, 4, FAKE, None, None, None) == jf.JF_ERR_INVALID_ARG
+    assert L.jf_tree_mask_build(FAKE, off(0, 3, 3), 2, 3, FAKE, None, None, None) == jf.JF_ERR_INVALID_ARG
+    assert L.jf_tree_mask_build(FAKE, off(0, 3, 7), 2, 5, FAKE, None, None, None) == jf.JF_ERR_INVALID_ARG
+    assert L.jf_tree_mask_build(FAKE, off(0, 3, 9), 2, 4, FAKE, None, None, None) == jf.JF_ERR_INVALID_ARG
+    big = np.arange(302, dtype=np.int32).ctypes.data_as(ctypes.c_void_p)
+    assert L.jf_tree_mask_build(FAKE, big, 301, 1, FAKE, None, None, None) == jf.JF_ERR_UNSUPPORTED
 
 
 def _attn(L, **kw):
-    a = dict(q=FAKE, kt=FAKE, vt=FAKE, mask=FAKE, kc=FAKE, vc=FAKE, num_pages=4, page_size=16,
-             bt=FAKE, max_pages=4, pl=np.array([10, 20], np.int32), B=2, N=8, Hq=8, Hkv=2, D=128,
-             scale=0.0, dtype=jf.JF_BF16, out=FAKE, lse=None, ws=None, ws_bytes=0, ps=None)
+    a = dict(q=FAKE, kt=FAKE, vt=FAKE, mask=FAKE, kc=FAKE, vc=FAKE, kv=None, ks=1.0, vs=1.0,
+             num_pages=4, page_size=16, bt=FAKE, max_pages=4, pl=np.array([10, 20], np.int32),
+             pdev=None, no=None, B=2, N=8, Hq=8, Hkv=2, D=128, scale=0.0, dtype=jf.JF_BF16,
+             out=FAKE, lse=None, ws=None, ws_bytes=0, ps=None)
     a.update(kw)
-    pl = a["pl"]
+    if a["kv"] is None:
+        a["kv"] = a["dtype"]
+    pl, no = a["pl"], a["no"]
     plp = None if pl is None else pl.ctypes.data_as(ctypes.c_void_p)
-    return L.jf_tree_attn_fwd(a["q"], a["kt"], a["vt"], a["mask"], a["kc"], a["vc"], a["num_pages"],
-                              a["page_size"], a["bt"], a["max_pages"], plp, a["B"], a["N"], a["Hq"],
-                              a["Hkv"], a["D"], a["scale"], a["dtype"], a["out"], a["lse"], a["ws"],
-                              a["ws_bytes"], a["ps"], None)
+    nop = None if no is None else np.asarray(no, np.int32).ctypes.data_as(ctypes.c_void_p)
+    return L.jf_tree_attn_fwd(a["q"], a["kt"], a["vt"], a["mask"], a["kc"], a["vc"], a["kv"], a["ks"],
+                              a["vs"], a["num_pages"], a["page_size"], a["bt"], a["max_pages"], plp,
+                              a["pdev"], nop, a["B"], a["N"], a["Hq"], a["Hkv"], a["D"], a["scale"],
+                              a["dtype"], a["out"], a["lse"], a["ws"], a["ws_bytes"], a["ps"], None)
+
+
+def _ws(L, B, N, Hq, Hkv, D, page, pl, dtype, no=None, cus=None):
+    plp = np.asarray(pl, np.int32).ctypes.data_as(ctypes.c_void_p)
+    nop = None if no is None else np.asarray(no, np.int32).ctypes.data_as(ctypes.c_void_p)
+    if cus is None:
+        return L.jf_tree_attn_workspace_size(B, N, Hq, Hkv, D, page, plp, nop, dtype)
+    return L.jf_tree_attn_workspace_size_cus(B, N, Hq, Hkv, D, page, plp, nop, dtype, cus)
 
 
 def test_attn_argument_errors():
@@ -73,9 +94,18 @@ def test_attn_argument_errors():
     assert _attn(L, pl=np.array([10, 65], np.int32)) == jf.JF_ERR_INVALID_ARG  # > 4 pages of 16
     assert _attn(L, page_size=0) == jf.JF_ERR_INVALID_ARG
     assert _attn(L, q=FAKE_ODD) == jf.JF_ERR_ALIGN
+    assert _attn(L, pdev=FAKE_ODD) == jf.JF_ERR_ALIGN
+    assert _attn(L, kv=9) == jf.JF_ERR_INVALID_ARG
+    assert _attn(L, kv=jf.JF_F32) == jf.JF_ERR_UNSUPPORTED       # the cache must match q or be FP8
+    assert _attn(L, kv=jf.JF_FP8_E4M3, dtype=jf.JF_F32) == jf.JF_ERR_UNSUPPORTED
+    # packed trees: offsets from 0, every sequence has nodes, N is the largest count
+    assert _attn(L, no=[0, 3, 11]) != jf.JF_ERR_INVALID_ARG      # counts 3 and 8
+    assert _attn(L, no=[1, 3, 8]) == jf.JF_ERR_INVALID_ARG
+    assert _attn(L, no=[0, 0, 8]) == jf.JF_ERR_INVALID_ARG
+    assert _attn(L, no=[0, 3, 7]) == jf.JF_ERR_INVALID_ARG       # largest count 4 != N = 8
     # this shape splits the keys, so a workspace is required
     pl = np.array([4096, 4096], np.int32)
-    need = L.jf_tree_attn_workspace_size(2, 256, 32, 8, 128, 4096, pl.ctypes.data_as(ctypes.c_void_p), 1)
+    need = _ws(L, 2, 256, 32, 8, 128, 4096, pl, 1)
     assert need > 0
     assert _attn(L, pl=pl, N=256, Hq=32, Hkv=8, max_pages=1, page_size=4096,
                  ws=FAKE, ws_bytes=need - 1) == jf.JF_ERR_WORKSPACE
@@ -83,15 +113,19 @@ def test_attn_argument_errors():
 
 def test_workspace_sizes_are_host_side_and_consistent():
     L = jf.lib()
-    pl = np.array([4096], np.int32).ctypes.data_as(ctypes.c_void_p)
-    a = L.jf_tree_attn_workspace_size(1, 256, 32, 8, 128, 4096, pl, 1)
+    a = _ws(L, 1, 256, 32, 8, 128, 4096, [4096], 1)
     assert a % 4 == 0
-    assert L.jf_tree_attn_workspace_size(1, 256, 32, 8, 128, 4096, pl, 0) == 0  # fp32 path: no splits
-    assert L.jf_tree_attn_workspace_size(1, 256, 32, 7, 128, 4096, pl, 1) == 0  # invalid -> 0
+    assert _ws(L, 1, 256, 32, 8, 128, 4096, [4096], 0) == 0    # fp32 path: no splits
+    assert _ws(L, 1, 256, 32, 7, 128, 4096, [4096], 1) == 0    # invalid -> 0
     assert L.jf_node_topk_workspace_size(256, 151936, 8) > 0
     assert L.jf_node_topk_workspace_size(4, 10, 65) == 0
     assert L.jf_fuse_proj_workspace_size(256, 4096, 3, 4096, 1) >= 0
     assert L.jf_fuse_proj_workspace_size(256, 100, 3, 4096, 1) == 0  # H_in % 64 != 0
+
+
+def _attn_ws_bytes(items):
+    rows = items * 256                      # fp32 O / l rows of 128 + one fp32 lse, per work item
+    return rows * 128 * 4 + rows * 4
 
 
 def test_attn_plan_for_fewer_compute_units():
@@ -100,15 +134,25 @@ def test_attn_plan_for_fewer_compute_units():
     # tiles) 192 units give splits of 12 blocks (6 a sequence) instead of 9
     # (8 a sequence), so the partials take 6/8 of the bytes
     L = jf.lib()
-    pl = np.array([4096], np.int32).ctypes.data_as(ctypes.c_void_p)
-    full = L.jf_tree_attn_workspace_size(1, 256, 32, 8, 128, 4096, pl, 1)
-    assert L.jf_tree_attn_workspace_size_cus(1, 256, 32, 8, 128, 4096, pl, 1, 0) == full
-    assert L.jf_tree_attn_workspace_size_cus(1, 256, 32, 8, 128, 4096, pl, 1, 100000) == full
-    rows8, rows6 = 8 * 8 * 1024, 6 * 8 * 1024
-    assert full == (rows8 * 128 * 2 + 255) // 256 * 256 + rows8 * 4
-    part = L.jf_tree_attn_workspace_size_cus(1, 256, 32, 8, 128, 4096, pl, 1, 192)
-    assert part == (rows6 * 128 * 2 + 255) // 256 * 256 + rows6 * 4
-    assert L.jf_tree_attn_workspace_size_cus(1, 256, 32, 7, 128, 4096, pl, 1, 192) == 0  # invalid -> 0
+    full = _ws(L, 1, 256, 32, 8, 128, 4096, [4096], 1)
+    assert _ws(L, 1, 256, 32, 8, 128, 4096, [4096], 1, cus=0) == full
+    assert _ws(L, 1, 256, 32, 8, 128, 4096, [4096], 1, cus=100000) == full
+    assert full == _attn_ws_bytes(8 * 8 * 4)
+    assert _ws(L, 1, 256, 32, 8, 128, 4096, [4096], 1, cus=192) == _attn_ws_bytes(6 * 8 * 4)
+    assert _ws(L, 1, 256, 32, 7, 128, 4096, [4096], 1, cus=192) == 0  # invalid -> 0
+
+
+def test_attn_plan_of_packed_trees():
+    # packed trees of 256 and 16 nodes (4 and 1 query tiles of 256 rows per KV
+    # head) are planned together: 68 and 65 key blocks, 8 KV heads -> 2696
+    # block units over 256 compute units; the workspace is whole work items
+    L = jf.lib()
+    packed = _ws(L, 2, 256, 32, 8, 128, 4096, [4096, 4096], 1, no=[0, 256, 272])
+    assert packed > 0 and packed % _attn_ws_bytes(1) == 0
+    # one compute unit's worth of splits: every (sequence, head, tile) unsplit
+    assert _ws(L, 2, 256, 32, 8, 128, 4096, [4096, 4096], 1, no=[0, 256, 272], cus=1) == 0
+    # invalid offsets -> 0
+    assert _ws(L, 2, 256, 32, 8, 128, 4096, [4096, 4096], 1, no=[0, 256, 256]) == 0
 
 
 def test_fuse_plan_for_fewer_compute_units():

@@ -16,28 +16,26 @@ from tree_causal_draft_parent_amd import jf, synth
 pytestmark = pytest.mark.gpu
 
 
-def run_gpu(inp, page_status=None, cus=0):
+def run_gpu(inp, status=None, cus=0, prefix_len=None, prefix_dev=None):
+    """The mask and the attention on the GPU.  prefix_len: host lengths (or
+    bounds when prefix_dev, a host array of device lengths, is given)."""
     d = upload_attn(inp)
-    mask, _, st = jf.jf_tree_mask_build(d["parent"])
+    no = inp.get("node_off")
+    mask, _, st = jf.jf_tree_mask_build(d["parent"], node_off=no)
+    pd = None if prefix_dev is None else dev_tensor(np.asarray(prefix_dev, np.int32))
     out, lse = jf.jf_tree_attn_fwd(d["q"], d["k_tree"], d["v_tree"], mask, d["k_cache"],
-                                   d["v_cache"], d["block_table"], inp["prefix_len"],
-                                   page_status=page_status, cus=cus)
+                                   d["v_cache"], d["block_table"],
+                                   inp["prefix_len"] if prefix_len is None else prefix_len,
+                                   status=status, cus=cus, prefix_len_dev=pd, node_off=no,
+                                   k_scale=inp.get("k_scale", 1.0), v_scale=inp.get("v_scale", 1.0))
     torch.cuda.synchronize()
     assert np.all(st.cpu().numpy() == -1)
     return host_f64(out), host_f64(lse)
 
 
-def compare(inp, rows=None, label="", cus=0):
-    B, N, Hq, D = inp["q"].shape
-    say(f"attn {label}: B={B} N={N} Hq={Hq} Hkv={inp['k_tree'].shape[2]} D={D} "
-        f"P={list(inp['prefix_len'][:4])} page={inp['page_size']} dtype={inp['dtype']} "
-        f"rows={'all' if rows is None else len(rows)} cus={cus}")
-    out, lse = run_gpu(inp, cus=cus)
-    ro, rl = oracle_attn(inp, rows=rows)
-    go = out.reshape(-1, D) if rows is None else out.reshape(-1, D)[rows]
-    gl = lse.reshape(-1) if rows is None else lse.reshape(-1)[rows]
-    ro = ro.reshape(-1, D)
-    rl = rl.reshape(-1)
+def check(inp, go, gl, ro, rl):
+    D = inp["D"]
+    go, gl, ro, rl = go.reshape(-1, D), gl.reshape(-1), ro.reshape(-1, D), rl.reshape(-1)
     err = np.max(np.abs(go - ro))
     lerr = np.max(np.abs(gl - rl))
     if inp["dtype"] == "f32":
@@ -48,7 +46,43 @@ def compare(inp, rows=None, label="", cus=0):
         assert rel_rms(go, ro) <= 1e-2, rel_rms(go, ro)
         assert lerr <= 2e-2, lerr
         assert rel_rms(gl, rl) <= 1e-2
+
+
+def compare(inp, rows=None, label="", cus=0, prefix_dev=None):
+    D = inp["D"]
+    say(f"attn {label}: B={inp['B']} N={inp['N']} Hq={inp['Hq']} Hkv={inp['Hkv']} D={D} "
+        f"P={list(inp['prefix_len'][:4])} page={inp['page_size']} dtype={inp['dtype']} "
+        f"kv={inp.get('kv_dtype')} packed={inp.get('node_off') is not None} "
+        f"rows={'all' if rows is None else len(rows)} cus={cus} dev_prefix={prefix_dev is not None}")
+    out, lse = run_gpu(inp, cus=cus, prefix_dev=prefix_dev)
+    real = inp["prefix_len"] if prefix_dev is None else np.asarray(prefix_dev, np.int32)
+    ro, rl = oracle_attn(inp, rows=rows, prefix_len=real)
+    go = out.reshape(-1, D) if rows is None else out.reshape(-1, D)[rows]
+    gl = lse.reshape(-1) if rows is None else lse.reshape(-1)[rows]
+    check(inp, go, gl, ro, rl)
     return out, lse
+
+
+def tile_rows(inp, extra, seed):
+    """Flat rows (t*Hq + h) covering every (sequence, KV head, query tile of
+    256 rows) at least once -- so every split of every work item feeds a
+    compared output -- plus `extra` uniform draws."""
+    rng = np.random.default_rng(seed)
+    B, Hq, Hkv = inp["B"], inp["Hq"], inp["Hkv"]
+    G = Hq // Hkv
+    no = inp.get("node_off")
+    off = no if no is not None else np.arange(B + 1) * inp["N"]
+    rows = []
+    for b in range(B):
+        n = int(off[b + 1] - off[b])
+        for g in range(Hkv):
+            for t0 in range(0, n * G, 256):
+                r = int(rng.integers(t0, min(t0 + 256, n * G)))       # query row of the tile
+                node, hq = r // G, g * G + r % G
+                rows.append((int(off[b]) + node) * Hq + hq)
+    T = int(off[-1])
+    rows += list(rng.choice(T * Hq, size=min(extra, T * Hq), replace=False))
+    return np.unique(np.asarray(rows, np.int64))
 
 
 def test_tiny_fp32_workload():
@@ -103,8 +137,25 @@ def test_bad_page_is_flagged_without_fault():
                                  page_size=16, seed=1)
     inp["block_table"][1, 0] = inp["num_pages"] + 5   # out of range, caught by the kernel
     ps = torch.zeros(1, dtype=torch.int32, device="cuda:0")
-    run_gpu(inp, page_status=ps)
+    run_gpu(inp, status=ps)
     assert int(ps.item()) == jf.JF_ERR_BAD_PAGE
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64)])
+@pytest.mark.parametrize("paged", [False, True])
+def test_bad_page_output_matches_zero_key_contract(dtype, D, paged):
+    # a block-table entry out of range reads as a zero key with a zero value
+    # (score 0, counted in the normaliser) on both dtypes, as the oracle says
+    inp = synth.make_attn_inputs(B=2, N=8, Hq=4, Hkv=1, D=D, dtype=dtype, prefix_lens=[40, 20],
+                                 page_size=16 if paged else 0, seed=2)
+    inp["block_table"][1, 0] = inp["num_pages"] + 5
+    ps = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    say(f"bad page output: {dtype} paged={paged}")
+    out, lse = run_gpu(inp, status=ps)
+    assert int(ps.item()) == jf.JF_ERR_BAD_PAGE
+    ro, rl, flag = oracle_attn(inp, bad_page_ok=True)
+    assert flag
+    check(inp, out, lse, ro, rl)
 
 
 def test_qwen3_8b_low_budget_full():
@@ -124,22 +175,17 @@ def test_splits_planned_for_fewer_compute_units(cus):
 
 def test_serving_batch_fewer_compute_units_sampled():
     inp = synth.make_workload(3, parts=("attn",))["attn"]
-    compare(inp, rows=_sample_rows(inp, 256, 5), label="serving b32", cus=192)
+    compare(inp, rows=tile_rows(inp, 256, 5), label="serving b32", cus=192)
 
 
-def _sample_rows(inp, n, seed):
-    B, N, Hq, _ = inp["q"].shape
-    return np.sort(np.random.default_rng(seed).choice(B * N * Hq, size=n, replace=False))
-
-
-def test_serving_batch_full_size_sampled():
+def test_serving_batch_all_rows():
     inp = synth.make_workload(3, parts=("attn",))["attn"]
-    compare(inp, rows=_sample_rows(inp, 512, 3), label="serving b32")
+    compare(inp, label="serving b32")
 
 
-def test_qwen3_30b_shape_full_size_sampled():
+def test_qwen3_30b_shape_all_rows():
     inp = synth.make_workload(4, parts=("attn",))["attn"]
-    compare(inp, rows=_sample_rows(inp, 256, 4), label="qwen3-30b")
+    compare(inp, label="qwen3-30b")
 
 
 def test_score_jump_past_reference_maximum():
@@ -166,8 +212,7 @@ def test_maximum_tree_size():
     # N = 1024 nodes, the call's limit: 16 tree blocks, 1024 * 4 query rows
     inp = synth.make_attn_inputs(B=1, N=1024, Hq=8, Hkv=2, D=128, dtype="bf16", prefix_lens=[512],
                                  seed=1024)
-    rows = np.sort(np.random.default_rng(5).choice(1024 * 8, 1024, replace=False))
-    compare(inp, rows=rows, label="N=1024")
+    compare(inp, rows=tile_rows(inp, 1024, 5), label="N=1024")
 
 
 def test_maximum_batch():
@@ -177,3 +222,115 @@ def test_maximum_batch():
     inp = synth.make_attn_inputs(B=256, N=8, Hq=4, Hkv=1, D=128, dtype="bf16", prefix_lens=pl,
                                  page_size=16, shuffled_pages=True, seed=256)
     compare(inp, label="B=256")
+
+
+# ---------------------------------------------------------------------------
+# Serving variants: packed trees of different sizes, device prefix lengths
+
+def _serving_packed(seed, counts, kv_dtype=None, B=None):
+    B = len(counts)
+    P = np.random.default_rng(seed).integers(512, 8193, size=B).astype(np.int32)
+    return synth.make_attn_inputs(B=B, N=0, Hq=32, Hkv=8, D=128, dtype="bf16", prefix_lens=P,
+                                  page_size=16, shuffled_pages=True, seed=seed, node_counts=counts,
+                                  kv_dtype=kv_dtype)
+
+
+def test_packed_serving_batch_mixed_tree_sizes():
+    # a serving-shaped batch (32 sequences, prefixes U[512, 8192], shuffled
+    # 16-token pages) whose trees have 16, 64 or 256 nodes
+    counts = np.random.default_rng(40).choice([16, 64, 256], size=32)
+    inp = _serving_packed(41, counts)
+    compare(inp, rows=tile_rows(inp, 4096, 6), label="packed serving 16/64/256")
+
+
+@pytest.mark.parametrize("counts", [[1, 64, 3, 130], [256, 1], [100, 100, 7]])
+def test_packed_small_batches_all_rows(counts):
+    P = np.array([0, 64, 65, 700][: len(counts)], np.int32)
+    inp = synth.make_attn_inputs(B=len(counts), N=0, Hq=8, Hkv=2, D=128, dtype="bf16",
+                                 prefix_lens=P, page_size=16, shuffled_pages=True, seed=42,
+                                 node_counts=counts)
+    compare(inp, label=f"packed {counts}")
+
+
+def test_packed_fp32_path():
+    inp = synth.make_attn_inputs(B=3, N=0, Hq=6, Hkv=3, D=64, dtype="f32", prefix_lens=[0, 17, 150],
+                                 page_size=16, shuffled_pages=True, seed=43, node_counts=[5, 20, 1])
+    compare(inp, label="packed fp32")
+
+
+def test_packed_equals_uniform_when_counts_are_equal():
+    # the same trees through both layouts, bit for bit
+    a = synth.make_attn_inputs(B=3, N=64, Hq=8, Hkv=2, D=128, dtype="bf16",
+                               prefix_lens=[100, 2000, 4000], page_size=16, shuffled_pages=True,
+                               seed=44)
+    b = dict(a)
+    b["node_off"] = np.array([0, 64, 128, 192], np.int64)
+    for key in ("q", "k_tree", "v_tree", "parent"):
+        b[key] = a[key].reshape((192,) + a[key].shape[2:])
+    oa, la = run_gpu(a)
+    ob, lb = run_gpu(b)
+    assert np.array_equal(oa.reshape(ob.shape), ob) and np.array_equal(la.reshape(lb.shape), lb)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_device_prefix_lengths_below_the_bounds(dtype):
+    # planned for the bounds, run at shorter device lengths (some reach a
+    # single split, some none of the prefix at all)
+    D = 128 if dtype == "bf16" else 64
+    inp = synth.make_attn_inputs(B=4, N=40, Hq=8, Hkv=2, D=D, dtype=dtype,
+                                 prefix_lens=[3000, 3000, 200, 1000], page_size=16,
+                                 shuffled_pages=True, seed=45)
+    compare(inp, rows=None, label="device prefix", prefix_dev=[2999, 64, 0, 1000])
+
+
+def test_one_graph_serves_two_prefix_length_vectors():
+    # one captured launch (planned for the bounds) replayed after the device
+    # lengths change: each replay matches the oracle at that replay's lengths
+    inp = synth.make_attn_inputs(B=3, N=0, Hq=32, Hkv=8, D=128, dtype="bf16",
+                                 prefix_lens=[4096, 2048, 1024], page_size=16, shuffled_pages=True,
+                                 seed=46, node_counts=[64, 16, 200])
+    d = upload_attn(inp)
+    no = inp["node_off"]
+    mask, _, _ = jf.jf_tree_mask_build(d["parent"], node_off=no)
+    pdev = dev_tensor(np.array([4096, 2048, 1024], np.int32))
+    out = torch.empty_like(d["q"])
+    lse = torch.empty(d["q"].shape[:-1], dtype=torch.float32, device="cuda")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    need = jf.jf_tree_attn_workspace_size(3, 200, 32, 8, 128, 16, inp["prefix_len"], jf.JF_BF16,
+                                          node_off=no)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+
+    def call():
+        jf.jf_tree_attn_fwd(d["q"], d["k_tree"], d["v_tree"], mask, d["k_cache"], d["v_cache"],
+                            d["block_table"], inp["prefix_len"], out=out, lse=lse, workspace=ws,
+                            status=st, prefix_len_dev=pdev, node_off=no)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for lens in ([4096, 2048, 1024], [17, 2048, 640], [3000, 0, 1]):
+        say(f"graph replay at device prefix lengths {lens}")
+        pdev.copy_(torch.tensor(lens, dtype=torch.int32))
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ro, rl = oracle_attn(inp, prefix_len=np.array(lens, np.int32))
+        check(inp, host_f64(out), host_f64(lse), ro, rl)
+    assert int(st.item()) == 0
+
+
+def test_device_prefix_length_above_its_bound_is_clamped_and_flagged():
+    inp = synth.make_attn_inputs(B=2, N=16, Hq=8, Hkv=2, D=128, dtype="bf16",
+                                 prefix_lens=[500, 300], page_size=16, shuffled_pages=True, seed=47)
+    st = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    out, lse = run_gpu(inp, status=st, prefix_dev=[900, -3])
+    assert int(st.item()) == jf.JF_ERR_BAD_PREFIX
+    ro, rl = oracle_attn(inp, prefix_len=np.array([500, 0], np.int32))
+    check(inp, out, lse, ro, rl)

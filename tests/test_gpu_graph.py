@@ -56,7 +56,7 @@ def _setup(i):
         jf.jf_fuse_proj(d["xs"], d["w"], y=o["y"], workspace=ws["fuse"])
         jf.jf_tree_attn_fwd(d["q"], d["k_tree"], d["v_tree"], o["mask"], d["k_cache"], d["v_cache"],
                             d["block_table"], a["prefix_len"], out=o["out"], lse=o["lse"],
-                            workspace=ws["attn"], page_status=page_status)
+                            workspace=ws["attn"], status=page_status)
         jf.jf_node_topk(d["logits"], wl.topk, idx=o["idx"], val=o["val"], lse=o["rlse"],
                         workspace=ws["topk"])
 
@@ -86,7 +86,7 @@ def _setup(i):
             jf.jf_tree_mask_build(d["parent"], o["mask"], o["depth"], o["seq_status"])
             jf.jf_tree_attn_fwd(d["q"], d["k_tree"], d["v_tree"], o["mask"], d["k_cache"], d["v_cache"],
                                 d["block_table"], a["prefix_len"], out=o["out"], lse=o["lse"],
-                                workspace=aws, page_status=page_status, cus=attn_cus)
+                                workspace=aws, status=page_status, cus=attn_cus)
             main.wait_stream(s_side)
             if topk_apart:
                 main.wait_stream(s_third)

@@ -65,3 +65,31 @@ def test_bad_trees_are_reported_per_sequence():
         assert np.array_equal(depth[b], od[0])
         assert np.array_equal(mask[b][ok_rows], om[0][ok_rows])
         assert np.all(mask[b][~ok_rows] == 0)
+
+
+@pytest.mark.parametrize("counts", [[16, 64, 256, 1, 100], [4096, 3], [65] * 40])
+def test_packed_trees_of_different_sizes(counts):
+    rng = np.random.default_rng(len(counts))
+    par = np.concatenate([synth.best_first_tree(rng, n, 16, (1, 8)) for n in counts]).astype(np.int32)
+    no = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    say(f"mask packed: counts={counts[:6]} T={no[-1]}")
+    m, d, s = jf.jf_tree_mask_build(dev_tensor(par), node_off=no)
+    torch.cuda.synchronize()
+    om, od, ost, _ = oracle.tree_mask(par, node_off=no)
+    assert ost == oracle.OK
+    assert np.array_equal(m.cpu().numpy().view(np.uint64), om)
+    assert np.array_equal(d.cpu().numpy(), od)
+    assert np.all(s.cpu().numpy() == -1)
+
+
+def test_packed_bad_tree_reports_local_index():
+    # sequence 1 (rows 2..4): node 1's parent 5 is out of its range [-1, 3)
+    par = np.array([-1, 0, -1, 5, 0], np.int32)
+    m, d, s = jf.jf_tree_mask_build(dev_tensor(par), node_off=np.array([0, 2, 5]))
+    torch.cuda.synchronize()
+    assert list(s.cpu().numpy()) == [-1, 1]
+    om, od, ost, bad = oracle.tree_mask(par, node_off=np.array([0, 2, 5]))
+    assert ost == oracle.BAD_TREE and bad == 3
+    ok = od > 0
+    assert np.array_equal(m.cpu().numpy().view(np.uint64)[ok], om[ok])
+    assert np.array_equal(d.cpu().numpy(), od)

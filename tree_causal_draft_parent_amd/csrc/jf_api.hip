@@ -40,20 +40,39 @@ const char *jf_status_string(int status) {
         case JF_ERR_BAD_TREE: return "JF_ERR_BAD_TREE";
         case JF_ERR_BAD_PAGE: return "JF_ERR_BAD_PAGE";
         case JF_ERR_HIP: return "JF_ERR_HIP";
+        case JF_ERR_BAD_PREFIX: return "JF_ERR_BAD_PREFIX";
         default: return "JF_ERR_UNKNOWN";
     }
 }
 
-int jf_abi_version(void) { return 5; }
+int jf_abi_version(void) { return 6; }
 
-jf_status jf_tree_mask_build(const int32_t *parent, int32_t B, int32_t N, uint64_t *mask,
-                             int32_t *depth, int32_t *seq_status, void *stream) {
+// Packed node offsets: node_off[0] = 0, at least one node a sequence, at
+// most N (the largest count, which sets the mask width).
+static jf_status check_node_off(const int32_t *node_off, int32_t B, int32_t N) {
+    if (!node_off) return JF_OK;
+    if (B > kMaxBatch) return JF_ERR_UNSUPPORTED;
+    if (node_off[0] != 0) return JF_ERR_INVALID_ARG;
+    int32_t nmax = 0;
+    for (int b = 0; b < B; ++b) {
+        const int64_t n = (int64_t)node_off[b + 1] - node_off[b];
+        if (n < 1 || n > N) return JF_ERR_INVALID_ARG;
+        if (n > nmax) nmax = (int32_t)n;
+    }
+    return nmax == N ? JF_OK : JF_ERR_INVALID_ARG;
+}
+
+jf_status jf_tree_mask_build(const int32_t *parent, const int32_t *node_off, int32_t B, int32_t N,
+                             uint64_t *mask, int32_t *depth, int32_t *seq_status, void *stream) {
     if (!parent || !mask) return JF_ERR_INVALID_ARG;
     if (B < 1 || N < 1 || N > 4096) return JF_ERR_INVALID_ARG;
+    jf_status st = check_node_off(node_off, B, N);
+    if (st != JF_OK) return st;
     if (!aligned(parent, 4) || !aligned(mask, 8) || (depth && !aligned(depth, 4)) ||
         (seq_status && !aligned(seq_status, 4)))
         return JF_ERR_ALIGN;
-    hipError_t e = launch_tree_mask(parent, B, N, mask, depth, seq_status, (hipStream_t)stream);
+    hipError_t e = launch_tree_mask(parent, node_off, B, N, mask, depth, seq_status,
+                                    (hipStream_t)stream);
     return e == hipSuccess ? JF_OK : JF_ERR_HIP;
 }
 
@@ -124,7 +143,8 @@ jf_status jf_fuse_proj_cus(const void *const *x, int32_t k, int64_t M, int64_t H
 
 // ---------------------------------------------------------------------------
 static jf_status check_attn_dims(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
-                                 const int32_t *prefix_len, jf_dtype dtype) {
+                                 const int32_t *prefix_len, const int32_t *node_off,
+                                 jf_dtype dtype) {
     if (!prefix_len) return JF_ERR_INVALID_ARG;
     if (B < 1 || N < 1 || Hq < 1 || Hkv < 1 || D < 1) return JF_ERR_INVALID_ARG;
     if (Hq % Hkv != 0) return JF_ERR_INVALID_ARG;
@@ -134,78 +154,91 @@ static jf_status check_attn_dims(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, 
     if (dtype == JF_F32 && D > 128) return JF_ERR_UNSUPPORTED;
     for (int b = 0; b < B; ++b)
         if (prefix_len[b] < 0) return JF_ERR_INVALID_ARG;
-    return JF_OK;
+    return check_node_off(node_off, B, N);
 }
 
 size_t jf_tree_attn_workspace_size_cus(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
                                        int32_t page_size, const int32_t *prefix_len,
-                                       jf_dtype dtype, int32_t cus) {
-    if (check_attn_dims(B, N, Hq, Hkv, D, prefix_len, dtype) != JF_OK || page_size < 1) return 0;
+                                       const int32_t *node_off, jf_dtype dtype, int32_t cus) {
+    if (check_attn_dims(B, N, Hq, Hkv, D, prefix_len, node_off, dtype) != JF_OK || page_size < 1)
+        return 0;
     if (dtype == JF_F32) return 0;
     AttnPlan p;
-    plan_tree_attn(p, B, N, Hq, Hkv, D, page_size, prefix_len, dtype, cus);
+    plan_tree_attn(p, B, N, Hq, Hkv, D, page_size, prefix_len, node_off, dtype, cus);
     return tree_attn_workspace_bytes(p);
 }
 
 size_t jf_tree_attn_workspace_size(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
-                                   int32_t page_size, const int32_t *prefix_len, jf_dtype dtype) {
-    return jf_tree_attn_workspace_size_cus(B, N, Hq, Hkv, D, page_size, prefix_len, dtype, 0);
+                                   int32_t page_size, const int32_t *prefix_len,
+                                   const int32_t *node_off, jf_dtype dtype) {
+    return jf_tree_attn_workspace_size_cus(B, N, Hq, Hkv, D, page_size, prefix_len, node_off, dtype,
+                                           0);
 }
 
 jf_status jf_tree_attn_fwd(const void *q, const void *k_tree, const void *v_tree,
                            const uint64_t *mask, const void *k_cache, const void *v_cache,
-                           int64_t num_pages, int32_t page_size, const int32_t *block_table,
-                           int32_t max_pages, const int32_t *prefix_len, int32_t B, int32_t N,
-                           int32_t Hq, int32_t Hkv, int32_t D, float scale, jf_dtype dtype,
-                           void *out, float *lse, void *workspace, size_t workspace_bytes,
-                           int32_t *page_status, void *stream) {
-    return jf_tree_attn_fwd_cus(q, k_tree, v_tree, mask, k_cache, v_cache, num_pages, page_size,
-                                block_table, max_pages, prefix_len, B, N, Hq, Hkv, D, scale, dtype,
-                                out, lse, workspace, workspace_bytes, page_status, 0, stream);
+                           jf_dtype kv_dtype, float k_scale, float v_scale, int64_t num_pages,
+                           int32_t page_size, const int32_t *block_table, int32_t max_pages,
+                           const int32_t *prefix_len, const int32_t *prefix_len_dev,
+                           const int32_t *node_off, int32_t B, int32_t N, int32_t Hq, int32_t Hkv,
+                           int32_t D, float scale, jf_dtype dtype, void *out, float *lse,
+                           void *workspace, size_t workspace_bytes, int32_t *status,
+                           void *stream) {
+    return jf_tree_attn_fwd_cus(q, k_tree, v_tree, mask, k_cache, v_cache, kv_dtype, k_scale,
+                                v_scale, num_pages, page_size, block_table, max_pages, prefix_len,
+                                prefix_len_dev, node_off, B, N, Hq, Hkv, D, scale, dtype, out, lse,
+                                workspace, workspace_bytes, status, 0, stream);
 }
 
 jf_status jf_tree_attn_fwd_cus(const void *q, const void *k_tree, const void *v_tree,
                                const uint64_t *mask, const void *k_cache, const void *v_cache,
-                               int64_t num_pages, int32_t page_size, const int32_t *block_table,
-                               int32_t max_pages, const int32_t *prefix_len, int32_t B, int32_t N,
-                               int32_t Hq, int32_t Hkv, int32_t D, float scale, jf_dtype dtype,
-                               void *out, float *lse, void *workspace, size_t workspace_bytes,
-                               int32_t *page_status, int32_t cus, void *stream) {
+                               jf_dtype kv_dtype, float k_scale, float v_scale, int64_t num_pages,
+                               int32_t page_size, const int32_t *block_table, int32_t max_pages,
+                               const int32_t *prefix_len, const int32_t *prefix_len_dev,
+                               const int32_t *node_off, int32_t B, int32_t N, int32_t Hq,
+                               int32_t Hkv, int32_t D, float scale, jf_dtype dtype, void *out,
+                               float *lse, void *workspace, size_t workspace_bytes,
+                               int32_t *status, int32_t cus, void *stream) {
     if (!q || !k_tree || !v_tree || !mask || !k_cache || !v_cache || !block_table || !out)
         return JF_ERR_INVALID_ARG;
-    jf_status st = check_attn_dims(B, N, Hq, Hkv, D, prefix_len, dtype);
+    jf_status st = check_attn_dims(B, N, Hq, Hkv, D, prefix_len, node_off, dtype);
     if (st != JF_OK) return st;
+    if (kv_dtype != JF_F32 && kv_dtype != JF_BF16 && kv_dtype != JF_FP8_E4M3)
+        return JF_ERR_INVALID_ARG;
+    if (kv_dtype != dtype) return JF_ERR_UNSUPPORTED;
     if (page_size < 1 || max_pages < 1 || num_pages < 0) return JF_ERR_INVALID_ARG;
     for (int b = 0; b < B; ++b)
         if ((int64_t)prefix_len[b] > (int64_t)max_pages * page_size) return JF_ERR_INVALID_ARG;
     const size_t al = 16;
     if (!aligned(q, al) || !aligned(k_tree, al) || !aligned(v_tree, al) || !aligned(k_cache, al) ||
         !aligned(v_cache, al) || !aligned(out, al) || !aligned(mask, 8) || !aligned(block_table, 4) ||
-        (lse && !aligned(lse, 4)) || (page_status && !aligned(page_status, 4)))
+        (lse && !aligned(lse, 4)) || (status && !aligned(status, 4)) ||
+        (prefix_len_dev && !aligned(prefix_len_dev, 4)))
         return JF_ERR_ALIGN;
+    const int64_t T = node_off ? (int64_t)node_off[B] : (int64_t)B * N;
     if (dtype == JF_BF16) {
         // the bf16 kernel addresses each tensor with 32-bit buffer offsets
         const int64_t lim = 0xffffff00LL;
-        if (num_pages * page_size * (int64_t)Hkv * D * 2 > lim ||
-            (int64_t)B * N * Hq * D * 2 > lim || (int64_t)B * N * Hkv * D * 2 > lim)
+        if (num_pages * page_size * (int64_t)Hkv * D * 2 > lim || T * Hq * D * 2 > lim ||
+            T * Hkv * D * 2 > lim)
             return JF_ERR_UNSUPPORTED;
     }
     if (!(scale > 0.f)) scale = 1.f / sqrtf((float)D);
     AttnPlan p;
-    plan_tree_attn(p, B, N, Hq, Hkv, D, page_size, prefix_len, dtype, cus);
+    plan_tree_attn(p, B, N, Hq, Hkv, D, page_size, prefix_len, node_off, dtype, cus);
     hipError_t e;
     if (dtype == JF_BF16) {
         const size_t need = tree_attn_workspace_bytes(p);
         if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
             return JF_ERR_WORKSPACE;
         e = launch_tree_attn_bf16(p, q, k_tree, v_tree, mask, k_cache, v_cache, num_pages, page_size,
-                                  block_table, max_pages, scale, out, lse, workspace, page_status,
-                                  (hipStream_t)stream);
+                                  block_table, max_pages, prefix_len_dev, scale, out, lse, workspace,
+                                  status, (hipStream_t)stream);
     } else {
         e = launch_tree_attn_f32(p, (const float *)q, (const float *)k_tree, (const float *)v_tree,
                                  mask, (const float *)k_cache, (const float *)v_cache, num_pages,
-                                 page_size, block_table, max_pages, scale, (float *)out, lse,
-                                 page_status, (hipStream_t)stream);
+                                 page_size, block_table, max_pages, prefix_len_dev, scale,
+                                 (float *)out, lse, status, (hipStream_t)stream);
     }
     return e == hipSuccess ? JF_OK : JF_ERR_HIP;
 }

@@ -88,10 +88,12 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 int num_cus();
 
 // ----- launchers (host) ------------------------------------------------------
-hipError_t launch_tree_mask(const int32_t *parent, int B, int N, uint64_t *mask,
-                            int32_t *depth, int32_t *seq_status, hipStream_t s);
-
 constexpr int kMaxBatch = 256;
+
+// node_off: HOST [B+1] packed node offsets (B <= kMaxBatch), or NULL for N
+// nodes per sequence.
+hipError_t launch_tree_mask(const int32_t *parent, const int32_t *node_off, int B, int N,
+                            uint64_t *mask, int32_t *depth, int32_t *seq_status, hipStream_t s);
 
 hipError_t launch_path_scores(const int32_t *parent, const float *logp, int B, int N, float *score,
                               int32_t *seq_status, hipStream_t s);
@@ -120,36 +122,38 @@ hipError_t launch_tree_expand(const float *score, const int32_t *depth, const in
                               float *new_score, int32_t *new_depth, hipStream_t s);
 
 struct AttnPlan {
-    int B, N, Hq, Hkv, D, G, R, W;
-    int n_qt;            // query tiles per (sequence, kv head)
-    int tq;              // query rows per tile
+    int B, N, Hq, Hkv, D, G, W;    // N: the largest tree; W = ceil(N / 64) mask words a row
     int chunk_blocks;    // 64-key blocks per split
-    int n_tree_blocks;   // ceil(N / 64)
     int page_size;
-    int total_chunks;    // sum over sequences of splits
     int total_items;     // workgroups of the split kernel
-    bool any_split;      // some sequence has more than one split
-    int prefix_len[kMaxBatch];
-    int chunk_start[kMaxBatch + 1];
+    bool any_split;      // some sequence has more than one split (by the bounds)
+    int cap[kMaxBatch];              // planned prefix bound of each sequence
+    int node_off[kMaxBatch + 1];     // tree rows of sequence b: node_off[b] .. node_off[b+1]-1
+    int item_start[kMaxBatch + 1];   // first work item of sequence b
 };
-// cus: compute units the split plan fills (<= 0: all of the device's)
+// prefix_cap: HOST [B] prefix bounds (the lengths themselves when no device
+// lengths are given); node_off: HOST [B+1] packed tree rows or NULL (N a
+// sequence); cus: compute units the split plan fills (<= 0: all).
 void plan_tree_attn(AttnPlan &p, int B, int N, int Hq, int Hkv, int D, int page_size,
-                    const int32_t *prefix_len, jf_dtype dtype, int cus = 0);
+                    const int32_t *prefix_cap, const int32_t *node_off, jf_dtype dtype,
+                    int cus = 0);
 size_t tree_attn_workspace_bytes(const AttnPlan &p);
 
 hipError_t launch_tree_attn_bf16(const AttnPlan &p, const void *q, const void *k_tree,
                                  const void *v_tree, const uint64_t *mask,
                                  const void *k_cache, const void *v_cache,
                                  int64_t num_pages, int page_size,
-                                 const int32_t *block_table, int max_pages, float scale,
+                                 const int32_t *block_table, int max_pages,
+                                 const int32_t *prefix_dev, float scale,
                                  void *out, float *lse, void *workspace,
-                                 int32_t *page_status, hipStream_t s);
+                                 int32_t *status, hipStream_t s);
 hipError_t launch_tree_attn_f32(const AttnPlan &p, const float *q, const float *k_tree,
                                 const float *v_tree, const uint64_t *mask,
                                 const float *k_cache, const float *v_cache,
                                 int64_t num_pages, int page_size,
-                                const int32_t *block_table, int max_pages, float scale,
-                                float *out, float *lse, int32_t *page_status,
+                                const int32_t *block_table, int max_pages,
+                                const int32_t *prefix_dev, float scale,
+                                float *out, float *lse, int32_t *status,
                                 hipStream_t s);
 
 struct TopkPlan {

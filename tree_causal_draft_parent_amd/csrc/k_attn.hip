@@ -44,9 +44,15 @@
 //     immediate.  V stays row-major: ds_read_b64_tr_b16 hands each lane four
 //     consecutive keys of one head-dim column, which is exactly the V^T
 //     operand layout.
-//   * Each split writes (O / l in bf16, log-sum-exp in fp32) partials; a merge
-//     kernel combines the splits of a row with LSE weights.  A sequence with
-//     one split writes the final output directly.
+//   * Each split writes (O / l, log-sum-exp) partials in fp32, 256 rows per
+//     work item; a merge kernel combines the splits of a row with LSE
+//     weights.  A sequence with one split writes the final output directly.
+//   * Serving batches: trees may be packed with a different node count per
+//     sequence (rows node_off[b] .. node_off[b+1]-1), and prefix lengths may
+//     come from device memory.  The host plans the splits and the grid from
+//     per-sequence prefix bounds; each workgroup reads the real length, and
+//     splits past it exit (the merge reads the same length), so one captured
+//     launch serves any lengths up to the bounds.
 #include "jf_internal.h"
 
 #include <vector>
@@ -75,31 +81,48 @@ struct AttnArgs {
     const uint16_t *q, *k_tree, *v_tree, *k_cache, *v_cache;
     const uint64_t *mask;
     const int32_t *block_table;
+    const int32_t *prefix_dev;   // device prefix lengths, or null (the bounds are the lengths)
     void *out;
     float *lse;
-    uint16_t *part_o;      // split partials O / l, bf16 (the output itself is bf16)
-    float *part_lse;
-    int32_t *page_status;
+    float *part_o;         // split partials O / l, fp32 [items * kTQ, kD]
+    float *part_lse;       // [items * kTQ]
+    int32_t *status;
     uint32_t q_bytes, tree_bytes, cache_bytes, mask_bytes;
     int64_t num_pages;
     int page_mode;  // 1: one page per sequence; 2: power-of-two pages >= 16; 0: other
-    int page_size, page_shift, max_pages, B, N, Hq, Hkv, G, R, W, n_qt, chunk_blocks,
-        n_tree_blocks, total_items;
+    int page_size, page_shift, max_pages, B, Hq, Hkv, G, W, chunk_blocks, total_items;
     float scale, c2, lazy_raw;
-    int prefix_len[kMaxBatch];
-    int chunk_start[kMaxBatch + 1];
+    int cap[kMaxBatch];              // planned prefix bound of each sequence
+    int node_off[kMaxBatch + 1];     // tree rows of sequence b: node_off[b] .. node_off[b+1]-1
+    int item_start[kMaxBatch + 1];   // first work item of sequence b
 };
 
 constexpr int kPageLds = 1024;     // page ids of one split staged in LDS
 
-__device__ __forceinline__ int find_seq(const AttnArgs &a, int cg) {
+// the sequence of work item `item`: the last b with item_start[b] <= item
+__device__ __forceinline__ int find_seq(const AttnArgs &a, int item) {
     int lo = 0, hi = a.B - 1;
     while (lo < hi) {
         int mid = (lo + hi + 1) >> 1;
-        if (a.chunk_start[mid] <= cg) lo = mid; else hi = mid - 1;
+        if (a.item_start[mid] <= item) lo = mid; else hi = mid - 1;
     }
     return lo;
 }
+
+// Prefix length of sequence b: the device value when given, clamped to the
+// planned bound [0, cap] (bad = true when it had to be clamped).
+__device__ __forceinline__ int prefix_of(const AttnArgs &a, int b, bool &bad) {
+    const int cap = a.cap[b];
+    if (!a.prefix_dev) return cap;
+    const int p = a.prefix_dev[b];
+    if (p < 0 || p > cap) {
+        bad = true;
+        return p < 0 ? 0 : cap;
+    }
+    return p;
+}
+
+__device__ __forceinline__ int div_up(int x, int y) { return (x + y - 1) / y; }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, uint32_t bytes) { return make_rsrc(p, bytes); }
 
@@ -108,9 +131,9 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 // Byte offset of (key row, 16-byte chunk) of block kb in its buffer, or kOob.
 // Prefix rows go through the split's page ids in LDS; tree rows index the
 // nodes' own K/V.  An out-of-range page id reads as zeros and is flagged.
-__device__ __forceinline__ uint32_t row_offset(const AttnArgs &a, const int *pages, int page0, int b,
-                                               int g, int P, int nPB, int kb, int row, int chunk,
-                                               bool &bad) {
+__device__ __forceinline__ uint32_t row_offset(const AttnArgs &a, const int *pages, int page0,
+                                               int64_t node0, int n, int g, int P, int nPB, int kb,
+                                               int row, int chunk, bool &bad) {
     if (kb < nPB) {
         const int pos = kb * kKB + row;
         if (pos >= P) return kOob;
@@ -130,8 +153,8 @@ __device__ __forceinline__ uint32_t row_offset(const AttnArgs &a, const int *pag
         return ((((uint32_t)page * a.page_size + slot) * a.Hkv + g) * kD + chunk * 8) * 2u;
     }
     const int j = (kb - nPB) * kKB + row;
-    if (j >= a.N) return kOob;
-    return ((((uint32_t)b * a.N + j) * a.Hkv + g) * kD + chunk * 8) * 2u;
+    if (j >= n) return kOob;
+    return ((((uint32_t)node0 + j) * a.Hkv + g) * kD + chunk * 8) * 2u;
 }
 
 // LDS byte offset of key row r of a tile: block r % 16, slot r / 16
@@ -149,7 +172,8 @@ struct SplitCtx {
     __amdgpu_buffer_rsrc_t r_kc, r_vc, r_m;  // whole prefix cache (paged layouts), mask buffer
     const uint16_t *kc0, *vc0;               // one-page layout: KV head g of prefix row 0
     const uint16_t *kt0, *vt0;               // KV head g of tree row 0 of the sequence
-    int b, g, P, nPB, page0, lane, wave;
+    int64_t node0;                           // first tree row of the sequence
+    int b, g, P, nPB, n, page0, lane, wave;  // n: the sequence's tree nodes
     bool pzero;                              // one-page layout with a bad page id: zeros
     uint32_t rowb;                           // bytes between consecutive keys
     uint32_t vrow;                           // lane's offset of its first copy in a block
@@ -210,7 +234,7 @@ __device__ __forceinline__ void issue_block(const AttnArgs &a, const SplitCtx &c
             const int j0 = (kb - c.nPB) * kKB;
             kp = c.kt0 + (int64_t)j0 * a.Hkv * kD;
             vp = c.vt0 + (int64_t)j0 * a.Hkv * kD;
-            rows = min(kKB, a.N - j0);
+            rows = min(kKB, c.n - j0);
         } else {
             const int p0 = kb * kKB;
             kp = c.kc0 + (int64_t)p0 * a.Hkv * kD;
@@ -250,8 +274,8 @@ __device__ __forceinline__ void issue_block(const AttnArgs &a, const SplitCtx &c
         } else {
 #pragma unroll
             for (int i = 0; i < kCpw; ++i)
-                off[i] = row_offset(a, pages, c.page0, c.b, c.g, c.P, c.nPB, kb, kCpw * c.wave + i + 16 * sub,
-                                    ch, bad);
+                off[i] = row_offset(a, pages, c.page0, c.node0, c.n, c.g, c.P, c.nPB, kb,
+                                    kCpw * c.wave + i + 16 * sub, ch, bad);
         }
 #pragma unroll
         for (int i = 0; i < kCpw; ++i) copy16(c.r_kc, dk + i * kKBlk, off[i]);
@@ -319,41 +343,54 @@ void k_tree_attn_split(AttnArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: lets wave math stay scalar
     const int half = lane >> 5, l32 = lane & 31;
 
-    // ---- work item ----
+    // ---- work item: (split, KV head, query tile) of one sequence ----
     const int item = xcd_remap(blockIdx.x, a.total_items);
-    const int qt = __builtin_amdgcn_readfirstlane(item % a.n_qt);
-    const int tmp = item / a.n_qt;
-    const int g = __builtin_amdgcn_readfirstlane(tmp % a.Hkv);
-    const int cg = __builtin_amdgcn_readfirstlane(tmp / a.Hkv);
-    const int b = __builtin_amdgcn_readfirstlane(find_seq(a, cg));
-    const int cidx = cg - a.chunk_start[b];
-    const int nchunks = a.chunk_start[b + 1] - a.chunk_start[b];
-    int P = __builtin_amdgcn_readfirstlane(a.prefix_len[b]);
+    const int b = __builtin_amdgcn_readfirstlane(find_seq(a, item));
+    const int64_t node0 = a.node_off[b];
+    const int n = __builtin_amdgcn_readfirstlane(a.node_off[b + 1] - a.node_off[b]);
+    const int R = n * a.G;                                   // query rows of the sequence
+    const int n_qt = div_up(R, kTQ);
+    const int local = item - a.item_start[b];
+    const int qt = __builtin_amdgcn_readfirstlane(local % n_qt);
+    const int g = __builtin_amdgcn_readfirstlane((local / n_qt) % a.Hkv);
+    const int cidx = __builtin_amdgcn_readfirstlane(local / n_qt / a.Hkv);
+    bool pbad = false;
+    int P = __builtin_amdgcn_readfirstlane(prefix_of(a, b, pbad));
     const int nPB = (P + kKB - 1) / kKB;
-    const int nB = nPB + a.n_tree_blocks;
+    const int nTB = div_up(n, kKB);
+    const int nB = nPB + nTB;
+    const int nchunks = div_up(nB, a.chunk_blocks);           // splits of the real length
+    if (cidx >= nchunks) {
+        // past the sequence's real length: nothing to do (the merge reads
+        // the same length and skips this split)
+        if (pbad && tid == 0 && a.status) *a.status = JF_ERR_BAD_PREFIX;
+        return;
+    }
     const int kb0 = cidx * a.chunk_blocks;
     const int kb1 = min(kb0 + a.chunk_blocks, nB);
+    const bool single = nchunks == 1;
+    const int64_t prow0 = (int64_t)item * kTQ;               // this item's partial rows
 
     SplitCtx c;
     c.r_kc = make_rsrc(a.k_cache, a.cache_bytes);
     c.r_vc = make_rsrc(a.v_cache, a.cache_bytes);
     c.r_m = make_rsrc(a.mask, a.mask_bytes);
-    c.b = b; c.g = g; c.P = P; c.nPB = nPB; c.lane = lane; c.wave = wave;
+    c.b = b; c.g = g; c.P = P; c.nPB = nPB; c.n = n; c.node0 = node0; c.lane = lane; c.wave = wave;
     c.rowb = (uint32_t)a.Hkv * kRow;
     c.vrow = (uint32_t)(kCpw * wave + 16 * (lane >> 4)) * c.rowb + (uint32_t)(lane & 15) * 16u;
-    c.kt0 = uniform_ptr(a.k_tree + ((int64_t)b * a.N * a.Hkv + g) * kD);
-    c.vt0 = uniform_ptr(a.v_tree + ((int64_t)b * a.N * a.Hkv + g) * kD);
+    c.kt0 = uniform_ptr(a.k_tree + (node0 * a.Hkv + g) * kD);
+    c.vt0 = uniform_ptr(a.v_tree + (node0 * a.Hkv + g) * kD);
     c.kc0 = a.k_cache;
     c.vc0 = a.v_cache;
     c.pzero = false;
     // ---- this lane's query row and mask dword ----
     const int r = qt * kTQ + wave * 32 + l32;
-    const bool row_ok = r < a.R;
+    const bool row_ok = r < R;
     const int node = row_ok ? r / a.G : 0;
     const int hq = g * a.G + (row_ok ? r % a.G : 0);
     {
         const int rm = qt * kTQ + (tid >> 1);
-        c.mrow = rm < a.R ? (uint32_t)((((int64_t)b * a.N + rm / a.G) * a.W) * 8 + (tid & 1) * 4) : kOob;
+        c.mrow = rm < R ? (uint32_t)(((node0 + rm / a.G) * a.W) * 8 + (tid & 1) * 4) : kOob;
     }
 
     if (tid == 0) { s_used = 0u; s_bad = 0; }
@@ -399,15 +436,15 @@ void k_tree_attn_split(AttnArgs a) {
     u32x4 qraw[kD / 16];
     {
         const __amdgpu_buffer_rsrc_t r_q = make_rsrc(a.q, a.q_bytes);
-        const uint32_t qoff = row_ok ? (uint32_t)(((((int64_t)b * a.N + node) * a.Hq + hq) * kD + half * 8) * 2) : kOob;
+        const uint32_t qoff = row_ok ? (uint32_t)((((node0 + node) * a.Hq + hq) * kD + half * 8) * 2) : kOob;
         load_q(qraw, r_q, qoff);
     }
     // ---- which tree blocks of this split does any row of the tile see? ----
     lds_barrier();   // s_pages / s_bad written above
     if (kb1 > nPB && tid < kTQ) {
         const int rr = qt * kTQ + tid;
-        if (rr < a.R) {
-            const uint64_t *mr = a.mask + ((int64_t)b * a.N + rr / a.G) * a.W;
+        if (rr < R) {
+            const uint64_t *mr = a.mask + (node0 + rr / a.G) * a.W;
             uint32_t bits = 0;
             for (int kb = max(kb0, nPB); kb < kb1; ++kb)
                 if (mr[kb - nPB] != 0ull) bits |= 1u << (kb - nPB);
@@ -424,22 +461,28 @@ void k_tree_attn_split(AttnArgs a) {
         // no row of the tile sees a key of this split: zero rows, lse = -inf;
         // the whole workgroup leaves here with nothing in flight
         if (row_ok) {
-            uint16_t *op;
-            if (nchunks == 1) {
-                const int64_t orow = ((int64_t)b * a.N + node) * a.Hq + hq;
-                op = (uint16_t *)a.out + orow * kD + half * 4;
+            if (single) {
+                const int64_t orow = (node0 + node) * a.Hq + hq;
+                uint16_t *op = (uint16_t *)a.out + orow * kD + half * 4;
                 if (a.lse && half == 0) a.lse[orow] = -INFINITY;
+#pragma unroll
+                for (int d = 0; d < kD / 32; ++d)
+#pragma unroll
+                    for (int gq = 0; gq < 4; ++gq) *(u32x2 *)(op + d * 32 + gq * 8) = u32x2{0u, 0u};
             } else {
-                const int64_t prow = ((int64_t)cg * a.Hkv + g) * a.R + r;
-                op = a.part_o + prow * kD + half * 4;
+                const int64_t prow = prow0 + wave * 32 + l32;
+                float *op = a.part_o + prow * kD + half * 4;
                 if (half == 0) a.part_lse[prow] = -INFINITY;
+#pragma unroll
+                for (int d = 0; d < kD / 32; ++d)
+#pragma unroll
+                    for (int gq = 0; gq < 4; ++gq) *(f32x4 *)(op + d * 32 + gq * 8) = f32x4{0.f, 0.f, 0.f, 0.f};
             }
-#pragma unroll
-            for (int d = 0; d < kD / 32; ++d)
-#pragma unroll
-                for (int gq = 0; gq < 4; ++gq) *(u32x2 *)(op + d * 32 + gq * 8) = u32x2{0u, 0u};
         }
-        if (tid == 0 && s_bad && a.page_status) *a.page_status = JF_ERR_BAD_PAGE;
+        if (tid == 0 && a.status) {
+            if (s_bad) *a.status = JF_ERR_BAD_PAGE;
+            if (pbad) *a.status = JF_ERR_BAD_PREFIX;
+        }
         __builtin_amdgcn_s_waitcnt(0);   // the query loads have returned
         return;
     }
@@ -493,7 +536,7 @@ void k_tree_attn_split(AttnArgs a) {
         if (is_tree || tail) {
             uint64_t vis;
             if (is_tree) {
-                const int left = a.N - (kb - nPB) * kKB;
+                const int left = n - (kb - nPB) * kKB;
                 const uint64_t word = *(const __attribute__((address_space(3))) uint64_t *)(
                     st + kKTile + kVTile + (wave * 32 + l32) * 8);
                 vis = word & (left >= 64 ? ~0ull : ((1ull << left) - 1ull));
@@ -705,84 +748,101 @@ void k_tree_attn_split(AttnArgs a) {
     // its 4-column pieces in LDS (the ring is idle once every copy has landed
     // and every wave is past its last step), then the wave writes 16-byte
     // chunks, 1 KiB per store instruction.  (A lane's own pieces would
-    // scatter 8 bytes over 64 rows per store instruction.)
+    // scatter 8 or 16 bytes over 32 rows per store instruction.)  A sequence
+    // with one split writes the bf16 output; otherwise the fp32 partials of
+    // the work item's rows.
     ring_barrier<0>();
-    constexpr int kOutRow = kRow + 16;                  // padded row: rows fall on shifted banks
-    lds_t *ob = (lds_t *)&ring[0][0] + wave * 32 * kOutRow;
+    if (single) {
+        constexpr int kOutRow = kRow + 16;              // padded row: rows fall on shifted banks
+        lds_t *ob = (lds_t *)&ring[0][0] + wave * 32 * kOutRow;
 #pragma unroll
-    for (int d = 0; d < kD / 32; ++d)
+        for (int d = 0; d < kD / 32; ++d)
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-            u32x2 w;
-            w[0] = pack_bf16x2(S.o[d][gq * 4 + 0] * inv, S.o[d][gq * 4 + 1] * inv);
-            w[1] = pack_bf16x2(S.o[d][gq * 4 + 2] * inv, S.o[d][gq * 4 + 3] * inv);
-            *(__attribute__((address_space(3))) u32x2 *)(ob + l32 * kOutRow + (d * 32 + gq * 8 + half * 4) * 2) = w;
-        }
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int c = 0; c < 32 * (kRow / 16) / kWave; ++c) {
-        const int idx = c * kWave + lane, row = idx >> 4, ch = idx & 15;
-        const int rr = qt * kTQ + wave * 32 + row;
-        const u32x4 v = *(const __attribute__((address_space(3))) u32x4 *)(ob + row * kOutRow + ch * 16);
-        if (rr < a.R) {
-            int64_t orow;
-            uint16_t *base;
-            if (nchunks == 1) {
-                orow = ((int64_t)b * a.N + rr / a.G) * a.Hq + g * a.G + rr % a.G;
-                base = (uint16_t *)a.out;
-            } else {
-                orow = ((int64_t)cg * a.Hkv + g) * a.R + rr;
-                base = a.part_o;
+            for (int gq = 0; gq < 4; ++gq) {
+                u32x2 w;
+                w[0] = pack_bf16x2(S.o[d][gq * 4 + 0] * inv, S.o[d][gq * 4 + 1] * inv);
+                w[1] = pack_bf16x2(S.o[d][gq * 4 + 2] * inv, S.o[d][gq * 4 + 3] * inv);
+                *(__attribute__((address_space(3))) u32x2 *)(ob + l32 * kOutRow + (d * 32 + gq * 8 + half * 4) * 2) = w;
             }
-            *(u32x4 *)(base + orow * kD + ch * 8) = v;
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int cc = 0; cc < 32 * (kRow / 16) / kWave; ++cc) {
+            const int idx = cc * kWave + lane, row = idx >> 4, ch = idx & 15;
+            const int rr = qt * kTQ + wave * 32 + row;
+            const u32x4 v = *(const __attribute__((address_space(3))) u32x4 *)(ob + row * kOutRow + ch * 16);
+            if (rr < R) {
+                const int64_t orow = (node0 + rr / a.G) * a.Hq + g * a.G + rr % a.G;
+                *(u32x4 *)((uint16_t *)a.out + orow * kD + ch * 8) = v;
+            }
         }
-    }
-    if (row_ok && half == 0) {
-        if (nchunks == 1) {
-            if (a.lse) a.lse[((int64_t)b * a.N + node) * a.Hq + hq] = lse_v;
-        } else {
-            a.part_lse[((int64_t)cg * a.Hkv + g) * a.R + r] = lse_v;
+        if (row_ok && half == 0 && a.lse) a.lse[(node0 + node) * a.Hq + hq] = lse_v;
+    } else {
+        constexpr int kPRow = kD * 4 + 16;              // padded fp32 row
+        lds_t *ob = (lds_t *)&ring[0][0] + wave * 32 * kPRow;
+#pragma unroll
+        for (int d = 0; d < kD / 32; ++d)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const f32x4 w = {S.o[d][gq * 4 + 0] * inv, S.o[d][gq * 4 + 1] * inv,
+                                 S.o[d][gq * 4 + 2] * inv, S.o[d][gq * 4 + 3] * inv};
+                *(__attribute__((address_space(3))) f32x4 *)(ob + l32 * kPRow + (d * 32 + gq * 8 + half * 4) * 4) = w;
+            }
+        __builtin_amdgcn_wave_barrier();
+        float *pbase = a.part_o + (prow0 + wave * 32) * kD;
+#pragma unroll
+        for (int cc = 0; cc < 32 * (kD * 4 / 16) / kWave; ++cc) {
+            const int idx = cc * kWave + lane, row = idx >> 5, ch = idx & 31;
+            const u32x4 v = *(const __attribute__((address_space(3))) u32x4 *)(ob + row * kPRow + ch * 16);
+            if (qt * kTQ + wave * 32 + row < R) *(u32x4 *)(pbase + row * kD + ch * 4) = v;
         }
+        if (row_ok && half == 0) a.part_lse[prow0 + wave * 32 + l32] = lse_v;
     }
-    if (tid == 0 && s_bad && a.page_status) *a.page_status = JF_ERR_BAD_PAGE;
+    if (tid == 0 && a.status) {
+        if (s_bad) *a.status = JF_ERR_BAD_PAGE;
+        if (pbad) *a.status = JF_ERR_BAD_PREFIX;
+    }
 }
 
 // Combine the splits of one row: O = sum_s w_s O_s / sum_s w_s with
 // w_s = exp(lse_s - max lse); lse = max + log sum w_s.  Sixteen threads per
-// row, eight output columns (one 16-byte load per split) each; one pass over
-// the splits, eight at a time, rescaling when the running maximum moves.
-// The grid's y index is the sequence, so that the split range of a block is
-// uniform (scalar kernel-argument reads, no dependent vector load).
+// row, eight output columns (two 16-byte loads per split) each; one pass over
+// the splits, four at a time, rescaling when the running maximum moves.  The
+// grid's y index is the sequence; the split count follows the sequence's
+// real prefix length, as in the split kernel.
 constexpr int kMergeTPR = kD / 8;        // threads per row
 __global__ __launch_bounds__(256) void k_tree_attn_merge(AttnArgs a) {
     const int sub = threadIdx.x % kMergeTPR;
     const int b = blockIdx.y;
-    const int c0 = a.chunk_start[b];
-    const int nc = a.chunk_start[b + 1] - c0;
+    const int n = a.node_off[b + 1] - a.node_off[b];
+    bool pbad = false;
+    const int P = prefix_of(a, b, pbad);
+    const int nc = div_up(div_up(P, kKB) + div_up(n, kKB), a.chunk_blocks);
     if (nc == 1) return;                                     // written by the split kernel
     const int in_seq = blockIdx.x * (256 / kMergeTPR) + threadIdx.x / kMergeTPR;
-    if (in_seq >= a.N * a.Hq) return;
-    const int64_t flat = (int64_t)b * a.N * a.Hq + in_seq;
+    if (in_seq >= n * a.Hq) return;
+    const int64_t flat = (int64_t)a.node_off[b] * a.Hq + in_seq;
     const int hq = in_seq % a.Hq;
     const int node = in_seq / a.Hq;
     const int g = hq / a.G;
     const int r = node * a.G + hq % a.G;
-    const int64_t stride = (int64_t)a.Hkv * a.R;             // rows between consecutive splits
-    const int64_t row0 = ((int64_t)c0 * a.Hkv + g) * a.R + r;
-    const uint16_t *po = a.part_o + row0 * kD + sub * 8;
-    // one pass, eight splits' loads in flight at a time, online rescaling
+    const int n_qt = div_up(n * a.G, kTQ);
+    // split c's work item: item_start[b] + (c * Hkv + g) * n_qt + r / kTQ
+    const int64_t row0 = ((int64_t)a.item_start[b] + (int64_t)g * n_qt + r / kTQ) * kTQ + r % kTQ;
+    const int64_t stride = (int64_t)a.Hkv * n_qt * kTQ;      // rows between consecutive splits
+    const float *po = a.part_o + row0 * kD + sub * 8;
     float M = -INFINITY;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float wsum = 0.f;
-    constexpr int kGroup = 8;
+    constexpr int kGroup = 4;
     for (int c = 0; c < nc; c += kGroup) {
         float l[kGroup];
-        u32x4 v[kGroup];
+        f32x4 v0[kGroup], v1[kGroup];
 #pragma unroll
         for (int u = 0; u < kGroup; ++u) {
             const bool ok = c + u < nc;
             l[u] = ok ? a.part_lse[row0 + (c + u) * stride] : -INFINITY;
-            v[u] = ok ? *(const u32x4 *)(po + (c + u) * stride * kD) : u32x4{0u, 0u, 0u, 0u};
+            v0[u] = ok ? *(const f32x4 *)(po + (c + u) * stride * kD) : f32x4{0.f, 0.f, 0.f, 0.f};
+            v1[u] = ok ? *(const f32x4 *)(po + (c + u) * stride * kD + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
         }
         float mg = M;
 #pragma unroll
@@ -798,8 +858,8 @@ __global__ __launch_bounds__(256) void k_tree_attn_merge(AttnArgs a) {
             const float w = l[u] == -INFINITY ? 0.f : __expf(l[u] - M);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                acc[2 * e] += w * bf16_lo(v[u][e]);
-                acc[2 * e + 1] += w * bf16_hi(v[u][e]);
+                acc[e] += w * v0[u][e];
+                acc[4 + e] += w * v1[u][e];
             }
             wsum += w;
         }
@@ -813,20 +873,23 @@ __global__ __launch_bounds__(256) void k_tree_attn_merge(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// fp32 path: one wavefront per (sequence, node, query head); keys are taken 64
-// at a time (one per lane), scores in fp32, online softmax with expf, each lane
-// accumulating D/64 output columns.  Meant for small problems.
+// fp32 path: one wavefront per (tree row, query head); keys are taken 64 at a
+// time (one per lane), scores in fp32, online softmax with expf, each lane
+// accumulating D/64 output columns.  Meant for small problems.  A bad page id
+// reads as a zero key (score 0) with a zero value, as on the bf16 path.
 struct AttnArgsF32 {
     const float *q, *k_tree, *v_tree;
     const uint64_t *mask;
     const float *k_cache, *v_cache;
     const int32_t *block_table;
+    const int32_t *prefix_dev;
     float *out, *lse;
-    int32_t *page_status;
+    int32_t *status;
     int64_t num_pages;
-    int page_size, max_pages, B, N, Hq, Hkv, G, W, D;
+    int page_size, max_pages, B, Hq, Hkv, G, W, D;
     float scale;
-    int prefix_len[kMaxBatch];
+    int cap[kMaxBatch];
+    int node_off[kMaxBatch + 1];
 };
 
 constexpr int kF32MaxD = 128;
@@ -835,45 +898,61 @@ __global__ __launch_bounds__(256) void k_tree_attn_f32(AttnArgsF32 a) {
     __shared__ float sq[4][kF32MaxD];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int64_t flat = (int64_t)blockIdx.x * 4 + wv;
-    const int64_t total = (int64_t)a.B * a.N * a.Hq;
+    const int64_t total = (int64_t)a.node_off[a.B] * a.Hq;
     if (flat >= total) return;
     const int hq = (int)(flat % a.Hq);
-    const int node = (int)((flat / a.Hq) % a.N);
-    const int b = (int)(flat / ((int64_t)a.Hq * a.N));
+    const int64_t t = flat / a.Hq;                // tree row
+    int b = 0;
+    {
+        int hi = a.B - 1;
+        while (b < hi) {
+            const int mid = (b + hi + 1) >> 1;
+            if (a.node_off[mid] <= t) b = mid; else hi = mid - 1;
+        }
+    }
+    const int64_t node0 = a.node_off[b];
+    const int n = a.node_off[b + 1] - a.node_off[b];
+    const int node = (int)(t - node0);
     const int g = hq / a.G;
     const int D = a.D;
-    const int P = a.prefix_len[b];
+    bool pbad = false;
+    int P = a.cap[b];
+    if (a.prefix_dev) {
+        const int pd = a.prefix_dev[b];
+        if (pd < 0 || pd > P) pbad = true;
+        P = pd < 0 ? 0 : (pd > P ? P : pd);
+    }
     for (int d = lane; d < D; d += 64) sq[wv][d] = a.q[flat * D + d];
     __builtin_amdgcn_wave_barrier();
-    const uint64_t *mrow = a.mask + ((int64_t)b * a.N + node) * a.W;
+    const uint64_t *mrow = a.mask + t * a.W;
     float m = -INFINITY, l = 0.f, acc0 = 0.f, acc1 = 0.f;
     bool bad = false;
-    const int nkeys = P + a.N;
+    const int nkeys = P + n;
     for (int kc = 0; kc < nkeys; kc += 64) {
         const int key = kc + lane;
         bool valid = false;
-        int64_t off = 0;
-        const float *kbase = a.k_cache, *vbase = a.v_cache;
+        int64_t off = -1;                         // -1: a zero key and value
+        const float *kbase = a.k_cache;
         if (key < P) {
             int64_t page = a.block_table[(int64_t)b * a.max_pages + key / a.page_size];
-            if (page >= 0 && page < a.num_pages) {
+            valid = true;
+            if (page >= 0 && page < a.num_pages)
                 off = ((page * a.page_size + key % a.page_size) * a.Hkv + g) * (int64_t)D;
-                valid = true;
-            } else {
+            else
                 bad = true;
-            }
         } else if (key < nkeys) {
             const int j = key - P;
             valid = (mrow[j >> 6] >> (j & 63)) & 1ull;
-            off = (((int64_t)b * a.N + j) * a.Hkv + g) * (int64_t)D;
+            off = ((node0 + j) * a.Hkv + g) * (int64_t)D;
             kbase = a.k_tree;
-            vbase = a.v_tree;
         }
         float s = -INFINITY;
         if (valid) {
-            const float *kr = kbase + off;
             float dot = 0.f;
-            for (int d = 0; d < D; ++d) dot = fmaf(sq[wv][d], kr[d], dot);
+            if (off >= 0) {
+                const float *kr = kbase + off;
+                for (int d = 0; d < D; ++d) dot = fmaf(sq[wv][d], kr[d], dot);
+            }
             s = dot * a.scale;
         }
         float cm = s;
@@ -887,35 +966,35 @@ __global__ __launch_bounds__(256) void k_tree_attn_f32(AttnArgsF32 a) {
         l = l * alpha + ps;
         acc0 *= alpha;
         acc1 *= alpha;
-        const float *vrow_base = vbase;
         for (int jj = 0; jj < 64; ++jj) {
             const float pj = __shfl(p, jj);
-            if (pj == 0.f) continue;  // uniform across the wave
             const int64_t oj = __shfl(off, jj);
+            if (pj == 0.f || oj < 0) continue;    // uniform across the wave
             const bool tree_j = (kc + jj) >= P;
             const float *vr = (tree_j ? a.v_tree : a.v_cache) + oj;
             if (lane < D) acc0 = fmaf(pj, vr[lane], acc0);
             if (lane + 64 < D) acc1 = fmaf(pj, vr[lane + 64], acc1);
         }
-        (void)vrow_base;
         m = mn;
     }
     const float inv = l > 0.f ? 1.f / l : 0.f;
     if (lane < D) a.out[flat * D + lane] = acc0 * inv;
     if (lane + 64 < D) a.out[flat * D + lane + 64] = acc1 * inv;
     if (a.lse && lane == 0) a.lse[flat] = l > 0.f ? m + logf(l) : -INFINITY;
-    if (bad && a.page_status) *a.page_status = JF_ERR_BAD_PAGE;
+    if (a.status && lane == 0) {
+        if (bad) *a.status = JF_ERR_BAD_PAGE;
+        if (pbad) *a.status = JF_ERR_BAD_PREFIX;
+    }
 }
 
 }  // namespace
 
 // ---------------------------------------------------------------------------
 // Predicted span (in quarter blocks) of the split kernel's workgroups for
-// splits of c blocks: each split gives `per_chunk` workgroups, launched in
-// the kernel's item order, each costing a fixed overhead plus its blocks on
-// the compute unit that frees first.
-static int64_t plan_span(int B, const int32_t *prefix_len, int n_tree_blocks, int c, int per_chunk,
-                         int cus) {
+// splits of c blocks: sequence b has nb[b] blocks and gives per_chunk[b]
+// workgroups per split, launched in the kernel's item order, each costing a
+// fixed overhead plus its blocks on the compute unit that frees first.
+static int64_t plan_span(int B, const int64_t *nb, const int64_t *per_chunk, int64_t c, int cus) {
     constexpr int64_t kOverhead = 16;    // quarter blocks: prologue, partial write and its merge
     std::vector<int64_t> heap((size_t)cus, 0);   // min-heap of compute-unit free times
     auto push_pop = [&](int64_t cost) {
@@ -935,10 +1014,9 @@ static int64_t plan_span(int B, const int32_t *prefix_len, int n_tree_blocks, in
         heap[i] = v;
     };
     for (int b = 0; b < B; ++b) {
-        const int64_t nb = (prefix_len[b] + kKB - 1) / kKB + n_tree_blocks;
-        for (int64_t k0 = 0; k0 < nb; k0 += c) {
-            const int64_t size = (k0 + c < nb ? c : nb - k0) * 4 + kOverhead;
-            for (int w = 0; w < per_chunk; ++w) push_pop(size);
+        for (int64_t k0 = 0; k0 < nb[b]; k0 += c) {
+            const int64_t size = (k0 + c < nb[b] ? c : nb[b] - k0) * 4 + kOverhead;
+            for (int64_t w = 0; w < per_chunk[b]; ++w) push_pop(size);
         }
     }
     int64_t span = 0;
@@ -947,100 +1025,89 @@ static int64_t plan_span(int B, const int32_t *prefix_len, int n_tree_blocks, in
 }
 
 // ---------------------------------------------------------------------------
-// Split planning.  Every (sequence, KV head, query tile) is a row of blocks;
-// cut all rows into splits of the same block count so that about one
-// workgroup per compute unit comes out (a workgroup fills a compute unit's
-// LDS), never less than two blocks a split.  A caller that runs other work
-// beside the attention can plan it for fewer compute units.
+// Split planning from the prefix bounds.  Every (sequence, KV head, query
+// tile) is a row of blocks; cut all rows into splits of the same block count
+// so that about one workgroup per compute unit comes out (a workgroup fills a
+// compute unit's LDS), never less than two blocks a split.  A caller that
+// runs other work beside the attention can plan it for fewer compute units.
 void plan_tree_attn(AttnPlan &p, int B, int N, int Hq, int Hkv, int D, int page_size,
-                    const int32_t *prefix_len, jf_dtype dtype, int cus) {
+                    const int32_t *prefix_cap, const int32_t *node_off, jf_dtype dtype, int cus) {
     p.B = B; p.N = N; p.Hq = Hq; p.Hkv = Hkv; p.D = D;
     p.page_size = page_size;
     p.G = Hq / Hkv;
-    p.R = N * p.G;
     p.W = (N + 63) / 64;
-    p.tq = kTQ;
-    p.n_qt = (p.R + kTQ - 1) / kTQ;
-    p.n_tree_blocks = (N + kKB - 1) / kKB;
-    int64_t units = 0;
-    int max_blocks = 1;
+    std::vector<int64_t> nb((size_t)B), per_chunk((size_t)B);
+    int64_t units = 0, max_blocks = 1, Pmax = 0;
     for (int b = 0; b < B; ++b) {
-        p.prefix_len[b] = prefix_len[b];
-        int nb = (prefix_len[b] + kKB - 1) / kKB + p.n_tree_blocks;
-        units += (int64_t)nb;
-        if (nb > max_blocks) max_blocks = nb;
+        p.cap[b] = prefix_cap[b];
+        p.node_off[b] = node_off ? node_off[b] : b * N;
+        const int64_t n = node_off ? node_off[b + 1] - node_off[b] : N;
+        nb[b] = (prefix_cap[b] + kKB - 1) / kKB + (n + kKB - 1) / kKB;
+        per_chunk[b] = (int64_t)Hkv * ((n * p.G + kTQ - 1) / kTQ);
+        units += nb[b] * per_chunk[b];
+        if (nb[b] > max_blocks) max_blocks = nb[b];
+        if (prefix_cap[b] > Pmax) Pmax = prefix_cap[b];
     }
-    units *= (int64_t)Hkv * p.n_qt;
+    p.node_off[B] = node_off ? node_off[B] : B * N;
     const int64_t target = cus > 0 && cus < num_cus() ? (int64_t)cus : (int64_t)num_cus();
     int64_t cb = (units + target - 1) / target;
     if (cb < 2) cb = 2;
     // a split's page ids must fit the LDS staging array
-    int64_t Pmax = 0;
-    for (int b = 0; b < B; ++b) Pmax = prefix_len[b] > Pmax ? prefix_len[b] : Pmax;
     if (page_size < Pmax) {
         int64_t cap = ((int64_t)(kPageLds - 2) * page_size) / kKB;
         if (cap < 1) cap = 1;
         if (cb > cap) cb = cap;
     }
     if (cb > max_blocks) cb = max_blocks;
+    auto n_items = [&](int64_t c) {
+        int64_t n = 0;
+        for (int b = 0; b < B; ++b) n += (nb[b] + c - 1) / c * per_chunk[b];
+        return n;
+    };
     // Ragged prefixes leave partial splits, and the workgroups can then spill
     // over one wave of the chip.  Splits of the base size are then compared
     // with smaller ones by a model of the dispatch (workgroups in launch order,
     // each to the compute unit that frees first; cost = a fixed per-workgroup
     // overhead + its block count), and the shortest predicted span is kept.
-    if (dtype != JF_F32) {
-        auto n_items = [&](int64_t c) {
-            int64_t n = 0;
-            for (int b = 0; b < B; ++b) {
-                const int64_t nb = (prefix_len[b] + kKB - 1) / kKB + p.n_tree_blocks;
-                n += (nb + c - 1) / c;
-            }
-            return n * Hkv * p.n_qt;
-        };
-        if (n_items(cb) > target) {
-            const int64_t base = cb;
-            int64_t best = -1;
-            int64_t best_cb = cb;
-            for (int d = 4; d <= 12; ++d) {        // base * 4/d: 1, 0.8, ..., 1/3 of the base size
-                int64_t c = (base * 4 + d - 1) / d;
-                if (c < 2) c = 2;
-                if (d > 4 && c == best_cb) continue;
-                const int64_t span = plan_span(B, prefix_len, p.n_tree_blocks, (int)c, Hkv * p.n_qt,
-                                               (int)target);
-                if (best < 0 || span < best) { best = span; best_cb = c; }
-            }
-            cb = best_cb;
+    if (dtype != JF_F32 && n_items(cb) > target) {
+        const int64_t base = cb;
+        int64_t best = -1;
+        int64_t best_cb = cb;
+        for (int d = 4; d <= 12; ++d) {        // base * 4/d: 1, 0.8, ..., 1/3 of the base size
+            int64_t c = (base * 4 + d - 1) / d;
+            if (c < 2) c = 2;
+            if (d > 4 && c == best_cb) continue;
+            const int64_t span = plan_span(B, nb.data(), per_chunk.data(), c, (int)target);
+            if (best < 0 || span < best) { best = span; best_cb = c; }
         }
+        cb = best_cb;
     }
     if (dtype == JF_F32) cb = max_blocks;  // the fp32 path does not split
     p.chunk_blocks = (int)cb;
-    int cs = 0;
+    int64_t items = 0;
     p.any_split = false;
     for (int b = 0; b < B; ++b) {
-        p.chunk_start[b] = cs;
-        int nb = (prefix_len[b] + kKB - 1) / kKB + p.n_tree_blocks;
-        int nc = (nb + p.chunk_blocks - 1) / p.chunk_blocks;
+        p.item_start[b] = (int)items;
+        const int64_t nc = (nb[b] + cb - 1) / cb;
         if (nc > 1) p.any_split = true;
-        cs += nc;
+        items += nc * per_chunk[b];
     }
-    p.chunk_start[B] = cs;
-    p.total_chunks = cs;
-    p.total_items = cs * Hkv * p.n_qt;
+    p.item_start[B] = (int)items;
+    p.total_items = (int)items;
 }
 
 size_t tree_attn_workspace_bytes(const AttnPlan &p) {
     if (!p.any_split) return 0;
-    const size_t rows = (size_t)p.total_chunks * p.Hkv * p.R;
-    size_t o = rows * kD * sizeof(uint16_t);
-    o = (o + 255) / 256 * 256;
-    return o + rows * sizeof(float);
+    const size_t rows = (size_t)p.total_items * kTQ;
+    return rows * kD * sizeof(float) + rows * sizeof(float);
 }
 
 hipError_t launch_tree_attn_bf16(const AttnPlan &p, const void *q, const void *k_tree,
                                  const void *v_tree, const uint64_t *mask, const void *k_cache,
                                  const void *v_cache, int64_t num_pages, int page_size,
-                                 const int32_t *block_table, int max_pages, float scale, void *out,
-                                 float *lse, void *workspace, int32_t *page_status, hipStream_t s) {
+                                 const int32_t *block_table, int max_pages,
+                                 const int32_t *prefix_dev, float scale, void *out, float *lse,
+                                 void *workspace, int32_t *status, hipStream_t s) {
     AttnArgs a;
     a.q = (const uint16_t *)q;
     a.k_tree = (const uint16_t *)k_tree;
@@ -1049,17 +1116,18 @@ hipError_t launch_tree_attn_bf16(const AttnPlan &p, const void *q, const void *k
     a.k_cache = (const uint16_t *)k_cache;
     a.v_cache = (const uint16_t *)v_cache;
     a.block_table = block_table;
+    a.prefix_dev = prefix_dev;
     a.out = out;
     a.lse = lse;
-    const size_t rows = (size_t)p.total_chunks * p.Hkv * p.R;
-    size_t obytes = (rows * kD * sizeof(uint16_t) + 255) / 256 * 256;
-    a.part_o = p.any_split ? (uint16_t *)workspace : nullptr;
-    a.part_lse = p.any_split ? (float *)((char *)workspace + obytes) : nullptr;
-    a.page_status = page_status;
-    a.q_bytes = (uint32_t)((int64_t)p.B * p.N * p.Hq * kD * 2);
-    a.tree_bytes = (uint32_t)((int64_t)p.B * p.N * p.Hkv * kD * 2);
+    const size_t rows = (size_t)p.total_items * kTQ;
+    a.part_o = p.any_split ? (float *)workspace : nullptr;
+    a.part_lse = p.any_split ? (float *)((char *)workspace + rows * kD * sizeof(float)) : nullptr;
+    a.status = status;
+    const int64_t T = p.node_off[p.B];
+    a.q_bytes = (uint32_t)(T * p.Hq * kD * 2);
+    a.tree_bytes = (uint32_t)(T * p.Hkv * kD * 2);
     a.cache_bytes = (uint32_t)(num_pages * page_size * (int64_t)p.Hkv * kD * 2);
-    a.mask_bytes = (uint32_t)((int64_t)p.B * p.N * p.W * 8);
+    a.mask_bytes = (uint32_t)(T * p.W * 8);
     a.num_pages = num_pages;
     a.page_size = page_size;
     a.page_shift = -1;
@@ -1071,20 +1139,21 @@ hipError_t launch_tree_attn_bf16(const AttnPlan &p, const void *q, const void *k
     a.max_pages = max_pages;
     {
         int Pmax = 0;
-        for (int b = 0; b < p.B; ++b) Pmax = p.prefix_len[b] > Pmax ? p.prefix_len[b] : Pmax;
+        for (int b = 0; b < p.B; ++b) Pmax = p.cap[b] > Pmax ? p.cap[b] : Pmax;
         a.page_mode = (max_pages == 1 && page_size >= Pmax) ? 1
                       : (a.page_shift >= 4 ? 2 : 0);
     }
-    a.B = p.B; a.N = p.N; a.Hq = p.Hq; a.Hkv = p.Hkv; a.G = p.G; a.R = p.R; a.W = p.W;
-    a.n_qt = p.n_qt;
+    a.B = p.B; a.Hq = p.Hq; a.Hkv = p.Hkv; a.G = p.G; a.W = p.W;
     a.chunk_blocks = p.chunk_blocks;
-    a.n_tree_blocks = p.n_tree_blocks;
     a.total_items = p.total_items;
     a.scale = scale;
     a.c2 = scale * kLog2e;
     a.lazy_raw = kLazyLog2 / a.c2;
-    for (int b = 0; b < p.B; ++b) a.prefix_len[b] = p.prefix_len[b];
-    for (int b = 0; b <= p.B; ++b) a.chunk_start[b] = p.chunk_start[b];
+    for (int b = 0; b < p.B; ++b) a.cap[b] = p.cap[b];
+    for (int b = 0; b <= p.B; ++b) {
+        a.node_off[b] = p.node_off[b];
+        a.item_start[b] = p.item_start[b];
+    }
     if (a.page_mode == 1)
         hipLaunchKernelGGL(k_tree_attn_split<false>, dim3(p.total_items), dim3(kNW * kWave), 0, s, a);
     else
@@ -1101,17 +1170,20 @@ hipError_t launch_tree_attn_bf16(const AttnPlan &p, const void *q, const void *k
 hipError_t launch_tree_attn_f32(const AttnPlan &p, const float *q, const float *k_tree,
                                 const float *v_tree, const uint64_t *mask, const float *k_cache,
                                 const float *v_cache, int64_t num_pages, int page_size,
-                                const int32_t *block_table, int max_pages, float scale,
-                                float *out, float *lse, int32_t *page_status, hipStream_t s) {
+                                const int32_t *block_table, int max_pages, const int32_t *prefix_dev,
+                                float scale, float *out, float *lse, int32_t *status,
+                                hipStream_t s) {
     AttnArgsF32 a;
     a.q = q; a.k_tree = k_tree; a.v_tree = v_tree; a.mask = mask;
     a.k_cache = k_cache; a.v_cache = v_cache; a.block_table = block_table;
-    a.out = out; a.lse = lse; a.page_status = page_status;
+    a.prefix_dev = prefix_dev;
+    a.out = out; a.lse = lse; a.status = status;
     a.num_pages = num_pages; a.page_size = page_size; a.max_pages = max_pages;
-    a.B = p.B; a.N = p.N; a.Hq = p.Hq; a.Hkv = p.Hkv; a.G = p.G; a.W = p.W; a.D = p.D;
+    a.B = p.B; a.Hq = p.Hq; a.Hkv = p.Hkv; a.G = p.G; a.W = p.W; a.D = p.D;
     a.scale = scale;
-    for (int b = 0; b < p.B; ++b) a.prefix_len[b] = p.prefix_len[b];
-    const int64_t total = (int64_t)p.B * p.N * p.Hq;
+    for (int b = 0; b < p.B; ++b) a.cap[b] = p.cap[b];
+    for (int b = 0; b <= p.B; ++b) a.node_off[b] = p.node_off[b];
+    const int64_t total = (int64_t)p.node_off[p.B] * p.Hq;
     hipLaunchKernelGGL(k_tree_attn_f32, dim3((unsigned)((total + 3) / 4)), dim3(256), 0, s, a);
     return hipGetLastError();
 }

@@ -21,7 +21,8 @@ LIB_PATH = os.path.join(_HERE, "libjf.so")
 
 JF_OK, JF_ERR_INVALID_ARG, JF_ERR_UNSUPPORTED, JF_ERR_ALIGN = 0, 1, 2, 3
 JF_ERR_WORKSPACE, JF_ERR_BAD_TREE, JF_ERR_BAD_PAGE, JF_ERR_HIP = 4, 5, 6, 7
-JF_F32, JF_BF16 = 0, 1
+JF_ERR_BAD_PREFIX = 8
+JF_F32, JF_BF16, JF_FP8_E4M3 = 0, 1, 2
 
 EXPORTS = ("jf_status_string", "jf_abi_version", "jf_tree_mask_build",
            "jf_fuse_proj_workspace_size", "jf_fuse_proj", "jf_fuse_proj_workspace_size_cus",
@@ -53,7 +54,7 @@ def lib():
     L.jf_status_string.restype = ctypes.c_char_p
     L.jf_abi_version.argtypes = []
     L.jf_abi_version.restype = ctypes.c_int
-    L.jf_tree_mask_build.argtypes = [P, I32, I32, P, P, P, P]
+    L.jf_tree_mask_build.argtypes = [P, P, I32, I32, P, P, P, P]
     L.jf_tree_mask_build.restype = ctypes.c_int
     L.jf_fuse_proj_workspace_size.argtypes = [I64, I64, I32, I64, ctypes.c_int]
     L.jf_fuse_proj_workspace_size.restype = SZ
@@ -65,15 +66,18 @@ def lib():
     L.jf_fuse_proj_cus.argtypes = [P, I32, I64, I64, I64, P, I64, ctypes.c_int, P, ctypes.c_int,
                                    P, SZ, I32, P]
     L.jf_fuse_proj_cus.restype = ctypes.c_int
-    L.jf_tree_attn_workspace_size.argtypes = [I32, I32, I32, I32, I32, I32, P, ctypes.c_int]
+    F = ctypes.c_float
+    L.jf_tree_attn_workspace_size.argtypes = [I32, I32, I32, I32, I32, I32, P, P, ctypes.c_int]
     L.jf_tree_attn_workspace_size.restype = SZ
-    L.jf_tree_attn_fwd.argtypes = [P, P, P, P, P, P, I64, I32, P, I32, P, I32, I32, I32, I32, I32,
-                                   ctypes.c_float, ctypes.c_int, P, P, P, SZ, P, P]
+    L.jf_tree_attn_fwd.argtypes = [P, P, P, P, P, P, ctypes.c_int, F, F, I64, I32, P, I32, P, P, P,
+                                   I32, I32, I32, I32, I32, F, ctypes.c_int, P, P, P, SZ, P, P]
     L.jf_tree_attn_fwd.restype = ctypes.c_int
-    L.jf_tree_attn_workspace_size_cus.argtypes = [I32, I32, I32, I32, I32, I32, P, ctypes.c_int, I32]
+    L.jf_tree_attn_workspace_size_cus.argtypes = [I32, I32, I32, I32, I32, I32, P, P, ctypes.c_int,
+                                                  I32]
     L.jf_tree_attn_workspace_size_cus.restype = SZ
-    L.jf_tree_attn_fwd_cus.argtypes = [P, P, P, P, P, P, I64, I32, P, I32, P, I32, I32, I32, I32, I32,
-                                       ctypes.c_float, ctypes.c_int, P, P, P, SZ, P, I32, P]
+    L.jf_tree_attn_fwd_cus.argtypes = [P, P, P, P, P, P, ctypes.c_int, F, F, I64, I32, P, I32, P, P,
+                                       P, I32, I32, I32, I32, I32, F, ctypes.c_int, P, P, P, SZ, P,
+                                       I32, P]
     L.jf_tree_attn_fwd_cus.restype = ctypes.c_int
     L.jf_node_topk_workspace_size.argtypes = [I64, I64, I32]
     L.jf_node_topk_workspace_size.restype = SZ
@@ -129,23 +133,39 @@ def _contig(name: str, t: torch.Tensor):
 
 
 # ---------------------------------------------------------------------------
+def _node_off(node_off):
+    """Host int32 [B+1] packed node offsets (or None), and the largest count."""
+    if node_off is None:
+        return None, 0
+    no = _host_i32(node_off)
+    return no, int(np.max(np.diff(no)))
+
+
 def jf_tree_mask_build(parent: torch.Tensor, mask: Optional[torch.Tensor] = None,
                        depth: Optional[torch.Tensor] = None,
-                       seq_status: Optional[torch.Tensor] = None, stream=None):
-    """parent [B, N] int32 -> (mask [B, N, ceil(N/64)] uint64 (as int64), depth [B, N],
-    seq_status [B]) on the parent's device."""
+                       seq_status: Optional[torch.Tensor] = None, node_off=None, stream=None):
+    """Uniform trees: parent [B, N] int32 -> (mask [B, N, ceil(N/64)] uint64
+    (as int64), depth [B, N], seq_status [B]).  Packed trees: parent [T] with
+    host node_off [B+1] -> (mask [T, W], depth [T], seq_status [B]) with W =
+    ceil(largest count / 64).  On the parent's device."""
     _contig("parent", parent)
-    B, N = parent.shape
+    no, nmax = _node_off(node_off)
+    if no is None:
+        B, N = parent.shape
+        rows = (B, N)
+    else:
+        B, N = len(no) - 1, nmax
+        rows = (parent.shape[0],)
     W = (N + 63) // 64
     dev = parent.device
     if mask is None:
-        mask = torch.empty((B, N, W), dtype=torch.int64, device=dev)
+        mask = torch.empty(rows + (W,), dtype=torch.int64, device=dev)
     if depth is None:
-        depth = torch.empty((B, N), dtype=torch.int32, device=dev)
+        depth = torch.empty(rows, dtype=torch.int32, device=dev)
     if seq_status is None:
         seq_status = torch.empty((B,), dtype=torch.int32, device=dev)
-    st = lib().jf_tree_mask_build(_p(parent), B, N, _p(mask), _p(depth), _p(seq_status),
-                                  _stream(stream))
+    st = lib().jf_tree_mask_build(_p(parent), None if no is None else no.ctypes.data_as(ctypes.c_void_p),
+                                  B, N, _p(mask), _p(depth), _p(seq_status), _stream(stream))
     _check("jf_tree_mask_build", st)
     return mask, depth, seq_status
 
@@ -199,53 +219,77 @@ def _host_i32(a) -> np.ndarray:
 
 
 def jf_tree_attn_workspace_size(B: int, N: int, Hq: int, Hkv: int, D: int, page_size: int,
-                                prefix_len, dtype: int, cus: int = 0) -> int:
+                                prefix_len, dtype: int, cus: int = 0, node_off=None) -> int:
     """cus > 0: the plan of jf_tree_attn_fwd(..., cus=cus) (see jf_tree_attn_fwd_cus)."""
     pl = _host_i32(prefix_len)
+    no, _ = _node_off(node_off)
+    nop = None if no is None else no.ctypes.data_as(ctypes.c_void_p)
     if cus > 0:
         return int(lib().jf_tree_attn_workspace_size_cus(B, N, Hq, Hkv, D, page_size,
-                                                         pl.ctypes.data_as(ctypes.c_void_p), dtype, cus))
+                                                         pl.ctypes.data_as(ctypes.c_void_p), nop,
+                                                         dtype, cus))
     return int(lib().jf_tree_attn_workspace_size(B, N, Hq, Hkv, D, page_size,
-                                                 pl.ctypes.data_as(ctypes.c_void_p), dtype))
+                                                 pl.ctypes.data_as(ctypes.c_void_p), nop, dtype))
+
+
+def _kv_code(t: torch.Tensor) -> int:
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return JF_FP8_E4M3
+    return _dtype_code(t)
 
 
 def jf_tree_attn_fwd(q, k_tree, v_tree, mask, k_cache, v_cache, block_table, prefix_len,
                      scale: float = 0.0, out=None, lse=None, with_lse: bool = True,
-                     workspace=None, page_status=None, stream=None, cus: int = 0):
-    """Tree attention.  q [B,N,Hq,D]; k_tree/v_tree [B,N,Hkv,D]; mask from
-    jf_tree_mask_build; k_cache/v_cache [num_pages, page_size, Hkv, D];
-    block_table [B, max_pages] int32 (device); prefix_len host ints [B].
-    cus > 0 plans the key splits for that many compute units
-    (jf_tree_attn_fwd_cus); the workspace must then be sized with the same cus."""
+                     workspace=None, status=None, stream=None, cus: int = 0,
+                     prefix_len_dev=None, node_off=None, k_scale: float = 1.0,
+                     v_scale: float = 1.0):
+    """Tree attention.  Uniform trees: q [B,N,Hq,D], k_tree/v_tree [B,N,Hkv,D];
+    packed trees (host node_off [B+1]): q [T,Hq,D], k_tree/v_tree [T,Hkv,D].
+    mask from jf_tree_mask_build; k_cache/v_cache [num_pages, page_size, Hkv, D]
+    of q's dtype, or E4M3 codes (uint8 / float8_e4m3fn) with per-tensor scales
+    k_scale / v_scale; block_table [B, max_pages] int32 (device); prefix_len
+    host ints [B]: the lengths, or their upper bounds when prefix_len_dev (a
+    device int32 [B] tensor) gives the lengths.  cus > 0 plans the key splits
+    for that many compute units (jf_tree_attn_fwd_cus); the workspace must
+    then be sized with the same cus.  status: a device int32 word for data
+    errors (bad page id, device prefix length outside its bound)."""
     for n, t in (("q", q), ("k_tree", k_tree), ("v_tree", v_tree), ("mask", mask),
                  ("k_cache", k_cache), ("v_cache", v_cache), ("block_table", block_table)):
         _contig(n, t)
-    B, N, Hq, D = q.shape
-    Hkv = k_tree.shape[2]
+    no, nmax = _node_off(node_off)
+    if no is None:
+        B, N, Hq, D = q.shape
+        Hkv = k_tree.shape[2]
+    else:
+        B, N = len(no) - 1, nmax
+        _, Hq, D = q.shape
+        Hkv = k_tree.shape[1]
     num_pages, page_size = k_cache.shape[0], k_cache.shape[1]
     max_pages = block_table.shape[1]
     dt = _dtype_code(q)
+    kv = _kv_code(k_cache)
     pl = _host_i32(prefix_len)
+    if prefix_len_dev is not None:
+        _contig("prefix_len_dev", prefix_len_dev)
+        if prefix_len_dev.dtype != torch.int32 or prefix_len_dev.shape != (B,):
+            raise ValueError("prefix_len_dev must be a device int32 [B] tensor")
     if out is None:
         out = torch.empty_like(q)
     if lse is None and with_lse:
-        lse = torch.empty((B, N, Hq), dtype=torch.float32, device=q.device)
-    need = jf_tree_attn_workspace_size(B, N, Hq, Hkv, D, page_size, pl, dt, cus)
+        lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+    need = jf_tree_attn_workspace_size(B, N, Hq, Hkv, D, page_size, pl, dt, cus, no)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    nop = None if no is None else no.ctypes.data_as(ctypes.c_void_p)
+    args = [_p(q), _p(k_tree), _p(v_tree), _p(mask), _p(k_cache), _p(v_cache), kv, float(k_scale),
+            float(v_scale), num_pages, page_size, _p(block_table), max_pages,
+            pl.ctypes.data_as(ctypes.c_void_p), _p(prefix_len_dev), nop, B, N, Hq, Hkv, D,
+            float(scale), dt, _p(out), _p(lse), _p(workspace), ws_bytes, _p(status)]
     if cus > 0:
-        st = lib().jf_tree_attn_fwd_cus(_p(q), _p(k_tree), _p(v_tree), _p(mask), _p(k_cache),
-                                        _p(v_cache), num_pages, page_size, _p(block_table), max_pages,
-                                        pl.ctypes.data_as(ctypes.c_void_p), B, N, Hq, Hkv, D,
-                                        float(scale), dt, _p(out), _p(lse), _p(workspace), ws_bytes,
-                                        _p(page_status), int(cus), _stream(stream))
+        st = lib().jf_tree_attn_fwd_cus(*args, int(cus), _stream(stream))
     else:
-        st = lib().jf_tree_attn_fwd(_p(q), _p(k_tree), _p(v_tree), _p(mask), _p(k_cache), _p(v_cache),
-                                    num_pages, page_size, _p(block_table), max_pages,
-                                    pl.ctypes.data_as(ctypes.c_void_p), B, N, Hq, Hkv, D,
-                                    float(scale), dt, _p(out), _p(lse), _p(workspace), ws_bytes,
-                                    _p(page_status), _stream(stream))
+        st = lib().jf_tree_attn_fwd(*args, _stream(stream))
     _check("jf_tree_attn_fwd", st)
     return out, lse
 
