@@ -20,9 +20,10 @@ def host_f64(t: torch.Tensor) -> np.ndarray:
 
 def upload_attn(inp):
     dt = inp["dtype"]
+    kv = None if inp.get("kv_dtype") == "fp8" else dt      # FP8 caches travel as raw bytes
     return dict(q=dev_tensor(inp["q"], dt), k_tree=dev_tensor(inp["k_tree"], dt),
-                v_tree=dev_tensor(inp["v_tree"], dt), k_cache=dev_tensor(inp["k_cache"], dt),
-                v_cache=dev_tensor(inp["v_cache"], dt), parent=dev_tensor(inp["parent"]),
+                v_tree=dev_tensor(inp["v_tree"], dt), k_cache=dev_tensor(inp["k_cache"], kv),
+                v_cache=dev_tensor(inp["v_cache"], kv), parent=dev_tensor(inp["parent"]),
                 block_table=dev_tensor(inp["block_table"]))
 
 

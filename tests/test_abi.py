@@ -98,6 +98,9 @@ def test_attn_argument_errors():
     assert _attn(L, kv=9) == jf.JF_ERR_INVALID_ARG
     assert _attn(L, kv=jf.JF_F32) == jf.JF_ERR_UNSUPPORTED       # the cache must match q or be FP8
     assert _attn(L, kv=jf.JF_FP8_E4M3, dtype=jf.JF_F32) == jf.JF_ERR_UNSUPPORTED
+    assert _attn(L, kv=jf.JF_FP8_E4M3, ks=0.0) == jf.JF_ERR_INVALID_ARG       # scales must be > 0
+    assert _attn(L, kv=jf.JF_FP8_E4M3, vs=-1.0) == jf.JF_ERR_INVALID_ARG
+    assert _attn(L, kv=jf.JF_FP8_E4M3, vs=float("inf")) == jf.JF_ERR_INVALID_ARG
     # packed trees: offsets from 0, every sequence has nodes, N is the largest count
     assert _attn(L, no=[0, 3, 11]) != jf.JF_ERR_INVALID_ARG      # counts 3 and 8
     assert _attn(L, no=[1, 3, 8]) == jf.JF_ERR_INVALID_ARG

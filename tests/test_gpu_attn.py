@@ -334,3 +334,54 @@ def test_device_prefix_length_above_its_bound_is_clamped_and_flagged():
     assert int(st.item()) == jf.JF_ERR_BAD_PREFIX
     ro, rl = oracle_attn(inp, prefix_len=np.array([500, 0], np.int32))
     check(inp, out, lse, ro, rl)
+
+
+# ---------------------------------------------------------------------------
+# FP8 (E4M3) prefix caches with per-tensor scales
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_fp8_cache_small_all_rows(paged):
+    # prefixes of 0, 1, 63, 64, 65 and 700 tokens; 100 nodes (two tree blocks)
+    inp = synth.make_attn_inputs(B=6, N=100, Hq=8, Hkv=2, D=128, dtype="bf16",
+                                 prefix_lens=[0, 1, 63, 64, 65, 700], page_size=16 if paged else 0,
+                                 shuffled_pages=paged, seed=80, kv_dtype="fp8")
+    compare(inp, label="fp8 ragged")
+
+
+def test_fp8_cache_splits_of_prefix_only_and_tree_only():
+    # 4096 prefix tokens and 256 nodes split over many work items: some splits
+    # hold only prefix blocks, some only tree blocks, one both
+    inp = synth.make_attn_inputs(B=1, N=256, Hq=32, Hkv=8, D=128, dtype="bf16",
+                                 prefix_lens=[4096], seed=81, kv_dtype="fp8")
+    compare(inp, label="fp8 n256")
+    compare(inp, label="fp8 n256", cus=7)
+
+
+def test_fp8_cache_serving_batch():
+    # the serving workload's shape: 32 sequences, prefixes U[512, 8192],
+    # shuffled 16-token pages, 64-node trees, FP8 prefix cache
+    w = synth.workload(3)
+    P = synth.prefix_lengths(3)
+    inp = synth.make_attn_inputs(B=w.B, N=w.N, Hq=w.Hq, Hkv=w.Hkv, D=w.D, dtype="bf16",
+                                 prefix_lens=P, page_size=w.page_size, shuffled_pages=True,
+                                 max_depth=w.max_depth, branching=w.branching, seed=82,
+                                 kv_dtype="fp8")
+    compare(inp, rows=tile_rows(inp, 4096, 8), label="fp8 serving b32")
+
+
+def test_fp8_cache_packed_with_device_prefix_lengths():
+    counts = np.random.default_rng(83).choice([16, 64, 256], size=8)
+    inp = _serving_packed(84, counts, kv_dtype="fp8")
+    real = (inp["prefix_len"] * 0.6).astype(np.int32)
+    compare(inp, rows=tile_rows(inp, 2048, 9), label="fp8 packed", prefix_dev=real)
+
+
+def test_fp8_bad_page_reads_zero():
+    inp = synth.make_attn_inputs(B=2, N=8, Hq=4, Hkv=1, D=128, dtype="bf16", prefix_lens=[40, 20],
+                                 page_size=16, seed=85, kv_dtype="fp8")
+    inp["block_table"][1, 0] = inp["num_pages"] + 5
+    ps = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    out, lse = run_gpu(inp, status=ps)
+    assert int(ps.item()) == jf.JF_ERR_BAD_PAGE
+    ro, rl, flag = oracle_attn(inp, bad_page_ok=True)
+    check(inp, out, lse, ro, rl)

@@ -205,7 +205,10 @@ jf_status jf_tree_attn_fwd_cus(const void *q, const void *k_tree, const void *v_
     if (st != JF_OK) return st;
     if (kv_dtype != JF_F32 && kv_dtype != JF_BF16 && kv_dtype != JF_FP8_E4M3)
         return JF_ERR_INVALID_ARG;
-    if (kv_dtype != dtype) return JF_ERR_UNSUPPORTED;
+    const bool fp8 = kv_dtype == JF_FP8_E4M3;
+    if (kv_dtype != dtype && !(fp8 && dtype == JF_BF16)) return JF_ERR_UNSUPPORTED;
+    if (fp8 && !(k_scale > 0.f && v_scale > 0.f && k_scale < INFINITY && v_scale < INFINITY))
+        return JF_ERR_INVALID_ARG;
     if (page_size < 1 || max_pages < 1 || num_pages < 0) return JF_ERR_INVALID_ARG;
     for (int b = 0; b < B; ++b)
         if ((int64_t)prefix_len[b] > (int64_t)max_pages * page_size) return JF_ERR_INVALID_ARG;
@@ -219,7 +222,7 @@ jf_status jf_tree_attn_fwd_cus(const void *q, const void *k_tree, const void *v_
     if (dtype == JF_BF16) {
         // the bf16 kernel addresses each tensor with 32-bit buffer offsets
         const int64_t lim = 0xffffff00LL;
-        if (num_pages * page_size * (int64_t)Hkv * D * 2 > lim || T * Hq * D * 2 > lim ||
+        if (num_pages * page_size * (int64_t)Hkv * D * (fp8 ? 1 : 2) > lim || T * Hq * D * 2 > lim ||
             T * Hkv * D * 2 > lim)
             return JF_ERR_UNSUPPORTED;
     }
@@ -232,8 +235,8 @@ jf_status jf_tree_attn_fwd_cus(const void *q, const void *k_tree, const void *v_
         if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
             return JF_ERR_WORKSPACE;
         e = launch_tree_attn_bf16(p, q, k_tree, v_tree, mask, k_cache, v_cache, num_pages, page_size,
-                                  block_table, max_pages, prefix_len_dev, scale, out, lse, workspace,
-                                  status, (hipStream_t)stream);
+                                  block_table, max_pages, prefix_len_dev, scale, fp8, k_scale,
+                                  v_scale, out, lse, workspace, status, (hipStream_t)stream);
     } else {
         e = launch_tree_attn_f32(p, (const float *)q, (const float *)k_tree, (const float *)v_tree,
                                  mask, (const float *)k_cache, (const float *)v_cache, num_pages,

@@ -144,7 +144,8 @@ hipError_t launch_tree_attn_bf16(const AttnPlan &p, const void *q, const void *k
                                  const void *k_cache, const void *v_cache,
                                  int64_t num_pages, int page_size,
                                  const int32_t *block_table, int max_pages,
-                                 const int32_t *prefix_dev, float scale,
+                                 const int32_t *prefix_dev, float scale, bool fp8,
+                                 float k_scale, float v_scale,
                                  void *out, float *lse, void *workspace,
                                  int32_t *status, hipStream_t s);
 hipError_t launch_tree_attn_f32(const AttnPlan &p, const float *q, const float *k_tree,

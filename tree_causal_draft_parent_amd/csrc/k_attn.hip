@@ -92,6 +92,7 @@ struct AttnArgs {
     int page_mode;  // 1: one page per sequence; 2: power-of-two pages >= 16; 0: other
     int page_size, page_shift, max_pages, B, Hq, Hkv, G, W, chunk_blocks, total_items;
     float scale, c2, lazy_raw;
+    float k_scale, v_scale, c2k;     // FP8 caches: value = code * scale; c2k = c2 * k_scale
     int cap[kMaxBatch];              // planned prefix bound of each sequence
     int node_off[kMaxBatch + 1];     // tree rows of sequence b: node_off[b] .. node_off[b+1]-1
     int item_start[kMaxBatch + 1];   // first work item of sequence b
@@ -174,6 +175,8 @@ struct SplitCtx {
     const uint16_t *kt0, *vt0;               // KV head g of tree row 0 of the sequence
     int64_t node0;                           // first tree row of the sequence
     int b, g, P, nPB, n, page0, lane, wave;  // n: the sequence's tree nodes
+    const uint8_t *kc8, *vc8;                // FP8 one-page layout: KV head g of prefix row 0
+    uint32_t rowb8;                          // FP8 bytes between consecutive prefix keys
     bool pzero;                              // one-page layout with a bad page id: zeros
     uint32_t rowb;                           // bytes between consecutive keys
     uint32_t vrow;                           // lane's offset of its first copy in a block
@@ -331,7 +334,14 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // kPaged = false: every prefix is one page (page_mode 1); true: page_mode 0 or 2.
-template <bool kPaged>
+// kFp8: the prefix cache holds E4M3 codes; each prefix block is loaded into
+// registers one block ahead, converted exactly to bf16 and written into the
+// same LDS layout the bf16 copies produce (tree blocks are bf16 and copied
+// as usual).  Scores of prefix keys are scaled by k_scale through the
+// exponent coefficient and the block maximum; the output accumulator holds
+// prefix values in code units until the split's first tree block (or the
+// end), where it is multiplied by v_scale once.
+template <bool kPaged, bool kFp8>
 __global__ __launch_bounds__(kNW * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_tree_attn_split(AttnArgs a) {
     __shared__ __attribute__((aligned(1024))) char ring[kNS][kStage];
@@ -382,6 +392,9 @@ void k_tree_attn_split(AttnArgs a) {
     c.vt0 = uniform_ptr(a.v_tree + (node0 * a.Hkv + g) * kD);
     c.kc0 = a.k_cache;
     c.vc0 = a.v_cache;
+    c.kc8 = (const uint8_t *)a.k_cache;
+    c.vc8 = (const uint8_t *)a.v_cache;
+    c.rowb8 = (uint32_t)a.Hkv * kD;
     c.pzero = false;
     // ---- this lane's query row and mask dword ----
     const int r = qt * kTQ + wave * 32 + l32;
@@ -408,8 +421,13 @@ void k_tree_attn_split(AttnArgs a) {
                 const int page = __builtin_amdgcn_readfirstlane(bt[0]);
                 if (page >= 0 && page < a.num_pages) {
                     const int64_t e0 = ((int64_t)page * a.page_size * a.Hkv + g) * kD;
-                    c.kc0 = uniform_ptr(a.k_cache + e0);
-                    c.vc0 = uniform_ptr(a.v_cache + e0);
+                    if constexpr (kFp8) {
+                        c.kc8 = (const uint8_t *)a.k_cache + e0;
+                        c.vc8 = (const uint8_t *)a.v_cache + e0;
+                    } else {
+                        c.kc0 = uniform_ptr(a.k_cache + e0);
+                        c.vc0 = uniform_ptr(a.v_cache + e0);
+                    }
                 } else {
                     c.pzero = true;     // the prefix reads as zero keys and values
                     if (tid == 0) s_bad = 1;
@@ -504,16 +522,18 @@ void k_tree_attn_split(AttnArgs a) {
     // waiting for block 0 leaves the later blocks in flight.
     int kb_iss = next_vis(kb0);         // next block to issue
     int n_iss = 0;                      // blocks issued so far
-    if (kb_iss < kb1) {
-        issue_block<kPaged>(a, c, s_pages, ring0, kb_iss, bad);
-        kb_iss = next_vis(kb_iss + 1);
-        n_iss = 1;
+    if constexpr (!kFp8) {
+        if (kb_iss < kb1) {
+            issue_block<kPaged>(a, c, s_pages, ring0, kb_iss, bad);
+            kb_iss = next_vis(kb_iss + 1);
+            n_iss = 1;
+        }
+        for (; n_iss < kNS - 1 && kb_iss < kb1; ++n_iss) {
+            issue_block<kPaged>(a, c, s_pages, ring0 + (n_iss % kNS) * kStage, kb_iss, bad);
+            kb_iss = next_vis(kb_iss + 1);
+        }
     }
     bf16x8 qf[kD / 16];                 // set from qraw after the first wait
-    for (; n_iss < kNS - 1 && kb_iss < kb1; ++n_iss) {
-        issue_block<kPaged>(a, c, s_pages, ring0 + (n_iss % kNS) * kStage, kb_iss, bad);
-        kb_iss = next_vis(kb_iss + 1);
-    }
 
     // ---- per-block pieces ----
     const int koff = k_lds(l32) + half * 16;                             // row l32, chunk half
@@ -598,8 +618,10 @@ void k_tree_attn_split(AttnArgs a) {
     // boundary pass the slot's MFMA results and VALU results through, and the
     // scores later slots read, so no optimisation can move work between
     // slots.
+    // cj: exponent coefficient of block j's raw scores (c2, or c2 * k_scale
+    // for an FP8 prefix block)
     auto step = [&](auto next_tag, const lds_t *stj, const lds_t *stn, int kbn,
-                    f32x16 &sc0, f32x16 &sc1, f32x16 &sn0, f32x16 &sn1) -> float {
+                    f32x16 &sc0, f32x16 &sc1, f32x16 &sn0, f32x16 &sn1, float cj) -> float {
         constexpr bool has_next = decltype(next_tag)::value;
         const float nb = S.m == -INFINITY ? 0.f : -S.m * a.c2;
         float ls[2] = {0.f, 0.f};                  // two partial row sums: shorter dependency chains
@@ -607,8 +629,8 @@ void k_tree_attn_split(AttnArgs a) {
         // exps of registers i, i+1 of tile sx as one bf16 pair; the row sum
         // uses the same bf16 probabilities as the MFMA
         auto exp_pair = [&](const f32x16 &sx, int i) -> uint32_t {
-            const float e0 = __builtin_amdgcn_exp2f(fmaf(sx[i], a.c2, nb));
-            const float e1 = __builtin_amdgcn_exp2f(fmaf(sx[i + 1], a.c2, nb));
+            const float e0 = __builtin_amdgcn_exp2f(fmaf(sx[i], cj, nb));
+            const float e1 = __builtin_amdgcn_exp2f(fmaf(sx[i + 1], cj, nb));
             const uint32_t w = pack_bf16x2(e0, e1);
             float &acc = ls[(i >> 1) & 1];
             acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w),
@@ -692,52 +714,182 @@ void k_tree_attn_split(AttnArgs a) {
 
     // ---- main loop over the visible blocks ----
     int kb_cur = next_vis(kb0);
-    const int n_vis_first = n_iss;      // blocks in flight before the first wait
     f32x16 sa0, sa1, sb0, sb1;
     float mx_cur = -INFINITY;
-    if (kb_cur < kb1) {
-        ring_wait((n_vis_first - 1) * kOps);          // block 0 and the queries have landed
-        asm volatile("" : "+v"(qraw[0]), "+v"(qraw[1]), "+v"(qraw[2]), "+v"(qraw[3]),
-                          "+v"(qraw[4]), "+v"(qraw[5]), "+v"(qraw[6]), "+v"(qraw[7]));
-#pragma unroll
-        for (int t = 0; t < kD / 16; ++t) qf[t] = as_bf16x8(qraw[t]);
-        qk(stage_of(0), sa0, sa1);
-        apply_mask(stage_of(0), kb_cur, sa0, sa1);
-        mx_cur = row_max(sa0, sa1);
-    }
     int j = 0;
-    // block j with a visible successor kb_nxt (which has landed after the wait)
-    auto iter_next = [&](f32x16 &sc0, f32x16 &sc1, f32x16 &sn0, f32x16 &sn1, int kb_nxt) {
-        ring_wait((n_iss - (j + 2)) * kOps);            // blocks issued after j+1 stay in flight
-        if (kb_iss < kb1) {                             // the stage of block j-1 is free
-            issue_block<kPaged>(a, c, s_pages, ring0 + (n_iss % kNS) * kStage, kb_iss, bad);
-            kb_iss = next_vis(kb_iss + 1);
-            ++n_iss;
+    bool o_codes = kFp8;                // FP8: O holds prefix values in code units
+    auto to_values = [&]() {            // O from code units to values (once)
+        if (kFp8 && o_codes) {
+#pragma unroll
+            for (int d = 0; d < kD / 32; ++d)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) S.o[d][i] *= a.v_scale;
+            o_codes = false;
         }
-        rescale(mx_cur);
-        mx_cur = step(Flag<true>{}, stage_of(j), stage_of(j + 1), kb_nxt, sc0, sc1, sn0, sn1);
-        kb_cur = kb_nxt;
-        ++j;
     };
-    // the last visible block (it landed before the previous step)
-    auto iter_last = [&](f32x16 &sc0, f32x16 &sc1) {
-        rescale(mx_cur);
-        step(Flag<false>{}, stage_of(j), stage_of(j), kb_cur, sc0, sc1, sc0, sc1);
-    };
-    if (kb_cur < kb1) {
-        // the loop only runs blocks with a successor (the last block's step is
-        // outside it, which keeps the loop's register pressure down)
-        bool in_b = false;                              // the last block's scores sit in sb
-        for (;;) {
-            int kn = next_vis(kb_cur + 1);
-            if (kn >= kb1) break;
-            iter_next(sa0, sa1, sb0, sb1, kn);
-            kn = next_vis(kb_cur + 1);
-            if (kn >= kb1) { in_b = true; break; }
-            iter_next(sb0, sb1, sa0, sa1, kn);
+    if constexpr (!kFp8) {
+        const int n_vis_first = n_iss;      // blocks in flight before the first wait
+        if (kb_cur < kb1) {
+            ring_wait((n_vis_first - 1) * kOps);          // block 0 and the queries have landed
+            asm volatile("" : "+v"(qraw[0]), "+v"(qraw[1]), "+v"(qraw[2]), "+v"(qraw[3]),
+                              "+v"(qraw[4]), "+v"(qraw[5]), "+v"(qraw[6]), "+v"(qraw[7]));
+#pragma unroll
+            for (int t = 0; t < kD / 16; ++t) qf[t] = as_bf16x8(qraw[t]);
+            qk(stage_of(0), sa0, sa1);
+            apply_mask(stage_of(0), kb_cur, sa0, sa1);
+            mx_cur = row_max(sa0, sa1);
         }
-        if (in_b) iter_last(sb0, sb1);
-        else iter_last(sa0, sa1);
+        // block j with a visible successor kb_nxt (which has landed after the wait)
+        auto iter_next = [&](f32x16 &sc0, f32x16 &sc1, f32x16 &sn0, f32x16 &sn1, int kb_nxt) {
+            ring_wait((n_iss - (j + 2)) * kOps);            // blocks issued after j+1 stay in flight
+            if (kb_iss < kb1) {                             // the stage of block j-1 is free
+                issue_block<kPaged>(a, c, s_pages, ring0 + (n_iss % kNS) * kStage, kb_iss, bad);
+                kb_iss = next_vis(kb_iss + 1);
+                ++n_iss;
+            }
+            rescale(mx_cur);
+            mx_cur = step(Flag<true>{}, stage_of(j), stage_of(j + 1), kb_nxt, sc0, sc1, sn0, sn1, a.c2);
+            kb_cur = kb_nxt;
+            ++j;
+        };
+        // the last visible block (it landed before the previous step)
+        auto iter_last = [&](f32x16 &sc0, f32x16 &sc1) {
+            rescale(mx_cur);
+            step(Flag<false>{}, stage_of(j), stage_of(j), kb_cur, sc0, sc1, sc0, sc1, a.c2);
+        };
+        if (kb_cur < kb1) {
+            // the loop only runs blocks with a successor (the last block's step is
+            // outside it, which keeps the loop's register pressure down)
+            bool in_b = false;                              // the last block's scores sit in sb
+            for (;;) {
+                int kn = next_vis(kb_cur + 1);
+                if (kn >= kb1) break;
+                iter_next(sa0, sa1, sb0, sb1, kn);
+                kn = next_vis(kb_cur + 1);
+                if (kn >= kb1) { in_b = true; break; }
+                iter_next(sb0, sb1, sa0, sa1, kn);
+            }
+            if (in_b) iter_last(sb0, sb1);
+            else iter_last(sa0, sa1);
+        }
+    } else {
+        // FP8 prefix blocks, one block in flight.  Thread t moves 16 codes
+        // (head dims 16 (t % 8) .. +15) of key row t / 8 of the K and V tiles.
+        const int r8 = tid >> 3, c8 = tid & 7;
+        __amdgpu_buffer_rsrc_t rk8, rv8;
+        if constexpr (!kPaged) {
+            const uint32_t nbytes = c.pzero ? 0u : (uint32_t)P * c.rowb8;
+            rk8 = make_rsrc(c.kc8, nbytes);
+            rv8 = make_rsrc(c.vc8, nbytes);
+        } else {
+            rk8 = make_rsrc(a.k_cache, a.cache_bytes);
+            rv8 = make_rsrc(a.v_cache, a.cache_bytes);
+        }
+        u32x4 k8 = {0u, 0u, 0u, 0u}, v8 = {0u, 0u, 0u, 0u};
+        auto issue8 = [&](int kb, int slot) {
+            if (kb >= nPB) {                              // tree block: bf16 copies as usual
+                issue_block<kPaged>(a, c, s_pages, ring0 + slot * kStage, kb, bad);
+                return;
+            }
+            const int pos = kb * kKB + r8;
+            uint32_t off = kOob;
+            if (pos < P) {
+                if constexpr (!kPaged) {
+                    off = (uint32_t)pos * c.rowb8 + c8 * 16u;
+                } else {
+                    int pg, slot_in;
+                    if (a.page_shift >= 0) {
+                        pg = pos >> a.page_shift;
+                        slot_in = pos & (a.page_size - 1);
+                    } else {
+                        pg = pos / a.page_size;
+                        slot_in = pos - pg * a.page_size;
+                    }
+                    const int page = s_pages[pg - c.page0];
+                    if (page >= 0 && page < a.num_pages)
+                        off = (((uint32_t)page * a.page_size + slot_in) * a.Hkv + g) * kD + c8 * 16u;
+                    else
+                        bad = true;
+                }
+            }
+            k8 = __builtin_amdgcn_raw_buffer_load_b128(rk8, off, 0, 0);
+            v8 = __builtin_amdgcn_raw_buffer_load_b128(rv8, off, 0, 0);
+        };
+        // wait for this wave's loads of block kb, then (a prefix block) write
+        // its codes as bf16 into stage `slot` (E4M3 -> bf16 is exact)
+        auto commit8 = [&](int kb, int slot) {
+            __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xf << 8));   // vmcnt(0)
+            if (kb >= nPB) return;
+            lds_t *st = (lds_t *)&ring[slot][0];
+            auto cvt16 = [](const u32x4 &x, u32x4 &lo, u32x4 &hi) {
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const uint32_t e01 = __builtin_bit_cast(uint32_t,
+                        __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w], 1.0f, false));
+                    const uint32_t e23 = __builtin_bit_cast(uint32_t,
+                        __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w], 1.0f, true));
+                    if (w < 2) { lo[2 * w] = e01; lo[2 * w + 1] = e23; }
+                    else { hi[2 * (w - 2)] = e01; hi[2 * (w - 2) + 1] = e23; }
+                }
+            };
+            u32x4 lo, hi;
+            cvt16(k8, lo, hi);
+            lds_t *kp = st + k_lds(r8) + c8 * 32;
+            *(__attribute__((address_space(3))) u32x4 *)kp = lo;
+            *(__attribute__((address_space(3))) u32x4 *)(kp + 16) = hi;
+            cvt16(v8, lo, hi);
+            lds_t *vp = st + kKTile + v_lds(r8) + c8 * 32;
+            *(__attribute__((address_space(3))) u32x4 *)vp = lo;
+            *(__attribute__((address_space(3))) u32x4 *)(vp + 16) = hi;
+        };
+        auto scaled_max = [&](float mx, int kb) { return kb < nPB ? mx * a.k_scale : mx; };
+        auto coef = [&](int kb) { return kb < nPB ? a.c2k : a.c2; };
+        if (kb_cur < kb1) {
+            issue8(kb_cur, 0);
+            commit8(kb_cur, 0);                           // also waits for the queries
+            lds_barrier();
+            asm volatile("" : "+v"(qraw[0]), "+v"(qraw[1]), "+v"(qraw[2]), "+v"(qraw[3]),
+                              "+v"(qraw[4]), "+v"(qraw[5]), "+v"(qraw[6]), "+v"(qraw[7]));
+#pragma unroll
+            for (int t = 0; t < kD / 16; ++t) qf[t] = as_bf16x8(qraw[t]);
+            const int kn = next_vis(kb_cur + 1);
+            if (kn < kb1) issue8(kn, 1);
+            qk(stage_of(0), sa0, sa1);
+            apply_mask(stage_of(0), kb_cur, sa0, sa1);
+            mx_cur = scaled_max(row_max(sa0, sa1), kb_cur);
+        }
+        auto iter_next = [&](f32x16 &sc0, f32x16 &sc1, f32x16 &sn0, f32x16 &sn1, int kb_nxt) {
+            commit8(kb_nxt, (j + 1) % kNS);               // block j+1 into its stage
+            lds_barrier();                                // ... visible to every wave
+            const int kn = next_vis(kb_nxt + 1);
+            if (kn < kb1) issue8(kn, (j + 2) % kNS);      // the stage of block j-2 is free
+            rescale(mx_cur);
+            if (kb_cur >= nPB) to_values();
+            const float mx = step(Flag<true>{}, stage_of(j), stage_of(j + 1), kb_nxt, sc0, sc1, sn0, sn1,
+                                  coef(kb_cur));
+            mx_cur = scaled_max(mx, kb_nxt);
+            kb_cur = kb_nxt;
+            ++j;
+        };
+        auto iter_last = [&](f32x16 &sc0, f32x16 &sc1) {
+            rescale(mx_cur);
+            if (kb_cur >= nPB) to_values();
+            step(Flag<false>{}, stage_of(j), stage_of(j), kb_cur, sc0, sc1, sc0, sc1, coef(kb_cur));
+        };
+        if (kb_cur < kb1) {
+            bool in_b = false;
+            for (;;) {
+                int kn = next_vis(kb_cur + 1);
+                if (kn >= kb1) break;
+                iter_next(sa0, sa1, sb0, sb1, kn);
+                kn = next_vis(kb_cur + 1);
+                if (kn >= kb1) { in_b = true; break; }
+                iter_next(sb0, sb1, sa0, sa1, kn);
+            }
+            if (in_b) iter_last(sb0, sb1);
+            else iter_last(sa0, sa1);
+        }
+        to_values();                                      // a split of prefix blocks only
     }
 
     if (bad) s_bad = 1;  // benign race: every writer stores 1
@@ -1106,8 +1258,9 @@ hipError_t launch_tree_attn_bf16(const AttnPlan &p, const void *q, const void *k
                                  const void *v_tree, const uint64_t *mask, const void *k_cache,
                                  const void *v_cache, int64_t num_pages, int page_size,
                                  const int32_t *block_table, int max_pages,
-                                 const int32_t *prefix_dev, float scale, void *out, float *lse,
-                                 void *workspace, int32_t *status, hipStream_t s) {
+                                 const int32_t *prefix_dev, float scale, bool fp8, float k_scale,
+                                 float v_scale, void *out, float *lse, void *workspace,
+                                 int32_t *status, hipStream_t s) {
     AttnArgs a;
     a.q = (const uint16_t *)q;
     a.k_tree = (const uint16_t *)k_tree;
@@ -1126,7 +1279,7 @@ hipError_t launch_tree_attn_bf16(const AttnPlan &p, const void *q, const void *k
     const int64_t T = p.node_off[p.B];
     a.q_bytes = (uint32_t)(T * p.Hq * kD * 2);
     a.tree_bytes = (uint32_t)(T * p.Hkv * kD * 2);
-    a.cache_bytes = (uint32_t)(num_pages * page_size * (int64_t)p.Hkv * kD * 2);
+    a.cache_bytes = (uint32_t)(num_pages * page_size * (int64_t)p.Hkv * kD * (fp8 ? 1 : 2));
     a.mask_bytes = (uint32_t)(T * p.W * 8);
     a.num_pages = num_pages;
     a.page_size = page_size;
@@ -1149,15 +1302,22 @@ hipError_t launch_tree_attn_bf16(const AttnPlan &p, const void *q, const void *k
     a.scale = scale;
     a.c2 = scale * kLog2e;
     a.lazy_raw = kLazyLog2 / a.c2;
+    a.k_scale = fp8 ? k_scale : 1.f;
+    a.v_scale = fp8 ? v_scale : 1.f;
+    a.c2k = a.c2 * a.k_scale;
     for (int b = 0; b < p.B; ++b) a.cap[b] = p.cap[b];
     for (int b = 0; b <= p.B; ++b) {
         a.node_off[b] = p.node_off[b];
         a.item_start[b] = p.item_start[b];
     }
-    if (a.page_mode == 1)
-        hipLaunchKernelGGL(k_tree_attn_split<false>, dim3(p.total_items), dim3(kNW * kWave), 0, s, a);
-    else
-        hipLaunchKernelGGL(k_tree_attn_split<true>, dim3(p.total_items), dim3(kNW * kWave), 0, s, a);
+    const dim3 grid(p.total_items), block(kNW * kWave);
+    if (a.page_mode == 1) {
+        if (fp8) hipLaunchKernelGGL((k_tree_attn_split<false, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((k_tree_attn_split<false, false>), grid, block, 0, s, a);
+    } else {
+        if (fp8) hipLaunchKernelGGL((k_tree_attn_split<true, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((k_tree_attn_split<true, false>), grid, block, 0, s, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !p.any_split) return e;
     const int64_t per_seq = (int64_t)p.N * p.Hq;
