@@ -60,11 +60,13 @@ def test_traffic_freshness_follows_the_calls_kernel_file(tmp_path, monkeypatch):
     path = tmp_path / "traffic.json"
     path.write_text(json.dumps(rec))
     monkeypatch.setattr(bench, "TRAFFIC_JSON", str(path))
-    assert bench.measured_traffic("fuse", "w") == 19
-    assert bench.measured_traffic("fuse", "other") is None
+    total, src = bench.measured_traffic("fuse", "w")
+    assert total == 19 and "k_fuse.hip sha256" in src and "traffic.json" in src
+    assert bench.measured_traffic("fuse", "other")[0] is None
     rec["file_sha256"]["k_fuse.hip"] = "changed"
     path.write_text(json.dumps(rec))
-    assert bench.measured_traffic("fuse", "w") is None
+    total, src = bench.measured_traffic("fuse", "w")
+    assert total is None and "changed" in src
 
 
 def test_trace_split_by_grid(tmp_path, capsys):
@@ -81,3 +83,24 @@ def test_trace_split_by_grid(tmp_path, capsys):
     profsum.main(["stats", str(d), "--by-grid"])
     out = capsys.readouterr().out
     assert "607744" in out and "131072" in out
+
+
+def test_flushed_and_warm_launches_are_told_apart(tmp_path, capsys):
+    # fill, A, B, A, fill, A, B, B: A's 1st and 3rd launches and B's 1st and
+    # 3rd follow a fill; A's 2nd and B's 2nd do not
+    cols = ["Kernel_Name", "Grid_Size_X", "Start_Timestamp", "End_Timestamp"]
+    a = "void jf::(anonymous namespace)::k_a(int)"
+    b = "void jf::(anonymous namespace)::k_b(int)"
+    fill = "void at::native::vectorized_elementwise_kernel<4, at::native::FillFunctor<float> >(int)"
+    seq = [(fill, 1), (a, 10), (b, 20), (a, 30), (fill, 1), (a, 50), (b, 60), (b, 70)]
+    with open(tmp_path / "r_kernel_trace.csv", "w") as f:
+        f.write(",".join(f'"{c}"' for c in cols) + "\n")
+        t = 0
+        for name, dur in seq:
+            f.write(f'"{name}",64,{t},{t + dur * 1000}\n')
+            t += 100000
+    per = profsum.read_trace_split(str(tmp_path), "FillFunctor")
+    assert per[("k_a", 64)] == ([10.0, 50.0], [30.0])
+    assert per[("k_b", 64)] == ([20.0, 60.0], [70.0])
+    profsum.main(["stats", str(tmp_path), "--cold-after", "FillFunctor"])
+    assert "| `k_a` | 64 | 2 | 30.00 | 1 | 30.00 |" in capsys.readouterr().out

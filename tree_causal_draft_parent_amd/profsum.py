@@ -1,8 +1,12 @@
 """Summaries of rocprofv3 CSV output for the draft-step kernels (host only).
 
-    python -m tree_causal_draft_parent_amd.profsum stats DIR [--by-grid]
+    python -m tree_causal_draft_parent_amd.profsum stats DIR [--by-grid] [--cold-after SUBSTR]
         per-kernel calls / average / total duration from *_kernel_stats.csv
-        (--by-grid: per kernel and grid size, from *_kernel_trace.csv)
+        (--by-grid: per kernel and grid size, from *_kernel_trace.csv;
+        --cold-after: split each row into flushed and warm launches, a
+        launch being flushed when a kernel whose name holds SUBSTR -- the
+        cache-evicting write -- ran after the previous launch of the same
+        kernel)
     python -m tree_causal_draft_parent_amd.profsum traffic --fetch DIR --write DIR \
             --copy-fetch DIR --copy-write DIR --copy-bytes N --out JSON
         per-launch FETCH_SIZE / WRITE_SIZE of every libjf kernel, scaled by the
@@ -112,7 +116,42 @@ def read_trace_by_grid(dirname: str):
     return per
 
 
+def read_trace_split(dirname: str, flush_substr: str):
+    """(kernel short name, grid size) -> (flushed durations, warm durations)
+    in us.  In dispatch (start-time) order, a launch is flushed when a kernel
+    whose full name contains flush_substr started after the previous launch
+    of the same kernel (or before the first one)."""
+    rows = []
+    with open(_one(dirname, "_kernel_trace.csv")) as f:
+        for r in csv.DictReader(f):
+            rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"],
+                         int(r["Grid_Size_X"])))
+    rows.sort(key=lambda t: t[0])
+    last_flush = -1
+    last_seen = {}
+    per = defaultdict(lambda: ([], []))
+    for i, (t0, t1, name, grid) in enumerate(rows):
+        if flush_substr in name:
+            last_flush = i
+            continue
+        key = (short_name(name), grid)
+        cold = last_flush > last_seen.get(key, -1)
+        last_seen[key] = i
+        per[key][0 if cold else 1].append((t1 - t0) / 1e3)
+    return per
+
+
 def cmd_stats(a):
+    if a.cold_after:
+        per = read_trace_split(a.dir, a.cold_after)
+        print("| kernel | grid (threads) | flushed calls | flushed avg us | warm calls | warm avg us |")
+        print("|---|---:|---:|---:|---:|---:|")
+        for (name, grid), (c, w) in sorted(per.items(), key=lambda kv: -sum(kv[1][0]) - sum(kv[1][1])):
+            if not name.startswith("k_"):
+                continue
+            fmt = lambda v: f"{_mean(v):.2f}" if v else "-"
+            print(f"| `{name}` | {grid} | {len(c)} | {fmt(c)} | {len(w)} | {fmt(w)} |")
+        return
     if a.by_grid:
         per = read_trace_by_grid(a.dir)
         print(f"{'kernel':44s} {'grid':>8s} {'calls':>6s} {'avg us':>9s} {'min us':>9s} {'max us':>9s}")
@@ -170,6 +209,8 @@ def main(argv=None):
     s.add_argument("dir")
     s.add_argument("--by-grid", action="store_true",
                    help="per (kernel, grid size) from the kernel trace instead of the stats file")
+    s.add_argument("--cold-after", default="",
+                   help="split launches into flushed / warm by the last kernel whose name holds this")
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
