@@ -169,6 +169,35 @@ def _mean(v):
     return sum(v) / len(v) if v else 0.0
 
 
+def read_counters_by_grid(dirname: str):
+    """(kernel short name, grid size) -> {counter: [per-dispatch values]} from
+    *_counter_collection.csv (values of one dispatch summed when the tool
+    splits them)."""
+    per = defaultdict(lambda: defaultdict(dict))
+    with open(_one(dirname, "_counter_collection.csv")) as f:
+        for r in csv.DictReader(f):
+            key = (short_name(r["Kernel_Name"]), int(r["Grid_Size"]))
+            d = per[key][r["Counter_Name"]]
+            did = r["Dispatch_Id"]
+            d[did] = d.get(did, 0.0) + float(r["Counter_Value"])
+    return {k: {c: list(v.values()) for c, v in cs.items()} for k, cs in per.items()}
+
+
+def cmd_counters(a):
+    """Per (kernel, grid) average of every counter over the given runs."""
+    merged = defaultdict(dict)
+    for d in a.dirs:
+        for key, cs in read_counters_by_grid(d).items():
+            for c, v in cs.items():
+                merged[key][c] = _mean(v)
+    for (name, grid), cs in sorted(merged.items()):
+        if not name.startswith("k_"):
+            continue
+        print(f"{name} grid={grid}")
+        for c, v in sorted(cs.items()):
+            print(f"    {c:32s} {v:16.1f}")
+
+
 def cmd_traffic(a):
     fetch = read_counter(a.fetch, "FETCH_SIZE")
     write = read_counter(a.write, "WRITE_SIZE")
@@ -220,8 +249,10 @@ def main(argv=None):
     t.add_argument("--workload", default="")
     t.add_argument("--commands", nargs="*", default=[])
     t.add_argument("--out", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("dirs", nargs="+")
     a = ap.parse_args(argv)
-    {"stats": cmd_stats, "traffic": cmd_traffic}[a.cmd](a)
+    {"stats": cmd_stats, "traffic": cmd_traffic, "counters": cmd_counters}[a.cmd](a)
 
 
 if __name__ == "__main__":
