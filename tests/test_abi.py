@@ -145,6 +145,16 @@ def test_attn_plan_for_fewer_compute_units():
     assert _ws(L, 1, 256, 32, 7, 128, 4096, [4096], 1, cus=192) == 0  # invalid -> 0
 
 
+def test_attn_plan_cuts_rows_into_nearly_equal_pieces():
+    # rows of 17, 9 and 5 key blocks (prefixes 1024, 512, 256 with 16 nodes,
+    # one KV head, one query tile each) = 31 block units; 4 compute units give
+    # a piece target of 8 blocks: 3 + 2 + 1 pieces (6, 6, 5 / 5, 4 / 5)
+    L = jf.lib()
+    assert _ws(L, 3, 16, 4, 1, 128, 16, [1024, 512, 256], 1, cus=4) == _attn_ws_bytes(6)
+    # one compute unit: every row in one piece, nothing to merge
+    assert _ws(L, 3, 16, 4, 1, 128, 16, [1024, 512, 256], 1, cus=1) == 0
+
+
 def test_attn_plan_of_packed_trees():
     # packed trees of 256 and 16 nodes (4 and 1 query tiles of 256 rows per KV
     # head) are planned together: 68 and 65 key blocks, 8 KV heads -> 2696

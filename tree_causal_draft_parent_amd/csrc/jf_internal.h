@@ -123,13 +123,14 @@ hipError_t launch_tree_expand(const float *score, const int32_t *depth, const in
 
 struct AttnPlan {
     int B, N, Hq, Hkv, D, G, W;    // N: the largest tree; W = ceil(N / 64) mask words a row
-    int chunk_blocks;    // 64-key blocks per split
+    int L;               // longest piece of a row (64-key blocks)
     int page_size;
     int total_items;     // workgroups of the split kernel
-    bool any_split;      // some sequence has more than one split (by the bounds)
+    bool any_split;      // some row has more than one piece (by the bounds)
     int cap[kMaxBatch];              // planned prefix bound of each sequence
     int node_off[kMaxBatch + 1];     // tree rows of sequence b: node_off[b] .. node_off[b+1]-1
-    int item_start[kMaxBatch + 1];   // first work item of sequence b
+    int item_start[kMaxBatch + 1];   // first work item of the sequence at dispatch position p
+    uint8_t seq_order[kMaxBatch];    // sequence at dispatch position p (longest pieces first)
 };
 // prefix_cap: HOST [B] prefix bounds (the lengths themselves when no device
 // lengths are given); node_off: HOST [B+1] packed tree rows or NULL (N a

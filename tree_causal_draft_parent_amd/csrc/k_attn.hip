@@ -10,10 +10,10 @@
 // bf16 path (gfx950 MFMA), split over keys:
 //   * A sequence's keys are cut into 64-key blocks: ceil(P/64) prefix blocks
 //     (read through the page table), then ceil(N/64) tree blocks (the nodes'
-//     own K/V).  Consecutive blocks form a split ("chunk"); one workgroup of
-//     eight waves (two per SIMD) handles one (chunk, KV head, tile of 256
-//     query rows).  Query row r = node * G + (h % G), so the G heads of a node
-//     share a mask row.
+//     own K/V).  A row (sequence, KV head, tile of 256 query rows) with all
+//     of its blocks is cut into pieces of nearly equal size; one workgroup of
+//     eight waves (two per SIMD) handles one piece.  Query row
+//     r = node * G + (h % G), so the G heads of a node share a mask row.
 //   * Per block, each wave computes S^T = K Q^T for its 32 rows with
 //     v_mfma_f32_32x32x16_bf16 (K from LDS as the A operand, Q^T held in
 //     registers as B), so each lane ends up owning one query row's scores.
@@ -44,17 +44,19 @@
 //     immediate.  V stays row-major: ds_read_b64_tr_b16 hands each lane four
 //     consecutive keys of one head-dim column, which is exactly the V^T
 //     operand layout.
-//   * Each split writes (O / l, log-sum-exp) partials in fp32, 256 rows per
-//     work item; a merge kernel combines the splits of a row with LSE
-//     weights.  A sequence with one split writes the final output directly.
+//   * Each piece of a row cut in several writes (O / l, log-sum-exp)
+//     partials in fp32, 256 rows per work item; a merge kernel combines the
+//     pieces of a row with LSE weights.  A row in one piece writes the final
+//     output directly.
 //   * Serving batches: trees may be packed with a different node count per
 //     sequence (rows node_off[b] .. node_off[b+1]-1), and prefix lengths may
-//     come from device memory.  The host plans the splits and the grid from
+//     come from device memory.  The host plans the pieces and the grid from
 //     per-sequence prefix bounds; each workgroup reads the real length, and
-//     splits past it exit (the merge reads the same length), so one captured
+//     pieces past it exit (the merge reads the same length), so one captured
 //     launch serves any lengths up to the bounds.
 #include "jf_internal.h"
 
+#include <algorithm>
 #include <vector>
 
 namespace jf {
@@ -84,24 +86,50 @@ struct AttnArgs {
     const int32_t *prefix_dev;   // device prefix lengths, or null (the bounds are the lengths)
     void *out;
     float *lse;
-    float *part_o;         // split partials O / l, fp32 [items * kTQ, kD]
+    float *part_o;         // piece partials O / l, fp32 [items * kTQ, kD]
     float *part_lse;       // [items * kTQ]
     int32_t *status;
     uint32_t q_bytes, tree_bytes, cache_bytes, mask_bytes;
     int64_t num_pages;
     int page_mode;  // 1: one page per sequence; 2: power-of-two pages >= 16; 0: other
-    int page_size, page_shift, max_pages, B, Hq, Hkv, G, W, chunk_blocks, total_items;
+    int page_size, page_shift, max_pages, B, Hq, Hkv, G, W, total_items;
+    int L;                           // longest piece (64-key blocks) of a row
     float scale, c2, lazy_raw;
     float k_scale, v_scale, c2k;     // FP8 caches: value = code * scale; c2k = c2 * k_scale
     int cap[kMaxBatch];              // planned prefix bound of each sequence
     int node_off[kMaxBatch + 1];     // tree rows of sequence b: node_off[b] .. node_off[b+1]-1
-    int item_start[kMaxBatch + 1];   // first work item of sequence b
+    int item_start[kMaxBatch + 1];   // first work item of the sequence at dispatch position p
+    uint8_t seq_order[kMaxBatch];    // sequence at dispatch position p
 };
 
-constexpr int kPageLds = 1024;     // page ids of one split staged in LDS
+constexpr int kPageLds = 2048;     // page ids of one piece staged in LDS
 
-// the sequence of work item `item`: the last b with item_start[b] <= item
-__device__ __forceinline__ int find_seq(const AttnArgs &a, int item) {
+__device__ __forceinline__ int div_up(int x, int y) { return (x + y - 1) / y; }
+
+// A row of sequence b has nbc = ceil(cap / 64) + ceil(n / 64) key blocks at
+// its planned (bound) length, cut into np = ceil(nbc / L) pieces: np - 1 of
+// ceil(nbc / np) blocks and a last, shorter one (which holds the tree blocks,
+// whose masking makes them the dearer ones).  Piece k starts at
+// min(k ceil(nbc / np), nbc); the last piece is never empty.
+__device__ __forceinline__ int piece_start(int k, int nbc, int np) {
+    return min(k * div_up(nbc, np), nbc);
+}
+
+// Workgroups are dealt round-robin over the XCDs by hardware id.  Deal
+// blocks of kXcdRun consecutive work items instead: the items of one block
+// (query tiles and KV heads of one piece, which share keys) meet in one XCD's
+// L2, and each XCD still takes its items in dispatch (longest-first) order.
+// Ids past the last whole round of blocks map to themselves.
+constexpr int kXcdRun = 8;
+__device__ __forceinline__ int xcd_interleave(int bid, int n) {
+    constexpr int kRound = kNumXcd * kXcdRun;
+    if (bid >= n / kRound * kRound) return bid;
+    const int xcd = bid % kNumXcd, local = bid / kNumXcd;
+    return ((local / kXcdRun) * kNumXcd + xcd) * kXcdRun + local % kXcdRun;
+}
+
+// the dispatch position of work item `item`: the last p with item_start[p] <= item
+__device__ __forceinline__ int find_pos(const AttnArgs &a, int item) {
     int lo = 0, hi = a.B - 1;
     while (lo < hi) {
         int mid = (lo + hi + 1) >> 1;
@@ -123,14 +151,12 @@ __device__ __forceinline__ int prefix_of(const AttnArgs &a, int b, bool &bad) {
     return p;
 }
 
-__device__ __forceinline__ int div_up(int x, int y) { return (x + y - 1) / y; }
-
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, uint32_t bytes) { return make_rsrc(p, bytes); }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // Byte offset of (key row, 16-byte chunk) of block kb in its buffer, or kOob.
-// Prefix rows go through the split's page ids in LDS; tree rows index the
+// Prefix rows go through the piece's page ids in LDS; tree rows index the
 // nodes' own K/V.  An out-of-range page id reads as zeros and is flagged.
 __device__ __forceinline__ uint32_t row_offset(const AttnArgs &a, const int *pages, int page0,
                                                int64_t node0, int n, int g, int P, int nPB, int kb,
@@ -192,21 +218,13 @@ __device__ __forceinline__ const uint16_t *uniform_ptr(const uint16_t *p) {
 }
 
 // This lane's eight 16-byte query fragments (k-steps t = 0..7 at +32 t bytes).
-// Issued as inline asm so that they are counted with the copies by the
-// explicit waits; the registers are read only after such a wait (and passed
-// through an empty asm statement there).
+// Plain buffer-load builtins: the compiler then knows the registers are
+// written when the loads return and waits before any read of them (a spill
+// or a copy included); the kernel also waits for them explicitly before the
+// first block copy.
 __device__ __forceinline__ void load_q(u32x4 (&d)[kD / 16], __amdgpu_buffer_rsrc_t r, uint32_t voff) {
-    asm volatile("buffer_load_dwordx4 %0, %8, %9, 0 offen\n\t"
-                 "buffer_load_dwordx4 %1, %8, %9, 0 offen offset:32\n\t"
-                 "buffer_load_dwordx4 %2, %8, %9, 0 offen offset:64\n\t"
-                 "buffer_load_dwordx4 %3, %8, %9, 0 offen offset:96\n\t"
-                 "buffer_load_dwordx4 %4, %8, %9, 0 offen offset:128\n\t"
-                 "buffer_load_dwordx4 %5, %8, %9, 0 offen offset:160\n\t"
-                 "buffer_load_dwordx4 %6, %8, %9, 0 offen offset:192\n\t"
-                 "buffer_load_dwordx4 %7, %8, %9, 0 offen offset:224"
-                 : "=&v"(d[0]), "=&v"(d[1]), "=&v"(d[2]), "=&v"(d[3]), "=&v"(d[4]), "=&v"(d[5]),
-                   "=&v"(d[6]), "=&v"(d[7])
-                 : "v"(voff), "s"(r) : "memory");
+#pragma unroll
+    for (int t = 0; t < kD / 16; ++t) d[t] = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 32u * t, 0, 0);
 }
 
 // 4 bytes per lane HBM -> LDS: lane L's dword lands at lds + 4 L.
@@ -339,7 +357,7 @@ __device__ __forceinline__ void lds_barrier() {
 // same LDS layout the bf16 copies produce (tree blocks are bf16 and copied
 // as usual).  Scores of prefix keys are scaled by k_scale through the
 // exponent coefficient and the block maximum; the output accumulator holds
-// prefix values in code units until the split's first tree block (or the
+// prefix values in code units until the piece's first tree block (or the
 // end), where it is multiplied by v_scale once.
 template <bool kPaged, bool kFp8>
 __global__ __launch_bounds__(kNW * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -353,14 +371,15 @@ void k_tree_attn_split(AttnArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: lets wave math stay scalar
     const int half = lane >> 5, l32 = lane & 31;
 
-    // ---- work item: (split, KV head, query tile) of one sequence ----
-    const int item = xcd_remap(blockIdx.x, a.total_items);
-    const int b = __builtin_amdgcn_readfirstlane(find_seq(a, item));
+    // ---- work item: (piece, KV head, query tile) of one sequence ----
+    const int item = xcd_interleave(blockIdx.x, a.total_items);
+    const int pos = __builtin_amdgcn_readfirstlane(find_pos(a, item));
+    const int b = __builtin_amdgcn_readfirstlane((int)a.seq_order[pos]);
     const int64_t node0 = a.node_off[b];
     const int n = __builtin_amdgcn_readfirstlane(a.node_off[b + 1] - a.node_off[b]);
     const int R = n * a.G;                                   // query rows of the sequence
     const int n_qt = div_up(R, kTQ);
-    const int local = item - a.item_start[b];
+    const int local = item - a.item_start[pos];
     const int qt = __builtin_amdgcn_readfirstlane(local % n_qt);
     const int g = __builtin_amdgcn_readfirstlane((local / n_qt) % a.Hkv);
     const int cidx = __builtin_amdgcn_readfirstlane(local / n_qt / a.Hkv);
@@ -368,17 +387,19 @@ void k_tree_attn_split(AttnArgs a) {
     int P = __builtin_amdgcn_readfirstlane(prefix_of(a, b, pbad));
     const int nPB = (P + kKB - 1) / kKB;
     const int nTB = div_up(n, kKB);
-    const int nB = nPB + nTB;
-    const int nchunks = div_up(nB, a.chunk_blocks);           // splits of the real length
-    if (cidx >= nchunks) {
+    const int nB = nPB + nTB;                                // blocks of the real length
+    const int nbc = div_up(a.cap[b], kKB) + nTB;             // blocks of the planned length
+    const int np = div_up(nbc, a.L);                         // pieces of each row
+    const int kb0 = __builtin_amdgcn_readfirstlane(piece_start(cidx, nbc, np));
+    const int kb1c = __builtin_amdgcn_readfirstlane(piece_start(cidx + 1, nbc, np));
+    if (kb0 >= nB) {
         // past the sequence's real length: nothing to do (the merge reads
-        // the same length and skips this split)
+        // the same length and skips this piece)
         if (pbad && tid == 0 && a.status) *a.status = JF_ERR_BAD_PREFIX;
         return;
     }
-    const int kb0 = cidx * a.chunk_blocks;
-    const int kb1 = min(kb0 + a.chunk_blocks, nB);
-    const bool single = nchunks == 1;
+    const int kb1 = min(kb1c, nB);
+    const bool single = cidx == 0 && kb1c >= nB;             // the only piece with keys
     const int64_t prow0 = (int64_t)item * kTQ;               // this item's partial rows
 
     SplitCtx c;
@@ -409,7 +430,7 @@ void k_tree_attn_split(AttnArgs a) {
     if (tid == 0) { s_used = 0u; s_bad = 0; }
     lds_barrier();
 
-    // ---- page ids of this split's prefix range ----
+    // ---- page ids of this piece's prefix range ----
     c.page0 = 0;
     {
         const int pos0 = kb0 * kKB;
@@ -447,8 +468,9 @@ void k_tree_attn_split(AttnArgs a) {
     }
 
     // ---- queries (Q^T fragments in registers), issued before the mask scan
-    // and the first copies so that their latency overlaps that work; the
-    // first ring wait covers them (loads complete in issue order).  They come
+    // so that their latency overlaps that work, and waited for before the
+    // first block copy (the compiler cannot count the copies, so a wait it
+    // placed itself would also wait for every copy in flight).  They come
     // after the page-table reads above, whose own waits would otherwise also
     // wait for them.
     u32x4 qraw[kD / 16];
@@ -457,7 +479,7 @@ void k_tree_attn_split(AttnArgs a) {
         const uint32_t qoff = row_ok ? (uint32_t)((((node0 + node) * a.Hq + hq) * kD + half * 8) * 2) : kOob;
         load_q(qraw, r_q, qoff);
     }
-    // ---- which tree blocks of this split does any row of the tile see? ----
+    // ---- which tree blocks of this piece does any row of the tile see? ----
     lds_barrier();   // s_pages / s_bad written above
     if (kb1 > nPB && tid < kTQ) {
         const int rr = qt * kTQ + tid;
@@ -471,12 +493,13 @@ void k_tree_attn_split(AttnArgs a) {
     }
     lds_barrier();
     const uint32_t used = __builtin_amdgcn_readfirstlane(s_used);   // uniform: block choice stays scalar
+    __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xf << 8));            // vmcnt(0): the queries have landed
     auto next_vis = [&](int kb) {        // first visible block >= kb (kb1 if none)
         while (kb < kb1 && kb >= nPB && !((used >> (kb - nPB)) & 1u)) ++kb;
         return kb;
     };
     if (next_vis(kb0) >= kb1) {
-        // no row of the tile sees a key of this split: zero rows, lse = -inf;
+        // no row of the tile sees a key of this piece: zero rows, lse = -inf;
         // the whole workgroup leaves here with nothing in flight
         if (row_ok) {
             if (single) {
@@ -730,7 +753,7 @@ void k_tree_attn_split(AttnArgs a) {
     if constexpr (!kFp8) {
         const int n_vis_first = n_iss;      // blocks in flight before the first wait
         if (kb_cur < kb1) {
-            ring_wait((n_vis_first - 1) * kOps);          // block 0 and the queries have landed
+            ring_wait((n_vis_first - 1) * kOps);          // block 0 has landed
             asm volatile("" : "+v"(qraw[0]), "+v"(qraw[1]), "+v"(qraw[2]), "+v"(qraw[3]),
                               "+v"(qraw[4]), "+v"(qraw[5]), "+v"(qraw[6]), "+v"(qraw[7]));
 #pragma unroll
@@ -846,7 +869,7 @@ void k_tree_attn_split(AttnArgs a) {
         auto coef = [&](int kb) { return kb < nPB ? a.c2k : a.c2; };
         if (kb_cur < kb1) {
             issue8(kb_cur, 0);
-            commit8(kb_cur, 0);                           // also waits for the queries
+            commit8(kb_cur, 0);
             lds_barrier();
             asm volatile("" : "+v"(qraw[0]), "+v"(qraw[1]), "+v"(qraw[2]), "+v"(qraw[3]),
                               "+v"(qraw[4]), "+v"(qraw[5]), "+v"(qraw[6]), "+v"(qraw[7]));
@@ -889,7 +912,7 @@ void k_tree_attn_split(AttnArgs a) {
             if (in_b) iter_last(sb0, sb1);
             else iter_last(sa0, sa1);
         }
-        to_values();                                      // a split of prefix blocks only
+        to_values();                                      // a piece of prefix blocks only
     }
 
     if (bad) s_bad = 1;  // benign race: every writer stores 1
@@ -897,11 +920,11 @@ void k_tree_attn_split(AttnArgs a) {
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
     const float lse_v = l_run > 0.f ? S.m * a.scale + logf(l_run) : -INFINITY;
     // The wave's 32 output rows are stored row-contiguous: each lane leaves
-    // its 4-column pieces in LDS (the ring is idle once every copy has landed
+    // its 4-column parts in LDS (the ring is idle once every copy has landed
     // and every wave is past its last step), then the wave writes 16-byte
-    // chunks, 1 KiB per store instruction.  (A lane's own pieces would
-    // scatter 8 or 16 bytes over 32 rows per store instruction.)  A sequence
-    // with one split writes the bf16 output; otherwise the fp32 partials of
+    // chunks, 1 KiB per store instruction.  (A lane's own parts would
+    // scatter 8 or 16 bytes over 32 rows per store instruction.)  The only
+    // piece with keys writes the bf16 output; otherwise the fp32 partials of
     // the work item's rows.
     ring_barrier<0>();
     if (single) {
@@ -955,21 +978,26 @@ void k_tree_attn_split(AttnArgs a) {
     }
 }
 
-// Combine the splits of one row: O = sum_s w_s O_s / sum_s w_s with
+// Combine the pieces of one row: O = sum_s w_s O_s / sum_s w_s with
 // w_s = exp(lse_s - max lse); lse = max + log sum w_s.  Sixteen threads per
-// row, eight output columns (two 16-byte loads per split) each; one pass over
-// the splits, four at a time, rescaling when the running maximum moves.  The
-// grid's y index is the sequence; the split count follows the sequence's
-// real prefix length, as in the split kernel.
+// row, eight output columns (two 16-byte loads per piece) each; one pass over
+// the pieces, four at a time, rescaling when the running maximum moves.  The
+// grid's y index is the dispatch position of the sequence; pieces that start
+// past the real length have no keys and were not written (the split kernel
+// reads the same length), and a row whose first piece holds every real block
+// was written by the split kernel.
 constexpr int kMergeTPR = kD / 8;        // threads per row
 __global__ __launch_bounds__(256) void k_tree_attn_merge(AttnArgs a) {
     const int sub = threadIdx.x % kMergeTPR;
-    const int b = blockIdx.y;
+    const int pos = blockIdx.y;
+    const int b = a.seq_order[pos];
     const int n = a.node_off[b + 1] - a.node_off[b];
     bool pbad = false;
     const int P = prefix_of(a, b, pbad);
-    const int nc = div_up(div_up(P, kKB) + div_up(n, kKB), a.chunk_blocks);
-    if (nc == 1) return;                                     // written by the split kernel
+    const int nB = div_up(P, kKB) + div_up(n, kKB);
+    const int nbc = div_up(a.cap[b], kKB) + div_up(n, kKB);
+    const int np = div_up(nbc, a.L);
+    if (piece_start(1, nbc, np) >= nB) return;               // written by the split kernel
     const int in_seq = blockIdx.x * (256 / kMergeTPR) + threadIdx.x / kMergeTPR;
     if (in_seq >= n * a.Hq) return;
     const int64_t flat = (int64_t)a.node_off[b] * a.Hq + in_seq;
@@ -978,10 +1006,12 @@ __global__ __launch_bounds__(256) void k_tree_attn_merge(AttnArgs a) {
     const int g = hq / a.G;
     const int r = node * a.G + hq % a.G;
     const int n_qt = div_up(n * a.G, kTQ);
-    // split c's work item: item_start[b] + (c * Hkv + g) * n_qt + r / kTQ
-    const int64_t row0 = ((int64_t)a.item_start[b] + (int64_t)g * n_qt + r / kTQ) * kTQ + r % kTQ;
-    const int64_t stride = (int64_t)a.Hkv * n_qt * kTQ;      // rows between consecutive splits
+    // piece c's work item: item_start[pos] + (c * Hkv + g) * n_qt + r / kTQ
+    const int64_t row0 = ((int64_t)a.item_start[pos] + (int64_t)g * n_qt + r / kTQ) * kTQ + r % kTQ;
+    const int64_t stride = (int64_t)a.Hkv * n_qt * kTQ;      // rows between consecutive pieces
     const float *po = a.part_o + row0 * kD + sub * 8;
+    int nc = np;                                             // pieces with keys
+    while (nc > 1 && piece_start(nc - 1, nbc, np) >= nB) --nc;
     float M = -INFINITY;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float wsum = 0.f;
@@ -1142,107 +1172,65 @@ __global__ __launch_bounds__(256) void k_tree_attn_f32(AttnArgsF32 a) {
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// Predicted span (in quarter blocks) of the split kernel's workgroups for
-// splits of c blocks: sequence b has nb[b] blocks and gives per_chunk[b]
-// workgroups per split, launched in the kernel's item order, each costing a
-// fixed overhead plus its blocks on the compute unit that frees first.
-static int64_t plan_span(int B, const int64_t *nb, const int64_t *per_chunk, int64_t c, int cus) {
-    constexpr int64_t kOverhead = 16;    // quarter blocks: prologue, partial write and its merge
-    std::vector<int64_t> heap((size_t)cus, 0);   // min-heap of compute-unit free times
-    auto push_pop = [&](int64_t cost) {
-        // replace the minimum (heap[0]) by heap[0] + cost and restore the heap
-        int64_t v = heap[0] + cost;
-        size_t i = 0;
-        const size_t n = heap.size();
-        for (;;) {
-            size_t l = 2 * i + 1, r = l + 1, m = i;
-            int64_t mv = v;
-            if (l < n && heap[l] < mv) { m = l; mv = heap[l]; }
-            if (r < n && heap[r] < mv) { m = r; mv = heap[r]; }
-            if (m == i) break;
-            heap[i] = heap[m];
-            i = m;
-        }
-        heap[i] = v;
-    };
-    for (int b = 0; b < B; ++b) {
-        for (int64_t k0 = 0; k0 < nb[b]; k0 += c) {
-            const int64_t size = (k0 + c < nb[b] ? c : nb[b] - k0) * 4 + kOverhead;
-            for (int64_t w = 0; w < per_chunk[b]; ++w) push_pop(size);
-        }
-    }
-    int64_t span = 0;
-    for (int64_t v : heap) span = v > span ? v : span;
-    return span;
-}
-
-// ---------------------------------------------------------------------------
 // Split planning from the prefix bounds.  Every (sequence, KV head, query
-// tile) is a row of blocks; cut all rows into splits of the same block count
-// so that about one workgroup per compute unit comes out (a workgroup fills a
-// compute unit's LDS), never less than two blocks a split.  A caller that
-// runs other work beside the attention can plan it for fewer compute units.
+// tile) is a row of 64-key blocks.  The piece target is L = ceil(units /
+// compute units) blocks (about one workgroup per compute unit's share; a
+// workgroup fills a compute unit's LDS), never less than two; a row of nb
+// blocks is cut into np = ceil(nb / L) pieces of ceil(nb / np) blocks (the
+// last one shorter), so no piece exceeds L and a long row does not leave a
+// tiny remainder.  Sequences are dispatched in decreasing piece size
+// (longest first): the hardware hands each workgroup to the compute unit that
+// frees first, and the short pieces of ragged batches then fill the gaps at
+// the end.  A caller that runs other work beside the
+// attention can plan it for fewer compute units.
 void plan_tree_attn(AttnPlan &p, int B, int N, int Hq, int Hkv, int D, int page_size,
                     const int32_t *prefix_cap, const int32_t *node_off, jf_dtype dtype, int cus) {
     p.B = B; p.N = N; p.Hq = Hq; p.Hkv = Hkv; p.D = D;
     p.page_size = page_size;
     p.G = Hq / Hkv;
     p.W = (N + 63) / 64;
-    std::vector<int64_t> nb((size_t)B), per_chunk((size_t)B);
+    std::vector<int64_t> nb((size_t)B), rows((size_t)B);
     int64_t units = 0, max_blocks = 1, Pmax = 0;
     for (int b = 0; b < B; ++b) {
         p.cap[b] = prefix_cap[b];
         p.node_off[b] = node_off ? node_off[b] : b * N;
         const int64_t n = node_off ? node_off[b + 1] - node_off[b] : N;
         nb[b] = (prefix_cap[b] + kKB - 1) / kKB + (n + kKB - 1) / kKB;
-        per_chunk[b] = (int64_t)Hkv * ((n * p.G + kTQ - 1) / kTQ);
-        units += nb[b] * per_chunk[b];
+        rows[b] = (int64_t)Hkv * ((n * p.G + kTQ - 1) / kTQ);
+        units += nb[b] * rows[b];
         if (nb[b] > max_blocks) max_blocks = nb[b];
         if (prefix_cap[b] > Pmax) Pmax = prefix_cap[b];
     }
     p.node_off[B] = node_off ? node_off[B] : B * N;
     const int64_t target = cus > 0 && cus < num_cus() ? (int64_t)cus : (int64_t)num_cus();
-    int64_t cb = (units + target - 1) / target;
-    if (cb < 2) cb = 2;
-    // a split's page ids must fit the LDS staging array
+    int64_t L = (units + target - 1) / target;
+    if (L < 2) L = 2;
+    // a piece's page ids must fit the LDS staging array
     if (page_size < Pmax) {
         int64_t cap = ((int64_t)(kPageLds - 2) * page_size) / kKB;
         if (cap < 1) cap = 1;
-        if (cb > cap) cb = cap;
+        if (L > cap) L = cap;
     }
-    if (cb > max_blocks) cb = max_blocks;
-    auto n_items = [&](int64_t c) {
-        int64_t n = 0;
-        for (int b = 0; b < B; ++b) n += (nb[b] + c - 1) / c * per_chunk[b];
-        return n;
-    };
-    // Ragged prefixes leave partial splits, and the workgroups can then spill
-    // over one wave of the chip.  Splits of the base size are then compared
-    // with smaller ones by a model of the dispatch (workgroups in launch order,
-    // each to the compute unit that frees first; cost = a fixed per-workgroup
-    // overhead + its block count), and the shortest predicted span is kept.
-    if (dtype != JF_F32 && n_items(cb) > target) {
-        const int64_t base = cb;
-        int64_t best = -1;
-        int64_t best_cb = cb;
-        for (int d = 4; d <= 12; ++d) {        // base * 4/d: 1, 0.8, ..., 1/3 of the base size
-            int64_t c = (base * 4 + d - 1) / d;
-            if (c < 2) c = 2;
-            if (d > 4 && c == best_cb) continue;
-            const int64_t span = plan_span(B, nb.data(), per_chunk.data(), c, (int)target);
-            if (best < 0 || span < best) { best = span; best_cb = c; }
-        }
-        cb = best_cb;
+    if (L > max_blocks || dtype == JF_F32) L = max_blocks;   // the fp32 path does not split
+    p.L = (int)L;
+    // dispatch order: decreasing size of the longest piece (ties: lower
+    // sequence first)
+    std::vector<int64_t> np((size_t)B), piece((size_t)B);
+    std::vector<int> order((size_t)B);
+    for (int b = 0; b < B; ++b) {
+        np[b] = (nb[b] + L - 1) / L;
+        piece[b] = (nb[b] + np[b] - 1) / np[b];
+        order[(size_t)b] = b;
     }
-    if (dtype == JF_F32) cb = max_blocks;  // the fp32 path does not split
-    p.chunk_blocks = (int)cb;
+    std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return piece[x] > piece[y]; });
     int64_t items = 0;
     p.any_split = false;
-    for (int b = 0; b < B; ++b) {
-        p.item_start[b] = (int)items;
-        const int64_t nc = (nb[b] + cb - 1) / cb;
-        if (nc > 1) p.any_split = true;
-        items += nc * per_chunk[b];
+    for (int i = 0; i < B; ++i) {
+        const int b = order[(size_t)i];
+        p.seq_order[i] = (uint8_t)b;
+        p.item_start[i] = (int)items;
+        if (np[b] > 1) p.any_split = true;
+        items += np[b] * rows[b];
     }
     p.item_start[B] = (int)items;
     p.total_items = (int)items;
@@ -1297,7 +1285,7 @@ hipError_t launch_tree_attn_bf16(const AttnPlan &p, const void *q, const void *k
                       : (a.page_shift >= 4 ? 2 : 0);
     }
     a.B = p.B; a.Hq = p.Hq; a.Hkv = p.Hkv; a.G = p.G; a.W = p.W;
-    a.chunk_blocks = p.chunk_blocks;
+    a.L = p.L;
     a.total_items = p.total_items;
     a.scale = scale;
     a.c2 = scale * kLog2e;
@@ -1310,6 +1298,7 @@ hipError_t launch_tree_attn_bf16(const AttnPlan &p, const void *q, const void *k
         a.node_off[b] = p.node_off[b];
         a.item_start[b] = p.item_start[b];
     }
+    for (int i = 0; i < p.B; ++i) a.seq_order[i] = p.seq_order[i];
     const dim3 grid(p.total_items), block(kNW * kWave);
     if (a.page_mode == 1) {
         if (fp8) hipLaunchKernelGGL((k_tree_attn_split<false, true>), grid, block, 0, s, a);
