@@ -147,10 +147,16 @@ def test_attn_plan_for_fewer_compute_units():
 
 def test_attn_plan_cuts_rows_into_nearly_equal_pieces():
     # rows of 17, 9 and 5 key blocks (prefixes 1024, 512, 256 with 16 nodes,
-    # one KV head, one query tile each) = 31 block units; 4 compute units give
-    # a piece target of 8 blocks: 3 + 2 + 1 pieces (6, 6, 5 / 5, 4 / 5)
+    # one KV head, one query tile each) = 31 block units.  4 compute units give
+    # a piece target of 8 blocks: 3 + 2 + 1 pieces (6, 6, 5 / 5, 4 / 5), 6
+    # work items, more than one wave; the dispatch model then prefers pieces
+    # of at most 9 blocks (9, 8 / 9 / 5): 4 items in one wave, span 9 + 4
+    # against 18 for the 6 items (each item costs its blocks plus 4)
     L = jf.lib()
-    assert _ws(L, 3, 16, 4, 1, 128, 16, [1024, 512, 256], 1, cus=4) == _attn_ws_bytes(6)
+    assert _ws(L, 3, 16, 4, 1, 128, 16, [1024, 512, 256], 1, cus=4) == _attn_ws_bytes(4)
+    # 2 compute units: a target of 16 blocks gives the same pieces (9, 8 / 9 /
+    # 5), 4 items in two waves
+    assert _ws(L, 3, 16, 4, 1, 128, 16, [1024, 512, 256], 1, cus=2) == _attn_ws_bytes(4)
     # one compute unit: every row in one piece, nothing to merge
     assert _ws(L, 3, 16, 4, 1, 128, 16, [1024, 512, 256], 1, cus=1) == 0
 

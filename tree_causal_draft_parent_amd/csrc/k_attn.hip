@@ -57,6 +57,7 @@
 #include "jf_internal.h"
 
 #include <algorithm>
+#include <queue>
 #include <vector>
 
 namespace jf {
@@ -1181,8 +1182,9 @@ __global__ __launch_bounds__(256) void k_tree_attn_f32(AttnArgsF32 a) {
 // tiny remainder.  Sequences are dispatched in decreasing piece size
 // (longest first): the hardware hands each workgroup to the compute unit that
 // frees first, and the short pieces of ragged batches then fill the gaps at
-// the end.  A caller that runs other work beside the
-// attention can plan it for fewer compute units.
+// the end.  When the pieces spill over one wave of workgroups, a few piece
+// sizes are compared by a model of that dispatch (below).  A caller that runs
+// other work beside the attention can plan it for fewer compute units.
 void plan_tree_attn(AttnPlan &p, int B, int N, int Hq, int Hkv, int D, int page_size,
                     const int32_t *prefix_cap, const int32_t *node_off, jf_dtype dtype, int cus) {
     p.B = B; p.N = N; p.Hq = Hq; p.Hkv = Hkv; p.D = D;
@@ -1206,23 +1208,81 @@ void plan_tree_attn(AttnPlan &p, int B, int N, int Hq, int Hkv, int D, int page_
     int64_t L = (units + target - 1) / target;
     if (L < 2) L = 2;
     // a piece's page ids must fit the LDS staging array
+    int64_t Lmax = max_blocks;
     if (page_size < Pmax) {
         int64_t cap = ((int64_t)(kPageLds - 2) * page_size) / kKB;
         if (cap < 1) cap = 1;
-        if (L > cap) L = cap;
+        if (Lmax > cap) Lmax = cap;
     }
-    if (L > max_blocks || dtype == JF_F32) L = max_blocks;   // the fp32 path does not split
-    p.L = (int)L;
-    // dispatch order: decreasing size of the longest piece (ties: lower
-    // sequence first)
+    if (L > Lmax) L = Lmax;
+    if (dtype == JF_F32) L = max_blocks;                  // the fp32 path does not split
+
+    // Pieces of at most Lc blocks: np[b] pieces of piece[b] blocks (the last
+    // shorter), sequences in decreasing piece size (ties: lower sequence
+    // first).  Returns the work item count.
     std::vector<int64_t> np((size_t)B), piece((size_t)B);
     std::vector<int> order((size_t)B);
-    for (int b = 0; b < B; ++b) {
-        np[b] = (nb[b] + L - 1) / L;
-        piece[b] = (nb[b] + np[b] - 1) / np[b];
-        order[(size_t)b] = b;
+    auto build = [&](int64_t Lc) {
+        int64_t items = 0;
+        for (int b = 0; b < B; ++b) {
+            np[b] = (nb[b] + Lc - 1) / Lc;
+            piece[b] = (nb[b] + np[b] - 1) / np[b];
+            order[(size_t)b] = b;
+            items += np[b] * rows[b];
+        }
+        std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return piece[x] > piece[y]; });
+        return items;
+    };
+    const int64_t items0 = build(L);
+    // More work items than compute units: the pieces after the first wave
+    // may leave a long tail (just over one wave is the worst case).  A few
+    // piece sizes are then compared by a model of the dispatch -- items in
+    // launch order, each to the compute unit that frees first, each costing
+    // a fixed overhead of 4 blocks plus its blocks -- and the shortest
+    // predicted span is kept (ties: the larger pieces, fewer partials).
+    if (dtype != JF_F32 && items0 > target && items0 <= 16 * target) {
+        auto span_of = [&](int64_t Lc) {
+            build(Lc);
+            constexpr int64_t kOverhead = 4;
+            std::priority_queue<int64_t, std::vector<int64_t>, std::greater<int64_t>> free_at;
+            for (int64_t c = 0; c < target; ++c) free_at.push(0);
+            int64_t span = 0;
+            for (int i = 0; i < B; ++i) {
+                const int b = order[(size_t)i];
+                for (int64_t k = 0; k < np[b]; ++k) {
+                    const int64_t k0 = k * piece[b];
+                    const int64_t size = (k0 + piece[b] < nb[b] ? piece[b] : nb[b] - k0) + kOverhead;
+                    for (int64_t r = 0; r < rows[b]; ++r) {
+                        const int64_t t = free_at.top() + size;
+                        free_at.pop();
+                        free_at.push(t);
+                        span = t > span ? t : span;
+                    }
+                }
+            }
+            return span;
+        };
+        // the smallest piece size whose items fit in w waves
+        auto fit_waves = [&](int64_t w) {
+            int64_t lo = L, hi = Lmax;
+            if (build(hi) > w * target) return (int64_t)-1;
+            while (lo < hi) {
+                const int64_t mid = (lo + hi) / 2;
+                if (build(mid) <= w * target) hi = mid; else lo = mid + 1;
+            }
+            return lo;
+        };
+        std::vector<int64_t> cand = {L, (3 * L + 3) / 4, (L + 1) / 2, fit_waves(1), fit_waves(2), fit_waves(3)};
+        int64_t best_L = L, best = -1;
+        for (int64_t c : cand) {
+            if (c < 2 || c > Lmax) continue;
+            const int64_t sp = span_of(c);
+            if (best < 0 || sp < best || (sp == best && c > best_L)) { best = sp; best_L = c; }
+        }
+        L = best_L;
+        build(L);
     }
-    std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return piece[x] > piece[y]; });
+    p.L = (int)L;
     int64_t items = 0;
     p.any_split = false;
     for (int i = 0; i < B; ++i) {
