@@ -173,6 +173,27 @@ def test_splits_planned_for_fewer_compute_units(cus):
     compare(synth.make_workload(2, parts=("attn",))["attn"], label="qwen3-8b n256", cus=cus)
 
 
+@pytest.mark.parametrize("cus", [80, 100])
+def test_pieces_spilling_over_one_wave(cus):
+    # 32 rows of 68 blocks on 80 or 100 compute units: the first piece target
+    # gives more work items than units, so the planner compares piece sizes by
+    # its dispatch model (80 units: 5 pieces a row, two full waves); all rows
+    compare(synth.make_workload(2, parts=("attn",))["attn"], label="qwen3-8b n256", cus=cus)
+
+
+@pytest.mark.parametrize("cus,dev", [(2, False), (5, False), (5, True), (12, True)])
+def test_ragged_batch_on_few_compute_units(cus, dev):
+    # ragged prefixes (one empty, one of a single page, some spanning many
+    # pieces) on 2-5 compute units: rows of 1-48 blocks cut into pieces of
+    # different sizes, dispatched longest first, many work items per unit;
+    # with device lengths below the bounds, pieces past a real length exit
+    inp = synth.make_attn_inputs(B=5, N=40, Hq=8, Hkv=2, D=128, dtype="bf16",
+                                 prefix_lens=[0, 70, 1000, 3000, 130], page_size=16,
+                                 shuffled_pages=True, seed=81)
+    compare(inp, label="ragged few units", cus=cus,
+            prefix_dev=[0, 10, 500, 2999, 64] if dev else None)
+
+
 def test_serving_batch_fewer_compute_units_sampled():
     inp = synth.make_workload(3, parts=("attn",))["attn"]
     compare(inp, rows=tile_rows(inp, 256, 5), label="serving b32", cus=192)
