@@ -834,6 +834,7 @@ def main():
     #       the projection and the top-k);
     #   "fuse_half": 1/2 for the projection, all units for the attention;
     #   "fit_five_eighths": 5/8 and 3/8;
+    #   "fit_nine_sixteenths": 9/16 and 7/16;
     #   "topk_apart": as fuse_half, the top-k on a third stream of its own.
     # The 16-node workload (id 1) times the one-stream graph only.  Its step
     # is launch-bound and every multi-stream plan measured slower than one
@@ -853,6 +854,7 @@ def main():
                  "fit_together": (n_cus // 2, (3 * n_cus) // 8, False),
                  "fuse_half": (n_cus // 2, 0, False),
                  "fit_five_eighths": ((5 * n_cus) // 8, (3 * n_cus) // 8, False),
+                 "fit_nine_sixteenths": ((9 * n_cus) // 16, (7 * n_cus) // 16, False),
                  "topk_apart": (n_cus // 2, 0, True)}
 
     def time_graph(fn, reps=None):

@@ -100,15 +100,18 @@ def _setup(i):
 # times only that schedule for it (its multi-stream plan loop once ended in a
 # host fault of unknown cause and is not run).
 @pytest.mark.parametrize("i,plan", [(1, "serial")] + [
-    (i, plan) for i in (2, 3, 4) for plan in ("serial", "streams", "fit_five_eighths", "topk_apart")])
+    (i, plan) for i in (2, 3, 4)
+    for plan in ("serial", "streams", "fit_five_eighths", "fit_nine_sixteenths", "topk_apart")])
 def test_step_graph_replays_match_eager(i, plan):
     # the schedules the benchmark times: one stream, two streams with all
-    # units, 5/8 + 3/8 of the units, and the top-k on a third stream; each
-    # replay must equal an eager run of the same schedule bit for bit
+    # units, 5/8 + 3/8 and 9/16 + 7/16 of the units, and the top-k on a third
+    # stream; each replay must equal an eager run of the same schedule bit for
+    # bit
     wl, d, o, step_serial, make_streams = _setup(i)
     n_cus = torch.cuda.get_device_properties(0).multi_processor_count
     step = {"serial": step_serial, "streams": make_streams(),
             "fit_five_eighths": make_streams((5 * n_cus) // 8, (3 * n_cus) // 8),
+            "fit_nine_sixteenths": make_streams((9 * n_cus) // 16, (7 * n_cus) // 16),
             "topk_apart": make_streams(n_cus // 2, 0, True)}[plan]
     say(f"graph replay: workload {wl.name}, plan {plan}")
     step()
