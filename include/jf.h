@@ -177,8 +177,10 @@ jf_status jf_fuse_proj_cus(const void *const *x, int32_t k, int64_t M,
  *               position then reads as a zero key with a zero value: score 0,
  *               counted in the normaliser), or to JF_ERR_BAD_PREFIX for a
  *               device prefix length outside its bound.
- *   dtype       JF_BF16: D == 128, MFMA split-KV path with fp32 split
- *               partials;  JF_F32: D <= 128, plain fp32 path (small problems).
+ *   dtype       JF_BF16: D == 128 or 64, MFMA path over row pieces with fp32
+ *               partials (D = 64 is computed at 128 with the upper half of
+ *               q, k and v read as zeros);  JF_F32: D <= 128, plain fp32 path
+ *               (small problems).
  *   Limits: 1 <= B <= 256, 1 <= N <= 1024, Hq % Hkv == 0; on the bf16
  *   path each of q, k_tree, k_cache (and their value twins) must be smaller
  *   than 4 GiB - 256 bytes (32-bit buffer offsets), else JF_ERR_UNSUPPORTED.

@@ -86,7 +86,8 @@ def test_attn_argument_errors():
     assert _attn(L, q=None) == jf.JF_ERR_INVALID_ARG
     assert _attn(L, pl=None) == jf.JF_ERR_INVALID_ARG
     assert _attn(L, Hq=6, Hkv=4) == jf.JF_ERR_INVALID_ARG
-    assert _attn(L, D=64) == jf.JF_ERR_UNSUPPORTED
+    assert _attn(L, D=96) == jf.JF_ERR_UNSUPPORTED          # bf16: D = 64 or 128
+    assert _attn(L, D=64) != jf.JF_ERR_UNSUPPORTED
     assert _attn(L, D=256, dtype=jf.JF_F32) == jf.JF_ERR_UNSUPPORTED
     assert _attn(L, N=2000) == jf.JF_ERR_UNSUPPORTED
     assert _attn(L, B=300, pl=np.zeros(300, np.int32)) == jf.JF_ERR_UNSUPPORTED

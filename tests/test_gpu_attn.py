@@ -406,3 +406,34 @@ def test_fp8_bad_page_reads_zero():
     assert int(ps.item()) == jf.JF_ERR_BAD_PAGE
     ro, rl, flag = oracle_attn(inp, bad_page_ok=True)
     check(inp, out, lse, ro, rl)
+
+
+# ---- head dim 64 on the bf16 path (computed at 128, the upper half zero) ----
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_head_dim_64_ragged(paged):
+    # prefixes of 0, 65, 700 and 2000 tokens, 100 nodes (two tree blocks),
+    # 8 query / 2 KV heads; all rows, contiguous and shuffled 16-token pages
+    inp = synth.make_attn_inputs(B=4, N=100, Hq=8, Hkv=2, D=64, dtype="bf16",
+                                 prefix_lens=[0, 65, 700, 2000], page_size=16 if paged else 0,
+                                 shuffled_pages=paged, seed=91)
+    compare(inp, label="D64 ragged")
+
+
+def test_head_dim_64_pieces_and_merge():
+    # 4096 prefix tokens, 256 nodes at 32 query / 8 KV heads: rows cut in
+    # pieces and merged, all rows; and on 7 compute units
+    inp = synth.make_attn_inputs(B=1, N=256, Hq=32, Hkv=8, D=64, dtype="bf16",
+                                 prefix_lens=[4096], page_size=0, seed=92)
+    compare(inp, label="D64 n256")
+    compare(inp, label="D64 n256", cus=7)
+
+
+def test_head_dim_64_packed_device_lengths_fp8():
+    # packed trees of 16, 64 and 200 nodes, device prefix lengths below the
+    # bounds, bf16 cache and FP8 (E4M3) cache
+    for kv in (None, "fp8"):
+        inp = synth.make_attn_inputs(B=3, N=0, Hq=16, Hkv=4, D=64, dtype="bf16",
+                                     prefix_lens=[3000, 1000, 64], page_size=16, shuffled_pages=True,
+                                     seed=93, node_counts=[16, 64, 200], kv_dtype=kv)
+        compare(inp, label=f"D64 packed kv={kv}", prefix_dev=[2500, 1000, 1])

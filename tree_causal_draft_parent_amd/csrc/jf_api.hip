@@ -150,7 +150,7 @@ static jf_status check_attn_dims(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, 
     if (Hq % Hkv != 0) return JF_ERR_INVALID_ARG;
     if (dtype != JF_BF16 && dtype != JF_F32) return JF_ERR_INVALID_ARG;
     if (B > kMaxBatch || N > 1024) return JF_ERR_UNSUPPORTED;
-    if (dtype == JF_BF16 && D != 128) return JF_ERR_UNSUPPORTED;
+    if (dtype == JF_BF16 && D != 128 && D != 64) return JF_ERR_UNSUPPORTED;
     if (dtype == JF_F32 && D > 128) return JF_ERR_UNSUPPORTED;
     for (int b = 0; b < B; ++b)
         if (prefix_len[b] < 0) return JF_ERR_INVALID_ARG;

@@ -58,6 +58,7 @@
 
 #include <algorithm>
 #include <queue>
+#include <type_traits>
 #include <vector>
 
 namespace jf {
@@ -95,6 +96,7 @@ struct AttnArgs {
     int page_mode;  // 1: one page per sequence; 2: power-of-two pages >= 16; 0: other
     int page_size, page_shift, max_pages, B, Hq, Hkv, G, W, total_items;
     int L;                           // longest piece (64-key blocks) of a row
+    int D;                           // head dim in memory: 128, or 64 (computed as 128, upper half zero)
     float scale, c2, lazy_raw;
     float k_scale, v_scale, c2k;     // FP8 caches: value = code * scale; c2k = c2 * k_scale
     int cap[kMaxBatch];              // planned prefix bound of each sequence
@@ -159,9 +161,11 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 // Byte offset of (key row, 16-byte chunk) of block kb in its buffer, or kOob.
 // Prefix rows go through the piece's page ids in LDS; tree rows index the
 // nodes' own K/V.  An out-of-range page id reads as zeros and is flagged.
+template <int kDm>
 __device__ __forceinline__ uint32_t row_offset(const AttnArgs &a, const int *pages, int page0,
                                                int64_t node0, int n, int g, int P, int nPB, int kb,
                                                int row, int chunk, bool &bad) {
+    if (chunk * 8 >= kDm) return kOob;                // past the head dim: reads as zeros
     if (kb < nPB) {
         const int pos = kb * kKB + row;
         if (pos >= P) return kOob;
@@ -178,11 +182,11 @@ __device__ __forceinline__ uint32_t row_offset(const AttnArgs &a, const int *pag
             bad = true;
             return kOob;
         }
-        return ((((uint32_t)page * a.page_size + slot) * a.Hkv + g) * kD + chunk * 8) * 2u;
+        return ((((uint32_t)page * a.page_size + slot) * a.Hkv + g) * kDm + chunk * 8) * 2u;
     }
     const int j = (kb - nPB) * kKB + row;
     if (j >= n) return kOob;
-    return ((((uint32_t)node0 + j) * a.Hkv + g) * kD + chunk * 8) * 2u;
+    return ((((uint32_t)node0 + j) * a.Hkv + g) * kDm + chunk * 8) * 2u;
 }
 
 // LDS byte offset of key row r of a tile: block r % 16, slot r / 16
@@ -208,6 +212,7 @@ struct SplitCtx {
     uint32_t rowb;                           // bytes between consecutive keys
     uint32_t vrow;                           // lane's offset of its first copy in a block
     uint32_t mrow;                           // lane's mask dword offset (kOob: none)
+    bool chunk_ok;                           // the lane's 16-byte chunk lies inside the head dim
 };
 
 // A pointer known to be the same in every lane, moved to scalar registers.
@@ -223,9 +228,11 @@ __device__ __forceinline__ const uint16_t *uniform_ptr(const uint16_t *p) {
 // written when the loads return and waits before any read of them (a spill
 // or a copy included); the kernel also waits for them explicitly before the
 // first block copy.
-__device__ __forceinline__ void load_q(u32x4 (&d)[kD / 16], __amdgpu_buffer_rsrc_t r, uint32_t voff) {
+// Fragments t >= tq lie past the head dim and read as zeros.
+__device__ __forceinline__ void load_q(u32x4 (&d)[kD / 16], __amdgpu_buffer_rsrc_t r, uint32_t voff, int tq) {
 #pragma unroll
-    for (int t = 0; t < kD / 16; ++t) d[t] = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 32u * t, 0, 0);
+    for (int t = 0; t < kD / 16; ++t)
+        d[t] = __builtin_amdgcn_raw_buffer_load_b128(r, t < tq ? voff + 32u * t : kOob, 0, 0);
 }
 
 // 4 bytes per lane HBM -> LDS: lane L's dword lands at lds + 4 L.
@@ -240,7 +247,7 @@ __device__ __forceinline__ void copy4s(__amdgpu_buffer_rsrc_t r, uint32_t lds, u
 // of each, lane L copying row n + 16*(L/16), 16-byte chunk L%16 -- and the
 // visibility words of the workgroup's 256 query rows (zeros for prefix
 // blocks), thread t copying dword t%2 of row t/2.
-template <bool kPaged>
+template <bool kPaged, int kDm>
 __device__ __forceinline__ void issue_block(const AttnArgs &a, const SplitCtx &c, const int *pages,
                                             uint32_t dst, int kb, bool &bad) {
     const bool tree = kb >= c.nPB;
@@ -254,13 +261,13 @@ __device__ __forceinline__ void issue_block(const AttnArgs &a, const SplitCtx &c
         int rows;
         if (tree) {
             const int j0 = (kb - c.nPB) * kKB;
-            kp = c.kt0 + (int64_t)j0 * a.Hkv * kD;
-            vp = c.vt0 + (int64_t)j0 * a.Hkv * kD;
+            kp = c.kt0 + (int64_t)j0 * a.Hkv * kDm;
+            vp = c.vt0 + (int64_t)j0 * a.Hkv * kDm;
             rows = min(kKB, c.n - j0);
         } else {
             const int p0 = kb * kKB;
-            kp = c.kc0 + (int64_t)p0 * a.Hkv * kD;
-            vp = c.vc0 + (int64_t)p0 * a.Hkv * kD;
+            kp = c.kc0 + (int64_t)p0 * a.Hkv * kDm;
+            vp = c.vc0 + (int64_t)p0 * a.Hkv * kDm;
             rows = c.pzero ? 0 : min(kKB, c.P - p0);
         }
         // every value here is wave-uniform; say so, so that the descriptors live in SGPRs
@@ -268,9 +275,9 @@ __device__ __forceinline__ void issue_block(const AttnArgs &a, const SplitCtx &c
         const __amdgpu_buffer_rsrc_t rk = make_rsrc(uniform_ptr(kp), nbytes);
         const __amdgpu_buffer_rsrc_t rv = make_rsrc(uniform_ptr(vp), nbytes);
 #pragma unroll
-        for (int i = 0; i < kCpw; ++i) copy16(rk, dk + i * kKBlk, c.vrow + i * c.rowb);
+        for (int i = 0; i < kCpw; ++i) copy16(rk, dk + i * kKBlk, c.chunk_ok ? c.vrow + i * c.rowb : kOob);
 #pragma unroll
-        for (int i = 0; i < kCpw; ++i) copy16(rv, dv + i * kVBlk, c.vrow + i * c.rowb);
+        for (int i = 0; i < kCpw; ++i) copy16(rv, dv + i * kVBlk, c.chunk_ok ? c.vrow + i * c.rowb : kOob);
     } else {
         // paged layouts: every group of 16 rows sits in one page (page_mode 2)
         // or every row is looked up (page_mode 0)
@@ -280,10 +287,10 @@ __device__ __forceinline__ void issue_block(const AttnArgs &a, const SplitCtx &c
             const int pos = kb * kKB + 16 * sub;
             const int lim = c.P - kb * kKB;
             uint32_t vbase = kOob;
-            if (16 * sub < lim) {
+            if (16 * sub < lim && c.chunk_ok) {
                 const int page = pages[(pos >> a.page_shift) - c.page0];
                 if (page >= 0 && page < a.num_pages)
-                    vbase = ((((uint32_t)page * a.page_size + (pos & (a.page_size - 1))) * a.Hkv + c.g) * kD +
+                    vbase = ((((uint32_t)page * a.page_size + (pos & (a.page_size - 1))) * a.Hkv + c.g) * kDm +
                              ch * 8) * 2u;
                 else
                     bad = true;
@@ -296,7 +303,7 @@ __device__ __forceinline__ void issue_block(const AttnArgs &a, const SplitCtx &c
         } else {
 #pragma unroll
             for (int i = 0; i < kCpw; ++i)
-                off[i] = row_offset(a, pages, c.page0, c.node0, c.n, c.g, c.P, c.nPB, kb,
+                off[i] = row_offset<kDm>(a, pages, c.page0, c.node0, c.n, c.g, c.P, c.nPB, kb,
                                     kCpw * c.wave + i + 16 * sub, ch, bad);
         }
 #pragma unroll
@@ -353,6 +360,9 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // kPaged = false: every prefix is one page (page_mode 1); true: page_mode 0 or 2.
+// kDm: the head dim of q, k and v in memory, 128 or 64; at 64 the kernel
+// computes at 128 with the upper half of every row read as zeros (the scores
+// are unchanged) and writes only the first 64 output columns.
 // kFp8: the prefix cache holds E4M3 codes; each prefix block is loaded into
 // registers one block ahead, converted exactly to bf16 and written into the
 // same LDS layout the bf16 copies produce (tree blocks are bf16 and copied
@@ -360,7 +370,7 @@ __device__ __forceinline__ void lds_barrier() {
 // exponent coefficient and the block maximum; the output accumulator holds
 // prefix values in code units until the piece's first tree block (or the
 // end), where it is multiplied by v_scale once.
-template <bool kPaged, bool kFp8>
+template <bool kPaged, bool kFp8, int kDm>
 __global__ __launch_bounds__(kNW * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_tree_attn_split(AttnArgs a) {
     __shared__ __attribute__((aligned(1024))) char ring[kNS][kStage];
@@ -408,15 +418,16 @@ void k_tree_attn_split(AttnArgs a) {
     c.r_vc = make_rsrc(a.v_cache, a.cache_bytes);
     c.r_m = make_rsrc(a.mask, a.mask_bytes);
     c.b = b; c.g = g; c.P = P; c.nPB = nPB; c.n = n; c.node0 = node0; c.lane = lane; c.wave = wave;
-    c.rowb = (uint32_t)a.Hkv * kRow;
+    c.rowb = (uint32_t)a.Hkv * kDm * 2;
     c.vrow = (uint32_t)(kCpw * wave + 16 * (lane >> 4)) * c.rowb + (uint32_t)(lane & 15) * 16u;
-    c.kt0 = uniform_ptr(a.k_tree + (node0 * a.Hkv + g) * kD);
-    c.vt0 = uniform_ptr(a.v_tree + (node0 * a.Hkv + g) * kD);
+    c.chunk_ok = (lane & 15) * 8 < kDm;
+    c.kt0 = uniform_ptr(a.k_tree + (node0 * a.Hkv + g) * kDm);
+    c.vt0 = uniform_ptr(a.v_tree + (node0 * a.Hkv + g) * kDm);
     c.kc0 = a.k_cache;
     c.vc0 = a.v_cache;
     c.kc8 = (const uint8_t *)a.k_cache;
     c.vc8 = (const uint8_t *)a.v_cache;
-    c.rowb8 = (uint32_t)a.Hkv * kD;
+    c.rowb8 = (uint32_t)a.Hkv * kDm;
     c.pzero = false;
     // ---- this lane's query row and mask dword ----
     const int r = qt * kTQ + wave * 32 + l32;
@@ -442,7 +453,7 @@ void k_tree_attn_split(AttnArgs a) {
                 // one page per sequence: a bad id reads as zeros and is flagged
                 const int page = __builtin_amdgcn_readfirstlane(bt[0]);
                 if (page >= 0 && page < a.num_pages) {
-                    const int64_t e0 = ((int64_t)page * a.page_size * a.Hkv + g) * kD;
+                    const int64_t e0 = ((int64_t)page * a.page_size * a.Hkv + g) * kDm;
                     if constexpr (kFp8) {
                         c.kc8 = (const uint8_t *)a.k_cache + e0;
                         c.vc8 = (const uint8_t *)a.v_cache + e0;
@@ -477,8 +488,8 @@ void k_tree_attn_split(AttnArgs a) {
     u32x4 qraw[kD / 16];
     {
         const __amdgpu_buffer_rsrc_t r_q = make_rsrc(a.q, a.q_bytes);
-        const uint32_t qoff = row_ok ? (uint32_t)((((node0 + node) * a.Hq + hq) * kD + half * 8) * 2) : kOob;
-        load_q(qraw, r_q, qoff);
+        const uint32_t qoff = row_ok ? (uint32_t)((((node0 + node) * a.Hq + hq) * kDm + half * 8) * 2) : kOob;
+        load_q(qraw, r_q, qoff, kDm / 16);
     }
     // ---- which tree blocks of this piece does any row of the tile see? ----
     lds_barrier();   // s_pages / s_bad written above
@@ -505,12 +516,13 @@ void k_tree_attn_split(AttnArgs a) {
         if (row_ok) {
             if (single) {
                 const int64_t orow = (node0 + node) * a.Hq + hq;
-                uint16_t *op = (uint16_t *)a.out + orow * kD + half * 4;
+                uint16_t *op = (uint16_t *)a.out + orow * kDm + half * 4;
                 if (a.lse && half == 0) a.lse[orow] = -INFINITY;
 #pragma unroll
                 for (int d = 0; d < kD / 32; ++d)
 #pragma unroll
-                    for (int gq = 0; gq < 4; ++gq) *(u32x2 *)(op + d * 32 + gq * 8) = u32x2{0u, 0u};
+                    for (int gq = 0; gq < 4; ++gq)
+                        if (d * 32 + gq * 8 < kDm) *(u32x2 *)(op + d * 32 + gq * 8) = u32x2{0u, 0u};
             } else {
                 const int64_t prow = prow0 + wave * 32 + l32;
                 float *op = a.part_o + prow * kD + half * 4;
@@ -548,12 +560,12 @@ void k_tree_attn_split(AttnArgs a) {
     int n_iss = 0;                      // blocks issued so far
     if constexpr (!kFp8) {
         if (kb_iss < kb1) {
-            issue_block<kPaged>(a, c, s_pages, ring0, kb_iss, bad);
+            issue_block<kPaged, kDm>(a, c, s_pages, ring0, kb_iss, bad);
             kb_iss = next_vis(kb_iss + 1);
             n_iss = 1;
         }
         for (; n_iss < kNS - 1 && kb_iss < kb1; ++n_iss) {
-            issue_block<kPaged>(a, c, s_pages, ring0 + (n_iss % kNS) * kStage, kb_iss, bad);
+            issue_block<kPaged, kDm>(a, c, s_pages, ring0 + (n_iss % kNS) * kStage, kb_iss, bad);
             kb_iss = next_vis(kb_iss + 1);
         }
     }
@@ -767,7 +779,7 @@ void k_tree_attn_split(AttnArgs a) {
         auto iter_next = [&](f32x16 &sc0, f32x16 &sc1, f32x16 &sn0, f32x16 &sn1, int kb_nxt) {
             ring_wait((n_iss - (j + 2)) * kOps);            // blocks issued after j+1 stay in flight
             if (kb_iss < kb1) {                             // the stage of block j-1 is free
-                issue_block<kPaged>(a, c, s_pages, ring0 + (n_iss % kNS) * kStage, kb_iss, bad);
+                issue_block<kPaged, kDm>(a, c, s_pages, ring0 + (n_iss % kNS) * kStage, kb_iss, bad);
                 kb_iss = next_vis(kb_iss + 1);
                 ++n_iss;
             }
@@ -812,12 +824,12 @@ void k_tree_attn_split(AttnArgs a) {
         u32x4 k8 = {0u, 0u, 0u, 0u}, v8 = {0u, 0u, 0u, 0u};
         auto issue8 = [&](int kb, int slot) {
             if (kb >= nPB) {                              // tree block: bf16 copies as usual
-                issue_block<kPaged>(a, c, s_pages, ring0 + slot * kStage, kb, bad);
+                issue_block<kPaged, kDm>(a, c, s_pages, ring0 + slot * kStage, kb, bad);
                 return;
             }
             const int pos = kb * kKB + r8;
             uint32_t off = kOob;
-            if (pos < P) {
+            if (pos < P && c8 * 16 < kDm) {
                 if constexpr (!kPaged) {
                     off = (uint32_t)pos * c.rowb8 + c8 * 16u;
                 } else {
@@ -831,7 +843,7 @@ void k_tree_attn_split(AttnArgs a) {
                     }
                     const int page = s_pages[pg - c.page0];
                     if (page >= 0 && page < a.num_pages)
-                        off = (((uint32_t)page * a.page_size + slot_in) * a.Hkv + g) * kD + c8 * 16u;
+                        off = (((uint32_t)page * a.page_size + slot_in) * a.Hkv + g) * kDm + c8 * 16u;
                     else
                         bad = true;
                 }
@@ -946,9 +958,9 @@ void k_tree_attn_split(AttnArgs a) {
             const int idx = cc * kWave + lane, row = idx >> 4, ch = idx & 15;
             const int rr = qt * kTQ + wave * 32 + row;
             const u32x4 v = *(const __attribute__((address_space(3))) u32x4 *)(ob + row * kOutRow + ch * 16);
-            if (rr < R) {
+            if (rr < R && ch * 8 < kDm) {
                 const int64_t orow = (node0 + rr / a.G) * a.Hq + g * a.G + rr % a.G;
-                *(u32x4 *)((uint16_t *)a.out + orow * kD + ch * 8) = v;
+                *(u32x4 *)((uint16_t *)a.out + orow * kDm + ch * 8) = v;
             }
         }
         if (row_ok && half == 0 && a.lse) a.lse[(node0 + node) * a.Hq + hq] = lse_v;
@@ -1000,7 +1012,7 @@ __global__ __launch_bounds__(256) void k_tree_attn_merge(AttnArgs a) {
     const int np = div_up(nbc, a.L);
     if (piece_start(1, nbc, np) >= nB) return;               // written by the split kernel
     const int in_seq = blockIdx.x * (256 / kMergeTPR) + threadIdx.x / kMergeTPR;
-    if (in_seq >= n * a.Hq) return;
+    if (in_seq >= n * a.Hq || sub * 8 >= a.D) return;    // (sub 0 writes the lse)
     const int64_t flat = (int64_t)a.node_off[b] * a.Hq + in_seq;
     const int hq = in_seq % a.Hq;
     const int node = in_seq / a.Hq;
@@ -1051,7 +1063,7 @@ __global__ __launch_bounds__(256) void k_tree_attn_merge(AttnArgs a) {
     u32x4 o;
 #pragma unroll
     for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
-    *(u32x4 *)((uint16_t *)a.out + flat * kD + sub * 8) = o;
+    *(u32x4 *)((uint16_t *)a.out + flat * a.D + sub * 8) = o;
     if (a.lse && sub == 0) a.lse[flat] = wsum > 0.f ? M + logf(wsum) : -INFINITY;
 }
 
@@ -1331,9 +1343,10 @@ hipError_t launch_tree_attn_bf16(const AttnPlan &p, const void *q, const void *k
     a.part_lse = p.any_split ? (float *)((char *)workspace + rows * kD * sizeof(float)) : nullptr;
     a.status = status;
     const int64_t T = p.node_off[p.B];
-    a.q_bytes = (uint32_t)(T * p.Hq * kD * 2);
-    a.tree_bytes = (uint32_t)(T * p.Hkv * kD * 2);
-    a.cache_bytes = (uint32_t)(num_pages * page_size * (int64_t)p.Hkv * kD * (fp8 ? 1 : 2));
+    a.D = p.D;
+    a.q_bytes = (uint32_t)(T * p.Hq * p.D * 2);
+    a.tree_bytes = (uint32_t)(T * p.Hkv * p.D * 2);
+    a.cache_bytes = (uint32_t)(num_pages * page_size * (int64_t)p.Hkv * p.D * (fp8 ? 1 : 2));
     a.mask_bytes = (uint32_t)(T * p.W * 8);
     a.num_pages = num_pages;
     a.page_size = page_size;
@@ -1366,13 +1379,18 @@ hipError_t launch_tree_attn_bf16(const AttnPlan &p, const void *q, const void *k
     }
     for (int i = 0; i < p.B; ++i) a.seq_order[i] = p.seq_order[i];
     const dim3 grid(p.total_items), block(kNW * kWave);
-    if (a.page_mode == 1) {
-        if (fp8) hipLaunchKernelGGL((k_tree_attn_split<false, true>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((k_tree_attn_split<false, false>), grid, block, 0, s, a);
-    } else {
-        if (fp8) hipLaunchKernelGGL((k_tree_attn_split<true, true>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((k_tree_attn_split<true, false>), grid, block, 0, s, a);
-    }
+    auto launch = [&](auto dm) {
+        constexpr int kDm = decltype(dm)::value;
+        if (a.page_mode == 1) {
+            if (fp8) hipLaunchKernelGGL((k_tree_attn_split<false, true, kDm>), grid, block, 0, s, a);
+            else hipLaunchKernelGGL((k_tree_attn_split<false, false, kDm>), grid, block, 0, s, a);
+        } else {
+            if (fp8) hipLaunchKernelGGL((k_tree_attn_split<true, true, kDm>), grid, block, 0, s, a);
+            else hipLaunchKernelGGL((k_tree_attn_split<true, false, kDm>), grid, block, 0, s, a);
+        }
+    };
+    if (p.D == 64) launch(std::integral_constant<int, 64>{});
+    else launch(std::integral_constant<int, kD>{});
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !p.any_split) return e;
     const int64_t per_seq = (int64_t)p.N * p.Hq;
