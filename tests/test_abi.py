@@ -162,6 +162,22 @@ def test_attn_plan_cuts_rows_into_nearly_equal_pieces():
     assert _ws(L, 3, 16, 4, 1, 128, 16, [1024, 512, 256], 1, cus=1) == 0
 
 
+def test_attn_plan_refuses_item_counts_beyond_32_bits():
+    # 256 sequences x 1024 nodes at 32/8 heads (128 rows each) with prefix
+    # bounds near 2^31 in 16-token pages: pieces of at most 2046 pages (511
+    # blocks) give ~2e9 work items, past the 32-bit item indices -> refused,
+    # before any device access (the pointers here are not real)
+    L = jf.lib()
+    pl = np.full(256, 2 ** 31 - 64, np.int32)
+    assert _attn(L, B=256, N=1024, Hq=32, Hkv=8, pl=pl, num_pages=1, page_size=16,
+                 max_pages=2 ** 27) == jf.JF_ERR_UNSUPPORTED
+    assert _ws(L, 256, 1024, 32, 8, 128, 16, pl, 1) == 0
+    # bounds of 2^28 tokens (~3e8 items) plan, and stop at the missing workspace
+    pl = np.full(256, 2 ** 28, np.int32)
+    assert _attn(L, B=256, N=1024, Hq=32, Hkv=8, pl=pl, num_pages=1, page_size=16,
+                 max_pages=2 ** 27) == jf.JF_ERR_WORKSPACE
+
+
 def test_attn_plan_of_packed_trees():
     # packed trees of 256 and 16 nodes (4 and 1 query tiles of 256 rows per KV
     # head) are planned together: 68 and 65 key blocks, 8 KV heads -> 2696

@@ -165,7 +165,7 @@ size_t jf_tree_attn_workspace_size_cus(int32_t B, int32_t N, int32_t Hq, int32_t
     if (dtype == JF_F32) return 0;
     AttnPlan p;
     plan_tree_attn(p, B, N, Hq, Hkv, D, page_size, prefix_len, node_off, dtype, cus);
-    return tree_attn_workspace_bytes(p);
+    return p.fits ? tree_attn_workspace_bytes(p) : 0;
 }
 
 size_t jf_tree_attn_workspace_size(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
@@ -231,6 +231,7 @@ jf_status jf_tree_attn_fwd_cus(const void *q, const void *k_tree, const void *v_
     plan_tree_attn(p, B, N, Hq, Hkv, D, page_size, prefix_len, node_off, dtype, cus);
     hipError_t e;
     if (dtype == JF_BF16) {
+        if (!p.fits) return JF_ERR_UNSUPPORTED;
         const size_t need = tree_attn_workspace_bytes(p);
         if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
             return JF_ERR_WORKSPACE;

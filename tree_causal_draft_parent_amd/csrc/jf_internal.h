@@ -127,6 +127,7 @@ struct AttnPlan {
     int page_size;
     int total_items;     // workgroups of the split kernel
     bool any_split;      // some row has more than one piece (by the bounds)
+    bool fits;           // the work items fit 32-bit indices (else the call is refused)
     int cap[kMaxBatch];              // planned prefix bound of each sequence
     int node_off[kMaxBatch + 1];     // tree rows of sequence b: node_off[b] .. node_off[b+1]-1
     int item_start[kMaxBatch + 1];   // first work item of the sequence at dispatch position p

@@ -1302,16 +1302,20 @@ void plan_tree_attn(AttnPlan &p, int B, int N, int Hq, int Hkv, int D, int page_
     }
     p.L = (int)L;
     int64_t items = 0;
+    for (int b = 0; b < B; ++b) items += np[b] * rows[b];
+    // work item indices and the grid are 32-bit: refuse plans beyond 2^30 items
+    p.fits = items <= ((int64_t)1 << 30);
     p.any_split = false;
+    items = 0;
     for (int i = 0; i < B; ++i) {
         const int b = order[(size_t)i];
         p.seq_order[i] = (uint8_t)b;
-        p.item_start[i] = (int)items;
+        p.item_start[i] = p.fits ? (int)items : 0;
         if (np[b] > 1) p.any_split = true;
         items += np[b] * rows[b];
     }
-    p.item_start[B] = (int)items;
-    p.total_items = (int)items;
+    p.item_start[B] = p.fits ? (int)items : 0;
+    p.total_items = p.fits ? (int)items : 0;
 }
 
 size_t tree_attn_workspace_bytes(const AttnPlan &p) {
