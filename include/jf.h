@@ -183,7 +183,9 @@ jf_status jf_fuse_proj_cus(const void *const *x, int32_t k, int64_t M,
  *               (small problems).
  *   Limits: 1 <= B <= 256, 1 <= N <= 1024, Hq % Hkv == 0; on the bf16
  *   path each of q, k_tree, k_cache (and their value twins) must be smaller
- *   than 4 GiB - 256 bytes (32-bit buffer offsets), else JF_ERR_UNSUPPORTED.
+ *   than 4 GiB - 256 bytes (32-bit buffer offsets), else JF_ERR_UNSUPPORTED;
+ *   so is a plan of more than 2^30 work items (prefix bounds of billions of
+ *   tokens).
  *   workspace:  jf_tree_attn_workspace_size() bytes with the same arguments.
  * ------------------------------------------------------------------------ */
 size_t jf_tree_attn_workspace_size(int32_t B, int32_t N, int32_t Hq,
