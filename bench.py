@@ -12,9 +12,10 @@ on the Qwen3-8B-shaped high-budget workload (1 sequence, 4096-token prefix,
 host, uploaded, and resident in HBM before the timed region.
 
 Prints one JSON line: value = tree nodes per second over K back-to-back steps
-(wall clock between device synchronisations), the step captured once as a HIP
-graph and replayed K times (--eager times the plain launches instead; both
-figures are reported), per-call HIP-event timings from an eager pass,
+(wall clock between device synchronisations), the steps run as HIP graphs of
+four consecutive steps, each step joined on every stream before the next
+begins (--steps-per-graph; the one-step graph and --eager's plain launches are
+reported beside it), per-call HIP-event timings from an eager pass,
 the roofline of the dominant call and of the tree attention, a cold-cache
 variant (a 512 MiB read between steps evicts the 256 MiB last-level cache),
 and the fp64 oracle timed on this host's cores on a bounded sample.
@@ -60,6 +61,9 @@ def parse():
     ap.add_argument("--topk-split", type=float, default=0.0,
                     help="fraction of the top-k rows run on the attention's stream in the two-stream "
                          "step (after the attention; the rest follow the projection on the other)")
+    ap.add_argument("--steps-per-graph", type=int, default=4,
+                    help="consecutive steps captured in one HIP graph, each joined on every stream "
+                         "before the next begins (1: one step a graph)")
     ap.add_argument("--one-stream", action="store_true",
                     help="headline from the graph of the step on one stream (default: two streams)")
     ap.add_argument("--cpu-sample-nodes", type=int, default=256)
@@ -857,36 +861,61 @@ def main():
                  "fit_nine_sixteenths": ((9 * n_cus) // 16, (7 * n_cus) // 16, False),
                  "topk_apart": (n_cus // 2, 0, True)}
 
-    def time_graph(fn, reps=None):
+    # A graph holds S consecutive steps.  Each step's streams join before the
+    # next step forks, so the steps run one after another exactly as in a
+    # draft loop that grows its tree over several steps per verification and
+    # captures them together; what S > 1 saves is the launch of a graph per
+    # step (its first kernels wait for the previous graph's last ones).
+    S = max(1, args.steps_per_graph)
+
+    def time_graph(fn, reps=None, per_graph=None):
+        """Time `reps` steps of fn: reps // S replays of a graph of S steps,
+        then one replay of a graph of the remaining reps % S steps."""
         reps = K if reps is None else reps
+        per_graph = S if per_graph is None else per_graph
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
             fn()
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            fn()
+        graphs = []
+        for n in (per_graph, reps % per_graph):
+            if n == 0:
+                graphs.append(None)
+                continue
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(n):
+                    fn()
+            graphs.append(g)
+        graph, tail = graphs
         for _ in range(args.warmup):
             graph.replay()
+        if tail is not None:
+            tail.replay()
         torch.cuda.synchronize()
         a0 = time.perf_counter()
-        for k in range(reps):
+        for _ in range(reps // per_graph):
             graph.replay()
+        if tail is not None:
+            tail.replay()
         torch.cuda.synchronize()
         a1 = time.perf_counter()
         return a0, a1
 
     ms_per_step = eager_ms_per_step
     serial_graph_ms = None
+    one_step_graph_ms = None
     plan_ms = {}
     plan = next(iter(plans))
     fuse_cus, attn_cus, topk_apart = plans[plan]
     if not args.eager:
         g0, g1 = time_graph(step)
         serial_graph_ms = (g1 - g0) * 1e3 / K
-        print(f"[bench] graph, one stream: {K} replays, {serial_graph_ms:.4f} ms/step", file=sys.stderr, flush=True)
+        print(f"[bench] graph, one stream: {K} steps, {S} a graph, {serial_graph_ms:.4f} ms/step",
+              file=sys.stderr, flush=True)
+        chosen = step
         if args.one_stream or not multi_stream_ok:
             t0, t1 = g0, g1
             plan = "one_stream"
@@ -907,9 +936,15 @@ def main():
                 fuse_cus, attn_cus, topk_apart = 0, 0, False
             else:
                 fuse_cus, attn_cus, topk_apart = plans[plan]
-                t0, t1 = time_graph(make_step_streams(fuse_cus, attn_cus, topk_apart))
+                chosen = make_step_streams(fuse_cus, attn_cus, topk_apart)
+                t0, t1 = time_graph(chosen)
         ms_per_step = (t1 - t0) * 1e3 / K
-        print(f"[bench] graph: {K} replays, {ms_per_step:.4f} ms/step", file=sys.stderr, flush=True)
+        print(f"[bench] graph: {K} steps, {S} a graph, {ms_per_step:.4f} ms/step", file=sys.stderr, flush=True)
+        if S > 1:
+            o0, o1 = time_graph(chosen, per_graph=1)
+            one_step_graph_ms = (o1 - o0) * 1e3 / K
+            print(f"[bench] graph of one step, same plan: {one_step_graph_ms:.4f} ms/step",
+                  file=sys.stderr, flush=True)
 
     # ---- cold-cache steps: evict the last-level cache before each step -------
     flush_buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
@@ -1061,6 +1096,9 @@ def main():
         "launch": ("eager" if args.eager else
                    "hip_graph" if args.one_stream or plan == "one_stream" else
                    "hip_graph_3_streams" if topk_apart else "hip_graph_2_streams"),
+        "steps_per_graph": None if args.eager else S,
+        "graph_one_step_ms_per_step": (None if args.eager else
+                                       round(ms_per_step if S == 1 else one_step_graph_ms, 5)),
         "graph_one_stream_ms_per_step": None if serial_graph_ms is None else round(serial_graph_ms, 5),
         "attn_cus_two_streams": attn_cus,
         "step_plan": plan,

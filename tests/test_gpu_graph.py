@@ -51,13 +51,14 @@ def _setup(i):
     )
     page_status = torch.zeros(1, dtype=torch.int32, device="cuda")
 
-    def step():
-        jf.jf_tree_mask_build(d["parent"], o["mask"], o["depth"], o["seq_status"])
-        jf.jf_fuse_proj(d["xs"], d["w"], y=o["y"], workspace=ws["fuse"])
-        jf.jf_tree_attn_fwd(d["q"], d["k_tree"], d["v_tree"], o["mask"], d["k_cache"], d["v_cache"],
-                            d["block_table"], a["prefix_len"], out=o["out"], lse=o["lse"],
+    def step(oo=None):
+        oo = o if oo is None else oo
+        jf.jf_tree_mask_build(d["parent"], oo["mask"], oo["depth"], oo["seq_status"])
+        jf.jf_fuse_proj(d["xs"], d["w"], y=oo["y"], workspace=ws["fuse"])
+        jf.jf_tree_attn_fwd(d["q"], d["k_tree"], d["v_tree"], oo["mask"], d["k_cache"], d["v_cache"],
+                            d["block_table"], a["prefix_len"], out=oo["out"], lse=oo["lse"],
                             workspace=ws["attn"], status=page_status)
-        jf.jf_node_topk(d["logits"], wl.topk, idx=o["idx"], val=o["val"], lse=o["rlse"],
+        jf.jf_node_topk(d["logits"], wl.topk, idx=oo["idx"], val=oo["val"], lse=oo["rlse"],
                         workspace=ws["topk"])
 
     # the same step on two or three streams: projection (then top-k) beside
@@ -67,25 +68,28 @@ def _setup(i):
     s_side, s_third = torch.cuda.Stream(), torch.cuda.Stream()
 
     def make_streams(fuse_cus=0, attn_cus=0, topk_apart=False):
+        """The step on two or three streams; its argument names the output
+        buffers (default: the shared ones)."""
         fws = torch.empty(max(jf.jf_fuse_proj_workspace_size(R, wl.H, wl.n_fused, wl.H, code, fuse_cus), 1),
                           dtype=torch.uint8, device="cuda")
         aws = torch.empty(max(jf.jf_tree_attn_workspace_size(B, N, wl.Hq, wl.Hkv, wl.D, a["page_size"],
                                                              a["prefix_len"], code, attn_cus), 1),
                           dtype=torch.uint8, device="cuda")
 
-        def step_streams():
+        def step_streams(oo=None):
+            oo = o if oo is None else oo
             main = torch.cuda.current_stream()
             s_side.wait_stream(main)
             if topk_apart:
                 s_third.wait_stream(main)
             with torch.cuda.stream(s_side):
-                jf.jf_fuse_proj(d["xs"], d["w"], y=o["y"], workspace=fws, cus=fuse_cus)
+                jf.jf_fuse_proj(d["xs"], d["w"], y=oo["y"], workspace=fws, cus=fuse_cus)
             with torch.cuda.stream(s_third if topk_apart else s_side):
-                jf.jf_node_topk(d["logits"], wl.topk, idx=o["idx"], val=o["val"], lse=o["rlse"],
+                jf.jf_node_topk(d["logits"], wl.topk, idx=oo["idx"], val=oo["val"], lse=oo["rlse"],
                                 workspace=ws["topk"])
-            jf.jf_tree_mask_build(d["parent"], o["mask"], o["depth"], o["seq_status"])
-            jf.jf_tree_attn_fwd(d["q"], d["k_tree"], d["v_tree"], o["mask"], d["k_cache"], d["v_cache"],
-                                d["block_table"], a["prefix_len"], out=o["out"], lse=o["lse"],
+            jf.jf_tree_mask_build(d["parent"], oo["mask"], oo["depth"], oo["seq_status"])
+            jf.jf_tree_attn_fwd(d["q"], d["k_tree"], d["v_tree"], oo["mask"], d["k_cache"], d["v_cache"],
+                                d["block_table"], a["prefix_len"], out=oo["out"], lse=oo["lse"],
                                 workspace=aws, status=page_status, cus=attn_cus)
             main.wait_stream(s_side)
             if topk_apart:
@@ -142,3 +146,50 @@ def test_step_graph_replays_match_eager(i, plan):
         torch.cuda.synchronize()
         for k in o:
             assert torch.equal(o[k], ref[k]), (rep, k)
+
+
+@pytest.mark.parametrize("i,plan", [(2, "serial"), (2, "fit_nine_sixteenths"), (3, "fit_five_eighths"),
+                                    (4, "streams")])
+def test_steps_chained_in_one_graph(i, plan):
+    # four consecutive steps captured in one graph, as the benchmark times
+    # them: every step writes its own output buffers while all four share the
+    # workspaces, so a step that started before the previous one had joined
+    # (its partials overwritten while still being merged) would change an
+    # output; each step's outputs must equal the eager step's bit for bit
+    wl, d, o, step_serial, make_streams = _setup(i)
+    n_cus = torch.cuda.get_device_properties(0).multi_processor_count
+    step = {"serial": step_serial, "streams": make_streams(),
+            "fit_five_eighths": make_streams((5 * n_cus) // 8, (3 * n_cus) // 8),
+            "fit_nine_sixteenths": make_streams((9 * n_cus) // 16, (7 * n_cus) // 16)}[plan]
+    say(f"four steps in one graph: workload {wl.name}, plan {plan}")
+    step()
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in o.items()}
+    outs = [{k: torch.empty_like(v) for k, v in o.items()} for _ in range(4)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for oo in outs:
+            step(oo)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for oo in outs:
+            step(oo)
+    torch.cuda.synchronize()
+    other = torch.randn(64, 4096, device="cuda").to(torch.bfloat16)
+    for rep in range(3):
+        for oo in outs:
+            for v in oo.values():
+                if v.dtype.is_floating_point:
+                    v.fill_(float("nan"))
+                else:
+                    v.fill_(-7)
+        jf.jf_node_topk(other, 8)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for n, oo in enumerate(outs):
+            for k in o:
+                assert torch.equal(oo[k], ref[k]), (rep, n, k)
