@@ -214,6 +214,25 @@ __global__ __launch_bounds__(Cfg<BM>::kWaves * kWave) void k_fuse_gemm_bf16(Fuse
     }
 
     // lane holds rows (r/4)*8 + half*4 + r%4 of each 32x32 block, column l32
+    if (f.split_k > 1) {
+        // Split-K partials keep the accumulators' own layout: tile by tile,
+        // wave by wave, each 32x32 block as 1024 floats ordered [r/4][lane][r%4].
+        // Every store is then 16 bytes a lane and 1 KiB contiguous a wave
+        // (k_fuse_reduce undoes the layout).
+        float *blk = f.part + ((int64_t)sk * f.tiles_m * f.tiles_n + (int64_t)tm * f.tiles_n + tn) * (BM * kBN)
+                     + (int64_t)wave * (C::TM * C::TN * 1024) + lane * 4;
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                     acc[i][j][4 * q + 3]};
+                    *(f32x4 *)(blk + (i * C::TN + j) * 1024 + q * 256) = v;
+                }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < C::TM; ++i)
 #pragma unroll
@@ -225,9 +244,7 @@ __global__ __launch_bounds__(Cfg<BM>::kWaves * kWave) void k_fuse_gemm_bf16(Fuse
                 const int64_t m = m0 + wm * (BM / C::WM) + i * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
                 if (m >= f.M) continue;
                 const float v = acc[i][j][r];
-                if (f.split_k > 1) {
-                    f.part[((int64_t)sk * f.M + m) * f.N + n] = v;
-                } else if (f.out_bf16) {
+                if (f.out_bf16) {
                     ((uint16_t *)f.y)[m * f.N + n] = (uint16_t)f32_to_bf16_rne(v);
                 } else {
                     ((float *)f.y)[m * f.N + n] = v;
@@ -237,43 +254,51 @@ __global__ __launch_bounds__(Cfg<BM>::kWaves * kWave) void k_fuse_gemm_bf16(Fuse
 }
 
 // y = sum over K slices of the fp32 partials (in slice order), converted to
-// the output type.  Four slices are loaded per round so that a thread's loads
-// overlap.
+// the output type.  A thread takes one 16-byte chunk of the partial layout
+// (four rows of one column of a 32x32 block: chunk c of a BM x 128 tile is
+// block c / 256, row group (c / 64) % 4, lane c % 64), so every load is 1 KiB
+// contiguous a wave; four slices are loaded per round so that a thread's
+// loads overlap.  Rows past M and columns past N are computed and dropped.
+template <int BM>
 __global__ __launch_bounds__(256) void k_fuse_reduce(const float *__restrict__ part, int split_k,
-                                                     int64_t MN, void *y, int out_bf16) {
-    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-    if (i >= MN) return;
-    if (i + 4 <= MN) {
-        f32x4 s = *(const f32x4 *)(part + i);
-        int k = 1;
-        for (; k + 4 <= split_k; k += 4) {
-            f32x4 v[4];
+                                                     int64_t M, int64_t N, int tiles_n, int64_t chunks,
+                                                     void *y, int out_bf16) {
+    typedef Cfg<BM> C;
+    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (c >= chunks) return;
+    const int64_t slice = chunks * 4;   // floats a slice
+    const float *p = part + c * 4;
+    f32x4 s = *(const f32x4 *)p;
+    int k = 1;
+    for (; k + 4 <= split_k; k += 4) {
+        f32x4 v[4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) v[u] = *(const f32x4 *)(part + (int64_t)(k + u) * MN + i);
+        for (int u = 0; u < 4; ++u) v[u] = *(const f32x4 *)(p + (int64_t)(k + u) * slice);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                s[0] += v[u][0]; s[1] += v[u][1]; s[2] += v[u][2]; s[3] += v[u][3];
-            }
+        for (int u = 0; u < 4; ++u) {
+            s[0] += v[u][0]; s[1] += v[u][1]; s[2] += v[u][2]; s[3] += v[u][3];
         }
-        for (; k < split_k; ++k) {
-            f32x4 v = *(const f32x4 *)(part + (int64_t)k * MN + i);
-            s[0] += v[0]; s[1] += v[1]; s[2] += v[2]; s[3] += v[3];
-        }
-        if (out_bf16) {
-            u32x2 w;
-            w[0] = pack_bf16x2(s[0], s[1]);
-            w[1] = pack_bf16x2(s[2], s[3]);
-            *(u32x2 *)((uint16_t *)y + i) = w;
-        } else {
-            *(f32x4 *)((float *)y + i) = s;
-        }
-    } else {
-        for (int64_t e = i; e < MN; ++e) {
-            float s = 0.f;
-            for (int k = 0; k < split_k; ++k) s += part[(int64_t)k * MN + e];
-            if (out_bf16) ((uint16_t *)y)[e] = (uint16_t)f32_to_bf16_rne(s);
-            else ((float *)y)[e] = s;
-        }
+    }
+    for (; k < split_k; ++k) {
+        const f32x4 v = *(const f32x4 *)(p + (int64_t)k * slice);
+        s[0] += v[0]; s[1] += v[1]; s[2] += v[2]; s[3] += v[3];
+    }
+    constexpr int kTileChunks = BM * kBN / 4;
+    const int64_t tile = c / kTileChunks;
+    const int rem = (int)(c % kTileChunks);
+    const int blk = rem >> 8, q = (rem >> 6) & 3, lane = rem & 63;
+    const int wave = blk / (C::TM * C::TN), i = (blk / C::TN) % C::TM, j = blk % C::TN;
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    const int64_t tm = tile / tiles_n, tn = tile % tiles_n;
+    const int64_t m0 = tm * BM + wm * (BM / C::WM) + i * 32 + q * 8 + (lane >> 5) * 4;
+    const int64_t n = tn * kBN + wn * (kBN / C::WN) + j * 32 + (lane & 31);
+    if (n >= N) return;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int64_t m = m0 + r;
+        if (m >= M) break;
+        if (out_bf16) ((uint16_t *)y)[m * N + n] = (uint16_t)f32_to_bf16_rne(s[r]);
+        else ((float *)y)[m * N + n] = s[r];
     }
 }
 
@@ -344,7 +369,9 @@ void plan_fuse(FusePlan &p, int64_t M, int64_t H_in, int k, int64_t H_out, jf_dt
 
 size_t fuse_workspace_bytes(const FusePlan &p) {
     if (p.split_k <= 1) return 0;
-    return (size_t)p.split_k * p.M * p.H_out * sizeof(float);
+    // whole tiles: the partials keep the GEMM tiles' layout
+    const size_t tiles = (size_t)((p.M + p.bm - 1) / p.bm) * (size_t)((p.H_out + kBN - 1) / kBN);
+    return (size_t)p.split_k * tiles * p.bm * kBN * sizeof(float);
 }
 
 hipError_t launch_fuse_bf16(const FusePlan &p, const void *const *x, int64_t ldx, const void *w,
@@ -375,10 +402,15 @@ hipError_t launch_fuse_bf16(const FusePlan &p, const void *const *x, int64_t ldx
         hipLaunchKernelGGL(k_fuse_gemm_bf16<32>, dim3(grid), dim3(Cfg<32>::kWaves * kWave), 0, s, f);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.split_k <= 1) return e;
-    const int64_t MN = p.M * p.H_out;
-    const unsigned g2 = (unsigned)(((MN + 3) / 4 + 255) / 256);
-    hipLaunchKernelGGL(k_fuse_reduce, dim3(g2), dim3(256), 0, s, (const float *)workspace, p.split_k,
-                       MN, y, (int)f.out_bf16);
+    const int64_t chunks = (int64_t)f.tiles_m * f.tiles_n * p.bm * kBN / 4;
+    const unsigned g2 = (unsigned)((chunks + 255) / 256);
+#define JF_REDUCE(BMV)                                                                              \
+    hipLaunchKernelGGL(k_fuse_reduce<BMV>, dim3(g2), dim3(256), 0, s, (const float *)workspace,      \
+                       p.split_k, p.M, p.H_out, f.tiles_n, chunks, y, (int)f.out_bf16)
+    if (p.bm == 256) JF_REDUCE(256);
+    else if (p.bm == 128) JF_REDUCE(128);
+    else JF_REDUCE(32);
+#undef JF_REDUCE
     return hipGetLastError();
 }
 
