@@ -563,8 +563,17 @@ __global__ __launch_bounds__(kWB * kWave) void k_topk_stage1(
             const int e = (int)threadIdx.x >> lg;           // candidate; < chunks * 64 / G, >= n only as spare
             const int part = (int)threadIdx.x & (G - 1);
             const uint64_t key = e < n ? mkeys[e] : 0ull;
+            // eight keys a round in flight (the reads are LDS broadcasts)
             int cnt = 0;
-            for (int j = part; j < n; j += G) cnt += mkeys[j] > key;
+            int j = part;
+            for (; j + 7 * G < n; j += 8 * G) {
+                uint64_t v[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) v[u] = mkeys[j + u * G];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) cnt += v[u] > key;
+            }
+            for (; j < n; j += G) cnt += mkeys[j] > key;
             for (int m = G >> 1; m >= 1; m >>= 1) cnt += __shfl_xor(cnt, m);
             // key 0: padding of a short slice, or a spare lane
             if (part == 0 && key != 0ull && cnt < k) {
