@@ -201,6 +201,11 @@ def test_fuse_plan_for_fewer_compute_units():
     assert L.jf_fuse_proj_workspace_size_cus(256, 4096, 3, 4096, 1, 192) == 6 * 256 * 4096 * 4
     assert L.jf_fuse_proj_workspace_size_cus(256, 4096, 3, 4096, 1, 32) == 0      # one slice: no partials
     assert L.jf_fuse_proj_workspace_size_cus(256, 100, 3, 4096, 1, 192) == 0      # invalid -> 0
+    # the MLP's gate/up projection, 256 x 4096 -> 24576: 192 tiles, more than
+    # half a wave of 256 units, so no K split (two slices would only make two
+    # half-length waves plus the partials); 96 tiles still split in two
+    assert L.jf_fuse_proj_workspace_size_cus(256, 4096, 1, 24576, 1, 256) == 0
+    assert L.jf_fuse_proj_workspace_size_cus(256, 4096, 1, 12288, 1, 256) == 3 * 256 * 12288 * 4
 
 
 def test_fuse_and_topk_argument_errors():

@@ -357,6 +357,10 @@ void plan_fuse(FusePlan &p, int64_t M, int64_t H_in, int k, int64_t H_out, jf_dt
     // leaves some to work on another stream)
     const int64_t target = cus > 0 && cus < num_cus() ? (int64_t)cus : (int64_t)num_cus();
     int64_t s = (target + tiles - 1) / tiles;
+    // With more than half a wave of tiles a split cannot shorten the call: two
+    // slices give two waves of half-length workgroups (the same total) plus
+    // the partials' write and read back.
+    if (2 * tiles > target) s = 1;
     const int64_t ksteps = K / kBK;
     int64_t max_s = ksteps / 8;  // at least eight K steps per slice
     if (max_s < 1) max_s = 1;
