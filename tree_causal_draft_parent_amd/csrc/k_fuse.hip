@@ -18,9 +18,10 @@
 // buffer_load ... lds (no registers); one copy fills 1 KiB = 8 K-contiguous rows
 // (rows n, n+T/8, ... of a T-row tile) and 16-byte block padding keeps the
 // 16-byte operand reads conflict-free.  Per-lane row offsets are computed once;
-// the K position rides in the scalar offset.  When the output has too few
-// tiles to fill the GPU, K is split and the slices' fp32 partials are summed
-// by a second kernel.
+// the K position rides in the scalar offset.  When the output has fewer tiles
+// than half the GPU's compute units, K is split; the slices write fp32
+// partials in the accumulators' own layout (16 bytes a lane) and a second
+// kernel sums them in slice order.
 #include "jf_internal.h"
 
 namespace jf {
