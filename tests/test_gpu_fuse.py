@@ -52,6 +52,17 @@ def test_bf16_ragged_tiles(M, H_in, H_out):
     _run(synth.make_fuse_inputs(M=M, H_in=H_in, H_out=H_out, n_fused=3, dtype="bf16", seed=M))
 
 
+@pytest.mark.parametrize("M,H_in,H_out", [(200, 1024, 300), (100, 512, 257), (20, 1024, 130), (256, 2048, 4100)])
+def test_split_k_ragged_tiles(M, H_in, H_out):
+    # K split into slices over few tiles whose rows or columns run past M or
+    # H_out (256-, 128- and 32-row tiles): the slices' partials cover whole
+    # tiles, and the sum drops what lies outside the output; bf16 and fp32
+    # outputs
+    inp = synth.make_fuse_inputs(M=M, H_in=H_in, H_out=H_out, n_fused=3, dtype="bf16", seed=M + H_out)
+    _run(inp)
+    _run(inp, out_dtype=torch.bfloat16)
+
+
 def test_bf16_out_and_strided_rows():
     inp = synth.make_fuse_inputs(M=70, H_in=256, H_out=300, n_fused=3, dtype="bf16", seed=2)
     _run(inp, out_dtype=torch.bfloat16)
