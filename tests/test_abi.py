@@ -162,6 +162,20 @@ def test_attn_plan_cuts_rows_into_nearly_equal_pieces():
     assert _ws(L, 3, 16, 4, 1, 128, 16, [1024, 512, 256], 1, cus=1) == 0
 
 
+def test_attn_plan_models_dispatch_per_xcd():
+    # rows of 17, 17, 3, 3 and 3 key blocks (prefixes 1024, 1024, 128 x 3 with
+    # 16 nodes, one KV head, one query tile) = 43 units; 8 compute units, one
+    # in each of the 8 XCDs.  The target of 6 blocks gives pieces 6, 6, 5 of
+    # the long rows: 9 items costing 10 10 9 10 10 9 7 7 7.  Workgroup ids go
+    # round-robin over the XCDs, so the ninth item (cost 7) queues behind the
+    # first (cost 10) in the first XCD: span 17 (one pool of 8 units would
+    # start it on a unit that frees at 7: span 14).  Pieces of at most 9-11 blocks (9, 8)
+    # give 7 items in one wave, span 13 <= 0.9 x 17, and win (the largest of
+    # the tied sizes); against the pool's 14 they would not.
+    L = jf.lib()
+    assert _ws(L, 5, 16, 4, 1, 128, 16, [1024, 1024, 128, 128, 128], 1, cus=8) == _attn_ws_bytes(7)
+
+
 def test_attn_plan_refuses_item_counts_beyond_32_bits():
     # 256 sequences x 1024 nodes at 32/8 heads (128 rows each) with prefix
     # bounds near 2^31 in 16-token pages: pieces of at most 2046 pages (511

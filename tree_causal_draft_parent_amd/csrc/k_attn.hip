@@ -124,7 +124,7 @@ __device__ __forceinline__ int piece_start(int k, int nbc, int np) {
 // L2, and each XCD still takes its items in dispatch (longest-first) order.
 // Ids past the last whole round of blocks map to themselves.
 constexpr int kXcdRun = 8;
-__device__ __forceinline__ int xcd_interleave(int bid, int n) {
+__host__ __device__ __forceinline__ int xcd_interleave(int bid, int n) {
     constexpr int kRound = kNumXcd * kXcdRun;
     if (bid >= n / kRound * kRound) return bid;
     const int xcd = bid % kNumXcd, local = bid / kNumXcd;
@@ -1248,35 +1248,47 @@ void plan_tree_attn(AttnPlan &p, int B, int N, int Hq, int Hkv, int D, int page_
     const int64_t items0 = build(L);
     // More work items than compute units: the pieces after the first wave
     // may leave a long tail (just over one wave is the worst case).  A few
-    // piece sizes are then compared by a model of the dispatch -- items in
-    // launch order, each to the compute unit that frees first, each costing
-    // a fixed overhead of 4 blocks plus its blocks -- and the shortest
-    // predicted span wins (ties: the larger pieces, fewer partials).
+    // piece sizes are then compared by a model of the dispatch and the
+    // shortest predicted span wins (ties: the larger pieces, fewer partials).
+    // The model follows the launch: workgroup ids are dealt round-robin over
+    // the XCDs and mapped to work items by xcd_interleave; each XCD hands its
+    // items in id order to whichever of its compute units frees first; an
+    // item costs a fixed overhead of 4 blocks plus its blocks.
     if (dtype != JF_F32 && items0 > target && items0 <= 16 * target) {
+        std::vector<int64_t> cost;
         auto span_of = [&](int64_t Lc) {
             build(Lc);
             constexpr int64_t kOverhead = 4;
-            std::priority_queue<int64_t, std::vector<int64_t>, std::greater<int64_t>> free_at;
-            for (int64_t c = 0; c < target; ++c) free_at.push(0);
-            int64_t span = 0;
+            cost.clear();
             for (int i = 0; i < B; ++i) {
                 const int b = order[(size_t)i];
                 for (int64_t k = 0; k < np[b]; ++k) {
                     const int64_t k0 = k * piece[b];
                     const int64_t size = (k0 + piece[b] < nb[b] ? piece[b] : nb[b] - k0) + kOverhead;
-                    for (int64_t r = 0; r < rows[b]; ++r) {
-                        const int64_t t = free_at.top() + size;
-                        free_at.pop();
-                        free_at.push(t);
-                        span = t > span ? t : span;
-                    }
+                    for (int64_t r = 0; r < rows[b]; ++r) cost.push_back(size);
                 }
+            }
+            const int64_t n = (int64_t)cost.size();
+            const int nq = target >= kNumXcd ? kNumXcd : 1;           // too few units to split: one pool
+            typedef std::priority_queue<int64_t, std::vector<int64_t>, std::greater<int64_t>> Queue;
+            std::vector<Queue> free_at((size_t)nq);
+            for (int x = 0; x < nq; ++x)
+                for (int64_t c = 0; c < target / nq + (x < target % nq ? 1 : 0); ++c) free_at[(size_t)x].push(0);
+            int64_t span = 0;
+            for (int64_t bid = 0; bid < n; ++bid) {
+                Queue &q = free_at[(size_t)(bid % nq)];
+                const int64_t t = q.top() + cost[(size_t)xcd_interleave((int)bid, (int)n)];
+                q.pop();
+                q.push(t);
+                span = t > span ? t : span;
             }
             return span;
         };
-        // the smallest piece size whose items fit in w waves
+        // the smallest piece size whose items fit in w waves (below L too:
+        // smaller pieces that fill two or three waves completely can beat
+        // larger ones that leave the last wave part empty)
         auto fit_waves = [&](int64_t w) {
-            int64_t lo = L, hi = Lmax;
+            int64_t lo = 2, hi = Lmax;
             if (build(hi) > w * target) return (int64_t)-1;
             while (lo < hi) {
                 const int64_t mid = (lo + hi) / 2;
@@ -1286,10 +1298,19 @@ void plan_tree_attn(AttnPlan &p, int B, int N, int Hq, int Hkv, int D, int page_
         };
         // The model ignores the partials' traffic and the merge; a size other
         // than L is taken only when it predicts a span at least 10 % shorter
-        // (measured: the serving batch's predicted 13 % gain came out as 6 %;
-        // packed 16/64/256-node trees, predicted 4 %, came out 7 % slower).
+        // (measured on the serving batch of 32 ragged prefixes: L = 68
+        // predicted 96, the chosen 46 predicted 80; 46 ran 3 % faster than 51,
+        // the choice of a model with one pool of compute units, and 10-15 %
+        // faster than 28-40 blocks).
         const int64_t span0 = span_of(L);
-        std::vector<int64_t> cand = {(3 * L + 3) / 4, (L + 1) / 2, fit_waves(1), fit_waves(2), fit_waves(3)};
+        std::vector<int64_t> cand = {(3 * L + 3) / 4, (L + 1) / 2};
+        for (int64_t w = 1; w <= 3; ++w) {
+            // w waves filled, and slightly larger pieces that leave a few
+            // units of the last wave free for the longest rows' tails
+            const int64_t c = fit_waves(w);
+            if (c < 0) continue;
+            for (int64_t d = 0; d <= 2; ++d) cand.push_back(c + d);
+        }
         int64_t best_L = L, best = -1;
         for (int64_t c : cand) {
             if (c < 2 || c > Lmax || c == L) continue;
