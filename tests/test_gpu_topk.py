@@ -75,11 +75,16 @@ def test_qwen3_8b_high_budget_rows_full_size():
     _check(bits, "bf16", w.topk)
 
 
-def test_qwen3_30b_rows_full_size_sampled():
+def test_qwen3_30b_rows_full_size():
+    # 4 x 256 nodes = 1024 rows of 151936 logits, every row
     w = synth.workload(4)
-    bits = synth.make_logits(R=w.B * w.N, V=w.V, dtype="bf16", seed=1017)
-    rows = np.random.default_rng(0).choice(w.B * w.N, size=96, replace=False)
-    _check(bits, "bf16", w.topk, rows=np.sort(rows))
+    _check(synth.make_logits(R=w.B * w.N, V=w.V, dtype="bf16", seed=1017), "bf16", w.topk)
+
+
+def test_serving_batch_rows_full_size():
+    # 32 sequences x 64 nodes = 2048 rows of 151936 logits, every row
+    w = synth.workload(3)
+    _check(synth.make_logits(R=w.B * w.N, V=w.V, dtype="bf16", seed=1016), "bf16", w.topk)
 
 
 # 128 rows or more with at most 16 slices a row take the one-block-a-row path
