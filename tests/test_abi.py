@@ -351,3 +351,55 @@ def test_product_path_does_not_import_the_oracle():
                 src = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in src and "from oracle" not in src, f
                 assert "liboracle" not in src, f
+
+
+def test_attn_plans_hold_whole_items_on_random_shapes():
+    # host-side planner properties over seeded random batches: the workspace is
+    # empty or whole work items (256 fp32 rows of 128 + an lse each), no more
+    # items than the block units allow, at least one item a (sequence, KV
+    # head, query tile) row; one compute unit never splits; repeated plans agree
+    L = jf.lib()
+    rng = np.random.default_rng(2024)
+    per_item = _attn_ws_bytes(1)
+    for _ in range(300):
+        B = int(rng.integers(1, 65))
+        N = int(rng.integers(1, 513))
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        Hq = Hkv * int(rng.choice([1, 2, 4, 8]))
+        paged = bool(rng.integers(0, 2))
+        pl = rng.integers(0, 20001, size=B).astype(np.int32)
+        page = 16 if paged else max(int(pl.max()), 1)
+        cus = int(rng.choice([0, 1, 8, 96, 112, 192, 256]))
+        ws = _ws(L, B, N, Hq, Hkv, 128, page, pl, 1, cus=cus)
+        assert ws == _ws(L, B, N, Hq, Hkv, 128, page, pl, 1, cus=cus)
+        assert ws % per_item == 0
+        rows = B * Hkv * -(-(N * (Hq // Hkv)) // 256)
+        blocks = [-(-int(p) // 64) + -(-N // 64) for p in pl]
+        units = Hkv * -(-(N * (Hq // Hkv)) // 256) * sum(blocks)
+        items = ws // per_item
+        if items:
+            assert rows < items <= units
+        if cus == 1:
+            assert ws == 0
+
+
+def test_fuse_plans_on_random_shapes():
+    # the projection's split: no workspace, or split_k >= 2 slices of whole
+    # 256/128/32-row x 128-column fp32 tiles; one compute unit never splits
+    L = jf.lib()
+    rng = np.random.default_rng(2025)
+    for _ in range(300):
+        M = int(rng.integers(1, 5000))
+        H_in = 64 * int(rng.integers(1, 65))
+        k = int(rng.integers(1, 5))
+        H_out = int(rng.integers(1, 20000))
+        cus = int(rng.choice([0, 1, 8, 96, 144, 192, 256]))
+        ws = L.jf_fuse_proj_workspace_size_cus(M, H_in, k, H_out, 1, cus)
+        bm = 256 if M >= 192 else (128 if M > 32 else 32)
+        tile = bm * 128 * 4
+        tiles = -(-M // bm) * -(-H_out // 128)
+        assert ws % (tiles * tile) == 0
+        s = ws // (tiles * tile)
+        assert s == 0 or 2 <= s <= (k * H_in // 64) // 8
+        if cus == 1:
+            assert ws == 0
