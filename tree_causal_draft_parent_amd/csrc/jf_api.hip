@@ -5,21 +5,26 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "jf_internal.h"
 
 namespace jf {
 
+// Compute units of the current device, cached per device.  Host threads may
+// call concurrently: each slot is atomic, and racing first calls store the
+// same value.
 int num_cus() {
-    static int cache[64] = {0};
+    static std::atomic<int> cache[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cache[dev] == 0) {
-        int n = 0;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
             n = 256;
-        cache[dev] = n;
+        cache[dev].store(n, std::memory_order_relaxed);
     }
-    return cache[dev];
+    return n;
 }
 
 static inline bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
