@@ -194,9 +194,13 @@ def test_ragged_batch_on_few_compute_units(cus, dev):
             prefix_dev=[0, 10, 500, 2999, 64] if dev else None)
 
 
-def test_serving_batch_fewer_compute_units_sampled():
+@pytest.mark.parametrize("cus", [192, 96, 112])
+def test_serving_batch_fewer_compute_units_sampled(cus):
+    # the serving batch planned for part of the chip: at 192 and 96 units the
+    # rows are cut into pieces of at most 65 blocks (376 work items, more
+    # than one wave); at 112 units every row stays whole (256 items)
     inp = synth.make_workload(3, parts=("attn",))["attn"]
-    compare(inp, rows=tile_rows(inp, 256, 5), label="serving b32", cus=192)
+    compare(inp, rows=tile_rows(inp, 256, 5), label="serving b32", cus=cus)
 
 
 def test_serving_batch_all_rows():
