@@ -95,9 +95,12 @@ def test_split_planned_for_fewer_compute_units(cus):
     _run(synth.make_workload(2, parts=("fuse",))["fuse"], cus=cus)
 
 
-def test_qwen3_30b_shape_full():
-    # 4 x 256 nodes = 1024 rows, 3 x 2048 -> 2048: every row and column
-    _run(synth.make_workload(4, parts=("fuse",))["fuse"])
+@pytest.mark.parametrize("cus", [0, 144, 96])
+def test_qwen3_30b_shape_full(cus):
+    # 4 x 256 nodes = 1024 rows, 3 x 2048 -> 2048 (64 tiles): every row and
+    # column, with the K split planned for all units (4 slices), for 144 (3)
+    # and for 96 (none: the tiles fill more than half of them)
+    _run(synth.make_workload(4, parts=("fuse",))["fuse"], cus=cus)
 
 
 def test_context_rows_full():
